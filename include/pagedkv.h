@@ -1,0 +1,279 @@
+/*
+ * pagedkv.h — C ABI of the MI355X (gfx950) paged KV-cache attention library.
+ *
+ * The library implements the PagedAttention hot path: a host-side block
+ * manager that maps each sequence's logical KV blocks to physical blocks of a
+ * shared pool, the cache-write kernel that appends new keys/values into their
+ * slots, decode attention over the paged cache (split-context partitions plus
+ * a reduction pass), and chunked-prefill attention (MFMA).
+ *
+ * Conventions for every entry point
+ *   - Return value: PKV_OK (0) or a negative PKV_E* code.  pkv_last_error()
+ *     returns a thread-local message for the last failing call.  Arguments are
+ *     validated on the host before anything is launched; on error nothing is
+ *     launched and no state changes.
+ *   - Device pointers (pools, q, out, tables, lens, slot mappings, workspace)
+ *     are owned by the caller (allocated e.g. with PyTorch) and must stay valid
+ *     until the work queued on `stream` has finished.  The library owns only
+ *     its host-side block-manager state.
+ *   - `stream` is a hipStream_t passed as void*; NULL is the default stream.
+ *     Kernels are queued asynchronously; PKV_EHIP reports a launch failure.
+ *   - Block ids, slot numbers and lengths read from device memory are the
+ *     caller's contract: kernels clamp block ids into [0, num_blocks) and
+ *     lengths into [0, max_context_len] so that a bad value can never make
+ *     them touch memory outside the buffers they were given, but the numbers
+ *     produced in that case are unspecified.
+ *   - block_size must be 16 (the pages' default block of 16 tokens).
+ *
+ * KV pool layout (one layer; the pages fix none, this is the library's own).
+ * Elements are `esize` bytes (4 for PKV_F32, 2 for PKV_F16 / PKV_BF16) and
+ * x = 16 / esize elements form one 16-byte chunk:
+ *   K element (block b, kv head g, token slot t, dim j) at element index
+ *       ((((b * n_kv_heads + g) * (head_dim / x) + j / x) * block_size + t) * x + j % x)
+ *   V element (b, g, t, j) at element index
+ *       (((b * n_kv_heads + g) * head_dim + j) * block_size + t)
+ * so one (block, kv head) tile of K or of V is block_size * head_dim * esize
+ * contiguous bytes, and a pool holds num_blocks * n_kv_heads such tiles.
+ * The token in physical slot s lives in block s / block_size at offset
+ * s % block_size.
+ */
+#ifndef PAGEDKV_H
+#define PAGEDKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* status codes */
+#define PKV_OK 0
+#define PKV_EINVAL (-1)        /* bad argument: null, shape, dtype, range */
+#define PKV_ENOMEM_BLOCKS (-2) /* the pool has too few free blocks; nothing changed */
+#define PKV_EUNSUPPORTED (-3)  /* valid but not built: head_dim, group size, block size */
+#define PKV_EHIP (-4)          /* a HIP call or kernel launch failed */
+#define PKV_ESTATE (-5)        /* unknown sequence id, or a pool in the wrong state */
+
+/* element types */
+#define PKV_F32 0
+#define PKV_F16 1
+#define PKV_BF16 2
+
+/* Text of the last error on this thread ("" after a success). */
+const char* pkv_last_error(void);
+
+/* ------------------------------------------------------------------------
+ * Pool sizing and the host block manager
+ * ------------------------------------------------------------------------ */
+
+/* Bytes of K plus V per token across n_layers layers:
+ * 2 * n_layers * n_kv_heads * head_dim * esize.
+ * ("How big is the KV cache?", vLLM Serving deep dive, bytes/token formula.) */
+int paged_kv_bytes_per_token(int32_t n_layers, int32_t n_kv_heads, int32_t head_dim,
+                             int32_t dtype, int64_t* bytes);
+
+/* Whole blocks of block_size tokens, spanning n_layers layers, that fit in
+ * budget_bytes: floor(budget / (block_size * bytes_per_token)).
+ * ("Worked memory example" and "Reading the startup logs", vLLM Serving deep
+ * dive: the "# GPU blocks" figure.) */
+int paged_kv_blocks_for_budget(int64_t budget_bytes, int32_t n_layers, int32_t n_kv_heads,
+                               int32_t head_dim, int32_t block_size, int32_t dtype,
+                               int64_t* num_blocks);
+
+typedef struct pkv_pool pkv_pool; /* opaque host state */
+
+typedef struct pkv_pool_desc {
+  int64_t num_blocks;  /* physical blocks in the pool, >= 1 */
+  int32_t block_size;  /* tokens per block; must be 16 */
+  int32_t n_kv_heads;  /* >= 1 */
+  int32_t head_dim;    /* 64 or 128 */
+  int32_t dtype;       /* PKV_F32, PKV_F16 or PKV_BF16 */
+  int32_t n_layers;    /* layers whose per-layer pools share these block ids, >= 1 */
+  int32_t reserved;    /* must be 0 */
+  /* Host array [num_blocks]: initial order of the free-block queue (a
+   * permutation of 0..num_blocks-1; copied).  NULL means 0, 1, ..., num_blocks-1. */
+  const int32_t* initial_free_order;
+} pkv_pool_desc;
+
+/* Create the block manager of one pool ("PagedAttention in depth", vLLM
+ * Serving deep dive: a global pool of fixed-size blocks and one block table
+ * per sequence; "Back to the queue, and into vLLM proper", Life of a prompt:
+ * the free block queue).  It owns host memory only; the device pools are
+ * caller-allocated buffers of paged_kv_pool_bytes() bytes each, per layer.
+ * *out receives the handle; release it with paged_kv_destroy. */
+int paged_kv_alloc(const pkv_pool_desc* desc, pkv_pool** out);
+
+/* Bytes of one layer's K pool and of one layer's V pool for desc:
+ * num_blocks * n_kv_heads * block_size * head_dim * esize each. */
+int paged_kv_pool_bytes(const pkv_pool_desc* desc, int64_t* k_bytes, int64_t* v_bytes);
+
+/* Free the host state.  Device pools are untouched (the caller owns them). */
+int paged_kv_destroy(pkv_pool* pool);
+
+/* New empty sequence; *seq receives its id (ids count up from 0). */
+int paged_kv_seq_create(pkv_pool* pool, int64_t* seq);
+
+/* New sequence that shares the physical blocks holding the parent's first
+ * n_prefix_tokens tokens (ceil(n / block_size) blocks, each reference count
+ * +1); its length is n_prefix_tokens.  ("Sharing and copy-on-write", vLLM
+ * Serving deep dive.)  PKV_ESTATE if parent is unknown, PKV_EINVAL if
+ * n_prefix_tokens is outside [0, parent length]. */
+int paged_kv_seq_fork(pkv_pool* pool, int64_t parent, int64_t n_prefix_tokens, int64_t* child);
+
+/* Reserve slots for n_tokens new tokens at the end of seq.
+ *   - A new block is taken from the head of the free queue only when the
+ *     sequence's last block is full (so L tokens own ceil(L / 16) blocks).
+ *   - If the last block is partly filled and shared (reference count > 1),
+ *     it is copied first: a fresh block replaces it in this sequence's table
+ *     only, the old block's count drops by one, and the pair (old, new) is
+ *     reported so the caller can copy the device data (paged_kv_copy_blocks)
+ *     before writing.  A full shared block is never written, so no copy.
+ *   ("PagedAttention in depth" and "Sharing and copy-on-write", vLLM Serving
+ *   deep dive; "Back to the queue, and into vLLM proper", Life of a prompt.)
+ * slot_mapping_out: host [n_tokens], receives physical slot
+ *   table[t / 16] * 16 + t % 16 of each new token t (may be NULL).
+ * cow_pairs_out: host [2 * max_cow] int32 (src, dst) pairs (may be NULL when
+ *   max_cow is 0); *n_cow receives the number written (0 or 1).
+ * All or nothing: PKV_ENOMEM_BLOCKS if the free queue cannot supply every
+ * block the append needs — nothing changes, so the caller can preempt
+ * ("The skeleton of a scheduler", LLM Serving from Scratch).  PKV_EINVAL if
+ * max_cow is too small for the copy the append needs (again no change). */
+int paged_kv_seq_append(pkv_pool* pool, int64_t seq, int64_t n_tokens, int64_t* slot_mapping_out,
+                        int32_t* cow_pairs_out, int32_t max_cow, int32_t* n_cow);
+
+/* Blocks the append of n_tokens would take from the free queue (new blocks
+ * plus a copy-on-write block), without changing anything. */
+int paged_kv_seq_blocks_needed(pkv_pool* pool, int64_t seq, int64_t n_tokens, int64_t* n_blocks);
+
+/* Finish seq: every block's reference count drops by one and blocks reaching
+ * zero rejoin the tail of the free queue at once, in the sequence's logical
+ * order ("Back to the queue, and into vLLM proper", Life of a prompt). */
+int paged_kv_seq_free(pkv_pool* pool, int64_t seq);
+
+/* Length (tokens) of seq. */
+int paged_kv_seq_len(pkv_pool* pool, int64_t seq, int64_t* len);
+
+/* Copy seq's block table (logical order) into blocks_out[cap]; *n receives
+ * its length (PKV_EINVAL if cap is smaller; blocks_out may then be NULL to
+ * query the length). */
+int paged_kv_seq_table(pkv_pool* pool, int64_t seq, int32_t* blocks_out, int64_t cap, int64_t* n);
+
+/* Export the block tables of n sequences as a host int32 [n][max_blocks]
+ * array, rows padded with -1, and their lengths as host int32 [n]
+ * (the table the attention kernels read, "How the attention kernel actually
+ * reads paged blocks", vLLM Serving deep dive).  PKV_EINVAL if a table is
+ * longer than max_blocks. */
+int paged_kv_block_tables(pkv_pool* pool, const int64_t* seqs, int32_t n, int32_t max_blocks,
+                          int32_t* tables_out, int32_t* lens_out);
+
+/* Free blocks in the queue. */
+int paged_kv_num_free(pkv_pool* pool, int64_t* n);
+
+/* Reference count of one block (0 for a free block). */
+int paged_kv_block_refcount(pkv_pool* pool, int64_t block, int32_t* ref);
+
+/* Copy the free queue, head first, into out[cap]; *n receives its length. */
+int paged_kv_free_queue(pkv_pool* pool, int32_t* out, int64_t cap, int64_t* n);
+
+/* ------------------------------------------------------------------------
+ * Device operations (HIP, gfx950)
+ * ------------------------------------------------------------------------ */
+
+/* Append new tokens' keys and values into their cache slots (the write that
+ * fills the blocks: "Back to the queue, and into vLLM proper" and "The
+ * decode stage, and how to spot the waste", Life of a prompt — each new key
+ * and value row is appended to the cached ones).
+ *   key, value   device, token i's row at key + i * key_token_stride
+ *                elements: [n_kv_heads][head_dim] contiguous, dtype elements;
+ *                pointers and strides 16-byte aligned.
+ *   k_pool, v_pool  device pools in the layout above (num_blocks blocks).
+ *   slot_mapping device int64 [num_tokens]; slot -1 means skip the token.
+ * A bit-exact copy: no conversion.  Slots >= num_blocks * block_size are
+ * skipped (caller contract). */
+int reshape_and_cache(const void* key, const void* value, int64_t key_token_stride,
+                      int64_t value_token_stride, void* k_pool, void* v_pool,
+                      const int64_t* slot_mapping, int64_t num_tokens, int64_t num_blocks,
+                      int32_t n_kv_heads, int32_t head_dim, int32_t block_size, int32_t dtype,
+                      void* stream);
+
+/* Copy whole blocks of one layer's K and V pools: pairs_dev is device int32
+ * [n_pairs][2] (src, dst), as reported by paged_kv_seq_append for a
+ * copy-on-write ("Sharing and copy-on-write", vLLM Serving deep dive).
+ * Pairs with an id outside [0, num_blocks) are skipped. */
+int paged_kv_copy_blocks(void* k_pool, void* v_pool, const int32_t* pairs_dev, int32_t n_pairs,
+                         int64_t num_blocks, int32_t n_kv_heads, int32_t head_dim,
+                         int32_t block_size, int32_t dtype, void* stream);
+
+/* Context tokens one decode partition covers (the split-context unit). */
+int32_t paged_attention_decode_partition_size(void);
+
+/* Device workspace bytes paged_attention_decode needs for these sizes
+ * (0 when every sequence fits in one partition). */
+int64_t paged_attention_decode_workspace_bytes(int32_t num_seqs, int32_t n_q_heads,
+                                               int32_t head_dim, int32_t max_context_len);
+
+/* Decode attention over the paged cache: one query token per sequence
+ * attends to all context_lens[s] cached keys of its sequence, the newest
+ * (already appended) included.  For query head h, KV head g = h / (n_q_heads
+ * / n_kv_heads):  out[s][h] = sum_j softmax_j(scale * q[s][h] . K_j) V_j.
+ * ("The decode stage, and how to spot the waste", Life of a prompt: one new
+ * query against the full K and V; "How the attention kernel actually reads
+ * paged blocks", vLLM Serving deep dive: the kernel reads the block table and
+ * works block by block.)  Long contexts are split into partitions of
+ * paged_attention_decode_partition_size() tokens whose partial softmax
+ * states are merged by a second reduction kernel.
+ *   out           device [num_seqs][n_q_heads][head_dim], out_dtype
+ *                 (PKV_F32, or the KV dtype).
+ *   q             device [num_seqs][n_q_heads][head_dim], kv_dtype.
+ *   block_tables  device int32 [num_seqs][max_blocks_per_seq].
+ *   context_lens  device int32 [num_seqs]; each in [1, max_context_len]
+ *                 (a sequence with 0 gets zeros).
+ *   max_context_len <= max_blocks_per_seq * block_size.
+ *   workspace     device, >= paged_attention_decode_workspace_bytes(...)
+ *                 bytes (may be NULL when that is 0); contents need no
+ *                 initialisation and are overwritten.
+ * Supported: head_dim 64/128, n_q_heads / n_kv_heads in {1, 2, 4, 8, 16},
+ * block_size 16.  Accumulation is fp32. */
+int paged_attention_decode(void* out, int32_t out_dtype, const void* q, const void* k_pool,
+                           const void* v_pool, const int32_t* block_tables,
+                           int32_t max_blocks_per_seq, const int32_t* context_lens,
+                           int32_t num_seqs, int32_t n_q_heads, int32_t n_kv_heads,
+                           int32_t head_dim, int32_t block_size, int64_t num_blocks,
+                           int32_t max_context_len, float scale, int32_t kv_dtype, void* workspace,
+                           int64_t workspace_bytes, void* stream);
+
+/* Chunked-prefill attention: chunk c holds the query tokens
+ * cu_q_lens[c] .. cu_q_lens[c+1]-1 (rows of q/out) of one sequence whose
+ * keys and values — the cached context plus the chunk itself, already
+ * appended with reshape_and_cache — number context_lens[c].  Query i of
+ * the chunk sits at absolute position p = context_lens[c] - q_len + i and
+ * attends causally to keys 0..p.  ("Chunked prefill" in The hands-on guide
+ * to LLM Inference with vLLM: each chunk's attention reads the KV of every
+ * chunk before it; "The detour, what really happens inside one forward
+ * pass", Life of a prompt: the Q K^T -> softmax -> V contraction.)
+ *   out, q        device [total_q][n_q_heads][head_dim] (out in out_dtype,
+ *                 q in kv_dtype).
+ *   block_tables  device int32 [n_chunks][max_blocks_per_seq].
+ *   cu_q_lens     device int32 [n_chunks + 1], cu_q_lens[0] = 0,
+ *                 non-decreasing, cu_q_lens[n_chunks] = total_q,
+ *                 each q_len <= max_q_len and <= context_lens[c].
+ *   context_lens  device int32 [n_chunks], <= max_context_len
+ *                 <= max_blocks_per_seq * block_size.
+ * Supported: kv_dtype PKV_F16 or PKV_BF16, head_dim 64/128, n_q_heads /
+ * n_kv_heads in {1, 2, 4, 8, 16}, block_size 16.  Products on MFMA, fp32
+ * accumulation and softmax. */
+int paged_attention_prefill_chunk(void* out, int32_t out_dtype, const void* q, const void* k_pool,
+                                  const void* v_pool, const int32_t* block_tables,
+                                  int32_t max_blocks_per_seq, const int32_t* cu_q_lens,
+                                  const int32_t* context_lens, int32_t n_chunks, int32_t total_q,
+                                  int32_t max_q_len, int32_t n_q_heads, int32_t n_kv_heads,
+                                  int32_t head_dim, int32_t block_size, int64_t num_blocks,
+                                  int32_t max_context_len, float scale, int32_t kv_dtype,
+                                  void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDKV_H */

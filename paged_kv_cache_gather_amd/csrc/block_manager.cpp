@@ -1,0 +1,338 @@
+// Host block manager: the free-block queue, per-block reference counts and
+// per-sequence block tables of one KV pool.
+//
+// Rules (restated from the pages):
+//  - a new block comes from the head of the free queue, and only when the
+//    sequence's last block is full; finished sequences return their blocks at
+//    once ("Back to the queue, and into vLLM proper", Life of a prompt;
+//    "PagedAttention in depth", vLLM Serving deep dive);
+//  - block tables may share physical blocks, counted by reference counts;
+//    appending into a shared, partly filled block copies that block for the
+//    appending sequence only ("Sharing and copy-on-write", vLLM Serving deep
+//    dive);
+//  - running out of blocks is reported, not fatal, and leaves the state as it
+//    was so the caller can preempt ("The skeleton of a scheduler", LLM
+//    Serving from Scratch).
+//
+// The free queue is a ring buffer over num_blocks entries (a block is either
+// queued or referenced, never both), so every operation is O(blocks touched).
+#include <algorithm>
+#include <mutex>
+#include <new>
+#include <unordered_map>
+#include <vector>
+
+#include "pkv_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+struct Sequence {
+  std::vector<int32_t> table;
+  int64_t len = 0;
+};
+
+}  // namespace
+
+namespace pkv {
+int fail(int code, const std::string& msg) {
+  g_last_error = msg;
+  return code;
+}
+int ok() {
+  g_last_error.clear();
+  return PKV_OK;
+}
+}  // namespace pkv
+
+struct pkv_pool {
+  int64_t num_blocks = 0;
+  int32_t block_size = 16;
+  int32_t n_kv_heads = 0;
+  int32_t head_dim = 0;
+  int32_t dtype = 0;
+  int32_t n_layers = 1;
+  // free queue ring buffer
+  std::vector<int32_t> ring;
+  int64_t head = 0;   // index of the queue's head in ring
+  int64_t count = 0;  // blocks in the queue
+  std::vector<int32_t> ref;
+  std::unordered_map<int64_t, Sequence> seqs;
+  int64_t next_id = 0;
+  std::mutex mu;
+
+  int32_t pop() {
+    int32_t b = ring[head];
+    head = (head + 1) % num_blocks;
+    --count;
+    ref[b] = 1;
+    return b;
+  }
+  void push(int32_t b) {
+    ring[(head + count) % num_blocks] = b;
+    ++count;
+  }
+  int64_t need(const Sequence& s, int64_t n) const {
+    const int64_t L = s.len, bs = block_size;
+    int64_t blocks = (L + n + bs - 1) / bs - (L + bs - 1) / bs;
+    if (n > 0 && L % bs != 0 && ref[s.table[L / bs]] > 1) ++blocks;
+    return blocks;
+  }
+};
+
+using pkv::fail;
+using pkv::ok;
+
+extern "C" {
+
+const char* pkv_last_error(void) { return g_last_error.c_str(); }
+
+int paged_kv_bytes_per_token(int32_t n_layers, int32_t n_kv_heads, int32_t head_dim,
+                             int32_t dtype, int64_t* bytes) {
+  const int es = pkv::esize_of(dtype);
+  if (!bytes || n_layers <= 0 || n_kv_heads <= 0 || head_dim <= 0 || !es)
+    return fail(PKV_EINVAL, "paged_kv_bytes_per_token: bad argument");
+  *bytes = 2ll * n_layers * n_kv_heads * head_dim * es;
+  return ok();
+}
+
+int paged_kv_blocks_for_budget(int64_t budget_bytes, int32_t n_layers, int32_t n_kv_heads,
+                               int32_t head_dim, int32_t block_size, int32_t dtype,
+                               int64_t* num_blocks) {
+  int64_t per_token = 0;
+  if (!num_blocks || budget_bytes < 0 || block_size <= 0)
+    return fail(PKV_EINVAL, "paged_kv_blocks_for_budget: bad argument");
+  int rc = paged_kv_bytes_per_token(n_layers, n_kv_heads, head_dim, dtype, &per_token);
+  if (rc) return rc;
+  *num_blocks = budget_bytes / (per_token * block_size);
+  return ok();
+}
+
+static int check_desc(const pkv_pool_desc* d) {
+  if (!d) return fail(PKV_EINVAL, "pool descriptor is NULL");
+  if (d->num_blocks < 1 || d->num_blocks > INT32_MAX)
+    return fail(PKV_EINVAL, "num_blocks must be in [1, 2^31)");
+  if (d->block_size != pkv::kBlockSize)
+    return fail(PKV_EUNSUPPORTED, "block_size must be 16");
+  if (d->n_kv_heads < 1 || d->n_layers < 1 || d->reserved != 0)
+    return fail(PKV_EINVAL, "n_kv_heads and n_layers must be >= 1, reserved 0");
+  if (!pkv::esize_of(d->dtype)) return fail(PKV_EINVAL, "unknown dtype");
+  if (d->head_dim != 64 && d->head_dim != 128)
+    return fail(PKV_EUNSUPPORTED, "head_dim must be 64 or 128");
+  return PKV_OK;
+}
+
+int paged_kv_pool_bytes(const pkv_pool_desc* desc, int64_t* k_bytes, int64_t* v_bytes) {
+  int rc = check_desc(desc);
+  if (rc) return rc;
+  const int64_t b = desc->num_blocks * desc->n_kv_heads * desc->block_size * desc->head_dim *
+                    pkv::esize_of(desc->dtype);
+  if (k_bytes) *k_bytes = b;
+  if (v_bytes) *v_bytes = b;
+  return ok();
+}
+
+int paged_kv_alloc(const pkv_pool_desc* desc, pkv_pool** out) {
+  int rc = check_desc(desc);
+  if (rc) return rc;
+  if (!out) return fail(PKV_EINVAL, "out is NULL");
+  pkv_pool* p = new (std::nothrow) pkv_pool();
+  if (!p) return fail(PKV_EINVAL, "host allocation failed");
+  p->num_blocks = desc->num_blocks;
+  p->block_size = desc->block_size;
+  p->n_kv_heads = desc->n_kv_heads;
+  p->head_dim = desc->head_dim;
+  p->dtype = desc->dtype;
+  p->n_layers = desc->n_layers;
+  try {
+    p->ring.resize(p->num_blocks);
+    p->ref.assign(p->num_blocks, 0);
+  } catch (...) {
+    delete p;
+    return fail(PKV_EINVAL, "host allocation failed");
+  }
+  if (desc->initial_free_order) {
+    std::vector<char> seen(p->num_blocks, 0);
+    for (int64_t i = 0; i < p->num_blocks; ++i) {
+      const int32_t b = desc->initial_free_order[i];
+      if (b < 0 || b >= p->num_blocks || seen[b]) {
+        delete p;
+        return fail(PKV_EINVAL, "initial_free_order is not a permutation of the pool");
+      }
+      seen[b] = 1;
+      p->ring[i] = b;
+    }
+  } else {
+    for (int64_t i = 0; i < p->num_blocks; ++i) p->ring[i] = (int32_t)i;
+  }
+  p->head = 0;
+  p->count = p->num_blocks;
+  *out = p;
+  return ok();
+}
+
+int paged_kv_destroy(pkv_pool* pool) {
+  if (!pool) return fail(PKV_EINVAL, "pool is NULL");
+  delete pool;
+  return ok();
+}
+
+int paged_kv_seq_create(pkv_pool* pool, int64_t* seq) {
+  if (!pool || !seq) return fail(PKV_EINVAL, "paged_kv_seq_create: NULL argument");
+  std::lock_guard<std::mutex> lk(pool->mu);
+  const int64_t id = pool->next_id++;
+  pool->seqs.emplace(id, Sequence{});
+  *seq = id;
+  return ok();
+}
+
+int paged_kv_seq_fork(pkv_pool* pool, int64_t parent, int64_t n_prefix_tokens, int64_t* child) {
+  if (!pool || !child) return fail(PKV_EINVAL, "paged_kv_seq_fork: NULL argument");
+  std::lock_guard<std::mutex> lk(pool->mu);
+  auto it = pool->seqs.find(parent);
+  if (it == pool->seqs.end()) return fail(PKV_ESTATE, "paged_kv_seq_fork: unknown parent");
+  if (n_prefix_tokens < 0 || n_prefix_tokens > it->second.len)
+    return fail(PKV_EINVAL, "paged_kv_seq_fork: prefix longer than the parent");
+  const int64_t nb = (n_prefix_tokens + pool->block_size - 1) / pool->block_size;
+  Sequence s;
+  s.table.assign(it->second.table.begin(), it->second.table.begin() + nb);
+  s.len = n_prefix_tokens;
+  for (int32_t b : s.table) ++pool->ref[b];
+  const int64_t id = pool->next_id++;
+  pool->seqs.emplace(id, std::move(s));
+  *child = id;
+  return ok();
+}
+
+int paged_kv_seq_blocks_needed(pkv_pool* pool, int64_t seq, int64_t n_tokens, int64_t* n_blocks) {
+  if (!pool || !n_blocks) return fail(PKV_EINVAL, "paged_kv_seq_blocks_needed: NULL argument");
+  if (n_tokens < 0) return fail(PKV_EINVAL, "n_tokens < 0");
+  std::lock_guard<std::mutex> lk(pool->mu);
+  auto it = pool->seqs.find(seq);
+  if (it == pool->seqs.end()) return fail(PKV_ESTATE, "unknown sequence");
+  *n_blocks = pool->need(it->second, n_tokens);
+  return ok();
+}
+
+int paged_kv_seq_append(pkv_pool* pool, int64_t seq, int64_t n_tokens, int64_t* slot_mapping_out,
+                        int32_t* cow_pairs_out, int32_t max_cow, int32_t* n_cow) {
+  if (!pool) return fail(PKV_EINVAL, "pool is NULL");
+  if (n_tokens < 0) return fail(PKV_EINVAL, "n_tokens < 0");
+  if (max_cow < 0 || (max_cow > 0 && !cow_pairs_out))
+    return fail(PKV_EINVAL, "cow_pairs_out is NULL with max_cow > 0");
+  std::lock_guard<std::mutex> lk(pool->mu);
+  auto it = pool->seqs.find(seq);
+  if (it == pool->seqs.end()) return fail(PKV_ESTATE, "paged_kv_seq_append: unknown sequence");
+  Sequence& s = it->second;
+  const int64_t bs = pool->block_size;
+  const int64_t L = s.len;
+  const bool cow = n_tokens > 0 && L % bs != 0 && pool->ref[s.table[L / bs]] > 1;
+  if (cow && max_cow < 1)
+    return fail(PKV_EINVAL, "append needs a copy-on-write pair but max_cow is 0");
+  const int64_t need = pool->need(s, n_tokens);
+  if (need > pool->count)
+    return fail(PKV_ENOMEM_BLOCKS, "out of KV blocks: need " + std::to_string(need) + ", free " +
+                                       std::to_string(pool->count));
+  int32_t ncow = 0;
+  if (cow) {
+    const int32_t old = s.table[L / bs];
+    const int32_t fresh = pool->pop();
+    --pool->ref[old];
+    s.table[L / bs] = fresh;
+    cow_pairs_out[0] = old;
+    cow_pairs_out[1] = fresh;
+    ncow = 1;
+  }
+  s.table.reserve((L + n_tokens + bs - 1) / bs);
+  for (int64_t t = L; t < L + n_tokens; ++t) {
+    if (t % bs == 0) s.table.push_back(pool->pop());
+    if (slot_mapping_out) slot_mapping_out[t - L] = (int64_t)s.table[t / bs] * bs + t % bs;
+  }
+  s.len = L + n_tokens;
+  if (n_cow) *n_cow = ncow;
+  return ok();
+}
+
+int paged_kv_seq_free(pkv_pool* pool, int64_t seq) {
+  if (!pool) return fail(PKV_EINVAL, "pool is NULL");
+  std::lock_guard<std::mutex> lk(pool->mu);
+  auto it = pool->seqs.find(seq);
+  if (it == pool->seqs.end()) return fail(PKV_ESTATE, "paged_kv_seq_free: unknown sequence");
+  for (int32_t b : it->second.table) {
+    if (--pool->ref[b] == 0) pool->push(b);
+  }
+  pool->seqs.erase(it);
+  return ok();
+}
+
+int paged_kv_seq_len(pkv_pool* pool, int64_t seq, int64_t* len) {
+  if (!pool || !len) return fail(PKV_EINVAL, "NULL argument");
+  std::lock_guard<std::mutex> lk(pool->mu);
+  auto it = pool->seqs.find(seq);
+  if (it == pool->seqs.end()) return fail(PKV_ESTATE, "unknown sequence");
+  *len = it->second.len;
+  return ok();
+}
+
+int paged_kv_seq_table(pkv_pool* pool, int64_t seq, int32_t* blocks_out, int64_t cap, int64_t* n) {
+  if (!pool || !n) return fail(PKV_EINVAL, "NULL argument");
+  std::lock_guard<std::mutex> lk(pool->mu);
+  auto it = pool->seqs.find(seq);
+  if (it == pool->seqs.end()) return fail(PKV_ESTATE, "unknown sequence");
+  const auto& t = it->second.table;
+  *n = (int64_t)t.size();
+  if (!blocks_out) return ok();
+  if (cap < (int64_t)t.size()) return fail(PKV_EINVAL, "paged_kv_seq_table: cap too small");
+  std::copy(t.begin(), t.end(), blocks_out);
+  return ok();
+}
+
+int paged_kv_block_tables(pkv_pool* pool, const int64_t* seqs, int32_t n, int32_t max_blocks,
+                          int32_t* tables_out, int32_t* lens_out) {
+  if (!pool || (n > 0 && (!seqs || !tables_out)) || n < 0 || max_blocks < 0)
+    return fail(PKV_EINVAL, "paged_kv_block_tables: bad argument");
+  std::lock_guard<std::mutex> lk(pool->mu);
+  for (int32_t i = 0; i < n; ++i) {
+    auto it = pool->seqs.find(seqs[i]);
+    if (it == pool->seqs.end()) return fail(PKV_ESTATE, "paged_kv_block_tables: unknown sequence");
+    if ((int64_t)it->second.table.size() > max_blocks)
+      return fail(PKV_EINVAL, "paged_kv_block_tables: table longer than max_blocks");
+    if (it->second.len > INT32_MAX) return fail(PKV_EINVAL, "sequence too long for int32 lens");
+  }
+  for (int32_t i = 0; i < n; ++i) {
+    const Sequence& s = pool->seqs.find(seqs[i])->second;
+    int32_t* row = tables_out + (int64_t)i * max_blocks;
+    std::fill(row, row + max_blocks, -1);
+    std::copy(s.table.begin(), s.table.end(), row);
+    if (lens_out) lens_out[i] = (int32_t)s.len;
+  }
+  return ok();
+}
+
+int paged_kv_num_free(pkv_pool* pool, int64_t* n) {
+  if (!pool || !n) return fail(PKV_EINVAL, "NULL argument");
+  std::lock_guard<std::mutex> lk(pool->mu);
+  *n = pool->count;
+  return ok();
+}
+
+int paged_kv_block_refcount(pkv_pool* pool, int64_t block, int32_t* ref) {
+  if (!pool || !ref) return fail(PKV_EINVAL, "NULL argument");
+  if (block < 0 || block >= pool->num_blocks) return fail(PKV_EINVAL, "block outside the pool");
+  std::lock_guard<std::mutex> lk(pool->mu);
+  *ref = pool->ref[block];
+  return ok();
+}
+
+int paged_kv_free_queue(pkv_pool* pool, int32_t* out, int64_t cap, int64_t* n) {
+  if (!pool || !n) return fail(PKV_EINVAL, "NULL argument");
+  std::lock_guard<std::mutex> lk(pool->mu);
+  *n = pool->count;
+  if (!out) return ok();
+  if (cap < pool->count) return fail(PKV_EINVAL, "paged_kv_free_queue: cap too small");
+  for (int64_t i = 0; i < pool->count; ++i) out[i] = pool->ring[(pool->head + i) % pool->num_blocks];
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,136 @@
+// Cache writes: reshape_and_cache (append new tokens' K/V into their slots)
+// and paged_kv_copy_blocks (whole-block copies for copy-on-write).
+//
+// Both are byte copies.  reshape_and_cache reads each new token's K and V row
+// in 16-byte chunks and writes them into the pool layout: a K chunk stays a
+// contiguous 16-byte unit (the layout keeps x = 16/esize consecutive dims of
+// one token together), while a V chunk is spread over x dim-rows, one
+// element each, since V tiles are dim-major.  Consecutive lanes take
+// consecutive tokens, so tokens that fill one block (a prefill chunk) write
+// contiguous runs.
+#include "pkv_device.h"
+#include "pkv_internal.h"
+
+namespace pkv {
+namespace {
+
+template <int ES>
+__global__ void __launch_bounds__(256)
+reshape_and_cache_kernel(const unsigned char* __restrict__ key, const unsigned char* __restrict__ value,
+                         int64_t kstride_b, int64_t vstride_b, unsigned char* __restrict__ kpool,
+                         unsigned char* __restrict__ vpool, const int64_t* __restrict__ slots,
+                         int64_t T, int64_t num_slots, int H, int D) {
+  constexpr int X = 16 / ES;  // elements per 16-byte chunk
+  const int C = D / X;        // chunks per head row
+  const int64_t total = T * H * C;
+  for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
+       idx += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t i = idx % T;
+    const int64_t rest = idx / T;
+    const int g = (int)(rest % H);
+    const int c = (int)(rest / H);
+    const int64_t slot = slots[i];
+    if (slot < 0 || slot >= num_slots) continue;
+    const int64_t blk = slot / kBlockSize;
+    const int off = (int)(slot % kBlockSize);
+    const int64_t tile = blk * H + g;
+    const u32x4 kv = ld16(key + i * kstride_b + ((int64_t)g * D + c * X) * ES);
+    const u32x4 vv = ld16(value + i * vstride_b + ((int64_t)g * D + c * X) * ES);
+    st16(kpool + (((tile * C + c) * kBlockSize + off) * 16), kv);
+    unsigned char* vrow = vpool + ((tile * D + (int64_t)c * X) * kBlockSize + off) * ES;
+    if constexpr (ES == 4) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        *reinterpret_cast<uint32_t*>(vrow + (int64_t)e * kBlockSize * ES) = vv[e];
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint16_t h = (uint16_t)((e & 1) ? (vv[e >> 1] >> 16) : (vv[e >> 1] & 0xffffu));
+        *reinterpret_cast<uint16_t*>(vrow + (int64_t)e * kBlockSize * ES) = h;
+      }
+    }
+  }
+}
+
+__global__ void __launch_bounds__(256)
+copy_blocks_kernel(unsigned char* __restrict__ kpool, unsigned char* __restrict__ vpool,
+                   const int32_t* __restrict__ pairs, int64_t num_blocks, int64_t block_bytes) {
+  const int64_t src = pairs[2 * blockIdx.x];
+  const int64_t dst = pairs[2 * blockIdx.x + 1];
+  if (src < 0 || dst < 0 || src >= num_blocks || dst >= num_blocks || src == dst) return;
+  const int64_t n16 = block_bytes / 16;
+  for (int64_t j = threadIdx.x; j < n16; j += blockDim.x) {
+    st16(kpool + dst * block_bytes + j * 16, ld16(kpool + src * block_bytes + j * 16));
+    st16(vpool + dst * block_bytes + j * 16, ld16(vpool + src * block_bytes + j * 16));
+  }
+}
+
+}  // namespace
+}  // namespace pkv
+
+using pkv::fail;
+using pkv::ok;
+
+extern "C" int reshape_and_cache(const void* key, const void* value, int64_t key_token_stride,
+                                 int64_t value_token_stride, void* k_pool, void* v_pool,
+                                 const int64_t* slot_mapping, int64_t num_tokens, int64_t num_blocks,
+                                 int32_t n_kv_heads, int32_t head_dim, int32_t block_size,
+                                 int32_t dtype, void* stream) {
+  const int es = pkv::esize_of(dtype);
+  if (!es) return fail(PKV_EINVAL, "reshape_and_cache: unknown dtype");
+  if (block_size != pkv::kBlockSize) return fail(PKV_EUNSUPPORTED, "block_size must be 16");
+  if (head_dim != 64 && head_dim != 128) return fail(PKV_EUNSUPPORTED, "head_dim must be 64 or 128");
+  if (num_tokens < 0 || num_blocks < 1 || n_kv_heads < 1)
+    return fail(PKV_EINVAL, "reshape_and_cache: bad sizes");
+  if (num_tokens == 0) return ok();
+  if (!key || !value || !k_pool || !v_pool || !slot_mapping)
+    return fail(PKV_EINVAL, "reshape_and_cache: NULL pointer");
+  const int64_t row = (int64_t)n_kv_heads * head_dim;
+  if (key_token_stride < row || value_token_stride < row)
+    return fail(PKV_EINVAL, "reshape_and_cache: token stride shorter than a row");
+  if (!pkv::aligned16(key) || !pkv::aligned16(value) || !pkv::aligned16(k_pool) ||
+      !pkv::aligned16(v_pool) || (key_token_stride * es) % 16 || (value_token_stride * es) % 16)
+    return fail(PKV_EINVAL, "reshape_and_cache: pointers and strides must be 16-byte aligned");
+  const int64_t total = num_tokens * n_kv_heads * (head_dim * es / 16);
+  int64_t grid = (total + 255) / 256;
+  if (grid > 16384) grid = 16384;
+  hipStream_t s = (hipStream_t)stream;
+  const int64_t num_slots = num_blocks * pkv::kBlockSize;
+  if (es == 4) {
+    hipLaunchKernelGGL(pkv::reshape_and_cache_kernel<4>, dim3((unsigned)grid), dim3(256), 0, s,
+                       (const unsigned char*)key, (const unsigned char*)value, key_token_stride * 4,
+                       value_token_stride * 4, (unsigned char*)k_pool, (unsigned char*)v_pool,
+                       slot_mapping, num_tokens, num_slots, n_kv_heads, head_dim);
+  } else {
+    hipLaunchKernelGGL(pkv::reshape_and_cache_kernel<2>, dim3((unsigned)grid), dim3(256), 0, s,
+                       (const unsigned char*)key, (const unsigned char*)value, key_token_stride * 2,
+                       value_token_stride * 2, (unsigned char*)k_pool, (unsigned char*)v_pool,
+                       slot_mapping, num_tokens, num_slots, n_kv_heads, head_dim);
+  }
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(PKV_EHIP, std::string("reshape_and_cache: ") + hipGetErrorString(e));
+  return ok();
+}
+
+extern "C" int paged_kv_copy_blocks(void* k_pool, void* v_pool, const int32_t* pairs_dev,
+                                    int32_t n_pairs, int64_t num_blocks, int32_t n_kv_heads,
+                                    int32_t head_dim, int32_t block_size, int32_t dtype,
+                                    void* stream) {
+  const int es = pkv::esize_of(dtype);
+  if (!es) return fail(PKV_EINVAL, "paged_kv_copy_blocks: unknown dtype");
+  if (block_size != pkv::kBlockSize) return fail(PKV_EUNSUPPORTED, "block_size must be 16");
+  if (n_pairs < 0 || num_blocks < 1 || n_kv_heads < 1 || head_dim < 1)
+    return fail(PKV_EINVAL, "paged_kv_copy_blocks: bad sizes");
+  if (n_pairs == 0) return ok();
+  if (!k_pool || !v_pool || !pairs_dev) return fail(PKV_EINVAL, "paged_kv_copy_blocks: NULL pointer");
+  if (!pkv::aligned16(k_pool) || !pkv::aligned16(v_pool))
+    return fail(PKV_EINVAL, "paged_kv_copy_blocks: pools must be 16-byte aligned");
+  const int64_t block_bytes = (int64_t)n_kv_heads * block_size * head_dim * es;
+  if (block_bytes % 16) return fail(PKV_EINVAL, "paged_kv_copy_blocks: block not a multiple of 16 B");
+  hipLaunchKernelGGL(pkv::copy_blocks_kernel, dim3((unsigned)n_pairs), dim3(256), 0,
+                     (hipStream_t)stream, (unsigned char*)k_pool, (unsigned char*)v_pool, pairs_dev,
+                     num_blocks, block_bytes);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(PKV_EHIP, std::string("paged_kv_copy_blocks: ") + hipGetErrorString(e));
+  return ok();
+}

@@ -1,0 +1,110 @@
+// Device-side helpers for the gfx950 kernels: element types, 16-byte vector
+// accesses, conversions and wave64 reductions.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "pagedkv.h"
+
+namespace pkv {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+
+// Storage types: raw bits, so the cache ops copy without conversion.
+struct F32 {
+  using bits = uint32_t;
+  static constexpr int kCode = PKV_F32;
+  static constexpr int kBytes = 4;
+};
+struct F16 {
+  using bits = uint16_t;
+  static constexpr int kCode = PKV_F16;
+  static constexpr int kBytes = 2;
+};
+struct BF16 {
+  using bits = uint16_t;
+  static constexpr int kCode = PKV_BF16;
+  static constexpr int kBytes = 2;
+};
+
+__device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ float f16lo(uint32_t w) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu));
+}
+__device__ __forceinline__ float f16hi(uint32_t w) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+}
+
+// Two packed elements of a 32-bit word -> fp32.
+template <typename T>
+__device__ __forceinline__ void unpack2(uint32_t w, float& lo, float& hi) {
+  if constexpr (T::kCode == PKV_BF16) {
+    lo = bf16lo(w);
+    hi = bf16hi(w);
+  } else {
+    lo = f16lo(w);
+    hi = f16hi(w);
+  }
+}
+
+// acc + a.lo*b.lo + a.hi*b.hi for two packed 16-bit elements, fp32 accumulate.
+template <typename T>
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float acc) {
+  if constexpr (T::kCode == PKV_BF16) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                           __builtin_bit_cast(bf16x2_t, b), acc, false);
+  } else {
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, a), __builtin_bit_cast(f16x2_t, b),
+                                  acc, false);
+  }
+}
+
+// fp32 -> storage bits, round to nearest even (finite inputs).
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40);  // NaN stays NaN
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+__device__ __forceinline__ uint16_t f32_to_f16_bits(float f) {
+  return __builtin_bit_cast(uint16_t, (_Float16)f);
+}
+
+template <int OutCode>
+__device__ __forceinline__ void store_out(void* out, int64_t idx, float v) {
+  if constexpr (OutCode == PKV_F32) {
+    reinterpret_cast<float*>(out)[idx] = v;
+  } else if constexpr (OutCode == PKV_BF16) {
+    reinterpret_cast<uint16_t*>(out)[idx] = f32_to_bf16_bits(v);
+  } else {
+    reinterpret_cast<uint16_t*>(out)[idx] = f32_to_f16_bits(v);
+  }
+}
+
+__device__ __forceinline__ u32x4 ld16(const void* p) {
+  return *reinterpret_cast<const u32x4*>(p);
+}
+__device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
+
+// Wave64 butterfly reductions (every lane receives the result).
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+__device__ __forceinline__ int64_t clamp_block(int64_t b, int64_t num_blocks) {
+  return b < 0 ? 0 : (b >= num_blocks ? num_blocks - 1 : b);
+}
+
+}  // namespace pkv

@@ -160,6 +160,8 @@ class Workload:
         """(owner, a, b) segments covering positions [t0, t1)."""
         if kind == "chunk":
             return [(int(idx), t0, t1)]
+        if kind == "group":
+            return [(GROUP_OWNER_BIT | int(idx), t0, t1)]
         pl = int(self.prefix_len[idx])
         segs = []
         if pl > 0 and t0 < pl:
@@ -169,8 +171,9 @@ class Workload:
         return segs
 
     def kv(self, kind: str, idx: int, t0: int, t1: int):
-        """Raw K and V bits [t1-t0, Hkv, d] of decode sequence (kind="decode")
-        or prefill chunk (kind="chunk") ``idx`` for positions [t0, t1)."""
+        """Raw K and V bits [t1-t0, Hkv, d] of decode sequence (kind="decode"),
+        prefill chunk (kind="chunk") or shared prefix group (kind="group")
+        ``idx`` for positions [t0, t1)."""
         ks, vs = [], []
         for owner, a, b in self._kv_segments(kind, idx, t0, t1):
             ks.append(values(self.seed, KIND_K, owner, a, b, self.n_kv_heads, self.head_dim, self.dtype))
@@ -317,3 +320,20 @@ def fill_device(dst, t0: int, t1: int, heads: int, dim: int, key: int, dtype: st
                            ctypes.c_void_p(tab.data_ptr()), ctypes.c_void_p(stream))
     if rc != 0:
         raise RuntimeError(f"synth_fill failed ({rc})")
+
+
+def build_lib(verbose: bool = False) -> str:
+    """Compile synth/fill.hip into synth/libsynth.so (hipcc, gfx950)."""
+    import subprocess
+    src = os.path.join(_HERE, "fill.hip")
+    out = lib_path()
+    cmd = [os.environ.get("HIPCC", "/opt/rocm/bin/hipcc"), "-O3", "-std=c++17", "-fPIC", "-shared",
+           "--offload-arch=gfx950", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+           src, "-o", out + ".tmp"]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode:
+        raise RuntimeError(f"synth build failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    os.replace(out + ".tmp", out)
+    if verbose:
+        print(f"built {out}")
+    return out

@@ -1,0 +1,59 @@
+"""Shared pieces of the GPU parity tests: oracle references for a workload's
+sequences, and the tolerance rule.
+
+Tolerance (per element, |got - ref| <= atol + rtol * |ref|):
+  * fp32 K/V: rtol 1e-5, atol 1e-6;
+  * fp16 / bf16 K/V with fp32 accumulation: rtol = atol = 2e-3.
+When the output itself is stored in fp16 / bf16, its final rounding adds up
+to u * |ref| (u = 2^-11 for fp16, 2^-8 for bf16, round to nearest), so that
+term is added to rtol: the fp32 result must be within the bound above and
+the stored value within one more rounding of it.
+"""
+import numpy as np
+
+import oracle
+
+U_OUT = {"f32": 0.0, "f16": 2.0 ** -11, "bf16": 2.0 ** -8}
+
+
+def tolerance(kv_dtype: str, out_dtype: str):
+    if kv_dtype == "f32":
+        atol, rtol = 1e-6, 1e-5
+    else:
+        atol, rtol = 2e-3, 2e-3
+    return atol, rtol + U_OUT[out_dtype]
+
+
+def assert_close(name, got, ref, atol, rtol):
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert got.shape == ref.shape, (got.shape, ref.shape)
+    assert np.all(np.isfinite(got)), f"{name}: non-finite output"
+    err = np.abs(got - ref)
+    lim = atol + rtol * np.abs(ref)
+    bad = err > lim
+    if bad.any():
+        i = np.unravel_index(np.argmax(err - lim), err.shape)
+        raise AssertionError(f"{name}: {int(bad.sum())}/{bad.size} outside tolerance; worst at {i}: "
+                             f"got {got[i]:.6g} ref {ref[i]:.6g} (max abs err {err.max():.3e})")
+
+
+def decode_reference(w, s):
+    """Oracle output [Hq, d] for decode sequence s of workload w."""
+    L = int(w.decode_lens[s])
+    k, v = w.kv("decode", s, 0, L)
+    q = w.q("decode", s, L - 1, L)
+    out, ws = oracle.attention(oracle.decode(w.dtype, q), [L - 1], oracle.decode(w.dtype, k),
+                               oracle.decode(w.dtype, v), w.scale)
+    assert np.all(np.abs(ws - 1) < 1e-9)
+    return out[0]
+
+
+def prefill_reference(w, c, n_threads=8):
+    """Oracle output [q_len, Hq, d] for prefill chunk c of workload w."""
+    ctx, ql = int(w.chunk_ctx[c]), int(w.chunk_qlen[c])
+    k, v = w.kv("chunk", c, 0, ctx + ql)
+    q = w.q("chunk", c, ctx, ctx + ql)
+    out, _ = oracle.attention(oracle.decode(w.dtype, q), np.arange(ctx, ctx + ql), oracle.decode(w.dtype, k),
+                              oracle.decode(w.dtype, v), w.scale, n_threads=n_threads)
+    return out

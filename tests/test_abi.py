@@ -1,0 +1,166 @@
+"""The C-ABI library on the host: it loads, exports every entry point the
+header declares, sizes pools like the oracle, and its block manager matches
+the reference model table for table and slot for slot.  No GPU calls."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+from hypothesis import given, settings, strategies as st
+
+import oracle
+import paged_kv_cache_gather_amd as pkv
+from oracle import block_manager as bm
+from tests.conftest import ROOT
+
+
+def _declared_functions():
+    text = open(os.path.join(ROOT, "include", "pagedkv.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[a-z0-9_]+\s*\*?\s*([a-z_][a-z0-9_]*)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_declares_the_four_entry_points():
+    names = _declared_functions()
+    for n in ("paged_kv_alloc", "reshape_and_cache", "paged_attention_decode", "paged_attention_prefill_chunk"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(pkv.LIB_PATH)
+    missing = [n for n in _declared_functions() if not hasattr(lib, n)]
+    assert not missing, missing
+
+
+def test_sizing_matches_oracle():
+    for L, H, d, dt, b in [(32, 8, 128, "bf16", 2), (40, 40, 128, "f16", 2), (22, 4, 64, "f16", 2), (1, 2, 64, "f32", 4)]:
+        assert pkv.paged_kv_bytes_per_token(L, H, d, dt) == oracle.kv_bytes_per_token(L, H, d, b)
+        budget = 54 << 30
+        assert pkv.paged_kv_blocks_for_budget(budget, L, H, d, dt) == oracle.blocks_for_budget(budget, L, H, d, b)
+    kb, vb = pkv.paged_kv_pool_bytes(32768, 8, 128, "bf16")
+    assert kb == vb == 32768 * 8 * 16 * 128 * 2
+
+
+def test_pool_descriptor_validation():
+    with pytest.raises(pkv.PagedKVError) as e:
+        pkv.paged_kv_alloc(16, 2, 96, "f16")
+    assert e.value.code == pkv.PKV_EUNSUPPORTED
+    with pytest.raises(pkv.PagedKVError) as e:
+        pkv.paged_kv_alloc(16, 2, 64, "f16", block_size=32)
+    assert e.value.code == pkv.PKV_EUNSUPPORTED
+    with pytest.raises(pkv.PagedKVError) as e:
+        pkv.paged_kv_alloc(4, 2, 64, "f16", initial_free_order=[0, 1, 1, 2])
+    assert e.value.code == pkv.PKV_EINVAL
+    with pytest.raises(pkv.PagedKVError):
+        pkv.paged_kv_alloc(0, 2, 64, "f16")
+
+
+def test_unknown_sequence_and_bad_fork():
+    p = pkv.paged_kv_alloc(8, 1, 64, "f16")
+    with pytest.raises(pkv.PagedKVError) as e:
+        pkv.paged_kv_seq_append(p, 99, 1)
+    assert e.value.code == pkv.PKV_ESTATE
+    s = pkv.paged_kv_seq_create(p)
+    pkv.paged_kv_seq_append(p, s, 5)
+    with pytest.raises(pkv.PagedKVError) as e:
+        pkv.paged_kv_seq_fork(p, s, 6)
+    assert e.value.code == pkv.PKV_EINVAL
+    pkv.paged_kv_seq_free(p, s)
+    with pytest.raises(pkv.PagedKVError) as e:
+        pkv.paged_kv_seq_free(p, s)
+    assert e.value.code == pkv.PKV_ESTATE
+
+
+def test_out_of_blocks_is_all_or_nothing():
+    p = pkv.paged_kv_alloc(3, 1, 64, "f16")
+    s = pkv.paged_kv_seq_create(p)
+    pkv.paged_kv_seq_append(p, s, 30)
+    before = (pkv.paged_kv_free_queue(p).tolist(), pkv.paged_kv_seq_table(p, s).tolist(), pkv.paged_kv_seq_len(p, s))
+    with pytest.raises(pkv.OutOfBlocks):
+        pkv.paged_kv_seq_append(p, s, 40)
+    after = (pkv.paged_kv_free_queue(p).tolist(), pkv.paged_kv_seq_table(p, s).tolist(), pkv.paged_kv_seq_len(p, s))
+    assert before == after
+
+
+def test_diagram_example_through_the_abi():
+    order = [7, 3, 11] + [b for b in range(16) if b not in (7, 3, 11)]
+    p = pkv.paged_kv_alloc(16, 1, 64, "f16", initial_free_order=order)
+    s = pkv.paged_kv_seq_create(p)
+    slots, cow = pkv.paged_kv_seq_append(p, s, 40)
+    assert pkv.paged_kv_seq_table(p, s).tolist() == [7, 3, 11] and cow == []
+    assert [slots[0], slots[17], slots[32]] == [112, 49, 176]
+    tab, lens = pkv.paged_kv_block_tables(p, [s], 5)
+    assert tab.tolist() == [[7, 3, 11, -1, -1]] and lens.tolist() == [40]
+
+
+def _compare(p, m, sids_p, sids_m):
+    assert pkv.paged_kv_free_queue(p).tolist() == m.free_queue()
+    for a, b in zip(sids_p, sids_m):
+        assert pkv.paged_kv_seq_table(p, a).tolist() == m.table(b)
+        assert pkv.paged_kv_seq_len(p, a) == m.lens[b]
+    for blk in range(m.num_blocks):
+        assert pkv.paged_kv_block_refcount(p, blk) == m.ref[blk]
+
+
+ops = st.lists(st.tuples(st.sampled_from(["create", "append", "fork", "free"]),
+                         st.integers(0, 1000), st.integers(0, 70)), min_size=1, max_size=60)
+
+
+@settings(max_examples=150, deadline=None)
+@given(ops=ops, nblocks=st.integers(1, 40), seed=st.integers(0, 2**16))
+def test_block_manager_matches_model(ops, nblocks, seed):
+    order = np.random.default_rng(seed).permutation(nblocks)
+    p = pkv.paged_kv_alloc(nblocks, 1, 64, "f16", initial_free_order=order)
+    m = bm.BlockManagerModel(nblocks, 16, order)
+    live_p, live_m = [], []
+    for op, pick, n in ops:
+        if op == "create" or not live_p:
+            live_p.append(pkv.paged_kv_seq_create(p))
+            live_m.append(m.create())
+            continue
+        i = pick % len(live_p)
+        if op == "append":
+            try:
+                sm, cm = m.append(live_m[i], n)
+            except bm.OutOfBlocks:
+                with pytest.raises(pkv.OutOfBlocks):
+                    pkv.paged_kv_seq_append(p, live_p[i], n)
+                continue
+            sp, cp = pkv.paged_kv_seq_append(p, live_p[i], n)
+            assert sp.tolist() == sm and cp == cm
+        elif op == "fork":
+            k = pick % (m.lens[live_m[i]] + 1)
+            live_p.append(pkv.paged_kv_seq_fork(p, live_p[i], k))
+            live_m.append(m.fork(live_m[i], k))
+        elif op == "free":
+            pkv.paged_kv_seq_free(p, live_p.pop(i))
+            m.release(live_m.pop(i))
+        _compare(p, m, live_p, live_m)
+    # conservation: every block is either queued or referenced
+    referenced = {b for s in live_m for b in m.table(s)}
+    assert len(referenced) + m.num_free() == nblocks
+    assert pkv.paged_kv_num_free(p) == m.num_free()
+
+
+def test_device_entry_points_validate_before_launch():
+    # host-side validation returns codes without touching a GPU
+    lib = ctypes.CDLL(pkv.LIB_PATH)
+    lib.paged_attention_decode.restype = ctypes.c_int
+    rc = lib.paged_attention_decode(None, 0, None, None, None, None, 1, None, 1, 32, 8, 96, 16,
+                                    ctypes.c_int64(8), 16, ctypes.c_float(0.1), 2, None, ctypes.c_int64(0), None)
+    assert rc == pkv.PKV_EUNSUPPORTED
+    rc = lib.paged_attention_decode(None, 0, None, None, None, None, 1, None, 1, 32, 8, 128, 16,
+                                    ctypes.c_int64(8), 64, ctypes.c_float(0.1), 2, None, ctypes.c_int64(0), None)
+    assert rc == pkv.PKV_EINVAL  # max_context_len beyond the table width
+    rc = lib.paged_attention_decode(None, 0, None, None, None, None, 4, None, 1, 30, 8, 128, 16,
+                                    ctypes.c_int64(8), 64, ctypes.c_float(0.1), 2, None, ctypes.c_int64(0), None)
+    assert rc == pkv.PKV_EINVAL  # 30 % 8
+    lib.reshape_and_cache.restype = ctypes.c_int
+    rc = lib.reshape_and_cache(None, None, ctypes.c_int64(1024), ctypes.c_int64(1024), None, None, None,
+                               ctypes.c_int64(4), ctypes.c_int64(8), 8, 128, 16, 2, None)
+    assert rc == pkv.PKV_EINVAL
+    assert pkv.paged_attention_decode_workspace_bytes(256, 32, 128, 512) == 0
+    part = pkv.paged_attention_decode_partition_size()
+    assert pkv.paged_attention_decode_workspace_bytes(256, 32, 128, 4096) == 256 * 32 * (-(-4096 // part)) * 130 * 4
