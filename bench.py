@@ -1,0 +1,228 @@
+#!/usr/bin/env python3
+"""Benchmark of the paged KV-cache decode step on one MI355X.
+
+Workload (default): the Llama-3-8B-shaped decode batch — one layer, 32 query
+heads over 8 KV heads, head_dim 128, bf16 K/V, block size 16, 256 sequences
+with context lengths uniform in [512, 4096], in groups of 8 that share the
+ref-counted blocks of a 1024-token prefix, the rest of the blocks scattered
+over a 32768-block pool.  One step = append each sequence's new token
+(reshape_and_cache) + paged decode attention (partition pass + split-K
+reduce), inputs resident in HBM.
+
+Prints one JSON line: decode tokens/s (one layer) with the partition kernel's
+achieved HBM bandwidth against the 8 TB/s peak, and the fp64 oracle timed on
+a bounded sample of the same batch on the host cores.
+
+  python bench.py [--steps K] [--warmup W] [--workload 2|3|4] [--no-cpu-baseline]
+  python bench.py --copy-calibration     # plain device copy of a known size
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def decode_bytes(b):
+    """Algorithmic bytes of one partition-pass launch, and the logical KV bytes.
+
+    Unit = one context token of one KV head: 2 * head_dim * esize bytes of K
+    and V.  Physical blocks shared by several sequences count once, with the
+    most tokens any sequence reads from them.  Plus q, block-table entries and
+    lengths read, and the outputs it writes for single-partition sequences."""
+    import numpy as np
+    from paged_kv_cache_gather_amd import paged_attention_decode_partition_size
+    w, d = b.w, b.decode
+    eb = w.elem_bytes
+    unit = 2 * w.head_dim * eb
+    lens = d.lens.astype(np.int64)
+    nb = -(-lens // 16)
+    rows = np.repeat(np.arange(w.n_decode), nb)
+    idx = np.concatenate([np.arange(n) for n in nb])
+    blk = d.tables_host[rows, idx].astype(np.int64)
+    valid = np.minimum(16, lens[rows] - 16 * idx)
+    best = np.zeros(w.num_blocks, np.int64)
+    np.maximum.at(best, blk, valid)
+    unique_tokens = int(best.sum())
+    logical_tokens = int(lens.sum())
+    out_bytes = b.out_dtype.itemsize
+    single = int((lens <= paged_attention_decode_partition_size()).sum())
+    extra = (w.n_decode * w.n_q_heads * w.head_dim * eb + int(nb.sum()) * 4 + 4 * w.n_decode
+             + single * w.n_q_heads * w.head_dim * out_bytes)
+    return {
+        "unit_bytes": unit * w.n_kv_heads,
+        "unique_units": unique_tokens,
+        "unique_kv_bytes": unique_tokens * unit * w.n_kv_heads,
+        "logical_kv_bytes": logical_tokens * unit * w.n_kv_heads,
+        "other_bytes": extra,
+        "algorithmic_bytes": unique_tokens * unit * w.n_kv_heads + extra,
+    }
+
+
+def host_allocator_us(b, reps=5):
+    """Per-step cost of the host block manager on this batch: append one token
+    to every sequence and export the block tables (median of reps).  Run after
+    the timed steps: it advances the host state of b's pool."""
+    import numpy as np
+    import paged_kv_cache_gather_amd as pkv
+    seqs = b.decode.seqs
+    maxb = int(-(-(b.decode.lens.max() + reps) // 16))
+    times = []
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        for q in seqs:
+            pkv.paged_kv_seq_append(b.pool, q, 1)
+        pkv.paged_kv_block_tables(b.pool, seqs, maxb)
+        times.append(time.perf_counter() - t0)
+    return float(np.median(times)) * 1e6
+
+
+def cpu_baseline(w, n_seqs):
+    """The fp64 oracle (as it stands) on every k-th sequence of the batch."""
+    import numpy as np
+    import oracle
+    threads = max(1, min(os.cpu_count() or 1, 16))
+    stride = max(1, w.n_decode // n_seqs)
+    sample = list(range(0, w.n_decode, stride))[:n_seqs]
+    inputs = []
+    for s in sample:
+        L = int(w.decode_lens[s])
+        k, v = w.kv("decode", s, 0, L)
+        inputs.append((w.q("decode", s, L - 1, L), k, v, L))
+    t0 = time.perf_counter()
+    for q, k, v, L in inputs:
+        oracle.attention(oracle.decode(w.dtype, q), [L - 1], oracle.decode(w.dtype, k), oracle.decode(w.dtype, v),
+                         w.scale, n_threads=threads)
+    dt = time.perf_counter() - t0
+    toks = int(sum(x[3] for x in inputs))
+    return {"value": len(sample) / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{len(sample)} of {w.n_decode} decode sequences (every {stride}th, {toks} context "
+                      f"tokens), fp64 decode+attention from contiguous K/V, {dt:.2f} s"}
+
+
+def copy_calibration():
+    import torch
+    n = 1 << 30
+    src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"copied {n} bytes x5")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", type=int, default=3, choices=[2, 3, 4])
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--out-dtype", default="kv", choices=["kv", "f32"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample", type=int, default=64)
+    ap.add_argument("--copy-calibration", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "bench.py measures one GPU: this library has no multi-GPU path "
+                                   "(decode shards by sequence or KV head with no exchange; see DESIGN.md)",
+                          "n_gpus": args.gpus}), flush=True)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import synth
+    from paged_kv_cache_gather_amd.batch import DeviceBatch
+
+    if args.copy_calibration:
+        copy_calibration()
+        return
+
+    w = synth.make_workload(args.workload, seed=args.seed)
+    log(f"building {w.name}: {w.description}")
+    t_build = time.perf_counter()
+    b = DeviceBatch(w, "cuda:0", fill="device", out_dtype=None if args.out_dtype == "kv" else "f32")
+    log(f"built in {time.perf_counter() - t_build:.1f} s")
+    out = b.new_decode_out()
+    stream = torch.cuda.current_stream()
+    K, W = args.steps, args.warmup
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+           torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+
+    def step(e=None):
+        if e is not None:
+            e[0].record(stream)
+        b.append_decode()
+        if e is not None:
+            e[1].record(stream)
+        b.attend_decode_split(out, between=(lambda: e[2].record(stream)) if e is not None else None)
+        if e is not None:
+            e[3].record(stream)
+
+    for _ in range(W):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        step(ev[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / K
+    part_ms = np.array([ev[i][1].elapsed_time(ev[i][2]) for i in range(K)])
+    append_ms = np.array([ev[i][0].elapsed_time(ev[i][1]) for i in range(K)])
+    reduce_ms = np.array([ev[i][2].elapsed_time(ev[i][3]) for i in range(K)])
+    by = decode_bytes(b)
+    part_s = float(part_ms.mean()) * 1e-3
+    achieved = by["algorithmic_bytes"] / part_s / 1e9
+    logical = (by["logical_kv_bytes"] + by["other_bytes"]) / part_s / 1e9
+    tok_s = w.n_decode / (ms_step * 1e-3)
+    log(f"step {ms_step * 1e3:.1f} us | append {append_ms.mean() * 1e3:.1f} us | partitions "
+        f"{part_ms.mean() * 1e3:.1f} us (p10 {np.percentile(part_ms, 10) * 1e3:.1f}, p90 "
+        f"{np.percentile(part_ms, 90) * 1e3:.1f}) | reduce {reduce_ms.mean() * 1e3:.1f} us")
+    log(f"unique {by['unique_kv_bytes'] / 1e9:.3f} GB, logical {by['logical_kv_bytes'] / 1e9:.3f} GB -> "
+        f"{achieved:.0f} GB/s unique ({achieved / HBM_PEAK_GBS:.1%}), {logical:.0f} GB/s logical")
+
+    res = {
+        "metric": "paged-attn decode tokens/sec and achieved HBM GB/s (% of peak), 1 GPU",
+        "value": tok_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "description": w.description, "layers": 1,
+                   "batch": w.n_decode, "n_q_heads": w.n_q_heads, "n_kv_heads": w.n_kv_heads,
+                   "head_dim": w.head_dim, "block_size": w.block_size, "num_blocks": w.num_blocks,
+                   "out_dtype": str(b.out_dtype).replace("torch.", ""), "seed": args.seed,
+                   "step": "reshape_and_cache + decode partition pass + split-K reduce"},
+        "roofline": {"bound": "hbm", "kernel": "decode_partition_kernel", "achieved": achieved,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": None},
+        "breakdown_us": {"append": float(append_ms.mean()) * 1e3, "partitions": float(part_ms.mean()) * 1e3,
+                         "reduce": float(reduce_ms.mean()) * 1e3,
+                         "host_allocator_step": host_allocator_us(b)},
+        "bytes": by,
+        "logical_gbs": logical,
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(w, args.cpu_sample)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

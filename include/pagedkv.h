@@ -243,6 +243,29 @@ int paged_attention_decode(void* out, int32_t out_dtype, const void* q, const vo
                            int32_t max_context_len, float scale, int32_t kv_dtype, void* workspace,
                            int64_t workspace_bytes, void* stream);
 
+/* The two passes of paged_attention_decode, for callers that schedule them
+ * separately (same arguments, same validation).  _partitions runs the
+ * partition pass: sequences that fit in one partition get their final output,
+ * longer ones leave partial softmax states in the workspace.  _reduce then
+ * merges those states into out (a no-op when max_context_len fits one
+ * partition).  Queue _reduce after _partitions on the same stream (or order
+ * them with events) and do not touch the workspace in between. */
+int paged_attention_decode_partitions(void* out, int32_t out_dtype, const void* q,
+                                      const void* k_pool, const void* v_pool,
+                                      const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                      const int32_t* context_lens, int32_t num_seqs,
+                                      int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
+                                      int32_t block_size, int64_t num_blocks,
+                                      int32_t max_context_len, float scale, int32_t kv_dtype,
+                                      void* workspace, int64_t workspace_bytes, void* stream);
+int paged_attention_decode_reduce(void* out, int32_t out_dtype, const void* q, const void* k_pool,
+                                  const void* v_pool, const int32_t* block_tables,
+                                  int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                  int32_t num_seqs, int32_t n_q_heads, int32_t n_kv_heads,
+                                  int32_t head_dim, int32_t block_size, int64_t num_blocks,
+                                  int32_t max_context_len, float scale, int32_t kv_dtype,
+                                  void* workspace, int64_t workspace_bytes, void* stream);
+
 /* Chunked-prefill attention: chunk c holds the query tokens
  * cu_q_lens[c] .. cu_q_lens[c+1]-1 (rows of q/out) of one sequence whose
  * keys and values — the cached context plus the chunk itself, already

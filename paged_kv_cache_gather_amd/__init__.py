@@ -86,6 +86,9 @@ _sig("paged_attention_decode_partition_size", _i32)
 _sig("paged_attention_decode_workspace_bytes", _i64, _i32, _i32, _i32, _i32)
 _sig("paged_attention_decode", ctypes.c_int, _P, _i32, _P, _P, _P, _P, _i32, _P, _i32, _i32, _i32,
      _i32, _i32, _i64, _i32, _f32, _i32, _P, _i64, _P)
+for _n in ("paged_attention_decode_partitions", "paged_attention_decode_reduce"):
+    _sig(_n, ctypes.c_int, _P, _i32, _P, _P, _P, _P, _i32, _P, _i32, _i32, _i32, _i32, _i32, _i64, _i32, _f32,
+         _i32, _P, _i64, _P)
 _sig("paged_attention_prefill_chunk", ctypes.c_int, _P, _i32, _P, _P, _P, _P, _i32, _P, _P, _i32,
      _i32, _i32, _i32, _i32, _i32, _i32, _i64, _i32, _f32, _i32, _P)
 
@@ -183,8 +186,11 @@ class Pool:
         return self._h
 
     def __del__(self):
-        if getattr(self, "_h", None) is not None:
-            _lib.paged_kv_destroy(self._h)
+        if getattr(self, "_h", None) is not None and _lib is not None:
+            try:
+                _lib.paged_kv_destroy(self._h)
+            except Exception:
+                pass
             self._h = None
 
 
@@ -335,12 +341,8 @@ def paged_attention_decode_workspace_bytes(num_seqs: int, n_q_heads: int, head_d
     return int(_lib.paged_attention_decode_workspace_bytes(num_seqs, n_q_heads, head_dim, max_context_len))
 
 
-def paged_attention_decode(out: torch.Tensor, q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
-                           block_tables: torch.Tensor, context_lens: torch.Tensor, max_context_len: int,
-                           n_kv_heads: int, num_blocks: int, scale: float, workspace=None,
-                           block_size: int = BLOCK_SIZE, stream=None):
-    """out [B, Hq, d] (f32 or the KV dtype); q [B, Hq, d] (KV dtype);
-    block_tables int32 [B, max_blocks]; context_lens int32 [B]."""
+def _decode_call(fn, out, q, k_pool, v_pool, block_tables, context_lens, max_context_len, n_kv_heads,
+                 num_blocks, scale, workspace, block_size, stream):
     _dev(out, "out")
     _dev(q, "q", k_pool.dtype)
     _dev(k_pool, "k_pool")
@@ -359,11 +361,36 @@ def paged_attention_decode(out: torch.Tensor, q: torch.Tensor, k_pool: torch.Ten
     if workspace is not None:
         _dev(workspace, "workspace")
         ws_bytes = workspace.numel() * workspace.element_size()
-    _check(_lib.paged_attention_decode(
-        _ptr(out), dtype_code(out.dtype), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_tables),
-        block_tables.shape[1], _ptr(context_lens), B, Hq, n_kv_heads, d, block_size, num_blocks,
-        max_context_len, float(scale), dtype_code(k_pool.dtype), _ptr(workspace), ws_bytes,
-        _stream(stream, q.device)))
+    _check(fn(_ptr(out), dtype_code(out.dtype), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_tables),
+              block_tables.shape[1], _ptr(context_lens), B, Hq, n_kv_heads, d, block_size, num_blocks,
+              max_context_len, float(scale), dtype_code(k_pool.dtype), _ptr(workspace), ws_bytes,
+              _stream(stream, q.device)))
+
+
+def paged_attention_decode(out: torch.Tensor, q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
+                           block_tables: torch.Tensor, context_lens: torch.Tensor, max_context_len: int,
+                           n_kv_heads: int, num_blocks: int, scale: float, workspace=None,
+                           block_size: int = BLOCK_SIZE, stream=None):
+    """out [B, Hq, d] (f32 or the KV dtype); q [B, Hq, d] (KV dtype);
+    block_tables int32 [B, max_blocks]; context_lens int32 [B]."""
+    _decode_call(_lib.paged_attention_decode, out, q, k_pool, v_pool, block_tables, context_lens,
+                 max_context_len, n_kv_heads, num_blocks, scale, workspace, block_size, stream)
+
+
+def paged_attention_decode_partitions(out, q, k_pool, v_pool, block_tables, context_lens, max_context_len,
+                                      n_kv_heads, num_blocks, scale, workspace=None,
+                                      block_size: int = BLOCK_SIZE, stream=None):
+    """Partition pass of paged_attention_decode (same arguments)."""
+    _decode_call(_lib.paged_attention_decode_partitions, out, q, k_pool, v_pool, block_tables, context_lens,
+                 max_context_len, n_kv_heads, num_blocks, scale, workspace, block_size, stream)
+
+
+def paged_attention_decode_reduce(out, q, k_pool, v_pool, block_tables, context_lens, max_context_len,
+                                  n_kv_heads, num_blocks, scale, workspace=None,
+                                  block_size: int = BLOCK_SIZE, stream=None):
+    """Split-context merge pass of paged_attention_decode (same arguments)."""
+    _decode_call(_lib.paged_attention_decode_reduce, out, q, k_pool, v_pool, block_tables, context_lens,
+                 max_context_len, n_kv_heads, num_blocks, scale, workspace, block_size, stream)
 
 
 def paged_attention_prefill_chunk(out: torch.Tensor, q: torch.Tensor, k_pool: torch.Tensor,

@@ -18,6 +18,7 @@ import synth
 from . import (paged_kv_alloc, paged_kv_seq_create, paged_kv_seq_fork, paged_kv_seq_append,
                paged_kv_seq_free, paged_kv_block_tables, paged_kv_copy_blocks, reshape_and_cache,
                paged_attention_decode, paged_attention_decode_workspace_bytes,
+               paged_attention_decode_partitions, paged_attention_decode_reduce,
                paged_attention_prefill_chunk, BLOCK_SIZE)
 
 TORCH_DTYPE = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
@@ -234,6 +235,18 @@ class DeviceBatch:
         w = self.w
         paged_attention_decode(out, d.q, self.k_pool, self.v_pool, d.tables, d.lens_dev, d.max_context_len,
                                w.n_kv_heads, w.num_blocks, w.scale, workspace=d.workspace, stream=stream)
+
+    def attend_decode_split(self, out: torch.Tensor, between=None, stream=None):
+        """The decode attention as its two passes, calling ``between()`` (if
+        given) after queueing the partition pass — e.g. to record an event."""
+        d = self.decode
+        w = self.w
+        args = (out, d.q, self.k_pool, self.v_pool, d.tables, d.lens_dev, d.max_context_len, w.n_kv_heads,
+                w.num_blocks, w.scale)
+        paged_attention_decode_partitions(*args, workspace=d.workspace, stream=stream)
+        if between is not None:
+            between()
+        paged_attention_decode_reduce(*args, workspace=d.workspace, stream=stream)
 
     def append_prefill(self, stream=None):
         p = self.prefill

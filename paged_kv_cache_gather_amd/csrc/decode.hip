@@ -10,28 +10,35 @@
 // waste", Life of a prompt).
 //
 // How (gfx950):
-//  * Work unit = (partition p of 512 context tokens, KV head g, sequence s),
+//  * Work unit = (KV head g, sequence s, partition p of 512 context tokens),
 //    one 256-thread workgroup (4 wave64s).  All G query heads that share the
 //    KV head are handled together, so every K/V byte is read once per step.
-//  * Phase 1, scores: each thread takes one token, reads its whole K row
-//    (16-byte chunks; the K layout keeps 8 dims of one token together) and
-//    forms G dot products with packed dot2 instructions (fp32 accumulate).
-//    The query is uniform across the workgroup and is read through the
-//    scalar unit.  Scores, pre-multiplied by scale*log2(e), go to LDS.
-//  * Phase 2, softmax: workgroup max per head, then p = 2^(s - max) in LDS and
-//    the per-head sum.
-//  * Phase 3, values: wave w takes blocks w, w+4, ...; lane l owns D/64
-//    consecutive dims and reads their dim-major V rows (16 tokens each,
-//    contiguous), accumulating p * v in fp32 with p broadcast from LDS.
-//    The four waves' partial sums are added through LDS.
-//  * A sequence that fits in one partition writes its normalised output
-//    directly; otherwise each partition writes (max, sum, unnormalised o) to
-//    the workspace and decode_reduce_kernel merges them:
+//    The grid runs KV head fastest: consecutive workgroups go round-robin to
+//    the 8 XCDs, so with 8 KV heads every workgroup of one head lands on the
+//    same XCD, and sequences that share prefix blocks (adjacent in the batch)
+//    hit that XCD's L2.  Partitions past a sequence's end come last and exit.
+//  * Each wave owns 128 consecutive tokens of the partition end to end:
+//    - scores: one token per lane; the lane reads its token's whole K row
+//      (16-byte chunks; the K layout keeps x dims of one token together, so
+//      each wave instruction reads 4 blocks x 256 contiguous bytes) and forms
+//      G dot products with packed dot2 instructions (fp32 accumulate).  The
+//      query is uniform across the workgroup and is read by the scalar unit.
+//    - wave-local softmax in base 2 (scores pre-scaled by scale*log2 e):
+//      max and sum by wave64 butterflies, probabilities to wave-private LDS.
+//    - values: each wave instruction reads 1 KiB of a block's dim-major V
+//      tile; lane l gets D/64 dims x (16/CPR) tokens and accumulates p*v in
+//      fp32 with the probabilities read from LDS; the CPR lanes sharing a
+//      dim are added with shuffles.
+//  * The four waves' (max, sum, o) states are merged through LDS.  A sequence
+//    that fits in one partition writes its normalised output; otherwise each
+//    partition writes (max, sum, unnormalised o) to the workspace and
+//    decode_reduce_kernel merges them:
 //      M = max_p m_p,  out = sum_p 2^(m_p - M) o_p / sum_p 2^(m_p - M) l_p.
 #include <math.h>
 
 #include <cmath>
 #include <string>
+#include <type_traits>
 
 #include "pkv_device.h"
 #include "pkv_internal.h"
@@ -39,35 +46,48 @@
 namespace pkv {
 namespace {
 
-constexpr int kPart = 512;        // context tokens per partition
-constexpr int kThreads = 256;     // threads per workgroup
+// Tuning knobs (compile-time; the defaults are the measured best on MI355X).
+#ifndef PKV_DECODE_PART
+#define PKV_DECODE_PART 512
+#endif
+#ifndef PKV_DECODE_MIN_WAVES
+#define PKV_DECODE_MIN_WAVES 2
+#endif
+#ifndef PKV_DECODE_V_UNROLL
+#define PKV_DECODE_V_UNROLL 2
+#endif
+constexpr int kPart = PKV_DECODE_PART;  // context tokens per partition
+constexpr int kVUnroll = PKV_DECODE_V_UNROLL;
+constexpr int kThreads = 256;           // threads per workgroup
 constexpr int kWaves = kThreads / 64;
-constexpr int kTokPerThread = kPart / kThreads;
 
 template <typename T, int D, int G, int OutCode>
-__global__ void __launch_bounds__(kThreads, 2)
+__global__ void __launch_bounds__(kThreads, PKV_DECODE_MIN_WAVES)
 decode_partition_kernel(void* __restrict__ out, float* __restrict__ ws_o, float* __restrict__ ws_ml,
                         const typename T::bits* __restrict__ q, const unsigned char* __restrict__ kpool,
                         const unsigned char* __restrict__ vpool, const int32_t* __restrict__ tables,
                         int max_blocks, const int32_t* __restrict__ lens, int Hkv, int64_t num_blocks,
                         int max_context_len, float scale_log2, int max_parts) {
   constexpr int ES = T::kBytes;
-  constexpr int X = 16 / ES;    // elements per 16-byte chunk
-  constexpr int C = D / X;      // chunks per K row
-  constexpr int DPL = D / 64;   // dims per lane in the V pass
-  constexpr int VCH = DPL * kBlockSize * ES / 16;  // 16-byte V chunks per lane per block
+  constexpr int X = 16 / ES;                 // elements per 16-byte chunk
+  constexpr int C = D / X;                   // chunks per K row
+  constexpr int TPW = kPart / kWaves;        // context tokens per wave
+  constexpr int IT = TPW / 64;               // score iterations per wave (one token per lane)
+  constexpr int CPR = ES;                    // 16-byte chunks per V dim-row of one block
+  constexpr int TPC = kBlockSize / CPR;      // tokens per V chunk
+  constexpr int NI = D * ES / 64;            // V chunks per lane per block (= dims per lane)
+  constexpr int VTILE = D * kBlockSize * ES; // bytes of one (block, head) V tile
 
-  // Scores/probabilities [G][kPart]; after the V pass the same memory holds
-  // the waves' partial outputs [kWaves][G][D] (kWaves * D <= kPart).
-  static_assert(kWaves * D <= kPart, "partial outputs must fit in the score buffer");
-  __shared__ float smem[G * kPart];
-  __shared__ float wred[kWaves][G];
-  float(*sc)[kPart] = reinterpret_cast<float(*)[kPart]>(smem);
-  float(*red)[G][D] = reinterpret_cast<float(*)[G][D]>(smem);
+  // Per-wave probabilities [kWaves][TPW][G]; after the V pass the same memory
+  // holds the waves' partial outputs [kWaves][G][D].
+  constexpr int SMEM = (kPart > kWaves * D ? kPart : kWaves * D) * G;
+  __shared__ __attribute__((aligned(16))) float smem[SMEM];
+  __shared__ float sml[kWaves][G][2];
 
-  const int p = blockIdx.x, g = blockIdx.y, s = blockIdx.z;
+  const int g = blockIdx.x, s = blockIdx.y, p = blockIdx.z;
   const int Hq = Hkv * G;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform per wave
 
   int L = lens[s];
   L = L < 0 ? 0 : (L > max_context_len ? max_context_len : L);
@@ -79,25 +99,24 @@ decode_partition_kernel(void* __restrict__ out, float* __restrict__ ws_o, float*
     return;
   }
   const int t0 = p * kPart;
-  const int n = (L - t0) < kPart ? (L - t0) : kPart;
-  const int32_t* tab = tables + (int64_t)s * max_blocks;
+  const int n = (L - t0) < kPart ? (L - t0) : kPart;  // tokens in this partition
+  const int wt0 = w * TPW;                               // wave's first token (partition-local)
+  const int wn = n - wt0 < 0 ? 0 : (n - wt0 > TPW ? TPW : n - wt0);
+  const int32_t* tab = tables + (int64_t)s * max_blocks + t0 / kBlockSize;
+  float(*sp)[G] = reinterpret_cast<float(*)[G]>(smem) + w * TPW;
 
-  // ---- phase 1: scores ---------------------------------------------------
-  float mx[G];
-#pragma unroll
-  for (int h = 0; h < G; ++h) mx[h] = -INFINITY;
+  // ---- scores: one token per lane, G heads, whole K row --------------------
+  float sreg[IT][G];
   const typename T::bits* qg = q + ((int64_t)s * Hq + g * G) * D;
-
-#pragma unroll 1
-  for (int k = 0; k < kTokPerThread; ++k) {
-    const int tl = tid + k * kThreads;
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    const int tl = wt0 + it * 64 + lane;
     float acc[G];
 #pragma unroll
     for (int h = 0; h < G; ++h) acc[h] = 0.f;
-    if (tl < n) {
-      const int t = t0 + tl;
-      const int64_t blk = clamp_block(tab[t >> 4], num_blocks);
-      const unsigned char* kp = kpool + (((blk * Hkv + g) * C) * kBlockSize + (t & 15)) * 16;
+    if (it * 64 < wn && tl < n) {
+      const int64_t blk = clamp_block(tab[tl >> 4], num_blocks);
+      const unsigned char* kp = kpool + (((blk * Hkv + g) * C) * kBlockSize + (tl & 15)) * 16;
       u32x4 kc[C];
 #pragma unroll
       for (int c = 0; c < C; ++c) kc[c] = ld16(kp + c * (kBlockSize * 16));
@@ -121,125 +140,135 @@ decode_partition_kernel(void* __restrict__ out, float* __restrict__ ws_o, float*
       }
     }
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      const float sv = tl < n ? acc[h] * scale_log2 : -INFINITY;
-      sc[h][tl] = sv;
-      mx[h] = fmaxf(mx[h], sv);
-    }
+    for (int h = 0; h < G; ++h) sreg[it][h] = tl < n ? acc[h] * scale_log2 : -INFINITY;
   }
 
-  // ---- phase 2: softmax over the partition --------------------------------
+  // ---- wave-local softmax state -------------------------------------------
+  float mw[G], lw[G];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
-    const float m = wave_max(mx[h]);
-    if (lane == 0) wred[w][h] = m;
+    float m = sreg[0][h];
+#pragma unroll
+    for (int it = 1; it < IT; ++it) m = fmaxf(m, sreg[it][h]);
+    mw[h] = wave_max(m);
   }
-  __syncthreads();
-  float M[G];
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
-    float m = wred[0][h];
+  for (int it = 0; it < IT; ++it) {
+    const bool valid = wt0 + it * 64 + lane < n;
+    float e[G];
 #pragma unroll
-    for (int i = 1; i < kWaves; ++i) m = fmaxf(m, wred[i][h]);
-    M[h] = m;
-  }
-  __syncthreads();
-  float ls[G];
+    for (int h = 0; h < G; ++h) e[h] = valid ? __builtin_amdgcn_exp2f(sreg[it][h] - mw[h]) : 0.f;
 #pragma unroll
-  for (int h = 0; h < G; ++h) ls[h] = 0.f;
+    for (int h = 0; h < G; ++h) sp[it * 64 + lane][h] = e[h];
 #pragma unroll
-  for (int k = 0; k < kTokPerThread; ++k) {
-    const int tl = tid + k * kThreads;
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      const float e = tl < n ? __builtin_amdgcn_exp2f(sc[h][tl] - M[h]) : 0.f;
-      sc[h][tl] = e;
-      ls[h] += e;
-    }
+    for (int h = 0; h < G; ++h) sreg[it][h] = e[h];
   }
 #pragma unroll
   for (int h = 0; h < G; ++h) {
-    const float l = wave_sum(ls[h]);
-    if (lane == 0) wred[w][h] = l;
+    float l = sreg[0][h];
+#pragma unroll
+    for (int it = 1; it < IT; ++it) l += sreg[it][h];
+    lw[h] = wave_sum(l);
   }
-  __syncthreads();
+  // the probabilities are read back by other lanes of this wave
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
-  // ---- phase 3: values ---------------------------------------------------
-  float o[G][DPL];
+  // ---- values: lane owns NI dims x TPC tokens of each block -----------------
+  // Chunk i of a block's V tile (1 KiB per wave instruction, fully coalesced)
+  // gives lane l the dim (i*64 + l) / CPR and tokens (l % CPR) * TPC + [0, TPC).
+  float o[G][NI];
 #pragma unroll
   for (int h = 0; h < G; ++h)
 #pragma unroll
-    for (int dd = 0; dd < DPL; ++dd) o[h][dd] = 0.f;
-  const int nblk = (n + kBlockSize - 1) / kBlockSize;
-  const int b0 = t0 / kBlockSize;
-#pragma unroll 1
-  for (int b = w; b < nblk; b += kWaves) {
-    const int64_t blk = clamp_block(tab[b0 + b], num_blocks);
-    const unsigned char* vp =
-        vpool + ((blk * Hkv + g) * D + (int64_t)lane * DPL) * kBlockSize * ES;
-    u32x4 vv[VCH];
+    for (int i = 0; i < NI; ++i) o[h][i] = 0.f;
+  const int tg = lane % CPR;
+  const int nbw = (wn + kBlockSize - 1) / kBlockSize;
+#pragma unroll kVUnroll
+  for (int bl = 0; bl < nbw; ++bl) {
+    const int tb = wt0 / kBlockSize + bl;  // partition-local block
+    const int64_t blk = clamp_block(tab[tb], num_blocks);
+    const unsigned char* vp = vpool + (blk * Hkv + g) * (int64_t)VTILE + lane * 16;
+    u32x4 vv[NI];
 #pragma unroll
-    for (int i = 0; i < VCH; ++i) vv[i] = ld16(vp + i * 16);
-    const int ntok = (n - b * kBlockSize) < kBlockSize ? (n - b * kBlockSize) : kBlockSize;
-    const float* pb = &sc[0][b * kBlockSize];
-    auto vel = [&](int dd, int t) -> float {
-      if constexpr (ES == 2) {
-        const int wd = (dd * kBlockSize + t) >> 1;
-        const uint32_t word = vv[wd >> 2][wd & 3];
-        float lo, hi;
-        unpack2<T>(word, lo, hi);
-        return (t & 1) ? hi : lo;
-      } else {
-        const int wd = dd * kBlockSize + t;
-        return __uint_as_float(vv[wd >> 2][wd & 3]);
+    for (int i = 0; i < NI; ++i) vv[i] = ld16(vp + i * 1024);
+    const int ntok = n - tb * kBlockSize;
+    const float(*pb)[G] = sp + bl * kBlockSize + tg * TPC;
+    auto accumulate = [&](auto masked) {
+#pragma unroll
+      for (int tt = 0; tt < TPC; ++tt) {
+        float pv[G];
+#pragma unroll
+        for (int h = 0; h < G; ++h) pv[h] = pb[tt][h];
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+          float x;
+          if constexpr (ES == 2) {
+            float lo, hi;
+            unpack2<T>(vv[i][tt >> 1], lo, hi);
+            x = (tt & 1) ? hi : lo;
+          } else {
+            x = __uint_as_float(vv[i][tt]);
+          }
+          if constexpr (decltype(masked)::value) {
+            x = tg * TPC + tt < ntok ? x : 0.f;  // slots past the context may hold anything
+          }
+#pragma unroll
+          for (int h = 0; h < G; ++h) o[h][i] = fmaf(pv[h], x, o[h][i]);
+        }
       }
     };
-    if (ntok == kBlockSize) {
+    if (ntok >= kBlockSize)
+      accumulate(std::false_type{});
+    else
+      accumulate(std::true_type{});
+  }
+  // add the CPR lanes that share a dim
 #pragma unroll
-      for (int t = 0; t < kBlockSize; ++t) {
+  for (int msk = 1; msk < CPR; msk <<= 1)
 #pragma unroll
-        for (int dd = 0; dd < DPL; ++dd) {
-          const float x = vel(dd, t);
+    for (int h = 0; h < G; ++h)
 #pragma unroll
-          for (int h = 0; h < G; ++h) o[h][dd] = fmaf(pb[h * kPart + t], x, o[h][dd]);
-        }
-      }
-    } else {
+      for (int i = 0; i < NI; ++i) o[h][i] += __shfl_xor(o[h][i], msk, 64);
+
+  __syncthreads();  // all waves are done with the probabilities
+  float(*so)[G][D] = reinterpret_cast<float(*)[G][D]>(smem);
+  if (tg == 0) {
 #pragma unroll
-      for (int t = 0; t < kBlockSize; ++t) {
-        if (t < ntok) {
+    for (int h = 0; h < G; ++h)
 #pragma unroll
-          for (int dd = 0; dd < DPL; ++dd) {
-            const float x = vel(dd, t);
+      for (int i = 0; i < NI; ++i) so[w][h][(i * 64 + lane) / CPR] = o[h][i];
+  }
+  if (lane == 0) {
 #pragma unroll
-            for (int h = 0; h < G; ++h) o[h][dd] = fmaf(pb[h * kPart + t], x, o[h][dd]);
-          }
-        }
-      }
+    for (int h = 0; h < G; ++h) {
+      sml[w][h][0] = mw[h];
+      sml[w][h][1] = lw[h];
     }
   }
-  __syncthreads();  // every wave is done reading sc
-#pragma unroll
-  for (int h = 0; h < G; ++h)
-#pragma unroll
-    for (int dd = 0; dd < DPL; ++dd) red[w][h][lane * DPL + dd] = o[h][dd];
   __syncthreads();
 
+  // ---- merge the waves' partial softmax states ------------------------------
   for (int i = tid; i < G * D; i += kThreads) {
     const int h = i / D, j = i % D;
-    float acc = red[0][h][j];
+    float M = sml[0][h][0];
 #pragma unroll
-    for (int k = 1; k < kWaves; ++k) acc += red[k][h][j];
-    float l = wred[0][h];
+    for (int k = 1; k < kWaves; ++k) M = fmaxf(M, sml[k][h][0]);
+    float acc = 0.f, l = 0.f;
 #pragma unroll
-    for (int k = 1; k < kWaves; ++k) l += wred[k][h];
+    for (int k = 0; k < kWaves; ++k) {
+      const float f = __builtin_amdgcn_exp2f(sml[k][h][0] - M);  // 0 for a wave with no tokens
+      acc = fmaf(f, so[k][h][j], acc);
+      l = fmaf(f, sml[k][h][1], l);
+    }
     const int64_t row = (int64_t)s * Hq + g * G + h;
     if (nparts == 1) {
       store_out<OutCode>(out, row * D + j, acc / l);
     } else {
       ws_o[(row * max_parts + p) * D + j] = acc;
       if (j == 0) {
-        ws_ml[(row * max_parts + p) * 2 + 0] = M[h];
+        ws_ml[(row * max_parts + p) * 2 + 0] = M;
         ws_ml[(row * max_parts + p) * 2 + 1] = l;
       }
     }
@@ -295,35 +324,35 @@ struct DecodeArgs {
 };
 
 template <typename T, int D, int G, int OutCode>
-void launch_decode(const DecodeArgs& a) {
-  hipLaunchKernelGGL((decode_partition_kernel<T, D, G, OutCode>),
-                     dim3((unsigned)a.max_parts, (unsigned)a.Hkv, (unsigned)a.B), dim3(kThreads), 0,
-                     a.stream, a.out, a.ws_o, a.ws_ml, (const typename T::bits*)a.q, a.kpool, a.vpool,
-                     a.tables, a.max_blocks, a.lens, a.Hkv, a.num_blocks, a.max_context_len,
-                     a.scale_log2, a.max_parts);
-  if (a.max_parts > 1) {
+void launch_decode(const DecodeArgs& a, bool partitions, bool reduce) {
+  if (partitions)
+    hipLaunchKernelGGL((decode_partition_kernel<T, D, G, OutCode>),
+                       dim3((unsigned)a.Hkv, (unsigned)a.B, (unsigned)a.max_parts), dim3(kThreads), 0,
+                       a.stream, a.out, a.ws_o, a.ws_ml, (const typename T::bits*)a.q, a.kpool, a.vpool,
+                       a.tables, a.max_blocks, a.lens, a.Hkv, a.num_blocks, a.max_context_len,
+                       a.scale_log2, a.max_parts);
+  if (reduce && a.max_parts > 1)
     hipLaunchKernelGGL((decode_reduce_kernel<D, OutCode>), dim3((unsigned)a.Hq, (unsigned)a.B),
                        dim3(64), 0, a.stream, a.out, a.ws_o, a.ws_ml, a.lens, a.Hq, G,
                        a.max_context_len, a.max_parts);
-  }
 }
 
 template <typename T, int D, int OutCode>
-int dispatch_g(const DecodeArgs& a, int G) {
+int dispatch_g(const DecodeArgs& a, int G, bool pa, bool re) {
   switch (G) {
-    case 1: launch_decode<T, D, 1, OutCode>(a); return 0;
-    case 2: launch_decode<T, D, 2, OutCode>(a); return 0;
-    case 4: launch_decode<T, D, 4, OutCode>(a); return 0;
-    case 8: launch_decode<T, D, 8, OutCode>(a); return 0;
-    case 16: launch_decode<T, D, 16, OutCode>(a); return 0;
+    case 1: launch_decode<T, D, 1, OutCode>(a, pa, re); return 0;
+    case 2: launch_decode<T, D, 2, OutCode>(a, pa, re); return 0;
+    case 4: launch_decode<T, D, 4, OutCode>(a, pa, re); return 0;
+    case 8: launch_decode<T, D, 8, OutCode>(a, pa, re); return 0;
+    case 16: launch_decode<T, D, 16, OutCode>(a, pa, re); return 0;
     default: return -1;
   }
 }
 
 template <typename T, int OutCode>
-int dispatch_d(const DecodeArgs& a, int D, int G) {
-  if (D == 64) return dispatch_g<T, 64, OutCode>(a, G);
-  if (D == 128) return dispatch_g<T, 128, OutCode>(a, G);
+int dispatch_d(const DecodeArgs& a, int D, int G, bool pa, bool re) {
+  if (D == 64) return dispatch_g<T, 64, OutCode>(a, G, pa, re);
+  if (D == 128) return dispatch_g<T, 128, OutCode>(a, G, pa, re);
   return -1;
 }
 
@@ -343,37 +372,38 @@ extern "C" int64_t paged_attention_decode_workspace_bytes(int32_t num_seqs, int3
   return (int64_t)num_seqs * n_q_heads * parts * (head_dim + 2) * (int64_t)sizeof(float);
 }
 
-extern "C" int paged_attention_decode(void* out, int32_t out_dtype, const void* q, const void* k_pool,
-                                      const void* v_pool, const int32_t* block_tables,
-                                      int32_t max_blocks_per_seq, const int32_t* context_lens,
-                                      int32_t num_seqs, int32_t n_q_heads, int32_t n_kv_heads,
-                                      int32_t head_dim, int32_t block_size, int64_t num_blocks,
-                                      int32_t max_context_len, float scale, int32_t kv_dtype,
-                                      void* workspace, int64_t workspace_bytes, void* stream) {
-  if (!pkv::esize_of(kv_dtype)) return fail(PKV_EINVAL, "paged_attention_decode: unknown kv dtype");
+static int decode_impl(const char* fn, bool pa, bool re, void* out, int32_t out_dtype, const void* q,
+                       const void* k_pool, const void* v_pool, const int32_t* block_tables,
+                       int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t num_seqs,
+                       int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim, int32_t block_size,
+                       int64_t num_blocks, int32_t max_context_len, float scale, int32_t kv_dtype,
+                       void* workspace, int64_t workspace_bytes, void* stream) {
+  const std::string F(fn);
+  if (!pkv::esize_of(kv_dtype)) return fail(PKV_EINVAL, F + ": unknown kv dtype");
   if (out_dtype != PKV_F32 && out_dtype != kv_dtype)
-    return fail(PKV_EINVAL, "paged_attention_decode: out dtype must be f32 or the kv dtype");
+    return fail(PKV_EINVAL, F + ": out dtype must be f32 or the kv dtype");
   if (block_size != pkv::kBlockSize) return fail(PKV_EUNSUPPORTED, "block_size must be 16");
   if (head_dim != 64 && head_dim != 128) return fail(PKV_EUNSUPPORTED, "head_dim must be 64 or 128");
-  if (num_seqs < 0 || num_seqs > 65535 || n_kv_heads < 1 || n_q_heads < 1 || n_kv_heads > 65535)
-    return fail(PKV_EINVAL, "paged_attention_decode: bad num_seqs or head counts");
+  if (num_seqs < 0 || num_seqs > 65535 || n_kv_heads < 1 || n_q_heads < 1 || n_kv_heads > 65535 ||
+      (int64_t)max_context_len > 65535ll * pkv::kPart)
+    return fail(PKV_EINVAL, F + ": bad num_seqs or head counts");
   if (n_q_heads % n_kv_heads) return fail(PKV_EINVAL, "n_q_heads must be a multiple of n_kv_heads");
   const int G = n_q_heads / n_kv_heads;
   if (G != 1 && G != 2 && G != 4 && G != 8 && G != 16)
     return fail(PKV_EUNSUPPORTED, "n_q_heads / n_kv_heads must be 1, 2, 4, 8 or 16");
   if (num_blocks < 1 || max_blocks_per_seq < 1 || max_context_len < 0 ||
       (int64_t)max_context_len > (int64_t)max_blocks_per_seq * block_size)
-    return fail(PKV_EINVAL, "paged_attention_decode: max_context_len exceeds the table width");
+    return fail(PKV_EINVAL, F + ": max_context_len exceeds the table width");
   if (num_seqs == 0) return ok();
   if (!out || !q || !k_pool || !v_pool || !block_tables || !context_lens)
-    return fail(PKV_EINVAL, "paged_attention_decode: NULL pointer");
+    return fail(PKV_EINVAL, F + ": NULL pointer");
   if (!pkv::aligned16(q) || !pkv::aligned16(k_pool) || !pkv::aligned16(v_pool) || !pkv::aligned16(out))
-    return fail(PKV_EINVAL, "paged_attention_decode: q, out and pools must be 16-byte aligned");
-  if (!std::isfinite(scale)) return fail(PKV_EINVAL, "paged_attention_decode: scale not finite");
+    return fail(PKV_EINVAL, F + ": q, out and pools must be 16-byte aligned");
+  if (!std::isfinite(scale)) return fail(PKV_EINVAL, F + ": scale not finite");
   const int max_parts = max_context_len > 0 ? (max_context_len + pkv::kPart - 1) / pkv::kPart : 1;
   const int64_t need = paged_attention_decode_workspace_bytes(num_seqs, n_q_heads, head_dim, max_context_len);
   if (need > 0 && (!workspace || workspace_bytes < need || !pkv::aligned16(workspace)))
-    return fail(PKV_EINVAL, "paged_attention_decode: workspace missing or too small (need " +
+    return fail(PKV_EINVAL, F + ": workspace missing or too small (need " +
                                 std::to_string(need) + " bytes)");
   pkv::DecodeArgs a;
   a.out = out;
@@ -395,18 +425,39 @@ extern "C" int paged_attention_decode(void* out, int32_t out_dtype, const void* 
   a.stream = (hipStream_t)stream;
   int rc = -1;
   switch (kv_dtype) {
-    case PKV_F32: rc = pkv::dispatch_d<pkv::F32, PKV_F32>(a, head_dim, G); break;
+    case PKV_F32: rc = pkv::dispatch_d<pkv::F32, PKV_F32>(a, head_dim, G, pa, re); break;
     case PKV_F16:
-      rc = out_dtype == PKV_F32 ? pkv::dispatch_d<pkv::F16, PKV_F32>(a, head_dim, G)
-                                : pkv::dispatch_d<pkv::F16, PKV_F16>(a, head_dim, G);
+      rc = out_dtype == PKV_F32 ? pkv::dispatch_d<pkv::F16, PKV_F32>(a, head_dim, G, pa, re)
+                                : pkv::dispatch_d<pkv::F16, PKV_F16>(a, head_dim, G, pa, re);
       break;
     case PKV_BF16:
-      rc = out_dtype == PKV_F32 ? pkv::dispatch_d<pkv::BF16, PKV_F32>(a, head_dim, G)
-                                : pkv::dispatch_d<pkv::BF16, PKV_BF16>(a, head_dim, G);
+      rc = out_dtype == PKV_F32 ? pkv::dispatch_d<pkv::BF16, PKV_F32>(a, head_dim, G, pa, re)
+                                : pkv::dispatch_d<pkv::BF16, PKV_BF16>(a, head_dim, G, pa, re);
       break;
   }
-  if (rc) return fail(PKV_EUNSUPPORTED, "paged_attention_decode: configuration not built");
+  if (rc) return fail(PKV_EUNSUPPORTED, F + ": configuration not built");
   const hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return fail(PKV_EHIP, std::string("paged_attention_decode: ") + hipGetErrorString(e));
+  if (e != hipSuccess) return fail(PKV_EHIP, std::string(F + ": ") + hipGetErrorString(e));
   return ok();
+}
+
+#define PKV_DECODE_PARAMS                                                                          \
+  void *out, int32_t out_dtype, const void *q, const void *k_pool, const void *v_pool,             \
+      const int32_t *block_tables, int32_t max_blocks_per_seq, const int32_t *context_lens,        \
+      int32_t num_seqs, int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,                   \
+      int32_t block_size, int64_t num_blocks, int32_t max_context_len, float scale,                \
+      int32_t kv_dtype, void *workspace, int64_t workspace_bytes, void *stream
+#define PKV_DECODE_ARGS                                                                            \
+  out, out_dtype, q, k_pool, v_pool, block_tables, max_blocks_per_seq, context_lens, num_seqs,     \
+      n_q_heads, n_kv_heads, head_dim, block_size, num_blocks, max_context_len, scale, kv_dtype,   \
+      workspace, workspace_bytes, stream
+
+extern "C" int paged_attention_decode(PKV_DECODE_PARAMS) {
+  return decode_impl("paged_attention_decode", true, true, PKV_DECODE_ARGS);
+}
+extern "C" int paged_attention_decode_partitions(PKV_DECODE_PARAMS) {
+  return decode_impl("paged_attention_decode_partitions", true, false, PKV_DECODE_ARGS);
+}
+extern "C" int paged_attention_decode_reduce(PKV_DECODE_PARAMS) {
+  return decode_impl("paged_attention_decode_reduce", false, true, PKV_DECODE_ARGS);
 }

@@ -1,11 +1,421 @@
-// Chunked-prefill attention (MFMA).  Placeholder entry point until the kernel
-// lands: validates nothing and reports the configuration as not built.
+// Chunked-prefill attention over the paged KV cache, on MFMA (gfx950).
+//
+// What is computed: chunk c holds q_len query tokens of one sequence whose
+// keys/values (the cached context plus the chunk itself, appended before the
+// call) number L.  Query i sits at absolute position p = L - q_len + i and
+// attends causally to keys 0..p:  out = softmax(scale * q K^T) V  row by row
+// ("The detour, what really happens inside one forward pass", Life of a
+// prompt, for the Q K^T -> softmax -> V contraction; "Chunked prefill" in The
+// hands-on guide to LLM Inference with vLLM: each chunk's attention reads the
+// KV cache of every chunk before it).  Keys and values are gathered block by
+// block through the chunk's block table ("How the attention kernel actually
+// reads paged blocks", vLLM Serving deep dive).
+//
+// How (gfx950, MFMA 16x16x32):
+//  * Workgroup = 4 wave64s over (KV head, 64 query tokens, chunk) for a GQA
+//    group of 4 query heads (or 128/256 tokens when fewer heads share a KV
+//    head).  Each wave owns 4 row tiles of 16 query rows (token tile x head):
+//    the heads of one KV head are stacked so every K/V tile staged in LDS
+//    serves all of them.
+//  * Keys advance 64 at a time (4 blocks).  The workgroup stages the step's
+//    K and V tiles in LDS (double buffered; the next step's global loads are
+//    issued before the current step's math).  K tiles keep the pool layout;
+//    V tiles are stored as fp16 (exact for bf16 values in fp16's normal
+//    range) because the P.V product runs in fp16 (see below).
+//  * Scores are formed transposed, S^T = K Q^T (A = K tile from LDS, B = the
+//    wave's Q rows kept in registers), so each lane owns one query row: the
+//    online softmax (base 2, running max and sum per row) needs only two
+//    cross-lane steps per tile for the max, and the probabilities feed the
+//    next product straight from the lane's registers.
+//  * O^T += V^T P^T with A = V^T (16 dims x 32 keys) and B = P^T.  The key
+//    order inside the 32-wide contraction is permuted identically in both
+//    operands (each lane holds keys 4q..4q+3 of two 16-key tiles), which
+//    matches the score tiles' register layout, so no shuffles are needed.
+//    P is rounded to fp16 (u = 2^-11) rather than bf16 (u = 2^-8): the
+//    latter's error on short causal rows comes close to the 2e-3 tolerance.
+//  * The causal mask is applied only on steps that reach the diagonal; keys
+//    past the context are masked and their V entries zeroed when staged.
+#include <math.h>
+
+#include <cmath>
+#include <string>
+
 #include "pkv_device.h"
 #include "pkv_internal.h"
 
-extern "C" int paged_attention_prefill_chunk(void*, int32_t, const void*, const void*, const void*,
-                                             const int32_t*, int32_t, const int32_t*, const int32_t*,
-                                             int32_t, int32_t, int32_t, int32_t, int32_t, int32_t,
-                                             int32_t, int64_t, int32_t, float, int32_t, void*) {
-  return pkv::fail(PKV_EUNSUPPORTED, "paged_attention_prefill_chunk: not built yet");
+namespace pkv {
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kPfThreads = 256;
+constexpr int kStepKeys = 64;  // keys per step: 4 blocks of 16
+
+template <typename T>
+__device__ __forceinline__ f32x4 mfma_qk(u32x4 a, u32x4 b, f32x4 c) {
+  if constexpr (T::kCode == PKV_BF16)
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a),
+                                                  __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4 mfma_pv(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a),
+                                                __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+  const uint16_t a = __builtin_bit_cast(uint16_t, (_Float16)lo);
+  const uint16_t b = __builtin_bit_cast(uint16_t, (_Float16)hi);
+  return (uint32_t)a | ((uint32_t)b << 16);
+}
+
+// One 16-byte chunk of a V tile (8 consecutive keys of one dim) -> fp16 bits,
+// keys at or past `valid` zeroed.
+template <typename T>
+__device__ __forceinline__ u32x4 v_chunk_to_f16(u32x4 v, int valid) {
+  u32x4 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float lo, hi;
+    if constexpr (T::kCode == PKV_BF16) {
+      lo = bf16lo(v[i]);
+      hi = bf16hi(v[i]);
+      lo = fminf(fmaxf(lo, -65504.f), 65504.f);  // saturate into fp16 range
+      hi = fminf(fmaxf(hi, -65504.f), 65504.f);
+    } else {
+      lo = f16lo(v[i]);
+      hi = f16hi(v[i]);
+    }
+    lo = 2 * i < valid ? lo : 0.f;
+    hi = 2 * i + 1 < valid ? hi : 0.f;
+    r[i] = pack_f16x2(lo, hi);
+  }
+  return r;
+}
+
+template <typename T, int D, int GW, int OutCode>
+__global__ void __launch_bounds__(kPfThreads, 1)
+prefill_chunk_kernel(void* __restrict__ out, const uint16_t* __restrict__ q,
+                     const unsigned char* __restrict__ kpool, const unsigned char* __restrict__ vpool,
+                     const int32_t* __restrict__ tables, int max_blocks, const int32_t* __restrict__ cu_q,
+                     const int32_t* __restrict__ lens, int total_q, int Hkv, int G, int64_t num_blocks,
+                     int max_context_len, float scale_log2) {
+  constexpr int TT = 4 / GW;               // 16-token tiles per wave
+  constexpr int RT = TT * GW;              // row tiles per wave (= 4)
+  constexpr int TW = 16 * TT;              // query tokens per wave
+  constexpr int TWG = 4 * TW;              // query tokens per workgroup
+  constexpr int DC = D / 32;               // 32-dim slices of the score contraction
+  constexpr int DT = D / 16;               // 16-dim tiles of the output
+  constexpr int TILE = D * kBlockSize * 2; // bytes of one (block, head) tile
+  constexpr int CPT = TILE / 16;           // 16-byte chunks per tile
+  constexpr int NCH = 4 * CPT / kPfThreads;  // staging chunks per thread per step (K and V each)
+
+  __shared__ __attribute__((aligned(16))) unsigned char lds[2][2][4 * TILE];  // [buffer][K, V]
+
+  const int c = blockIdx.z;
+  const int qs = cu_q[c];
+  int qlen = cu_q[c + 1] - qs;
+  int L = lens[c];
+  L = L < 0 ? 0 : (L > max_context_len ? max_context_len : L);
+  qlen = qlen < 0 ? 0 : (qlen > L ? L : qlen);
+  const int ctx = L - qlen;
+  const int tile0 = blockIdx.y * TWG;
+  if (tile0 >= qlen) return;
+
+  const int hgroups = G / GW;
+  const int g = blockIdx.x / hgroups;
+  const int h0 = g * G + (blockIdx.x % hgroups) * GW;  // first query head of this workgroup
+  const int Hq = Hkv * G;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int q4 = lane >> 4, r16 = lane & 15;
+
+  const int i0 = tile0 + w * TW;                   // wave's first query token (chunk-local)
+  const int wg_end = qlen < tile0 + TWG ? qlen : tile0 + TWG;
+  const int nsteps = (ctx + wg_end + kStepKeys - 1) / kStepKeys;
+  const bool active = i0 < qlen;
+  const int wave_end = qlen < i0 + TW ? qlen : i0 + TW;
+  const int kmax_w = ctx + wave_end;                // keys this wave needs: [0, kmax_w)
+  const int32_t* tab = tables + (int64_t)c * max_blocks;
+  const int nblk = (L + kBlockSize - 1) / kBlockSize;
+
+  // ---- the wave's query rows as B operands of S^T = K Q^T -------------------
+  u32x4 bq[RT][DC];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    const int tt = rt / GW, hh = rt % GW;
+    int tok = i0 + 16 * tt + r16;
+    tok = tok < qlen ? tok : qlen - 1;
+    int row = qs + tok;
+    row = row < 0 ? 0 : (row >= total_q ? total_q - 1 : row);
+    const uint16_t* qp = q + ((int64_t)row * Hq + h0 + hh) * D + 8 * q4;
+#pragma unroll
+    for (int dc = 0; dc < DC; ++dc) bq[rt][dc] = active ? ld16(qp + 32 * dc) : u32x4{0, 0, 0, 0};
+  }
+
+  f32x4 o[RT][DT];
+  float m[RT], l[RT];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    m[rt] = -INFINITY;
+    l[rt] = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) o[rt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  // ---- staging of one step's K/V tiles (4 blocks) --------------------------
+  u32x4 kst[NCH], vst[NCH];
+  auto load_step = [&](int s) {
+#pragma unroll
+    for (int k = 0; k < NCH; ++k) {
+      const int ci = tid + kPfThreads * k;
+      const int bi = ci / CPT, off = (ci % CPT) * 16;
+      const int lb = 4 * s + bi;  // logical block
+      if (lb < nblk) {
+        const int64_t blk = clamp_block(tab[lb], num_blocks);
+        const int64_t base = (blk * Hkv + g) * (int64_t)TILE + off;
+        kst[k] = ld16(kpool + base);
+        // V chunk: one dim, keys (off % 32) / 2 .. +8 of the block
+        const int valid = L - (lb * kBlockSize + (off % 32) / 2);
+        vst[k] = v_chunk_to_f16<T>(ld16(vpool + base), valid);
+      } else {
+        kst[k] = u32x4{0, 0, 0, 0};
+        vst[k] = u32x4{0, 0, 0, 0};
+      }
+    }
+  };
+  auto store_step = [&](int buf) {
+#pragma unroll
+    for (int k = 0; k < NCH; ++k) {
+      const int ci = tid + kPfThreads * k;
+      st16(&lds[buf][0][ci * 16], kst[k]);
+      st16(&lds[buf][1][ci * 16], vst[k]);
+    }
+  };
+
+  load_step(0);
+  store_step(0);
+  __syncthreads();
+
+#pragma unroll 1
+  for (int s = 0; s < nsteps; ++s) {
+    const int buf = s & 1;
+    if (s + 1 < nsteps) load_step(s + 1);
+    if (active && kStepKeys * s < kmax_w) {
+      const unsigned char* kl = lds[buf][0];
+      const unsigned char* vl = lds[buf][1];
+      // S^T tiles: st[rt][kt] holds keys 16kt + 4q4 + r of row r16
+      f32x4 st[RT][4];
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) {
+        u32x4 ka[DC];
+#pragma unroll
+        for (int dc = 0; dc < DC; ++dc)
+          ka[dc] = *reinterpret_cast<const u32x4*>(kl + kt * TILE + ((4 * dc + q4) * kBlockSize + r16) * 16);
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int dc = 0; dc < DC; ++dc) acc = mfma_qk<T>(ka[dc], bq[rt][dc], acc);
+          st[rt][kt] = acc;
+        }
+      }
+      // online softmax, one row per lane
+      const bool diag = kStepKeys * s + kStepKeys - 1 > ctx + i0;
+      u32x4 pb[RT][2];
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+        const int pos = ctx + i0 + 16 * (rt / GW) + r16;
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            float v = st[rt][kt][r] * scale_log2;
+            if (diag) {
+              const int key = kStepKeys * s + 16 * kt + 4 * q4 + r;
+              v = key <= pos ? v : -INFINITY;
+            }
+            st[rt][kt][r] = v;
+            mx = fmaxf(mx, v);
+          }
+        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        const float mn = fmaxf(m[rt], mx);
+        const float alpha = __builtin_amdgcn_exp2f(m[rt] - mn);
+        m[rt] = mn;
+        float ls = 0.f;
+        float e[4][4];
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            e[kt][r] = __builtin_amdgcn_exp2f(st[rt][kt][r] - mn);
+            ls += e[kt][r];
+          }
+        l[rt] = fmaf(l[rt], alpha, ls);
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) o[rt][dt] *= alpha;
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh) {
+          pb[rt][kh][0] = pack_f16x2(e[2 * kh][0], e[2 * kh][1]);
+          pb[rt][kh][1] = pack_f16x2(e[2 * kh][2], e[2 * kh][3]);
+          pb[rt][kh][2] = pack_f16x2(e[2 * kh + 1][0], e[2 * kh + 1][1]);
+          pb[rt][kh][3] = pack_f16x2(e[2 * kh + 1][2], e[2 * kh + 1][3]);
+        }
+      }
+      // O^T += V^T P^T
+#pragma unroll
+      for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          const int dim = 16 * dt + r16;
+          const u32x2 a0 = *reinterpret_cast<const u32x2*>(vl + (2 * kh) * TILE + dim * 32 + 8 * q4);
+          const u32x2 a1 = *reinterpret_cast<const u32x2*>(vl + (2 * kh + 1) * TILE + dim * 32 + 8 * q4);
+          const u32x4 va = {a0[0], a0[1], a1[0], a1[1]};
+#pragma unroll
+          for (int rt = 0; rt < RT; ++rt) o[rt][dt] = mfma_pv(va, pb[rt][kh], o[rt][dt]);
+        }
+    }
+    if (s + 1 < nsteps) store_step(buf ^ 1);
+    __syncthreads();
+  }
+
+  // ---- normalise and write the wave's rows ---------------------------------
+  if (!active) return;
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    float lt = l[rt];
+    lt += __shfl_xor(lt, 16, 64);
+    lt += __shfl_xor(lt, 32, 64);
+    const float inv = 1.f / lt;
+    const int tok = i0 + 16 * (rt / GW) + r16;
+    if (tok < qlen && qs + tok < total_q) {
+      const int64_t rowbase = ((int64_t)(qs + tok) * Hq + h0 + rt % GW) * D;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) store_out<OutCode>(out, rowbase + 16 * dt + 4 * q4 + r, o[rt][dt][r] * inv);
+    }
+  }
+}
+
+struct PrefillArgs {
+  void* out;
+  const uint16_t* q;
+  const unsigned char* kpool;
+  const unsigned char* vpool;
+  const int32_t* tables;
+  int max_blocks;
+  const int32_t* cu_q;
+  const int32_t* lens;
+  int n_chunks, total_q, max_q_len, Hkv, G;
+  int64_t num_blocks;
+  int max_context_len;
+  float scale_log2;
+  hipStream_t stream;
+};
+
+template <typename T, int D, int GW, int OutCode>
+void launch_prefill(const PrefillArgs& a) {
+  constexpr int TWG = 4 * 16 * (4 / GW);
+  const unsigned gy = (unsigned)((a.max_q_len + TWG - 1) / TWG);
+  hipLaunchKernelGGL((prefill_chunk_kernel<T, D, GW, OutCode>),
+                     dim3((unsigned)(a.Hkv * (a.G / GW)), gy, (unsigned)a.n_chunks), dim3(kPfThreads), 0,
+                     a.stream, a.out, a.q, a.kpool, a.vpool, a.tables, a.max_blocks, a.cu_q, a.lens, a.total_q,
+                     a.Hkv, a.G, a.num_blocks, a.max_context_len, a.scale_log2);
+}
+
+template <typename T, int D, int OutCode>
+int prefill_dispatch_g(const PrefillArgs& a) {
+  switch (a.G) {
+    case 1: launch_prefill<T, D, 1, OutCode>(a); return 0;
+    case 2: launch_prefill<T, D, 2, OutCode>(a); return 0;
+    case 4:
+    case 8:
+    case 16: launch_prefill<T, D, 4, OutCode>(a); return 0;
+    default: return -1;
+  }
+}
+
+template <typename T, int OutCode>
+int prefill_dispatch_d(const PrefillArgs& a, int D) {
+  if (D == 64) return prefill_dispatch_g<T, 64, OutCode>(a);
+  if (D == 128) return prefill_dispatch_g<T, 128, OutCode>(a);
+  return -1;
+}
+
+}  // namespace
+}  // namespace pkv
+
+using pkv::fail;
+using pkv::ok;
+
+extern "C" int paged_attention_prefill_chunk(void* out, int32_t out_dtype, const void* q, const void* k_pool,
+                                             const void* v_pool, const int32_t* block_tables,
+                                             int32_t max_blocks_per_seq, const int32_t* cu_q_lens,
+                                             const int32_t* context_lens, int32_t n_chunks, int32_t total_q,
+                                             int32_t max_q_len, int32_t n_q_heads, int32_t n_kv_heads,
+                                             int32_t head_dim, int32_t block_size, int64_t num_blocks,
+                                             int32_t max_context_len, float scale, int32_t kv_dtype,
+                                             void* stream) {
+  const std::string F("paged_attention_prefill_chunk");
+  if (kv_dtype != PKV_F16 && kv_dtype != PKV_BF16)
+    return fail(kv_dtype == PKV_F32 ? PKV_EUNSUPPORTED : PKV_EINVAL, F + ": kv dtype must be f16 or bf16");
+  if (out_dtype != PKV_F32 && out_dtype != kv_dtype)
+    return fail(PKV_EINVAL, F + ": out dtype must be f32 or the kv dtype");
+  if (block_size != pkv::kBlockSize) return fail(PKV_EUNSUPPORTED, "block_size must be 16");
+  if (head_dim != 64 && head_dim != 128) return fail(PKV_EUNSUPPORTED, "head_dim must be 64 or 128");
+  if (n_kv_heads < 1 || n_q_heads < 1 || n_q_heads % n_kv_heads)
+    return fail(PKV_EINVAL, F + ": n_q_heads must be a positive multiple of n_kv_heads");
+  const int G = n_q_heads / n_kv_heads;
+  if (G != 1 && G != 2 && G != 4 && G != 8 && G != 16)
+    return fail(PKV_EUNSUPPORTED, F + ": n_q_heads / n_kv_heads must be 1, 2, 4, 8 or 16");
+  if (n_chunks < 0 || n_chunks > 65535 || total_q < 0 || max_q_len < 0)
+    return fail(PKV_EINVAL, F + ": bad n_chunks, total_q or max_q_len");
+  if (num_blocks < 1 || max_blocks_per_seq < 1 || max_context_len < 0 ||
+      (int64_t)max_context_len > (int64_t)max_blocks_per_seq * block_size)
+    return fail(PKV_EINVAL, F + ": max_context_len exceeds the table width");
+  if ((int64_t)n_kv_heads * (G >= 4 ? G / 4 : 1) > 65535 || max_q_len / 64 > 65535)
+    return fail(PKV_EINVAL, F + ": grid too large");
+  if (n_chunks == 0 || total_q == 0 || max_q_len == 0) return ok();
+  if (!out || !q || !k_pool || !v_pool || !block_tables || !cu_q_lens || !context_lens)
+    return fail(PKV_EINVAL, F + ": NULL pointer");
+  if (!pkv::aligned16(q) || !pkv::aligned16(k_pool) || !pkv::aligned16(v_pool))
+    return fail(PKV_EINVAL, F + ": q and pools must be 16-byte aligned");
+  if (!std::isfinite(scale)) return fail(PKV_EINVAL, F + ": scale not finite");
+  pkv::PrefillArgs a;
+  a.out = out;
+  a.q = (const uint16_t*)q;
+  a.kpool = (const unsigned char*)k_pool;
+  a.vpool = (const unsigned char*)v_pool;
+  a.tables = block_tables;
+  a.max_blocks = max_blocks_per_seq;
+  a.cu_q = cu_q_lens;
+  a.lens = context_lens;
+  a.n_chunks = n_chunks;
+  a.total_q = total_q;
+  a.max_q_len = max_q_len;
+  a.Hkv = n_kv_heads;
+  a.G = G;
+  a.num_blocks = num_blocks;
+  a.max_context_len = max_context_len;
+  a.scale_log2 = (float)((double)scale * 1.4426950408889634);
+  a.stream = (hipStream_t)stream;
+  int rc;
+  if (kv_dtype == PKV_BF16)
+    rc = out_dtype == PKV_F32 ? pkv::prefill_dispatch_d<pkv::BF16, PKV_F32>(a, head_dim)
+                              : pkv::prefill_dispatch_d<pkv::BF16, PKV_BF16>(a, head_dim);
+  else
+    rc = out_dtype == PKV_F32 ? pkv::prefill_dispatch_d<pkv::F16, PKV_F32>(a, head_dim)
+                              : pkv::prefill_dispatch_d<pkv::F16, PKV_F16>(a, head_dim);
+  if (rc) return fail(PKV_EUNSUPPORTED, F + ": configuration not built");
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(PKV_EHIP, F + ": " + hipGetErrorString(e));
+  return ok();
 }

@@ -49,11 +49,14 @@ def decode_reference(w, s):
     return out[0]
 
 
-def prefill_reference(w, c, n_threads=8):
-    """Oracle output [q_len, Hq, d] for prefill chunk c of workload w."""
+def prefill_reference(w, c, rows=None, n_threads=8):
+    """Oracle output [len(rows), Hq, d] for prefill chunk c of workload w
+    (rows: chunk-local query indices, default all)."""
     ctx, ql = int(w.chunk_ctx[c]), int(w.chunk_qlen[c])
-    k, v = w.kv("chunk", c, 0, ctx + ql)
-    q = w.q("chunk", c, ctx, ctx + ql)
-    out, _ = oracle.attention(oracle.decode(w.dtype, q), np.arange(ctx, ctx + ql), oracle.decode(w.dtype, k),
+    rows = np.arange(ql) if rows is None else np.asarray(rows)
+    last = int(rows.max()) + 1
+    k, v = w.kv("chunk", c, 0, ctx + last)
+    qb = w.q("chunk", c, ctx, ctx + ql)[rows]
+    out, _ = oracle.attention(oracle.decode(w.dtype, qb), ctx + rows, oracle.decode(w.dtype, k),
                               oracle.decode(w.dtype, v), w.scale, n_threads=n_threads)
     return out
