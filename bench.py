@@ -25,7 +25,8 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-HBM_PEAK_GBS = 8000.0  # MI355X HBM3E
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16/fp16 MFMA
 
 
 def log(*a):
@@ -65,6 +66,94 @@ def decode_bytes(b):
         "logical_kv_bytes": logical_tokens * unit * w.n_kv_heads,
         "other_bytes": extra,
         "algorithmic_bytes": unique_tokens * unit * w.n_kv_heads + extra,
+    }
+
+
+def profiled_traffic(profile, sources):
+    """HBM bytes per launch measured with rocprofv3 FETCH_SIZE + WRITE_SIZE
+    (scaled by a plain-copy calibration) and recorded in profiles/<profile>.md,
+    or None when the kernel sources changed since those counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", profile + ".md")
+    if not os.path.exists(path):
+        return None
+    rec = {}
+    for line in open(path):
+        if ":" in line and line.split(":")[0] in ("traffic_bytes_per_launch", "kernel_sources_sha256_16"):
+            k, v = line.split(":", 1)
+            rec[k.strip()] = v.strip()
+    m = hashlib.sha256()
+    for src in sources:
+        m.update(open(os.path.join(ROOT, "paged_kv_cache_gather_amd", "csrc", src), "rb").read())
+    if rec.get("kernel_sources_sha256_16") != m.hexdigest()[:16] or "traffic_bytes_per_launch" not in rec:
+        return None
+    return int(rec["traffic_bytes_per_launch"])
+
+
+def prefill_flops(w):
+    """Algorithmic FLOPs of one prefill launch: 4 * d * Hq per unmasked
+    (query, key) pair (two multiply-adds per dim, for Q K^T and for P V);
+    query i of a chunk with c cached tokens sees c + i + 1 keys."""
+    import numpy as np
+    pairs = 0
+    for c, ql in zip(w.chunk_ctx.astype(np.int64), w.chunk_qlen.astype(np.int64)):
+        pairs += int(ql * c + ql * (ql + 1) // 2)
+    return 4 * w.head_dim * w.n_q_heads * pairs, pairs
+
+
+def mixed_step(steps, warmup, seed):
+    """The mixed chunked-prefill + decode step (16 chunks of 512 queries and
+    240 decodes): append both, then prefill attention and decode attention."""
+    import numpy as np
+    import torch
+    import synth
+    from paged_kv_cache_gather_amd.batch import DeviceBatch
+    w = synth.make_workload(5, seed=seed)
+    log(f"building {w.name}: {w.description}")
+    b = DeviceBatch(w, "cuda:0", fill="device")
+    outp, outd = b.new_prefill_out(), b.new_decode_out()
+    st = torch.cuda.current_stream()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
+
+    def step(e=None):
+        rec = (lambda i: e[i].record(st)) if e is not None else (lambda i: None)
+        rec(0)
+        b.append_prefill()
+        b.append_decode()
+        rec(1)
+        b.attend_prefill(outp)
+        rec(2)
+        b.attend_decode_split(outd, between=lambda: rec(3))
+        rec(4)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(ev[i])
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    pre = np.array([e[1].elapsed_time(e[2]) for e in ev])
+    dpart = np.array([e[2].elapsed_time(e[3]) for e in ev])
+    flops, pairs = prefill_flops(w)
+    by = decode_bytes(b)
+    tf = flops / (pre.mean() * 1e-3) / 1e12
+    toks = int(w.chunk_qlen.sum()) + w.n_decode
+    log(f"mixed step {ms * 1e3:.1f} us | prefill {pre.mean() * 1e3:.1f} us = {tf:.0f} TFLOP/s "
+        f"({tf / MFMA_BF16_PEAK_TFLOPS:.1%} of MFMA peak) | decode partitions {dpart.mean() * 1e3:.1f} us = "
+        f"{by['algorithmic_bytes'] / (dpart.mean() * 1e-3) / 1e9:.0f} GB/s")
+    return {
+        "workload": w.name, "description": w.description, "ms_per_step": ms,
+        "tokens_per_step": toks, "tokens_per_s": toks / (ms * 1e-3),
+        "prefill": {"kernel": "prefill_chunk_kernel", "bound": "mfma", "us": float(pre.mean()) * 1e3,
+                    "algorithmic_flops": flops, "causal_pairs": pairs, "achieved": tf,
+                    "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": tf / MFMA_BF16_PEAK_TFLOPS},
+        "decode": {"kernel": "decode_partition_kernel", "bound": "hbm", "us": float(dpart.mean()) * 1e3,
+                   "algorithmic_bytes": by["algorithmic_bytes"],
+                   "achieved": by["algorithmic_bytes"] / (dpart.mean() * 1e-3) / 1e9, "peak": HBM_PEAK_GBS,
+                   "unit": "GB/s",
+                   "frac": by["algorithmic_bytes"] / (dpart.mean() * 1e-3) / 1e9 / HBM_PEAK_GBS},
     }
 
 
@@ -131,6 +220,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=64)
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--no-mixed", action="store_true", help="skip the mixed prefill+decode step")
+    ap.add_argument("--only-mixed", action="store_true", help="run only the mixed prefill+decode step")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -147,6 +238,10 @@ def main():
 
     if args.copy_calibration:
         copy_calibration()
+        return
+
+    if args.only_mixed:
+        print(json.dumps(mixed_step(args.steps, args.warmup, args.seed)), flush=True)
         return
 
     w = synth.make_workload(args.workload, seed=args.seed)
@@ -212,7 +307,10 @@ def main():
                    "out_dtype": str(b.out_dtype).replace("torch.", ""), "seed": args.seed,
                    "step": "reshape_and_cache + decode partition pass + split-K reduce"},
         "roofline": {"bound": "hbm", "kernel": "decode_partition_kernel", "achieved": achieved,
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": None},
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": (profiled_traffic("decode_partition_llama3_8b_decode", ["decode.hip", "pkv_device.h"])
+                                 if w.name == "llama3_8b_decode" and args.seed == 0 else None),
+                     "algorithmic_bytes": by["algorithmic_bytes"]},
         "breakdown_us": {"append": float(append_ms.mean()) * 1e3, "partitions": float(part_ms.mean()) * 1e3,
                          "reduce": float(reduce_ms.mean()) * 1e3,
                          "host_allocator_step": host_allocator_us(b)},
@@ -221,6 +319,10 @@ def main():
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, args.cpu_sample)
+    if not args.no_mixed:
+        del b
+        torch.cuda.empty_cache()
+        res["mixed_step"] = mixed_step(max(5, K // 2), max(2, W // 2), args.seed)
     print(json.dumps(res), flush=True)
 
 
