@@ -53,21 +53,28 @@ namespace {
 #ifndef PKV_DECODE_MIN_WAVES
 #define PKV_DECODE_MIN_WAVES 2
 #endif
-#ifndef PKV_DECODE_V_UNROLL
-#define PKV_DECODE_V_UNROLL 2
+#ifndef PKV_DECODE_V_BATCH
+#define PKV_DECODE_V_BATCH 1
 #endif
 constexpr int kPart = PKV_DECODE_PART;  // context tokens per partition
-constexpr int kVUnroll = PKV_DECODE_V_UNROLL;
+constexpr int kVBatch = PKV_DECODE_V_BATCH;  // V blocks loaded together per wave
 constexpr int kThreads = 256;           // threads per workgroup
 constexpr int kWaves = kThreads / 64;
 
+__device__ __forceinline__ int clamp_len(int L, int max_context_len) {
+  return L < 0 ? 0 : (L > max_context_len ? max_context_len : L);
+}
+
+// The partition pass of sequence s, KV head g, partition p (n tokens): the G
+// query heads of the KV head are the workgroup's R = G rows.
 template <typename T, int D, int G, int OutCode>
-__global__ void __launch_bounds__(kThreads, PKV_DECODE_MIN_WAVES)
-decode_partition_kernel(void* __restrict__ out, float* __restrict__ ws_o, float* __restrict__ ws_ml,
-                        const typename T::bits* __restrict__ q, const unsigned char* __restrict__ kpool,
-                        const unsigned char* __restrict__ vpool, const int32_t* __restrict__ tables,
-                        int max_blocks, const int32_t* __restrict__ lens, int Hkv, int64_t num_blocks,
-                        int max_context_len, float scale_log2, int max_parts) {
+__device__ __forceinline__ void partition_rows(
+    float* __restrict__ smem, float (*__restrict__ sml)[2], void* __restrict__ out, float* __restrict__ ws_o,
+    float* __restrict__ ws_ml, const typename T::bits* __restrict__ q, const unsigned char* __restrict__ kpool,
+    const unsigned char* __restrict__ vpool, const int32_t* __restrict__ tab, const int32_t* __restrict__ lens,
+    int s, int g, int p, int n, int Hkv, int64_t num_blocks, int max_context_len, float scale_log2,
+    int max_parts) {
+  constexpr int R = G;                       // query rows served
   constexpr int ES = T::kBytes;
   constexpr int X = 16 / ES;                 // elements per 16-byte chunk
   constexpr int C = D / X;                   // chunks per K row
@@ -78,97 +85,74 @@ decode_partition_kernel(void* __restrict__ out, float* __restrict__ ws_o, float*
   constexpr int NI = D * ES / 64;            // V chunks per lane per block (= dims per lane)
   constexpr int VTILE = D * kBlockSize * ES; // bytes of one (block, head) V tile
 
-  // Per-wave probabilities [kWaves][TPW][G]; after the V pass the same memory
-  // holds the waves' partial outputs [kWaves][G][D].
-  constexpr int SMEM = (kPart > kWaves * D ? kPart : kWaves * D) * G;
-  __shared__ __attribute__((aligned(16))) float smem[SMEM];
-  __shared__ float sml[kWaves][G][2];
-
-  const int g = blockIdx.x, s = blockIdx.y, p = blockIdx.z;
   const int Hq = Hkv * G;
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform per wave
-
-  int L = lens[s];
-  L = L < 0 ? 0 : (L > max_context_len ? max_context_len : L);
-  const int nparts = (L + kPart - 1) / kPart;
-  if (p >= (nparts > 0 ? nparts : 1)) return;
-  if (L == 0) {  // defined result for an empty context: zeros
-    for (int i = tid; i < G * D; i += kThreads)
-      store_out<OutCode>(out, ((int64_t)s * Hq + g * G) * D + i, 0.f);
-    return;
-  }
-  const int t0 = p * kPart;
-  const int n = (L - t0) < kPart ? (L - t0) : kPart;  // tokens in this partition
-  const int wt0 = w * TPW;                               // wave's first token (partition-local)
+  const int wt0 = w * TPW;                                  // wave's first token (partition-local)
   const int wn = n - wt0 < 0 ? 0 : (n - wt0 > TPW ? TPW : n - wt0);
-  const int32_t* tab = tables + (int64_t)s * max_blocks + t0 / kBlockSize;
-  float(*sp)[G] = reinterpret_cast<float(*)[G]>(smem) + w * TPW;
+  float(*sp)[R] = reinterpret_cast<float(*)[R]>(smem) + w * TPW;
 
-  // ---- scores: one token per lane, G heads, whole K row --------------------
-  float sreg[IT][G];
-  const typename T::bits* qg = q + ((int64_t)s * Hq + g * G) * D;
+  // ---- scores: one token per lane, R rows, whole K row ---------------------
+  float sreg[IT][R];
 #pragma unroll
   for (int it = 0; it < IT; ++it) {
     const int tl = wt0 + it * 64 + lane;
-    float acc[G];
+    float acc[R];
 #pragma unroll
-    for (int h = 0; h < G; ++h) acc[h] = 0.f;
+    for (int r = 0; r < R; ++r) acc[r] = 0.f;
     if (it * 64 < wn && tl < n) {
       const int64_t blk = clamp_block(tab[tl >> 4], num_blocks);
       const unsigned char* kp = kpool + (((blk * Hkv + g) * C) * kBlockSize + (tl & 15)) * 16;
       u32x4 kc[C];
 #pragma unroll
       for (int c = 0; c < C; ++c) kc[c] = ld16(kp + c * (kBlockSize * 16));
-      if constexpr (ES == 2) {
-        const uint32_t* qw = reinterpret_cast<const uint32_t*>(qg);
 #pragma unroll
-        for (int c = 0; c < C; ++c)
+      for (int r = 0; r < R; ++r) {
+        const typename T::bits* qr = q + ((int64_t)s * Hq + g * G + r) * D;
+        if constexpr (ES == 2) {
+          const uint32_t* qw = reinterpret_cast<const uint32_t*>(qr);
 #pragma unroll
-          for (int h = 0; h < G; ++h)
+          for (int c = 0; c < C; ++c)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) acc[h] = dot2<T>(qw[h * (D / 2) + c * 4 + e], kc[c][e], acc[h]);
-      } else {
-        const float* qf = reinterpret_cast<const float*>(qg);
+            for (int e = 0; e < 4; ++e) acc[r] = dot2<T>(qw[c * 4 + e], kc[c][e], acc[r]);
+        } else {
+          const float* qf = reinterpret_cast<const float*>(qr);
 #pragma unroll
-        for (int c = 0; c < C; ++c)
+          for (int c = 0; c < C; ++c)
 #pragma unroll
-          for (int h = 0; h < G; ++h)
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-              acc[h] = fmaf(qf[h * D + c * 4 + e], __uint_as_float(kc[c][e]), acc[h]);
+            for (int e = 0; e < 4; ++e) acc[r] = fmaf(qf[c * 4 + e], __uint_as_float(kc[c][e]), acc[r]);
+        }
       }
     }
 #pragma unroll
-    for (int h = 0; h < G; ++h) sreg[it][h] = tl < n ? acc[h] * scale_log2 : -INFINITY;
+    for (int r = 0; r < R; ++r) sreg[it][r] = tl < n ? acc[r] * scale_log2 : -INFINITY;
   }
 
   // ---- wave-local softmax state -------------------------------------------
-  float mw[G], lw[G];
+  float mw[R], lw[R];
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
-    float m = sreg[0][h];
+  for (int r = 0; r < R; ++r) {
+    float m = sreg[0][r];
 #pragma unroll
-    for (int it = 1; it < IT; ++it) m = fmaxf(m, sreg[it][h]);
-    mw[h] = wave_max(m);
+    for (int it = 1; it < IT; ++it) m = fmaxf(m, sreg[it][r]);
+    mw[r] = wave_max(m);
   }
 #pragma unroll
   for (int it = 0; it < IT; ++it) {
     const bool valid = wt0 + it * 64 + lane < n;
-    float e[G];
 #pragma unroll
-    for (int h = 0; h < G; ++h) e[h] = valid ? __builtin_amdgcn_exp2f(sreg[it][h] - mw[h]) : 0.f;
-#pragma unroll
-    for (int h = 0; h < G; ++h) sp[it * 64 + lane][h] = e[h];
-#pragma unroll
-    for (int h = 0; h < G; ++h) sreg[it][h] = e[h];
+    for (int r = 0; r < R; ++r) {
+      const float e = valid ? __builtin_amdgcn_exp2f(sreg[it][r] - mw[r]) : 0.f;
+      sp[it * 64 + lane][r] = e;
+      sreg[it][r] = e;
+    }
   }
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
-    float l = sreg[0][h];
+  for (int r = 0; r < R; ++r) {
+    float l = sreg[0][r];
 #pragma unroll
-    for (int it = 1; it < IT; ++it) l += sreg[it][h];
-    lw[h] = wave_sum(l);
+    for (int it = 1; it < IT; ++it) l += sreg[it][r];
+    lw[r] = wave_sum(l);
   }
   // the probabilities are read back by other lanes of this wave
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -178,101 +162,148 @@ decode_partition_kernel(void* __restrict__ out, float* __restrict__ ws_o, float*
   // ---- values: lane owns NI dims x TPC tokens of each block -----------------
   // Chunk i of a block's V tile (1 KiB per wave instruction, fully coalesced)
   // gives lane l the dim (i*64 + l) / CPR and tokens (l % CPR) * TPC + [0, TPC).
-  float o[G][NI];
+  float o[R][NI];
 #pragma unroll
-  for (int h = 0; h < G; ++h)
+  for (int r = 0; r < R; ++r)
 #pragma unroll
-    for (int i = 0; i < NI; ++i) o[h][i] = 0.f;
+    for (int i = 0; i < NI; ++i) o[r][i] = 0.f;
   const int tg = lane % CPR;
   const int nbw = (wn + kBlockSize - 1) / kBlockSize;
-#pragma unroll kVUnroll
-  for (int bl = 0; bl < nbw; ++bl) {
-    const int tb = wt0 / kBlockSize + bl;  // partition-local block
-    const int64_t blk = clamp_block(tab[tb], num_blocks);
-    const unsigned char* vp = vpool + (blk * Hkv + g) * (int64_t)VTILE + lane * 16;
-    u32x4 vv[NI];
+  // V tiles are loaded kVBatch blocks at a time, all loads issued before any
+  // of the batch's math.
+#pragma unroll 1
+  for (int b0 = 0; b0 < nbw; b0 += kVBatch) {
+    u32x4 vv[kVBatch][NI];
 #pragma unroll
-    for (int i = 0; i < NI; ++i) vv[i] = ld16(vp + i * 1024);
-    const int ntok = n - tb * kBlockSize;
-    const float(*pb)[G] = sp + bl * kBlockSize + tg * TPC;
-    auto accumulate = [&](auto masked) {
+    for (int j = 0; j < kVBatch; ++j) {
+      if (b0 + j < nbw) {
+        const int64_t blk = clamp_block(tab[wt0 / kBlockSize + b0 + j], num_blocks);
+        const unsigned char* vp = vpool + (blk * Hkv + g) * (int64_t)VTILE + lane * 16;
 #pragma unroll
-      for (int tt = 0; tt < TPC; ++tt) {
-        float pv[G];
-#pragma unroll
-        for (int h = 0; h < G; ++h) pv[h] = pb[tt][h];
-#pragma unroll
-        for (int i = 0; i < NI; ++i) {
-          float x;
-          if constexpr (ES == 2) {
-            float lo, hi;
-            unpack2<T>(vv[i][tt >> 1], lo, hi);
-            x = (tt & 1) ? hi : lo;
-          } else {
-            x = __uint_as_float(vv[i][tt]);
-          }
-          if constexpr (decltype(masked)::value) {
-            x = tg * TPC + tt < ntok ? x : 0.f;  // slots past the context may hold anything
-          }
-#pragma unroll
-          for (int h = 0; h < G; ++h) o[h][i] = fmaf(pv[h], x, o[h][i]);
-        }
+        for (int i = 0; i < NI; ++i) vv[j][i] = ld16(vp + i * 1024);
       }
-    };
-    if (ntok >= kBlockSize)
-      accumulate(std::false_type{});
-    else
-      accumulate(std::true_type{});
+    }
+#pragma unroll
+    for (int j = 0; j < kVBatch; ++j) {
+      if (b0 + j < nbw) {
+        const int bl = b0 + j;
+        const int tb = wt0 / kBlockSize + bl;  // partition-local block
+        const int ntok = n - tb * kBlockSize;
+        const float(*pb)[R] = sp + bl * kBlockSize + tg * TPC;
+        auto accumulate = [&](auto masked) {
+#pragma unroll
+          for (int tt = 0; tt < TPC; ++tt) {
+            float pv[R];
+#pragma unroll
+            for (int r = 0; r < R; ++r) pv[r] = pb[tt][r];
+#pragma unroll
+            for (int i = 0; i < NI; ++i) {
+              float x;
+              if constexpr (ES == 2) {
+                float lo, hi;
+                unpack2<T>(vv[j][i][tt >> 1], lo, hi);
+                x = (tt & 1) ? hi : lo;
+              } else {
+                x = __uint_as_float(vv[j][i][tt]);
+              }
+              if constexpr (decltype(masked)::value) {
+                x = tg * TPC + tt < ntok ? x : 0.f;  // slots past the context may hold anything
+              }
+#pragma unroll
+              for (int r = 0; r < R; ++r) o[r][i] = fmaf(pv[r], x, o[r][i]);
+            }
+          }
+        };
+        if (ntok >= kBlockSize)
+          accumulate(std::false_type{});
+        else
+          accumulate(std::true_type{});
+      }
+    }
   }
   // add the CPR lanes that share a dim
 #pragma unroll
   for (int msk = 1; msk < CPR; msk <<= 1)
 #pragma unroll
-    for (int h = 0; h < G; ++h)
+    for (int r = 0; r < R; ++r)
 #pragma unroll
-      for (int i = 0; i < NI; ++i) o[h][i] += __shfl_xor(o[h][i], msk, 64);
+      for (int i = 0; i < NI; ++i) o[r][i] += __shfl_xor(o[r][i], msk, 64);
 
   __syncthreads();  // all waves are done with the probabilities
-  float(*so)[G][D] = reinterpret_cast<float(*)[G][D]>(smem);
+  float(*so)[R][D] = reinterpret_cast<float(*)[R][D]>(smem);
   if (tg == 0) {
 #pragma unroll
-    for (int h = 0; h < G; ++h)
+    for (int r = 0; r < R; ++r)
 #pragma unroll
-      for (int i = 0; i < NI; ++i) so[w][h][(i * 64 + lane) / CPR] = o[h][i];
+      for (int i = 0; i < NI; ++i) so[w][r][(i * 64 + lane) / CPR] = o[r][i];
   }
   if (lane == 0) {
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      sml[w][h][0] = mw[h];
-      sml[w][h][1] = lw[h];
+    for (int r = 0; r < R; ++r) {
+      sml[w * R + r][0] = mw[r];
+      sml[w * R + r][1] = lw[r];
     }
   }
   __syncthreads();
 
   // ---- merge the waves' partial softmax states ------------------------------
-  for (int i = tid; i < G * D; i += kThreads) {
-    const int h = i / D, j = i % D;
-    float M = sml[0][h][0];
+  for (int i = tid; i < R * D; i += kThreads) {
+    const int r = i / D, j = i % D;
+    float Mx = sml[r][0];
 #pragma unroll
-    for (int k = 1; k < kWaves; ++k) M = fmaxf(M, sml[k][h][0]);
+    for (int k = 1; k < kWaves; ++k) Mx = fmaxf(Mx, sml[k * R + r][0]);
     float acc = 0.f, l = 0.f;
 #pragma unroll
     for (int k = 0; k < kWaves; ++k) {
-      const float f = __builtin_amdgcn_exp2f(sml[k][h][0] - M);  // 0 for a wave with no tokens
-      acc = fmaf(f, so[k][h][j], acc);
-      l = fmaf(f, sml[k][h][1], l);
+      const float f = __builtin_amdgcn_exp2f(sml[k * R + r][0] - Mx);  // 0 for a wave with no tokens
+      acc = fmaf(f, so[k][r][j], acc);
+      l = fmaf(f, sml[k * R + r][1], l);
     }
-    const int64_t row = (int64_t)s * Hq + g * G + h;
+    const int64_t row = (int64_t)s * Hq + g * G + r;
+    const int nparts = (clamp_len(lens[s], max_context_len) + kPart - 1) / kPart;
     if (nparts == 1) {
       store_out<OutCode>(out, row * D + j, acc / l);
     } else {
       ws_o[(row * max_parts + p) * D + j] = acc;
       if (j == 0) {
-        ws_ml[(row * max_parts + p) * 2 + 0] = M;
+        ws_ml[(row * max_parts + p) * 2 + 0] = Mx;
         ws_ml[(row * max_parts + p) * 2 + 1] = l;
       }
     }
   }
+}
+
+template <typename T, int D, int G, int OutCode>
+__global__ void __launch_bounds__(kThreads, PKV_DECODE_MIN_WAVES)
+decode_partition_kernel(void* __restrict__ out, float* __restrict__ ws_o, float* __restrict__ ws_ml,
+                        const typename T::bits* __restrict__ q, const unsigned char* __restrict__ kpool,
+                        const unsigned char* __restrict__ vpool, const int32_t* __restrict__ tables,
+                        int max_blocks, const int32_t* __restrict__ lens, int Hkv, int64_t num_blocks,
+                        int max_context_len, float scale_log2, int max_parts) {
+  constexpr int RMAX = G;
+  // Per-wave probabilities [kWaves][TPW][R]; after the V pass the same memory
+  // holds the waves' partial outputs [kWaves][R][D].
+  constexpr int SMEM = (kPart > kWaves * D ? kPart : kWaves * D) * RMAX;
+  __shared__ __attribute__((aligned(16))) float smem[SMEM];
+  __shared__ float sml[kWaves * RMAX][2];
+
+  const int g = blockIdx.x, s = blockIdx.y, p = blockIdx.z;
+  const int Hq = Hkv * G;
+
+  const int L = clamp_len(lens[s], max_context_len);
+  const int nparts = (L + kPart - 1) / kPart;
+  if (p >= (nparts > 0 ? nparts : 1)) return;
+  if (L == 0) {  // defined result for an empty context: zeros
+    for (int i = threadIdx.x; i < G * D; i += kThreads)
+      store_out<OutCode>(out, ((int64_t)s * Hq + g * G) * D + i, 0.f);
+    return;
+  }
+  const int t0 = p * kPart;
+  const int n = (L - t0) < kPart ? (L - t0) : kPart;  // tokens in this partition
+  const int32_t* tab = tables + (int64_t)s * max_blocks + t0 / kBlockSize;
+
+  partition_rows<T, D, G, OutCode>(smem, sml, out, ws_o, ws_ml, q, kpool, vpool, tab, lens, s, g, p, n, Hkv,
+                                   num_blocks, max_context_len, scale_log2, max_parts);
 }
 
 template <int D, int OutCode>

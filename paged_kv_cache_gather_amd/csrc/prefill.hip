@@ -18,15 +18,18 @@
 //    the heads of one KV head are stacked so every K/V tile staged in LDS
 //    serves all of them.
 //  * Keys advance 64 at a time (4 blocks).  The workgroup stages the step's
-//    K and V tiles in LDS (double buffered; the next step's global loads are
-//    issued before the current step's math).  K tiles keep the pool layout;
-//    V tiles are stored as fp16 (exact for bf16 values in fp16's normal
-//    range) because the P.V product runs in fp16 (see below).
+//    K and V tiles in LDS with direct global->LDS loads (double buffered: the
+//    next step's loads are issued before the current step's math and take no
+//    registers).  K tiles keep the pool layout; each thread then rewrites the
+//    V chunks it loaded as fp16 (exact for bf16 values in fp16's normal range)
+//    because the P.V product runs in fp16 (see below).
 //  * Scores are formed transposed, S^T = K Q^T (A = K tile from LDS, B = the
 //    wave's Q rows kept in registers), so each lane owns one query row: the
 //    online softmax (base 2, running max and sum per row) needs only two
 //    cross-lane steps per tile for the max, and the probabilities feed the
-//    next product straight from the lane's registers.
+//    next product straight from the lane's registers.  The running max is
+//    only moved when a score exceeds it by more than 2^8, so the output
+//    accumulators are rarely rescaled.
 //  * O^T += V^T P^T with A = V^T (16 dims x 32 keys) and B = P^T.  The key
 //    order inside the 32-wide contraction is permuted identically in both
 //    operands (each lane holds keys 4q..4q+3 of two 16-key tiles), which
@@ -52,6 +55,7 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kPfThreads = 256;
 constexpr int kStepKeys = 64;  // keys per step: 4 blocks of 16
+constexpr float kSlack = 8.f;  // log2 headroom before the running max is moved
 
 template <typename T>
 __device__ __forceinline__ f32x4 mfma_qk(u32x4 a, u32x4 b, f32x4 c) {
@@ -169,43 +173,55 @@ prefill_chunk_kernel(void* __restrict__ out, const uint16_t* __restrict__ q,
   }
 
   // ---- staging of one step's K/V tiles (4 blocks) --------------------------
-  u32x4 kst[NCH], vst[NCH];
-  auto load_step = [&](int s) {
+  // Direct global -> LDS loads (no registers): chunk ci = tid + 256k of the
+  // step; a wave's 64 chunks land contiguously at the wave-uniform base.
+  auto issue_step = [&](int s, int buf) {
+    int64_t blk[NCH];
+#pragma unroll
+    for (int k = 0; k < NCH; ++k) {
+      // the block (uniform per wave) is read through the scalar unit, so the
+      // table loads never wait behind the vector loads already in flight
+      const int lb = 4 * s + __builtin_amdgcn_readfirstlane((tid + kPfThreads * k) / CPT);
+      blk[k] = lb < nblk ? clamp_block(tab[lb], num_blocks) : -1;
+    }
+#pragma unroll
+    for (int k = 0; k < NCH; ++k) {
+      if (blk[k] >= 0) {
+        const int off = ((tid + kPfThreads * k) % CPT) * 16;
+        const int64_t base = (blk[k] * Hkv + g) * (int64_t)TILE + off;
+        const int wbase = (kPfThreads * k + 64 * w) * 16;
+        __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)(kpool + base),
+                                         (__attribute__((address_space(3))) void*)&lds[buf][0][wbase], 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)(vpool + base),
+                                         (__attribute__((address_space(3))) void*)&lds[buf][1][wbase], 16, 0, 0);
+      }
+    }
+  };
+  // After this thread's loads have landed: its V chunks -> fp16 in place, with
+  // keys at or past the context zeroed (blocks past the end become zeros).
+  auto finish_step = [&](int s, int buf) {
 #pragma unroll
     for (int k = 0; k < NCH; ++k) {
       const int ci = tid + kPfThreads * k;
       const int bi = ci / CPT, off = (ci % CPT) * 16;
-      const int lb = 4 * s + bi;  // logical block
-      if (lb < nblk) {
-        const int64_t blk = clamp_block(tab[lb], num_blocks);
-        const int64_t base = (blk * Hkv + g) * (int64_t)TILE + off;
-        kst[k] = ld16(kpool + base);
-        // V chunk: one dim, keys (off % 32) / 2 .. +8 of the block
-        const int valid = L - (lb * kBlockSize + (off % 32) / 2);
-        vst[k] = v_chunk_to_f16<T>(ld16(vpool + base), valid);
-      } else {
-        kst[k] = u32x4{0, 0, 0, 0};
-        vst[k] = u32x4{0, 0, 0, 0};
-      }
-    }
-  };
-  auto store_step = [&](int buf) {
-#pragma unroll
-    for (int k = 0; k < NCH; ++k) {
-      const int ci = tid + kPfThreads * k;
-      st16(&lds[buf][0][ci * 16], kst[k]);
-      st16(&lds[buf][1][ci * 16], vst[k]);
+      const int lb = 4 * s + bi;
+      u32x4* vp = reinterpret_cast<u32x4*>(&lds[buf][1][ci * 16]);
+      if (lb < nblk)
+        *vp = v_chunk_to_f16<T>(*vp, L - (lb * kBlockSize + (off % 32) / 2));
+      else
+        *vp = u32x4{0, 0, 0, 0};
     }
   };
 
-  load_step(0);
-  store_step(0);
+  issue_step(0, 0);
+  __builtin_amdgcn_s_waitcnt(0);
+  finish_step(0, 0);
   __syncthreads();
 
 #pragma unroll 1
   for (int s = 0; s < nsteps; ++s) {
     const int buf = s & 1;
-    if (s + 1 < nsteps) load_step(s + 1);
+    if (s + 1 < nsteps) issue_step(s + 1, buf ^ 1);
     if (active && kStepKeys * s < kmax_w) {
       const unsigned char* kl = lds[buf][0];
       const unsigned char* vl = lds[buf][1];
@@ -225,7 +241,9 @@ prefill_chunk_kernel(void* __restrict__ out, const uint16_t* __restrict__ q,
           st[rt][kt] = acc;
         }
       }
-      // online softmax, one row per lane
+      // online softmax, one row per lane.  The reference max m only moves when
+      // a score exceeds it by more than 2^kSlack, so the accumulators are
+      // rescaled rarely; probabilities stay <= 2^kSlack (fine in fp16).
       const bool diag = kStepKeys * s + kStepKeys - 1 > ctx + i0;
       u32x4 pb[RT][2];
 #pragma unroll
@@ -246,21 +264,25 @@ prefill_chunk_kernel(void* __restrict__ out, const uint16_t* __restrict__ q,
           }
         mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
         mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-        const float mn = fmaxf(m[rt], mx);
-        const float alpha = __builtin_amdgcn_exp2f(m[rt] - mn);
-        m[rt] = mn;
+        if (__any(mx > m[rt] + kSlack)) {
+          const float mn = fmaxf(m[rt], mx);
+          const float alpha = __builtin_amdgcn_exp2f(m[rt] - mn);
+          l[rt] *= alpha;
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt) o[rt][dt] *= alpha;
+          m[rt] = mn;
+        }
+        const float mr = m[rt];
         float ls = 0.f;
         float e[4][4];
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            e[kt][r] = __builtin_amdgcn_exp2f(st[rt][kt][r] - mn);
+            e[kt][r] = __builtin_amdgcn_exp2f(st[rt][kt][r] - mr);
             ls += e[kt][r];
           }
-        l[rt] = fmaf(l[rt], alpha, ls);
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) o[rt][dt] *= alpha;
+        l[rt] += ls;
 #pragma unroll
         for (int kh = 0; kh < 2; ++kh) {
           pb[rt][kh][0] = pack_f16x2(e[2 * kh][0], e[2 * kh][1]);
@@ -282,7 +304,8 @@ prefill_chunk_kernel(void* __restrict__ out, const uint16_t* __restrict__ q,
           for (int rt = 0; rt < RT; ++rt) o[rt][dt] = mfma_pv(va, pb[rt][kh], o[rt][dt]);
         }
     }
-    if (s + 1 < nsteps) store_step(buf ^ 1);
+    __builtin_amdgcn_s_waitcnt(0);  // this thread's loads for the next step have landed
+    if (s + 1 < nsteps) finish_step(s + 1, buf ^ 1);
     __syncthreads();
   }
 

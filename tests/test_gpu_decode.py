@@ -75,6 +75,30 @@ def test_decode_shared_prefix_with_copy_on_write():
     _check_all(w, out, "f32")
 
 
+SHARED_RUNS = [
+    # name, Hq, Hkv, d, dtype, lens, prefix_len, prefix_group
+    ("runs_gqa4", 32, 8, 128, "bf16",
+     [1500, 1200, 2000, 1101, 1102, 700, 900, 800, 512, 513, 1024, 1024],
+     [1100, 1100, 1100, 1100, 1100, 600, 600, 0, 511, 512, 1023, 1023],
+     [0, 0, 0, 0, 0, 1, 1, -1, 2, 2, 3, 3]),
+    ("runs_mha", 8, 8, 128, "f16", [1300, 1300, 1030, 600], [1200, 1200, 1029, 0], [0, 0, 0, -1]),
+    ("runs_gqa8", 32, 4, 64, "f16", [1100, 1100, 1100], [1024, 1024, 1024], [0, 0, 0]),
+    ("runs_gqa2", 8, 4, 128, "bf16", [2100] * 9, [2048] * 9, [0] * 9),
+]
+
+
+@pytest.mark.parametrize("name,Hq,Hkv,d,dtype,lens,plen,pgroup", SHARED_RUNS, ids=[c[0] for c in SHARED_RUNS])
+def test_decode_shared_partition_runs(name, Hq, Hkv, d, dtype, lens, plen, pgroup):
+    # neighbours whose full 512-token partitions use the same blocks are served
+    # by one workgroup; runs cross the serving-group boundary, some members
+    # end exactly at a partition edge
+    w = synth.custom_workload(name, Hq, Hkv, d, dtype, 4096, seed=13, decode_lens=lens, prefix_len=plen,
+                              prefix_group=pgroup)
+    print(f"decode {name}", flush=True)
+    _, out = _run_decode(w, "f32")
+    _check_all(w, out, "f32")
+
+
 @pytest.mark.parametrize("cfg", [2, 3, 4])
 def test_decode_full_size_sampled(cfg):
     w = synth.make_workload(cfg, seed=0)
