@@ -284,8 +284,10 @@ int paged_attention_decode_reduce(void* out, int32_t out_dtype, const void* q, c
  *   context_lens  device int32 [n_chunks], <= max_context_len
  *                 <= max_blocks_per_seq * block_size.
  * Supported: kv_dtype PKV_F16 or PKV_BF16, head_dim 64/128, n_q_heads /
- * n_kv_heads in {1, 2, 4, 8, 16}, block_size 16.  Products on MFMA, fp32
- * accumulation and softmax. */
+ * n_kv_heads in {1, 2, 4, 8, 16}, block_size 16, scale finite and > 0
+ * (PKV_EINVAL otherwise).  Products on MFMA, fp32 accumulation and softmax;
+ * the P.V product takes V and the probabilities in fp16, so bf16 V entries
+ * beyond fp16's range (|v| > 65504) are clamped to it. */
 int paged_attention_prefill_chunk(void* out, int32_t out_dtype, const void* q, const void* k_pool,
                                   const void* v_pool, const int32_t* block_tables,
                                   int32_t max_blocks_per_seq, const int32_t* cu_q_lens,

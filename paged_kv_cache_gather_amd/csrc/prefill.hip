@@ -18,9 +18,9 @@
 //    the heads of one KV head are stacked so every K/V tile staged in LDS
 //    serves all of them.
 //  * Keys advance 64 at a time (4 blocks).  The workgroup stages the step's
-//    K and V tiles in LDS with direct global->LDS loads (double buffered: the
-//    next step's loads are issued before the current step's math and take no
-//    registers).  K tiles keep the pool layout; each thread then rewrites the
+//    K and V tiles in LDS with direct global->LDS loads (three buffers: the
+//    loads for two steps ahead are issued before the current step's math and
+//    take no registers).  K tiles keep the pool layout; each thread then rewrites the
 //    V chunks it loaded as fp16 (exact for bf16 values in fp16's normal range)
 //    because the P.V product runs in fp16 (see below).
 //  * Scores are formed transposed, S^T = K Q^T (A = K tile from LDS, B = the
@@ -53,7 +53,11 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kPfThreads = 256;
+#ifndef PKV_PREFILL_WAVES
+#define PKV_PREFILL_WAVES 8
+#endif
+constexpr int kPfWaves = PKV_PREFILL_WAVES;  // waves per workgroup (4: one per SIMD, 8: two)
+constexpr int kPfThreads = 64 * kPfWaves;
 constexpr int kStepKeys = 64;  // keys per step: 4 blocks of 16
 constexpr float kSlack = 8.f;  // log2 headroom before the running max is moved
 
@@ -72,10 +76,19 @@ __device__ __forceinline__ f32x4 mfma_pv(u32x4 a, u32x4 b, f32x4 c) {
                                                 __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
 }
 
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2v_t __attribute__((ext_vector_type(2)));
+
+// Two fp32 -> packed fp16, round to nearest even (one v_cvt_pk_f16_f32).
 __device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
-  const uint16_t a = __builtin_bit_cast(uint16_t, (_Float16)lo);
-  const uint16_t b = __builtin_bit_cast(uint16_t, (_Float16)hi);
-  return (uint32_t)a | ((uint32_t)b << 16);
+  const f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2v_t));
+}
+
+// Two fp32 -> packed fp16, round toward zero: exact for values fp16 holds and
+// saturating (to +-65504) for finite values beyond its range.
+__device__ __forceinline__ uint32_t pack_f16x2_rtz(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo, hi));
 }
 
 // One 16-byte chunk of a V tile (8 consecutive keys of one dim) -> fp16 bits,
@@ -83,24 +96,28 @@ __device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
 template <typename T>
 __device__ __forceinline__ u32x4 v_chunk_to_f16(u32x4 v, int valid) {
   u32x4 r;
+  if constexpr (T::kCode == PKV_BF16) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    float lo, hi;
-    if constexpr (T::kCode == PKV_BF16) {
-      lo = bf16lo(v[i]);
-      hi = bf16hi(v[i]);
-      lo = fminf(fmaxf(lo, -65504.f), 65504.f);  // saturate into fp16 range
-      hi = fminf(fmaxf(hi, -65504.f), 65504.f);
-    } else {
-      lo = f16lo(v[i]);
-      hi = f16hi(v[i]);
+    for (int i = 0; i < 4; ++i) r[i] = pack_f16x2_rtz(bf16lo(v[i]), bf16hi(v[i]));
+  } else {
+    r = v;
+  }
+  if (valid < 8) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t lo = 2 * i < valid ? 0xffffu : 0u;
+      const uint32_t hi = 2 * i + 1 < valid ? 0xffff0000u : 0u;
+      r[i] &= lo | hi;
     }
-    lo = 2 * i < valid ? lo : 0.f;
-    hi = 2 * i + 1 < valid ? hi : 0.f;
-    r[i] = pack_f16x2(lo, hi);
   }
   return r;
 }
+
+// Position of 8-byte key group q (keys 4q..4q+3) of dim j inside the dim's
+// 32-byte row of an fp16 V tile in LDS.  Odd groups of 8 dims have their two
+// 16-byte halves swapped, so a V^T operand read (16 dims x one key group per
+// 32 lanes) touches every LDS bank once instead of twice.
+__device__ __forceinline__ int v_slot(int j, int q) { return (q ^ (((j >> 3) & 1) << 1)) * 8; }
 
 template <typename T, int D, int GW, int OutCode>
 __global__ void __launch_bounds__(kPfThreads, 1)
@@ -109,17 +126,20 @@ prefill_chunk_kernel(void* __restrict__ out, const uint16_t* __restrict__ q,
                      const int32_t* __restrict__ tables, int max_blocks, const int32_t* __restrict__ cu_q,
                      const int32_t* __restrict__ lens, int total_q, int Hkv, int G, int64_t num_blocks,
                      int max_context_len, float scale_log2) {
-  constexpr int TT = 4 / GW;               // 16-token tiles per wave
-  constexpr int RT = TT * GW;              // row tiles per wave (= 4)
-  constexpr int TW = 16 * TT;              // query tokens per wave
-  constexpr int TWG = 4 * TW;              // query tokens per workgroup
+  constexpr int RT = 16 / kPfWaves;        // row tiles (16 query rows each) per wave
+  constexpr int HW = GW < RT ? GW : RT;    // heads per wave
+  constexpr int TTW = RT / HW;             // 16-token tiles per wave
+  constexpr int WPT = GW / HW;             // waves sharing a token tile (different heads)
+  constexpr int TW = 16 * TTW;             // query tokens per wave
+  constexpr int TWG = 16 * TTW * (kPfWaves / WPT);  // query tokens per workgroup
   constexpr int DC = D / 32;               // 32-dim slices of the score contraction
   constexpr int DT = D / 16;               // 16-dim tiles of the output
   constexpr int TILE = D * kBlockSize * 2; // bytes of one (block, head) tile
   constexpr int CPT = TILE / 16;           // 16-byte chunks per tile
   constexpr int NCH = 4 * CPT / kPfThreads;  // staging chunks per thread per step (K and V each)
 
-  __shared__ __attribute__((aligned(16))) unsigned char lds[2][2][4 * TILE];  // [buffer][K, V]
+  constexpr int NBUF = 3;  // steps staged ahead: the current one plus two in flight
+  __shared__ __attribute__((aligned(16))) unsigned char lds[NBUF][2][4 * TILE];  // [buffer][K, V]
 
   const int c = blockIdx.z;
   const int qs = cu_q[c];
@@ -139,7 +159,8 @@ prefill_chunk_kernel(void* __restrict__ out, const uint16_t* __restrict__ q,
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int q4 = lane >> 4, r16 = lane & 15;
 
-  const int i0 = tile0 + w * TW;                   // wave's first query token (chunk-local)
+  const int i0 = tile0 + (w / WPT) * TW;           // wave's first query token (chunk-local)
+  const int hb = (w % WPT) * HW;                   // wave's first head within the workgroup
   const int wg_end = qlen < tile0 + TWG ? qlen : tile0 + TWG;
   const int nsteps = (ctx + wg_end + kStepKeys - 1) / kStepKeys;
   const bool active = i0 < qlen;
@@ -152,7 +173,7 @@ prefill_chunk_kernel(void* __restrict__ out, const uint16_t* __restrict__ q,
   u32x4 bq[RT][DC];
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
-    const int tt = rt / GW, hh = rt % GW;
+    const int tt = rt / HW, hh = hb + rt % HW;
     int tok = i0 + 16 * tt + r16;
     tok = tok < qlen ? tok : qlen - 1;
     int row = qs + tok;
@@ -175,7 +196,8 @@ prefill_chunk_kernel(void* __restrict__ out, const uint16_t* __restrict__ q,
   // ---- staging of one step's K/V tiles (4 blocks) --------------------------
   // Direct global -> LDS loads (no registers): chunk ci = tid + 256k of the
   // step; a wave's 64 chunks land contiguously at the wave-uniform base.
-  auto issue_step = [&](int s, int buf) {
+  // Returns the number of loads this thread issued (uniform per wave).
+  auto issue_step = [&](int s, int buf) -> int {
     int64_t blk[NCH];
 #pragma unroll
     for (int k = 0; k < NCH; ++k) {
@@ -184,6 +206,7 @@ prefill_chunk_kernel(void* __restrict__ out, const uint16_t* __restrict__ q,
       const int lb = 4 * s + __builtin_amdgcn_readfirstlane((tid + kPfThreads * k) / CPT);
       blk[k] = lb < nblk ? clamp_block(tab[lb], num_blocks) : -1;
     }
+    int issued = 0;
 #pragma unroll
     for (int k = 0; k < NCH; ++k) {
       if (blk[k] >= 0) {
@@ -194,8 +217,10 @@ prefill_chunk_kernel(void* __restrict__ out, const uint16_t* __restrict__ q,
                                          (__attribute__((address_space(3))) void*)&lds[buf][0][wbase], 16, 0, 0);
         __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)(vpool + base),
                                          (__attribute__((address_space(3))) void*)&lds[buf][1][wbase], 16, 0, 0);
+        issued += 2;
       }
     }
+    return issued;
   };
   // After this thread's loads have landed: its V chunks -> fp16 in place, with
   // keys at or past the context zeroed (blocks past the end become zeros).
@@ -205,23 +230,56 @@ prefill_chunk_kernel(void* __restrict__ out, const uint16_t* __restrict__ q,
       const int ci = tid + kPfThreads * k;
       const int bi = ci / CPT, off = (ci % CPT) * 16;
       const int lb = 4 * s + bi;
-      u32x4* vp = reinterpret_cast<u32x4*>(&lds[buf][1][ci * 16]);
+      const u32x4 raw = *reinterpret_cast<const u32x4*>(&lds[buf][1][ci * 16]);
+      // this chunk holds keys 8*hf..8*hf+7 of dim j; both halves of a dim row
+      // belong to adjacent lanes of one wave, so swapping them is race-free
+      const int bo = bi * TILE, j = (off % TILE) / 32, hf = (off % 32) / 16;
+      u32x4* vp = reinterpret_cast<u32x4*>(&lds[buf][1][bo + j * 32 + v_slot(j, 2 * hf)]);
       if (lb < nblk)
-        *vp = v_chunk_to_f16<T>(*vp, L - (lb * kBlockSize + (off % 32) / 2));
+        *vp = v_chunk_to_f16<T>(raw, L - (lb * kBlockSize + 8 * hf));
       else
         *vp = u32x4{0, 0, 0, 0};
     }
   };
 
+  // Wait until at most `keep` vector-memory operations of this wave are
+  // outstanding (loads complete in issue order, so every earlier one is done).
+  auto wait_vm = [](int keep) {
+    // s_waitcnt immediate: vmcnt in bits 3:0, expcnt 6:4 and lgkmcnt 11:8 left at their maxima
+    switch (keep) {
+      case 0: __builtin_amdgcn_s_waitcnt(0xF70); break;
+      case 1: __builtin_amdgcn_s_waitcnt(0xF71); break;
+      case 2: __builtin_amdgcn_s_waitcnt(0xF72); break;
+      case 3: __builtin_amdgcn_s_waitcnt(0xF73); break;
+      case 4: __builtin_amdgcn_s_waitcnt(0xF74); break;
+      case 5: __builtin_amdgcn_s_waitcnt(0xF75); break;
+      case 6: __builtin_amdgcn_s_waitcnt(0xF76); break;
+      case 7: __builtin_amdgcn_s_waitcnt(0xF77); break;
+      default: __builtin_amdgcn_s_waitcnt(0xF78); break;
+    }
+  };
+  static_assert(2 * NCH <= 8, "wait_vm covers at most 8 loads in flight per thread");
+  // Workgroup barrier for LDS hand-off only: waits for this thread's LDS
+  // writes (lgkmcnt) but, unlike __syncthreads(), not for the global->LDS
+  // loads still in flight for later steps.
+  auto lds_barrier = [] {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt unconstrained
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+
   issue_step(0, 0);
-  __builtin_amdgcn_s_waitcnt(0);
+  int ahead = nsteps > 1 ? issue_step(1, 1) : 0;  // loads of the step after the next one to be finished
+  wait_vm(ahead);
   finish_step(0, 0);
-  __syncthreads();
+  lds_barrier();
 
 #pragma unroll 1
   for (int s = 0; s < nsteps; ++s) {
-    const int buf = s & 1;
-    if (s + 1 < nsteps) issue_step(s + 1, buf ^ 1);
+    const int buf = s % NBUF;
+    const int nxt = (s + 1) % NBUF;
+    const int far = s + 2 < nsteps ? issue_step(s + 2, (s + 2) % NBUF) : 0;
     if (active && kStepKeys * s < kmax_w) {
       const unsigned char* kl = lds[buf][0];
       const unsigned char* vl = lds[buf][1];
@@ -248,22 +306,23 @@ prefill_chunk_kernel(void* __restrict__ out, const uint16_t* __restrict__ q,
       u32x4 pb[RT][2];
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) {
-        const int pos = ctx + i0 + 16 * (rt / GW) + r16;
+        const int pos = ctx + i0 + 16 * (rt / HW) + r16;
+        // max over raw scores (scale > 0, so it commutes with the scaling),
+        // then moved to base-2 units
         float mx = -INFINITY;
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            float v = st[rt][kt][r] * scale_log2;
             if (diag) {
               const int key = kStepKeys * s + 16 * kt + 4 * q4 + r;
-              v = key <= pos ? v : -INFINITY;
+              st[rt][kt][r] = key <= pos ? st[rt][kt][r] : -INFINITY;
             }
-            st[rt][kt][r] = v;
-            mx = fmaxf(mx, v);
+            mx = fmaxf(mx, st[rt][kt][r]);
           }
         mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
         mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        mx *= scale_log2;
         if (__any(mx > m[rt] + kSlack)) {
           const float mn = fmaxf(m[rt], mx);
           const float alpha = __builtin_amdgcn_exp2f(m[rt] - mn);
@@ -279,7 +338,7 @@ prefill_chunk_kernel(void* __restrict__ out, const uint16_t* __restrict__ q,
         for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            e[kt][r] = __builtin_amdgcn_exp2f(st[rt][kt][r] - mr);
+            e[kt][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(st[rt][kt][r], scale_log2, -mr));
             ls += e[kt][r];
           }
         l[rt] += ls;
@@ -297,16 +356,17 @@ prefill_chunk_kernel(void* __restrict__ out, const uint16_t* __restrict__ q,
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
           const int dim = 16 * dt + r16;
-          const u32x2 a0 = *reinterpret_cast<const u32x2*>(vl + (2 * kh) * TILE + dim * 32 + 8 * q4);
-          const u32x2 a1 = *reinterpret_cast<const u32x2*>(vl + (2 * kh + 1) * TILE + dim * 32 + 8 * q4);
+          const int vo = dim * 32 + v_slot(dim, q4);
+          const u32x2 a0 = *reinterpret_cast<const u32x2*>(vl + (2 * kh) * TILE + vo);
+          const u32x2 a1 = *reinterpret_cast<const u32x2*>(vl + (2 * kh + 1) * TILE + vo);
           const u32x4 va = {a0[0], a0[1], a1[0], a1[1]};
 #pragma unroll
           for (int rt = 0; rt < RT; ++rt) o[rt][dt] = mfma_pv(va, pb[rt][kh], o[rt][dt]);
         }
     }
-    __builtin_amdgcn_s_waitcnt(0);  // this thread's loads for the next step have landed
-    if (s + 1 < nsteps) finish_step(s + 1, buf ^ 1);
-    __syncthreads();
+    wait_vm(far);  // this thread's loads for step s + 1 have landed
+    if (s + 1 < nsteps) finish_step(s + 1, nxt);
+    lds_barrier();
   }
 
   // ---- normalise and write the wave's rows ---------------------------------
@@ -317,9 +377,9 @@ prefill_chunk_kernel(void* __restrict__ out, const uint16_t* __restrict__ q,
     lt += __shfl_xor(lt, 16, 64);
     lt += __shfl_xor(lt, 32, 64);
     const float inv = 1.f / lt;
-    const int tok = i0 + 16 * (rt / GW) + r16;
+    const int tok = i0 + 16 * (rt / HW) + r16;
     if (tok < qlen && qs + tok < total_q) {
-      const int64_t rowbase = ((int64_t)(qs + tok) * Hq + h0 + rt % GW) * D;
+      const int64_t rowbase = ((int64_t)(qs + tok) * Hq + h0 + hb + rt % HW) * D;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
@@ -346,7 +406,9 @@ struct PrefillArgs {
 
 template <typename T, int D, int GW, int OutCode>
 void launch_prefill(const PrefillArgs& a) {
-  constexpr int TWG = 4 * 16 * (4 / GW);
+  constexpr int RT = 16 / kPfWaves;
+  constexpr int HW = GW < RT ? GW : RT;
+  constexpr int TWG = 16 * (RT / HW) * (kPfWaves / (GW / HW));
   const unsigned gy = (unsigned)((a.max_q_len + TWG - 1) / TWG);
   hipLaunchKernelGGL((prefill_chunk_kernel<T, D, GW, OutCode>),
                      dim3((unsigned)(a.Hkv * (a.G / GW)), gy, (unsigned)a.n_chunks), dim3(kPfThreads), 0,
@@ -411,7 +473,7 @@ extern "C" int paged_attention_prefill_chunk(void* out, int32_t out_dtype, const
     return fail(PKV_EINVAL, F + ": NULL pointer");
   if (!pkv::aligned16(q) || !pkv::aligned16(k_pool) || !pkv::aligned16(v_pool))
     return fail(PKV_EINVAL, F + ": q and pools must be 16-byte aligned");
-  if (!std::isfinite(scale)) return fail(PKV_EINVAL, F + ": scale not finite");
+  if (!std::isfinite(scale) || !(scale > 0.f)) return fail(PKV_EINVAL, F + ": scale must be finite and > 0");
   pkv::PrefillArgs a;
   a.out = out;
   a.q = (const uint16_t*)q;
