@@ -42,6 +42,7 @@
 
 #include <cmath>
 #include <string>
+#include <type_traits>
 
 #include "pkv_device.h"
 #include "pkv_internal.h"
@@ -113,12 +114,6 @@ __device__ __forceinline__ u32x4 v_chunk_to_f16(u32x4 v, int valid) {
   return r;
 }
 
-// Position of 8-byte key group q (keys 4q..4q+3) of dim j inside the dim's
-// 32-byte row of an fp16 V tile in LDS.  Odd groups of 8 dims have their two
-// 16-byte halves swapped, so a V^T operand read (16 dims x one key group per
-// 32 lanes) touches every LDS bank once instead of twice.
-__device__ __forceinline__ int v_slot(int j, int q) { return (q ^ (((j >> 3) & 1) << 1)) * 8; }
-
 template <typename T, int D, int GW, int OutCode>
 __global__ void __launch_bounds__(kPfThreads, 1)
 prefill_chunk_kernel(void* __restrict__ out, const uint16_t* __restrict__ q,
@@ -183,19 +178,46 @@ prefill_chunk_kernel(void* __restrict__ out, const uint16_t* __restrict__ q,
     for (int dc = 0; dc < DC; ++dc) bq[rt][dc] = active ? ld16(qp + 32 * dc) : u32x4{0, 0, 0, 0};
   }
 
+  // Key order inside the 32 keys of a block pair (2kh, 2kh+1) of a step.  Row
+  // m = 4a + r of score tile kt = 2kh + sub holds the pair's key
+  //   16 (a>>1) + 8 (a&1) + 4 (sub ^ (a>>1)) + r,
+  // so (i) the 16 rows of one tile sit at 16 distinct token offsets, which
+  // keeps the K reads free of LDS bank conflicts, and (ii) the lanes of group
+  // a (q4 = a) own, across the pair's two tiles, the 8 consecutive keys
+  // 8(a&1)..8(a&1)+7 of block 2kh + (a>>1): exactly one 16-byte chunk of a V
+  // row, read whole as the V^T operand.  For odd blocks the two 4-key halves
+  // arrive in the order (4..7, 0..3); the staging stores their V chunks that
+  // way round.
+  auto pair_key = [](int m, int sub) {
+    const int a = m >> 2;
+    return 16 * (a >> 1) + 8 * (a & 1) + 4 * (sub ^ (a >> 1)) + (m & 3);
+  };
+  int k_row_off[2], key_base[2];
+#pragma unroll
+  for (int sub = 0; sub < 2; ++sub) {
+    const int kr = pair_key(r16, sub);  // key whose K row this lane loads
+    k_row_off[sub] = (kr >> 4) * TILE + ((kr & 15) + q4 * kBlockSize) * 16;
+    key_base[sub] = pair_key(4 * q4, sub);  // key of score element r = 0 held by this lane
+  }
+  // V^T operand: dims 16dt + r16, the lane group's 8 keys; odd groups of 8
+  // dims keep their two 16-byte halves swapped (bank-conflict-free reads)
+  const int v_off = (q4 >> 1) * TILE + r16 * 32 + (((q4 & 1) ^ (r16 >> 3)) * 16);
+  const u32x4 ones = {0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u};  // fp16 1.0 x 8
+
   f32x4 o[RT][DT];
-  float m[RT], l[RT];
+  f32x4 lsum[RT];  // element 0: running row sum of the fp16 probabilities (an MFMA against ones)
+  float m[RT];
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
     m[rt] = -INFINITY;
-    l[rt] = 0.f;
+    lsum[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) o[rt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
   // ---- staging of one step's K/V tiles (4 blocks) --------------------------
-  // Direct global -> LDS loads (no registers): chunk ci = tid + 256k of the
-  // step; a wave's 64 chunks land contiguously at the wave-uniform base.
+  // Direct global -> LDS loads (no registers): chunk ci = tid + kPfThreads k
+  // of the step; a wave's 64 chunks land contiguously at the wave-uniform base.
   // Returns the number of loads this thread issued (uniform per wave).
   auto issue_step = [&](int s, int buf) -> int {
     int64_t blk[NCH];
@@ -222,26 +244,24 @@ prefill_chunk_kernel(void* __restrict__ out, const uint16_t* __restrict__ q,
     }
     return issued;
   };
-  // After this thread's loads have landed: its V chunks -> fp16 in place, with
-  // keys at or past the context zeroed (blocks past the end become zeros).
+  // After this thread's loads have landed: its V chunks -> fp16, keys at or
+  // past the context zeroed (blocks past the end become zeros), moved to the
+  // swizzled slot of their dim row; odd blocks with their 4-key halves swapped.
   auto finish_step = [&](int s, int buf) {
 #pragma unroll
     for (int k = 0; k < NCH; ++k) {
       const int ci = tid + kPfThreads * k;
-      const int bi = ci / CPT, off = (ci % CPT) * 16;
+      const int bi = __builtin_amdgcn_readfirstlane(ci / CPT), off = (ci % CPT) * 16;
       const int lb = 4 * s + bi;
       const u32x4 raw = *reinterpret_cast<const u32x4*>(&lds[buf][1][ci * 16]);
-      // this chunk holds keys 8*hf..8*hf+7 of dim j; both halves of a dim row
-      // belong to adjacent lanes of one wave, so swapping them is race-free
-      const int bo = bi * TILE, j = (off % TILE) / 32, hf = (off % 32) / 16;
-      u32x4* vp = reinterpret_cast<u32x4*>(&lds[buf][1][bo + j * 32 + v_slot(j, 2 * hf)]);
-      if (lb < nblk)
-        *vp = v_chunk_to_f16<T>(raw, L - (lb * kBlockSize + 8 * hf));
-      else
-        *vp = u32x4{0, 0, 0, 0};
+      // keys 8hf..8hf+7 of dim j; both halves of a dim row belong to
+      // adjacent lanes of one wave, so the in-place exchange is race-free
+      const int j = off / 32, hf = (off % 32) / 16;
+      u32x4 v = lb < nblk ? v_chunk_to_f16<T>(raw, L - (lb * kBlockSize + 8 * hf)) : u32x4{0, 0, 0, 0};
+      if (bi & 1) v = u32x4{v[2], v[3], v[0], v[1]};
+      *reinterpret_cast<u32x4*>(&lds[buf][1][bi * TILE + j * 32 + ((hf ^ ((j >> 3) & 1)) * 16)]) = v;
     }
   };
-
   // Wait until at most `keep` vector-memory operations of this wave are
   // outstanding (loads complete in issue order, so every earlier one is done).
   auto wait_vm = [](int keep) {
@@ -275,108 +295,113 @@ prefill_chunk_kernel(void* __restrict__ out, const uint16_t* __restrict__ q,
   finish_step(0, 0);
   lds_barrier();
 
-#pragma unroll 1
-  for (int s = 0; s < nsteps; ++s) {
-    const int buf = s % NBUF;
-    const int nxt = (s + 1) % NBUF;
-    const int far = s + 2 < nsteps ? issue_step(s + 2, (s + 2) % NBUF) : 0;
-    if (active && kStepKeys * s < kmax_w) {
-      const unsigned char* kl = lds[buf][0];
-      const unsigned char* vl = lds[buf][1];
-      // S^T tiles: st[rt][kt] holds keys 16kt + 4q4 + r of row r16
-      f32x4 st[RT][4];
+  // One step of 64 keys for this wave's row tiles; kDiag: the step reaches
+  // the causal diagonal (or the end of the context) and needs the mask.
+  auto attend_step = [&](auto diag_tag, int s, const unsigned char* kl, const unsigned char* vl)
+      __attribute__((always_inline)) {
+    constexpr bool kDiag = decltype(diag_tag)::value;
+    // S^T tiles: st[rt][kt] holds, for row r16, keys 32(kt/2) + key_base[kt%2] + r
+    f32x4 st[RT][4];
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt) {
-        u32x4 ka[DC];
+    for (int kt = 0; kt < 4; ++kt) {
+      u32x4 ka[DC];
 #pragma unroll
-        for (int dc = 0; dc < DC; ++dc)
-          ka[dc] = *reinterpret_cast<const u32x4*>(kl + kt * TILE + ((4 * dc + q4) * kBlockSize + r16) * 16);
-#pragma unroll
-        for (int rt = 0; rt < RT; ++rt) {
-          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int dc = 0; dc < DC; ++dc) acc = mfma_qk<T>(ka[dc], bq[rt][dc], acc);
-          st[rt][kt] = acc;
-        }
-      }
-      // online softmax, one row per lane.  The reference max m only moves when
-      // a score exceeds it by more than 2^kSlack, so the accumulators are
-      // rescaled rarely; probabilities stay <= 2^kSlack (fine in fp16).
-      const bool diag = kStepKeys * s + kStepKeys - 1 > ctx + i0;
-      u32x4 pb[RT][2];
+      for (int dc = 0; dc < DC; ++dc)
+        ka[dc] = *reinterpret_cast<const u32x4*>(kl + (kt >> 1) * 2 * TILE + k_row_off[kt & 1] +
+                                                 dc * 4 * kBlockSize * 16);
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) {
-        const int pos = ctx + i0 + 16 * (rt / HW) + r16;
-        // max over raw scores (scale > 0, so it commutes with the scaling),
-        // then moved to base-2 units
-        float mx = -INFINITY;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            if (diag) {
-              const int key = kStepKeys * s + 16 * kt + 4 * q4 + r;
-              st[rt][kt][r] = key <= pos ? st[rt][kt][r] : -INFINITY;
-            }
-            mx = fmaxf(mx, st[rt][kt][r]);
-          }
-        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-        mx *= scale_log2;
-        if (__any(mx > m[rt] + kSlack)) {
-          const float mn = fmaxf(m[rt], mx);
-          const float alpha = __builtin_amdgcn_exp2f(m[rt] - mn);
-          l[rt] *= alpha;
-#pragma unroll
-          for (int dt = 0; dt < DT; ++dt) o[rt][dt] *= alpha;
-          m[rt] = mn;
-        }
-        const float mr = m[rt];
-        float ls = 0.f;
-        float e[4][4];
-#pragma unroll
-        for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            e[kt][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(st[rt][kt][r], scale_log2, -mr));
-            ls += e[kt][r];
-          }
-        l[rt] += ls;
-#pragma unroll
-        for (int kh = 0; kh < 2; ++kh) {
-          pb[rt][kh][0] = pack_f16x2(e[2 * kh][0], e[2 * kh][1]);
-          pb[rt][kh][1] = pack_f16x2(e[2 * kh][2], e[2 * kh][3]);
-          pb[rt][kh][2] = pack_f16x2(e[2 * kh + 1][0], e[2 * kh + 1][1]);
-          pb[rt][kh][3] = pack_f16x2(e[2 * kh + 1][2], e[2 * kh + 1][3]);
-        }
+        for (int dc = 0; dc < DC; ++dc) acc = mfma_qk<T>(ka[dc], bq[rt][dc], acc);
+        st[rt][kt] = acc;
       }
-      // O^T += V^T P^T
-#pragma unroll
-      for (int kh = 0; kh < 2; ++kh)
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-          const int dim = 16 * dt + r16;
-          const int vo = dim * 32 + v_slot(dim, q4);
-          const u32x2 a0 = *reinterpret_cast<const u32x2*>(vl + (2 * kh) * TILE + vo);
-          const u32x2 a1 = *reinterpret_cast<const u32x2*>(vl + (2 * kh + 1) * TILE + vo);
-          const u32x4 va = {a0[0], a0[1], a1[0], a1[1]};
-#pragma unroll
-          for (int rt = 0; rt < RT; ++rt) o[rt][dt] = mfma_pv(va, pb[rt][kh], o[rt][dt]);
-        }
     }
-    wait_vm(far);  // this thread's loads for step s + 1 have landed
-    if (s + 1 < nsteps) finish_step(s + 1, nxt);
-    lds_barrier();
-  }
+    // online softmax, one row per lane.  The reference max m only moves when
+    // a score exceeds it by more than 2^kSlack, so the accumulators are
+    // rescaled rarely; probabilities stay <= 2^kSlack (fine in fp16).
+    u32x4 pb[RT][2];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      if constexpr (kDiag) {
+        const int lim = ctx + i0 + 16 * (rt / HW) + r16 - kStepKeys * s;  // last visible key of the step
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            st[rt][kt][r] = 32 * (kt >> 1) + key_base[kt & 1] + r <= lim ? st[rt][kt][r] : -INFINITY;
+      }
+      // max over raw scores (scale > 0, so it commutes with the scaling),
+      // then moved to base-2 units
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) mx = fmaxf(mx, st[rt][kt][r]);
+      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      mx *= scale_log2;
+      if (__any(mx > m[rt] + kSlack)) {
+        const float mn = fmaxf(m[rt], mx);
+        const float alpha = __builtin_amdgcn_exp2f(m[rt] - mn);
+        lsum[rt][0] *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) o[rt][dt] *= alpha;
+        m[rt] = mn;
+      }
+      const float mr = m[rt];
+      float e[4][4];
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) e[kt][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(st[rt][kt][r], scale_log2, -mr));
+#pragma unroll
+      for (int kh = 0; kh < 2; ++kh) {
+        pb[rt][kh][0] = pack_f16x2(e[2 * kh][0], e[2 * kh][1]);
+        pb[rt][kh][1] = pack_f16x2(e[2 * kh][2], e[2 * kh][3]);
+        pb[rt][kh][2] = pack_f16x2(e[2 * kh + 1][0], e[2 * kh + 1][1]);
+        pb[rt][kh][3] = pack_f16x2(e[2 * kh + 1][2], e[2 * kh + 1][3]);
+      }
+    }
+    // O^T += V^T P^T, and the row sums as ones . P^T
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh) {
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) lsum[rt] = mfma_pv(ones, pb[rt][kh], lsum[rt]);
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const u32x4 va = *reinterpret_cast<const u32x4*>(vl + 2 * kh * TILE + dt * 16 * 32 + v_off);
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) o[rt][dt] = mfma_pv(va, pb[rt][kh], o[rt][dt]);
+      }
+    }
+  };
+
+  // Steps before s_diag lie wholly below this wave's first query row and need
+  // no mask; the two ranges run as separate loops (each with the workgroup's
+  // staging and one barrier per step, so waves with different split points
+  // still meet at every barrier).
+  auto run_steps = [&](auto diag_tag, int s_begin, int s_end) __attribute__((always_inline)) {
+#pragma unroll 1
+    for (int s = s_begin; s < s_end; ++s) {
+      const int buf = s % NBUF;
+      const int far = s + 2 < nsteps ? issue_step(s + 2, (s + 2) % NBUF) : 0;
+      if (active && kStepKeys * s < kmax_w) attend_step(diag_tag, s, lds[buf][0], lds[buf][1]);
+      wait_vm(far);  // this thread's loads for step s + 1 have landed
+      if (s + 1 < nsteps) finish_step(s + 1, (s + 1) % NBUF);
+      lds_barrier();
+    }
+  };
+  int s_diag = (ctx + i0 + 1) / kStepKeys;  // first step with a key past row i0's position
+  s_diag = s_diag < nsteps ? s_diag : nsteps;
+  run_steps(std::false_type{}, 0, s_diag);
+  run_steps(std::true_type{}, s_diag, nsteps);
 
   // ---- normalise and write the wave's rows ---------------------------------
   if (!active) return;
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
-    float lt = l[rt];
-    lt += __shfl_xor(lt, 16, 64);
-    lt += __shfl_xor(lt, 32, 64);
-    const float inv = 1.f / lt;
+    const float inv = 1.f / lsum[rt][0];
     const int tok = i0 + 16 * (rt / HW) + r16;
     if (tok < qlen && qs + tok < total_q) {
       const int64_t rowbase = ((int64_t)(qs + tok) * Hq + h0 + hb + rt % HW) * D;
