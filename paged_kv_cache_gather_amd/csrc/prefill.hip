@@ -114,6 +114,36 @@ __device__ __forceinline__ u32x4 v_chunk_to_f16(u32x4 v, int valid) {
   return r;
 }
 
+// Max over lanes l, l^16, l^32, l^48 (the four lanes that hold one score row),
+// with gfx950's cross-row lane swaps instead of a round trip through LDS.
+__device__ __forceinline__ float row_max4(float x) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+// Byte offset of an LDS location (its address in the LDS aperture).
+__device__ __forceinline__ uint32_t lds_offset(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// 16 bytes per lane from global memory straight into LDS at lds_base + 16 * lane
+// (lds_base wave-uniform).  Issued as inline asm so the compiler's wait-count
+// pass does not see an LDS write in flight (it would then wait for every LDS
+// read to drain before the first use of any); completion is tracked here with
+// explicit vmcnt waits and workgroup barriers.
+__device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(gptr), "s"(lds_base)
+               : "memory", "m0");
+}
+
+// Scheduling-group masks of __builtin_amdgcn_sched_group_barrier.
+constexpr int kSchedMfma = 0x008;
+constexpr int kSchedDsRead = 0x100;
+
 template <typename T, int D, int GW, int OutCode>
 __global__ void __launch_bounds__(kPfThreads, 1)
 prefill_chunk_kernel(void* __restrict__ out, const uint16_t* __restrict__ q,
@@ -133,8 +163,10 @@ prefill_chunk_kernel(void* __restrict__ out, const uint16_t* __restrict__ q,
   constexpr int CPT = TILE / 16;           // 16-byte chunks per tile
   constexpr int NCH = 4 * CPT / kPfThreads;  // staging chunks per thread per step (K and V each)
 
-  constexpr int NBUF = 3;  // steps staged ahead: the current one plus two in flight
+  constexpr int kAhead = 3;           // steps whose loads are in flight while a step is consumed
+  constexpr int NBUF = kAhead + 1;
   __shared__ __attribute__((aligned(16))) unsigned char lds[NBUF][2][4 * TILE];  // [buffer][K, V]
+  static_assert(kPfWaves == 8, "the phase schedule pairs waves w and w + 4 on one SIMD");
 
   const int c = blockIdx.z;
   const int qs = cu_q[c];
@@ -216,48 +248,60 @@ prefill_chunk_kernel(void* __restrict__ out, const uint16_t* __restrict__ q,
   }
 
   // ---- staging of one step's K/V tiles (4 blocks) --------------------------
-  // Direct global -> LDS loads (no registers): chunk ci = tid + kPfThreads k
-  // of the step; a wave's 64 chunks land contiguously at the wave-uniform base.
-  // Returns the number of loads this thread issued (uniform per wave).
-  auto issue_step = [&](int s, int buf) -> int {
-    int64_t blk[NCH];
+  // Chunk ci = tid + kPfThreads k of a step: tile bi = ci / CPT (uniform per
+  // wave), byte offset (ci % CPT) * 16 in it.  Direct global -> LDS loads (no
+  // registers); a wave's 64 chunks land contiguously at a wave-uniform base.
+  // Block ids of step t for this thread's chunks, -1 past the context; read
+  // through the scalar unit a phase before they are used.
+  // The table entry is read unconditionally (index clamped to the last
+  // block) so nothing waits for it until issue_blocks uses it.
+  auto load_blocks = [&](int t, int32_t (&blk)[NCH]) {
 #pragma unroll
     for (int k = 0; k < NCH; ++k) {
-      // the block (uniform per wave) is read through the scalar unit, so the
-      // table loads never wait behind the vector loads already in flight
-      const int lb = 4 * s + __builtin_amdgcn_readfirstlane((tid + kPfThreads * k) / CPT);
-      blk[k] = lb < nblk ? clamp_block(tab[lb], num_blocks) : -1;
+      const int lb = 4 * t + __builtin_amdgcn_readfirstlane((tid + kPfThreads * k) / CPT);
+      blk[k] = tab[lb < nblk ? lb : nblk - 1];
     }
-    int issued = 0;
+  };
+  auto issue_blocks = [&](int t, const int32_t (&blk)[NCH], int buf) {
 #pragma unroll
     for (int k = 0; k < NCH; ++k) {
-      if (blk[k] >= 0) {
+      const int lb = 4 * t + __builtin_amdgcn_readfirstlane((tid + kPfThreads * k) / CPT);
+      if (t < nsteps && lb < nblk) {
         const int off = ((tid + kPfThreads * k) % CPT) * 16;
-        const int64_t base = (blk[k] * Hkv + g) * (int64_t)TILE + off;
+        const int64_t base = (clamp_block(blk[k], num_blocks) * Hkv + g) * (int64_t)TILE + off;
         const int wbase = (kPfThreads * k + 64 * w) * 16;
-        __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)(kpool + base),
-                                         (__attribute__((address_space(3))) void*)&lds[buf][0][wbase], 16, 0, 0);
-        __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)(vpool + base),
-                                         (__attribute__((address_space(3))) void*)&lds[buf][1][wbase], 16, 0, 0);
-        issued += 2;
+        dma16(kpool + base, lds_offset(&lds[buf][0][wbase]));
+        dma16(vpool + base, lds_offset(&lds[buf][1][wbase]));
       }
     }
-    return issued;
   };
-  // After this thread's loads have landed: its V chunks -> fp16, keys at or
-  // past the context zeroed (blocks past the end become zeros), moved to the
-  // swizzled slot of their dim row; odd blocks with their 4-key halves swapped.
-  auto finish_step = [&](int s, int buf) {
+  // Number of loads issue_blocks issues for this thread at step t.
+  auto n_loads = [&](int t) -> int {
+    int n = 0;
+#pragma unroll
+    for (int k = 0; k < NCH; ++k) {
+      const int lb = 4 * t + __builtin_amdgcn_readfirstlane((tid + kPfThreads * k) / CPT);
+      n += (t < nsteps && lb < nblk) ? 2 : 0;
+    }
+    return n;
+  };
+  // This thread's raw V chunks of a staged step (after its loads landed).
+  auto read_raw = [&](int buf, u32x4 (&raw)[NCH]) {
+#pragma unroll
+    for (int k = 0; k < NCH; ++k) raw[k] = *reinterpret_cast<const u32x4*>(&lds[buf][1][(tid + kPfThreads * k) * 16]);
+  };
+  // Raw V chunks -> fp16, keys at or past the context zeroed (blocks past the
+  // end become zeros), written to the swizzled slot of their dim row; odd
+  // blocks with their 4-key halves swapped.  Both halves of a dim row belong
+  // to adjacent lanes of one wave, so the in-place exchange is race-free.
+  auto finish_step = [&](int s, int buf, const u32x4 (&raw)[NCH]) {
 #pragma unroll
     for (int k = 0; k < NCH; ++k) {
       const int ci = tid + kPfThreads * k;
       const int bi = __builtin_amdgcn_readfirstlane(ci / CPT), off = (ci % CPT) * 16;
       const int lb = 4 * s + bi;
-      const u32x4 raw = *reinterpret_cast<const u32x4*>(&lds[buf][1][ci * 16]);
-      // keys 8hf..8hf+7 of dim j; both halves of a dim row belong to
-      // adjacent lanes of one wave, so the in-place exchange is race-free
-      const int j = off / 32, hf = (off % 32) / 16;
-      u32x4 v = lb < nblk ? v_chunk_to_f16<T>(raw, L - (lb * kBlockSize + 8 * hf)) : u32x4{0, 0, 0, 0};
+      const int j = off / 32, hf = (off % 32) / 16;  // dim j, keys 8hf..8hf+7
+      u32x4 v = lb < nblk ? v_chunk_to_f16<T>(raw[k], L - (lb * kBlockSize + 8 * hf)) : u32x4{0, 0, 0, 0};
       if (bi & 1) v = u32x4{v[2], v[3], v[0], v[1]};
       *reinterpret_cast<u32x4*>(&lds[buf][1][bi * TILE + j * 32 + ((hf ^ ((j >> 3) & 1)) * 16)]) = v;
     }
@@ -278,49 +322,53 @@ prefill_chunk_kernel(void* __restrict__ out, const uint16_t* __restrict__ q,
       default: __builtin_amdgcn_s_waitcnt(0xF78); break;
     }
   };
-  static_assert(2 * NCH <= 8, "wait_vm covers at most 8 loads in flight per thread");
+  static_assert(4 * NCH <= 8, "wait_vm covers at most 8 loads in flight per thread");
   // Workgroup barrier for LDS hand-off only: waits for this thread's LDS
   // writes (lgkmcnt) but, unlike __syncthreads(), not for the global->LDS
   // loads still in flight for later steps.
+  // It also closes a phase: no instruction is scheduled across it.
   auto lds_barrier = [] {
+    __builtin_amdgcn_sched_barrier(0);
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt unconstrained
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
   };
 
-  issue_step(0, 0);
-  int ahead = nsteps > 1 ? issue_step(1, 1) : 0;  // loads of the step after the next one to be finished
-  wait_vm(ahead);
-  finish_step(0, 0);
-  lds_barrier();
-
-  // One step of 64 keys for this wave's row tiles; kDiag: the step reaches
-  // the causal diagonal (or the end of the context) and needs the mask.
-  auto attend_step = [&](auto diag_tag, int s, const unsigned char* kl, const unsigned char* vl)
-      __attribute__((always_inline)) {
-    constexpr bool kDiag = decltype(diag_tag)::value;
-    // S^T tiles: st[rt][kt] holds, for row r16, keys 32(kt/2) + key_base[kt%2] + r
-    f32x4 st[RT][4];
+  // ---- the three compute phases of a 64-key step ----------------------------
+  f32x4 st[RT][4];  // S^T tiles: st[rt][kt] holds, for row r16, keys 32(kt/2) + key_base[kt%2] + r
+  u32x4 pb[RT][2];  // fp16 probabilities as B operands of O^T += V^T P^T, per 32-key half
+  // All K operand reads are issued before the MFMAs (one LDS latency per
+  // phase); the MFMAs run dim-slice outermost so 4 x RT accumulation chains
+  // are in flight.
+  auto phase_qk = [&](const unsigned char* kl) {
+    u32x4 ka[4][DC];
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt) {
-      u32x4 ka[DC];
+    for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
       for (int dc = 0; dc < DC; ++dc)
-        ka[dc] = *reinterpret_cast<const u32x4*>(kl + (kt >> 1) * 2 * TILE + k_row_off[kt & 1] +
-                                                 dc * 4 * kBlockSize * 16);
+        ka[kt][dc] = *reinterpret_cast<const u32x4*>(kl + (kt >> 1) * 2 * TILE + k_row_off[kt & 1] +
+                                                     dc * 4 * kBlockSize * 16);
 #pragma unroll
-      for (int rt = 0; rt < RT; ++rt) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-        for (int dc = 0; dc < DC; ++dc) acc = mfma_qk<T>(ka[dc], bq[rt][dc], acc);
-        st[rt][kt] = acc;
-      }
-    }
-    // online softmax, one row per lane.  The reference max m only moves when
-    // a score exceeds it by more than 2^kSlack, so the accumulators are
-    // rescaled rarely; probabilities stay <= 2^kSlack (fine in fp16).
-    u32x4 pb[RT][2];
+      for (int rt = 0; rt < RT; ++rt) st[rt][kt] = mfma_qk<T>(ka[kt][0], bq[rt][0], f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+    for (int dc = 1; dc < DC; ++dc)
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) st[rt][kt] = mfma_qk<T>(ka[kt][dc], bq[rt][dc], st[rt][kt]);
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 4 * DC, 0);
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 4 * DC * RT, 0);
+  };
+  // Online softmax, one row per lane; kDiag: the step reaches the causal
+  // diagonal (or the end of the context) and needs the mask.  The reference
+  // max m only moves when a score exceeds it by more than 2^kSlack, so the
+  // accumulators are rescaled rarely; probabilities stay <= 2^kSlack.
+  auto phase_softmax = [&](auto diag_tag, int s) __attribute__((always_inline)) {
+    constexpr bool kDiag = decltype(diag_tag)::value;
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
       if constexpr (kDiag) {
@@ -338,9 +386,7 @@ prefill_chunk_kernel(void* __restrict__ out, const uint16_t* __restrict__ q,
       for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
         for (int r = 0; r < 4; ++r) mx = fmaxf(mx, st[rt][kt][r]);
-      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      mx *= scale_log2;
+      mx = row_max4(mx) * scale_log2;
       if (__any(mx > m[rt] + kSlack)) {
         const float mn = fmaxf(m[rt], mx);
         const float alpha = __builtin_amdgcn_exp2f(m[rt] - mn);
@@ -363,37 +409,84 @@ prefill_chunk_kernel(void* __restrict__ out, const uint16_t* __restrict__ q,
         pb[rt][kh][3] = pack_f16x2(e[2 * kh + 1][2], e[2 * kh + 1][3]);
       }
     }
-    // O^T += V^T P^T, and the row sums as ones . P^T
+  };
+  // O^T += V^T P^T, and the row sums as ones . P^T; all V operand reads first.
+  auto phase_pv = [&](const unsigned char* vl) {
+    u32x4 va[2][DT];
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+        va[kh][dt] = *reinterpret_cast<const u32x4*>(vl + 2 * kh * TILE + dt * 16 * 32 + v_off);
 #pragma unroll
     for (int kh = 0; kh < 2; ++kh) {
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) lsum[rt] = mfma_pv(ones, pb[rt][kh], lsum[rt]);
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        const u32x4 va = *reinterpret_cast<const u32x4*>(vl + 2 * kh * TILE + dt * 16 * 32 + v_off);
+      for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-        for (int rt = 0; rt < RT; ++rt) o[rt][dt] = mfma_pv(va, pb[rt][kh], o[rt][dt]);
-      }
+        for (int rt = 0; rt < RT; ++rt) o[rt][dt] = mfma_pv(va[kh][dt], pb[rt][kh], o[rt][dt]);
     }
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2 * DT, 0);
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 2 * RT * (DT + 1), 0);
   };
 
+  // ---- schedule ----------------------------------------------------------------
+  // A step is four phases separated by workgroup barriers: QK (MFMA), softmax
+  // (VALU), PV (MFMA), staging (loads for kAhead steps on, V conversion of the
+  // next step).  Waves 4..7 run one phase behind waves 0..3; as waves w and
+  // w + 4 share a SIMD, one of them issues MFMAs while the other runs VALU work.
+  // Every wave passes the same number of barriers (4 per step plus one).
+  //
+  // Hazards, with phase k of the workgroup between barriers k-1 and k (waves
+  // 0..3 run step s's phases at 4s..4s+3, waves 4..7 at 4s+1..4s+4):
+  //  * K(s+1) is read from phase 4s+4 on; each wave waits for its own loads of
+  //    step s+1 in its PV phase (at 4s+2 or 4s+3);
+  //  * converted V(s+1) is written at 4s+3 / 4s+4 and read from 4s+6 on;
+  //  * buffer (s+kAhead) % NBUF, loaded at 4s+3 / 4s+4, last held step s-1,
+  //    whose final read (PV of waves 4..7) is at 4s-1.
+  const int grp = w >> 2;
+  int s_diag = (ctx + i0 + 1) / kStepKeys;  // first step with a key past row i0's position
+  s_diag = s_diag < nsteps ? s_diag : nsteps;
+
+  for (int t = 0; t < kAhead && t < nsteps; ++t) {
+    int32_t blk[NCH];
+    load_blocks(t, blk);
+    issue_blocks(t, blk, t);
+  }
+  {
+    wait_vm(n_loads(1) + n_loads(2));  // step 0's loads have landed
+    u32x4 raw[NCH];
+    read_raw(0, raw);
+    finish_step(0, 0, raw);
+  }
+  lds_barrier();
+  if (grp) lds_barrier();
+
   // Steps before s_diag lie wholly below this wave's first query row and need
-  // no mask; the two ranges run as separate loops (each with the workgroup's
-  // staging and one barrier per step, so waves with different split points
-  // still meet at every barrier).
+  // no mask; the two ranges run as separate loops (one code path each keeps
+  // the register budget).
   auto run_steps = [&](auto diag_tag, int s_begin, int s_end) __attribute__((always_inline)) {
 #pragma unroll 1
     for (int s = s_begin; s < s_end; ++s) {
       const int buf = s % NBUF;
-      const int far = s + 2 < nsteps ? issue_step(s + 2, (s + 2) % NBUF) : 0;
-      if (active && kStepKeys * s < kmax_w) attend_step(diag_tag, s, lds[buf][0], lds[buf][1]);
-      wait_vm(far);  // this thread's loads for step s + 1 have landed
-      if (s + 1 < nsteps) finish_step(s + 1, (s + 1) % NBUF);
+      const bool work = active && kStepKeys * s < kmax_w;
+      if (work) phase_qk(lds[buf][0]);
       lds_barrier();
+      int32_t blk[NCH];
+      load_blocks(s + kAhead, blk);  // in flight during the softmax
+      if (work) phase_softmax(diag_tag, s);
+      lds_barrier();
+      wait_vm(n_loads(s + 2));  // this thread's loads of step s + 1 have landed
+      u32x4 raw[NCH];
+      read_raw((s + 1) % NBUF, raw);
+      if (work) phase_pv(lds[buf][1]);
+      lds_barrier();
+      issue_blocks(s + kAhead, blk, (s + kAhead) % NBUF);
+      if (s + 1 < nsteps) finish_step(s + 1, (s + 1) % NBUF, raw);
+      if (grp == 0 || s + 1 < nsteps) lds_barrier();
     }
   };
-  int s_diag = (ctx + i0 + 1) / kStepKeys;  // first step with a key past row i0's position
-  s_diag = s_diag < nsteps ? s_diag : nsteps;
   run_steps(std::false_type{}, 0, s_diag);
   run_steps(std::true_type{}, s_diag, nsteps);
 
