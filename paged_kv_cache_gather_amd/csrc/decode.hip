@@ -53,11 +53,7 @@ namespace {
 #ifndef PKV_DECODE_MIN_WAVES
 #define PKV_DECODE_MIN_WAVES 2
 #endif
-#ifndef PKV_DECODE_V_BATCH
-#define PKV_DECODE_V_BATCH 1
-#endif
 constexpr int kPart = PKV_DECODE_PART;  // context tokens per partition
-constexpr int kVBatch = PKV_DECODE_V_BATCH;  // V blocks loaded together per wave
 constexpr int kThreads = 256;           // threads per workgroup
 constexpr int kWaves = kThreads / 64;
 
@@ -169,57 +165,48 @@ __device__ __forceinline__ void partition_rows(
     for (int i = 0; i < NI; ++i) o[r][i] = 0.f;
   const int tg = lane % CPR;
   const int nbw = (wn + kBlockSize - 1) / kBlockSize;
-  // V tiles are loaded kVBatch blocks at a time, all loads issued before any
-  // of the batch's math.
+  // V tiles, one block (D * 16 elements) per step of the wave.
+  auto load_v = [&](int bl, u32x4 (&vv)[NI]) {
+    const int64_t blk = clamp_block(tab[wt0 / kBlockSize + bl], num_blocks);
+    const unsigned char* vp = vpool + (blk * Hkv + g) * (int64_t)VTILE + lane * 16;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) vv[i] = ld16(vp + i * 1024);
+  };
+  u32x4 vcur[NI];
 #pragma unroll 1
-  for (int b0 = 0; b0 < nbw; b0 += kVBatch) {
-    u32x4 vv[kVBatch][NI];
+  for (int bl = 0; bl < nbw; ++bl) {
+    load_v(bl, vcur);
+    const int tb = wt0 / kBlockSize + bl;  // partition-local block
+    const int ntok = n - tb * kBlockSize;
+    const float(*pb)[R] = sp + bl * kBlockSize + tg * TPC;
+    auto accumulate = [&](auto masked) {
 #pragma unroll
-    for (int j = 0; j < kVBatch; ++j) {
-      if (b0 + j < nbw) {
-        const int64_t blk = clamp_block(tab[wt0 / kBlockSize + b0 + j], num_blocks);
-        const unsigned char* vp = vpool + (blk * Hkv + g) * (int64_t)VTILE + lane * 16;
+      for (int tt = 0; tt < TPC; ++tt) {
+        float pv[R];
 #pragma unroll
-        for (int i = 0; i < NI; ++i) vv[j][i] = ld16(vp + i * 1024);
-      }
-    }
+        for (int r = 0; r < R; ++r) pv[r] = pb[tt][r];
 #pragma unroll
-    for (int j = 0; j < kVBatch; ++j) {
-      if (b0 + j < nbw) {
-        const int bl = b0 + j;
-        const int tb = wt0 / kBlockSize + bl;  // partition-local block
-        const int ntok = n - tb * kBlockSize;
-        const float(*pb)[R] = sp + bl * kBlockSize + tg * TPC;
-        auto accumulate = [&](auto masked) {
-#pragma unroll
-          for (int tt = 0; tt < TPC; ++tt) {
-            float pv[R];
-#pragma unroll
-            for (int r = 0; r < R; ++r) pv[r] = pb[tt][r];
-#pragma unroll
-            for (int i = 0; i < NI; ++i) {
-              float x;
-              if constexpr (ES == 2) {
-                float lo, hi;
-                unpack2<T>(vv[j][i][tt >> 1], lo, hi);
-                x = (tt & 1) ? hi : lo;
-              } else {
-                x = __uint_as_float(vv[j][i][tt]);
-              }
-              if constexpr (decltype(masked)::value) {
-                x = tg * TPC + tt < ntok ? x : 0.f;  // slots past the context may hold anything
-              }
-#pragma unroll
-              for (int r = 0; r < R; ++r) o[r][i] = fmaf(pv[r], x, o[r][i]);
-            }
+        for (int i = 0; i < NI; ++i) {
+          float x;
+          if constexpr (ES == 2) {
+            float lo, hi;
+            unpack2<T>(vcur[i][tt >> 1], lo, hi);
+            x = (tt & 1) ? hi : lo;
+          } else {
+            x = __uint_as_float(vcur[i][tt]);
           }
-        };
-        if (ntok >= kBlockSize)
-          accumulate(std::false_type{});
-        else
-          accumulate(std::true_type{});
+          if constexpr (decltype(masked)::value) {
+            x = tg * TPC + tt < ntok ? x : 0.f;  // slots past the context may hold anything
+          }
+#pragma unroll
+          for (int r = 0; r < R; ++r) o[r][i] = fmaf(pv[r], x, o[r][i]);
+        }
       }
-    }
+    };
+    if (ntok >= kBlockSize)
+      accumulate(std::false_type{});
+    else
+      accumulate(std::true_type{});
   }
   // add the CPR lanes that share a dim
 #pragma unroll
@@ -273,6 +260,317 @@ __device__ __forceinline__ void partition_rows(
   }
 }
 
+// ---- partitions shared by neighbouring sequences ----------------------------
+// Sequences forked from a common prefix name the same ref-counted physical
+// blocks for it ("Memory sharing" with reference counts, vLLM Serving deep
+// dive).  When neighbours in the batch name the same 32 blocks for a full
+// partition p, one workgroup reads those K/V bytes once and serves all of
+// them: with k sequences the partition is a (k G) x 512 x D contraction, done
+// on MFMA by decode_shared_kernel.  Runs are formed inside aligned windows of
+// KM = kRunRows / G sequences, so membership is decided from neighbours:
+// s joins the run of s - 1 when both fill p, name the same blocks for it and
+// s is not at a window start.  Runs of one sequence stay with the
+// per-sequence kernel.
+constexpr int kRunRows = 32;                     // query rows of a shared run (two 16-row MFMA tiles)
+constexpr int kPartBlocks = kPart / kBlockSize;  // blocks per partition
+static_assert(kPartBlocks <= 64, "one wave compares a partition's block ids");
+
+// Do sequences a and b both fill partition p and name the same blocks for it?
+// (Uniform per wave.)
+__device__ __forceinline__ bool same_partition(const int32_t* __restrict__ tables, int max_blocks,
+                                               const int32_t* __restrict__ lens, int max_context_len, int a,
+                                               int b, int p) {
+  const int need = (p + 1) * kPart;
+  if (clamp_len(lens[a], max_context_len) < need || clamp_len(lens[b], max_context_len) < need) return false;
+  const int lane = threadIdx.x & 63;
+  bool eq = true;
+  if (lane < kPartBlocks)
+    eq = tables[(int64_t)a * max_blocks + p * kPartBlocks + lane] ==
+         tables[(int64_t)b * max_blocks + p * kPartBlocks + lane];
+  return __all(eq);
+}
+
+// Does s join the run of s - 1 for partition p?
+template <int KM>
+__device__ __forceinline__ bool joins_prev(const int32_t* __restrict__ tables, int max_blocks,
+                                           const int32_t* __restrict__ lens, int max_context_len, int s,
+                                           int p) {
+  return s % KM != 0 && same_partition(tables, max_blocks, lens, max_context_len, s - 1, s, p);
+}
+
+// Is (s, p) served by a shared workgroup, i.e. is s in a run of two or more?
+template <typename T, int G>
+__device__ __forceinline__ bool in_shared_run(const int32_t* __restrict__ tables, int max_blocks,
+                                              const int32_t* __restrict__ lens, int B, int max_context_len,
+                                              int s, int p) {
+  if constexpr (T::kBytes != 2) {
+    return false;  // fp32 K/V: no MFMA path
+  } else {
+    constexpr int KM = kRunRows / G;
+    if ((p + 1) * kPart > clamp_len(lens[s], max_context_len)) return false;
+    return joins_prev<KM>(tables, max_blocks, lens, max_context_len, s, p) ||
+           (s + 1 < B && joins_prev<KM>(tables, max_blocks, lens, max_context_len, s + 1, p));
+  }
+}
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+
+template <typename T>
+__device__ __forceinline__ f32x4 mfma_qk(u32x4 a, u32x4 b, f32x4 c) {
+  if constexpr (T::kCode == PKV_BF16)
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a),
+                                                  __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma_f16(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a),
+                                                __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
+}
+// 8 bf16 / f16 values -> 8 fp16 (bf16: round toward zero, exact for values
+// fp16 holds, saturating beyond its range).
+template <typename T>
+__device__ __forceinline__ u32x4 to_f16x8(u32x4 v) {
+  if constexpr (T::kCode == PKV_BF16) {
+    u32x4 r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      r[i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(bf16lo(v[i]), bf16hi(v[i])));
+    return r;
+  } else {
+    return v;
+  }
+}
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2v_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+  const f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2v_t));
+}
+// Max / sum over lanes l, l^16, l^32, l^48 (the lanes holding one MFMA row).
+__device__ __forceinline__ float rows4_max(float x) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float rows4_sum(float x) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+template <int D>
+struct SharedLds {
+  float o[kWaves][kRunRows][D];  // the waves' unnormalised outputs
+  float ml[kWaves][kRunRows][2];  // and (max, sum) per row
+};
+
+// One run: sequences s .. s + k - 1 share partition p (2 <= k, k G <= 32 rows;
+// row r = member r / G, head r % G).  K/V of the partition's 32 blocks are
+// read once.  Each wave takes 128 tokens (8 blocks) whole:
+//  * S^T = K Q^T on MFMA 16x16x32 with K rows loaded from the pool straight
+//    into operand layout: in each pair of blocks, row m = 4a + r of score
+//    tile `sub` is the pair's key 8a + 4 sub + r, so the lanes of group a own
+//    keys 8a..8a+7 (one 16-byte V chunk per dim) across the two tiles;
+//  * exact softmax over the wave's 128 keys (base 2), probabilities in fp16;
+//  * O^T += V^T P^T with V chunks loaded into operand layout and converted to
+//    fp16; the waves' (max, sum, o) are merged through LDS and written as each
+//    member's partition result.
+template <typename T, int D, int G, int OutCode>
+__device__ __forceinline__ void shared_run(int s, int k, int g, int p, SharedLds<D>& sh, void* __restrict__ out,
+                                           float* __restrict__ ws_o, float* __restrict__ ws_ml,
+                                           const typename T::bits* __restrict__ q,
+                                           const unsigned char* __restrict__ kpool,
+                                           const unsigned char* __restrict__ vpool,
+                                           const int32_t* __restrict__ tables, int max_blocks,
+                                           const int32_t* __restrict__ lens, int Hkv, int64_t num_blocks,
+                                           int max_context_len, float scale_log2, int max_parts) {
+  constexpr int DC = D / 32;   // 32-dim slices of the score contraction
+  constexpr int DT = D / 16;   // 16-dim tiles of the output
+  constexpr int RT = kRunRows / 16;
+  constexpr int TILE = D * kBlockSize * 2;  // bytes of one (block, head) tile
+  constexpr int WB = kPartBlocks / kWaves;  // blocks per wave
+  static_assert(WB % 2 == 0, "waves take whole block pairs");
+  const int Hq = Hkv * G;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int q4 = lane >> 4, r16 = lane & 15;
+
+  // query rows as B operands: lane (q4, r16) holds row 16 rt + r16, dims 32 dc + 8 q4 ..
+  u32x4 bq[RT][DC];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    const int row = 16 * rt + r16;
+    const int mi = row / G < k ? row / G : 0;
+    const typename T::bits* qp = q + ((int64_t)(s + mi) * Hq + g * G + row % G) * D + 8 * q4;
+#pragma unroll
+    for (int dc = 0; dc < DC; ++dc) bq[rt][dc] = ld16(qp + 32 * dc);
+  }
+
+  const int32_t* tab = tables + (int64_t)s * max_blocks + p * kPartBlocks + w * WB;
+  // this lane's K row inside a block pair for score tile `sub`
+  const int k_half = r16 >> 3;                          // which block of the pair
+  const int k_tok = 8 * ((r16 >> 2) & 1) + (r16 & 3);  // token, + 4 sub
+  // all of the wave's K operand loads are issued before the first MFMA
+  u32x4 ka[WB][DC];  // tile 2 kp + sub
+#pragma unroll
+  for (int kp = 0; kp < WB / 2; ++kp) {
+    const int64_t kb = clamp_block(tab[2 * kp + k_half], num_blocks);
+    const unsigned char* kr = kpool + ((kb * Hkv + g) * (D / 8) + q4) * (kBlockSize * 16) + k_tok * 16;
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+      for (int dc = 0; dc < DC; ++dc) ka[2 * kp + sub][dc] = ld16(kr + (4 * sub + dc * 4 * kBlockSize) * 16);
+  }
+  f32x4 st[WB][RT];
+#pragma unroll
+  for (int kt = 0; kt < WB; ++kt)
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int dc = 0; dc < DC; ++dc) acc = mfma_qk<T>(ka[kt][dc], bq[rt][dc], acc);
+      st[kt][rt] = acc;
+    }
+  // the V operand loads are issued next, ahead of the softmax
+  u32x4 vraw[WB / 2][DT];
+#pragma unroll
+  for (int kp = 0; kp < WB / 2; ++kp) {
+    const int64_t vb = clamp_block(tab[2 * kp + (q4 >> 1)], num_blocks);
+    const unsigned char* vr = vpool + (vb * Hkv + g) * (int64_t)TILE + r16 * 32 + (q4 & 1) * 16;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) vraw[kp][dt] = ld16(vr + dt * 16 * 32);
+  }
+  // exact softmax over the wave's keys, per row
+  float m[RT], l[RT];
+  u32x4 pb[WB / 2][RT];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kt = 0; kt < WB; ++kt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        st[kt][rt][r] *= scale_log2;
+        mx = fmaxf(mx, st[kt][rt][r]);
+      }
+    m[rt] = rows4_max(mx);
+    float ls = 0.f;
+#pragma unroll
+    for (int kt = 0; kt < WB; ++kt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        st[kt][rt][r] = __builtin_amdgcn_exp2f(st[kt][rt][r] - m[rt]);
+        ls += st[kt][rt][r];
+      }
+    l[rt] = rows4_sum(ls);
+#pragma unroll
+    for (int kp = 0; kp < WB / 2; ++kp)
+      pb[kp][rt] = u32x4{pack_f16x2(st[2 * kp][rt][0], st[2 * kp][rt][1]),
+                         pack_f16x2(st[2 * kp][rt][2], st[2 * kp][rt][3]),
+                         pack_f16x2(st[2 * kp + 1][rt][0], st[2 * kp + 1][rt][1]),
+                         pack_f16x2(st[2 * kp + 1][rt][2], st[2 * kp + 1][rt][3])};
+  }
+  // O^T += V^T P^T: lane (q4, r16) holds dim 16 dt + r16, keys 8 q4 .. 8 q4 + 7 of the pair
+  f32x4 o[RT][DT];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) o[rt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int kp = 0; kp < WB / 2; ++kp)
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      const u32x4 va = to_f16x8<T>(vraw[kp][dt]);
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) o[rt][dt] = mfma_f16(va, pb[kp][rt], o[rt][dt]);
+    }
+  // merge the waves: lane (q4, r16) holds o^T[dim 16 dt + 4 q4 + r][row 16 rt + r16]
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sh.o[w][16 * rt + r16][16 * dt + 4 * q4 + r] = o[rt][dt][r];
+    if (q4 == 0) {
+      sh.ml[w][16 * rt + r16][0] = m[rt];
+      sh.ml[w][16 * rt + r16][1] = l[rt];
+    }
+  }
+  __syncthreads();
+  const int rows = k * G;
+  for (int i = tid; i < rows * D; i += kThreads) {
+    const int row = i / D, j = i % D;
+    float Mx = sh.ml[0][row][0];
+#pragma unroll
+    for (int x = 1; x < kWaves; ++x) Mx = fmaxf(Mx, sh.ml[x][row][0]);
+    float acc = 0.f, den = 0.f;
+#pragma unroll
+    for (int x = 0; x < kWaves; ++x) {
+      const float f = __builtin_amdgcn_exp2f(sh.ml[x][row][0] - Mx);
+      acc = fmaf(f, sh.o[x][row][j], acc);
+      den = fmaf(f, sh.ml[x][row][1], den);
+    }
+    const int seq = s + row / G;
+    const int64_t orow = (int64_t)seq * Hq + g * G + row % G;
+    const int nparts = (clamp_len(lens[seq], max_context_len) + kPart - 1) / kPart;
+    if (nparts == 1) {
+      store_out<OutCode>(out, orow * D + j, acc / den);
+    } else {
+      ws_o[(orow * max_parts + p) * D + j] = acc;
+      if (j == 0) {
+        ws_ml[(orow * max_parts + p) * 2 + 0] = Mx;
+        ws_ml[(orow * max_parts + p) * 2 + 1] = den;
+      }
+    }
+  }
+  __syncthreads();  // the LDS is reused by the window's next run
+}
+
+// Grid (KV head, run window, partition): finds the runs of the window's
+// KM = kRunRows / G sequences for partition p and serves each.
+template <typename T, int D, int G, int OutCode>
+__global__ void __launch_bounds__(kThreads, 2)
+decode_shared_kernel(void* __restrict__ out, float* __restrict__ ws_o, float* __restrict__ ws_ml,
+                     const typename T::bits* __restrict__ q, const unsigned char* __restrict__ kpool,
+                     const unsigned char* __restrict__ vpool, const int32_t* __restrict__ tables,
+                     int max_blocks, const int32_t* __restrict__ lens, int B, int Hkv, int64_t num_blocks,
+                     int max_context_len, float scale_log2, int max_parts) {
+  if constexpr (T::kBytes != 2) {
+    return;
+  } else {
+    constexpr int KM = kRunRows / G;
+    static_assert(KM <= 32, "run window fits a 32-bit mask");
+    __shared__ __attribute__((aligned(16))) SharedLds<D> sh;
+    __shared__ uint32_t joins;
+    const int g = blockIdx.x, win = blockIdx.y, p = blockIdx.z;
+    const int s_first = win * KM;
+    if (s_first >= B) return;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    if (tid == 0) joins = 0u;
+    __syncthreads();
+    for (int i = 1 + w; i < KM && s_first + i < B; i += kWaves) {
+      const bool j = joins_prev<KM>(tables, max_blocks, lens, max_context_len, s_first + i, p);
+      if (j && lane == 0) atomicOr(&joins, 1u << i);
+    }
+    __syncthreads();
+    const uint32_t jm = joins;
+    // a run: a member that does not join its predecessor, then those that do
+    for (int s0 = 0; s0 + 1 < KM; ++s0) {
+      if (!((jm >> (s0 + 1)) & 1u) || ((jm >> s0) & 1u)) continue;
+      int k = 2;
+      while (s0 + k < KM && ((jm >> (s0 + k)) & 1u)) ++k;
+      shared_run<T, D, G, OutCode>(s_first + s0, k, g, p, sh, out, ws_o, ws_ml, q, kpool, vpool, tables,
+                                   max_blocks, lens, Hkv, num_blocks, max_context_len, scale_log2, max_parts);
+    }
+  }
+}
+
 template <typename T, int D, int G, int OutCode>
 __global__ void __launch_bounds__(kThreads, PKV_DECODE_MIN_WAVES)
 decode_partition_kernel(void* __restrict__ out, float* __restrict__ ws_o, float* __restrict__ ws_ml,
@@ -298,6 +596,7 @@ decode_partition_kernel(void* __restrict__ out, float* __restrict__ ws_o, float*
       store_out<OutCode>(out, ((int64_t)s * Hq + g * G) * D + i, 0.f);
     return;
   }
+  if (in_shared_run<T, G>(tables, max_blocks, lens, gridDim.y, max_context_len, s, p)) return;
   const int t0 = p * kPart;
   const int n = (L - t0) < kPart ? (L - t0) : kPart;  // tokens in this partition
   const int32_t* tab = tables + (int64_t)s * max_blocks + t0 / kBlockSize;
@@ -352,10 +651,19 @@ struct DecodeArgs {
   float scale_log2;
   int max_parts;
   hipStream_t stream;
+  hipStream_t side_stream;  // runs the shared-partition kernel alongside, or null
 };
 
 template <typename T, int D, int G, int OutCode>
 void launch_decode(const DecodeArgs& a, bool partitions, bool reduce) {
+  if (partitions && T::kBytes == 2) {
+    constexpr int KM = kRunRows / G;
+    hipLaunchKernelGGL((decode_shared_kernel<T, D, G, OutCode>),
+                       dim3((unsigned)a.Hkv, (unsigned)((a.B + KM - 1) / KM), (unsigned)a.max_parts),
+                       dim3(kThreads), 0, a.side_stream ? a.side_stream : a.stream, a.out, a.ws_o, a.ws_ml,
+                       (const typename T::bits*)a.q, a.kpool, a.vpool, a.tables, a.max_blocks, a.lens, a.B,
+                       a.Hkv, a.num_blocks, a.max_context_len, a.scale_log2, a.max_parts);
+  }
   if (partitions)
     hipLaunchKernelGGL((decode_partition_kernel<T, D, G, OutCode>),
                        dim3((unsigned)a.Hkv, (unsigned)a.B, (unsigned)a.max_parts), dim3(kThreads), 0,
@@ -402,6 +710,42 @@ extern "C" int64_t paged_attention_decode_workspace_bytes(int32_t num_seqs, int3
   if (parts <= 1) return 0;
   return (int64_t)num_seqs * n_q_heads * parts * (head_dim + 2) * (int64_t)sizeof(float);
 }
+
+// A helper stream per (host thread, device) on which the shared-partition
+// kernel runs concurrently with the per-sequence kernel.  It is forked from
+// and joined back to the caller's stream with events, so everything ordered
+// on the caller's stream stays ordered.  Created on first use, kept for the
+// life of the thread; null when the caller's stream is not on the current
+// device or creation fails (both kernels then run on the caller's stream).
+namespace {
+struct SideStream {
+  hipStream_t stream = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+  bool failed = false;
+};
+SideStream* side_stream_for(hipStream_t user) {
+  constexpr int kMaxDevices = 64;
+  thread_local SideStream cache[kMaxDevices];
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  if (user) {
+    int sdev = -1;
+    if (hipStreamGetDevice(user, &sdev) != hipSuccess || sdev != dev) return nullptr;
+  }
+  SideStream& ss = cache[dev];
+  if (ss.failed) return nullptr;
+  if (!ss.stream) {
+    if (hipStreamCreateWithFlags(&ss.stream, hipStreamNonBlocking) != hipSuccess ||
+        hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&ss.join, hipEventDisableTiming) != hipSuccess) {
+      ss.failed = true;
+      (void)hipGetLastError();
+      return nullptr;
+    }
+  }
+  return &ss;
+}
+}  // namespace
 
 static int decode_impl(const char* fn, bool pa, bool re, void* out, int32_t out_dtype, const void* q,
                        const void* k_pool, const void* v_pool, const int32_t* block_tables,
@@ -454,18 +798,31 @@ static int decode_impl(const char* fn, bool pa, bool re, void* out, int32_t out_
   a.scale_log2 = (float)((double)scale * 1.4426950408889634);
   a.max_parts = max_parts;
   a.stream = (hipStream_t)stream;
-  int rc = -1;
-  switch (kv_dtype) {
-    case PKV_F32: rc = pkv::dispatch_d<pkv::F32, PKV_F32>(a, head_dim, G, pa, re); break;
-    case PKV_F16:
-      rc = out_dtype == PKV_F32 ? pkv::dispatch_d<pkv::F16, PKV_F32>(a, head_dim, G, pa, re)
-                                : pkv::dispatch_d<pkv::F16, PKV_F16>(a, head_dim, G, pa, re);
-      break;
-    case PKV_BF16:
-      rc = out_dtype == PKV_F32 ? pkv::dispatch_d<pkv::BF16, PKV_F32>(a, head_dim, G, pa, re)
-                                : pkv::dispatch_d<pkv::BF16, PKV_BF16>(a, head_dim, G, pa, re);
-      break;
+  a.side_stream = nullptr;
+  SideStream* side = (pa && kv_dtype != PKV_F32) ? side_stream_for(a.stream) : nullptr;
+  if (side) {
+    if (hipEventRecord(side->fork, a.stream) != hipSuccess ||
+        hipStreamWaitEvent(side->stream, side->fork, 0) != hipSuccess)
+      return fail(PKV_EHIP, F + ": fork to the helper stream failed");
+    a.side_stream = side->stream;
   }
+  auto dispatch = [&](bool do_pa, bool do_re) -> int {
+    switch (kv_dtype) {
+      case PKV_F32: return pkv::dispatch_d<pkv::F32, PKV_F32>(a, head_dim, G, do_pa, do_re);
+      case PKV_F16:
+        return out_dtype == PKV_F32 ? pkv::dispatch_d<pkv::F16, PKV_F32>(a, head_dim, G, do_pa, do_re)
+                                    : pkv::dispatch_d<pkv::F16, PKV_F16>(a, head_dim, G, do_pa, do_re);
+      case PKV_BF16:
+        return out_dtype == PKV_F32 ? pkv::dispatch_d<pkv::BF16, PKV_F32>(a, head_dim, G, do_pa, do_re)
+                                    : pkv::dispatch_d<pkv::BF16, PKV_BF16>(a, head_dim, G, do_pa, do_re);
+    }
+    return -1;
+  };
+  int rc = pa ? dispatch(true, false) : 0;
+  if (side && (hipEventRecord(side->join, side->stream) != hipSuccess ||
+               hipStreamWaitEvent(a.stream, side->join, 0) != hipSuccess))
+    return fail(PKV_EHIP, F + ": join from the helper stream failed");
+  if (!rc && re) rc = dispatch(false, true);  // after the join: the reduce reads both kernels' partials
   if (rc) return fail(PKV_EUNSUPPORTED, F + ": configuration not built");
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(PKV_EHIP, std::string(F + ": ") + hipGetErrorString(e));

@@ -84,14 +84,20 @@ SHARED_RUNS = [
     ("runs_mha", 8, 8, 128, "f16", [1300, 1300, 1030, 600], [1200, 1200, 1029, 0], [0, 0, 0, -1]),
     ("runs_gqa8", 32, 4, 64, "f16", [1100, 1100, 1100], [1024, 1024, 1024], [0, 0, 0]),
     ("runs_gqa2", 8, 4, 128, "bf16", [2100] * 9, [2048] * 9, [0] * 9),
+    # a group of six over sequences 5..10 straddles the 8-sequence window of
+    # G = 4 (two runs of three); its shared prefix ends inside a block
+    ("runs_cross_window", 32, 8, 128, "bf16", [600] * 5 + [1100, 1500, 1030, 2049, 1100, 1200] + [700],
+     [0] * 5 + [1029] * 6 + [0], [-1] * 5 + [0] * 6 + [-1]),
+    ("runs_f16_d64", 16, 4, 64, "f16", [1030, 1030, 1536, 3000, 520], [1025, 1025, 1025, 1025, 0],
+     [0, 0, 0, 0, -1]),
 ]
 
 
 @pytest.mark.parametrize("name,Hq,Hkv,d,dtype,lens,plen,pgroup", SHARED_RUNS, ids=[c[0] for c in SHARED_RUNS])
 def test_decode_shared_partition_runs(name, Hq, Hkv, d, dtype, lens, plen, pgroup):
     # neighbours whose full 512-token partitions use the same blocks are served
-    # by one workgroup; runs cross the serving-group boundary, some members
-    # end exactly at a partition edge
+    # by one MFMA workgroup; runs cross the 32 / G-sequence run window, some
+    # members end exactly at a partition edge
     w = synth.custom_workload(name, Hq, Hkv, d, dtype, 4096, seed=13, decode_lens=lens, prefix_len=plen,
                               prefix_group=pgroup)
     print(f"decode {name}", flush=True)
