@@ -226,12 +226,8 @@ int64_t paged_attention_decode_workspace_bytes(int32_t num_seqs, int32_t n_q_hea
  * Shared blocks: when neighbouring sequences in the batch name the same
  * blocks for a whole partition (sequences forked from one prefix: "Memory
  * sharing", vLLM Serving deep dive), one workgroup reads that partition once
- * for all of them (up to 32 query rows, on MFMA; f16/bf16 K/V only).  That
- * pass runs on a helper stream the library owns (one per host thread and
- * device, default priority), forked from `stream` and joined back to it with
- * events before the call returns its work to `stream`; ordering on `stream`
- * is unchanged.  If `stream` is not on the current device the helper stream
- * is not used.
+ * for all of them (up to 32 query rows, on MFMA; f16/bf16 K/V only): a
+ * third kernel, queued on `stream` before the per-sequence partition pass.
  *   out           device [num_seqs][n_q_heads][head_dim], out_dtype
  *                 (PKV_F32, or the KV dtype).
  *   q             device [num_seqs][n_q_heads][head_dim], kv_dtype.

@@ -280,6 +280,11 @@ static_assert(kPartBlocks <= 64, "one wave compares a partition's block ids");
 __device__ __forceinline__ bool same_partition(const int32_t* __restrict__ tables, int max_blocks,
                                                const int32_t* __restrict__ lens, int max_context_len, int a,
                                                int b, int p) {
+  // first block ids, then lengths, then all the partition's ids (the reads
+  // stay in the table: p * kPartBlocks < max_blocks whenever the caller's
+  // sequence fills partition p)
+  const int64_t fa = (int64_t)a * max_blocks + p * kPartBlocks, fb = (int64_t)b * max_blocks + p * kPartBlocks;
+  if (tables[fa] != tables[fb]) return false;
   const int need = (p + 1) * kPart;
   if (clamp_len(lens[a], max_context_len) < need || clamp_len(lens[b], max_context_len) < need) return false;
   const int lane = threadIdx.x & 63;
@@ -553,9 +558,25 @@ decode_shared_kernel(void* __restrict__ out, float* __restrict__ ws_o, float* __
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     if (tid == 0) joins = 0u;
+    // candidates, one lane per member: both fill p and their first block ids
+    // for p agree (one round of loads); then the full comparison for those
+    uint32_t cand = 0;
+    {
+      const int i = lane, a = s_first + i;
+      bool c = false;
+      if (i >= 1 && i < KM && a < B) {
+        const int need = (p + 1) * kPart;
+        c = clamp_len(lens[a - 1], max_context_len) >= need && clamp_len(lens[a], max_context_len) >= need &&
+            tables[(int64_t)(a - 1) * max_blocks + p * kPartBlocks] ==
+                tables[(int64_t)a * max_blocks + p * kPartBlocks];
+      }
+      cand = (uint32_t)__ballot(c);
+    }
     __syncthreads();
-    for (int i = 1 + w; i < KM && s_first + i < B; i += kWaves) {
-      const bool j = joins_prev<KM>(tables, max_blocks, lens, max_context_len, s_first + i, p);
+    if (cand == 0) return;
+    for (int i = 1 + w; i < KM; i += kWaves) {
+      if (!((cand >> i) & 1u)) continue;
+      const bool j = same_partition(tables, max_blocks, lens, max_context_len, s_first + i - 1, s_first + i, p);
       if (j && lane == 0) atomicOr(&joins, 1u << i);
     }
     __syncthreads();
@@ -651,7 +672,6 @@ struct DecodeArgs {
   float scale_log2;
   int max_parts;
   hipStream_t stream;
-  hipStream_t side_stream;  // runs the shared-partition kernel alongside, or null
 };
 
 template <typename T, int D, int G, int OutCode>
@@ -660,7 +680,7 @@ void launch_decode(const DecodeArgs& a, bool partitions, bool reduce) {
     constexpr int KM = kRunRows / G;
     hipLaunchKernelGGL((decode_shared_kernel<T, D, G, OutCode>),
                        dim3((unsigned)a.Hkv, (unsigned)((a.B + KM - 1) / KM), (unsigned)a.max_parts),
-                       dim3(kThreads), 0, a.side_stream ? a.side_stream : a.stream, a.out, a.ws_o, a.ws_ml,
+                       dim3(kThreads), 0, a.stream, a.out, a.ws_o, a.ws_ml,
                        (const typename T::bits*)a.q, a.kpool, a.vpool, a.tables, a.max_blocks, a.lens, a.B,
                        a.Hkv, a.num_blocks, a.max_context_len, a.scale_log2, a.max_parts);
   }
@@ -710,42 +730,6 @@ extern "C" int64_t paged_attention_decode_workspace_bytes(int32_t num_seqs, int3
   if (parts <= 1) return 0;
   return (int64_t)num_seqs * n_q_heads * parts * (head_dim + 2) * (int64_t)sizeof(float);
 }
-
-// A helper stream per (host thread, device) on which the shared-partition
-// kernel runs concurrently with the per-sequence kernel.  It is forked from
-// and joined back to the caller's stream with events, so everything ordered
-// on the caller's stream stays ordered.  Created on first use, kept for the
-// life of the thread; null when the caller's stream is not on the current
-// device or creation fails (both kernels then run on the caller's stream).
-namespace {
-struct SideStream {
-  hipStream_t stream = nullptr;
-  hipEvent_t fork = nullptr, join = nullptr;
-  bool failed = false;
-};
-SideStream* side_stream_for(hipStream_t user) {
-  constexpr int kMaxDevices = 64;
-  thread_local SideStream cache[kMaxDevices];
-  int dev = -1;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
-  if (user) {
-    int sdev = -1;
-    if (hipStreamGetDevice(user, &sdev) != hipSuccess || sdev != dev) return nullptr;
-  }
-  SideStream& ss = cache[dev];
-  if (ss.failed) return nullptr;
-  if (!ss.stream) {
-    if (hipStreamCreateWithFlags(&ss.stream, hipStreamNonBlocking) != hipSuccess ||
-        hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming) != hipSuccess ||
-        hipEventCreateWithFlags(&ss.join, hipEventDisableTiming) != hipSuccess) {
-      ss.failed = true;
-      (void)hipGetLastError();
-      return nullptr;
-    }
-  }
-  return &ss;
-}
-}  // namespace
 
 static int decode_impl(const char* fn, bool pa, bool re, void* out, int32_t out_dtype, const void* q,
                        const void* k_pool, const void* v_pool, const int32_t* block_tables,
@@ -798,14 +782,6 @@ static int decode_impl(const char* fn, bool pa, bool re, void* out, int32_t out_
   a.scale_log2 = (float)((double)scale * 1.4426950408889634);
   a.max_parts = max_parts;
   a.stream = (hipStream_t)stream;
-  a.side_stream = nullptr;
-  SideStream* side = (pa && kv_dtype != PKV_F32) ? side_stream_for(a.stream) : nullptr;
-  if (side) {
-    if (hipEventRecord(side->fork, a.stream) != hipSuccess ||
-        hipStreamWaitEvent(side->stream, side->fork, 0) != hipSuccess)
-      return fail(PKV_EHIP, F + ": fork to the helper stream failed");
-    a.side_stream = side->stream;
-  }
   auto dispatch = [&](bool do_pa, bool do_re) -> int {
     switch (kv_dtype) {
       case PKV_F32: return pkv::dispatch_d<pkv::F32, PKV_F32>(a, head_dim, G, do_pa, do_re);
@@ -818,11 +794,7 @@ static int decode_impl(const char* fn, bool pa, bool re, void* out, int32_t out_
     }
     return -1;
   };
-  int rc = pa ? dispatch(true, false) : 0;
-  if (side && (hipEventRecord(side->join, side->stream) != hipSuccess ||
-               hipStreamWaitEvent(a.stream, side->join, 0) != hipSuccess))
-    return fail(PKV_EHIP, F + ": join from the helper stream failed");
-  if (!rc && re) rc = dispatch(false, true);  // after the join: the reduce reads both kernels' partials
+  const int rc = dispatch(pa, re);
   if (rc) return fail(PKV_EUNSUPPORTED, F + ": configuration not built");
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(PKV_EHIP, std::string(F + ": ") + hipGetErrorString(e));
