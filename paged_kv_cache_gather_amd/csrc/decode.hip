@@ -9,7 +9,11 @@
 // against the full K and V is in "The decode stage, and how to spot the
 // waste", Life of a prompt).
 //
-// How (gfx950):
+// How (gfx950): three kernels per step on one stream.  decode_shared_kernel
+// first serves the partitions that neighbouring sequences share (see the
+// section on shared partitions below); decode_partition_kernel serves the
+// rest; decode_reduce_kernel merges split-context partials.
+// decode_partition_kernel:
 //  * Work unit = (KV head g, sequence s, partition p of 512 context tokens),
 //    one 256-thread workgroup (4 wave64s).  All G query heads that share the
 //    KV head are handled together, so every K/V byte is read once per step.

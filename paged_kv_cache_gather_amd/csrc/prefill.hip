@@ -12,30 +12,31 @@
 // reads paged blocks", vLLM Serving deep dive).
 //
 // How (gfx950, MFMA 16x16x32):
-//  * Workgroup = 4 wave64s over (KV head, 64 query tokens, chunk) for a GQA
-//    group of 4 query heads (or 128/256 tokens when fewer heads share a KV
-//    head).  Each wave owns 4 row tiles of 16 query rows (token tile x head):
-//    the heads of one KV head are stacked so every K/V tile staged in LDS
-//    serves all of them.
-//  * Keys advance 64 at a time (4 blocks).  The workgroup stages the step's
-//    K and V tiles in LDS with direct global->LDS loads (three buffers: the
-//    loads for two steps ahead are issued before the current step's math and
-//    take no registers).  K tiles keep the pool layout; each thread then rewrites the
-//    V chunks it loaded as fp16 (exact for bf16 values in fp16's normal range)
-//    because the P.V product runs in fp16 (see below).
+//  * Workgroup = 8 wave64s over (KV head, 64 query tokens, chunk) for a GQA
+//    group of 4 query heads (more tokens when fewer heads share a KV head).
+//    Each wave owns 2 row tiles of 16 query rows (token tile x head): the
+//    heads of one KV head are stacked so every K/V tile staged in LDS serves
+//    all of them.
+//  * Keys advance 64 at a time (4 blocks).  The step's K and V tiles are
+//    staged in LDS with direct global->LDS loads issued three steps ahead
+//    (four buffers, no registers); each thread rewrites the V chunks it loaded
+//    as fp16, because the P.V product runs in fp16 (see below).
 //  * Scores are formed transposed, S^T = K Q^T (A = K tile from LDS, B = the
 //    wave's Q rows kept in registers), so each lane owns one query row: the
-//    online softmax (base 2, running max and sum per row) needs only two
-//    cross-lane steps per tile for the max, and the probabilities feed the
-//    next product straight from the lane's registers.  The running max is
-//    only moved when a score exceeds it by more than 2^8, so the output
-//    accumulators are rarely rescaled.
+//    online softmax (base 2) needs one cross-lane max per row tile and step,
+//    and the probabilities feed the next product from the lane's registers.
+//    The running max only moves when a score exceeds it by more than 2^8, so
+//    the output accumulators are rarely rescaled.
 //  * O^T += V^T P^T with A = V^T (16 dims x 32 keys) and B = P^T.  The key
-//    order inside the 32-wide contraction is permuted identically in both
-//    operands (each lane holds keys 4q..4q+3 of two 16-key tiles), which
-//    matches the score tiles' register layout, so no shuffles are needed.
-//    P is rounded to fp16 (u = 2^-11) rather than bf16 (u = 2^-8): the
-//    latter's error on short causal rows comes close to the 2e-3 tolerance.
+//    order inside each block pair is permuted identically in both operands
+//    so that a lane's 8 contraction slots are 8 consecutive keys of one block:
+//    each V^T operand is one 16-byte LDS read.  P is rounded to fp16
+//    (u = 2^-11) rather than bf16 (u = 2^-8): the latter's error on short
+//    causal rows comes close to the 2e-3 tolerance.  Row sums of P come from
+//    an MFMA against ones.
+//  * A step is four phases between workgroup barriers (QK, softmax, PV,
+//    staging); waves 4..7, which share SIMDs with waves 0..3, run one phase
+//    behind, so MFMA and VALU phases of the two groups overlap.
 //  * The causal mask is applied only on steps that reach the diagonal; keys
 //    past the context are masked and their V entries zeroed when staged.
 #include <math.h>
