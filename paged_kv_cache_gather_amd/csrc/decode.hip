@@ -20,7 +20,8 @@
 //    The grid runs KV head fastest: consecutive workgroups go round-robin to
 //    the 8 XCDs, so with 8 KV heads every workgroup of one head lands on the
 //    same XCD, and sequences that share prefix blocks (adjacent in the batch)
-//    hit that XCD's L2.  Partitions past a sequence's end come last and exit.
+//    hit that XCD's L2.  Partitions run from the last to the first, so the
+//    long sequences' extra partitions start early.
 //  * Each wave owns 128 consecutive tokens of the partition end to end:
 //    - scores: one token per lane; the lane reads its token's whole K row
 //      (16-byte chunks; the K layout keeps x dims of one token together, so
@@ -374,8 +375,12 @@ __device__ __forceinline__ float rows4_sum(float x) {
 
 template <int D>
 struct SharedLds {
-  float o[kWaves][kRunRows][D];  // the waves' unnormalised outputs
+  float o[kWaves][kRunRows][D];   // the waves' unnormalised outputs
   float ml[kWaves][kRunRows][2];  // and (max, sum) per row
+  float wgt[kRunRows][kWaves];    // merge weights 2^(m_w - M) per row
+  float row_m[kRunRows], row_l[kRunRows];
+  int row_parts[kRunRows];        // partitions of the row's sequence
+  int32_t blk[kPartBlocks];       // the partition's block ids
 };
 
 // One run: sequences s .. s + k - 1 share partition p (2 <= k, k G <= 32 rows;
@@ -420,11 +425,13 @@ __device__ __forceinline__ void shared_run(int s, int k, int g, int p, SharedLds
     for (int dc = 0; dc < DC; ++dc) bq[rt][dc] = ld16(qp + 32 * dc);
   }
 
-  const int32_t* tab = tables + (int64_t)s * max_blocks + p * kPartBlocks + w * WB;
+  // the partition's block ids, read once into LDS
+  if (tid < kPartBlocks) sh.blk[tid] = tables[(int64_t)s * max_blocks + p * kPartBlocks + tid];
+  __syncthreads();
+  const int32_t* tab = sh.blk + w * WB;
   // this lane's K row inside a block pair for score tile `sub`
   const int k_half = r16 >> 3;                          // which block of the pair
   const int k_tok = 8 * ((r16 >> 2) & 1) + (r16 & 3);  // token, + 4 sub
-  // all of the wave's K operand loads are issued before the first MFMA
   u32x4 ka[WB][DC];  // tile 2 kp + sub
 #pragma unroll
   for (int kp = 0; kp < WB / 2; ++kp) {
@@ -512,28 +519,35 @@ __device__ __forceinline__ void shared_run(int s, int k, int g, int p, SharedLds
   }
   __syncthreads();
   const int rows = k * G;
-  for (int i = tid; i < rows * D; i += kThreads) {
-    const int row = i / D, j = i % D;
-    float Mx = sh.ml[0][row][0];
+  if (tid < rows) {  // per row: merged max and sum, the waves' weights, the sequence's partitions
+    float Mx = sh.ml[0][tid][0];
 #pragma unroll
-    for (int x = 1; x < kWaves; ++x) Mx = fmaxf(Mx, sh.ml[x][row][0]);
-    float acc = 0.f, den = 0.f;
+    for (int x = 1; x < kWaves; ++x) Mx = fmaxf(Mx, sh.ml[x][tid][0]);
+    float den = 0.f;
 #pragma unroll
     for (int x = 0; x < kWaves; ++x) {
-      const float f = __builtin_amdgcn_exp2f(sh.ml[x][row][0] - Mx);
-      acc = fmaf(f, sh.o[x][row][j], acc);
-      den = fmaf(f, sh.ml[x][row][1], den);
+      const float f = __builtin_amdgcn_exp2f(sh.ml[x][tid][0] - Mx);  // 0 for a wave with no keys
+      sh.wgt[tid][x] = f;
+      den = fmaf(f, sh.ml[x][tid][1], den);
     }
-    const int seq = s + row / G;
-    const int64_t orow = (int64_t)seq * Hq + g * G + row % G;
-    const int nparts = (clamp_len(lens[seq], max_context_len) + kPart - 1) / kPart;
-    if (nparts == 1) {
-      store_out<OutCode>(out, orow * D + j, acc / den);
+    sh.row_m[tid] = Mx;
+    sh.row_l[tid] = den;
+    sh.row_parts[tid] = (clamp_len(lens[s + tid / G], max_context_len) + kPart - 1) / kPart;
+  }
+  __syncthreads();
+  for (int i = tid; i < rows * D; i += kThreads) {
+    const int row = i / D, j = i % D;
+    float acc = 0.f;
+#pragma unroll
+    for (int x = 0; x < kWaves; ++x) acc = fmaf(sh.wgt[row][x], sh.o[x][row][j], acc);
+    const int64_t orow = (int64_t)(s + row / G) * Hq + g * G + row % G;
+    if (sh.row_parts[row] == 1) {
+      store_out<OutCode>(out, orow * D + j, acc / sh.row_l[row]);
     } else {
       ws_o[(orow * max_parts + p) * D + j] = acc;
       if (j == 0) {
-        ws_ml[(orow * max_parts + p) * 2 + 0] = Mx;
-        ws_ml[(orow * max_parts + p) * 2 + 1] = den;
+        ws_ml[(orow * max_parts + p) * 2 + 0] = sh.row_m[row];
+        ws_ml[(orow * max_parts + p) * 2 + 1] = sh.row_l[row];
       }
     }
   }
@@ -560,8 +574,6 @@ decode_shared_kernel(void* __restrict__ out, float* __restrict__ ws_o, float* __
     const int s_first = win * KM;
     if (s_first >= B) return;
     const int tid = threadIdx.x, lane = tid & 63;
-    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    if (tid == 0) joins = 0u;
     // candidates, one lane per member: both fill p and their first block ids
     // for p agree (one round of loads); then the full comparison for those
     uint32_t cand = 0;
@@ -576,12 +588,19 @@ decode_shared_kernel(void* __restrict__ out, float* __restrict__ ws_o, float* __
       }
       cand = (uint32_t)__ballot(c);
     }
+    if (cand == 0) return;  // uniform: every wave computed the same mask
+    if (tid == 0) joins = cand;
     __syncthreads();
-    if (cand == 0) return;
-    for (int i = 1 + w; i < KM; i += kWaves) {
-      if (!((cand >> i) & 1u)) continue;
-      const bool j = same_partition(tables, max_blocks, lens, max_context_len, s_first + i - 1, s_first + i, p);
-      if (j && lane == 0) atomicOr(&joins, 1u << i);
+    // full comparison of the candidates' partition block ids, one thread per
+    // (member, entry): a mismatch clears the member's bit
+    for (int t = tid; t < KM * kPartBlocks; t += kThreads) {
+      const int i = t / kPartBlocks, e = t % kPartBlocks;
+      if ((cand >> i) & 1u) {
+        const int a = s_first + i;
+        if (tables[(int64_t)(a - 1) * max_blocks + p * kPartBlocks + e] !=
+            tables[(int64_t)a * max_blocks + p * kPartBlocks + e])
+          atomicAnd(&joins, ~(1u << i));
+      }
     }
     __syncthreads();
     const uint32_t jm = joins;
@@ -610,7 +629,9 @@ decode_partition_kernel(void* __restrict__ out, float* __restrict__ ws_o, float*
   __shared__ __attribute__((aligned(16))) float smem[SMEM];
   __shared__ float sml[kWaves * RMAX][2];
 
-  const int g = blockIdx.x, s = blockIdx.y, p = blockIdx.z;
+  // last partitions first: long sequences' work starts early, the tail is
+  // made of partitions every sequence has
+  const int g = blockIdx.x, s = blockIdx.y, p = gridDim.z - 1 - blockIdx.z;
   const int Hq = Hkv * G;
 
   const int L = clamp_len(lens[s], max_context_len);
