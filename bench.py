@@ -182,6 +182,61 @@ def host_allocator_us(b, reps=5):
     return float(np.median(times)) * 1e6
 
 
+def prefix_cache_host(n_req=256, group=8, prefix=1024, lens=(512, 4096), seed=0):
+    """Host cost of automatic prefix caching in the block manager: n_req
+    requests in groups of `group` whose prompts share a `prefix`-token start
+    (the decode batch's sharing structure, prompts of lengths U[lens]); each
+    request looks its prompt up, appends the uncached rest with token ids
+    (labelling the blocks it fills) and is freed.  The reference model runs
+    the same operations beside it."""
+    import numpy as np
+    import paged_kv_cache_gather_amd as pkv
+    from oracle import block_manager as bm
+    rng = np.random.default_rng(seed)
+    prompts = []
+    for g in range(n_req // group):
+        base = rng.integers(0, 32000, size=prefix).tolist()
+        for _ in range(group):
+            L = int(rng.integers(lens[0], lens[1] + 1))
+            prompts.append(base[:min(prefix, L - 1)] + rng.integers(0, 32000, size=max(0, L - prefix)).tolist()
+                           if L > prefix else base[:L])
+    nblocks = sum(-(-len(t) // 16) for t in prompts) + 64
+    total_blocks = sum(len(t) // 16 for t in prompts)
+
+    def run_lib():
+        pool = pkv.paged_kv_alloc(nblocks, 8, 128, "bf16")
+        pkv.paged_kv_prefix_cache_enable(pool)
+        t0 = time.perf_counter()
+        reused = 0
+        for t in prompts:
+            sq, n = pkv.paged_kv_seq_create_cached(pool, t)
+            pkv.paged_kv_seq_append_tokens(pool, sq, t[n:])
+            reused += n
+            pkv.paged_kv_seq_free(pool, sq)
+        return time.perf_counter() - t0, reused, pkv.paged_kv_prefix_cache_stats(pool)
+
+    def run_model():
+        m = bm.BlockManagerModel(nblocks, 16)
+        m.enable_caching(True)
+        t0 = time.perf_counter()
+        reused = 0
+        for t in prompts:
+            sq, n = m.create_cached(t)
+            m.append_tokens(sq, t[n:])
+            reused += n
+            m.release(sq)
+        return time.perf_counter() - t0, reused, m.cache_stats()
+
+    dt, reused, stats = run_lib()
+    dtm, reused_m, stats_m = run_model()
+    assert reused == reused_m and stats == stats_m
+    toks = sum(len(t) for t in prompts)
+    return {"requests": len(prompts), "prompt_tokens": toks, "reused_tokens": reused,
+            "full_prompt_blocks": total_blocks, "stats": stats,
+            "us_per_request": dt / len(prompts) * 1e6, "prompt_tokens_per_s": toks / dt,
+            "model_us_per_request": dtm / len(prompts) * 1e6}
+
+
 def cpu_baseline(w, n_seqs):
     """The fp64 oracle (as it stands) on every k-th sequence of the batch."""
     import numpy as np
@@ -325,6 +380,7 @@ def main():
                          "host_allocator_step": host_allocator_us(b)},
         "bytes": by,
         "logical_gbs": logical,
+        "prefix_cache_host": prefix_cache_host(),
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, args.cpu_sample)

@@ -148,8 +148,50 @@ int paged_kv_seq_blocks_needed(pkv_pool* pool, int64_t seq, int64_t n_tokens, in
 
 /* Finish seq: every block's reference count drops by one and blocks reaching
  * zero rejoin the tail of the free queue at once, in the sequence's logical
- * order ("Back to the queue, and into vLLM proper", Life of a prompt). */
+ * order ("Back to the queue, and into vLLM proper", Life of a prompt).  With
+ * prefix caching on, a released labelled block keeps its label while it
+ * waits in the queue (see paged_kv_prefix_cache_enable). */
 int paged_kv_seq_free(pkv_pool* pool, int64_t seq);
+
+/* Automatic prefix caching ("Trick 3, Prefix caching", How AI actually
+ * answers you; "Prefix caching (automatic KV reuse)", vLLM Serving deep dive;
+ * The hands-on guide to LLM Inference with vLLM, Automatic Prefix Caching).
+ * Off by default.  When on, every full block of a sequence whose token ids
+ * are known is labelled with a fingerprint of its 16 tokens chained with the
+ * fingerprint of the block before it (a 64-bit mix; a lookup also compares
+ * the stored tokens and previous fingerprint).  Only full blocks are
+ * labelled, and a block whose content is already labelled elsewhere is not.
+ * A released labelled block stays reusable while it waits in the free queue
+ * and loses its label when the queue hands it out again, so unused cached
+ * blocks are evicted least recently released first.  Turning caching off
+ * drops every label.  Token ids are known for sequences made by
+ * paged_kv_seq_create / paged_kv_seq_create_cached and extended only with
+ * paged_kv_seq_append_tokens (forks inherit the parent's); a plain
+ * paged_kv_seq_append makes the rest of that sequence unlabelled. */
+int paged_kv_prefix_cache_enable(pkv_pool* pool, int32_t enable);
+
+/* New sequence for a prompt of n_tokens token ids: its leading full blocks
+ * whose labels are cached are reused (reference count +1; a cached block
+ * waiting in the free queue leaves it), stopping at the first miss and
+ * leaving at least the prompt's last token uncached.  *n_cached receives the
+ * number of reused tokens (a multiple of 16), which is the new sequence's
+ * length: append the remaining n_tokens - *n_cached tokens with
+ * paged_kv_seq_append_tokens and compute only those.  With caching off the
+ * sequence starts empty.  tokens is host int32 [n_tokens]. */
+int paged_kv_seq_create_cached(pkv_pool* pool, const int32_t* tokens, int64_t n_tokens, int64_t* seq,
+                               int64_t* n_cached);
+
+/* paged_kv_seq_append with the new tokens' ids (host int32 [n_tokens]), so
+ * that the blocks it fills can be labelled for prefix caching.  Same slots,
+ * copy-on-write and all-or-nothing behaviour as paged_kv_seq_append. */
+int paged_kv_seq_append_tokens(pkv_pool* pool, int64_t seq, const int32_t* tokens, int64_t n_tokens,
+                               int64_t* slot_mapping_out, int32_t* cow_pairs_out, int32_t max_cow,
+                               int32_t* n_cow);
+
+/* Prefix-cache counters: labelled blocks now, full prompt blocks looked up
+ * and found by paged_kv_seq_create_cached so far (any pointer may be NULL). */
+int paged_kv_prefix_cache_stats(pkv_pool* pool, int64_t* cached_blocks, int64_t* queried_blocks,
+                                int64_t* hit_blocks);
 
 /* Length (tokens) of seq. */
 int paged_kv_seq_len(pkv_pool* pool, int64_t seq, int64_t* len);

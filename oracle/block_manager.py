@@ -20,6 +20,15 @@ with it table for table, slot for slot:
   skeleton of a scheduler", LLM Serving from Scratch); here an append that
   cannot get all the blocks it needs changes nothing and reports the shortage,
   so the caller can preempt.
+* Prefix caching ("Trick 3, Prefix caching", How AI actually answers you;
+  "Prefix caching (automatic KV reuse)", vLLM Serving deep dive): a full
+  block is labelled by its own tokens together with the label of the block
+  before it, so equal labels mean equal text up to and including the block.
+  Here a label is that exact pair (an interned tuple), not a hash.  Only full
+  blocks are labelled; a new prompt reuses its leading labelled blocks (the
+  prompt's last token always computed); unused labelled blocks are evicted
+  least recently released first — a released block keeps its label in the
+  free queue until the queue hands it out again.
 """
 from __future__ import annotations
 
@@ -42,6 +51,28 @@ class BlockManagerModel:
         self.tables: dict[int, list[int]] = {}
         self.lens: dict[int, int] = {}
         self._next = 0
+        # prefix cache
+        self.caching = False
+        self.labels: dict[int, int] = {}        # label id -> block
+        self.block_label = [None] * num_blocks  # block -> label id
+        self._label_ids: dict[tuple, int] = {}  # (previous label id, tokens) -> label id
+        self.tokens: dict[int, list[int] | None] = {}  # None: not known
+        self.queried = 0
+        self.hits = 0
+
+    def _label_id(self, prev: int, toks) -> int:
+        key = (prev, tuple(int(t) for t in toks))
+        if key not in self._label_ids:
+            self._label_ids[key] = len(self._label_ids)
+        return self._label_ids[key]
+
+    def _seq_labels(self, sid: int) -> list[int]:
+        toks = self.tokens[sid]
+        out, prev = [], -1
+        for i in range(self.lens[sid] // self.bs):
+            prev = self._label_id(prev, toks[i * self.bs:(i + 1) * self.bs])
+            out.append(prev)
+        return out
 
     # -- sequences -------------------------------------------------------
     def create(self) -> int:
@@ -49,7 +80,51 @@ class BlockManagerModel:
         self._next += 1
         self.tables[sid] = []
         self.lens[sid] = 0
+        self.tokens[sid] = []
         return sid
+
+    def enable_caching(self, on: bool = True):
+        if not on:
+            self.labels.clear()
+            self.block_label = [None] * self.num_blocks
+        self.caching = bool(on)
+
+    def create_cached(self, tokens) -> tuple[int, int]:
+        """New sequence for a prompt; reuses its leading labelled full blocks.
+        Returns (sequence, reused tokens)."""
+        tokens = [int(t) for t in tokens]
+        sid = self.create()
+        if self.caching and tokens:
+            prev = -1
+            for i in range((len(tokens) - 1) // self.bs):
+                lab = self._label_id(prev, tokens[i * self.bs:(i + 1) * self.bs])
+                self.queried += 1
+                if lab not in self.labels:
+                    break
+                b = self.labels[lab]
+                self.hits += 1
+                if self.ref[b] == 0:
+                    self.free.remove(b)
+                self.ref[b] += 1
+                self.tables[sid].append(b)
+                prev = lab
+        self.lens[sid] = len(self.tables[sid]) * self.bs
+        self.tokens[sid] = tokens[:self.lens[sid]]
+        return sid, self.lens[sid]
+
+    def _label_new_full_blocks(self, sid: int, first: int):
+        if not self.caching or self.tokens[sid] is None:
+            return
+        labs = self._seq_labels(sid)
+        for i in range(first, len(labs)):
+            b = self.tables[sid][i]
+            if self.block_label[b] is not None or labs[i] in self.labels:
+                continue
+            self.labels[labs[i]] = b
+            self.block_label[b] = labs[i]
+
+    def cache_stats(self) -> dict:
+        return {"cached_blocks": len(self.labels), "queried_blocks": self.queried, "hit_blocks": self.hits}
 
     def fork(self, parent: int, n_prefix: int) -> int:
         """New sequence sharing the blocks of the parent's first n_prefix tokens."""
@@ -61,10 +136,17 @@ class BlockManagerModel:
         for b in self.tables[child]:
             self.ref[b] += 1
         self.lens[child] = n_prefix
+        pt = self.tokens[parent]
+        self.tokens[child] = None if pt is None else list(pt[:n_prefix])
         return child
 
     def _pop(self) -> int:
         b = self.free.popleft()
+        lab = self.block_label[b]
+        if lab is not None:  # evicted: it is about to hold new data
+            if self.labels.get(lab) == b:
+                del self.labels[lab]
+            self.block_label[b] = None
         self.ref[b] = 1
         return b
 
@@ -75,8 +157,25 @@ class BlockManagerModel:
             need += 1
         return need
 
+    def append_tokens(self, sid: int, tokens):
+        """append() with the new tokens' ids, labelling the blocks they fill."""
+        tokens = [int(t) for t in tokens]
+        L = self.lens[sid] if sid in self.lens else 0
+        slots, cow = self._append(sid, len(tokens))
+        if self.tokens[sid] is not None:
+            self.tokens[sid].extend(tokens)
+            self._label_new_full_blocks(sid, L // self.bs)
+        return slots, cow
+
     def append(self, sid: int, n: int):
-        """Make room for n new tokens; returns (slots, cow_pairs)."""
+        """Make room for n new tokens; returns (slots, cow_pairs).  The tokens
+        are not known, so nothing of the sequence from here on is labelled."""
+        slots, cow = self._append(sid, n)
+        if n > 0:
+            self.tokens[sid] = None
+        return slots, cow
+
+    def _append(self, sid: int, n: int):
         if sid not in self.tables or n < 0:
             raise ValueError("bad append")
         if self.blocks_needed(sid, n) > len(self.free):
@@ -107,6 +206,7 @@ class BlockManagerModel:
             if self.ref[b] == 0:
                 self.free.append(b)
         del self.lens[sid]
+        del self.tokens[sid]
 
     # -- views -----------------------------------------------------------
     def table(self, sid: int) -> list[int]:

@@ -79,6 +79,10 @@ _sig("paged_kv_block_tables", ctypes.c_int, _P, _P, _i32, _i32, _P, _P)
 _sig("paged_kv_num_free", ctypes.c_int, _P, _pi64)
 _sig("paged_kv_block_refcount", ctypes.c_int, _P, _i64, _pi32)
 _sig("paged_kv_free_queue", ctypes.c_int, _P, _P, _i64, _pi64)
+_sig("paged_kv_prefix_cache_enable", ctypes.c_int, _P, _i32)
+_sig("paged_kv_seq_create_cached", ctypes.c_int, _P, _P, _i64, _pi64, _pi64)
+_sig("paged_kv_seq_append_tokens", ctypes.c_int, _P, _i64, _P, _i64, _P, _P, _i32, _pi32)
+_sig("paged_kv_prefix_cache_stats", ctypes.c_int, _P, _pi64, _pi64, _pi64)
 _sig("reshape_and_cache", ctypes.c_int, _P, _P, _i64, _i64, _P, _P, _P, _i64, _i64, _i32, _i32,
      _i32, _i32, _P)
 _sig("paged_kv_copy_blocks", ctypes.c_int, _P, _P, _P, _i32, _i64, _i32, _i32, _i32, _i32, _P)
@@ -233,6 +237,36 @@ def paged_kv_seq_append(pool: Pool, seq: int, n_tokens: int):
     _check(_lib.paged_kv_seq_append(pool.handle, seq, n_tokens, slots.ctypes.data, cow.ctypes.data, 1,
                                     ctypes.byref(ncow)))
     return slots, [(int(cow[0]), int(cow[1]))] if ncow.value else []
+
+
+def paged_kv_prefix_cache_enable(pool: Pool, enable: bool = True):
+    _check(_lib.paged_kv_prefix_cache_enable(pool.handle, 1 if enable else 0))
+
+
+def paged_kv_seq_create_cached(pool: Pool, tokens) -> tuple[int, int]:
+    """New sequence for a prompt of token ids; returns (seq, n_cached tokens reused)."""
+    tok = np.ascontiguousarray(tokens, dtype=np.int32)
+    s, n = _i64(), _i64()
+    _check(_lib.paged_kv_seq_create_cached(pool.handle, tok.ctypes.data if tok.size else None, tok.size,
+                                           ctypes.byref(s), ctypes.byref(n)))
+    return s.value, n.value
+
+
+def paged_kv_seq_append_tokens(pool: Pool, seq: int, tokens):
+    """paged_kv_seq_append with token ids; returns (slot_mapping, cow pairs)."""
+    tok = np.ascontiguousarray(tokens, dtype=np.int32)
+    slots = np.empty(tok.size, dtype=np.int64)
+    cow = np.empty(2, dtype=np.int32)
+    ncow = _i32()
+    _check(_lib.paged_kv_seq_append_tokens(pool.handle, seq, tok.ctypes.data if tok.size else None, tok.size,
+                                           slots.ctypes.data, cow.ctypes.data, 1, ctypes.byref(ncow)))
+    return slots, [(int(cow[0]), int(cow[1]))] if ncow.value else []
+
+
+def paged_kv_prefix_cache_stats(pool: Pool) -> dict:
+    c, q, h = _i64(), _i64(), _i64()
+    _check(_lib.paged_kv_prefix_cache_stats(pool.handle, ctypes.byref(c), ctypes.byref(q), ctypes.byref(h)))
+    return {"cached_blocks": c.value, "queried_blocks": q.value, "hit_blocks": h.value}
 
 
 def paged_kv_seq_blocks_needed(pool: Pool, seq: int, n_tokens: int) -> int:

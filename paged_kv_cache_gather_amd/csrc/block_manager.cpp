@@ -1,5 +1,6 @@
 // Host block manager: the free-block queue, per-block reference counts and
-// per-sequence block tables of one KV pool.
+// per-sequence block tables of one KV pool, with optional automatic prefix
+// caching.
 //
 // Rules (restated from the pages):
 //  - a new block comes from the head of the free queue, and only when the
@@ -12,11 +13,25 @@
 //    dive);
 //  - running out of blocks is reported, not fatal, and leaves the state as it
 //    was so the caller can preempt ("The skeleton of a scheduler", LLM
-//    Serving from Scratch).
+//    Serving from Scratch);
+//  - prefix caching ("Trick 3, Prefix caching", How AI actually answers you;
+//    "Prefix caching (automatic KV reuse)", vLLM Serving deep dive; the
+//    Automatic Prefix Caching paragraph of The hands-on guide to LLM
+//    Inference with vLLM): a full block is labelled by a fingerprint of its
+//    own tokens chained with the fingerprint of the block before it; a new
+//    prompt reuses every leading full block whose label is known; only full
+//    blocks are labelled; unused labelled blocks are thrown out least
+//    recently used first.
 //
-// The free queue is a ring buffer over num_blocks entries (a block is either
-// queued or referenced, never both), so every operation is O(blocks touched).
+// The free queue is a doubly linked list over block ids (a block is either
+// queued or referenced, never both), so a cache hit can take a free block out
+// of the middle.  A freed labelled block keeps its label while it waits in
+// the queue; it loses the label only when the queue hands it out again, so
+// the queue's FIFO order is the eviction order (least recently released
+// first).  Every operation is O(blocks touched).
 #include <algorithm>
+#include <cstdint>
+#include <string>
 #include <mutex>
 #include <new>
 #include <unordered_map>
@@ -31,7 +46,30 @@ thread_local std::string g_last_error;
 struct Sequence {
   std::vector<int32_t> table;
   int64_t len = 0;
+  // token ids of every position, while they are all known (sequences
+  // created from tokens and extended with paged_kv_seq_append_tokens); the
+  // fingerprints of the full blocks among them
+  bool tracked = true;
+  std::vector<int32_t> tokens;
+  std::vector<uint64_t> fp;
 };
+
+// Fingerprint of a full block: a 64-bit chained mix of the previous block's
+// fingerprint and the block's tokens (splitmix64 finaliser per token).  A
+// lookup also compares the stored tokens and previous fingerprint, so a
+// label match means equal tokens here and an equal chain before.
+constexpr uint64_t kFpRoot = 0x243f6a8885a308d3ull;
+uint64_t mix64(uint64_t x) {
+  x += 0x9e3779b97f4a7c15ull;
+  x = (x ^ (x >> 30)) * 0xbf58476d1ce4e5b9ull;
+  x = (x ^ (x >> 27)) * 0x94d049bb133111ebull;
+  return x ^ (x >> 31);
+}
+uint64_t block_fp(uint64_t prev, const int32_t* tok, int n) {
+  uint64_t h = mix64(prev);
+  for (int i = 0; i < n; ++i) h = mix64(h ^ (uint64_t)(uint32_t)tok[i]);
+  return h;
+}
 
 }  // namespace
 
@@ -53,31 +91,74 @@ struct pkv_pool {
   int32_t head_dim = 0;
   int32_t dtype = 0;
   int32_t n_layers = 1;
-  // free queue ring buffer
-  std::vector<int32_t> ring;
-  int64_t head = 0;   // index of the queue's head in ring
+  // free queue: doubly linked list, head first
+  std::vector<int32_t> nxt, prv;
+  int32_t qhead = -1, qtail = -1;
   int64_t count = 0;  // blocks in the queue
   std::vector<int32_t> ref;
   std::unordered_map<int64_t, Sequence> seqs;
   int64_t next_id = 0;
+  // prefix cache: label -> block; per labelled block its label, the previous
+  // block's label and its tokens
+  bool caching = false;
+  std::unordered_map<uint64_t, int32_t> labels;
+  std::vector<char> labelled;
+  std::vector<uint64_t> blabel, bprev;
+  std::vector<int32_t> btok;
+  int64_t queried = 0, hits = 0;
   std::mutex mu;
 
-  int32_t pop() {
-    int32_t b = ring[head];
-    head = (head + 1) % num_blocks;
+  void unlink(int32_t b) {
+    const int32_t p = prv[b], n = nxt[b];
+    if (p >= 0) nxt[p] = n; else qhead = n;
+    if (n >= 0) prv[n] = p; else qtail = p;
+    prv[b] = nxt[b] = -1;
     --count;
-    ref[b] = 1;
-    return b;
   }
   void push(int32_t b) {
-    ring[(head + count) % num_blocks] = b;
+    prv[b] = qtail;
+    nxt[b] = -1;
+    if (qtail >= 0) nxt[qtail] = b; else qhead = b;
+    qtail = b;
     ++count;
+  }
+  void drop_label(int32_t b) {
+    if (!labelled.empty() && labelled[b]) {
+      auto it = labels.find(blabel[b]);
+      if (it != labels.end() && it->second == b) labels.erase(it);
+      labelled[b] = 0;
+    }
+  }
+  int32_t pop() {
+    const int32_t b = qhead;
+    unlink(b);
+    drop_label(b);  // evicted: the block is about to hold new data
+    ref[b] = 1;
+    return b;
   }
   int64_t need(const Sequence& s, int64_t n) const {
     const int64_t L = s.len, bs = block_size;
     int64_t blocks = (L + n + bs - 1) / bs - (L + bs - 1) / bs;
     if (n > 0 && L % bs != 0 && ref[s.table[L / bs]] > 1) ++blocks;
     return blocks;
+  }
+  // label the full blocks of s from index `from` on (its tokens are known)
+  void label_full_blocks(Sequence& s, int64_t from) {
+    const int64_t bs = block_size, nfull = s.len / bs;
+    for (int64_t i = (int64_t)s.fp.size(); i < nfull; ++i) {
+      const uint64_t prev = i ? s.fp[i - 1] : kFpRoot;
+      s.fp.push_back(block_fp(prev, s.tokens.data() + i * bs, (int)bs));
+    }
+    if (!caching) return;
+    for (int64_t i = from; i < nfull; ++i) {
+      const int32_t b = s.table[i];
+      if (labelled[b] || labels.count(s.fp[i])) continue;  // already known content
+      labels.emplace(s.fp[i], b);
+      labelled[b] = 1;
+      blabel[b] = s.fp[i];
+      bprev[b] = i ? s.fp[i - 1] : kFpRoot;
+      std::copy(s.tokens.begin() + i * bs, s.tokens.begin() + (i + 1) * bs, btok.begin() + (int64_t)b * bs);
+    }
   }
 };
 
@@ -146,7 +227,8 @@ int paged_kv_alloc(const pkv_pool_desc* desc, pkv_pool** out) {
   p->dtype = desc->dtype;
   p->n_layers = desc->n_layers;
   try {
-    p->ring.resize(p->num_blocks);
+    p->nxt.assign(p->num_blocks, -1);
+    p->prv.assign(p->num_blocks, -1);
     p->ref.assign(p->num_blocks, 0);
   } catch (...) {
     delete p;
@@ -161,13 +243,11 @@ int paged_kv_alloc(const pkv_pool_desc* desc, pkv_pool** out) {
         return fail(PKV_EINVAL, "initial_free_order is not a permutation of the pool");
       }
       seen[b] = 1;
-      p->ring[i] = b;
     }
+    for (int64_t i = 0; i < p->num_blocks; ++i) p->push(desc->initial_free_order[i]);
   } else {
-    for (int64_t i = 0; i < p->num_blocks; ++i) p->ring[i] = (int32_t)i;
+    for (int64_t i = 0; i < p->num_blocks; ++i) p->push((int32_t)i);
   }
-  p->head = 0;
-  p->count = p->num_blocks;
   *out = p;
   return ok();
 }
@@ -198,6 +278,11 @@ int paged_kv_seq_fork(pkv_pool* pool, int64_t parent, int64_t n_prefix_tokens, i
   Sequence s;
   s.table.assign(it->second.table.begin(), it->second.table.begin() + nb);
   s.len = n_prefix_tokens;
+  s.tracked = it->second.tracked;
+  if (s.tracked) {
+    s.tokens.assign(it->second.tokens.begin(), it->second.tokens.begin() + n_prefix_tokens);
+    s.fp.assign(it->second.fp.begin(), it->second.fp.begin() + n_prefix_tokens / pool->block_size);
+  }
   for (int32_t b : s.table) ++pool->ref[b];
   const int64_t id = pool->next_id++;
   pool->seqs.emplace(id, std::move(s));
@@ -215,21 +300,22 @@ int paged_kv_seq_blocks_needed(pkv_pool* pool, int64_t seq, int64_t n_tokens, in
   return ok();
 }
 
-int paged_kv_seq_append(pkv_pool* pool, int64_t seq, int64_t n_tokens, int64_t* slot_mapping_out,
-                        int32_t* cow_pairs_out, int32_t max_cow, int32_t* n_cow) {
-  if (!pool) return fail(PKV_EINVAL, "pool is NULL");
-  if (n_tokens < 0) return fail(PKV_EINVAL, "n_tokens < 0");
+static int append_impl(const char* fn, pkv_pool* pool, int64_t seq, const int32_t* tokens, int64_t n_tokens,
+                       int64_t* slot_mapping_out, int32_t* cow_pairs_out, int32_t max_cow, int32_t* n_cow) {
+  const std::string F(fn);
+  if (!pool) return fail(PKV_EINVAL, F + ": pool is NULL");
+  if (n_tokens < 0) return fail(PKV_EINVAL, F + ": n_tokens < 0");
   if (max_cow < 0 || (max_cow > 0 && !cow_pairs_out))
-    return fail(PKV_EINVAL, "cow_pairs_out is NULL with max_cow > 0");
+    return fail(PKV_EINVAL, F + ": cow_pairs_out is NULL with max_cow > 0");
   std::lock_guard<std::mutex> lk(pool->mu);
   auto it = pool->seqs.find(seq);
-  if (it == pool->seqs.end()) return fail(PKV_ESTATE, "paged_kv_seq_append: unknown sequence");
+  if (it == pool->seqs.end()) return fail(PKV_ESTATE, F + ": unknown sequence");
   Sequence& s = it->second;
   const int64_t bs = pool->block_size;
   const int64_t L = s.len;
   const bool cow = n_tokens > 0 && L % bs != 0 && pool->ref[s.table[L / bs]] > 1;
   if (cow && max_cow < 1)
-    return fail(PKV_EINVAL, "append needs a copy-on-write pair but max_cow is 0");
+    return fail(PKV_EINVAL, F + ": append needs a copy-on-write pair but max_cow is 0");
   const int64_t need = pool->need(s, n_tokens);
   if (need > pool->count)
     return fail(PKV_ENOMEM_BLOCKS, "out of KV blocks: need " + std::to_string(need) + ", free " +
@@ -250,7 +336,98 @@ int paged_kv_seq_append(pkv_pool* pool, int64_t seq, int64_t n_tokens, int64_t* 
     if (slot_mapping_out) slot_mapping_out[t - L] = (int64_t)s.table[t / bs] * bs + t % bs;
   }
   s.len = L + n_tokens;
+  if (tokens && s.tracked) {
+    s.tokens.insert(s.tokens.end(), tokens, tokens + n_tokens);
+    pool->label_full_blocks(s, L / bs);
+  } else if (n_tokens > 0) {
+    s.tracked = false;  // contents unknown from here on: nothing of it is labelled
+    s.tokens.clear();
+    s.tokens.shrink_to_fit();
+  }
   if (n_cow) *n_cow = ncow;
+  return ok();
+}
+
+int paged_kv_seq_append(pkv_pool* pool, int64_t seq, int64_t n_tokens, int64_t* slot_mapping_out,
+                        int32_t* cow_pairs_out, int32_t max_cow, int32_t* n_cow) {
+  return append_impl("paged_kv_seq_append", pool, seq, nullptr, n_tokens, slot_mapping_out, cow_pairs_out,
+                     max_cow, n_cow);
+}
+
+int paged_kv_seq_append_tokens(pkv_pool* pool, int64_t seq, const int32_t* tokens, int64_t n_tokens,
+                               int64_t* slot_mapping_out, int32_t* cow_pairs_out, int32_t max_cow,
+                               int32_t* n_cow) {
+  if (n_tokens > 0 && !tokens) return fail(PKV_EINVAL, "paged_kv_seq_append_tokens: tokens is NULL");
+  return append_impl("paged_kv_seq_append_tokens", pool, seq, tokens, n_tokens, slot_mapping_out,
+                     cow_pairs_out, max_cow, n_cow);
+}
+
+int paged_kv_prefix_cache_enable(pkv_pool* pool, int32_t enable) {
+  if (!pool) return fail(PKV_EINVAL, "pool is NULL");
+  std::lock_guard<std::mutex> lk(pool->mu);
+  if (enable && !pool->caching) {
+    try {
+      pool->labelled.assign(pool->num_blocks, 0);
+      pool->blabel.assign(pool->num_blocks, 0);
+      pool->bprev.assign(pool->num_blocks, 0);
+      pool->btok.assign(pool->num_blocks * pool->block_size, 0);
+    } catch (...) {
+      return fail(PKV_EINVAL, "paged_kv_prefix_cache_enable: host allocation failed");
+    }
+    pool->caching = true;
+  } else if (!enable && pool->caching) {
+    pool->labels.clear();
+    std::vector<char>().swap(pool->labelled);
+    std::vector<uint64_t>().swap(pool->blabel);
+    std::vector<uint64_t>().swap(pool->bprev);
+    std::vector<int32_t>().swap(pool->btok);
+    pool->caching = false;
+  }
+  return ok();
+}
+
+int paged_kv_seq_create_cached(pkv_pool* pool, const int32_t* tokens, int64_t n_tokens, int64_t* seq,
+                               int64_t* n_cached) {
+  if (!pool || !seq || !n_cached || (n_tokens > 0 && !tokens) || n_tokens < 0)
+    return fail(PKV_EINVAL, "paged_kv_seq_create_cached: bad argument");
+  std::lock_guard<std::mutex> lk(pool->mu);
+  const int64_t bs = pool->block_size;
+  Sequence s;
+  if (pool->caching && n_tokens > 0) {
+    const int64_t nq = (n_tokens - 1) / bs;  // the last token is always computed
+    uint64_t prev = kFpRoot;
+    for (int64_t i = 0; i < nq; ++i) {
+      const int32_t* tk = tokens + i * bs;
+      const uint64_t fp = block_fp(prev, tk, (int)bs);
+      ++pool->queried;
+      auto hit = pool->labels.find(fp);
+      if (hit == pool->labels.end()) break;
+      const int32_t b = hit->second;
+      if (pool->bprev[b] != prev || !std::equal(tk, tk + bs, pool->btok.begin() + (int64_t)b * bs)) break;
+      ++pool->hits;
+      if (pool->ref[b] == 0) pool->unlink(b);  // an unused cached block leaves the free queue
+      ++pool->ref[b];
+      s.table.push_back(b);
+      s.fp.push_back(fp);
+      prev = fp;
+    }
+  }
+  s.len = (int64_t)s.table.size() * bs;
+  s.tokens.assign(tokens, tokens + s.len);
+  const int64_t id = pool->next_id++;
+  pool->seqs.emplace(id, std::move(s));
+  *seq = id;
+  *n_cached = (int64_t)pool->seqs[id].len;
+  return ok();
+}
+
+int paged_kv_prefix_cache_stats(pkv_pool* pool, int64_t* cached_blocks, int64_t* queried_blocks,
+                                int64_t* hit_blocks) {
+  if (!pool) return fail(PKV_EINVAL, "pool is NULL");
+  std::lock_guard<std::mutex> lk(pool->mu);
+  if (cached_blocks) *cached_blocks = (int64_t)pool->labels.size();
+  if (queried_blocks) *queried_blocks = pool->queried;
+  if (hit_blocks) *hit_blocks = pool->hits;
   return ok();
 }
 
@@ -331,7 +508,8 @@ int paged_kv_free_queue(pkv_pool* pool, int32_t* out, int64_t cap, int64_t* n) {
   *n = pool->count;
   if (!out) return ok();
   if (cap < pool->count) return fail(PKV_EINVAL, "paged_kv_free_queue: cap too small");
-  for (int64_t i = 0; i < pool->count; ++i) out[i] = pool->ring[(pool->head + i) % pool->num_blocks];
+  int64_t i = 0;
+  for (int32_t b = pool->qhead; b >= 0; b = pool->nxt[b]) out[i++] = b;
   return ok();
 }
 
