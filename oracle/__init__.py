@@ -20,8 +20,8 @@ _SRC = os.path.join(_HERE, "oracle.c")
 _SO = os.path.join(_HERE, "liboracle.so")
 _LIB = None
 
-DTYPE_CODE = {"f32": 0, "f16": 1, "bf16": 2}
-ESIZE = {"f32": 4, "f16": 2, "bf16": 2}
+DTYPE_CODE = {"f32": 0, "f16": 1, "bf16": 2, "fp8_e4m3": 3}
+ESIZE = {"f32": 4, "f16": 2, "bf16": 2, "fp8_e4m3": 1}
 
 
 def build(verbose: bool = False) -> str:
@@ -49,7 +49,9 @@ def _lib():
         L.orc_scatter.argtypes = [ctypes.c_int, P, P, i64, i64, i64, P, P, P, i64, i32, i32, i32]
         L.orc_copy_blocks.argtypes = [ctypes.c_int, P, P, P, i64, i64, i32, i32, i32]
         L.orc_attention.argtypes = [i64, P, P, i64, P, P, i32, i32, i32, dbl, P, P, P, i32]
-        for f in (L.orc_decode, L.orc_gather, L.orc_scatter, L.orc_copy_blocks, L.orc_attention):
+        L.orc_quantize_e4m3.argtypes = [P, i64, ctypes.c_float, P]
+        for f in (L.orc_decode, L.orc_gather, L.orc_scatter, L.orc_copy_blocks, L.orc_attention,
+                  L.orc_quantize_e4m3):
             f.restype = ctypes.c_int
         _LIB = L
     return _LIB
@@ -91,6 +93,28 @@ def decode(dtype: str, bits: np.ndarray) -> np.ndarray:
     if rc:
         raise ValueError("bad dtype")
     return out
+
+
+def e4m3_inv_scale(scale: float) -> np.float32:
+    """The fp32 reciprocal of an 8-bit pool's scale (IEEE division, rounded
+    to nearest)."""
+    return np.float32(1.0) / np.float32(scale)
+
+
+def quantize_e4m3(x: np.ndarray, scale: float) -> np.ndarray:
+    """fp32 values -> E4M3 codes (uint8) for a pool with this scale: the
+    nearest E4M3 value of x * (1/scale) in fp32, ties to even, saturating at
+    448 (the 8-bit cache of "Quantization", vLLM Serving deep dive; the format
+    and the scale rule are readings, see oracle.c)."""
+    x32 = np.ascontiguousarray(x, dtype=np.float32)
+    out = np.empty(x32.shape, dtype=np.uint8)
+    _lib().orc_quantize_e4m3(_p(x32), x32.size, ctypes.c_float(float(e4m3_inv_scale(scale))), _p(out))
+    return out
+
+
+def dequantize_e4m3(codes: np.ndarray, scale: float) -> np.ndarray:
+    """E4M3 codes -> fp64 values value(code) * scale (exact in fp64)."""
+    return decode("fp8_e4m3", np.ascontiguousarray(codes, dtype=np.uint8)) * float(np.float32(scale))
 
 
 def slot(table, t: int, block_size: int) -> int:

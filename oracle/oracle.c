@@ -33,6 +33,17 @@
  *  - orc_copy_blocks: copy-on-write copies a whole block ("Sharing and
  *    copy-on-write", vLLM Serving deep dive).
  *
+ *  - e4m3_value / orc_quantize_e4m3: the 8-bit KV cache.  The pages say the
+ *    cache may be kept in FP8 (one byte per element: the KV-size formula of
+ *    "The hands-on guide to LLM Inference with vLLM"; "Quantization" in the
+ *    vLLM Serving deep dive; "Trick 6, Quantization" in "How AI actually
+ *    answers you") but fix neither the 8-bit format nor a scale rule.  The
+ *    readings taken here: the OCP E4M3 format (bias 7, no infinities, largest
+ *    finite 448), one fp32 scale per pool, stored code = the E4M3 value
+ *    nearest to x * (1/scale) (both in fp32; ties to the even code; finite
+ *    magnitudes beyond 448 and infinities saturate to 448), read back as
+ *    value(code) * scale.
+ *
  * Pool layout (per layer, elements of `esize` bytes, x = 16 / esize):
  *   K element (blk, head g, token t, dim j) at index
  *       ((((blk * H + g) * (d / x) + j / x) * bs + t) * x + j % x)
@@ -46,13 +57,14 @@
 #include <omp.h>
 #endif
 
-enum { ORC_F32 = 0, ORC_F16 = 1, ORC_BF16 = 2 };
+enum { ORC_F32 = 0, ORC_F16 = 1, ORC_BF16 = 2, ORC_FP8_E4M3 = 3 };
 
 static int esize_of(int dtype) {
   switch (dtype) {
     case ORC_F32: return 4;
     case ORC_F16: return 2;
     case ORC_BF16: return 2;
+    case ORC_FP8_E4M3: return 1;
     default: return 0;
   }
 }
@@ -81,6 +93,24 @@ static double bf16_value(uint16_t b) {
   return (double)f;
 }
 
+/* OCP E4M3 -> double, from the format's definition: 1 sign bit, 4 exponent
+ * bits (bias 7), 3 mantissa bits.  Exponent 0 holds the subnormals
+ * m/8 * 2^-6; exponent 15 with mantissa 7 is NaN; there are no infinities. */
+static double e4m3_value(uint8_t b) {
+  int sign = (b >> 7) & 1;
+  int e = (b >> 3) & 0xf;
+  int m = b & 0x7;
+  double v;
+  if (e == 15 && m == 7) {
+    v = NAN;
+  } else if (e == 0) {
+    v = ldexp((double)m, -9); /* m/8 * 2^-6 */
+  } else {
+    v = ldexp((double)(8 + m), e - 10); /* (1 + m/8) * 2^(e-7) */
+  }
+  return sign ? -v : v;
+}
+
 static double f32_value(uint32_t u) {
   float f;
   memcpy(&f, &u, 4);
@@ -93,9 +123,42 @@ static double elem_value(int dtype, const unsigned char* base, int64_t idx) {
     memcpy(&u, base + idx * 4, 4);
     return f32_value(u);
   }
+  if (dtype == ORC_FP8_E4M3) return e4m3_value(base[idx]);
   uint16_t h;
   memcpy(&h, base + idx * 2, 2);
   return dtype == ORC_F16 ? f16_value(h) : bf16_value(h);
+}
+
+/* The E4M3 code nearest to y: the finite codes are searched one by one (ties
+ * go to the even code, i.e. the even mantissa); magnitudes of 448 and beyond,
+ * infinities included, give 448; NaN gives the NaN code 0x7f; the sign bit is
+ * y's, so values that round to zero keep their sign. */
+static uint8_t e4m3_nearest(float y) {
+  const uint8_t sign = signbit(y) ? 0x80 : 0;
+  if (isnan(y)) return sign | 0x7f;
+  const double a = fabs((double)y);
+  if (a >= 448.0) return sign | 0x7e;
+  int best = 0;
+  double best_d = a; /* distance to +0 */
+  for (int c = 1; c <= 0x7e; ++c) {
+    const double d = fabs(e4m3_value((uint8_t)c) - a);
+    if (d < best_d || (d == best_d && (c & 1) == 0)) {
+      best = c;
+      best_d = d;
+    }
+  }
+  return (uint8_t)(sign | best);
+}
+
+/* Quantise n fp32 values for the 8-bit cache: code = nearest E4M3 value of
+ * the fp32 product x * inv_scale, where inv_scale is the fp32 reciprocal of
+ * the pool's scale. */
+int orc_quantize_e4m3(const float* x, int64_t n, float inv_scale, uint8_t* out) {
+  for (int64_t i = 0; i < n; ++i) {
+    const float y = x[i] * inv_scale; /* one fp32 product, rounded to nearest even */
+    out[i] = e4m3_nearest(y);
+  }
+  return 0;
 }
 
 int orc_decode(int dtype, const void* src, int64_t n, double* dst) {
