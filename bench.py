@@ -15,9 +15,11 @@ a bounded sample of the same batch on the host cores.  The partition pass is
 two kernels queued back to back on the caller's stream: decode_shared_kernel
 (partitions whose blocks neighbouring sequences share, read once for all of
 them) and decode_partition_kernel (every other partition); it is timed with
-HIP events around the whole pass.
+HIP events around the whole pass.  The JSON also carries the same step over
+an 8-bit (E4M3) cache (fp8_kv_decode: rows quantised on the way in, half the
+bytes per step) and the mixed chunked-prefill + decode step.
 
-  python bench.py [--steps K] [--warmup W] [--workload 2|3|4] [--no-cpu-baseline]
+  python bench.py [--steps K] [--warmup W] [--workload 2|3|4] [--no-cpu-baseline] [--no-fp8] [--no-mixed]
   python bench.py --copy-calibration     # plain device copy of a known size
 """
 import argparse
@@ -41,14 +43,14 @@ def decode_bytes(b):
     """Algorithmic bytes of one partition-pass launch, and the logical KV bytes.
 
     Unit = one context token of one KV head: 2 * head_dim * esize bytes of K
-    and V.  Physical blocks shared by several sequences count once, with the
+    and V (esize 1 for an 8-bit cache).  Physical blocks shared by several sequences count once, with the
     most tokens any sequence reads from them.  Plus q, block-table entries and
     lengths read, and the outputs it writes for single-partition sequences."""
     import numpy as np
     from paged_kv_cache_gather_amd import paged_attention_decode_partition_size
     w, d = b.w, b.decode
     eb = w.elem_bytes
-    unit = 2 * w.head_dim * eb
+    unit = 2 * w.head_dim * (1 if b.fp8 else eb)
     lens = d.lens.astype(np.int64)
     nb = -(-lens // 16)
     rows = np.repeat(np.arange(w.n_decode), nb)
@@ -271,6 +273,78 @@ def copy_calibration():
     log(f"copied {n} bytes x5")
 
 
+def time_decode(b, out, K, W):
+    """W untimed then K timed decode steps of batch b: append the new tokens,
+    then the partition pass and the reduce, with HIP events between them on
+    the stream they run on."""
+    import numpy as np
+    import torch
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+           torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+
+    def step(e=None):
+        if e is not None:
+            e[0].record(stream)
+        b.append_decode()
+        if e is not None:
+            e[1].record(stream)
+        b.attend_decode_split(out, between=(lambda: e[2].record(stream)) if e is not None else None)
+        if e is not None:
+            e[3].record(stream)
+
+    for _ in range(W):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        step(ev[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    return {"ms_step": (t1 - t0) * 1e3 / K,
+            "part_ms": np.array([ev[i][1].elapsed_time(ev[i][2]) for i in range(K)]),
+            "append_ms": np.array([ev[i][0].elapsed_time(ev[i][1]) for i in range(K)]),
+            "reduce_ms": np.array([ev[i][2].elapsed_time(ev[i][3]) for i in range(K)])}
+
+
+# scales of the 8-bit leg: the synthetic values are standard normal quantiles
+# (|x| < 4.4), which these map inside E4M3's +-448
+FP8_K_SCALE, FP8_V_SCALE = 0.0125, 0.0103
+
+
+def fp8_decode_leg(w, K, W, out_dtype, seed):
+    """The same decode step over an 8-bit (E4M3) cache: the new rows are
+    quantised by reshape_and_cache_fp8, the partition pass reads half the
+    bytes (decode_shared_kernel + decode_fp8_partition_kernel)."""
+    import torch
+    from paged_kv_cache_gather_amd.batch import DeviceBatch
+    b = DeviceBatch(w, "cuda:0", fill="device", out_dtype=out_dtype, kv_cache="fp8_e4m3", k_scale=FP8_K_SCALE,
+                    v_scale=FP8_V_SCALE)
+    out = b.new_decode_out()
+    t = time_decode(b, out, K, W)
+    by = decode_bytes(b)
+    part_us = float(t["part_ms"].mean()) * 1e3
+    achieved = by["algorithmic_bytes"] / (part_us * 1e-6) / 1e9
+    log(f"fp8 cache: step {t['ms_step'] * 1e3:.1f} us | append {t['append_ms'].mean() * 1e3:.1f} us | partitions "
+        f"{part_us:.1f} us = {achieved:.0f} GB/s ({achieved / HBM_PEAK_GBS:.1%}) | reduce "
+        f"{t['reduce_ms'].mean() * 1e3:.1f} us")
+    res = {"kv_cache": "fp8_e4m3 (OCP E4M3, one fp32 scale per pool)", "k_scale": FP8_K_SCALE,
+           "v_scale": FP8_V_SCALE, "ms_per_step": t["ms_step"], "tokens_per_s": w.n_decode / (t["ms_step"] * 1e-3),
+           "breakdown_us": {"append": float(t["append_ms"].mean()) * 1e3, "partitions": part_us,
+                            "reduce": float(t["reduce_ms"].mean()) * 1e3},
+           "roofline": {"bound": "hbm", "kernel": "decode partition pass, 8-bit cache "
+                                                  "(decode_fp8_partition_kernel + decode_shared_kernel)",
+                        "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                        "traffic": (profiled_traffic("decode_fp8_partition_llama3_8b_decode",
+                                                     ["decode.hip", "pkv_device.h"])
+                                    if w.name == "llama3_8b_decode" and seed == 0 else None),
+                        "algorithmic_bytes": by["algorithmic_bytes"]},
+           "bytes": by}
+    del b
+    torch.cuda.empty_cache()
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -284,6 +358,8 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--no-mixed", action="store_true", help="skip the mixed prefill+decode step")
     ap.add_argument("--only-mixed", action="store_true", help="run only the mixed prefill+decode step")
+    ap.add_argument("--no-fp8", action="store_true", help="skip the 8-bit-cache decode leg")
+    ap.add_argument("--only-fp8", action="store_true", help="run only the 8-bit-cache decode leg")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -307,38 +383,18 @@ def main():
         return
 
     w = synth.make_workload(args.workload, seed=args.seed)
+    if args.only_fp8:
+        print(json.dumps(fp8_decode_leg(w, args.steps, args.warmup, None if args.out_dtype == "kv" else "f32",
+                                        args.seed)), flush=True)
+        return
     log(f"building {w.name}: {w.description}")
     t_build = time.perf_counter()
     b = DeviceBatch(w, "cuda:0", fill="device", out_dtype=None if args.out_dtype == "kv" else "f32")
     log(f"built in {time.perf_counter() - t_build:.1f} s")
     out = b.new_decode_out()
-    stream = torch.cuda.current_stream()
     K, W = args.steps, args.warmup
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
-           torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
-
-    def step(e=None):
-        if e is not None:
-            e[0].record(stream)
-        b.append_decode()
-        if e is not None:
-            e[1].record(stream)
-        b.attend_decode_split(out, between=(lambda: e[2].record(stream)) if e is not None else None)
-        if e is not None:
-            e[3].record(stream)
-
-    for _ in range(W):
-        step()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(K):
-        step(ev[i])
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms_step = (t1 - t0) * 1e3 / K
-    part_ms = np.array([ev[i][1].elapsed_time(ev[i][2]) for i in range(K)])
-    append_ms = np.array([ev[i][0].elapsed_time(ev[i][1]) for i in range(K)])
-    reduce_ms = np.array([ev[i][2].elapsed_time(ev[i][3]) for i in range(K)])
+    t = time_decode(b, out, K, W)
+    ms_step, part_ms, append_ms, reduce_ms = t["ms_step"], t["part_ms"], t["append_ms"], t["reduce_ms"]
     by = decode_bytes(b)
     part_s = float(part_ms.mean()) * 1e-3
     achieved = by["algorithmic_bytes"] / part_s / 1e9
@@ -384,9 +440,11 @@ def main():
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, args.cpu_sample)
+    del b, out
+    torch.cuda.empty_cache()
+    if not args.no_fp8:
+        res["fp8_kv_decode"] = fp8_decode_leg(w, K, W, None if args.out_dtype == "kv" else "f32", args.seed)
     if not args.no_mixed:
-        del b
-        torch.cuda.empty_cache()
         res["mixed_step"] = mixed_step(max(5, K // 2), max(2, W // 2), args.seed)
     print(json.dumps(res), flush=True)
 

@@ -26,8 +26,8 @@
  *   - block_size must be 16 (the pages' default block of 16 tokens).
  *
  * KV pool layout (one layer; the pages fix none, this is the library's own).
- * Elements are `esize` bytes (4 for PKV_F32, 2 for PKV_F16 / PKV_BF16) and
- * x = 16 / esize elements form one 16-byte chunk:
+ * Elements are `esize` bytes (4 for PKV_F32, 2 for PKV_F16 / PKV_BF16, 1 for
+ * PKV_FP8_E4M3) and x = 16 / esize elements form one 16-byte chunk:
  *   K element (block b, kv head g, token slot t, dim j) at element index
  *       ((((b * n_kv_heads + g) * (head_dim / x) + j / x) * block_size + t) * x + j % x)
  *   V element (b, g, t, j) at element index
@@ -59,6 +59,12 @@ extern "C" {
 #define PKV_F32 0
 #define PKV_F16 1
 #define PKV_BF16 2
+/* 8-bit cache: OCP E4M3 codes (1 sign, 4 exponent bits with bias 7, 3
+ * mantissa bits; no infinities; 0x7f / 0xff are NaN; largest finite 448).
+ * The pages allow an 8-bit cache ("Quantization", vLLM Serving deep dive:
+ * about twice the tokens per byte of HBM) without fixing the format; each
+ * pool carries one fp32 scale, a cached value being value(code) * scale. */
+#define PKV_FP8_E4M3 3
 
 /* Text of the last error on this thread ("" after a success). */
 const char* pkv_last_error(void);
@@ -239,6 +245,27 @@ int reshape_and_cache(const void* key, const void* value, int64_t key_token_stri
                       int32_t n_kv_heads, int32_t head_dim, int32_t block_size, int32_t dtype,
                       void* stream);
 
+/* reshape_and_cache into an 8-bit pool pair (dtype PKV_FP8_E4M3): the new
+ * rows are quantised on the way in.  Element x of a key row is stored as the
+ * E4M3 code nearest to fp32(x) * fp32(1 / k_scale) (the reciprocal rounded to
+ * nearest once, the product rounded to nearest; ties to the even code;
+ * finite magnitudes beyond 448 and infinities saturate to +-448; NaN gives a
+ * NaN code; a value that rounds to zero keeps its sign), values likewise with
+ * v_scale.  The pages allow the 8-bit cache ("Quantization", vLLM Serving deep
+ * dive) but give no rounding or scale rule: this is the library's reading.
+ *   key, value   device rows as for reshape_and_cache, in src_dtype
+ *                (PKV_F32, PKV_F16 or PKV_BF16).
+ *   k_pool, v_pool  device 8-bit pools (num_blocks * n_kv_heads * block_size
+ *                * head_dim bytes each) in the layout above with esize 1.
+ *   k_scale, v_scale  finite and > 0 (PKV_EINVAL otherwise).
+ * Rows that are already E4M3 codes are copied unchanged by reshape_and_cache
+ * with dtype PKV_FP8_E4M3. */
+int reshape_and_cache_fp8(const void* key, const void* value, int32_t src_dtype,
+                          int64_t key_token_stride, int64_t value_token_stride, void* k_pool,
+                          void* v_pool, const int64_t* slot_mapping, int64_t num_tokens,
+                          int64_t num_blocks, int32_t n_kv_heads, int32_t head_dim,
+                          int32_t block_size, float k_scale, float v_scale, void* stream);
+
 /* Copy whole blocks of one layer's K and V pools: pairs_dev is device int32
  * [n_pairs][2] (src, dst), as reported by paged_kv_seq_append for a
  * copy-on-write ("Sharing and copy-on-write", vLLM Serving deep dive).
@@ -280,8 +307,9 @@ int64_t paged_attention_decode_workspace_bytes(int32_t num_seqs, int32_t n_q_hea
  *   workspace     device, >= paged_attention_decode_workspace_bytes(...)
  *                 bytes (may be NULL when that is 0); contents need no
  *                 initialisation and are overwritten.
- * Supported: head_dim 64/128, n_q_heads / n_kv_heads in {1, 2, 4, 8, 16},
- * block_size 16.  Accumulation is fp32. */
+ * Supported: kv_dtype PKV_F32, PKV_F16 or PKV_BF16 (8-bit pools go to
+ * paged_attention_decode_fp8), head_dim 64/128, n_q_heads / n_kv_heads in
+ * {1, 2, 4, 8, 16}, block_size 16.  Accumulation is fp32. */
 int paged_attention_decode(void* out, int32_t out_dtype, const void* q, const void* k_pool,
                            const void* v_pool, const int32_t* block_tables,
                            int32_t max_blocks_per_seq, const int32_t* context_lens,
@@ -289,6 +317,45 @@ int paged_attention_decode(void* out, int32_t out_dtype, const void* q, const vo
                            int32_t head_dim, int32_t block_size, int64_t num_blocks,
                            int32_t max_context_len, float scale, int32_t kv_dtype, void* workspace,
                            int64_t workspace_bytes, void* stream);
+
+/* Decode attention over an 8-bit cache (PKV_FP8_E4M3 pools written by
+ * reshape_and_cache_fp8): the same result as paged_attention_decode with
+ * every cached key and value replaced by value(code) * k_scale (resp.
+ * v_scale).  The query stays in q_dtype (PKV_F16 or PKV_BF16); out_dtype is
+ * PKV_F32 or q_dtype.  Other arguments, the workspace size
+ * (paged_attention_decode_workspace_bytes) and the supported shapes are those
+ * of paged_attention_decode.  The codes are widened exactly to q_dtype for the
+ * score products and to fp16 for the value products (both on MFMA, fp32
+ * accumulation, probabilities in fp16); k_scale folds into the softmax scale
+ * and v_scale into the output.  k_scale, v_scale finite and > 0.  Half the
+ * bytes of a 16-bit cache per decode step ("Quantization", vLLM Serving deep
+ * dive). */
+int paged_attention_decode_fp8(void* out, int32_t out_dtype, const void* q, int32_t q_dtype,
+                               const void* k_pool, const void* v_pool, float k_scale,
+                               float v_scale, const int32_t* block_tables,
+                               int32_t max_blocks_per_seq, const int32_t* context_lens,
+                               int32_t num_seqs, int32_t n_q_heads, int32_t n_kv_heads,
+                               int32_t head_dim, int32_t block_size, int64_t num_blocks,
+                               int32_t max_context_len, float scale, void* workspace,
+                               int64_t workspace_bytes, void* stream);
+/* Its two passes, as paged_attention_decode_partitions / _reduce are for
+ * paged_attention_decode (same arguments and ordering rule). */
+int paged_attention_decode_fp8_partitions(void* out, int32_t out_dtype, const void* q, int32_t q_dtype,
+                                          const void* k_pool, const void* v_pool, float k_scale,
+                                          float v_scale, const int32_t* block_tables,
+                                          int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                          int32_t num_seqs, int32_t n_q_heads, int32_t n_kv_heads,
+                                          int32_t head_dim, int32_t block_size, int64_t num_blocks,
+                                          int32_t max_context_len, float scale, void* workspace,
+                                          int64_t workspace_bytes, void* stream);
+int paged_attention_decode_fp8_reduce(void* out, int32_t out_dtype, const void* q, int32_t q_dtype,
+                                      const void* k_pool, const void* v_pool, float k_scale,
+                                      float v_scale, const int32_t* block_tables,
+                                      int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                      int32_t num_seqs, int32_t n_q_heads, int32_t n_kv_heads,
+                                      int32_t head_dim, int32_t block_size, int64_t num_blocks,
+                                      int32_t max_context_len, float scale, void* workspace,
+                                      int64_t workspace_bytes, void* stream);
 
 /* The two passes of paged_attention_decode, for callers that schedule them
  * separately (same arguments, same validation).  _partitions runs the

@@ -20,12 +20,15 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libpagedkv.so")
 
 PKV_OK, PKV_EINVAL, PKV_ENOMEM_BLOCKS, PKV_EUNSUPPORTED, PKV_EHIP, PKV_ESTATE = 0, -1, -2, -3, -4, -5
-PKV_F32, PKV_F16, PKV_BF16 = 0, 1, 2
+PKV_F32, PKV_F16, PKV_BF16, PKV_FP8_E4M3 = 0, 1, 2, 3
 BLOCK_SIZE = 16
 
-_TORCH_CODE = {torch.float32: PKV_F32, torch.float16: PKV_F16, torch.bfloat16: PKV_BF16}
-_NAME_CODE = {"f32": PKV_F32, "f16": PKV_F16, "bf16": PKV_BF16}
-CODE_TORCH = {v: k for k, v in _TORCH_CODE.items()}
+# 8-bit pools are uint8 (or float8_e4m3fn) tensors holding E4M3 codes
+_TORCH_CODE = {torch.float32: PKV_F32, torch.float16: PKV_F16, torch.bfloat16: PKV_BF16,
+               torch.uint8: PKV_FP8_E4M3, torch.float8_e4m3fn: PKV_FP8_E4M3}
+_NAME_CODE = {"f32": PKV_F32, "f16": PKV_F16, "bf16": PKV_BF16, "fp8_e4m3": PKV_FP8_E4M3}
+CODE_TORCH = {PKV_F32: torch.float32, PKV_F16: torch.float16, PKV_BF16: torch.bfloat16,
+              PKV_FP8_E4M3: torch.uint8}
 
 
 class PagedKVError(RuntimeError):
@@ -85,6 +88,8 @@ _sig("paged_kv_seq_append_tokens", ctypes.c_int, _P, _i64, _P, _i64, _P, _P, _i3
 _sig("paged_kv_prefix_cache_stats", ctypes.c_int, _P, _pi64, _pi64, _pi64)
 _sig("reshape_and_cache", ctypes.c_int, _P, _P, _i64, _i64, _P, _P, _P, _i64, _i64, _i32, _i32,
      _i32, _i32, _P)
+_sig("reshape_and_cache_fp8", ctypes.c_int, _P, _P, _i32, _i64, _i64, _P, _P, _P, _i64, _i64, _i32, _i32, _i32,
+     _f32, _f32, _P)
 _sig("paged_kv_copy_blocks", ctypes.c_int, _P, _P, _P, _i32, _i64, _i32, _i32, _i32, _i32, _P)
 _sig("paged_attention_decode_partition_size", _i32)
 _sig("paged_attention_decode_workspace_bytes", _i64, _i32, _i32, _i32, _i32)
@@ -93,6 +98,10 @@ _sig("paged_attention_decode", ctypes.c_int, _P, _i32, _P, _P, _P, _P, _i32, _P,
 for _n in ("paged_attention_decode_partitions", "paged_attention_decode_reduce"):
     _sig(_n, ctypes.c_int, _P, _i32, _P, _P, _P, _P, _i32, _P, _i32, _i32, _i32, _i32, _i32, _i64, _i32, _f32,
          _i32, _P, _i64, _P)
+for _n in ("paged_attention_decode_fp8", "paged_attention_decode_fp8_partitions",
+           "paged_attention_decode_fp8_reduce"):
+    _sig(_n, ctypes.c_int, _P, _i32, _P, _i32, _P, _P, _f32, _f32, _P, _i32, _P, _i32, _i32, _i32, _i32, _i32, _i64,
+         _i32, _f32, _P, _i64, _P)
 _sig("paged_attention_prefill_chunk", ctypes.c_int, _P, _i32, _P, _P, _P, _P, _i32, _P, _P, _i32,
      _i32, _i32, _i32, _i32, _i32, _i32, _i64, _i32, _f32, _i32, _P)
 
@@ -352,6 +361,37 @@ def reshape_and_cache(key: torch.Tensor, value: torch.Tensor, k_pool: torch.Tens
                                   block_size, dtype_code(key.dtype), _stream(stream, key.device)))
 
 
+def _is_codes(t: torch.Tensor) -> bool:
+    return t.dtype in (torch.uint8, torch.float8_e4m3fn)
+
+
+def reshape_and_cache_fp8(key: torch.Tensor, value: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
+                          slot_mapping: torch.Tensor, num_blocks: int, n_kv_heads: int, head_dim: int,
+                          k_scale: float, v_scale: float, block_size: int = BLOCK_SIZE, stream=None):
+    """Quantising cache write: key/value rows (f32, f16 or bf16) -> E4M3 codes
+    in 8-bit pools (uint8 or float8_e4m3fn tensors)."""
+    _dev(key, "key", contiguous=False)
+    _dev(value, "value", key.dtype, contiguous=False)
+    _dev(slot_mapping, "slot_mapping", torch.int64)
+    _dev(k_pool, "k_pool")
+    _dev(v_pool, "v_pool")
+    if not (_is_codes(k_pool) and _is_codes(v_pool)):
+        raise PagedKVError(PKV_EINVAL, "8-bit pools must be uint8 or float8_e4m3fn tensors")
+    T = slot_mapping.numel()
+    if key.shape[0] != T or value.shape[0] != T:
+        raise PagedKVError(PKV_EINVAL, "key/value must have one row per slot")
+    for t, name in ((key, "key"), (value, "value")):
+        if t[0].numel() != n_kv_heads * head_dim or (t.dim() > 1 and not t[0].is_contiguous()):
+            raise PagedKVError(PKV_EINVAL, f"{name} rows must be contiguous [n_kv_heads*head_dim]")
+    need = num_blocks * n_kv_heads * block_size * head_dim
+    if k_pool.numel() < need or v_pool.numel() < need:
+        raise PagedKVError(PKV_EINVAL, "pool tensors smaller than num_blocks blocks")
+    _check(_lib.reshape_and_cache_fp8(_ptr(key), _ptr(value), dtype_code(key.dtype), key.stride(0), value.stride(0),
+                                      _ptr(k_pool), _ptr(v_pool), _ptr(slot_mapping), T, num_blocks, n_kv_heads,
+                                      head_dim, block_size, float(k_scale), float(v_scale),
+                                      _stream(stream, key.device)))
+
+
 def paged_kv_copy_blocks(k_pool: torch.Tensor, v_pool: torch.Tensor, pairs: torch.Tensor, num_blocks: int,
                          n_kv_heads: int, head_dim: int, block_size: int = BLOCK_SIZE, stream=None):
     """pairs: device int32 [n, 2] (src, dst)."""
@@ -425,6 +465,62 @@ def paged_attention_decode_reduce(out, q, k_pool, v_pool, block_tables, context_
     """Split-context merge pass of paged_attention_decode (same arguments)."""
     _decode_call(_lib.paged_attention_decode_reduce, out, q, k_pool, v_pool, block_tables, context_lens,
                  max_context_len, n_kv_heads, num_blocks, scale, workspace, block_size, stream)
+
+
+def _decode_fp8_call(fn, out, q, k_pool, v_pool, block_tables, context_lens, max_context_len, n_kv_heads,
+                     num_blocks, scale, k_scale, v_scale, workspace, block_size, stream):
+    _dev(out, "out")
+    _dev(q, "q")
+    _dev(k_pool, "k_pool")
+    _dev(v_pool, "v_pool")
+    _dev(block_tables, "block_tables", torch.int32)
+    _dev(context_lens, "context_lens", torch.int32)
+    if not (_is_codes(k_pool) and _is_codes(v_pool)):
+        raise PagedKVError(PKV_EINVAL, "8-bit pools must be uint8 or float8_e4m3fn tensors")
+    if q.dim() != 3 or out.shape != q.shape:
+        raise PagedKVError(PKV_EINVAL, "q and out must be [num_seqs, n_q_heads, head_dim]")
+    B, Hq, d = q.shape
+    if block_tables.dim() != 2 or block_tables.shape[0] != B or context_lens.numel() != B:
+        raise PagedKVError(PKV_EINVAL, "block_tables/context_lens must have one row per sequence")
+    need = num_blocks * n_kv_heads * block_size * d
+    if k_pool.numel() < need or v_pool.numel() < need:
+        raise PagedKVError(PKV_EINVAL, "pool tensors smaller than num_blocks blocks")
+    ws_bytes = 0
+    if workspace is not None:
+        _dev(workspace, "workspace")
+        ws_bytes = workspace.numel() * workspace.element_size()
+    _check(fn(_ptr(out), dtype_code(out.dtype), _ptr(q), dtype_code(q.dtype), _ptr(k_pool), _ptr(v_pool),
+              float(k_scale), float(v_scale), _ptr(block_tables), block_tables.shape[1], _ptr(context_lens), B, Hq,
+              n_kv_heads, d, block_size, num_blocks, max_context_len, float(scale), _ptr(workspace), ws_bytes,
+              _stream(stream, q.device)))
+
+
+def paged_attention_decode_fp8(out: torch.Tensor, q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
+                               block_tables: torch.Tensor, context_lens: torch.Tensor, max_context_len: int,
+                               n_kv_heads: int, num_blocks: int, scale: float, k_scale: float, v_scale: float,
+                               workspace=None, block_size: int = BLOCK_SIZE, stream=None):
+    """Decode over 8-bit pools (uint8 / float8_e4m3fn codes with scales
+    k_scale, v_scale): out [B, Hq, d] (f32 or q's dtype); q [B, Hq, d] f16 or bf16."""
+    _decode_fp8_call(_lib.paged_attention_decode_fp8, out, q, k_pool, v_pool, block_tables, context_lens,
+                     max_context_len, n_kv_heads, num_blocks, scale, k_scale, v_scale, workspace, block_size, stream)
+
+
+def paged_attention_decode_fp8_partitions(out, q, k_pool, v_pool, block_tables, context_lens, max_context_len,
+                                          n_kv_heads, num_blocks, scale, k_scale, v_scale, workspace=None,
+                                          block_size: int = BLOCK_SIZE, stream=None):
+    """Partition pass of paged_attention_decode_fp8 (same arguments)."""
+    _decode_fp8_call(_lib.paged_attention_decode_fp8_partitions, out, q, k_pool, v_pool, block_tables,
+                     context_lens, max_context_len, n_kv_heads, num_blocks, scale, k_scale, v_scale, workspace,
+                     block_size, stream)
+
+
+def paged_attention_decode_fp8_reduce(out, q, k_pool, v_pool, block_tables, context_lens, max_context_len,
+                                      n_kv_heads, num_blocks, scale, k_scale, v_scale, workspace=None,
+                                      block_size: int = BLOCK_SIZE, stream=None):
+    """Split-context merge pass of paged_attention_decode_fp8 (same arguments)."""
+    _decode_fp8_call(_lib.paged_attention_decode_fp8_reduce, out, q, k_pool, v_pool, block_tables, context_lens,
+                     max_context_len, n_kv_heads, num_blocks, scale, k_scale, v_scale, workspace, block_size,
+                     stream)
 
 
 def paged_attention_prefill_chunk(out: torch.Tensor, q: torch.Tensor, k_pool: torch.Tensor,

@@ -5,7 +5,10 @@ context and, each step, the appended tokens; the attention calls read it back
 through the block tables.
 
 Values come from ``synth`` (the seeded generator), filled on the device or
-uploaded from the host.  Nothing here computes attention.
+uploaded from the host.  With ``kv_cache="fp8_e4m3"`` the pools hold 8-bit
+codes: the same rows are quantised on the way in (reshape_and_cache_fp8) and
+decode reads them with paged_attention_decode_fp8.  Nothing here computes
+attention.
 """
 from __future__ import annotations
 
@@ -17,9 +20,10 @@ import torch
 import synth
 from . import (paged_kv_alloc, paged_kv_seq_create, paged_kv_seq_fork, paged_kv_seq_append,
                paged_kv_seq_free, paged_kv_block_tables, paged_kv_copy_blocks, reshape_and_cache,
-               paged_attention_decode, paged_attention_decode_workspace_bytes,
-               paged_attention_decode_partitions, paged_attention_decode_reduce,
-               paged_attention_prefill_chunk, BLOCK_SIZE)
+               reshape_and_cache_fp8, paged_attention_decode, paged_attention_decode_fp8,
+               paged_attention_decode_fp8_partitions, paged_attention_decode_fp8_reduce,
+               paged_attention_decode_workspace_bytes, paged_attention_decode_partitions,
+               paged_attention_decode_reduce, paged_attention_prefill_chunk, BLOCK_SIZE)
 
 TORCH_DTYPE = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
 _VIEW = {"f32": torch.int32, "f16": torch.int16, "bf16": torch.int16}
@@ -68,17 +72,24 @@ class DeviceBatch:
     """Device pools plus the decode and prefill inputs of one step of ``w``."""
 
     def __init__(self, w: synth.Workload, device="cuda:0", fill: str = "device",
-                 out_dtype: str | None = None, stage_tokens: int = 1 << 16):
+                 out_dtype: str | None = None, stage_tokens: int = 1 << 16, kv_cache: str | None = None,
+                 k_scale: float = 1.0, v_scale: float = 1.0):
         self.w = w
         self.device = torch.device(device)
         self.fill = fill
         self.tdt = TORCH_DTYPE[w.dtype]
         self.out_dtype = TORCH_DTYPE[out_dtype or w.dtype]
+        self.fp8 = kv_cache == "fp8_e4m3"
+        if kv_cache not in (None, w.dtype, "fp8_e4m3"):
+            raise ValueError(f"kv_cache {kv_cache!r}: the workload's dtype or fp8_e4m3")
+        self.k_scale, self.v_scale = float(k_scale), float(v_scale)
         H, d = w.n_kv_heads, w.head_dim
-        self.pool = paged_kv_alloc(w.num_blocks, H, d, w.dtype, initial_free_order=w.free_order)
+        self.pool = paged_kv_alloc(w.num_blocks, H, d, "fp8_e4m3" if self.fp8 else w.dtype,
+                                   initial_free_order=w.free_order)
         n = w.num_blocks * H * BLOCK_SIZE * d
-        self.k_pool = torch.zeros(n, dtype=self.tdt, device=self.device)
-        self.v_pool = torch.zeros(n, dtype=self.tdt, device=self.device)
+        pdt = torch.uint8 if self.fp8 else self.tdt
+        self.k_pool = torch.zeros(n, dtype=pdt, device=self.device)
+        self.v_pool = torch.zeros(n, dtype=pdt, device=self.device)
         self._stage = max(stage_tokens, 1)
         self.decode = self._build_decode() if w.n_decode else None
         self.prefill = self._build_prefill() if w.n_chunks else None
@@ -116,8 +127,16 @@ class DeviceBatch:
             b = min(t1, a + self._stage)
             k, v = self._kv_rows(kind, idx, a, b)
             sl = torch.from_numpy(np.ascontiguousarray(slots[a - t0:b - t0])).to(self.device)
-            reshape_and_cache(k.view(b - a, -1), v.view(b - a, -1), self.k_pool, self.v_pool, sl,
-                              w.num_blocks, w.n_kv_heads, w.head_dim)
+            self._cache(k.view(b - a, -1), v.view(b - a, -1), sl)
+
+    def _cache(self, k, v, slots, stream=None):
+        w = self.w
+        if self.fp8:
+            reshape_and_cache_fp8(k, v, self.k_pool, self.v_pool, slots, w.num_blocks, w.n_kv_heads, w.head_dim,
+                                  self.k_scale, self.v_scale, stream=stream)
+        else:
+            reshape_and_cache(k, v, self.k_pool, self.v_pool, slots, w.num_blocks, w.n_kv_heads, w.head_dim,
+                              stream=stream)
 
     def _cow(self, pairs):
         if pairs:
@@ -227,14 +246,18 @@ class DeviceBatch:
     def append_decode(self, stream=None):
         d = self.decode
         w = self.w
-        reshape_and_cache(d.k_new.view(w.n_decode, -1), d.v_new.view(w.n_decode, -1), self.k_pool,
-                          self.v_pool, d.slots, w.num_blocks, w.n_kv_heads, w.head_dim, stream=stream)
+        self._cache(d.k_new.view(w.n_decode, -1), d.v_new.view(w.n_decode, -1), d.slots, stream=stream)
 
     def attend_decode(self, out: torch.Tensor, stream=None):
         d = self.decode
         w = self.w
-        paged_attention_decode(out, d.q, self.k_pool, self.v_pool, d.tables, d.lens_dev, d.max_context_len,
-                               w.n_kv_heads, w.num_blocks, w.scale, workspace=d.workspace, stream=stream)
+        if self.fp8:
+            paged_attention_decode_fp8(out, d.q, self.k_pool, self.v_pool, d.tables, d.lens_dev, d.max_context_len,
+                                       w.n_kv_heads, w.num_blocks, w.scale, self.k_scale, self.v_scale,
+                                       workspace=d.workspace, stream=stream)
+        else:
+            paged_attention_decode(out, d.q, self.k_pool, self.v_pool, d.tables, d.lens_dev, d.max_context_len,
+                                   w.n_kv_heads, w.num_blocks, w.scale, workspace=d.workspace, stream=stream)
 
     def attend_decode_split(self, out: torch.Tensor, between=None, stream=None):
         """The decode attention as its two passes, calling ``between()`` (if
@@ -243,19 +266,23 @@ class DeviceBatch:
         w = self.w
         args = (out, d.q, self.k_pool, self.v_pool, d.tables, d.lens_dev, d.max_context_len, w.n_kv_heads,
                 w.num_blocks, w.scale)
-        paged_attention_decode_partitions(*args, workspace=d.workspace, stream=stream)
+        if self.fp8:
+            args += (self.k_scale, self.v_scale)
+        (paged_attention_decode_fp8_partitions if self.fp8 else paged_attention_decode_partitions)(
+            *args, workspace=d.workspace, stream=stream)
         if between is not None:
             between()
-        paged_attention_decode_reduce(*args, workspace=d.workspace, stream=stream)
+        (paged_attention_decode_fp8_reduce if self.fp8 else paged_attention_decode_reduce)(
+            *args, workspace=d.workspace, stream=stream)
 
     def append_prefill(self, stream=None):
         p = self.prefill
-        w = self.w
         T = p.k_new.shape[0]
-        reshape_and_cache(p.k_new.view(T, -1), p.v_new.view(T, -1), self.k_pool, self.v_pool, p.slots,
-                          w.num_blocks, w.n_kv_heads, w.head_dim, stream=stream)
+        self._cache(p.k_new.view(T, -1), p.v_new.view(T, -1), p.slots, stream=stream)
 
     def attend_prefill(self, out: torch.Tensor, stream=None):
+        if self.fp8:
+            raise ValueError("chunked prefill reads 16-bit pools")
         p = self.prefill
         w = self.w
         paged_attention_prefill_chunk(out, p.q, self.k_pool, self.v_pool, p.tables, p.cu_q_lens, p.lens_dev,

@@ -1,13 +1,19 @@
 // Cache writes: reshape_and_cache (append new tokens' K/V into their slots)
 // and paged_kv_copy_blocks (whole-block copies for copy-on-write).
 //
-// Both are byte copies.  reshape_and_cache reads each new token's K and V row
+// reshape_and_cache and paged_kv_copy_blocks are byte copies;
+// reshape_and_cache_fp8 quantises 32- or 16-bit rows into an 8-bit pool on the
+// way (the 8-bit cache of "Quantization", vLLM Serving deep dive), with the
+// same chunk walk.  reshape_and_cache reads each new token's K and V row
 // in 16-byte chunks and writes them into the pool layout: a K chunk stays a
 // contiguous 16-byte unit (the layout keeps x = 16/esize consecutive dims of
 // one token together), while a V chunk is spread over x dim-rows, one
 // element each, since V tiles are dim-major.  Consecutive lanes take
 // consecutive tokens, so tokens that fill one block (a prefill chunk) write
 // contiguous runs.
+#include <cmath>
+#include <string>
+
 #include "pkv_device.h"
 #include "pkv_internal.h"
 
@@ -42,6 +48,9 @@ reshape_and_cache_kernel(const unsigned char* __restrict__ key, const unsigned c
 #pragma unroll
       for (int e = 0; e < 4; ++e)
         *reinterpret_cast<uint32_t*>(vrow + (int64_t)e * kBlockSize * ES) = vv[e];
+    } else if constexpr (ES == 1) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) vrow[(int64_t)e * kBlockSize] = (unsigned char)(vv[e >> 2] >> (8 * (e & 3)));
     } else {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
@@ -49,6 +58,73 @@ reshape_and_cache_kernel(const unsigned char* __restrict__ key, const unsigned c
         *reinterpret_cast<uint16_t*>(vrow + (int64_t)e * kBlockSize * ES) = h;
       }
     }
+  }
+}
+
+// fp32 -> E4M3 code of the nearest value (ties to even): finite magnitudes
+// beyond 448 and infinities saturate first, NaN stays NaN.  Four values per
+// 32-bit word, the first in the low byte.
+__device__ __forceinline__ float e4m3_saturate(float y) {
+  return y != y ? y : fminf(fmaxf(y, -448.f), 448.f);
+}
+__device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
+  uint32_t w = __builtin_amdgcn_cvt_pk_fp8_f32(e4m3_saturate(a), e4m3_saturate(b), 0, false);
+  return __builtin_amdgcn_cvt_pk_fp8_f32(e4m3_saturate(c), e4m3_saturate(d), w, true);
+}
+
+// 16 source elements (one 16-dim chunk of a row) -> 16 codes, x * inv each.
+template <typename S>
+__device__ __forceinline__ u32x4 quantise16(const unsigned char* src, float inv) {
+  float f[16];
+  if constexpr (S::kBytes == 4) {
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      const u32x4 w = ld16(src + 16 * h);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) f[4 * h + e] = __uint_as_float(w[e]);
+    }
+  } else {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const u32x4 w = ld16(src + 16 * h);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) unpack2<S>(w[e], f[8 * h + 2 * e], f[8 * h + 2 * e + 1]);
+    }
+  }
+  u32x4 r;
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+    r[e] = e4m3x4(f[4 * e] * inv, f[4 * e + 1] * inv, f[4 * e + 2] * inv, f[4 * e + 3] * inv);
+  return r;
+}
+
+// One work item = one 16-dim chunk of one token's head row: the K chunk is
+// one 16-byte store, the V chunk 16 one-byte stores (dim-major V).
+template <typename S>
+__global__ void __launch_bounds__(256)
+reshape_and_cache_fp8_kernel(const unsigned char* __restrict__ key, const unsigned char* __restrict__ value,
+                             int64_t kstride_b, int64_t vstride_b, unsigned char* __restrict__ kpool,
+                             unsigned char* __restrict__ vpool, const int64_t* __restrict__ slots, int64_t T,
+                             int64_t num_slots, int H, int D, float k_inv, float v_inv) {
+  const int C = D / 16;
+  const int64_t total = T * H * C;
+  for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
+       idx += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t i = idx % T;
+    const int64_t rest = idx / T;
+    const int g = (int)(rest % H);
+    const int c = (int)(rest / H);
+    const int64_t slot = slots[i];
+    if (slot < 0 || slot >= num_slots) continue;
+    const int64_t tile = (slot / kBlockSize) * H + g;
+    const int off = (int)(slot % kBlockSize);
+    const int64_t col = ((int64_t)g * D + c * 16) * S::kBytes;
+    const u32x4 kq = quantise16<S>(key + i * kstride_b + col, k_inv);
+    const u32x4 vq = quantise16<S>(value + i * vstride_b + col, v_inv);
+    st16(kpool + ((tile * C + c) * kBlockSize + off) * 16, kq);
+    unsigned char* vrow = vpool + (tile * D + (int64_t)c * 16) * kBlockSize + off;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) vrow[(int64_t)e * kBlockSize] = (unsigned char)(vq[e >> 2] >> (8 * (e & 3)));
   }
 }
 
@@ -96,7 +172,12 @@ extern "C" int reshape_and_cache(const void* key, const void* value, int64_t key
   if (grid > 16384) grid = 16384;
   hipStream_t s = (hipStream_t)stream;
   const int64_t num_slots = num_blocks * pkv::kBlockSize;
-  if (es == 4) {
+  if (es == 1) {
+    hipLaunchKernelGGL(pkv::reshape_and_cache_kernel<1>, dim3((unsigned)grid), dim3(256), 0, s,
+                       (const unsigned char*)key, (const unsigned char*)value, key_token_stride,
+                       value_token_stride, (unsigned char*)k_pool, (unsigned char*)v_pool,
+                       slot_mapping, num_tokens, num_slots, n_kv_heads, head_dim);
+  } else if (es == 4) {
     hipLaunchKernelGGL(pkv::reshape_and_cache_kernel<4>, dim3((unsigned)grid), dim3(256), 0, s,
                        (const unsigned char*)key, (const unsigned char*)value, key_token_stride * 4,
                        value_token_stride * 4, (unsigned char*)k_pool, (unsigned char*)v_pool,
@@ -109,6 +190,56 @@ extern "C" int reshape_and_cache(const void* key, const void* value, int64_t key
   }
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(PKV_EHIP, std::string("reshape_and_cache: ") + hipGetErrorString(e));
+  return ok();
+}
+
+extern "C" int reshape_and_cache_fp8(const void* key, const void* value, int32_t src_dtype,
+                                     int64_t key_token_stride, int64_t value_token_stride, void* k_pool,
+                                     void* v_pool, const int64_t* slot_mapping, int64_t num_tokens,
+                                     int64_t num_blocks, int32_t n_kv_heads, int32_t head_dim,
+                                     int32_t block_size, float k_scale, float v_scale, void* stream) {
+  if (src_dtype != PKV_F32 && src_dtype != PKV_F16 && src_dtype != PKV_BF16)
+    return fail(PKV_EINVAL, "reshape_and_cache_fp8: source dtype must be f32, f16 or bf16");
+  const int es = pkv::esize_of(src_dtype);
+  if (block_size != pkv::kBlockSize) return fail(PKV_EUNSUPPORTED, "block_size must be 16");
+  if (head_dim != 64 && head_dim != 128) return fail(PKV_EUNSUPPORTED, "head_dim must be 64 or 128");
+  if (num_tokens < 0 || num_blocks < 1 || n_kv_heads < 1)
+    return fail(PKV_EINVAL, "reshape_and_cache_fp8: bad sizes");
+  if (!std::isfinite(k_scale) || !std::isfinite(v_scale) || !(k_scale > 0.f) || !(v_scale > 0.f))
+    return fail(PKV_EINVAL, "reshape_and_cache_fp8: scales must be finite and > 0");
+  if (num_tokens == 0) return ok();
+  if (!key || !value || !k_pool || !v_pool || !slot_mapping)
+    return fail(PKV_EINVAL, "reshape_and_cache_fp8: NULL pointer");
+  const int64_t row = (int64_t)n_kv_heads * head_dim;
+  if (key_token_stride < row || value_token_stride < row)
+    return fail(PKV_EINVAL, "reshape_and_cache_fp8: token stride shorter than a row");
+  if (!pkv::aligned16(key) || !pkv::aligned16(value) || !pkv::aligned16(k_pool) ||
+      !pkv::aligned16(v_pool) || (key_token_stride * es) % 16 || (value_token_stride * es) % 16)
+    return fail(PKV_EINVAL, "reshape_and_cache_fp8: pointers and strides must be 16-byte aligned");
+  // the reciprocals are rounded to nearest once, here (IEEE fp32 division)
+  const float k_inv = 1.0f / k_scale, v_inv = 1.0f / v_scale;
+  if (!std::isfinite(k_inv) || !std::isfinite(v_inv))
+    return fail(PKV_EINVAL, "reshape_and_cache_fp8: scale too small");
+  const int64_t total = num_tokens * n_kv_heads * (head_dim / 16);
+  int64_t grid = (total + 255) / 256;
+  if (grid > 16384) grid = 16384;
+  hipStream_t s = (hipStream_t)stream;
+  const int64_t num_slots = num_blocks * pkv::kBlockSize;
+  auto launch = [&](auto src) {
+    using S = decltype(src);
+    hipLaunchKernelGGL(pkv::reshape_and_cache_fp8_kernel<S>, dim3((unsigned)grid), dim3(256), 0, s,
+                       (const unsigned char*)key, (const unsigned char*)value, key_token_stride * es,
+                       value_token_stride * es, (unsigned char*)k_pool, (unsigned char*)v_pool, slot_mapping,
+                       num_tokens, num_slots, n_kv_heads, head_dim, k_inv, v_inv);
+  };
+  if (src_dtype == PKV_F32)
+    launch(pkv::F32{});
+  else if (src_dtype == PKV_F16)
+    launch(pkv::F16{});
+  else
+    launch(pkv::BF16{});
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(PKV_EHIP, std::string("reshape_and_cache_fp8: ") + hipGetErrorString(e));
   return ok();
 }
 

@@ -12,7 +12,11 @@
 // How (gfx950): three kernels per step on one stream.  decode_shared_kernel
 // first serves the partitions that neighbouring sequences share (see the
 // section on shared partitions below); decode_partition_kernel serves the
-// rest; decode_reduce_kernel merges split-context partials.
+// rest; decode_reduce_kernel merges split-context partials.  Over an 8-bit
+// (E4M3) cache the rest is served by decode_fp8_partition_kernel instead, on
+// MFMA like the shared kernel: the codes are widened in registers, exactly,
+// and the pools' scales fold into the softmax scale (keys) and the written
+// partials (values).
 // decode_partition_kernel:
 //  * Work unit = (KV head g, sequence s, partition p of 512 context tokens),
 //    one 256-thread workgroup (4 wave64s).  All G query heads that share the
@@ -280,46 +284,59 @@ constexpr int kRunRows = 32;                     // query rows of a shared run (
 constexpr int kPartBlocks = kPart / kBlockSize;  // blocks per partition
 static_assert(kPartBlocks <= 64, "one wave compares a partition's block ids");
 
-// Do sequences a and b both fill partition p and name the same blocks for it?
-// (Uniform per wave.)
-__device__ __forceinline__ bool same_partition(const int32_t* __restrict__ tables, int max_blocks,
-                                               const int32_t* __restrict__ lens, int max_context_len, int a,
-                                               int b, int p) {
-  // first block ids, then lengths, then all the partition's ids (the reads
-  // stay in the table: p * kPartBlocks < max_blocks whenever the caller's
-  // sequence fills partition p)
-  const int64_t fa = (int64_t)a * max_blocks + p * kPartBlocks, fb = (int64_t)b * max_blocks + p * kPartBlocks;
-  if (tables[fa] != tables[fb]) return false;
-  const int need = (p + 1) * kPart;
-  if (clamp_len(lens[a], max_context_len) < need || clamp_len(lens[b], max_context_len) < need) return false;
-  const int lane = threadIdx.x & 63;
-  bool eq = true;
-  if (lane < kPartBlocks)
-    eq = tables[(int64_t)a * max_blocks + p * kPartBlocks + lane] ==
-         tables[(int64_t)b * max_blocks + p * kPartBlocks + lane];
-  return __all(eq);
-}
-
-// Does s join the run of s - 1 for partition p?
-template <int KM>
-__device__ __forceinline__ bool joins_prev(const int32_t* __restrict__ tables, int max_blocks,
-                                           const int32_t* __restrict__ lens, int max_context_len, int s,
-                                           int p) {
-  return s % KM != 0 && same_partition(tables, max_blocks, lens, max_context_len, s - 1, s, p);
-}
-
 // Is (s, p) served by a shared workgroup, i.e. is s in a run of two or more?
+// The loads that decide it for most (s, p) — the neighbours' lengths and
+// first block ids for p — are issued together by probe_share, before the
+// caller's own exits, so that the decision costs one round of loads; only
+// candidates (a neighbour with the same first block) compare all ids.
+struct ShareProbe {
+  int32_t id, id_prev, id_next;  // first block id of p for s, s - 1, s + 1
+  int L_prev, L_next;            // lengths of s - 1, s + 1 (-1: not in s's window)
+};
+
 template <typename T, int G>
-__device__ __forceinline__ bool in_shared_run(const int32_t* __restrict__ tables, int max_blocks,
-                                              const int32_t* __restrict__ lens, int B, int max_context_len,
-                                              int s, int p) {
-  if constexpr (T::kBytes != 2) {
+__device__ __forceinline__ ShareProbe probe_share(const int32_t* __restrict__ tables, int max_blocks,
+                                                  const int32_t* __restrict__ lens, int B, int s, int p) {
+  ShareProbe r{0, 0, 0, -1, -1};
+  if constexpr (T::kBytes != 4) {
+    constexpr int KM = kRunRows / G;
+    const int64_t col = (int64_t)p * kPartBlocks;  // < max_blocks for every p < max_parts
+    const bool hp = s % KM != 0, hn = s + 1 < B && (s + 1) % KM != 0;
+    r.id = tables[(int64_t)s * max_blocks + col];
+    if (hp) {
+      r.id_prev = tables[(int64_t)(s - 1) * max_blocks + col];
+      r.L_prev = lens[s - 1];
+    }
+    if (hn) {
+      r.id_next = tables[(int64_t)(s + 1) * max_blocks + col];
+      r.L_next = lens[s + 1];
+    }
+  }
+  return r;
+}
+
+template <typename T, int G>
+__device__ __forceinline__ bool in_shared_run(const ShareProbe& pr, const int32_t* __restrict__ tables,
+                                              int max_blocks, int max_context_len, int s, int p, int L) {
+  if constexpr (T::kBytes == 4) {
     return false;  // fp32 K/V: no MFMA path
   } else {
-    constexpr int KM = kRunRows / G;
-    if ((p + 1) * kPart > clamp_len(lens[s], max_context_len)) return false;
-    return joins_prev<KM>(tables, max_blocks, lens, max_context_len, s, p) ||
-           (s + 1 < B && joins_prev<KM>(tables, max_blocks, lens, max_context_len, s + 1, p));
+    const int need = (p + 1) * kPart;
+    if (L < need) return false;
+    // does s join s - 1, or s + 1 join s: both fill p, same first id (then all ids)
+    const bool cp = pr.L_prev >= 0 && clamp_len(pr.L_prev, max_context_len) >= need && pr.id_prev == pr.id;
+    const bool cn = pr.L_next >= 0 && clamp_len(pr.L_next, max_context_len) >= need && pr.id_next == pr.id;
+    if (!cp && !cn) return false;
+    const int64_t col = (int64_t)p * kPartBlocks;
+    const int lane = threadIdx.x & 63;
+    bool ep = true, en = true;
+    if (lane < kPartBlocks) {
+      const int32_t mine = tables[(int64_t)s * max_blocks + col + lane];
+      if (cp) ep = tables[(int64_t)(s - 1) * max_blocks + col + lane] == mine;
+      if (cn) en = tables[(int64_t)(s + 1) * max_blocks + col + lane] == mine;
+    }
+    const bool all_p = __all(ep), all_n = __all(en);
+    return (cp && all_p) || (cn && all_n);
   }
 }
 
@@ -373,138 +390,225 @@ __device__ __forceinline__ float rows4_sum(float x) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
-template <int D>
-struct SharedLds {
-  float o[kWaves][kRunRows][D];   // the waves' unnormalised outputs
-  float ml[kWaves][kRunRows][2];  // and (max, sum) per row
-  float wgt[kRunRows][kWaves];    // merge weights 2^(m_w - M) per row
-  float row_m[kRunRows], row_l[kRunRows];
-  int row_parts[kRunRows];        // partitions of the row's sequence
-  int32_t blk[kPartBlocks];       // the partition's block ids
+template <int D, int ROWS>
+struct RunLds {
+  float o[kWaves][ROWS][D + 4];  // the waves' unnormalised outputs (rows padded: LDS banks)
+  float ml[kWaves][ROWS][2];  // and (max, sum) per row
+  float wgt[ROWS][kWaves];    // merge weights 2^(m_w - M) per row
+  float row_m[ROWS], row_l[ROWS];
+  int row_parts[ROWS];        // partitions of the row's sequence
+  int32_t blk[kPartBlocks];   // the partition's block ids
 };
 
-// One run: sequences s .. s + k - 1 share partition p (2 <= k, k G <= 32 rows;
-// row r = member r / G, head r % G).  K/V of the partition's 32 blocks are
-// read once.  Each wave takes 128 tokens (8 blocks) whole:
+// 8 E4M3 codes (two words, the first code in the low byte) -> one 8-element
+// MFMA operand of fp16 or bf16 values.  Exact: both types hold every E4M3
+// value.
+template <typename QT>
+__device__ __forceinline__ u32x4 e4m3x8_to(uint32_t w0, uint32_t w1) {
+  u32x4 r;
+  if constexpr (QT::kCode == PKV_BF16) {
+    r[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, false));
+    r[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, true));
+    r[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, false));
+    r[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true));
+  } else {
+    r[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w0, 1.0f, false));
+    r[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w0, 1.0f, true));
+    r[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w1, 1.0f, false));
+    r[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w1, 1.0f, true));
+  }
+  return r;
+}
+
+__device__ __forceinline__ uint64_t ld8(const void* p) { return *reinterpret_cast<const uint64_t*>(p); }
+
+// One partition on MFMA for the query rows of k sequences s .. s + k - 1
+// that name the same blocks for it (16 RT rows: row r = member r / G, head
+// r % G; rows past k G repeat member 0 and are not stored).  The first n
+// tokens of the partition are valid (Masked; otherwise all kPart).  K/V of
+// the partition's blocks are read once.  Each wave takes 128 tokens (8
+// blocks) whole:
 //  * S^T = K Q^T on MFMA 16x16x32 with K rows loaded from the pool straight
 //    into operand layout: in each pair of blocks, row m = 4a + r of score
 //    tile `sub` is the pair's key 8a + 4 sub + r, so the lanes of group a own
-//    keys 8a..8a+7 (one 16-byte V chunk per dim) across the two tiles;
-//  * exact softmax over the wave's 128 keys (base 2), probabilities in fp16;
-//  * O^T += V^T P^T with V chunks loaded into operand layout and converted to
-//    fp16; the waves' (max, sum, o) are merged through LDS and written as each
-//    member's partition result.
-template <typename T, int D, int G, int OutCode>
-__device__ __forceinline__ void shared_run(int s, int k, int g, int p, SharedLds<D>& sh, void* __restrict__ out,
-                                           float* __restrict__ ws_o, float* __restrict__ ws_ml,
-                                           const typename T::bits* __restrict__ q,
-                                           const unsigned char* __restrict__ kpool,
-                                           const unsigned char* __restrict__ vpool,
-                                           const int32_t* __restrict__ tables, int max_blocks,
-                                           const int32_t* __restrict__ lens, int Hkv, int64_t num_blocks,
-                                           int max_context_len, float scale_log2, int max_parts) {
-  constexpr int DC = D / 32;   // 32-dim slices of the score contraction
-  constexpr int DT = D / 16;   // 16-dim tiles of the output
-  constexpr int RT = kRunRows / 16;
-  constexpr int TILE = D * kBlockSize * 2;  // bytes of one (block, head) tile
-  constexpr int WB = kPartBlocks / kWaves;  // blocks per wave
+//    keys 8a..8a+7 (one V operand per dim) across the two tiles.  8-bit keys
+//    are widened to the query's type, and a lane's 16-byte K chunk (16 dims)
+//    feeds two contraction slices; the query operands take the same dims;
+//  * exact softmax over the wave's keys (base 2), probabilities in fp16;
+//  * O^T += V^T P^T with V loaded into operand layout and widened to fp16;
+//    the waves' (max, sum, o) are merged through LDS and written as each
+//    member's partition result (8-bit values: times v_mul, the pool scale).
+template <typename KV, typename QT, int D, int G, int RT, bool Masked, int OutCode>
+__device__ __forceinline__ void mfma_partition(int s, int k, int n, int g, int p, RunLds<D, 16 * RT>& sh,
+                                               void* __restrict__ out, float* __restrict__ ws_o,
+                                               float* __restrict__ ws_ml, const typename QT::bits* __restrict__ q,
+                                               const unsigned char* __restrict__ kpool,
+                                               const unsigned char* __restrict__ vpool,
+                                               const int32_t* __restrict__ tables, int max_blocks,
+                                               const int32_t* __restrict__ lens, int Hkv, int64_t num_blocks,
+                                               int max_context_len, float scale_log2, float v_mul, int max_parts) {
+  constexpr bool F8 = KV::kBytes == 1;
+  static_assert(F8 || (KV::kBytes == 2 && KV::kCode == QT::kCode), "16-bit K/V take queries of their type");
+  static_assert(F8 || !Masked, "partial partitions go to MFMA for 8-bit K/V only");
+  constexpr int DC = D / 32;                         // 32-dim slices of the score contraction
+  constexpr int DT = D / 16;                         // 16-dim tiles of the output
+  constexpr int CH = D * KV::kBytes / 16;            // 16-byte K chunks per token
+  constexpr int KC = F8 ? D / 64 : DC;               // K chunks per lane and score tile
+  constexpr int VROW = kBlockSize * KV::kBytes;      // bytes of one dim of a V tile
+  constexpr int TILE = D * VROW;                     // bytes of one (block, head) tile
+  constexpr int WB = kPartBlocks / kWaves;           // blocks per wave
   static_assert(WB % 2 == 0, "waves take whole block pairs");
+  using vraw_t = typename std::conditional<F8, uint64_t, u32x4>::type;
   const int Hq = Hkv * G;
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int q4 = lane >> 4, r16 = lane & 15;
 
-  // query rows as B operands: lane (q4, r16) holds row 16 rt + r16, dims 32 dc + 8 q4 ..
+  // query rows as B operands: lane (q4, r16) holds row 16 rt + r16 and the
+  // dims of its K operand (16-bit K: 32 dc + 8 q4 ..; 8-bit K: 64 (dc/2) +
+  // 16 q4 + 8 (dc%2) ..)
   u32x4 bq[RT][DC];
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
     const int row = 16 * rt + r16;
     const int mi = row / G < k ? row / G : 0;
-    const typename T::bits* qp = q + ((int64_t)(s + mi) * Hq + g * G + row % G) * D + 8 * q4;
+    const typename QT::bits* qp = q + ((int64_t)(s + mi) * Hq + g * G + row % G) * D;
 #pragma unroll
-    for (int dc = 0; dc < DC; ++dc) bq[rt][dc] = ld16(qp + 32 * dc);
+    for (int dc = 0; dc < DC; ++dc)
+      bq[rt][dc] = ld16(qp + (F8 ? 64 * (dc >> 1) + 16 * q4 + 8 * (dc & 1) : 32 * dc + 8 * q4));
   }
 
-  // the partition's block ids, read once into LDS
-  if (tid < kPartBlocks) sh.blk[tid] = tables[(int64_t)s * max_blocks + p * kPartBlocks + tid];
+  // the partition's block ids, read once into LDS (0 past the valid tokens)
+  if (tid < kPartBlocks)
+    sh.blk[tid] = (!Masked || tid * kBlockSize < n) ? tables[(int64_t)s * max_blocks + p * kPartBlocks + tid] : 0;
   __syncthreads();
   const int32_t* tab = sh.blk + w * WB;
-  // this lane's K row inside a block pair for score tile `sub`
-  const int k_half = r16 >> 3;                          // which block of the pair
-  const int k_tok = 8 * ((r16 >> 2) & 1) + (r16 & 3);  // token, + 4 sub
-  u32x4 ka[WB][DC];  // tile 2 kp + sub
-#pragma unroll
-  for (int kp = 0; kp < WB / 2; ++kp) {
-    const int64_t kb = clamp_block(tab[2 * kp + k_half], num_blocks);
-    const unsigned char* kr = kpool + ((kb * Hkv + g) * (D / 8) + q4) * (kBlockSize * 16) + k_tok * 16;
-#pragma unroll
-    for (int sub = 0; sub < 2; ++sub)
-#pragma unroll
-      for (int dc = 0; dc < DC; ++dc) ka[2 * kp + sub][dc] = ld16(kr + (4 * sub + dc * 4 * kBlockSize) * 16);
-  }
-  f32x4 st[WB][RT];
-#pragma unroll
-  for (int kt = 0; kt < WB; ++kt)
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int dc = 0; dc < DC; ++dc) acc = mfma_qk<T>(ka[kt][dc], bq[rt][dc], acc);
-      st[kt][rt] = acc;
-    }
-  // the V operand loads are issued next, ahead of the softmax
-  u32x4 vraw[WB / 2][DT];
-#pragma unroll
-  for (int kp = 0; kp < WB / 2; ++kp) {
-    const int64_t vb = clamp_block(tab[2 * kp + (q4 >> 1)], num_blocks);
-    const unsigned char* vr = vpool + (vb * Hkv + g) * (int64_t)TILE + r16 * 32 + (q4 & 1) * 16;
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) vraw[kp][dt] = ld16(vr + dt * 16 * 32);
-  }
-  // exact softmax over the wave's keys, per row
+  const int wbase = w * WB * kBlockSize;  // the wave's first token in the partition
   float m[RT], l[RT];
-  u32x4 pb[WB / 2][RT];
-#pragma unroll
-  for (int rt = 0; rt < RT; ++rt) {
-    float mx = -INFINITY;
-#pragma unroll
-    for (int kt = 0; kt < WB; ++kt)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        st[kt][rt][r] *= scale_log2;
-        mx = fmaxf(mx, st[kt][rt][r]);
-      }
-    m[rt] = rows4_max(mx);
-    float ls = 0.f;
-#pragma unroll
-    for (int kt = 0; kt < WB; ++kt)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        st[kt][rt][r] = __builtin_amdgcn_exp2f(st[kt][rt][r] - m[rt]);
-        ls += st[kt][rt][r];
-      }
-    l[rt] = rows4_sum(ls);
-#pragma unroll
-    for (int kp = 0; kp < WB / 2; ++kp)
-      pb[kp][rt] = u32x4{pack_f16x2(st[2 * kp][rt][0], st[2 * kp][rt][1]),
-                         pack_f16x2(st[2 * kp][rt][2], st[2 * kp][rt][3]),
-                         pack_f16x2(st[2 * kp + 1][rt][0], st[2 * kp + 1][rt][1]),
-                         pack_f16x2(st[2 * kp + 1][rt][2], st[2 * kp + 1][rt][3])};
-  }
-  // O^T += V^T P^T: lane (q4, r16) holds dim 16 dt + r16, keys 8 q4 .. 8 q4 + 7 of the pair
   f32x4 o[RT][DT];
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) o[rt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  if (!Masked || wbase < n) {  // uniform per wave
+    // this lane's K row inside a block pair for score tile `sub`
+    const int k_half = r16 >> 3;                          // which block of the pair
+    const int k_tok = 8 * ((r16 >> 2) & 1) + (r16 & 3);  // token, + 4 sub
+    u32x4 ka[WB][KC];  // tile 2 kp + sub
 #pragma unroll
-  for (int kp = 0; kp < WB / 2; ++kp)
+    for (int kp = 0; kp < WB / 2; ++kp) {
+      const bool in = !Masked || wbase + (2 * kp + k_half) * kBlockSize < n;
+      const int64_t kb = clamp_block(tab[2 * kp + k_half], num_blocks);
+      const unsigned char* kr = kpool + ((kb * Hkv + g) * CH + q4) * (kBlockSize * 16) + k_tok * 16;
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      const u32x4 va = to_f16x8<T>(vraw[kp][dt]);
+      for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
-      for (int rt = 0; rt < RT; ++rt) o[rt][dt] = mfma_f16(va, pb[kp][rt], o[rt][dt]);
+        for (int c = 0; c < KC; ++c)
+          ka[2 * kp + sub][c] = in ? ld16(kr + (4 * sub + c * 4 * kBlockSize) * 16) : u32x4{0u, 0u, 0u, 0u};
     }
+    f32x4 st[WB][RT];
+    if constexpr (F8) {
+#pragma unroll
+      for (int kt = 0; kt < WB; ++kt)
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) st[kt][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kt = 0; kt < WB; ++kt)
+#pragma unroll
+        for (int dc = 0; dc < DC; ++dc) {
+          const u32x4 a = e4m3x8_to<QT>(ka[kt][dc >> 1][2 * (dc & 1)], ka[kt][dc >> 1][2 * (dc & 1) + 1]);
+#pragma unroll
+          for (int rt = 0; rt < RT; ++rt) st[kt][rt] = mfma_qk<QT>(a, bq[rt][dc], st[kt][rt]);
+        }
+    } else {
+#pragma unroll
+      for (int kt = 0; kt < WB; ++kt)
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int dc = 0; dc < DC; ++dc) acc = mfma_qk<QT>(ka[kt][dc], bq[rt][dc], acc);
+          st[kt][rt] = acc;
+        }
+    }
+    // the V operand loads are issued next, ahead of the softmax: lane (q4,
+    // r16) takes dim 16 dt + r16, keys 8 q4 .. 8 q4 + 7 of the pair (half of
+    // the dim's row in block q4 / 2)
+    vraw_t vraw[WB / 2][DT];
+#pragma unroll
+    for (int kp = 0; kp < WB / 2; ++kp) {
+      const bool in = !Masked || wbase + (2 * kp + (q4 >> 1)) * kBlockSize < n;
+      const int64_t vb = clamp_block(tab[2 * kp + (q4 >> 1)], num_blocks);
+      const unsigned char* vr = vpool + (vb * Hkv + g) * (int64_t)TILE + r16 * VROW + (q4 & 1) * (VROW / 2);
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        if constexpr (F8)
+          vraw[kp][dt] = in ? ld8(vr + dt * 16 * VROW) : 0ull;
+        else
+          vraw[kp][dt] = ld16(vr + dt * 16 * VROW);
+      }
+    }
+    // exact softmax over the wave's keys, per row
+    u32x4 pb[WB / 2][RT];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kt = 0; kt < WB; ++kt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          float x = st[kt][rt][r] * scale_log2;
+          if constexpr (Masked) {  // keys past the context may hold anything
+            const int key = wbase + (kt >> 1) * 2 * kBlockSize + 8 * q4 + 4 * (kt & 1) + r;
+            x = key < n ? x : -INFINITY;
+          }
+          st[kt][rt][r] = x;
+          mx = fmaxf(mx, x);
+        }
+      m[rt] = rows4_max(mx);
+      float ls = 0.f;
+#pragma unroll
+      for (int kt = 0; kt < WB; ++kt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          st[kt][rt][r] = __builtin_amdgcn_exp2f(st[kt][rt][r] - m[rt]);
+          ls += st[kt][rt][r];
+        }
+      l[rt] = rows4_sum(ls);
+#pragma unroll
+      for (int kp = 0; kp < WB / 2; ++kp)
+        pb[kp][rt] = u32x4{pack_f16x2(st[2 * kp][rt][0], st[2 * kp][rt][1]),
+                           pack_f16x2(st[2 * kp][rt][2], st[2 * kp][rt][3]),
+                           pack_f16x2(st[2 * kp + 1][rt][0], st[2 * kp + 1][rt][1]),
+                           pack_f16x2(st[2 * kp + 1][rt][2], st[2 * kp + 1][rt][3])};
+    }
+    // O^T += V^T P^T: lane (q4, r16) holds dim 16 dt + r16, keys 8 q4 .. 8 q4 + 7 of the pair
+#pragma unroll
+    for (int kp = 0; kp < WB / 2; ++kp)
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        u32x4 va;
+        if constexpr (F8) {
+          uint64_t bytes = vraw[kp][dt];
+          if constexpr (Masked) {  // zero the codes of keys past the context (they may be NaN codes)
+            const int nv = n - (wbase + kp * 2 * kBlockSize + 8 * q4);
+            bytes &= nv >= 8 ? ~0ull : (nv <= 0 ? 0ull : (1ull << (8 * nv)) - 1ull);
+          }
+          va = e4m3x8_to<F16>((uint32_t)bytes, (uint32_t)(bytes >> 32));
+        } else {
+          va = to_f16x8<KV>(vraw[kp][dt]);
+        }
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) o[rt][dt] = mfma_f16(va, pb[kp][rt], o[rt][dt]);
+      }
+  } else {
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      m[rt] = -INFINITY;  // a wave without keys: weight 0 in the merge
+      l[rt] = 0.f;
+    }
+  }
   // merge the waves: lane (q4, r16) holds o^T[dim 16 dt + 4 q4 + r][row 16 rt + r16]
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
@@ -540,6 +644,7 @@ __device__ __forceinline__ void shared_run(int s, int k, int g, int p, SharedLds
     float acc = 0.f;
 #pragma unroll
     for (int x = 0; x < kWaves; ++x) acc = fmaf(sh.wgt[row][x], sh.o[x][row][j], acc);
+    if constexpr (F8) acc *= v_mul;
     const int64_t orow = (int64_t)(s + row / G) * Hq + g * G + row % G;
     if (sh.row_parts[row] == 1) {
       store_out<OutCode>(out, orow * D + j, acc / sh.row_l[row]);
@@ -556,19 +661,19 @@ __device__ __forceinline__ void shared_run(int s, int k, int g, int p, SharedLds
 
 // Grid (KV head, run window, partition): finds the runs of the window's
 // KM = kRunRows / G sequences for partition p and serves each.
-template <typename T, int D, int G, int OutCode>
+template <typename KV, typename QT, int D, int G, int OutCode>
 __global__ void __launch_bounds__(kThreads, 2)
 decode_shared_kernel(void* __restrict__ out, float* __restrict__ ws_o, float* __restrict__ ws_ml,
-                     const typename T::bits* __restrict__ q, const unsigned char* __restrict__ kpool,
+                     const typename QT::bits* __restrict__ q, const unsigned char* __restrict__ kpool,
                      const unsigned char* __restrict__ vpool, const int32_t* __restrict__ tables,
                      int max_blocks, const int32_t* __restrict__ lens, int B, int Hkv, int64_t num_blocks,
-                     int max_context_len, float scale_log2, int max_parts) {
-  if constexpr (T::kBytes != 2) {
+                     int max_context_len, float scale_log2, float v_mul, int max_parts) {
+  if constexpr (KV::kBytes == 4) {
     return;
   } else {
     constexpr int KM = kRunRows / G;
     static_assert(KM <= 32, "run window fits a 32-bit mask");
-    __shared__ __attribute__((aligned(16))) SharedLds<D> sh;
+    __shared__ __attribute__((aligned(16))) RunLds<D, kRunRows> sh;
     __shared__ uint32_t joins;
     const int g = blockIdx.x, win = blockIdx.y, p = blockIdx.z;
     const int s_first = win * KM;
@@ -609,10 +714,45 @@ decode_shared_kernel(void* __restrict__ out, float* __restrict__ ws_o, float* __
       if (!((jm >> (s0 + 1)) & 1u) || ((jm >> s0) & 1u)) continue;
       int k = 2;
       while (s0 + k < KM && ((jm >> (s0 + k)) & 1u)) ++k;
-      shared_run<T, D, G, OutCode>(s_first + s0, k, g, p, sh, out, ws_o, ws_ml, q, kpool, vpool, tables,
-                                   max_blocks, lens, Hkv, num_blocks, max_context_len, scale_log2, max_parts);
+      mfma_partition<KV, QT, D, G, kRunRows / 16, false, OutCode>(
+          s_first + s0, k, kPart, g, p, sh, out, ws_o, ws_ml, q, kpool, vpool, tables, max_blocks, lens, Hkv,
+          num_blocks, max_context_len, scale_log2, v_mul, max_parts);
     }
   }
+}
+
+// The per-sequence partitions of an 8-bit cache, on MFMA as well: widening
+// the codes costs one conversion per two values, more than the VALU kernel's
+// issue budget leaves at full bandwidth, while the matrix cores have room to
+// pad the G query rows of a KV head to 16.
+template <typename QT, int D, int G, int OutCode>
+__global__ void __launch_bounds__(kThreads, 2)
+decode_fp8_partition_kernel(void* __restrict__ out, float* __restrict__ ws_o, float* __restrict__ ws_ml,
+                            const typename QT::bits* __restrict__ q, const unsigned char* __restrict__ kpool,
+                            const unsigned char* __restrict__ vpool, const int32_t* __restrict__ tables,
+                            int max_blocks, const int32_t* __restrict__ lens, int Hkv, int64_t num_blocks,
+                            int max_context_len, float scale_log2, float v_mul, int max_parts) {
+  static_assert(G <= 16, "one 16-row tile");
+  __shared__ __attribute__((aligned(16))) RunLds<D, 16> sh;
+  // last partitions first, as in decode_partition_kernel
+  const int g = blockIdx.x, s = blockIdx.y, p = gridDim.z - 1 - blockIdx.z;
+  const int Hq = Hkv * G;
+  const int Lraw = lens[s];
+  const ShareProbe pr = probe_share<FP8, G>(tables, max_blocks, lens, gridDim.y, s, p);
+  const int L = clamp_len(Lraw, max_context_len);
+  const int nparts = (L + kPart - 1) / kPart;
+  if (p >= (nparts > 0 ? nparts : 1)) return;
+  if (L == 0) {  // defined result for an empty context: zeros
+    for (int i = threadIdx.x; i < G * D; i += kThreads)
+      store_out<OutCode>(out, ((int64_t)s * Hq + g * G) * D + i, 0.f);
+    return;
+  }
+  if (in_shared_run<FP8, G>(pr, tables, max_blocks, max_context_len, s, p, L)) return;
+  const int t0 = p * kPart;
+  const int n = (L - t0) < kPart ? (L - t0) : kPart;  // tokens in this partition, >= 1
+  mfma_partition<FP8, QT, D, G, 1, true, OutCode>(s, 1, n, g, p, sh, out, ws_o, ws_ml, q, kpool, vpool, tables,
+                                                  max_blocks, lens, Hkv, num_blocks, max_context_len, scale_log2,
+                                                  v_mul, max_parts);
 }
 
 template <typename T, int D, int G, int OutCode>
@@ -634,7 +774,9 @@ decode_partition_kernel(void* __restrict__ out, float* __restrict__ ws_o, float*
   const int g = blockIdx.x, s = blockIdx.y, p = gridDim.z - 1 - blockIdx.z;
   const int Hq = Hkv * G;
 
-  const int L = clamp_len(lens[s], max_context_len);
+  const int Lraw = lens[s];
+  const ShareProbe pr = probe_share<T, G>(tables, max_blocks, lens, gridDim.y, s, p);
+  const int L = clamp_len(Lraw, max_context_len);
   const int nparts = (L + kPart - 1) / kPart;
   if (p >= (nparts > 0 ? nparts : 1)) return;
   if (L == 0) {  // defined result for an empty context: zeros
@@ -642,7 +784,7 @@ decode_partition_kernel(void* __restrict__ out, float* __restrict__ ws_o, float*
       store_out<OutCode>(out, ((int64_t)s * Hq + g * G) * D + i, 0.f);
     return;
   }
-  if (in_shared_run<T, G>(tables, max_blocks, lens, gridDim.y, max_context_len, s, p)) return;
+  if (in_shared_run<T, G>(pr, tables, max_blocks, max_context_len, s, p, L)) return;
   const int t0 = p * kPart;
   const int n = (L - t0) < kPart ? (L - t0) : kPart;  // tokens in this partition
   const int32_t* tab = tables + (int64_t)s * max_blocks + t0 / kBlockSize;
@@ -695,48 +837,81 @@ struct DecodeArgs {
   int64_t num_blocks;
   int max_context_len;
   float scale_log2;
+  float v_mul;  // 8-bit cache: the V pool's scale
   int max_parts;
   hipStream_t stream;
 };
 
+template <typename KV, typename QT, int D, int G, int OutCode>
+void launch_shared(const DecodeArgs& a) {
+  constexpr int KM = kRunRows / G;
+  hipLaunchKernelGGL((decode_shared_kernel<KV, QT, D, G, OutCode>),
+                     dim3((unsigned)a.Hkv, (unsigned)((a.B + KM - 1) / KM), (unsigned)a.max_parts), dim3(kThreads),
+                     0, a.stream, a.out, a.ws_o, a.ws_ml, (const typename QT::bits*)a.q, a.kpool, a.vpool,
+                     a.tables, a.max_blocks, a.lens, a.B, a.Hkv, a.num_blocks, a.max_context_len, a.scale_log2,
+                     a.v_mul, a.max_parts);
+}
+
+template <int D, int OutCode>
+void launch_reduce(const DecodeArgs& a, int G) {
+  if (a.max_parts > 1)
+    hipLaunchKernelGGL((decode_reduce_kernel<D, OutCode>), dim3((unsigned)a.Hq, (unsigned)a.B), dim3(64), 0,
+                       a.stream, a.out, a.ws_o, a.ws_ml, a.lens, a.Hq, G, a.max_context_len, a.max_parts);
+}
+
 template <typename T, int D, int G, int OutCode>
 void launch_decode(const DecodeArgs& a, bool partitions, bool reduce) {
-  if (partitions && T::kBytes == 2) {
-    constexpr int KM = kRunRows / G;
-    hipLaunchKernelGGL((decode_shared_kernel<T, D, G, OutCode>),
-                       dim3((unsigned)a.Hkv, (unsigned)((a.B + KM - 1) / KM), (unsigned)a.max_parts),
-                       dim3(kThreads), 0, a.stream, a.out, a.ws_o, a.ws_ml,
-                       (const typename T::bits*)a.q, a.kpool, a.vpool, a.tables, a.max_blocks, a.lens, a.B,
-                       a.Hkv, a.num_blocks, a.max_context_len, a.scale_log2, a.max_parts);
-  }
+  if (partitions && T::kBytes == 2) launch_shared<T, T, D, G, OutCode>(a);
   if (partitions)
     hipLaunchKernelGGL((decode_partition_kernel<T, D, G, OutCode>),
                        dim3((unsigned)a.Hkv, (unsigned)a.B, (unsigned)a.max_parts), dim3(kThreads), 0,
                        a.stream, a.out, a.ws_o, a.ws_ml, (const typename T::bits*)a.q, a.kpool, a.vpool,
                        a.tables, a.max_blocks, a.lens, a.Hkv, a.num_blocks, a.max_context_len,
                        a.scale_log2, a.max_parts);
-  if (reduce && a.max_parts > 1)
-    hipLaunchKernelGGL((decode_reduce_kernel<D, OutCode>), dim3((unsigned)a.Hq, (unsigned)a.B),
-                       dim3(64), 0, a.stream, a.out, a.ws_o, a.ws_ml, a.lens, a.Hq, G,
-                       a.max_context_len, a.max_parts);
+  if (reduce) launch_reduce<D, OutCode>(a, G);
 }
 
-template <typename T, int D, int OutCode>
+// 8-bit cache: shared runs, then the per-sequence MFMA partitions, then the
+// reduction.
+template <typename QT, int D, int G, int OutCode>
+void launch_decode_fp8(const DecodeArgs& a, bool partitions, bool reduce) {
+  if (partitions) {
+    launch_shared<FP8, QT, D, G, OutCode>(a);
+    hipLaunchKernelGGL((decode_fp8_partition_kernel<QT, D, G, OutCode>),
+                       dim3((unsigned)a.Hkv, (unsigned)a.B, (unsigned)a.max_parts), dim3(kThreads), 0, a.stream,
+                       a.out, a.ws_o, a.ws_ml, (const typename QT::bits*)a.q, a.kpool, a.vpool, a.tables,
+                       a.max_blocks, a.lens, a.Hkv, a.num_blocks, a.max_context_len, a.scale_log2, a.v_mul,
+                       a.max_parts);
+  }
+  if (reduce) launch_reduce<D, OutCode>(a, G);
+}
+
+// Launcher<T, D, G, OutCode>::run(args, partitions, reduce)
+template <typename T, int D, int G, int OutCode>
+struct Plain {
+  static void run(const DecodeArgs& a, bool pa, bool re) { launch_decode<T, D, G, OutCode>(a, pa, re); }
+};
+template <typename QT, int D, int G, int OutCode>
+struct Fp8 {
+  static void run(const DecodeArgs& a, bool pa, bool re) { launch_decode_fp8<QT, D, G, OutCode>(a, pa, re); }
+};
+
+template <template <typename, int, int, int> class Launcher, typename T, int D, int OutCode>
 int dispatch_g(const DecodeArgs& a, int G, bool pa, bool re) {
   switch (G) {
-    case 1: launch_decode<T, D, 1, OutCode>(a, pa, re); return 0;
-    case 2: launch_decode<T, D, 2, OutCode>(a, pa, re); return 0;
-    case 4: launch_decode<T, D, 4, OutCode>(a, pa, re); return 0;
-    case 8: launch_decode<T, D, 8, OutCode>(a, pa, re); return 0;
-    case 16: launch_decode<T, D, 16, OutCode>(a, pa, re); return 0;
+    case 1: Launcher<T, D, 1, OutCode>::run(a, pa, re); return 0;
+    case 2: Launcher<T, D, 2, OutCode>::run(a, pa, re); return 0;
+    case 4: Launcher<T, D, 4, OutCode>::run(a, pa, re); return 0;
+    case 8: Launcher<T, D, 8, OutCode>::run(a, pa, re); return 0;
+    case 16: Launcher<T, D, 16, OutCode>::run(a, pa, re); return 0;
     default: return -1;
   }
 }
 
-template <typename T, int OutCode>
+template <template <typename, int, int, int> class Launcher, typename T, int OutCode>
 int dispatch_d(const DecodeArgs& a, int D, int G, bool pa, bool re) {
-  if (D == 64) return dispatch_g<T, 64, OutCode>(a, G, pa, re);
-  if (D == 128) return dispatch_g<T, 128, OutCode>(a, G, pa, re);
+  if (D == 64) return dispatch_g<Launcher, T, 64, OutCode>(a, G, pa, re);
+  if (D == 128) return dispatch_g<Launcher, T, 128, OutCode>(a, G, pa, re);
   return -1;
 }
 
@@ -756,16 +931,25 @@ extern "C" int64_t paged_attention_decode_workspace_bytes(int32_t num_seqs, int3
   return (int64_t)num_seqs * n_q_heads * parts * (head_dim + 2) * (int64_t)sizeof(float);
 }
 
-static int decode_impl(const char* fn, bool pa, bool re, void* out, int32_t out_dtype, const void* q,
-                       const void* k_pool, const void* v_pool, const int32_t* block_tables,
-                       int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t num_seqs,
-                       int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim, int32_t block_size,
-                       int64_t num_blocks, int32_t max_context_len, float scale, int32_t kv_dtype,
-                       void* workspace, int64_t workspace_bytes, void* stream) {
+// Validation and dispatch shared by the 16-bit/fp32 entry points (fp8 =
+// false: q in the KV dtype, unit scales) and the 8-bit one.
+static int decode_impl(const char* fn, bool pa, bool re, bool fp8, void* out, int32_t out_dtype, const void* q,
+                       int32_t q_dtype, const void* k_pool, const void* v_pool, float k_scale, float v_scale,
+                       const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
+                       int32_t num_seqs, int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
+                       int32_t block_size, int64_t num_blocks, int32_t max_context_len, float scale,
+                       int32_t kv_dtype, void* workspace, int64_t workspace_bytes, void* stream) {
   const std::string F(fn);
   if (!pkv::esize_of(kv_dtype)) return fail(PKV_EINVAL, F + ": unknown kv dtype");
-  if (out_dtype != PKV_F32 && out_dtype != kv_dtype)
-    return fail(PKV_EINVAL, F + ": out dtype must be f32 or the kv dtype");
+  if (fp8 != (kv_dtype == PKV_FP8_E4M3))
+    return fail(PKV_EINVAL, fp8 ? F + ": pools must hold E4M3 codes"
+                                : F + ": 8-bit pools are read by paged_attention_decode_fp8");
+  if (fp8 && q_dtype != PKV_F16 && q_dtype != PKV_BF16)
+    return fail(PKV_EINVAL, F + ": q dtype must be f16 or bf16");
+  if (out_dtype != PKV_F32 && out_dtype != q_dtype)
+    return fail(PKV_EINVAL, F + ": out dtype must be f32 or the query's dtype");
+  if (fp8 && (!std::isfinite(k_scale) || !std::isfinite(v_scale) || !(k_scale > 0.f) || !(v_scale > 0.f)))
+    return fail(PKV_EINVAL, F + ": k_scale and v_scale must be finite and > 0");
   if (block_size != pkv::kBlockSize) return fail(PKV_EUNSUPPORTED, "block_size must be 16");
   if (head_dim != 64 && head_dim != 128) return fail(PKV_EUNSUPPORTED, "head_dim must be 64 or 128");
   if (num_seqs < 0 || num_seqs > 65535 || n_kv_heads < 1 || n_q_heads < 1 || n_kv_heads > 65535 ||
@@ -804,18 +988,30 @@ static int decode_impl(const char* fn, bool pa, bool re, void* out, int32_t out_
   a.Hkv = n_kv_heads;
   a.num_blocks = num_blocks;
   a.max_context_len = max_context_len;
-  a.scale_log2 = (float)((double)scale * 1.4426950408889634);
+  // scores in base 2; an 8-bit key pool's scale folds into the softmax scale
+  a.scale_log2 = (float)((double)scale * (double)k_scale * 1.4426950408889634);
+  if (!std::isfinite(a.scale_log2)) return fail(PKV_EINVAL, F + ": scale * k_scale overflows");
+  a.v_mul = v_scale;
   a.max_parts = max_parts;
   a.stream = (hipStream_t)stream;
+  using pkv::dispatch_d;
+  using pkv::Fp8;
+  using pkv::Plain;
   auto dispatch = [&](bool do_pa, bool do_re) -> int {
     switch (kv_dtype) {
-      case PKV_F32: return pkv::dispatch_d<pkv::F32, PKV_F32>(a, head_dim, G, do_pa, do_re);
+      case PKV_F32: return dispatch_d<Plain, pkv::F32, PKV_F32>(a, head_dim, G, do_pa, do_re);
       case PKV_F16:
-        return out_dtype == PKV_F32 ? pkv::dispatch_d<pkv::F16, PKV_F32>(a, head_dim, G, do_pa, do_re)
-                                    : pkv::dispatch_d<pkv::F16, PKV_F16>(a, head_dim, G, do_pa, do_re);
+        return out_dtype == PKV_F32 ? dispatch_d<Plain, pkv::F16, PKV_F32>(a, head_dim, G, do_pa, do_re)
+                                    : dispatch_d<Plain, pkv::F16, PKV_F16>(a, head_dim, G, do_pa, do_re);
       case PKV_BF16:
-        return out_dtype == PKV_F32 ? pkv::dispatch_d<pkv::BF16, PKV_F32>(a, head_dim, G, do_pa, do_re)
-                                    : pkv::dispatch_d<pkv::BF16, PKV_BF16>(a, head_dim, G, do_pa, do_re);
+        return out_dtype == PKV_F32 ? dispatch_d<Plain, pkv::BF16, PKV_F32>(a, head_dim, G, do_pa, do_re)
+                                    : dispatch_d<Plain, pkv::BF16, PKV_BF16>(a, head_dim, G, do_pa, do_re);
+      case PKV_FP8_E4M3:
+        if (q_dtype == PKV_BF16)
+          return out_dtype == PKV_F32 ? dispatch_d<Fp8, pkv::BF16, PKV_F32>(a, head_dim, G, do_pa, do_re)
+                                      : dispatch_d<Fp8, pkv::BF16, PKV_BF16>(a, head_dim, G, do_pa, do_re);
+        return out_dtype == PKV_F32 ? dispatch_d<Fp8, pkv::F16, PKV_F32>(a, head_dim, G, do_pa, do_re)
+                                    : dispatch_d<Fp8, pkv::F16, PKV_F16>(a, head_dim, G, do_pa, do_re);
     }
     return -1;
   };
@@ -833,16 +1029,36 @@ static int decode_impl(const char* fn, bool pa, bool re, void* out, int32_t out_
       int32_t block_size, int64_t num_blocks, int32_t max_context_len, float scale,                \
       int32_t kv_dtype, void *workspace, int64_t workspace_bytes, void *stream
 #define PKV_DECODE_ARGS                                                                            \
-  out, out_dtype, q, k_pool, v_pool, block_tables, max_blocks_per_seq, context_lens, num_seqs,     \
-      n_q_heads, n_kv_heads, head_dim, block_size, num_blocks, max_context_len, scale, kv_dtype,   \
-      workspace, workspace_bytes, stream
+  out, out_dtype, q, kv_dtype, k_pool, v_pool, 1.0f, 1.0f, block_tables, max_blocks_per_seq,       \
+      context_lens, num_seqs, n_q_heads, n_kv_heads, head_dim, block_size, num_blocks,             \
+      max_context_len, scale, kv_dtype, workspace, workspace_bytes, stream
 
 extern "C" int paged_attention_decode(PKV_DECODE_PARAMS) {
-  return decode_impl("paged_attention_decode", true, true, PKV_DECODE_ARGS);
+  return decode_impl("paged_attention_decode", true, true, false, PKV_DECODE_ARGS);
 }
 extern "C" int paged_attention_decode_partitions(PKV_DECODE_PARAMS) {
-  return decode_impl("paged_attention_decode_partitions", true, false, PKV_DECODE_ARGS);
+  return decode_impl("paged_attention_decode_partitions", true, false, false, PKV_DECODE_ARGS);
 }
 extern "C" int paged_attention_decode_reduce(PKV_DECODE_PARAMS) {
-  return decode_impl("paged_attention_decode_reduce", false, true, PKV_DECODE_ARGS);
+  return decode_impl("paged_attention_decode_reduce", false, true, false, PKV_DECODE_ARGS);
+}
+#define PKV_DECODE_FP8_PARAMS                                                                      \
+  void *out, int32_t out_dtype, const void *q, int32_t q_dtype, const void *k_pool,                \
+      const void *v_pool, float k_scale, float v_scale, const int32_t *block_tables,               \
+      int32_t max_blocks_per_seq, const int32_t *context_lens, int32_t num_seqs, int32_t n_q_heads, \
+      int32_t n_kv_heads, int32_t head_dim, int32_t block_size, int64_t num_blocks,                \
+      int32_t max_context_len, float scale, void *workspace, int64_t workspace_bytes, void *stream
+#define PKV_DECODE_FP8_ARGS                                                                        \
+  out, out_dtype, q, q_dtype, k_pool, v_pool, k_scale, v_scale, block_tables, max_blocks_per_seq,  \
+      context_lens, num_seqs, n_q_heads, n_kv_heads, head_dim, block_size, num_blocks,             \
+      max_context_len, scale, PKV_FP8_E4M3, workspace, workspace_bytes, stream
+
+extern "C" int paged_attention_decode_fp8(PKV_DECODE_FP8_PARAMS) {
+  return decode_impl("paged_attention_decode_fp8", true, true, true, PKV_DECODE_FP8_ARGS);
+}
+extern "C" int paged_attention_decode_fp8_partitions(PKV_DECODE_FP8_PARAMS) {
+  return decode_impl("paged_attention_decode_fp8_partitions", true, false, true, PKV_DECODE_FP8_ARGS);
+}
+extern "C" int paged_attention_decode_fp8_reduce(PKV_DECODE_FP8_PARAMS) {
+  return decode_impl("paged_attention_decode_fp8_reduce", false, true, true, PKV_DECODE_FP8_ARGS);
 }

@@ -30,6 +30,12 @@ struct BF16 {
   static constexpr int kCode = PKV_BF16;
   static constexpr int kBytes = 2;
 };
+// OCP E4M3 codes of the 8-bit cache (values are code * the pool's scale).
+struct FP8 {
+  using bits = uint8_t;
+  static constexpr int kCode = PKV_FP8_E4M3;
+  static constexpr int kBytes = 1;
+};
 
 __device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }

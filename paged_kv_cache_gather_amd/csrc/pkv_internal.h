@@ -19,6 +19,7 @@ inline int esize_of(int32_t dtype) {
     case PKV_F32: return 4;
     case PKV_F16: return 2;
     case PKV_BF16: return 2;
+    case PKV_FP8_E4M3: return 1;
     default: return 0;
   }
 }

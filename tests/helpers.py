@@ -60,3 +60,28 @@ def prefill_reference(w, c, rows=None, n_threads=8):
     out, _ = oracle.attention(oracle.decode(w.dtype, qb), ctx + rows, oracle.decode(w.dtype, k),
                               oracle.decode(w.dtype, v), w.scale, n_threads=n_threads)
     return out
+
+
+# scales of the 8-bit cache in the tests: the synthetic values are standard
+# normal quantiles (|x| < 4.4), so these map them to at most ~350 / ~430,
+# inside E4M3's 448 (not powers of two, so the reciprocal rounds)
+FP8_K_SCALE, FP8_V_SCALE = 0.0125, 0.0103
+
+
+def quantised_kv(w, kind, idx, t0, t1, k_scale=FP8_K_SCALE, v_scale=FP8_V_SCALE):
+    """Dequantised fp64 K/V of positions [t0, t1): the workload's rows put
+    through the oracle's E4M3 quantiser and read back with the scales."""
+    k, v = w.kv(kind, idx, t0, t1)
+    kq = oracle.quantize_e4m3(oracle.decode(w.dtype, k).astype(np.float32), k_scale)
+    vq = oracle.quantize_e4m3(oracle.decode(w.dtype, v).astype(np.float32), v_scale)
+    return oracle.dequantize_e4m3(kq, k_scale), oracle.dequantize_e4m3(vq, v_scale)
+
+
+def decode_reference_fp8(w, s, k_scale=FP8_K_SCALE, v_scale=FP8_V_SCALE):
+    """Oracle output [Hq, d] for decode sequence s over an 8-bit cache."""
+    L = int(w.decode_lens[s])
+    k, v = quantised_kv(w, "decode", s, 0, L, k_scale, v_scale)
+    q = w.q("decode", s, L - 1, L)
+    out, ws = oracle.attention(oracle.decode(w.dtype, q), [L - 1], k, v, w.scale)
+    assert np.all(np.abs(ws - 1) < 1e-9)
+    return out[0]

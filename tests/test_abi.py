@@ -164,3 +164,43 @@ def test_device_entry_points_validate_before_launch():
     assert pkv.paged_attention_decode_workspace_bytes(256, 32, 128, 512) == 0
     part = pkv.paged_attention_decode_partition_size()
     assert pkv.paged_attention_decode_workspace_bytes(256, 32, 128, 4096) == 256 * 32 * (-(-4096 // part)) * 130 * 4
+
+
+def test_fp8_entry_points_validate_before_launch():
+    lib = ctypes.CDLL(pkv.LIB_PATH)
+    f8, bf16, f32 = pkv.PKV_FP8_E4M3, pkv.PKV_BF16, pkv.PKV_F32
+    fake = ctypes.c_void_p(1 << 20)  # never dereferenced: validation fails first
+    i64, flt = ctypes.c_int64, ctypes.c_float
+    lib.paged_attention_decode.restype = ctypes.c_int
+    # 8-bit pools through the 16-bit entry point
+    rc = lib.paged_attention_decode(fake, f32, fake, fake, fake, fake, 4, fake, 1, 32, 8, 128, 16, i64(8), 64,
+                                    flt(0.1), f8, fake, i64(1 << 20), None)
+    assert rc == pkv.PKV_EINVAL
+    lib.paged_attention_decode_fp8.restype = ctypes.c_int
+
+    def dec(q_dtype=bf16, out_dtype=f32, ks=1.0, vs=1.0, d=128):
+        return lib.paged_attention_decode_fp8(fake, out_dtype, fake, q_dtype, fake, fake, flt(ks), flt(vs), fake, 4,
+                                              fake, 1, 32, 8, d, 16, i64(8), 64, flt(0.1), fake, i64(1 << 20), None)
+    for ks, vs in ((0.0, 1.0), (1.0, -2.0), (float("inf"), 1.0), (1.0, float("nan"))):
+        assert dec(ks=ks, vs=vs) == pkv.PKV_EINVAL
+    assert dec(q_dtype=f32) == pkv.PKV_EINVAL        # queries must be 16-bit
+    assert dec(q_dtype=f8) == pkv.PKV_EINVAL
+    assert dec(out_dtype=pkv.PKV_F16) == pkv.PKV_EINVAL  # out: f32 or the query's dtype
+    assert dec(d=96) == pkv.PKV_EUNSUPPORTED
+    lib.reshape_and_cache_fp8.restype = ctypes.c_int
+
+    def write(src=bf16, ks=1.0, vs=1.0):
+        return lib.reshape_and_cache_fp8(fake, fake, src, i64(1024), i64(1024), fake, fake, fake, i64(4), i64(8), 8,
+                                         128, 16, flt(ks), flt(vs), None)
+    assert write(src=f8) == pkv.PKV_EINVAL
+    assert write(ks=0.0) == pkv.PKV_EINVAL and write(vs=float("inf")) == pkv.PKV_EINVAL
+    assert write(ks=1e-45) == pkv.PKV_EINVAL  # reciprocal overflows
+
+
+def test_fp8_pool_sizing():
+    # one byte per element: half the bytes per token of a 16-bit cache, twice the blocks per budget
+    assert pkv.paged_kv_bytes_per_token(32, 8, 128, "fp8_e4m3") == oracle.kv_bytes_per_token(32, 8, 128, 1)
+    budget = 54 << 30
+    assert pkv.paged_kv_blocks_for_budget(budget, 32, 8, 128, "fp8_e4m3") == oracle.blocks_for_budget(
+        budget, 32, 8, 128, 1)
+    assert pkv.paged_kv_pool_bytes(1024, 8, 128, "fp8_e4m3") == (1024 * 8 * 16 * 128,) * 2
