@@ -50,6 +50,8 @@ def _lib():
         L.orc_copy_blocks.argtypes = [ctypes.c_int, P, P, P, i64, i64, i32, i32, i32]
         L.orc_attention.argtypes = [i64, P, P, i64, P, P, i32, i32, i32, dbl, P, P, P, i32]
         L.orc_quantize_e4m3.argtypes = [P, i64, ctypes.c_float, P]
+        L.orc_swap_blocks.argtypes = [ctypes.c_int, P, P, i64, P, P, i64, P, i64, i32, i32, i32]
+        L.orc_swap_blocks.restype = ctypes.c_int
         for f in (L.orc_decode, L.orc_gather, L.orc_scatter, L.orc_copy_blocks, L.orc_attention,
                   L.orc_quantize_e4m3):
             f.restype = ctypes.c_int
@@ -166,6 +168,19 @@ def copy_blocks(dtype: str, k_pool: np.ndarray, v_pool: np.ndarray, pairs, num_b
                                 num_blocks, block_size, n_kv_heads, head_dim)
     if rc:
         raise ValueError(f"copy_blocks failed ({rc})")
+
+
+def swap_blocks(dtype: str, src_k: np.ndarray, src_v: np.ndarray, src_num_blocks: int, dst_k: np.ndarray,
+                dst_v: np.ndarray, dst_num_blocks: int, pairs, block_size: int, n_kv_heads: int, head_dim: int):
+    """Copy whole blocks between two pool pairs (GPU pool and host swap pool),
+    in place in dst: pairs [n, 2] of (src block, dst block)."""
+    pr = np.ascontiguousarray(pairs, dtype=np.int32).reshape(-1, 2)
+    assert dst_k.flags.c_contiguous and dst_v.flags.c_contiguous
+    sk, sv = np.ascontiguousarray(src_k), np.ascontiguousarray(src_v)
+    rc = _lib().orc_swap_blocks(DTYPE_CODE[dtype], _p(sk), _p(sv), src_num_blocks, _p(dst_k), _p(dst_v),
+                                dst_num_blocks, _p(pr), pr.shape[0], block_size, n_kv_heads, head_dim)
+    if rc:
+        raise ValueError(f"swap_blocks failed ({rc})")
 
 
 def pool_elems(num_blocks: int, block_size: int, n_kv_heads: int, head_dim: int) -> int:

@@ -29,6 +29,17 @@ with it table for table, slot for slot:
   prompt's last token always computed); unused labelled blocks are evicted
   least recently released first — a released block keeps its label in the
   free queue until the queue hands it out again.
+* Swapping ("The scheduler: waiting, running, swapped", vLLM Serving deep
+  dive; the CPU blocks of "Back to the queue, and into vLLM proper", Life of
+  a prompt): a preempted sequence's blocks are parked in a pool of host
+  ("CPU") blocks and restored later.  Here the CPU blocks have their own FIFO
+  queue; swapping out gives each of the sequence's blocks, in logical order, a
+  CPU block from the head of that queue (a private copy, also of blocks the
+  sequence shares) and then releases the GPU blocks as a finished sequence
+  would; swapping in gives each CPU block a GPU block from the head of the
+  free queue and returns the CPU blocks to their queue's tail.  Both are all or
+  nothing.  A swapped-out sequence can only be swapped in, freed or read
+  back; anything else on it is a state error.
 """
 from __future__ import annotations
 
@@ -37,6 +48,10 @@ from collections import deque
 
 class OutOfBlocks(Exception):
     pass
+
+
+class StateError(Exception):
+    """An operation the sequence's state does not allow (swapped out)."""
 
 
 class BlockManagerModel:
@@ -59,6 +74,10 @@ class BlockManagerModel:
         self.tokens: dict[int, list[int] | None] = {}  # None: not known
         self.queried = 0
         self.hits = 0
+        # swap space: host blocks with their own FIFO queue
+        self.num_cpu_blocks = 0
+        self.cpu_free: deque = deque()
+        self.swapped: set[int] = set()
 
     def _label_id(self, prev: int, toks) -> int:
         key = (prev, tuple(int(t) for t in toks))
@@ -128,6 +147,8 @@ class BlockManagerModel:
 
     def fork(self, parent: int, n_prefix: int) -> int:
         """New sequence sharing the blocks of the parent's first n_prefix tokens."""
+        if parent in self.swapped:
+            raise StateError("fork of a swapped-out sequence")
         if parent not in self.tables or not 0 <= n_prefix <= self.lens[parent]:
             raise ValueError("bad fork")
         nb = -(-n_prefix // self.bs)
@@ -151,6 +172,8 @@ class BlockManagerModel:
         return b
 
     def blocks_needed(self, sid: int, n: int) -> int:
+        if sid in self.swapped:
+            raise StateError("swapped out")
         L = self.lens[sid]
         need = -(-(L + n) // self.bs) - (-(-L // self.bs))
         if n > 0 and L % self.bs != 0 and self.ref[self.tables[sid][L // self.bs]] > 1:
@@ -176,6 +199,8 @@ class BlockManagerModel:
         return slots, cow
 
     def _append(self, sid: int, n: int):
+        if sid in self.swapped:
+            raise StateError("append to a swapped-out sequence")
         if sid not in self.tables or n < 0:
             raise ValueError("bad append")
         if self.blocks_needed(sid, n) > len(self.free):
@@ -200,13 +225,66 @@ class BlockManagerModel:
 
     def release(self, sid: int):
         """Finish a sequence: drop its references; blocks at zero rejoin the
-        free queue's tail at once."""
-        for b in self.tables.pop(sid):
+        free queue's tail at once (a swapped-out sequence's CPU blocks rejoin
+        theirs)."""
+        if sid in self.swapped:
+            self.cpu_free.extend(self.tables.pop(sid))
+            self.swapped.discard(sid)
+        else:
+            for b in self.tables.pop(sid):
+                self.ref[b] -= 1
+                if self.ref[b] == 0:
+                    self.free.append(b)
+        del self.lens[sid]
+        del self.tokens[sid]
+
+    # -- swapping ----------------------------------------------------------
+    def set_swap_space(self, n: int):
+        """n host blocks, queued 0, 1, ..., n-1; only while nothing is swapped out."""
+        if self.swapped:
+            raise StateError("sequences are swapped out")
+        if n < 0:
+            raise ValueError("negative swap space")
+        self.num_cpu_blocks = int(n)
+        self.cpu_free = deque(range(self.num_cpu_blocks))
+
+    def swap_out(self, sid: int) -> list[tuple[int, int]]:
+        """Park sid's blocks in CPU blocks; returns (GPU block, CPU block)
+        copies in logical order."""
+        if sid in self.swapped:
+            raise StateError("already swapped out")
+        if sid not in self.tables:
+            raise ValueError("unknown sequence")
+        table = self.tables[sid]
+        if len(table) > len(self.cpu_free):
+            raise OutOfBlocks()
+        pairs = [(b, self.cpu_free.popleft()) for b in table]
+        for b in table:
             self.ref[b] -= 1
             if self.ref[b] == 0:
                 self.free.append(b)
-        del self.lens[sid]
-        del self.tokens[sid]
+        self.tables[sid] = [c for _, c in pairs]
+        self.swapped.add(sid)
+        return pairs
+
+    def swap_in(self, sid: int) -> list[tuple[int, int]]:
+        """Restore sid into fresh GPU blocks; returns (CPU block, GPU block)
+        copies in logical order.  Its full blocks are labelled again when
+        their text is known and not cached elsewhere."""
+        if sid not in self.swapped:
+            raise StateError("not swapped out")
+        table = self.tables[sid]
+        if len(table) > len(self.free):
+            raise OutOfBlocks()
+        pairs = [(c, self._pop()) for c in table]
+        self.cpu_free.extend(table)
+        self.tables[sid] = [g for _, g in pairs]
+        self.swapped.discard(sid)
+        self._label_new_full_blocks(sid, 0)
+        return pairs
+
+    def cpu_free_queue(self) -> list[int]:
+        return list(self.cpu_free)
 
     # -- views -----------------------------------------------------------
     def table(self, sid: int) -> list[int]:
@@ -223,6 +301,8 @@ class BlockManagerModel:
         out = np.full((len(sids), max_blocks), pad, dtype=np.int32)
         lens = np.zeros(len(sids), dtype=np.int32)
         for i, s in enumerate(sids):
+            if s in self.swapped:
+                raise StateError("swapped out")
             t = self.tables[s]
             if len(t) > max_blocks:
                 raise ValueError("table wider than max_blocks")

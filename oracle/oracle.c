@@ -33,6 +33,12 @@
  *  - orc_copy_blocks: copy-on-write copies a whole block ("Sharing and
  *    copy-on-write", vLLM Serving deep dive).
  *
+ *  - orc_swap_blocks: swapping parks a preempted sequence's blocks in a pool
+ *    of pinned host memory and restores them later ("The scheduler: waiting,
+ *    running, swapped", vLLM Serving deep dive; the CPU blocks of "Back to
+ *    the queue, and into vLLM proper", Life of a prompt): whole blocks are
+ *    copied from one pool pair to another.
+ *
  *  - e4m3_value / orc_quantize_e4m3: the 8-bit KV cache.  The pages say the
  *    cache may be kept in FP8 (one byte per element: the KV-size formula of
  *    "The hands-on guide to LLM Inference with vLLM"; "Quantization" in the
@@ -249,6 +255,24 @@ int orc_copy_blocks(int dtype, void* k_pool, void* v_pool, const int32_t* pairs,
             block_bytes);
     memmove((unsigned char*)v_pool + dst * block_bytes, (unsigned char*)v_pool + src * block_bytes,
             block_bytes);
+  }
+  return 0;
+}
+
+/* Copy whole blocks from one pool pair to another: block pairs[2*i] of
+ * (src_k, src_v) to block pairs[2*i+1] of (dst_k, dst_v).  Returns -2 when a
+ * block lies outside its pool. */
+int orc_swap_blocks(int dtype, const void* src_k, const void* src_v, int64_t src_num_blocks, void* dst_k,
+                    void* dst_v, int64_t dst_num_blocks, const int32_t* pairs, int64_t n, int32_t bs, int32_t H,
+                    int32_t d) {
+  int es = esize_of(dtype);
+  if (!es) return -1;
+  int64_t block_bytes = (int64_t)H * bs * d * es;
+  for (int64_t i = 0; i < n; ++i) {
+    int64_t src = pairs[2 * i], dst = pairs[2 * i + 1];
+    if (src < 0 || dst < 0 || src >= src_num_blocks || dst >= dst_num_blocks) return -2;
+    memcpy((unsigned char*)dst_k + dst * block_bytes, (const unsigned char*)src_k + src * block_bytes, block_bytes);
+    memcpy((unsigned char*)dst_v + dst * block_bytes, (const unsigned char*)src_v + src * block_bytes, block_bytes);
   }
   return 0;
 }

@@ -408,3 +408,89 @@ def test_out_of_blocks_changes_nothing():
     with pytest.raises(bm.OutOfBlocks):
         m.append(s, 40)
     assert (m.free_queue(), m.table(s), m.lens[s]) == before
+
+
+# --------------------------------------------------------------------------
+# swapping: CPU blocks, the block copy between pools, the model's rules
+# --------------------------------------------------------------------------
+def test_cpu_blocks_from_the_swap_space(sizing):
+    c = sizing["cpu_pool"]
+    nb = oracle.blocks_for_budget(c["swap_gib"] * GIB, c["n_layers"], c["n_kv_heads"], c["d_head"],
+                                  c["dtype_bytes"], c["block_size"])
+    assert nb == c["cpu_blocks"], c["cite"]
+
+
+def test_swap_blocks_is_a_whole_block_copy():
+    rng = np.random.default_rng(7)
+    H, d, nb_src, nb_dst = 2, 64, 6, 4
+    per = H * 16 * d
+    sk = rng.integers(0, 2**16, size=nb_src * per, dtype=np.uint16)
+    sv = rng.integers(0, 2**16, size=nb_src * per, dtype=np.uint16)
+    dk = np.zeros(nb_dst * per, np.uint16)
+    dv = np.zeros_like(dk)
+    pairs = [(5, 0), (2, 3), (0, 1)]
+    oracle.swap_blocks("bf16", sk, sv, nb_src, dk, dv, nb_dst, pairs, 16, H, d)
+    for s, t in pairs:
+        assert np.array_equal(dk.reshape(nb_dst, per)[t], sk.reshape(nb_src, per)[s])
+        assert np.array_equal(dv.reshape(nb_dst, per)[t], sv.reshape(nb_src, per)[s])
+    assert not dk.reshape(nb_dst, per)[2].any()  # untouched block
+    with pytest.raises(ValueError):
+        oracle.swap_blocks("bf16", sk, sv, nb_src, dk, dv, nb_dst, [(6, 0)], 16, H, d)
+
+
+def test_swap_out_and_in_restores_the_sequence():
+    # a preempted sequence parks its blocks in CPU blocks; its GPU blocks are
+    # reused by another sequence meanwhile; swapping in restores every value
+    rng = np.random.default_rng(8)
+    H, d, nb, ncpu = 2, 64, 8, 6
+    m = bm.BlockManagerModel(nb, 16, rng.permutation(nb))
+    m.set_swap_space(ncpu)
+    kp = np.zeros(nb * H * 16 * d, np.uint16)
+    vp = np.zeros_like(kp)
+    ck, cv = np.zeros(ncpu * H * 16 * d, np.uint16), np.zeros(ncpu * H * 16 * d, np.uint16)
+    a = m.create()
+    slots, _ = m.append(a, 70)
+    kb = rng.integers(0, 2**16, size=(70, H, d), dtype=np.uint16)
+    vb = rng.integers(0, 2**16, size=(70, H, d), dtype=np.uint16)
+    oracle.scatter("bf16", kb, vb, kp, vp, slots, nb, 16, H, d)
+    out_pairs = m.swap_out(a)
+    assert [g for g, _ in out_pairs] == m.free_queue()[-5:]  # released to the tail in logical order
+    oracle.swap_blocks("bf16", kp, vp, nb, ck, cv, ncpu, out_pairs, 16, H, d)
+    other = m.create()
+    s2, _ = m.append(other, 16 * 6)  # takes the freed blocks too
+    junk = np.full((96, H, d), 0x7FC0, np.uint16)
+    oracle.scatter("bf16", junk, junk, kp, vp, s2, nb, 16, H, d)
+    m.release(other)
+    in_pairs = m.swap_in(a)
+    oracle.swap_blocks("bf16", ck, cv, ncpu, kp, vp, nb, in_pairs, 16, H, d)
+    k, v = oracle.gather("bf16", kp, vp, nb, 16, H, d, m.table(a), 70)
+    assert np.array_equal(k, oracle.decode("bf16", kb), equal_nan=True)
+    assert np.array_equal(v, oracle.decode("bf16", vb), equal_nan=True)
+
+
+def test_swap_rules():
+    m = bm.BlockManagerModel(10, 16, list(range(10)))
+    m.set_swap_space(4)
+    root = m.create()
+    m.append(root, 40)                      # blocks 0, 1, 2
+    child = m.fork(root, 40)                # shares them
+    assert m.swap_out(root) == [(0, 0), (1, 1), (2, 2)]
+    assert [m.ref[b] for b in (0, 1, 2)] == [1, 1, 1] and m.table(child) == [0, 1, 2]
+    for op in (lambda: m.append(root, 1), lambda: m.fork(root, 1), lambda: m.swap_out(root),
+               lambda: m.blocks_needed(root, 1), lambda: m.padded_tables([root], 4),
+               lambda: m.set_swap_space(8)):
+        with pytest.raises(bm.StateError):
+            op()
+    big = m.create()
+    m.append(big, 33)                       # three blocks; one CPU block is left
+    with pytest.raises(bm.OutOfBlocks):
+        m.swap_out(big)
+    assert m.cpu_free_queue() == [3] and m.table(big) == [3, 4, 5]
+    m.append(big, 16 * 4)                   # the GPU pool is now exhausted
+    with pytest.raises(bm.OutOfBlocks):
+        m.swap_in(root)
+    assert root in m.swapped and m.cpu_free_queue() == [3]
+    m.release(root)                         # a swapped-out sequence frees its CPU blocks
+    assert m.cpu_free_queue() == [3, 0, 1, 2]
+    with pytest.raises(bm.StateError):
+        m.swap_in(child)
