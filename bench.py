@@ -17,7 +17,8 @@ two kernels queued back to back on the caller's stream: decode_shared_kernel
 them) and decode_partition_kernel (every other partition); it is timed with
 HIP events around the whole pass.  The JSON also carries the same step over
 an 8-bit (E4M3) cache (fp8_kv_decode: rows quantised on the way in, half the
-bytes per step) and the mixed chunked-prefill + decode step.
+bytes per step), the swap copies of 32 sequences between HBM and pinned host
+blocks (swap), and the mixed chunked-prefill + decode step.
 
   python bench.py [--steps K] [--warmup W] [--workload 2|3|4] [--no-cpu-baseline] [--no-fp8] [--no-mixed]
   python bench.py --copy-calibration     # plain device copy of a known size
@@ -239,6 +240,61 @@ def prefix_cache_host(n_req=256, group=8, prefix=1024, lens=(512, 4096), seed=0)
             "model_us_per_request": dtm / len(prompts) * 1e6}
 
 
+HOST_LINK_PEAK_GBS = 64.0  # PCIe 5.0 x16, one direction
+
+
+def swap_leg(b, n_seqs=32, reps=10):
+    """Swap copies (paged_kv_swap_blocks) of the first n_seqs sequences'
+    blocks between the HBM pools and pinned host pools, one launch each way,
+    timed with HIP events; beside them a plain copy of the same number of
+    bytes between a contiguous device buffer and pinned host memory (torch's
+    copy_, the runtime's DMA path) as the host link's practical ceiling.
+    Swapping in writes the same bytes back into the same blocks, so the batch
+    is unchanged."""
+    import numpy as np
+    import torch
+    import paged_kv_cache_gather_amd as pkv
+    w, d = b.w, b.decode
+    rows = d.tables_host[:n_seqs]
+    blocks = np.unique(rows[rows >= 0]).astype(np.int32)
+    n = int(blocks.size)
+    per = w.n_kv_heads * 16 * w.head_dim
+    cpu_k = torch.empty(n * per, dtype=b.k_pool.dtype, pin_memory=True)
+    cpu_v = torch.empty(n * per, dtype=b.k_pool.dtype, pin_memory=True)
+    idx = np.arange(n, dtype=np.int32)
+    p_out = torch.from_numpy(np.stack([blocks, idx], 1)).to("cuda:0")
+    p_in = torch.from_numpy(np.stack([idx, blocks], 1)).to("cuda:0")
+    nbytes = 2 * n * per * b.k_pool.element_size()
+    st = torch.cuda.current_stream()
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(st)
+        for _ in range(reps):
+            fn()
+        e1.record(st)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps * 1e-3
+
+    t_out = timed(lambda: pkv.paged_kv_swap_blocks(b.k_pool, b.v_pool, cpu_k, cpu_v, p_out, w.num_blocks, n,
+                                                   w.n_kv_heads, w.head_dim))
+    t_in = timed(lambda: pkv.paged_kv_swap_blocks(cpu_k, cpu_v, b.k_pool, b.v_pool, p_in, n, w.num_blocks,
+                                                  w.n_kv_heads, w.head_dim))
+    dev_buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda:0")
+    host_buf = torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
+    t_d2h = timed(lambda: host_buf.copy_(dev_buf, non_blocking=True))
+    t_h2d = timed(lambda: dev_buf.copy_(host_buf, non_blocking=True))
+    gb = lambda t: nbytes / t / 1e9
+    log(f"swap {n} blocks ({nbytes / 1e6:.0f} MB): out {t_out * 1e3:.2f} ms = {gb(t_out):.1f} GB/s, in "
+        f"{t_in * 1e3:.2f} ms = {gb(t_in):.1f} GB/s | contiguous copy d2h {gb(t_d2h):.1f}, h2d {gb(t_h2d):.1f} GB/s")
+    return {"kernel": "swap_blocks_kernel", "sequences": n_seqs, "blocks": n, "bytes": nbytes,
+            "out_ms": t_out * 1e3, "in_ms": t_in * 1e3, "out_gbs": gb(t_out), "in_gbs": gb(t_in),
+            "copy_d2h_gbs": gb(t_d2h), "copy_h2d_gbs": gb(t_h2d), "link_peak_gbs": HOST_LINK_PEAK_GBS,
+            "out_frac_of_copy": t_d2h / t_out, "in_frac_of_copy": t_h2d / t_in}
+
+
 def cpu_baseline(w, n_seqs):
     """The fp64 oracle (as it stands) on every k-th sequence of the batch."""
     import numpy as np
@@ -359,6 +415,7 @@ def main():
     ap.add_argument("--no-mixed", action="store_true", help="skip the mixed prefill+decode step")
     ap.add_argument("--only-mixed", action="store_true", help="run only the mixed prefill+decode step")
     ap.add_argument("--no-fp8", action="store_true", help="skip the 8-bit-cache decode leg")
+    ap.add_argument("--no-swap", action="store_true", help="skip the swap-copy leg")
     ap.add_argument("--only-fp8", action="store_true", help="run only the 8-bit-cache decode leg")
     args = ap.parse_args()
 
@@ -438,6 +495,8 @@ def main():
         "logical_gbs": logical,
         "prefix_cache_host": prefix_cache_host(),
     }
+    if not args.no_swap:
+        res["swap"] = swap_leg(b)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, args.cpu_sample)
     del b, out

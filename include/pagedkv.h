@@ -225,6 +225,58 @@ int paged_kv_block_refcount(pkv_pool* pool, int64_t block, int32_t* ref);
 int paged_kv_free_queue(pkv_pool* pool, int32_t* out, int64_t cap, int64_t* n);
 
 /* ------------------------------------------------------------------------
+ * Swap space: host ("CPU") blocks for preempted sequences
+ * ("The scheduler: waiting, running, swapped", vLLM Serving deep dive: a
+ * preempted sequence's blocks are copied to CPU swap space and restored
+ * later; "Back to the queue, and into vLLM proper", Life of a prompt: the CPU
+ * blocks are a pool of pinned host memory sized like the GPU pool,
+ * paged_kv_blocks_for_budget of the swap space).  The host pools themselves
+ * (one K and one V pool per layer, same layout and block size as the GPU
+ * pools) are caller-allocated pinned memory; the block manager only hands out
+ * their block ids, FIFO, and reports the copies to run with
+ * paged_kv_swap_blocks.
+ * ------------------------------------------------------------------------ */
+
+/* Give the pool num_cpu_blocks host blocks, queued 0, 1, ..., n-1 (0 removes
+ * the swap space).  PKV_ESTATE while any sequence is swapped out. */
+int paged_kv_swap_space(pkv_pool* pool, int64_t num_cpu_blocks);
+
+/* Swap a sequence out: each of its blocks, in logical order, gets a host
+ * block from the head of the host queue (a private copy, also of blocks it
+ * shares with other sequences), then its GPU blocks are released as by
+ * paged_kv_seq_free (reference counts drop; blocks reaching zero join the
+ * free queue's tail, where they keep their bytes and any prefix-cache label
+ * until the queue hands them out).  pairs_out (host int32 [cap][2]) receives
+ * the copies (GPU block, host block), *n_pairs their number (= the table
+ * length).  Queue the copy (paged_kv_swap_blocks, GPU pools -> host pools)
+ * before any later write into blocks allocated after this call, on the same
+ * stream.  All or nothing: PKV_ENOMEM_BLOCKS if the host queue is too short,
+ * PKV_EINVAL if cap is smaller than the table, PKV_ESTATE if the sequence is
+ * unknown or already swapped out.  While swapped out a sequence can only be
+ * swapped in, freed (its host blocks rejoin their queue) or read with
+ * paged_kv_seq_table / paged_kv_seq_len (the table then names host blocks);
+ * appends, forks, paged_kv_seq_blocks_needed and paged_kv_block_tables return
+ * PKV_ESTATE. */
+int paged_kv_seq_swap_out(pkv_pool* pool, int64_t seq, int32_t* pairs_out, int64_t cap, int64_t* n_pairs);
+
+/* Swap a sequence back in: each host block, in logical order, gets a GPU
+ * block from the head of the free queue, then the host blocks rejoin their
+ * queue's tail.  pairs_out receives (host block, GPU block); queue the copy
+ * (host pools -> GPU pools) before anything reads the sequence.  Its full
+ * blocks are labelled again for prefix caching when their tokens are known and
+ * the same text is not cached already.  All or nothing: PKV_ENOMEM_BLOCKS if
+ * the free queue is too short, PKV_EINVAL if cap is too small, PKV_ESTATE if
+ * the sequence is not swapped out. */
+int paged_kv_seq_swap_in(pkv_pool* pool, int64_t seq, int32_t* pairs_out, int64_t cap, int64_t* n_pairs);
+
+/* *swapped = 1 if the sequence is swapped out, else 0. */
+int paged_kv_seq_is_swapped(pkv_pool* pool, int64_t seq, int32_t* swapped);
+
+/* Copy the host block queue, head first, into out[cap]; *n receives its
+ * length (out may be NULL to query it). */
+int paged_kv_cpu_free_queue(pkv_pool* pool, int32_t* out, int64_t cap, int64_t* n);
+
+/* ------------------------------------------------------------------------
  * Device operations (HIP, gfx950)
  * ------------------------------------------------------------------------ */
 
@@ -272,6 +324,22 @@ int reshape_and_cache_fp8(const void* key, const void* value, int32_t src_dtype,
  * Pairs with an id outside [0, num_blocks) are skipped. */
 int paged_kv_copy_blocks(void* k_pool, void* v_pool, const int32_t* pairs_dev, int32_t n_pairs,
                          int64_t num_blocks, int32_t n_kv_heads, int32_t head_dim,
+                         int32_t block_size, int32_t dtype, void* stream);
+
+/* Copy whole blocks from one pool pair to another: for each pair i, block
+ * pairs[2i] of (src_k_pool, src_v_pool) to block pairs[2i+1] of (dst_k_pool,
+ * dst_v_pool) — the swap-out / swap-in copies of paged_kv_seq_swap_out /
+ * _swap_in ("The scheduler: waiting, running, swapped", vLLM Serving deep
+ * dive).  Pools and pairs may be device memory or pinned host memory
+ * (hipHostMalloc, e.g. PyTorch's pin_memory): the kernel reads and writes
+ * host blocks over the host link itself, all pairs in one launch.  Block
+ * bytes = n_kv_heads * block_size * head_dim * esize(dtype) per pool.  Pairs
+ * with an id outside [0, src_num_blocks) / [0, dst_num_blocks) are skipped;
+ * pairs must name distinct destination blocks.  PKV_EINVAL for memory the GPU
+ * cannot reach (pageable host memory). */
+int paged_kv_swap_blocks(const void* src_k_pool, const void* src_v_pool, int64_t src_num_blocks,
+                         void* dst_k_pool, void* dst_v_pool, int64_t dst_num_blocks,
+                         const int32_t* pairs, int32_t n_pairs, int32_t n_kv_heads, int32_t head_dim,
                          int32_t block_size, int32_t dtype, void* stream);
 
 /* Context tokens one decode partition covers (the split-context unit). */

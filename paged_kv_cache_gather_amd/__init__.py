@@ -86,6 +86,12 @@ _sig("paged_kv_prefix_cache_enable", ctypes.c_int, _P, _i32)
 _sig("paged_kv_seq_create_cached", ctypes.c_int, _P, _P, _i64, _pi64, _pi64)
 _sig("paged_kv_seq_append_tokens", ctypes.c_int, _P, _i64, _P, _i64, _P, _P, _i32, _pi32)
 _sig("paged_kv_prefix_cache_stats", ctypes.c_int, _P, _pi64, _pi64, _pi64)
+_sig("paged_kv_swap_space", ctypes.c_int, _P, _i64)
+_sig("paged_kv_seq_swap_out", ctypes.c_int, _P, _i64, _P, _i64, _pi64)
+_sig("paged_kv_seq_swap_in", ctypes.c_int, _P, _i64, _P, _i64, _pi64)
+_sig("paged_kv_seq_is_swapped", ctypes.c_int, _P, _i64, _pi32)
+_sig("paged_kv_cpu_free_queue", ctypes.c_int, _P, _P, _i64, _pi64)
+_sig("paged_kv_swap_blocks", ctypes.c_int, _P, _P, _i64, _P, _P, _i64, _P, _i32, _i32, _i32, _i32, _i32, _P)
 _sig("reshape_and_cache", ctypes.c_int, _P, _P, _i64, _i64, _P, _P, _P, _i64, _i64, _i32, _i32,
      _i32, _i32, _P)
 _sig("reshape_and_cache_fp8", ctypes.c_int, _P, _P, _i32, _i64, _i64, _P, _P, _P, _i64, _i64, _i32, _i32, _i32,
@@ -332,6 +338,42 @@ def paged_kv_free_queue(pool: Pool) -> np.ndarray:
     return out
 
 
+def paged_kv_swap_space(pool: Pool, num_cpu_blocks: int):
+    _check(_lib.paged_kv_swap_space(pool.handle, num_cpu_blocks))
+
+
+def _swap(fn, pool: Pool, seq: int) -> np.ndarray:
+    n = _i64()
+    _check(_lib.paged_kv_seq_table(pool.handle, seq, None, 0, ctypes.byref(n)))
+    pairs = np.empty((max(n.value, 1), 2), dtype=np.int32)
+    _check(fn(pool.handle, seq, pairs.ctypes.data, pairs.shape[0], ctypes.byref(n)))
+    return pairs[:n.value]
+
+
+def paged_kv_seq_swap_out(pool: Pool, seq: int) -> np.ndarray:
+    """Returns the copies to run, int32 [n, 2] of (GPU block, host block)."""
+    return _swap(_lib.paged_kv_seq_swap_out, pool, seq)
+
+
+def paged_kv_seq_swap_in(pool: Pool, seq: int) -> np.ndarray:
+    """Returns the copies to run, int32 [n, 2] of (host block, GPU block)."""
+    return _swap(_lib.paged_kv_seq_swap_in, pool, seq)
+
+
+def paged_kv_seq_is_swapped(pool: Pool, seq: int) -> bool:
+    r = _i32()
+    _check(_lib.paged_kv_seq_is_swapped(pool.handle, seq, ctypes.byref(r)))
+    return bool(r.value)
+
+
+def paged_kv_cpu_free_queue(pool: Pool) -> np.ndarray:
+    n = _i64()
+    _check(_lib.paged_kv_cpu_free_queue(pool.handle, None, 0, ctypes.byref(n)))
+    out = np.empty(n.value, dtype=np.int32)
+    _check(_lib.paged_kv_cpu_free_queue(pool.handle, out.ctypes.data, out.size, ctypes.byref(n)))
+    return out
+
+
 # --------------------------------------------------------------------------
 # device operations
 # --------------------------------------------------------------------------
@@ -404,6 +446,35 @@ def paged_kv_copy_blocks(k_pool: torch.Tensor, v_pool: torch.Tensor, pairs: torc
         raise PagedKVError(PKV_EINVAL, "pool tensors smaller than num_blocks blocks")
     _check(_lib.paged_kv_copy_blocks(_ptr(k_pool), _ptr(v_pool), _ptr(pairs), n, num_blocks, n_kv_heads,
                                      head_dim, block_size, dtype_code(k_pool.dtype), _stream(stream, k_pool.device)))
+
+
+def _reachable(t: torch.Tensor, name: str):
+    if not isinstance(t, torch.Tensor) or not (t.is_cuda or t.is_pinned()):
+        raise PagedKVError(PKV_EINVAL, f"{name} must be a device tensor or pinned host memory")
+    if not t.is_contiguous():
+        raise PagedKVError(PKV_EINVAL, f"{name} must be contiguous")
+    return t
+
+
+def paged_kv_swap_blocks(src_k: torch.Tensor, src_v: torch.Tensor, dst_k: torch.Tensor, dst_v: torch.Tensor,
+                         pairs: torch.Tensor, src_num_blocks: int, dst_num_blocks: int, n_kv_heads: int,
+                         head_dim: int, block_size: int = BLOCK_SIZE, stream=None):
+    """Whole-block copies between pool pairs (device or pinned host tensors);
+    pairs int32 [n, 2] (src, dst), device or pinned host."""
+    for t, name in ((src_k, "src_k"), (src_v, "src_v"), (dst_k, "dst_k"), (dst_v, "dst_v"), (pairs, "pairs")):
+        _reachable(t, name)
+    if pairs.dtype != torch.int32:
+        raise PagedKVError(PKV_EINVAL, "pairs must be int32")
+    dt = {src_k.dtype, src_v.dtype, dst_k.dtype, dst_v.dtype}
+    if len(dt) != 1:
+        raise PagedKVError(PKV_EINVAL, "pools must share a dtype")
+    per = n_kv_heads * block_size * head_dim
+    if min(src_k.numel(), src_v.numel()) < src_num_blocks * per or min(dst_k.numel(), dst_v.numel()) < dst_num_blocks * per:
+        raise PagedKVError(PKV_EINVAL, "pool tensors smaller than their block counts")
+    dev = src_k.device if src_k.is_cuda else (dst_k.device if dst_k.is_cuda else None)
+    _check(_lib.paged_kv_swap_blocks(_ptr(src_k), _ptr(src_v), src_num_blocks, _ptr(dst_k), _ptr(dst_v),
+                                     dst_num_blocks, _ptr(pairs), pairs.numel() // 2, n_kv_heads, head_dim,
+                                     block_size, dtype_code(src_k.dtype), _stream(stream, dev)))
 
 
 def paged_attention_decode_partition_size() -> int:

@@ -21,7 +21,16 @@
 //    own tokens chained with the fingerprint of the block before it; a new
 //    prompt reuses every leading full block whose label is known; only full
 //    blocks are labelled; unused labelled blocks are thrown out least
-//    recently used first.
+//    recently used first;
+//  - swapping ("The scheduler: waiting, running, swapped", vLLM Serving deep
+//    dive; the CPU blocks of "Back to the queue, and into vLLM proper", Life
+//    of a prompt): a preempted sequence's blocks are parked in a pool of
+//    pinned host blocks and restored later.  The host blocks have their own
+//    FIFO queue; swapping out gives each block of the sequence, in logical
+//    order, a host block (a private copy, also of shared blocks) and releases
+//    the GPU blocks as a finished sequence would; swapping in takes GPU
+//    blocks from the head of the free queue and returns the host blocks to
+//    their queue's tail.  Both are all or nothing.
 //
 // The free queue is a doubly linked list over block ids (a block is either
 // queued or referenced, never both), so a cache hit can take a free block out
@@ -31,6 +40,7 @@
 // first).  Every operation is O(blocks touched).
 #include <algorithm>
 #include <cstdint>
+#include <deque>
 #include <string>
 #include <mutex>
 #include <new>
@@ -52,6 +62,8 @@ struct Sequence {
   bool tracked = true;
   std::vector<int32_t> tokens;
   std::vector<uint64_t> fp;
+  // swapped out: `table` holds host (CPU) block ids
+  bool swapped = false;
 };
 
 // Fingerprint of a full block: a 64-bit chained mix of the previous block's
@@ -106,6 +118,10 @@ struct pkv_pool {
   std::vector<uint64_t> blabel, bprev;
   std::vector<int32_t> btok;
   int64_t queried = 0, hits = 0;
+  // swap space: host blocks, FIFO
+  int64_t num_cpu_blocks = 0;
+  std::deque<int32_t> cpu_free;
+  int64_t n_swapped = 0;
   std::mutex mu;
 
   void unlink(int32_t b) {
@@ -272,6 +288,7 @@ int paged_kv_seq_fork(pkv_pool* pool, int64_t parent, int64_t n_prefix_tokens, i
   std::lock_guard<std::mutex> lk(pool->mu);
   auto it = pool->seqs.find(parent);
   if (it == pool->seqs.end()) return fail(PKV_ESTATE, "paged_kv_seq_fork: unknown parent");
+  if (it->second.swapped) return fail(PKV_ESTATE, "paged_kv_seq_fork: parent is swapped out");
   if (n_prefix_tokens < 0 || n_prefix_tokens > it->second.len)
     return fail(PKV_EINVAL, "paged_kv_seq_fork: prefix longer than the parent");
   const int64_t nb = (n_prefix_tokens + pool->block_size - 1) / pool->block_size;
@@ -296,6 +313,7 @@ int paged_kv_seq_blocks_needed(pkv_pool* pool, int64_t seq, int64_t n_tokens, in
   std::lock_guard<std::mutex> lk(pool->mu);
   auto it = pool->seqs.find(seq);
   if (it == pool->seqs.end()) return fail(PKV_ESTATE, "unknown sequence");
+  if (it->second.swapped) return fail(PKV_ESTATE, "paged_kv_seq_blocks_needed: sequence is swapped out");
   *n_blocks = pool->need(it->second, n_tokens);
   return ok();
 }
@@ -311,6 +329,7 @@ static int append_impl(const char* fn, pkv_pool* pool, int64_t seq, const int32_
   auto it = pool->seqs.find(seq);
   if (it == pool->seqs.end()) return fail(PKV_ESTATE, F + ": unknown sequence");
   Sequence& s = it->second;
+  if (s.swapped) return fail(PKV_ESTATE, F + ": sequence is swapped out");
   const int64_t bs = pool->block_size;
   const int64_t L = s.len;
   const bool cow = n_tokens > 0 && L % bs != 0 && pool->ref[s.table[L / bs]] > 1;
@@ -436,10 +455,104 @@ int paged_kv_seq_free(pkv_pool* pool, int64_t seq) {
   std::lock_guard<std::mutex> lk(pool->mu);
   auto it = pool->seqs.find(seq);
   if (it == pool->seqs.end()) return fail(PKV_ESTATE, "paged_kv_seq_free: unknown sequence");
-  for (int32_t b : it->second.table) {
-    if (--pool->ref[b] == 0) pool->push(b);
+  if (it->second.swapped) {  // its host blocks rejoin their queue
+    for (int32_t c : it->second.table) pool->cpu_free.push_back(c);
+    --pool->n_swapped;
+  } else {
+    for (int32_t b : it->second.table) {
+      if (--pool->ref[b] == 0) pool->push(b);
+    }
   }
   pool->seqs.erase(it);
+  return ok();
+}
+
+int paged_kv_swap_space(pkv_pool* pool, int64_t num_cpu_blocks) {
+  if (!pool) return fail(PKV_EINVAL, "pool is NULL");
+  if (num_cpu_blocks < 0 || num_cpu_blocks > INT32_MAX)
+    return fail(PKV_EINVAL, "paged_kv_swap_space: num_cpu_blocks must be in [0, 2^31)");
+  std::lock_guard<std::mutex> lk(pool->mu);
+  if (pool->n_swapped) return fail(PKV_ESTATE, "paged_kv_swap_space: sequences are swapped out");
+  pool->num_cpu_blocks = num_cpu_blocks;
+  pool->cpu_free.clear();
+  for (int64_t c = 0; c < num_cpu_blocks; ++c) pool->cpu_free.push_back((int32_t)c);
+  return ok();
+}
+
+int paged_kv_seq_swap_out(pkv_pool* pool, int64_t seq, int32_t* pairs_out, int64_t cap, int64_t* n_pairs) {
+  if (!pool || !n_pairs) return fail(PKV_EINVAL, "paged_kv_seq_swap_out: NULL argument");
+  std::lock_guard<std::mutex> lk(pool->mu);
+  auto it = pool->seqs.find(seq);
+  if (it == pool->seqs.end()) return fail(PKV_ESTATE, "paged_kv_seq_swap_out: unknown sequence");
+  Sequence& s = it->second;
+  if (s.swapped) return fail(PKV_ESTATE, "paged_kv_seq_swap_out: already swapped out");
+  const int64_t n = (int64_t)s.table.size();
+  if (n > 0 && (!pairs_out || cap < n))
+    return fail(PKV_EINVAL, "paged_kv_seq_swap_out: pairs_out holds fewer than " + std::to_string(n) + " pairs");
+  if (n > (int64_t)pool->cpu_free.size())
+    return fail(PKV_ENOMEM_BLOCKS, "out of CPU blocks: need " + std::to_string(n) + ", free " +
+                                       std::to_string(pool->cpu_free.size()));
+  for (int64_t i = 0; i < n; ++i) {
+    const int32_t c = pool->cpu_free.front();
+    pool->cpu_free.pop_front();
+    pairs_out[2 * i] = s.table[i];
+    pairs_out[2 * i + 1] = c;
+  }
+  for (int64_t i = 0; i < n; ++i) {  // release the GPU blocks, in logical order
+    const int32_t b = s.table[i];
+    if (--pool->ref[b] == 0) pool->push(b);
+    s.table[i] = pairs_out[2 * i + 1];
+  }
+  s.swapped = true;
+  ++pool->n_swapped;
+  *n_pairs = n;
+  return ok();
+}
+
+int paged_kv_seq_swap_in(pkv_pool* pool, int64_t seq, int32_t* pairs_out, int64_t cap, int64_t* n_pairs) {
+  if (!pool || !n_pairs) return fail(PKV_EINVAL, "paged_kv_seq_swap_in: NULL argument");
+  std::lock_guard<std::mutex> lk(pool->mu);
+  auto it = pool->seqs.find(seq);
+  if (it == pool->seqs.end()) return fail(PKV_ESTATE, "paged_kv_seq_swap_in: unknown sequence");
+  Sequence& s = it->second;
+  if (!s.swapped) return fail(PKV_ESTATE, "paged_kv_seq_swap_in: not swapped out");
+  const int64_t n = (int64_t)s.table.size();
+  if (n > 0 && (!pairs_out || cap < n))
+    return fail(PKV_EINVAL, "paged_kv_seq_swap_in: pairs_out holds fewer than " + std::to_string(n) + " pairs");
+  if (n > pool->count)
+    return fail(PKV_ENOMEM_BLOCKS, "out of KV blocks: need " + std::to_string(n) + ", free " +
+                                       std::to_string(pool->count));
+  for (int64_t i = 0; i < n; ++i) {
+    const int32_t c = s.table[i];
+    const int32_t g = pool->pop();
+    pairs_out[2 * i] = c;
+    pairs_out[2 * i + 1] = g;
+    s.table[i] = g;
+    pool->cpu_free.push_back(c);
+  }
+  s.swapped = false;
+  --pool->n_swapped;
+  if (s.tracked) pool->label_full_blocks(s, 0);
+  *n_pairs = n;
+  return ok();
+}
+
+int paged_kv_seq_is_swapped(pkv_pool* pool, int64_t seq, int32_t* swapped) {
+  if (!pool || !swapped) return fail(PKV_EINVAL, "NULL argument");
+  std::lock_guard<std::mutex> lk(pool->mu);
+  auto it = pool->seqs.find(seq);
+  if (it == pool->seqs.end()) return fail(PKV_ESTATE, "unknown sequence");
+  *swapped = it->second.swapped ? 1 : 0;
+  return ok();
+}
+
+int paged_kv_cpu_free_queue(pkv_pool* pool, int32_t* out, int64_t cap, int64_t* n) {
+  if (!pool || !n) return fail(PKV_EINVAL, "NULL argument");
+  std::lock_guard<std::mutex> lk(pool->mu);
+  *n = (int64_t)pool->cpu_free.size();
+  if (!out) return ok();
+  if (cap < *n) return fail(PKV_EINVAL, "paged_kv_cpu_free_queue: cap too small");
+  std::copy(pool->cpu_free.begin(), pool->cpu_free.end(), out);
   return ok();
 }
 
@@ -473,6 +586,7 @@ int paged_kv_block_tables(pkv_pool* pool, const int64_t* seqs, int32_t n, int32_
   for (int32_t i = 0; i < n; ++i) {
     auto it = pool->seqs.find(seqs[i]);
     if (it == pool->seqs.end()) return fail(PKV_ESTATE, "paged_kv_block_tables: unknown sequence");
+    if (it->second.swapped) return fail(PKV_ESTATE, "paged_kv_block_tables: a sequence is swapped out");
     if ((int64_t)it->second.table.size() > max_blocks)
       return fail(PKV_EINVAL, "paged_kv_block_tables: table longer than max_blocks");
     if (it->second.len > INT32_MAX) return fail(PKV_EINVAL, "sequence too long for int32 lens");

@@ -1,5 +1,7 @@
-// Cache writes: reshape_and_cache (append new tokens' K/V into their slots)
-// and paged_kv_copy_blocks (whole-block copies for copy-on-write).
+// Cache writes: reshape_and_cache (append new tokens' K/V into their slots),
+// paged_kv_copy_blocks (whole-block copies for copy-on-write) and
+// paged_kv_swap_blocks (whole-block copies between the HBM pools and pools of
+// pinned host blocks, for swapping).
 //
 // reshape_and_cache and paged_kv_copy_blocks are byte copies;
 // reshape_and_cache_fp8 quantises 32- or 16-bit rows into an 8-bit pool on the
@@ -141,6 +143,48 @@ copy_blocks_kernel(unsigned char* __restrict__ kpool, unsigned char* __restrict_
   }
 }
 
+// Whole blocks from one pool pair to another, either side in HBM or in pinned
+// host memory (read and written by the kernel over the host link).  Grid
+// (pair, K or V): 256 threads stream the block, four 16-byte loads in flight
+// per thread before their stores.
+__global__ void __launch_bounds__(256)
+swap_blocks_kernel(const unsigned char* __restrict__ src_k, const unsigned char* __restrict__ src_v,
+                   unsigned char* __restrict__ dst_k, unsigned char* __restrict__ dst_v,
+                   const int32_t* __restrict__ pairs, int64_t src_num_blocks, int64_t dst_num_blocks,
+                   int64_t block_bytes) {
+  const int64_t src = pairs[2 * (int64_t)blockIdx.x];
+  const int64_t dst = pairs[2 * (int64_t)blockIdx.x + 1];
+  if (src < 0 || dst < 0 || src >= src_num_blocks || dst >= dst_num_blocks) return;
+  const unsigned char* s = (blockIdx.y ? src_v : src_k) + src * block_bytes;
+  unsigned char* d = (blockIdx.y ? dst_v : dst_k) + dst * block_bytes;
+  const int64_t n16 = block_bytes / 16;
+  for (int64_t j = threadIdx.x; j < n16; j += 4 * 256) {
+    u32x4 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (j + u * 256 < n16) v[u] = ld16(s + (j + u * 256) * 16);
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (j + u * 256 < n16) st16(d + (j + u * 256) * 16, v[u]);
+  }
+}
+
+// The address a kernel uses for p: device memory as is, pinned host memory
+// through its device mapping; nullptr for memory a kernel cannot reach.
+const void* device_view(const void* p) {
+  hipPointerAttribute_t a;
+  if (hipPointerGetAttributes(&a, p) != hipSuccess) {
+    (void)hipGetLastError();  // do not leave the error for the next call
+    return nullptr;
+  }
+  if (a.type == hipMemoryTypeDevice) return p;
+  if (a.type == hipMemoryTypeHost && a.devicePointer) {
+    const char* base_h = static_cast<const char*>(a.hostPointer ? a.hostPointer : p);
+    return static_cast<const char*>(a.devicePointer) + (static_cast<const char*>(p) - base_h);
+  }
+  return nullptr;
+}
+
 }  // namespace
 }  // namespace pkv
 
@@ -263,5 +307,36 @@ extern "C" int paged_kv_copy_blocks(void* k_pool, void* v_pool, const int32_t* p
                      num_blocks, block_bytes);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(PKV_EHIP, std::string("paged_kv_copy_blocks: ") + hipGetErrorString(e));
+  return ok();
+}
+
+extern "C" int paged_kv_swap_blocks(const void* src_k_pool, const void* src_v_pool, int64_t src_num_blocks,
+                                    void* dst_k_pool, void* dst_v_pool, int64_t dst_num_blocks,
+                                    const int32_t* pairs, int32_t n_pairs, int32_t n_kv_heads, int32_t head_dim,
+                                    int32_t block_size, int32_t dtype, void* stream) {
+  const int es = pkv::esize_of(dtype);
+  if (!es) return fail(PKV_EINVAL, "paged_kv_swap_blocks: unknown dtype");
+  if (block_size != pkv::kBlockSize) return fail(PKV_EUNSUPPORTED, "block_size must be 16");
+  if (n_pairs < 0 || src_num_blocks < 1 || dst_num_blocks < 1 || n_kv_heads < 1 || head_dim < 1)
+    return fail(PKV_EINVAL, "paged_kv_swap_blocks: bad sizes");
+  if (n_pairs == 0) return ok();
+  if (!src_k_pool || !src_v_pool || !dst_k_pool || !dst_v_pool || !pairs)
+    return fail(PKV_EINVAL, "paged_kv_swap_blocks: NULL pointer");
+  if (!pkv::aligned16(src_k_pool) || !pkv::aligned16(src_v_pool) || !pkv::aligned16(dst_k_pool) ||
+      !pkv::aligned16(dst_v_pool))
+    return fail(PKV_EINVAL, "paged_kv_swap_blocks: pools must be 16-byte aligned");
+  const int64_t block_bytes = (int64_t)n_kv_heads * block_size * head_dim * es;
+  if (block_bytes % 16) return fail(PKV_EINVAL, "paged_kv_swap_blocks: block not a multiple of 16 B");
+  const void* v[5] = {src_k_pool, src_v_pool, dst_k_pool, dst_v_pool, pairs};
+  for (auto& p : v) {
+    p = pkv::device_view(p);
+    if (!p) return fail(PKV_EINVAL, "paged_kv_swap_blocks: pools and pairs must be device or pinned host memory");
+  }
+  hipLaunchKernelGGL(pkv::swap_blocks_kernel, dim3((unsigned)n_pairs, 2), dim3(256), 0, (hipStream_t)stream,
+                     (const unsigned char*)v[0], (const unsigned char*)v[1], (unsigned char*)const_cast<void*>(v[2]),
+                     (unsigned char*)const_cast<void*>(v[3]), (const int32_t*)v[4], src_num_blocks, dst_num_blocks,
+                     block_bytes);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(PKV_EHIP, std::string("paged_kv_swap_blocks: ") + hipGetErrorString(e));
   return ok();
 }
