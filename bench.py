@@ -18,7 +18,8 @@ them) and decode_partition_kernel (every other partition); it is timed with
 HIP events around the whole pass.  The JSON also carries the same step over
 an 8-bit (E4M3) cache (fp8_kv_decode: rows quantised on the way in, half the
 bytes per step), the swap copies of 32 sequences between HBM and pinned host
-blocks (swap), and the mixed chunked-prefill + decode step.
+blocks (swap), verify attention of 5 new tokens per sequence (verify), and
+the mixed chunked-prefill + decode step.
 
   python bench.py [--steps K] [--warmup W] [--workload 2|3|4] [--no-cpu-baseline] [--no-fp8] [--no-mixed]
   python bench.py --copy-calibration     # plain device copy of a known size
@@ -295,6 +296,80 @@ def swap_leg(b, n_seqs=32, reps=10):
             "out_frac_of_copy": t_d2h / t_out, "in_frac_of_copy": t_h2d / t_in}
 
 
+def verify_bytes(b):
+    """Algorithmic bytes of one verify launch: every sequence's keys and
+    values (its context plus the new tokens) once per KV head, the queries,
+    block-table entries, lengths and the outputs."""
+    import numpy as np
+    w, p = b.w, b.prefill
+    keys = (p.ctx + p.qlen).astype(np.int64)
+    eb = w.elem_bytes
+    total_q = int(p.qlen.sum())
+    kv = int(keys.sum()) * 2 * w.head_dim * eb * w.n_kv_heads
+    other = (2 * total_q * w.n_q_heads * w.head_dim * eb + int((-(-keys // 16)).sum()) * 4 + 8 * len(keys))
+    return {"unit_bytes": 2 * w.head_dim * eb * w.n_kv_heads, "kv_bytes": kv, "other_bytes": other,
+            "algorithmic_bytes": kv + other}
+
+
+def verify_leg(steps, warmup, seed, k=5):
+    """Checking k drafted tokens per sequence (k + 1 - 1 = k new query tokens
+    each) on the Llama-3-8B-shaped batch: 256 sequences with the decode
+    batch's context lengths; one step = append the new tokens + verify
+    attention (paged_attention_verify), timed with HIP events; beside it the
+    chunked-prefill kernel on the same batch."""
+    import numpy as np
+    import torch
+    import synth
+    from paged_kv_cache_gather_amd.batch import DeviceBatch
+    lens = synth.make_workload(3, seed).decode_lens
+    w = synth.custom_workload("llama3_8b_verify", 32, 8, 128, "bf16", 70000, seed, chunk_ctx=lens - 1,
+                              chunk_qlen=np.full(lens.size, k),
+                              description=f"Llama-3-8B-shaped verify step: 256 sequences, {k} new tokens each over "
+                                          "contexts L-1 with L~U[512,4096], Hq32/Hkv8, d=128, bf16")
+    b = DeviceBatch(w, "cuda:0", fill="device")
+    out = b.new_prefill_out()
+    st = torch.cuda.current_stream()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+
+    def step(e=None):
+        rec = (lambda i: e[i].record(st)) if e is not None else (lambda i: None)
+        rec(0)
+        b.append_prefill()
+        rec(1)
+        b.attend_verify(out)
+        rec(2)
+        b.attend_prefill(out)
+        rec(3)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    for i in range(steps):
+        step(ev[i])
+    torch.cuda.synchronize()
+    app = np.array([e[0].elapsed_time(e[1]) for e in ev]) * 1e3
+    ver = np.array([e[1].elapsed_time(e[2]) for e in ev]) * 1e3
+    pre = np.array([e[2].elapsed_time(e[3]) for e in ev]) * 1e3
+    by = verify_bytes(b)
+    ach = by["algorithmic_bytes"] / (ver.mean() * 1e-6) / 1e9
+    toks = int(w.chunk_qlen.sum())
+    log(f"verify ({k} tokens x {w.n_chunks} seqs): append {app.mean():.1f} us | verify {ver.mean():.1f} us = "
+        f"{ach:.0f} GB/s ({ach / HBM_PEAK_GBS:.1%}) | same batch through the prefill kernel {pre.mean():.1f} us")
+    res = {"workload": w.name, "description": w.description, "new_tokens_per_seq": k,
+           "step_us": float(app.mean() + ver.mean()), "tokens_per_s": toks / ((app.mean() + ver.mean()) * 1e-6),
+           "breakdown_us": {"append": float(app.mean()), "verify": float(ver.mean()),
+                            "prefill_kernel_same_batch": float(pre.mean())},
+           "roofline": {"bound": "hbm", "kernel": "verify_partition_kernel + decode_reduce_kernel",
+                        "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": ach / HBM_PEAK_GBS,
+                        "traffic": (profiled_traffic("verify_llama3_8b_verify", ["decode.hip", "pkv_device.h"])
+                                    if seed == 0 else None),
+                        "algorithmic_bytes": by["algorithmic_bytes"]},
+           "bytes": by}
+    del b
+    torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(w, n_seqs):
     """The fp64 oracle (as it stands) on every k-th sequence of the batch."""
     import numpy as np
@@ -416,6 +491,8 @@ def main():
     ap.add_argument("--only-mixed", action="store_true", help="run only the mixed prefill+decode step")
     ap.add_argument("--no-fp8", action="store_true", help="skip the 8-bit-cache decode leg")
     ap.add_argument("--no-swap", action="store_true", help="skip the swap-copy leg")
+    ap.add_argument("--no-verify", action="store_true", help="skip the verify-attention leg")
+    ap.add_argument("--only-verify", action="store_true", help="run only the verify-attention leg")
     ap.add_argument("--only-fp8", action="store_true", help="run only the 8-bit-cache decode leg")
     args = ap.parse_args()
 
@@ -437,6 +514,9 @@ def main():
 
     if args.only_mixed:
         print(json.dumps(mixed_step(args.steps, args.warmup, args.seed)), flush=True)
+        return
+    if args.only_verify:
+        print(json.dumps(verify_leg(args.steps, args.warmup, args.seed)), flush=True)
         return
 
     w = synth.make_workload(args.workload, seed=args.seed)
@@ -503,6 +583,8 @@ def main():
     torch.cuda.empty_cache()
     if not args.no_fp8:
         res["fp8_kv_decode"] = fp8_decode_leg(w, K, W, None if args.out_dtype == "kv" else "f32", args.seed)
+    if not args.no_verify:
+        res["verify"] = verify_leg(max(5, K // 2), max(2, W // 2), args.seed)
     if not args.no_mixed:
         res["mixed_step"] = mixed_step(max(5, K // 2), max(2, W // 2), args.seed)
     print(json.dumps(res), flush=True)

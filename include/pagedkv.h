@@ -479,6 +479,37 @@ int paged_attention_prefill_chunk(void* out, int32_t out_dtype, const void* q, c
                                   int32_t max_context_len, float scale, int32_t kv_dtype,
                                   void* stream);
 
+/* Device workspace bytes paged_attention_verify needs for these sizes (0 when
+ * every context fits in one partition). */
+int64_t paged_attention_verify_workspace_bytes(int32_t total_q, int32_t n_q_heads, int32_t head_dim,
+                                               int32_t max_context_len);
+
+/* Verify attention: a few new query tokens per sequence (the drafted tokens
+ * of speculative decoding plus one, checked by the large model in one pass:
+ * "Speculative decoding" in the vLLM Serving deep dive and in How AI
+ * actually answers you), each attending causally to the sequence's cached
+ * keys and the new keys before it.  The same arguments and result as
+ * paged_attention_prefill_chunk (sequence c's new tokens are rows
+ * cu_q_lens[c] .. cu_q_lens[c+1]-1 of q / out, query i at absolute position
+ * context_lens[c] - q_len + i, keys already appended), computed the way a
+ * decode step is: 512-token split-context partitions read once per KV head
+ * for all of the sequence's new tokens (MFMA, fp32 accumulation, fp16
+ * probabilities), partial states merged per token.
+ *   workspace  device, >= paged_attention_verify_workspace_bytes(total_q,
+ *              n_q_heads, head_dim, max_context_len) bytes (NULL when 0).
+ * Supported: kv_dtype PKV_F16 or PKV_BF16 (out PKV_F32 or kv_dtype),
+ * head_dim 64/128, n_q_heads / n_kv_heads in {1, 2, 4, 8, 16}, max_q_len <=
+ * 64 (PKV_EUNSUPPORTED above: use paged_attention_prefill_chunk), n_seqs and
+ * total_q <= 65535, scale finite. */
+int paged_attention_verify(void* out, int32_t out_dtype, const void* q, const void* k_pool,
+                           const void* v_pool, const int32_t* block_tables,
+                           int32_t max_blocks_per_seq, const int32_t* cu_q_lens,
+                           const int32_t* context_lens, int32_t n_seqs, int32_t total_q,
+                           int32_t max_q_len, int32_t n_q_heads, int32_t n_kv_heads,
+                           int32_t head_dim, int32_t block_size, int64_t num_blocks,
+                           int32_t max_context_len, float scale, int32_t kv_dtype, void* workspace,
+                           int64_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

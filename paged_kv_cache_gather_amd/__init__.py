@@ -108,6 +108,9 @@ for _n in ("paged_attention_decode_fp8", "paged_attention_decode_fp8_partitions"
            "paged_attention_decode_fp8_reduce"):
     _sig(_n, ctypes.c_int, _P, _i32, _P, _i32, _P, _P, _f32, _f32, _P, _i32, _P, _i32, _i32, _i32, _i32, _i32, _i64,
          _i32, _f32, _P, _i64, _P)
+_sig("paged_attention_verify_workspace_bytes", _i64, _i32, _i32, _i32, _i32)
+_sig("paged_attention_verify", ctypes.c_int, _P, _i32, _P, _P, _P, _P, _i32, _P, _P, _i32, _i32, _i32, _i32, _i32,
+     _i32, _i32, _i64, _i32, _f32, _i32, _P, _i64, _P)
 _sig("paged_attention_prefill_chunk", ctypes.c_int, _P, _i32, _P, _P, _P, _P, _i32, _P, _P, _i32,
      _i32, _i32, _i32, _i32, _i32, _i32, _i64, _i32, _f32, _i32, _P)
 
@@ -592,6 +595,43 @@ def paged_attention_decode_fp8_reduce(out, q, k_pool, v_pool, block_tables, cont
     _decode_fp8_call(_lib.paged_attention_decode_fp8_reduce, out, q, k_pool, v_pool, block_tables, context_lens,
                      max_context_len, n_kv_heads, num_blocks, scale, k_scale, v_scale, workspace, block_size,
                      stream)
+
+
+def paged_attention_verify_workspace_bytes(total_q: int, n_q_heads: int, head_dim: int, max_context_len: int) -> int:
+    return int(_lib.paged_attention_verify_workspace_bytes(total_q, n_q_heads, head_dim, max_context_len))
+
+
+def paged_attention_verify(out: torch.Tensor, q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
+                           block_tables: torch.Tensor, cu_q_lens: torch.Tensor, context_lens: torch.Tensor,
+                           max_q_len: int, max_context_len: int, n_kv_heads: int, num_blocks: int, scale: float,
+                           workspace=None, block_size: int = BLOCK_SIZE, stream=None):
+    """Same arguments as paged_attention_prefill_chunk plus a workspace
+    (paged_attention_verify_workspace_bytes); for a few query tokens per sequence."""
+    _dev(out, "out")
+    _dev(q, "q", k_pool.dtype)
+    _dev(k_pool, "k_pool")
+    _dev(v_pool, "v_pool", k_pool.dtype)
+    _dev(block_tables, "block_tables", torch.int32)
+    _dev(cu_q_lens, "cu_q_lens", torch.int32)
+    _dev(context_lens, "context_lens", torch.int32)
+    if q.dim() != 3 or out.shape != q.shape:
+        raise PagedKVError(PKV_EINVAL, "q and out must be [total_q, n_q_heads, head_dim]")
+    total_q, Hq, d = q.shape
+    n = context_lens.numel()
+    if block_tables.dim() != 2 or block_tables.shape[0] != n or cu_q_lens.numel() != n + 1:
+        raise PagedKVError(PKV_EINVAL, "block_tables/cu_q_lens must match context_lens")
+    need = num_blocks * n_kv_heads * block_size * d
+    if k_pool.numel() < need or v_pool.numel() < need:
+        raise PagedKVError(PKV_EINVAL, "pool tensors smaller than num_blocks blocks")
+    ws_bytes = 0
+    if workspace is not None:
+        _dev(workspace, "workspace")
+        ws_bytes = workspace.numel() * workspace.element_size()
+    _check(_lib.paged_attention_verify(
+        _ptr(out), dtype_code(out.dtype), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_tables),
+        block_tables.shape[1], _ptr(cu_q_lens), _ptr(context_lens), n, total_q, max_q_len, Hq, n_kv_heads, d,
+        block_size, num_blocks, max_context_len, float(scale), dtype_code(k_pool.dtype), _ptr(workspace), ws_bytes,
+        _stream(stream, q.device)))
 
 
 def paged_attention_prefill_chunk(out: torch.Tensor, q: torch.Tensor, k_pool: torch.Tensor,

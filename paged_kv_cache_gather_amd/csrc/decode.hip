@@ -62,6 +62,16 @@ namespace {
 #ifndef PKV_DECODE_MIN_WAVES
 #define PKV_DECODE_MIN_WAVES 2
 #endif
+// parts a wave's 128 tokens are processed in by the MFMA routine (1 or 2)
+#ifndef PKV_SHARED_PARTS
+#define PKV_SHARED_PARTS 2
+#endif
+#ifndef PKV_FP8_PARTS
+#define PKV_FP8_PARTS 2
+#endif
+#ifndef PKV_VERIFY_PARTS
+#define PKV_VERIFY_PARTS 2
+#endif
 constexpr int kPart = PKV_DECODE_PART;  // context tokens per partition
 constexpr int kThreads = 256;           // threads per workgroup
 constexpr int kWaves = kThreads / 64;
@@ -422,10 +432,40 @@ __device__ __forceinline__ u32x4 e4m3x8_to(uint32_t w0, uint32_t w1) {
 
 __device__ __forceinline__ uint64_t ld8(const void* p) { return *reinterpret_cast<const uint64_t*>(p); }
 
-// One partition on MFMA for the query rows of k sequences s .. s + k - 1
-// that name the same blocks for it (16 RT rows: row r = member r / G, head
-// r % G; rows past k G repeat member 0 and are not stored).  The first n
-// tokens of the partition are valid (Masked; otherwise all kPart).  K/V of
+// Which query rows an MFMA partition serves.  Row r of the 16 RT-row tile is
+// member r / G, query head r % G of the KV head; a member owns one query
+// token and a row of q / out in units of Hq rows (base).
+//  * SeqRows: members are sequences s .. s + k - 1 of a decode batch, one
+//    token each, sharing the partition's blocks (a shared run, or k = 1);
+//  * TokenRows: members are query tokens q0 .. q0 + k - 1 of one sequence at
+//    absolute positions pos0 .. pos0 + k - 1, each attending keys 0 .. its
+//    position (causal), as in verifying several drafted tokens at once.
+struct SeqRows {
+  static constexpr bool kCausal = false;
+  int s, k;
+  const int32_t* lens;
+  int max_context_len;
+  __device__ int table_row() const { return s; }
+  __device__ int members() const { return k; }
+  __device__ int64_t base(int mi) const { return (int64_t)s + mi; }
+  __device__ int parts(int mi) const { return (clamp_len(lens[s + mi], max_context_len) + kPart - 1) / kPart; }
+  __device__ int limit(int) const { return 0x7fffffff; }
+};
+struct TokenRows {
+  static constexpr bool kCausal = true;
+  int s, q0, k, pos0;
+  __device__ int table_row() const { return s; }
+  __device__ int members() const { return k; }
+  __device__ int64_t base(int mi) const { return (int64_t)q0 + mi; }
+  __device__ int parts(int mi) const { return (pos0 + mi + kPart) / kPart; }  // partitions holding keys 0 .. pos
+  __device__ int limit(int mi) const { return pos0 + mi + 1; }
+};
+
+// One partition on MFMA for the query rows R describes, whose members all
+// read the same blocks for it (16 RT rows: row r = member r / G, head r % G;
+// rows past k G repeat member 0 and are not stored).  The first n tokens of
+// the partition are valid (Masked; otherwise all kPart), and with causal rows
+// member m sees keys below R.limit(m) only.  K/V of
 // the partition's blocks are read once.  Each wave takes 128 tokens (8
 // blocks) whole:
 //  * S^T = K Q^T on MFMA 16x16x32 with K rows loaded from the pool straight
@@ -438,18 +478,18 @@ __device__ __forceinline__ uint64_t ld8(const void* p) { return *reinterpret_cas
 //  * O^T += V^T P^T with V loaded into operand layout and widened to fp16;
 //    the waves' (max, sum, o) are merged through LDS and written as each
 //    member's partition result (8-bit values: times v_mul, the pool scale).
-template <typename KV, typename QT, int D, int G, int RT, bool Masked, int OutCode>
-__device__ __forceinline__ void mfma_partition(int s, int k, int n, int g, int p, RunLds<D, 16 * RT>& sh,
+template <typename KV, typename QT, int D, int G, int RT, bool Masked, int OutCode, int NH, typename Rows>
+__device__ __forceinline__ void mfma_partition(const Rows& R, int n, int g, int p, RunLds<D, 16 * RT>& sh,
                                                void* __restrict__ out, float* __restrict__ ws_o,
                                                float* __restrict__ ws_ml, const typename QT::bits* __restrict__ q,
                                                const unsigned char* __restrict__ kpool,
                                                const unsigned char* __restrict__ vpool,
-                                               const int32_t* __restrict__ tables, int max_blocks,
-                                               const int32_t* __restrict__ lens, int Hkv, int64_t num_blocks,
-                                               int max_context_len, float scale_log2, float v_mul, int max_parts) {
+                                               const int32_t* __restrict__ tables, int max_blocks, int Hkv,
+                                               int64_t num_blocks, float scale_log2, float v_mul, int max_parts) {
   constexpr bool F8 = KV::kBytes == 1;
+  constexpr bool kCausal = Rows::kCausal;
   static_assert(F8 || (KV::kBytes == 2 && KV::kCode == QT::kCode), "16-bit K/V take queries of their type");
-  static_assert(F8 || !Masked, "partial partitions go to MFMA for 8-bit K/V only");
+  static_assert(Masked || !kCausal, "causal rows need the masked path");
   constexpr int DC = D / 32;                         // 32-dim slices of the score contraction
   constexpr int DT = D / 16;                         // 16-dim tiles of the output
   constexpr int CH = D * KV::kBytes / 16;            // 16-byte K chunks per token
@@ -457,22 +497,27 @@ __device__ __forceinline__ void mfma_partition(int s, int k, int n, int g, int p
   constexpr int VROW = kBlockSize * KV::kBytes;      // bytes of one dim of a V tile
   constexpr int TILE = D * VROW;                     // bytes of one (block, head) tile
   constexpr int WB = kPartBlocks / kWaves;           // blocks per wave
-  static_assert(WB % 2 == 0, "waves take whole block pairs");
+  constexpr int HB = WB / NH;                        // blocks per part of a wave
+  static_assert(HB % 2 == 0 && HB * NH == WB, "wave parts take whole block pairs");
   using vraw_t = typename std::conditional<F8, uint64_t, u32x4>::type;
   const int Hq = Hkv * G;
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int q4 = lane >> 4, r16 = lane & 15;
+  const int k = R.members();
 
   // query rows as B operands: lane (q4, r16) holds row 16 rt + r16 and the
   // dims of its K operand (16-bit K: 32 dc + 8 q4 ..; 8-bit K: 64 (dc/2) +
   // 16 q4 + 8 (dc%2) ..)
   u32x4 bq[RT][DC];
+  int klim[RT];  // causal rows: keys of this partition the lane's row sees
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
     const int row = 16 * rt + r16;
     const int mi = row / G < k ? row / G : 0;
-    const typename QT::bits* qp = q + ((int64_t)(s + mi) * Hq + g * G + row % G) * D;
+    const int lim = R.limit(mi) - p * kPart;
+    klim[rt] = lim < n ? lim : n;
+    const typename QT::bits* qp = q + (R.base(mi) * Hq + g * G + row % G) * D;
 #pragma unroll
     for (int dc = 0; dc < DC; ++dc)
       bq[rt][dc] = ld16(qp + (F8 ? 64 * (dc >> 1) + 16 * q4 + 8 * (dc & 1) : 32 * dc + 8 * q4));
@@ -480,7 +525,8 @@ __device__ __forceinline__ void mfma_partition(int s, int k, int n, int g, int p
 
   // the partition's block ids, read once into LDS (0 past the valid tokens)
   if (tid < kPartBlocks)
-    sh.blk[tid] = (!Masked || tid * kBlockSize < n) ? tables[(int64_t)s * max_blocks + p * kPartBlocks + tid] : 0;
+    sh.blk[tid] =
+        (!Masked || tid * kBlockSize < n) ? tables[(int64_t)R.table_row() * max_blocks + p * kPartBlocks + tid] : 0;
   __syncthreads();
   const int32_t* tab = sh.blk + w * WB;
   const int wbase = w * WB * kBlockSize;  // the wave's first token in the partition
@@ -495,113 +541,144 @@ __device__ __forceinline__ void mfma_partition(int s, int k, int n, int g, int p
     // this lane's K row inside a block pair for score tile `sub`
     const int k_half = r16 >> 3;                          // which block of the pair
     const int k_tok = 8 * ((r16 >> 2) & 1) + (r16 & 3);  // token, + 4 sub
-    u32x4 ka[WB][KC];  // tile 2 kp + sub
-#pragma unroll
-    for (int kp = 0; kp < WB / 2; ++kp) {
-      const bool in = !Masked || wbase + (2 * kp + k_half) * kBlockSize < n;
-      const int64_t kb = clamp_block(tab[2 * kp + k_half], num_blocks);
-      const unsigned char* kr = kpool + ((kb * Hkv + g) * CH + q4) * (kBlockSize * 16) + k_tok * 16;
-#pragma unroll
-      for (int sub = 0; sub < 2; ++sub)
-#pragma unroll
-        for (int c = 0; c < KC; ++c)
-          ka[2 * kp + sub][c] = in ? ld16(kr + (4 * sub + c * 4 * kBlockSize) * 16) : u32x4{0u, 0u, 0u, 0u};
-    }
-    f32x4 st[WB][RT];
-    if constexpr (F8) {
-#pragma unroll
-      for (int kt = 0; kt < WB; ++kt)
-#pragma unroll
-        for (int rt = 0; rt < RT; ++rt) st[kt][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kt = 0; kt < WB; ++kt)
-#pragma unroll
-        for (int dc = 0; dc < DC; ++dc) {
-          const u32x4 a = e4m3x8_to<QT>(ka[kt][dc >> 1][2 * (dc & 1)], ka[kt][dc >> 1][2 * (dc & 1) + 1]);
-#pragma unroll
-          for (int rt = 0; rt < RT; ++rt) st[kt][rt] = mfma_qk<QT>(a, bq[rt][dc], st[kt][rt]);
-        }
-    } else {
-#pragma unroll
-      for (int kt = 0; kt < WB; ++kt)
-#pragma unroll
-        for (int rt = 0; rt < RT; ++rt) {
-          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int dc = 0; dc < DC; ++dc) acc = mfma_qk<QT>(ka[kt][dc], bq[rt][dc], acc);
-          st[kt][rt] = acc;
-        }
-    }
-    // the V operand loads are issued next, ahead of the softmax: lane (q4,
-    // r16) takes dim 16 dt + r16, keys 8 q4 .. 8 q4 + 7 of the pair (half of
-    // the dim's row in block q4 / 2)
-    vraw_t vraw[WB / 2][DT];
-#pragma unroll
-    for (int kp = 0; kp < WB / 2; ++kp) {
-      const bool in = !Masked || wbase + (2 * kp + (q4 >> 1)) * kBlockSize < n;
-      const int64_t vb = clamp_block(tab[2 * kp + (q4 >> 1)], num_blocks);
-      const unsigned char* vr = vpool + (vb * Hkv + g) * (int64_t)TILE + r16 * VROW + (q4 & 1) * (VROW / 2);
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        if constexpr (F8)
-          vraw[kp][dt] = in ? ld8(vr + dt * 16 * VROW) : 0ull;
-        else
-          vraw[kp][dt] = ld16(vr + dt * 16 * VROW);
-      }
-    }
-    // exact softmax over the wave's keys, per row
-    u32x4 pb[WB / 2][RT];
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
-      float mx = -INFINITY;
-#pragma unroll
-      for (int kt = 0; kt < WB; ++kt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          float x = st[kt][rt][r] * scale_log2;
-          if constexpr (Masked) {  // keys past the context may hold anything
-            const int key = wbase + (kt >> 1) * 2 * kBlockSize + 8 * q4 + 4 * (kt & 1) + r;
-            x = key < n ? x : -INFINITY;
-          }
-          st[kt][rt][r] = x;
-          mx = fmaxf(mx, x);
-        }
-      m[rt] = rows4_max(mx);
-      float ls = 0.f;
-#pragma unroll
-      for (int kt = 0; kt < WB; ++kt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          st[kt][rt][r] = __builtin_amdgcn_exp2f(st[kt][rt][r] - m[rt]);
-          ls += st[kt][rt][r];
-        }
-      l[rt] = rows4_sum(ls);
-#pragma unroll
-      for (int kp = 0; kp < WB / 2; ++kp)
-        pb[kp][rt] = u32x4{pack_f16x2(st[2 * kp][rt][0], st[2 * kp][rt][1]),
-                           pack_f16x2(st[2 * kp][rt][2], st[2 * kp][rt][3]),
-                           pack_f16x2(st[2 * kp + 1][rt][0], st[2 * kp + 1][rt][1]),
-                           pack_f16x2(st[2 * kp + 1][rt][2], st[2 * kp + 1][rt][3])};
+      m[rt] = -INFINITY;
+      l[rt] = 0.f;
     }
-    // O^T += V^T P^T: lane (q4, r16) holds dim 16 dt + r16, keys 8 q4 .. 8 q4 + 7 of the pair
+    // the wave's blocks in NH parts, one after the other with a running
+    // softmax (fewer registers in flight per part)
 #pragma unroll
-    for (int kp = 0; kp < WB / 2; ++kp)
+    for (int h = 0; h < NH; ++h) {
+      const int hb = h * HB;                      // the part's first block (wave-local)
+      const int hbase = wbase + hb * kBlockSize;  // and token (partition-local)
+      if (Masked && hbase >= n) break;            // uniform
+      u32x4 ka[HB][KC];  // tile 2 kp + sub
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        u32x4 va;
-        if constexpr (F8) {
-          uint64_t bytes = vraw[kp][dt];
-          if constexpr (Masked) {  // zero the codes of keys past the context (they may be NaN codes)
-            const int nv = n - (wbase + kp * 2 * kBlockSize + 8 * q4);
-            bytes &= nv >= 8 ? ~0ull : (nv <= 0 ? 0ull : (1ull << (8 * nv)) - 1ull);
-          }
-          va = e4m3x8_to<F16>((uint32_t)bytes, (uint32_t)(bytes >> 32));
-        } else {
-          va = to_f16x8<KV>(vraw[kp][dt]);
-        }
+      for (int kp = 0; kp < HB / 2; ++kp) {
+        const bool in = !Masked || hbase + (2 * kp + k_half) * kBlockSize < n;
+        const int64_t kb = clamp_block(tab[hb + 2 * kp + k_half], num_blocks);
+        const unsigned char* kr = kpool + ((kb * Hkv + g) * CH + q4) * (kBlockSize * 16) + k_tok * 16;
 #pragma unroll
-        for (int rt = 0; rt < RT; ++rt) o[rt][dt] = mfma_f16(va, pb[kp][rt], o[rt][dt]);
+        for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+          for (int c = 0; c < KC; ++c)
+            ka[2 * kp + sub][c] = in ? ld16(kr + (4 * sub + c * 4 * kBlockSize) * 16) : u32x4{0u, 0u, 0u, 0u};
       }
+      f32x4 st[HB][RT];
+      if constexpr (F8) {
+#pragma unroll
+        for (int kt = 0; kt < HB; ++kt)
+#pragma unroll
+          for (int rt = 0; rt < RT; ++rt) st[kt][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kt = 0; kt < HB; ++kt)
+#pragma unroll
+          for (int dc = 0; dc < DC; ++dc) {
+            const u32x4 a = e4m3x8_to<QT>(ka[kt][dc >> 1][2 * (dc & 1)], ka[kt][dc >> 1][2 * (dc & 1) + 1]);
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) st[kt][rt] = mfma_qk<QT>(a, bq[rt][dc], st[kt][rt]);
+          }
+      } else {
+#pragma unroll
+        for (int kt = 0; kt < HB; ++kt)
+#pragma unroll
+          for (int rt = 0; rt < RT; ++rt) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int dc = 0; dc < DC; ++dc) acc = mfma_qk<QT>(ka[kt][dc], bq[rt][dc], acc);
+            st[kt][rt] = acc;
+          }
+      }
+      // the V operand loads are issued next, ahead of the softmax: lane (q4,
+      // r16) takes dim 16 dt + r16, keys 8 q4 .. 8 q4 + 7 of the pair (half
+      // of the dim's row in block q4 / 2)
+      vraw_t vraw[HB / 2][DT];
+#pragma unroll
+      for (int kp = 0; kp < HB / 2; ++kp) {
+        const bool in = !Masked || hbase + (2 * kp + (q4 >> 1)) * kBlockSize < n;
+        const int64_t vb = clamp_block(tab[hb + 2 * kp + (q4 >> 1)], num_blocks);
+        const unsigned char* vr = vpool + (vb * Hkv + g) * (int64_t)TILE + r16 * VROW + (q4 & 1) * (VROW / 2);
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          if constexpr (F8)
+            vraw[kp][dt] = in ? ld8(vr + dt * 16 * VROW) : 0ull;
+          else
+            vraw[kp][dt] = ld16(vr + dt * 16 * VROW);
+        }
+      }
+      // exact softmax over the wave's keys, per row (running over the parts)
+      u32x4 pb[HB / 2][RT];
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kt = 0; kt < HB; ++kt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            float x = st[kt][rt][r] * scale_log2;
+            if constexpr (Masked) {  // keys past the context may hold anything
+              const int key = hbase + (kt >> 1) * 2 * kBlockSize + 8 * q4 + 4 * (kt & 1) + r;
+              x = key < (kCausal ? klim[rt] : n) ? x : -INFINITY;
+            }
+            st[kt][rt][r] = x;
+            mx = fmaxf(mx, x);
+          }
+        const float mnew = fmaxf(m[rt], rows4_max(mx));
+        // a causal row may see none of the keys so far: its weights are 0
+        const float mref = (kCausal && mnew == -INFINITY) ? 0.f : mnew;
+        if (h > 0) {  // rescale what the earlier parts accumulated
+          const float alpha = __builtin_amdgcn_exp2f(m[rt] - mref);
+          l[rt] *= alpha;
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt) o[rt][dt] *= alpha;
+        }
+        float ls = 0.f;
+#pragma unroll
+        for (int kt = 0; kt < HB; ++kt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            st[kt][rt][r] = __builtin_amdgcn_exp2f(st[kt][rt][r] - mref);
+            ls += st[kt][rt][r];
+          }
+        l[rt] += rows4_sum(ls);
+        m[rt] = mnew;
+#pragma unroll
+        for (int kp = 0; kp < HB / 2; ++kp)
+          pb[kp][rt] = u32x4{pack_f16x2(st[2 * kp][rt][0], st[2 * kp][rt][1]),
+                             pack_f16x2(st[2 * kp][rt][2], st[2 * kp][rt][3]),
+                             pack_f16x2(st[2 * kp + 1][rt][0], st[2 * kp + 1][rt][1]),
+                             pack_f16x2(st[2 * kp + 1][rt][2], st[2 * kp + 1][rt][3])};
+      }
+      // O^T += V^T P^T: lane (q4, r16) holds dim 16 dt + r16, keys 8 q4 .. 8 q4 + 7 of the pair
+#pragma unroll
+      for (int kp = 0; kp < HB / 2; ++kp)
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          u32x4 va;
+          if constexpr (F8) {
+            uint64_t bytes = vraw[kp][dt];
+            if constexpr (Masked) {  // zero the codes of keys past the context (they may be NaN codes)
+              const int nv = n - (hbase + kp * 2 * kBlockSize + 8 * q4);
+              bytes &= nv >= 8 ? ~0ull : (nv <= 0 ? 0ull : (1ull << (8 * nv)) - 1ull);
+            }
+            va = e4m3x8_to<F16>((uint32_t)bytes, (uint32_t)(bytes >> 32));
+          } else {
+            u32x4 vv = vraw[kp][dt];
+            if constexpr (Masked) {  // zero keys past the context (they may hold NaN)
+              const int nv = n - (hbase + kp * 2 * kBlockSize + 8 * q4);
+              if (nv < 8) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                  vv[e] &= 2 * e + 1 < nv ? 0xffffffffu : (2 * e < nv ? 0x0000ffffu : 0u);
+              }
+            }
+            va = to_f16x8<KV>(vv);
+          }
+#pragma unroll
+          for (int rt = 0; rt < RT; ++rt) o[rt][dt] = mfma_f16(va, pb[kp][rt], o[rt][dt]);
+        }
+    }
   } else {
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
@@ -630,13 +707,15 @@ __device__ __forceinline__ void mfma_partition(int s, int k, int n, int g, int p
     float den = 0.f;
 #pragma unroll
     for (int x = 0; x < kWaves; ++x) {
-      const float f = __builtin_amdgcn_exp2f(sh.ml[x][tid][0] - Mx);  // 0 for a wave with no keys
+      // 0 for a wave with no keys (a causal row may have none in the whole partition)
+      const float mw = sh.ml[x][tid][0];
+      const float f = (kCausal && mw == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mw - Mx);
       sh.wgt[tid][x] = f;
       den = fmaf(f, sh.ml[x][tid][1], den);
     }
     sh.row_m[tid] = Mx;
     sh.row_l[tid] = den;
-    sh.row_parts[tid] = (clamp_len(lens[s + tid / G], max_context_len) + kPart - 1) / kPart;
+    sh.row_parts[tid] = R.parts(tid / G);
   }
   __syncthreads();
   for (int i = tid; i < rows * D; i += kThreads) {
@@ -645,7 +724,7 @@ __device__ __forceinline__ void mfma_partition(int s, int k, int n, int g, int p
 #pragma unroll
     for (int x = 0; x < kWaves; ++x) acc = fmaf(sh.wgt[row][x], sh.o[x][row][j], acc);
     if constexpr (F8) acc *= v_mul;
-    const int64_t orow = (int64_t)(s + row / G) * Hq + g * G + row % G;
+    const int64_t orow = R.base(row / G) * Hq + g * G + row % G;
     if (sh.row_parts[row] == 1) {
       store_out<OutCode>(out, orow * D + j, acc / sh.row_l[row]);
     } else {
@@ -714,9 +793,9 @@ decode_shared_kernel(void* __restrict__ out, float* __restrict__ ws_o, float* __
       if (!((jm >> (s0 + 1)) & 1u) || ((jm >> s0) & 1u)) continue;
       int k = 2;
       while (s0 + k < KM && ((jm >> (s0 + k)) & 1u)) ++k;
-      mfma_partition<KV, QT, D, G, kRunRows / 16, false, OutCode>(
-          s_first + s0, k, kPart, g, p, sh, out, ws_o, ws_ml, q, kpool, vpool, tables, max_blocks, lens, Hkv,
-          num_blocks, max_context_len, scale_log2, v_mul, max_parts);
+      mfma_partition<KV, QT, D, G, kRunRows / 16, false, OutCode, PKV_SHARED_PARTS>(
+          SeqRows{s_first + s0, k, lens, max_context_len}, kPart, g, p, sh, out, ws_o, ws_ml, q, kpool, vpool,
+          tables, max_blocks, Hkv, num_blocks, scale_log2, v_mul, max_parts);
     }
   }
 }
@@ -750,9 +829,9 @@ decode_fp8_partition_kernel(void* __restrict__ out, float* __restrict__ ws_o, fl
   if (in_shared_run<FP8, G>(pr, tables, max_blocks, max_context_len, s, p, L)) return;
   const int t0 = p * kPart;
   const int n = (L - t0) < kPart ? (L - t0) : kPart;  // tokens in this partition, >= 1
-  mfma_partition<FP8, QT, D, G, 1, true, OutCode>(s, 1, n, g, p, sh, out, ws_o, ws_ml, q, kpool, vpool, tables,
-                                                  max_blocks, lens, Hkv, num_blocks, max_context_len, scale_log2,
-                                                  v_mul, max_parts);
+  mfma_partition<FP8, QT, D, G, 1, true, OutCode, PKV_FP8_PARTS>(SeqRows{s, 1, lens, max_context_len}, n, g, p, sh, out, ws_o,
+                                                  ws_ml, q, kpool, vpool, tables, max_blocks, Hkv, num_blocks,
+                                                  scale_log2, v_mul, max_parts);
 }
 
 template <typename T, int D, int G, int OutCode>
@@ -793,16 +872,23 @@ decode_partition_kernel(void* __restrict__ out, float* __restrict__ ws_o, float*
                                    num_blocks, max_context_len, scale_log2, max_parts);
 }
 
-template <int D, int OutCode>
+template <int D, int OutCode, bool PerToken>
 __global__ void __launch_bounds__(64)
-decode_reduce_kernel(void* __restrict__ out, const float* __restrict__ ws_o,
-                     const float* __restrict__ ws_ml, const int32_t* __restrict__ lens, int Hq, int G,
+decode_reduce_kernel(void* __restrict__ out, const float* __restrict__ ws_o, const float* __restrict__ ws_ml,
+                     const int32_t* __restrict__ lens, const int32_t* __restrict__ tok_parts, int Hq,
                      int max_context_len, int max_parts) {
+  // row blockIdx.y: a sequence (decode) or a query token (verify: its own
+  // partition count, written by the partition pass)
   constexpr int DPL = D / 64;
   const int h = blockIdx.x, s = blockIdx.y, lane = threadIdx.x;
-  int L = lens[s];
-  L = L < 0 ? 0 : (L > max_context_len ? max_context_len : L);
-  const int nparts = (L + kPart - 1) / kPart;
+  int nparts;
+  if constexpr (PerToken) {
+    nparts = tok_parts[s];
+  } else {
+    int L = lens[s];
+    L = L < 0 ? 0 : (L > max_context_len ? max_context_len : L);
+    nparts = (L + kPart - 1) / kPart;
+  }
   if (nparts <= 1) return;
   const int64_t row = (int64_t)s * Hq + h;
   const float* ml = ws_ml + row * max_parts * 2;
@@ -820,7 +906,54 @@ decode_reduce_kernel(void* __restrict__ out, const float* __restrict__ ws_o,
   }
 #pragma unroll
   for (int dd = 0; dd < DPL; ++dd) store_out<OutCode>(out, row * D + lane * DPL + dd, acc[dd] / den);
-  (void)G;
+}
+
+// ---- verify attention: several new query tokens per sequence ---------------
+// Checking drafted tokens ("speculative decoding": a small model drafts k
+// tokens, the large one checks them in one pass) appends k + 1 tokens to a
+// sequence and attends each of them causally to the cached keys and the new
+// keys before it — a prefill chunk with a tiny q_len.  Its bytes are those of
+// a decode step (the whole context once per KV head), its contraction
+// (q_len G) rows deep: the same MFMA partition routine as the shared decode
+// runs, with the sequence's new tokens as the members and a causal limit per
+// row.  Grid (KV head, sequence, partition), partitions last to first; a
+// workgroup serves the query tokens in groups of 32 / G (32 rows), each group
+// reading the partition's K/V (the second from L2).  Rows whose keys span
+// several partitions leave partial states merged by decode_reduce_kernel,
+// which learns each token's own partition count from tok_parts.
+template <typename T, int D, int G, int OutCode>
+__global__ void __launch_bounds__(kThreads, 2)
+verify_partition_kernel(void* __restrict__ out, float* __restrict__ ws_o, float* __restrict__ ws_ml,
+                        int32_t* __restrict__ tok_parts, const typename T::bits* __restrict__ q,
+                        const unsigned char* __restrict__ kpool, const unsigned char* __restrict__ vpool,
+                        const int32_t* __restrict__ tables, int max_blocks, const int32_t* __restrict__ cu_q,
+                        const int32_t* __restrict__ lens, int total_q, int max_q_len, int Hkv, int64_t num_blocks,
+                        int max_context_len, float scale_log2, int max_parts) {
+  constexpr int TPG = kRunRows / G;  // query tokens per 32-row group
+  __shared__ __attribute__((aligned(16))) RunLds<D, kRunRows> sh;
+  const int g = blockIdx.x, s = blockIdx.y, p = gridDim.z - 1 - blockIdx.z;
+  int q0 = cu_q[s], q1 = cu_q[s + 1];
+  q0 = q0 < 0 ? 0 : (q0 > total_q ? total_q : q0);
+  q1 = q1 < q0 ? q0 : (q1 > total_q ? total_q : q1);
+  const int L = clamp_len(lens[s], max_context_len);
+  int ql = q1 - q0;
+  ql = ql > max_q_len ? max_q_len : ql;
+  ql = ql > L ? L : ql;
+  const int pos_first = L - ql;  // absolute position of the first new token
+  if (tok_parts && g == 0 && p == 0 && (int)threadIdx.x < ql)
+    tok_parts[q0 + threadIdx.x] = (pos_first + (int)threadIdx.x + kPart) / kPart;
+  const int nparts = (L + kPart - 1) / kPart;
+  if (ql == 0 || p >= nparts) return;
+  const int t0 = p * kPart;
+  const int n = (L - t0) < kPart ? (L - t0) : kPart;
+  for (int tg = 0; tg * TPG < ql; ++tg) {
+    const int k = ql - tg * TPG < TPG ? ql - tg * TPG : TPG;
+    const int pos0 = pos_first + tg * TPG;
+    if (pos0 + k - 1 < t0) continue;  // no token of the group reaches this partition (uniform)
+    mfma_partition<T, T, D, G, kRunRows / 16, true, OutCode, PKV_VERIFY_PARTS>(TokenRows{s, q0 + tg * TPG, k, pos0}, n, g, p, sh,
+                                                            out, ws_o, ws_ml, q, kpool, vpool, tables, max_blocks,
+                                                            Hkv, num_blocks, scale_log2, 1.f, max_parts);
+  }
 }
 
 struct DecodeArgs {
@@ -840,6 +973,10 @@ struct DecodeArgs {
   float v_mul;  // 8-bit cache: the V pool's scale
   int max_parts;
   hipStream_t stream;
+  // verify attention
+  const int32_t* cu_q = nullptr;
+  int total_q = 0, max_q_len = 0;
+  int32_t* tok_parts = nullptr;
 };
 
 template <typename KV, typename QT, int D, int G, int OutCode>
@@ -854,9 +991,11 @@ void launch_shared(const DecodeArgs& a) {
 
 template <int D, int OutCode>
 void launch_reduce(const DecodeArgs& a, int G) {
+  (void)G;
   if (a.max_parts > 1)
-    hipLaunchKernelGGL((decode_reduce_kernel<D, OutCode>), dim3((unsigned)a.Hq, (unsigned)a.B), dim3(64), 0,
-                       a.stream, a.out, a.ws_o, a.ws_ml, a.lens, a.Hq, G, a.max_context_len, a.max_parts);
+    hipLaunchKernelGGL((decode_reduce_kernel<D, OutCode, false>), dim3((unsigned)a.Hq, (unsigned)a.B), dim3(64),
+                       0, a.stream, a.out, a.ws_o, a.ws_ml, a.lens, (const int32_t*)nullptr, a.Hq,
+                       a.max_context_len, a.max_parts);
 }
 
 template <typename T, int D, int G, int OutCode>
@@ -886,6 +1025,20 @@ void launch_decode_fp8(const DecodeArgs& a, bool partitions, bool reduce) {
   if (reduce) launch_reduce<D, OutCode>(a, G);
 }
 
+// verify attention: the partition pass, then the per-token merge
+template <typename T, int D, int G, int OutCode>
+void launch_verify(const DecodeArgs& a) {
+  hipLaunchKernelGGL((verify_partition_kernel<T, D, G, OutCode>),
+                     dim3((unsigned)a.Hkv, (unsigned)a.B, (unsigned)a.max_parts), dim3(kThreads), 0, a.stream, a.out,
+                     a.ws_o, a.ws_ml, a.tok_parts, (const typename T::bits*)a.q, a.kpool, a.vpool, a.tables,
+                     a.max_blocks, a.cu_q, a.lens, a.total_q, a.max_q_len, a.Hkv, a.num_blocks, a.max_context_len,
+                     a.scale_log2, a.max_parts);
+  if (a.max_parts > 1)
+    hipLaunchKernelGGL((decode_reduce_kernel<D, OutCode, true>), dim3((unsigned)a.Hq, (unsigned)a.total_q),
+                       dim3(64), 0, a.stream, a.out, a.ws_o, a.ws_ml, a.lens, a.tok_parts, a.Hq, a.max_context_len,
+                       a.max_parts);
+}
+
 // Launcher<T, D, G, OutCode>::run(args, partitions, reduce)
 template <typename T, int D, int G, int OutCode>
 struct Plain {
@@ -894,6 +1047,11 @@ struct Plain {
 template <typename QT, int D, int G, int OutCode>
 struct Fp8 {
   static void run(const DecodeArgs& a, bool pa, bool re) { launch_decode_fp8<QT, D, G, OutCode>(a, pa, re); }
+};
+
+template <typename T, int D, int G, int OutCode>
+struct Verify {
+  static void run(const DecodeArgs& a, bool, bool) { launch_verify<T, D, G, OutCode>(a); }
 };
 
 template <template <typename, int, int, int> class Launcher, typename T, int D, int OutCode>
@@ -1061,4 +1219,89 @@ extern "C" int paged_attention_decode_fp8_partitions(PKV_DECODE_FP8_PARAMS) {
 }
 extern "C" int paged_attention_decode_fp8_reduce(PKV_DECODE_FP8_PARAMS) {
   return decode_impl("paged_attention_decode_fp8_reduce", false, true, true, PKV_DECODE_FP8_ARGS);
+}
+
+// ---- verify attention entry points ------------------------------------------
+extern "C" int64_t paged_attention_verify_workspace_bytes(int32_t total_q, int32_t n_q_heads, int32_t head_dim,
+                                                          int32_t max_context_len) {
+  if (total_q <= 0 || n_q_heads <= 0 || head_dim <= 0 || max_context_len <= 0) return 0;
+  const int64_t parts = (max_context_len + pkv::kPart - 1) / pkv::kPart;
+  if (parts <= 1) return 0;
+  return (int64_t)total_q * n_q_heads * parts * (head_dim + 2) * (int64_t)sizeof(float) + (int64_t)total_q * 4;
+}
+
+extern "C" int paged_attention_verify(void* out, int32_t out_dtype, const void* q, const void* k_pool,
+                                      const void* v_pool, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                      const int32_t* cu_q_lens, const int32_t* context_lens, int32_t n_seqs,
+                                      int32_t total_q, int32_t max_q_len, int32_t n_q_heads, int32_t n_kv_heads,
+                                      int32_t head_dim, int32_t block_size, int64_t num_blocks,
+                                      int32_t max_context_len, float scale, int32_t kv_dtype, void* workspace,
+                                      int64_t workspace_bytes, void* stream) {
+  const std::string F("paged_attention_verify");
+  if (kv_dtype != PKV_F16 && kv_dtype != PKV_BF16)
+    return fail(pkv::esize_of(kv_dtype) ? PKV_EUNSUPPORTED : PKV_EINVAL, F + ": kv dtype must be f16 or bf16");
+  if (out_dtype != PKV_F32 && out_dtype != kv_dtype)
+    return fail(PKV_EINVAL, F + ": out dtype must be f32 or the kv dtype");
+  if (block_size != pkv::kBlockSize) return fail(PKV_EUNSUPPORTED, "block_size must be 16");
+  if (head_dim != 64 && head_dim != 128) return fail(PKV_EUNSUPPORTED, "head_dim must be 64 or 128");
+  if (n_kv_heads < 1 || n_q_heads < 1 || n_kv_heads > 65535 || n_q_heads % n_kv_heads)
+    return fail(PKV_EINVAL, F + ": n_q_heads must be a positive multiple of n_kv_heads");
+  const int G = n_q_heads / n_kv_heads;
+  if (G != 1 && G != 2 && G != 4 && G != 8 && G != 16)
+    return fail(PKV_EUNSUPPORTED, F + ": n_q_heads / n_kv_heads must be 1, 2, 4, 8 or 16");
+  if (n_seqs < 0 || n_seqs > 65535 || total_q < 0 || total_q > 65535 || max_q_len < 0)
+    return fail(PKV_EINVAL, F + ": bad n_seqs, total_q or max_q_len");
+  if (max_q_len > 64)
+    return fail(PKV_EUNSUPPORTED, F + ": more than 64 query tokens per sequence (use paged_attention_prefill_chunk)");
+  if (num_blocks < 1 || max_blocks_per_seq < 1 || max_context_len < 0 ||
+      (int64_t)max_context_len > (int64_t)max_blocks_per_seq * block_size ||
+      (int64_t)max_context_len > 65535ll * pkv::kPart)
+    return fail(PKV_EINVAL, F + ": max_context_len exceeds the table width");
+  if (n_seqs == 0 || total_q == 0 || max_q_len == 0) return ok();
+  if (!out || !q || !k_pool || !v_pool || !block_tables || !cu_q_lens || !context_lens)
+    return fail(PKV_EINVAL, F + ": NULL pointer");
+  if (!pkv::aligned16(q) || !pkv::aligned16(k_pool) || !pkv::aligned16(v_pool) || !pkv::aligned16(out))
+    return fail(PKV_EINVAL, F + ": q, out and pools must be 16-byte aligned");
+  if (!std::isfinite(scale)) return fail(PKV_EINVAL, F + ": scale not finite");
+  const int max_parts = max_context_len > 0 ? (max_context_len + pkv::kPart - 1) / pkv::kPart : 1;
+  const int64_t need = paged_attention_verify_workspace_bytes(total_q, n_q_heads, head_dim, max_context_len);
+  if (need > 0 && (!workspace || workspace_bytes < need || !pkv::aligned16(workspace)))
+    return fail(PKV_EINVAL, F + ": workspace missing or too small (need " + std::to_string(need) + " bytes)");
+  pkv::DecodeArgs a;
+  a.out = out;
+  const int64_t rows = (int64_t)total_q * n_q_heads;
+  a.ws_o = (float*)workspace;
+  a.ws_ml = need > 0 ? a.ws_o + rows * max_parts * head_dim : nullptr;
+  a.tok_parts = need > 0 ? (int32_t*)(a.ws_ml + rows * max_parts * 2) : nullptr;
+  a.q = q;
+  a.kpool = (const unsigned char*)k_pool;
+  a.vpool = (const unsigned char*)v_pool;
+  a.tables = block_tables;
+  a.max_blocks = max_blocks_per_seq;
+  a.lens = context_lens;
+  a.B = n_seqs;
+  a.Hq = n_q_heads;
+  a.Hkv = n_kv_heads;
+  a.num_blocks = num_blocks;
+  a.max_context_len = max_context_len;
+  a.scale_log2 = (float)((double)scale * 1.4426950408889634);
+  a.v_mul = 1.f;
+  a.max_parts = max_parts;
+  a.stream = (hipStream_t)stream;
+  a.cu_q = cu_q_lens;
+  a.total_q = total_q;
+  a.max_q_len = max_q_len;
+  using pkv::dispatch_d;
+  using pkv::Verify;
+  int rc;
+  if (kv_dtype == PKV_BF16)
+    rc = out_dtype == PKV_F32 ? dispatch_d<Verify, pkv::BF16, PKV_F32>(a, head_dim, G, true, true)
+                              : dispatch_d<Verify, pkv::BF16, PKV_BF16>(a, head_dim, G, true, true);
+  else
+    rc = out_dtype == PKV_F32 ? dispatch_d<Verify, pkv::F16, PKV_F32>(a, head_dim, G, true, true)
+                              : dispatch_d<Verify, pkv::F16, PKV_F16>(a, head_dim, G, true, true);
+  if (rc) return fail(PKV_EUNSUPPORTED, F + ": configuration not built");
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(PKV_EHIP, F + ": " + hipGetErrorString(e));
+  return ok();
 }
