@@ -510,6 +510,18 @@ int paged_attention_verify(void* out, int32_t out_dtype, const void* q, const vo
                            int32_t max_context_len, float scale, int32_t kv_dtype, void* workspace,
                            int64_t workspace_bytes, void* stream);
 
+/* paged_attention_verify over an 8-bit cache (PKV_FP8_E4M3 pools, scales as
+ * for paged_attention_decode_fp8): queries and output in q_dtype (PKV_F16 or
+ * PKV_BF16; out PKV_F32 or q_dtype); everything else as paged_attention_verify. */
+int paged_attention_verify_fp8(void* out, int32_t out_dtype, const void* q, int32_t q_dtype,
+                               const void* k_pool, const void* v_pool, float k_scale, float v_scale,
+                               const int32_t* block_tables, int32_t max_blocks_per_seq,
+                               const int32_t* cu_q_lens, const int32_t* context_lens, int32_t n_seqs,
+                               int32_t total_q, int32_t max_q_len, int32_t n_q_heads,
+                               int32_t n_kv_heads, int32_t head_dim, int32_t block_size,
+                               int64_t num_blocks, int32_t max_context_len, float scale,
+                               void* workspace, int64_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

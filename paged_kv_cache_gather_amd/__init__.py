@@ -111,6 +111,8 @@ for _n in ("paged_attention_decode_fp8", "paged_attention_decode_fp8_partitions"
 _sig("paged_attention_verify_workspace_bytes", _i64, _i32, _i32, _i32, _i32)
 _sig("paged_attention_verify", ctypes.c_int, _P, _i32, _P, _P, _P, _P, _i32, _P, _P, _i32, _i32, _i32, _i32, _i32,
      _i32, _i32, _i64, _i32, _f32, _i32, _P, _i64, _P)
+_sig("paged_attention_verify_fp8", ctypes.c_int, _P, _i32, _P, _i32, _P, _P, _f32, _f32, _P, _i32, _P, _P, _i32, _i32,
+     _i32, _i32, _i32, _i32, _i32, _i64, _i32, _f32, _P, _i64, _P)
 _sig("paged_attention_prefill_chunk", ctypes.c_int, _P, _i32, _P, _P, _P, _P, _i32, _P, _P, _i32,
      _i32, _i32, _i32, _i32, _i32, _i32, _i64, _i32, _f32, _i32, _P)
 
@@ -632,6 +634,42 @@ def paged_attention_verify(out: torch.Tensor, q: torch.Tensor, k_pool: torch.Ten
         block_tables.shape[1], _ptr(cu_q_lens), _ptr(context_lens), n, total_q, max_q_len, Hq, n_kv_heads, d,
         block_size, num_blocks, max_context_len, float(scale), dtype_code(k_pool.dtype), _ptr(workspace), ws_bytes,
         _stream(stream, q.device)))
+
+
+def paged_attention_verify_fp8(out: torch.Tensor, q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
+                               block_tables: torch.Tensor, cu_q_lens: torch.Tensor, context_lens: torch.Tensor,
+                               max_q_len: int, max_context_len: int, n_kv_heads: int, num_blocks: int, scale: float,
+                               k_scale: float, v_scale: float, workspace=None, block_size: int = BLOCK_SIZE,
+                               stream=None):
+    """paged_attention_verify over 8-bit pools (uint8 / float8_e4m3fn codes
+    with scales); q f16 or bf16, out f32 or q's dtype."""
+    _dev(out, "out")
+    _dev(q, "q")
+    _dev(k_pool, "k_pool")
+    _dev(v_pool, "v_pool")
+    _dev(block_tables, "block_tables", torch.int32)
+    _dev(cu_q_lens, "cu_q_lens", torch.int32)
+    _dev(context_lens, "context_lens", torch.int32)
+    if not (_is_codes(k_pool) and _is_codes(v_pool)):
+        raise PagedKVError(PKV_EINVAL, "8-bit pools must be uint8 or float8_e4m3fn tensors")
+    if q.dim() != 3 or out.shape != q.shape:
+        raise PagedKVError(PKV_EINVAL, "q and out must be [total_q, n_q_heads, head_dim]")
+    total_q, Hq, d = q.shape
+    n = context_lens.numel()
+    if block_tables.dim() != 2 or block_tables.shape[0] != n or cu_q_lens.numel() != n + 1:
+        raise PagedKVError(PKV_EINVAL, "block_tables/cu_q_lens must match context_lens")
+    need = num_blocks * n_kv_heads * block_size * d
+    if k_pool.numel() < need or v_pool.numel() < need:
+        raise PagedKVError(PKV_EINVAL, "pool tensors smaller than num_blocks blocks")
+    ws_bytes = 0
+    if workspace is not None:
+        _dev(workspace, "workspace")
+        ws_bytes = workspace.numel() * workspace.element_size()
+    _check(_lib.paged_attention_verify_fp8(
+        _ptr(out), dtype_code(out.dtype), _ptr(q), dtype_code(q.dtype), _ptr(k_pool), _ptr(v_pool), float(k_scale),
+        float(v_scale), _ptr(block_tables), block_tables.shape[1], _ptr(cu_q_lens), _ptr(context_lens), n, total_q,
+        max_q_len, Hq, n_kv_heads, d, block_size, num_blocks, max_context_len, float(scale), _ptr(workspace),
+        ws_bytes, _stream(stream, q.device)))
 
 
 def paged_attention_prefill_chunk(out: torch.Tensor, q: torch.Tensor, k_pool: torch.Tensor,

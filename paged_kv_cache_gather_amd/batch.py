@@ -24,7 +24,7 @@ from . import (paged_kv_alloc, paged_kv_seq_create, paged_kv_seq_fork, paged_kv_
                paged_attention_decode_fp8_partitions, paged_attention_decode_fp8_reduce,
                paged_attention_decode_workspace_bytes, paged_attention_decode_partitions,
                paged_attention_decode_reduce, paged_attention_prefill_chunk, paged_attention_verify,
-               paged_attention_verify_workspace_bytes, BLOCK_SIZE)
+               paged_attention_verify_workspace_bytes, paged_attention_verify_fp8, BLOCK_SIZE)
 
 TORCH_DTYPE = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
 _VIEW = {"f32": torch.int32, "f16": torch.int16, "bf16": torch.int16}
@@ -292,18 +292,22 @@ class DeviceBatch:
 
     def attend_verify(self, out: torch.Tensor, stream=None):
         """The chunks' attention through paged_attention_verify (a few query
-        tokens per sequence: checking drafted tokens)."""
-        if self.fp8:
-            raise ValueError("verify attention reads 16-bit pools")
+        tokens per sequence: checking drafted tokens), or its 8-bit variant."""
         p = self.prefill
         w = self.w
         total = int(p.qlen.sum())
         need = paged_attention_verify_workspace_bytes(total, w.n_q_heads, w.head_dim, p.max_context_len)
         if need and (getattr(self, "_verify_ws", None) is None or self._verify_ws.numel() * 4 < need):
             self._verify_ws = torch.empty(need // 4 + 1, dtype=torch.float32, device=self.device)
-        paged_attention_verify(out, p.q, self.k_pool, self.v_pool, p.tables, p.cu_q_lens, p.lens_dev, p.max_q_len,
-                               p.max_context_len, w.n_kv_heads, w.num_blocks, w.scale,
-                               workspace=self._verify_ws if need else None, stream=stream)
+        ws = self._verify_ws if need else None
+        if self.fp8:
+            paged_attention_verify_fp8(out, p.q, self.k_pool, self.v_pool, p.tables, p.cu_q_lens, p.lens_dev,
+                                       p.max_q_len, p.max_context_len, w.n_kv_heads, w.num_blocks, w.scale,
+                                       self.k_scale, self.v_scale, workspace=ws, stream=stream)
+        else:
+            paged_attention_verify(out, p.q, self.k_pool, self.v_pool, p.tables, p.cu_q_lens, p.lens_dev,
+                                   p.max_q_len, p.max_context_len, w.n_kv_heads, w.num_blocks, w.scale, workspace=ws,
+                                   stream=stream)
 
     def new_decode_out(self):
         w = self.w

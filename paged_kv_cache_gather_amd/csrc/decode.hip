@@ -921,14 +921,14 @@ decode_reduce_kernel(void* __restrict__ out, const float* __restrict__ ws_o, con
 // reading the partition's K/V (the second from L2).  Rows whose keys span
 // several partitions leave partial states merged by decode_reduce_kernel,
 // which learns each token's own partition count from tok_parts.
-template <typename T, int D, int G, int OutCode>
+template <typename KV, typename QT, int D, int G, int OutCode>
 __global__ void __launch_bounds__(kThreads, 2)
 verify_partition_kernel(void* __restrict__ out, float* __restrict__ ws_o, float* __restrict__ ws_ml,
-                        int32_t* __restrict__ tok_parts, const typename T::bits* __restrict__ q,
+                        int32_t* __restrict__ tok_parts, const typename QT::bits* __restrict__ q,
                         const unsigned char* __restrict__ kpool, const unsigned char* __restrict__ vpool,
                         const int32_t* __restrict__ tables, int max_blocks, const int32_t* __restrict__ cu_q,
                         const int32_t* __restrict__ lens, int total_q, int max_q_len, int Hkv, int64_t num_blocks,
-                        int max_context_len, float scale_log2, int max_parts) {
+                        int max_context_len, float scale_log2, float v_mul, int max_parts) {
   constexpr int TPG = kRunRows / G;  // query tokens per 32-row group
   __shared__ __attribute__((aligned(16))) RunLds<D, kRunRows> sh;
   const int g = blockIdx.x, s = blockIdx.y, p = gridDim.z - 1 - blockIdx.z;
@@ -950,9 +950,9 @@ verify_partition_kernel(void* __restrict__ out, float* __restrict__ ws_o, float*
     const int k = ql - tg * TPG < TPG ? ql - tg * TPG : TPG;
     const int pos0 = pos_first + tg * TPG;
     if (pos0 + k - 1 < t0) continue;  // no token of the group reaches this partition (uniform)
-    mfma_partition<T, T, D, G, kRunRows / 16, true, OutCode, PKV_VERIFY_PARTS>(TokenRows{s, q0 + tg * TPG, k, pos0}, n, g, p, sh,
-                                                            out, ws_o, ws_ml, q, kpool, vpool, tables, max_blocks,
-                                                            Hkv, num_blocks, scale_log2, 1.f, max_parts);
+    mfma_partition<KV, QT, D, G, kRunRows / 16, true, OutCode, PKV_VERIFY_PARTS>(
+        TokenRows{s, q0 + tg * TPG, k, pos0}, n, g, p, sh, out, ws_o, ws_ml, q, kpool, vpool, tables, max_blocks, Hkv,
+        num_blocks, scale_log2, v_mul, max_parts);
   }
 }
 
@@ -1026,13 +1026,13 @@ void launch_decode_fp8(const DecodeArgs& a, bool partitions, bool reduce) {
 }
 
 // verify attention: the partition pass, then the per-token merge
-template <typename T, int D, int G, int OutCode>
+template <typename KV, typename QT, int D, int G, int OutCode>
 void launch_verify(const DecodeArgs& a) {
-  hipLaunchKernelGGL((verify_partition_kernel<T, D, G, OutCode>),
+  hipLaunchKernelGGL((verify_partition_kernel<KV, QT, D, G, OutCode>),
                      dim3((unsigned)a.Hkv, (unsigned)a.B, (unsigned)a.max_parts), dim3(kThreads), 0, a.stream, a.out,
-                     a.ws_o, a.ws_ml, a.tok_parts, (const typename T::bits*)a.q, a.kpool, a.vpool, a.tables,
+                     a.ws_o, a.ws_ml, a.tok_parts, (const typename QT::bits*)a.q, a.kpool, a.vpool, a.tables,
                      a.max_blocks, a.cu_q, a.lens, a.total_q, a.max_q_len, a.Hkv, a.num_blocks, a.max_context_len,
-                     a.scale_log2, a.max_parts);
+                     a.scale_log2, a.v_mul, a.max_parts);
   if (a.max_parts > 1)
     hipLaunchKernelGGL((decode_reduce_kernel<D, OutCode, true>), dim3((unsigned)a.Hq, (unsigned)a.total_q),
                        dim3(64), 0, a.stream, a.out, a.ws_o, a.ws_ml, a.lens, a.tok_parts, a.Hq, a.max_context_len,
@@ -1051,7 +1051,11 @@ struct Fp8 {
 
 template <typename T, int D, int G, int OutCode>
 struct Verify {
-  static void run(const DecodeArgs& a, bool, bool) { launch_verify<T, D, G, OutCode>(a); }
+  static void run(const DecodeArgs& a, bool, bool) { launch_verify<T, T, D, G, OutCode>(a); }
+};
+template <typename QT, int D, int G, int OutCode>
+struct VerifyFp8 {
+  static void run(const DecodeArgs& a, bool, bool) { launch_verify<FP8, QT, D, G, OutCode>(a); }
 };
 
 template <template <typename, int, int, int> class Launcher, typename T, int D, int OutCode>
@@ -1230,18 +1234,23 @@ extern "C" int64_t paged_attention_verify_workspace_bytes(int32_t total_q, int32
   return (int64_t)total_q * n_q_heads * parts * (head_dim + 2) * (int64_t)sizeof(float) + (int64_t)total_q * 4;
 }
 
-extern "C" int paged_attention_verify(void* out, int32_t out_dtype, const void* q, const void* k_pool,
-                                      const void* v_pool, const int32_t* block_tables, int32_t max_blocks_per_seq,
-                                      const int32_t* cu_q_lens, const int32_t* context_lens, int32_t n_seqs,
-                                      int32_t total_q, int32_t max_q_len, int32_t n_q_heads, int32_t n_kv_heads,
-                                      int32_t head_dim, int32_t block_size, int64_t num_blocks,
-                                      int32_t max_context_len, float scale, int32_t kv_dtype, void* workspace,
-                                      int64_t workspace_bytes, void* stream) {
-  const std::string F("paged_attention_verify");
-  if (kv_dtype != PKV_F16 && kv_dtype != PKV_BF16)
-    return fail(pkv::esize_of(kv_dtype) ? PKV_EUNSUPPORTED : PKV_EINVAL, F + ": kv dtype must be f16 or bf16");
-  if (out_dtype != PKV_F32 && out_dtype != kv_dtype)
-    return fail(PKV_EINVAL, F + ": out dtype must be f32 or the kv dtype");
+static int verify_impl(const char* fn, bool fp8, void* out, int32_t out_dtype, const void* q, int32_t q_dtype,
+                       const void* k_pool, const void* v_pool, float k_scale, float v_scale,
+                       const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* cu_q_lens,
+                       const int32_t* context_lens, int32_t n_seqs, int32_t total_q, int32_t max_q_len,
+                       int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim, int32_t block_size,
+                       int64_t num_blocks, int32_t max_context_len, float scale, int32_t kv_dtype, void* workspace,
+                       int64_t workspace_bytes, void* stream) {
+  const std::string F(fn);
+  if (!fp8 && kv_dtype != PKV_F16 && kv_dtype != PKV_BF16)
+    return fail(kv_dtype == PKV_F32 ? PKV_EUNSUPPORTED : PKV_EINVAL,
+                F + (kv_dtype == PKV_FP8_E4M3 ? ": 8-bit pools are read by paged_attention_verify_fp8"
+                                              : ": kv dtype must be f16 or bf16"));
+  if (q_dtype != PKV_F16 && q_dtype != PKV_BF16) return fail(PKV_EINVAL, F + ": q dtype must be f16 or bf16");
+  if (out_dtype != PKV_F32 && out_dtype != q_dtype)
+    return fail(PKV_EINVAL, F + ": out dtype must be f32 or the query's dtype");
+  if (fp8 && (!std::isfinite(k_scale) || !std::isfinite(v_scale) || !(k_scale > 0.f) || !(v_scale > 0.f)))
+    return fail(PKV_EINVAL, F + ": k_scale and v_scale must be finite and > 0");
   if (block_size != pkv::kBlockSize) return fail(PKV_EUNSUPPORTED, "block_size must be 16");
   if (head_dim != 64 && head_dim != 128) return fail(PKV_EUNSUPPORTED, "head_dim must be 64 or 128");
   if (n_kv_heads < 1 || n_q_heads < 1 || n_kv_heads > 65535 || n_q_heads % n_kv_heads)
@@ -1284,8 +1293,9 @@ extern "C" int paged_attention_verify(void* out, int32_t out_dtype, const void* 
   a.Hkv = n_kv_heads;
   a.num_blocks = num_blocks;
   a.max_context_len = max_context_len;
-  a.scale_log2 = (float)((double)scale * 1.4426950408889634);
-  a.v_mul = 1.f;
+  a.scale_log2 = (float)((double)scale * (double)k_scale * 1.4426950408889634);
+  if (!std::isfinite(a.scale_log2)) return fail(PKV_EINVAL, F + ": scale * k_scale overflows");
+  a.v_mul = v_scale;
   a.max_parts = max_parts;
   a.stream = (hipStream_t)stream;
   a.cu_q = cu_q_lens;
@@ -1293,15 +1303,52 @@ extern "C" int paged_attention_verify(void* out, int32_t out_dtype, const void* 
   a.max_q_len = max_q_len;
   using pkv::dispatch_d;
   using pkv::Verify;
+  using pkv::VerifyFp8;
   int rc;
-  if (kv_dtype == PKV_BF16)
-    rc = out_dtype == PKV_F32 ? dispatch_d<Verify, pkv::BF16, PKV_F32>(a, head_dim, G, true, true)
-                              : dispatch_d<Verify, pkv::BF16, PKV_BF16>(a, head_dim, G, true, true);
-  else
-    rc = out_dtype == PKV_F32 ? dispatch_d<Verify, pkv::F16, PKV_F32>(a, head_dim, G, true, true)
-                              : dispatch_d<Verify, pkv::F16, PKV_F16>(a, head_dim, G, true, true);
+  const bool f32o = out_dtype == PKV_F32;
+  if (fp8) {
+    if (q_dtype == PKV_BF16)
+      rc = f32o ? dispatch_d<VerifyFp8, pkv::BF16, PKV_F32>(a, head_dim, G, true, true)
+                : dispatch_d<VerifyFp8, pkv::BF16, PKV_BF16>(a, head_dim, G, true, true);
+    else
+      rc = f32o ? dispatch_d<VerifyFp8, pkv::F16, PKV_F32>(a, head_dim, G, true, true)
+                : dispatch_d<VerifyFp8, pkv::F16, PKV_F16>(a, head_dim, G, true, true);
+  } else if (kv_dtype == PKV_BF16) {
+    rc = f32o ? dispatch_d<Verify, pkv::BF16, PKV_F32>(a, head_dim, G, true, true)
+              : dispatch_d<Verify, pkv::BF16, PKV_BF16>(a, head_dim, G, true, true);
+  } else {
+    rc = f32o ? dispatch_d<Verify, pkv::F16, PKV_F32>(a, head_dim, G, true, true)
+              : dispatch_d<Verify, pkv::F16, PKV_F16>(a, head_dim, G, true, true);
+  }
   if (rc) return fail(PKV_EUNSUPPORTED, F + ": configuration not built");
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(PKV_EHIP, F + ": " + hipGetErrorString(e));
   return ok();
+}
+
+extern "C" int paged_attention_verify(void* out, int32_t out_dtype, const void* q, const void* k_pool,
+                                      const void* v_pool, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                      const int32_t* cu_q_lens, const int32_t* context_lens, int32_t n_seqs,
+                                      int32_t total_q, int32_t max_q_len, int32_t n_q_heads, int32_t n_kv_heads,
+                                      int32_t head_dim, int32_t block_size, int64_t num_blocks,
+                                      int32_t max_context_len, float scale, int32_t kv_dtype, void* workspace,
+                                      int64_t workspace_bytes, void* stream) {
+  return verify_impl("paged_attention_verify", false, out, out_dtype, q, kv_dtype, k_pool, v_pool, 1.f, 1.f,
+                     block_tables, max_blocks_per_seq, cu_q_lens, context_lens, n_seqs, total_q, max_q_len, n_q_heads,
+                     n_kv_heads, head_dim, block_size, num_blocks, max_context_len, scale, kv_dtype, workspace,
+                     workspace_bytes, stream);
+}
+
+extern "C" int paged_attention_verify_fp8(void* out, int32_t out_dtype, const void* q, int32_t q_dtype,
+                                          const void* k_pool, const void* v_pool, float k_scale, float v_scale,
+                                          const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                          const int32_t* cu_q_lens, const int32_t* context_lens, int32_t n_seqs,
+                                          int32_t total_q, int32_t max_q_len, int32_t n_q_heads, int32_t n_kv_heads,
+                                          int32_t head_dim, int32_t block_size, int64_t num_blocks,
+                                          int32_t max_context_len, float scale, void* workspace,
+                                          int64_t workspace_bytes, void* stream) {
+  return verify_impl("paged_attention_verify_fp8", true, out, out_dtype, q, q_dtype, k_pool, v_pool, k_scale,
+                     v_scale, block_tables, max_blocks_per_seq, cu_q_lens, context_lens, n_seqs, total_q, max_q_len,
+                     n_q_heads, n_kv_heads, head_dim, block_size, num_blocks, max_context_len, scale, PKV_FP8_E4M3,
+                     workspace, workspace_bytes, stream);
 }

@@ -85,3 +85,14 @@ def decode_reference_fp8(w, s, k_scale=FP8_K_SCALE, v_scale=FP8_V_SCALE):
     out, ws = oracle.attention(oracle.decode(w.dtype, q), [L - 1], k, v, w.scale)
     assert np.all(np.abs(ws - 1) < 1e-9)
     return out[0]
+
+
+def prefill_reference_fp8(w, c, rows=None, k_scale=FP8_K_SCALE, v_scale=FP8_V_SCALE, n_threads=8):
+    """Oracle output [len(rows), Hq, d] for chunk c over an 8-bit cache."""
+    ctx, ql = int(w.chunk_ctx[c]), int(w.chunk_qlen[c])
+    rows = np.arange(ql) if rows is None else np.asarray(rows)
+    last = int(rows.max()) + 1
+    k, v = quantised_kv(w, "chunk", c, 0, ctx + last, k_scale, v_scale)
+    qb = w.q("chunk", c, ctx, ctx + ql)[rows]
+    out, _ = oracle.attention(oracle.decode(w.dtype, qb), ctx + rows, k, v, w.scale, n_threads=n_threads)
+    return out

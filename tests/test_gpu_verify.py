@@ -98,3 +98,29 @@ def test_verify_rejects_long_chunks_and_bad_workspace():
         pkv.paged_attention_verify(out, p.q, b.k_pool, b.v_pool, p.tables, p.cu_q_lens, p.lens_dev, 64,
                                    p.max_context_len, 2, w.num_blocks, w.scale)
     assert e.value.code == pkv.PKV_EINVAL
+
+
+FP8_CASES = [
+    ("llama3_fp8", 32, 8, 128, "bf16", [0, 17, 507, 508, 1020, 3000], [5, 8, 5, 5, 8, 3]),
+    ("gqa16_fp8_f16", 32, 2, 64, "f16", [600, 5], [5, 2]),
+    ("mha_fp8", 8, 8, 128, "f16", [300], [40]),
+]
+
+
+@pytest.mark.parametrize("name,Hq,Hkv,d,dtype,ctx,ql", FP8_CASES, ids=[c[0] for c in FP8_CASES])
+def test_verify_over_an_8bit_cache(name, Hq, Hkv, d, dtype, ctx, ql):
+    from paged_kv_cache_gather_amd.batch import DeviceBatch
+    from tests.helpers import FP8_K_SCALE, FP8_V_SCALE, prefill_reference_fp8
+    w = synth.custom_workload(name, Hq, Hkv, d, dtype, 2048, seed=37, chunk_ctx=ctx, chunk_qlen=ql)
+    print(f"verify fp8 {name}", flush=True)
+    b = DeviceBatch(w, DEV, fill="host", out_dtype="f32", kv_cache="fp8_e4m3", k_scale=FP8_K_SCALE,
+                    v_scale=FP8_V_SCALE)
+    b.append_prefill()
+    out = b.new_prefill_out()
+    b.attend_verify(out)
+    torch.cuda.synchronize()
+    atol, rtol = tolerance(dtype, "f32")
+    got = out.double().cpu().numpy()
+    cu = np.concatenate([[0], np.cumsum(w.chunk_qlen)])
+    for c in range(w.n_chunks):
+        assert_close(f"{name} seq {c}", got[cu[c]:cu[c + 1]], prefill_reference_fp8(w, c), atol, rtol)
