@@ -66,12 +66,16 @@ namespace {
 #ifndef PKV_SHARED_PARTS
 #define PKV_SHARED_PARTS 2
 #endif
+#ifndef PKV_SHARED_WAVES
+#define PKV_SHARED_WAVES 4
+#endif
 #ifndef PKV_FP8_PARTS
 #define PKV_FP8_PARTS 2
 #endif
 #ifndef PKV_VERIFY_PARTS
 #define PKV_VERIFY_PARTS 2
 #endif
+
 constexpr int kPart = PKV_DECODE_PART;  // context tokens per partition
 constexpr int kThreads = 256;           // threads per workgroup
 constexpr int kWaves = kThreads / 64;
@@ -400,11 +404,11 @@ __device__ __forceinline__ float rows4_sum(float x) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
-template <int D, int ROWS>
+template <int D, int ROWS, int NW = kWaves>
 struct RunLds {
-  float o[kWaves][ROWS][D + 4];  // the waves' unnormalised outputs (rows padded: LDS banks)
-  float ml[kWaves][ROWS][2];  // and (max, sum) per row
-  float wgt[ROWS][kWaves];    // merge weights 2^(m_w - M) per row
+  float o[NW][ROWS][D + 4];  // the waves' unnormalised outputs (rows padded: LDS banks)
+  float ml[NW][ROWS][2];     // and (max, sum) per row
+  float wgt[ROWS][NW];       // merge weights 2^(m_w - M) per row
   float row_m[ROWS], row_l[ROWS];
   int row_parts[ROWS];        // partitions of the row's sequence
   int32_t blk[kPartBlocks];   // the partition's block ids
@@ -478,8 +482,8 @@ struct TokenRows {
 //  * O^T += V^T P^T with V loaded into operand layout and widened to fp16;
 //    the waves' (max, sum, o) are merged through LDS and written as each
 //    member's partition result (8-bit values: times v_mul, the pool scale).
-template <typename KV, typename QT, int D, int G, int RT, bool Masked, int OutCode, int NH, typename Rows>
-__device__ __forceinline__ void mfma_partition(const Rows& R, int n, int g, int p, RunLds<D, 16 * RT>& sh,
+template <typename KV, typename QT, int D, int G, int RT, bool Masked, int OutCode, int NH, int NW, typename Rows>
+__device__ __forceinline__ void mfma_partition(const Rows& R, int n, int g, int p, RunLds<D, 16 * RT, NW>& sh,
                                                void* __restrict__ out, float* __restrict__ ws_o,
                                                float* __restrict__ ws_ml, const typename QT::bits* __restrict__ q,
                                                const unsigned char* __restrict__ kpool,
@@ -488,6 +492,13 @@ __device__ __forceinline__ void mfma_partition(const Rows& R, int n, int g, int 
                                                int64_t num_blocks, float scale_log2, float v_mul, int max_parts) {
   constexpr bool F8 = KV::kBytes == 1;
   constexpr bool kCausal = Rows::kCausal;
+  // key order of the score tiles: 16-bit K/V take each block's tokens in
+  // order (a K operand instruction reads 1 KiB contiguous; a lane's eight
+  // keys are four of each block of a pair, two 8-byte V pieces); 8-bit K/V
+  // keep the paired order (a lane's eight keys are one 8-byte V piece, where
+  // natural order would need 4-byte pieces and twice the V instructions)
+  static_assert(KV::kBytes != 4, "fp32 K/V have no MFMA path");
+  constexpr bool kNatural = !F8;
   static_assert(F8 || (KV::kBytes == 2 && KV::kCode == QT::kCode), "16-bit K/V take queries of their type");
   static_assert(Masked || !kCausal, "causal rows need the masked path");
   constexpr int DC = D / 32;                         // 32-dim slices of the score contraction
@@ -496,7 +507,7 @@ __device__ __forceinline__ void mfma_partition(const Rows& R, int n, int g, int 
   constexpr int KC = F8 ? D / 64 : DC;               // K chunks per lane and score tile
   constexpr int VROW = kBlockSize * KV::kBytes;      // bytes of one dim of a V tile
   constexpr int TILE = D * VROW;                     // bytes of one (block, head) tile
-  constexpr int WB = kPartBlocks / kWaves;           // blocks per wave
+  constexpr int WB = kPartBlocks / NW;               // blocks per wave (NW waves of 64 lanes)
   constexpr int HB = WB / NH;                        // blocks per part of a wave
   static_assert(HB % 2 == 0 && HB * NH == WB, "wave parts take whole block pairs");
   using vraw_t = typename std::conditional<F8, uint64_t, u32x4>::type;
@@ -538,9 +549,6 @@ __device__ __forceinline__ void mfma_partition(const Rows& R, int n, int g, int 
     for (int dt = 0; dt < DT; ++dt) o[rt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   if (!Masked || wbase < n) {  // uniform per wave
-    // this lane's K row inside a block pair for score tile `sub`
-    const int k_half = r16 >> 3;                          // which block of the pair
-    const int k_tok = 8 * ((r16 >> 2) & 1) + (r16 & 3);  // token, + 4 sub
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
       m[rt] = -INFINITY;
@@ -553,17 +561,36 @@ __device__ __forceinline__ void mfma_partition(const Rows& R, int n, int g, int 
       const int hb = h * HB;                      // the part's first block (wave-local)
       const int hbase = wbase + hb * kBlockSize;  // and token (partition-local)
       if (Masked && hbase >= n) break;            // uniform
-      u32x4 ka[HB][KC];  // tile 2 kp + sub
+      // K operands: score tile kt, row m
+      u32x4 ka[HB][KC];
+      if constexpr (kNatural) {
+        // tile kt = block hb + kt, row m = its token m: an instruction reads
+        // 4 chunks x 16 tokens = 1 KiB contiguous
 #pragma unroll
-      for (int kp = 0; kp < HB / 2; ++kp) {
-        const bool in = !Masked || hbase + (2 * kp + k_half) * kBlockSize < n;
-        const int64_t kb = clamp_block(tab[hb + 2 * kp + k_half], num_blocks);
-        const unsigned char* kr = kpool + ((kb * Hkv + g) * CH + q4) * (kBlockSize * 16) + k_tok * 16;
-#pragma unroll
-        for (int sub = 0; sub < 2; ++sub)
+        for (int kt = 0; kt < HB; ++kt) {
+          const bool in = !Masked || hbase + kt * kBlockSize < n;
+          const int64_t kb = clamp_block(tab[hb + kt], num_blocks);
+          const unsigned char* kr = kpool + ((kb * Hkv + g) * CH + q4) * (kBlockSize * 16) + r16 * 16;
 #pragma unroll
           for (int c = 0; c < KC; ++c)
-            ka[2 * kp + sub][c] = in ? ld16(kr + (4 * sub + c * 4 * kBlockSize) * 16) : u32x4{0u, 0u, 0u, 0u};
+            ka[kt][c] = in ? ld16(kr + c * 4 * kBlockSize * 16) : u32x4{0u, 0u, 0u, 0u};
+        }
+      } else {
+        // tile 2 kp + sub of block pair kp, row m = 4a + r = the pair's key
+        // 8a + 4 sub + r (lane group a owns keys 8a .. 8a + 7)
+        const int k_half = r16 >> 3;                          // which block of the pair
+        const int k_tok = 8 * ((r16 >> 2) & 1) + (r16 & 3);  // token, + 4 sub
+#pragma unroll
+        for (int kp = 0; kp < HB / 2; ++kp) {
+          const bool in = !Masked || hbase + (2 * kp + k_half) * kBlockSize < n;
+          const int64_t kb = clamp_block(tab[hb + 2 * kp + k_half], num_blocks);
+          const unsigned char* kr = kpool + ((kb * Hkv + g) * CH + q4) * (kBlockSize * 16) + k_tok * 16;
+#pragma unroll
+          for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+            for (int c = 0; c < KC; ++c)
+              ka[2 * kp + sub][c] = in ? ld16(kr + (4 * sub + c * 4 * kBlockSize) * 16) : u32x4{0u, 0u, 0u, 0u};
+        }
       }
       f32x4 st[HB][RT];
       if constexpr (F8) {
@@ -590,21 +617,38 @@ __device__ __forceinline__ void mfma_partition(const Rows& R, int n, int g, int 
             st[kt][rt] = acc;
           }
       }
-      // the V operand loads are issued next, ahead of the softmax: lane (q4,
-      // r16) takes dim 16 dt + r16, keys 8 q4 .. 8 q4 + 7 of the pair (half
-      // of the dim's row in block q4 / 2)
+      // V operands, issued next, ahead of the softmax: lane (q4, r16) takes
+      // dim 16 dt + r16 and the eight keys its probabilities cover — natural
+      // order: keys 4 q4 .. 4 q4 + 3 of both blocks of the pair (two 8-byte
+      // pieces of the dim's rows); paired order: keys 8 q4 .. 8 q4 + 7 of the
+      // pair (one piece of block q4 / 2's row)
       vraw_t vraw[HB / 2][DT];
 #pragma unroll
       for (int kp = 0; kp < HB / 2; ++kp) {
-        const bool in = !Masked || hbase + (2 * kp + (q4 >> 1)) * kBlockSize < n;
-        const int64_t vb = clamp_block(tab[hb + 2 * kp + (q4 >> 1)], num_blocks);
-        const unsigned char* vr = vpool + (vb * Hkv + g) * (int64_t)TILE + r16 * VROW + (q4 & 1) * (VROW / 2);
+        if constexpr (kNatural) {
+          const bool inA = !Masked || hbase + 2 * kp * kBlockSize < n;
+          const bool inB = !Masked || hbase + (2 * kp + 1) * kBlockSize < n;
+          const int64_t vbA = clamp_block(tab[hb + 2 * kp], num_blocks);
+          const int64_t vbB = clamp_block(tab[hb + 2 * kp + 1], num_blocks);
+          const unsigned char* vrA = vpool + (vbA * Hkv + g) * (int64_t)TILE + r16 * VROW + q4 * (VROW / 4);
+          const unsigned char* vrB = vpool + (vbB * Hkv + g) * (int64_t)TILE + r16 * VROW + q4 * (VROW / 4);
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-          if constexpr (F8)
-            vraw[kp][dt] = in ? ld8(vr + dt * 16 * VROW) : 0ull;
-          else
-            vraw[kp][dt] = ld16(vr + dt * 16 * VROW);
+          for (int dt = 0; dt < DT; ++dt) {
+            const uint64_t a = inA ? ld8(vrA + dt * 16 * VROW) : 0ull;
+            const uint64_t b = inB ? ld8(vrB + dt * 16 * VROW) : 0ull;
+            vraw[kp][dt] = u32x4{(uint32_t)a, (uint32_t)(a >> 32), (uint32_t)b, (uint32_t)(b >> 32)};
+          }
+        } else {
+          const bool in = !Masked || hbase + (2 * kp + (q4 >> 1)) * kBlockSize < n;
+          const int64_t vb = clamp_block(tab[hb + 2 * kp + (q4 >> 1)], num_blocks);
+          const unsigned char* vr = vpool + (vb * Hkv + g) * (int64_t)TILE + r16 * VROW + (q4 & 1) * (VROW / 2);
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt) {
+            if constexpr (F8)
+              vraw[kp][dt] = in ? ld8(vr + dt * 16 * VROW) : 0ull;
+            else
+              vraw[kp][dt] = ld16(vr + dt * 16 * VROW);
+          }
         }
       }
       // exact softmax over the wave's keys, per row (running over the parts)
@@ -618,7 +662,8 @@ __device__ __forceinline__ void mfma_partition(const Rows& R, int n, int g, int 
           for (int r = 0; r < 4; ++r) {
             float x = st[kt][rt][r] * scale_log2;
             if constexpr (Masked) {  // keys past the context may hold anything
-              const int key = hbase + (kt >> 1) * 2 * kBlockSize + 8 * q4 + 4 * (kt & 1) + r;
+              const int key = kNatural ? hbase + kt * kBlockSize + 4 * q4 + r
+                                       : hbase + (kt >> 1) * 2 * kBlockSize + 8 * q4 + 4 * (kt & 1) + r;
               x = key < (kCausal ? klim[rt] : n) ? x : -INFINITY;
             }
             st[kt][rt][r] = x;
@@ -643,6 +688,7 @@ __device__ __forceinline__ void mfma_partition(const Rows& R, int n, int g, int 
           }
         l[rt] += rows4_sum(ls);
         m[rt] = mnew;
+        // B operand of the pair: the lane's four keys of tile 2 kp, then of 2 kp + 1
 #pragma unroll
         for (int kp = 0; kp < HB / 2; ++kp)
           pb[kp][rt] = u32x4{pack_f16x2(st[2 * kp][rt][0], st[2 * kp][rt][1]),
@@ -650,7 +696,7 @@ __device__ __forceinline__ void mfma_partition(const Rows& R, int n, int g, int 
                              pack_f16x2(st[2 * kp + 1][rt][0], st[2 * kp + 1][rt][1]),
                              pack_f16x2(st[2 * kp + 1][rt][2], st[2 * kp + 1][rt][3])};
       }
-      // O^T += V^T P^T: lane (q4, r16) holds dim 16 dt + r16, keys 8 q4 .. 8 q4 + 7 of the pair
+      // O^T += V^T P^T over each pair's 32 keys
 #pragma unroll
       for (int kp = 0; kp < HB / 2; ++kp)
 #pragma unroll
@@ -666,11 +712,12 @@ __device__ __forceinline__ void mfma_partition(const Rows& R, int n, int g, int 
           } else {
             u32x4 vv = vraw[kp][dt];
             if constexpr (Masked) {  // zero keys past the context (they may hold NaN)
-              const int nv = n - (hbase + kp * 2 * kBlockSize + 8 * q4);
-              if (nv < 8) {
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
-                  vv[e] &= 2 * e + 1 < nv ? 0xffffffffu : (2 * e < nv ? 0x0000ffffu : 0u);
+              for (int half = 0; half < 2; ++half) {  // blocks 2 kp and 2 kp + 1
+                const int nv = n - (hbase + (2 * kp + half) * kBlockSize + 4 * q4);
+#pragma unroll
+                for (int e = 0; e < 2; ++e)
+                  vv[2 * half + e] &= 2 * e + 1 < nv ? 0xffffffffu : (2 * e < nv ? 0x0000ffffu : 0u);
               }
             }
             va = to_f16x8<KV>(vv);
@@ -703,10 +750,10 @@ __device__ __forceinline__ void mfma_partition(const Rows& R, int n, int g, int 
   if (tid < rows) {  // per row: merged max and sum, the waves' weights, the sequence's partitions
     float Mx = sh.ml[0][tid][0];
 #pragma unroll
-    for (int x = 1; x < kWaves; ++x) Mx = fmaxf(Mx, sh.ml[x][tid][0]);
+    for (int x = 1; x < NW; ++x) Mx = fmaxf(Mx, sh.ml[x][tid][0]);
     float den = 0.f;
 #pragma unroll
-    for (int x = 0; x < kWaves; ++x) {
+    for (int x = 0; x < NW; ++x) {
       // 0 for a wave with no keys (a causal row may have none in the whole partition)
       const float mw = sh.ml[x][tid][0];
       const float f = (kCausal && mw == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mw - Mx);
@@ -718,11 +765,11 @@ __device__ __forceinline__ void mfma_partition(const Rows& R, int n, int g, int 
     sh.row_parts[tid] = R.parts(tid / G);
   }
   __syncthreads();
-  for (int i = tid; i < rows * D; i += kThreads) {
+  for (int i = tid; i < rows * D; i += NW * 64) {
     const int row = i / D, j = i % D;
     float acc = 0.f;
 #pragma unroll
-    for (int x = 0; x < kWaves; ++x) acc = fmaf(sh.wgt[row][x], sh.o[x][row][j], acc);
+    for (int x = 0; x < NW; ++x) acc = fmaf(sh.wgt[row][x], sh.o[x][row][j], acc);
     if constexpr (F8) acc *= v_mul;
     const int64_t orow = R.base(row / G) * Hq + g * G + row % G;
     if (sh.row_parts[row] == 1) {
@@ -740,8 +787,9 @@ __device__ __forceinline__ void mfma_partition(const Rows& R, int n, int g, int 
 
 // Grid (KV head, run window, partition): finds the runs of the window's
 // KM = kRunRows / G sequences for partition p and serves each.
+constexpr int kSharedWaves = PKV_SHARED_WAVES;  // waves per shared-run workgroup (4 or 8)
 template <typename KV, typename QT, int D, int G, int OutCode>
-__global__ void __launch_bounds__(kThreads, 2)
+__global__ void __launch_bounds__(kSharedWaves * 64, kSharedWaves == 8 ? 1 : 2)
 decode_shared_kernel(void* __restrict__ out, float* __restrict__ ws_o, float* __restrict__ ws_ml,
                      const typename QT::bits* __restrict__ q, const unsigned char* __restrict__ kpool,
                      const unsigned char* __restrict__ vpool, const int32_t* __restrict__ tables,
@@ -752,7 +800,7 @@ decode_shared_kernel(void* __restrict__ out, float* __restrict__ ws_o, float* __
   } else {
     constexpr int KM = kRunRows / G;
     static_assert(KM <= 32, "run window fits a 32-bit mask");
-    __shared__ __attribute__((aligned(16))) RunLds<D, kRunRows> sh;
+    __shared__ __attribute__((aligned(16))) RunLds<D, kRunRows, kSharedWaves> sh;
     __shared__ uint32_t joins;
     const int g = blockIdx.x, win = blockIdx.y, p = blockIdx.z;
     const int s_first = win * KM;
@@ -777,7 +825,7 @@ decode_shared_kernel(void* __restrict__ out, float* __restrict__ ws_o, float* __
     __syncthreads();
     // full comparison of the candidates' partition block ids, one thread per
     // (member, entry): a mismatch clears the member's bit
-    for (int t = tid; t < KM * kPartBlocks; t += kThreads) {
+    for (int t = tid; t < KM * kPartBlocks; t += kSharedWaves * 64) {
       const int i = t / kPartBlocks, e = t % kPartBlocks;
       if ((cand >> i) & 1u) {
         const int a = s_first + i;
@@ -793,7 +841,7 @@ decode_shared_kernel(void* __restrict__ out, float* __restrict__ ws_o, float* __
       if (!((jm >> (s0 + 1)) & 1u) || ((jm >> s0) & 1u)) continue;
       int k = 2;
       while (s0 + k < KM && ((jm >> (s0 + k)) & 1u)) ++k;
-      mfma_partition<KV, QT, D, G, kRunRows / 16, false, OutCode, PKV_SHARED_PARTS>(
+      mfma_partition<KV, QT, D, G, kRunRows / 16, false, OutCode, PKV_SHARED_PARTS, kSharedWaves>(
           SeqRows{s_first + s0, k, lens, max_context_len}, kPart, g, p, sh, out, ws_o, ws_ml, q, kpool, vpool,
           tables, max_blocks, Hkv, num_blocks, scale_log2, v_mul, max_parts);
     }
@@ -829,7 +877,7 @@ decode_fp8_partition_kernel(void* __restrict__ out, float* __restrict__ ws_o, fl
   if (in_shared_run<FP8, G>(pr, tables, max_blocks, max_context_len, s, p, L)) return;
   const int t0 = p * kPart;
   const int n = (L - t0) < kPart ? (L - t0) : kPart;  // tokens in this partition, >= 1
-  mfma_partition<FP8, QT, D, G, 1, true, OutCode, PKV_FP8_PARTS>(SeqRows{s, 1, lens, max_context_len}, n, g, p, sh, out, ws_o,
+  mfma_partition<FP8, QT, D, G, 1, true, OutCode, PKV_FP8_PARTS, kWaves>(SeqRows{s, 1, lens, max_context_len}, n, g, p, sh, out, ws_o,
                                                   ws_ml, q, kpool, vpool, tables, max_blocks, Hkv, num_blocks,
                                                   scale_log2, v_mul, max_parts);
 }
@@ -950,7 +998,7 @@ verify_partition_kernel(void* __restrict__ out, float* __restrict__ ws_o, float*
     const int k = ql - tg * TPG < TPG ? ql - tg * TPG : TPG;
     const int pos0 = pos_first + tg * TPG;
     if (pos0 + k - 1 < t0) continue;  // no token of the group reaches this partition (uniform)
-    mfma_partition<KV, QT, D, G, kRunRows / 16, true, OutCode, PKV_VERIFY_PARTS>(
+    mfma_partition<KV, QT, D, G, kRunRows / 16, true, OutCode, PKV_VERIFY_PARTS, kWaves>(
         TokenRows{s, q0 + tg * TPG, k, pos0}, n, g, p, sh, out, ws_o, ws_ml, q, kpool, vpool, tables, max_blocks, Hkv,
         num_blocks, scale_log2, v_mul, max_parts);
   }
@@ -983,7 +1031,8 @@ template <typename KV, typename QT, int D, int G, int OutCode>
 void launch_shared(const DecodeArgs& a) {
   constexpr int KM = kRunRows / G;
   hipLaunchKernelGGL((decode_shared_kernel<KV, QT, D, G, OutCode>),
-                     dim3((unsigned)a.Hkv, (unsigned)((a.B + KM - 1) / KM), (unsigned)a.max_parts), dim3(kThreads),
+                     dim3((unsigned)a.Hkv, (unsigned)((a.B + KM - 1) / KM), (unsigned)a.max_parts),
+                     dim3(kSharedWaves * 64),
                      0, a.stream, a.out, a.ws_o, a.ws_ml, (const typename QT::bits*)a.q, a.kpool, a.vpool,
                      a.tables, a.max_blocks, a.lens, a.B, a.Hkv, a.num_blocks, a.max_context_len, a.scale_log2,
                      a.v_mul, a.max_parts);
