@@ -1,4 +1,6 @@
-// Decode attention over the paged KV cache (one query token per sequence).
+// Decode attention over the paged KV cache (one query token per sequence),
+// and verify attention (a few new query tokens per sequence) on the same
+// split-context machinery.
 //
 // What is computed: for each sequence s and query head h (KV head
 // g = h / G, G = n_q_heads / n_kv_heads), the softmax-weighted sum of the V
@@ -16,7 +18,9 @@
 // (E4M3) cache the rest is served by decode_fp8_partition_kernel instead, on
 // MFMA like the shared kernel: the codes are widened in registers, exactly,
 // and the pools' scales fold into the softmax scale (keys) and the written
-// partials (values).
+// partials (values).  Verify attention (verify_partition_kernel, further
+// below) serves a sequence's new tokens with the same MFMA routine as the
+// shared kernel (mfma_partition) and a causal limit per row.
 // decode_partition_kernel:
 //  * Work unit = (KV head g, sequence s, partition p of 512 context tokens),
 //    one 256-thread workgroup (4 wave64s).  All G query heads that share the
@@ -469,16 +473,14 @@ struct TokenRows {
 // read the same blocks for it (16 RT rows: row r = member r / G, head r % G;
 // rows past k G repeat member 0 and are not stored).  The first n tokens of
 // the partition are valid (Masked; otherwise all kPart), and with causal rows
-// member m sees keys below R.limit(m) only.  K/V of
-// the partition's blocks are read once.  Each wave takes 128 tokens (8
-// blocks) whole:
+// member m sees keys below R.limit(m) only.  K/V of the partition's blocks
+// are read once.  Each of the NW waves takes kPart / NW tokens, in NH parts
+// one after the other with a running softmax:
 //  * S^T = K Q^T on MFMA 16x16x32 with K rows loaded from the pool straight
-//    into operand layout: in each pair of blocks, row m = 4a + r of score
-//    tile `sub` is the pair's key 8a + 4 sub + r, so the lanes of group a own
-//    keys 8a..8a+7 (one V operand per dim) across the two tiles.  8-bit keys
-//    are widened to the query's type, and a lane's 16-byte K chunk (16 dims)
+//    into operand layout (key order: see kNatural below).  8-bit keys are
+//    widened to the query's type, and a lane's 16-byte K chunk (16 dims)
 //    feeds two contraction slices; the query operands take the same dims;
-//  * exact softmax over the wave's keys (base 2), probabilities in fp16;
+//  * softmax over the wave's keys (base 2), probabilities in fp16;
 //  * O^T += V^T P^T with V loaded into operand layout and widened to fp16;
 //    the waves' (max, sum, o) are merged through LDS and written as each
 //    member's partition result (8-bit values: times v_mul, the pool scale).
