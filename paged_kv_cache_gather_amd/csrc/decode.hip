@@ -933,7 +933,10 @@ decode_reduce_kernel(void* __restrict__ out, const float* __restrict__ ws_o, con
   const int h = blockIdx.x, s = blockIdx.y, lane = threadIdx.x;
   int nparts;
   if constexpr (PerToken) {
+    // clamped: a row no sequence covers (cu_q_lens breaks its contract)
+    // reads nothing beyond its own workspace row
     nparts = tok_parts[s];
+    nparts = nparts < 0 ? 0 : (nparts > max_parts ? max_parts : nparts);
   } else {
     int L = lens[s];
     L = L < 0 ? 0 : (L > max_context_len ? max_context_len : L);
@@ -942,17 +945,48 @@ decode_reduce_kernel(void* __restrict__ out, const float* __restrict__ ws_o, con
   if (nparts <= 1) return;
   const int64_t row = (int64_t)s * Hq + h;
   const float* ml = ws_ml + row * max_parts * 2;
+  const float* ob = ws_o + row * max_parts * D + lane * DPL;
+  // The partials of PB partitions are loaded together (indexes clamped to
+  // the last partition, so every load is in bounds and none waits on
+  // another); the arithmetic is the plain two passes, partitions in order.
+  constexpr int PB = 8;
+  float mp[PB], lp[PB], op[PB][DPL];
+  auto load = [&](int p0, bool with_o) {
+#pragma unroll
+    for (int j = 0; j < PB; ++j) {
+      const int p = p0 + j < nparts ? p0 + j : nparts - 1;
+      mp[j] = ml[2 * p];
+      lp[j] = ml[2 * p + 1];
+      if (with_o)
+#pragma unroll
+        for (int dd = 0; dd < DPL; ++dd) op[j][dd] = ob[(int64_t)p * D + dd];
+    }
+  };
+  load(0, true);
   float M = -INFINITY;
-  for (int p = 0; p < nparts; ++p) M = fmaxf(M, ml[2 * p]);
+#pragma unroll
+  for (int j = 0; j < PB; ++j)
+    if (j < nparts) M = fmaxf(M, mp[j]);
+  for (int p0 = PB; p0 < nparts; p0 += PB) {  // more than PB partitions: the maxima first
+    load(p0, false);
+#pragma unroll
+    for (int j = 0; j < PB; ++j)
+      if (p0 + j < nparts) M = fmaxf(M, mp[j]);
+  }
+  if (nparts > PB) load(0, true);
   float den = 0.f, acc[DPL];
 #pragma unroll
   for (int dd = 0; dd < DPL; ++dd) acc[dd] = 0.f;
-  for (int p = 0; p < nparts; ++p) {
-    const float wgt = __builtin_amdgcn_exp2f(ml[2 * p] - M);
-    den = fmaf(wgt, ml[2 * p + 1], den);
-    const float* op = ws_o + (row * max_parts + p) * D + lane * DPL;
+  for (int p0 = 0; p0 < nparts; p0 += PB) {
+    if (p0 > 0) load(p0, true);
 #pragma unroll
-    for (int dd = 0; dd < DPL; ++dd) acc[dd] = fmaf(wgt, op[dd], acc[dd]);
+    for (int j = 0; j < PB; ++j) {
+      if (p0 + j >= nparts) break;
+      const float wgt = __builtin_amdgcn_exp2f(mp[j] - M);
+      den = fmaf(wgt, lp[j], den);
+#pragma unroll
+      for (int dd = 0; dd < DPL; ++dd) acc[dd] = fmaf(wgt, op[j][dd], acc[dd]);
+    }
   }
 #pragma unroll
   for (int dd = 0; dd < DPL; ++dd) store_out<OutCode>(out, row * D + lane * DPL + dd, acc[dd] / den);
