@@ -63,6 +63,22 @@ def test_decode_small(name, Hq, Hkv, d, dtype, lens, out_kind):
     _check_all(w, out, out_dtype)
 
 
+def test_decode_long_contexts():
+    # 9 to 33 partitions of 512 tokens: the split-context merge takes its
+    # partials in batches of 8, so counts on both sides of 8, 16 and 32
+    lens = [4097, 4608, 8192, 8193, 12000, 16500]
+    w = synth.custom_workload("llama3_long", 32, 8, 128, "bf16", 4096, seed=6, decode_lens=lens)
+    for out_dtype in ("f32", "bf16"):
+        print(f"decode llama3_long out={out_dtype}", flush=True)
+        _, out = _run_decode(w, out_dtype, fill="device")
+        _check_all(w, out, out_dtype)
+    w = synth.custom_workload("long_shared", 32, 8, 128, "bf16", 4096, seed=7, decode_lens=[9000, 9000, 5000],
+                              prefix_len=[8800, 8800, 0], prefix_group=[0, 0, -1])
+    print("decode long_shared", flush=True)
+    _, out = _run_decode(w, "f32", fill="device")
+    _check_all(w, out, "f32")
+
+
 def test_decode_shared_prefix_with_copy_on_write():
     # groups of 4 sharing prefixes whose last block is partly filled, so the
     # first private append of each member copies that block

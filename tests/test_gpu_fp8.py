@@ -142,6 +142,7 @@ FP8_DECODE = [
     ("gqa8_d64", 32, 4, 64, "bf16", [100, 900, 1024]),
     ("gqa16_d64", 32, 2, 64, "bf16", [100, 900]),
     ("gqa16_d128", 16, 1, 128, "f16", [1000, 513, 64]),
+    ("long_contexts", 32, 8, 128, "bf16", [4609, 8192, 9001]),
 ]
 
 

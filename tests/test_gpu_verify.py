@@ -47,6 +47,8 @@ CASES = [
     ("gqa2_d64", 8, 4, 64, "f16", [0, 700, 1023], [16, 17, 2]),
     ("gqa8_d64", 32, 4, 64, "bf16", [513, 3, 1500], [4, 9, 5]),
     ("gqa16_d128", 32, 2, 128, "f16", [1000, 10, 509], [5, 2, 7]),
+    # rows over 8 to 18 partitions (the merge takes partials in batches of 8)
+    ("long_contexts", 32, 8, 128, "bf16", [4090, 8190, 9000], [8, 5, 3]),
 ]
 
 
