@@ -76,6 +76,10 @@ namespace {
 #ifndef PKV_FP8_PARTS
 #define PKV_FP8_PARTS 2
 #endif
+// workgroups that share a run window's runs
+#ifndef PKV_RUN_SLOTS
+#define PKV_RUN_SLOTS 2
+#endif
 #ifndef PKV_VERIFY_PARTS
 #define PKV_VERIFY_PARTS 2
 #endif
@@ -787,9 +791,14 @@ __device__ __forceinline__ void mfma_partition(const Rows& R, int n, int g, int 
   __syncthreads();  // the LDS is reused by the window's next run
 }
 
-// Grid (KV head, run window, partition): finds the runs of the window's
-// KM = kRunRows / G sequences for partition p and serves each.
+// Grid (KV head, run window, slot).  The workgroups of a window find its
+// runs for every partition the same way and deal them out: the window's
+// candidate runs, counted over its partitions in order, go round-robin to the
+// kRunSlots slots, so that runs of one window (and partitions) are served side
+// by side instead of one after another.
 constexpr int kSharedWaves = PKV_SHARED_WAVES;  // waves per shared-run workgroup (4 or 8)
+constexpr int kRunSlots = PKV_RUN_SLOTS;        // workgroups per run window
+constexpr int kProbeParts = 64;                 // partitions probed per round
 template <typename KV, typename QT, int D, int G, int OutCode>
 __global__ void __launch_bounds__(kSharedWaves * 64, kSharedWaves == 8 ? 1 : 2)
 decode_shared_kernel(void* __restrict__ out, float* __restrict__ ws_o, float* __restrict__ ws_ml,
@@ -802,50 +811,71 @@ decode_shared_kernel(void* __restrict__ out, float* __restrict__ ws_o, float* __
   } else {
     constexpr int KM = kRunRows / G;
     static_assert(KM <= 32, "run window fits a 32-bit mask");
+    constexpr int kThr = kSharedWaves * 64;
     __shared__ __attribute__((aligned(16))) RunLds<D, kRunRows, kSharedWaves> sh;
+    __shared__ uint32_t cmask[kProbeParts];  // per partition: bit i = member i may join member i - 1
     __shared__ uint32_t joins;
-    const int g = blockIdx.x, win = blockIdx.y, p = blockIdx.z;
+    const int g = blockIdx.x, win = blockIdx.y, slot = blockIdx.z;
     const int s_first = win * KM;
     if (s_first >= B) return;
-    const int tid = threadIdx.x, lane = tid & 63;
-    // candidates, one lane per member: both fill p and their first block ids
-    // for p agree (one round of loads); then the full comparison for those
-    uint32_t cand = 0;
-    {
-      const int i = lane, a = s_first + i;
-      bool c = false;
-      if (i >= 1 && i < KM && a < B) {
-        const int need = (p + 1) * kPart;
-        c = clamp_len(lens[a - 1], max_context_len) >= need && clamp_len(lens[a], max_context_len) >= need &&
-            tables[(int64_t)(a - 1) * max_blocks + p * kPartBlocks] ==
-                tables[(int64_t)a * max_blocks + p * kPartBlocks];
+    const int tid = threadIdx.x;
+    int unit = 0;  // candidate runs of the window so far, in (partition, member) order
+    for (int pc = 0; pc < max_parts; pc += kProbeParts) {
+      const int np = max_parts - pc < kProbeParts ? max_parts - pc : kProbeParts;
+      // candidates, one thread per (partition, member): both fill the
+      // partition and their first block ids for it agree (one round of loads;
+      // every load is in bounds, so none waits on another)
+      if (tid < kProbeParts) cmask[tid] = 0u;
+      __syncthreads();
+      for (int t = tid; t < np * KM; t += kThr) {
+        const int pp = t / KM, i = t % KM, a = s_first + i, p = pc + pp;
+        if (i >= 1 && a < B) {
+          const int need = (p + 1) * kPart;
+          const int La = lens[a - 1], Lb = lens[a];
+          const int32_t ia = tables[(int64_t)(a - 1) * max_blocks + p * kPartBlocks];
+          const int32_t ib = tables[(int64_t)a * max_blocks + p * kPartBlocks];
+          if (clamp_len(La, max_context_len) >= need && clamp_len(Lb, max_context_len) >= need && ia == ib)
+            atomicOr(&cmask[pp], 1u << i);
+        }
       }
-      cand = (uint32_t)__ballot(c);
-    }
-    if (cand == 0) return;  // uniform: every wave computed the same mask
-    if (tid == 0) joins = cand;
-    __syncthreads();
-    // full comparison of the candidates' partition block ids, one thread per
-    // (member, entry): a mismatch clears the member's bit
-    for (int t = tid; t < KM * kPartBlocks; t += kSharedWaves * 64) {
-      const int i = t / kPartBlocks, e = t % kPartBlocks;
-      if ((cand >> i) & 1u) {
-        const int a = s_first + i;
-        if (tables[(int64_t)(a - 1) * max_blocks + p * kPartBlocks + e] !=
-            tables[(int64_t)a * max_blocks + p * kPartBlocks + e])
-          atomicAnd(&joins, ~(1u << i));
+      __syncthreads();
+      for (int pp = 0; pp < np; ++pp) {
+        const uint32_t cm = cmask[pp];  // uniform
+        if (cm == 0u) continue;
+        const int p = pc + pp;
+        // candidate runs: a member without its bit, then the members with it
+        for (int c0 = 0; c0 + 1 < KM; ++c0) {
+          if (!((cm >> (c0 + 1)) & 1u) || ((cm >> c0) & 1u)) continue;
+          int kc = 2;
+          while (c0 + kc < KM && ((cm >> (c0 + kc)) & 1u)) ++kc;
+          if (unit++ % kRunSlots != slot) continue;
+          // full comparison of the candidate run's block ids for p, one
+          // thread per (member, entry): a mismatch clears the member's bit
+          if (tid == 0) joins = cm;
+          __syncthreads();
+          for (int t = tid; t < (kc - 1) * kPartBlocks; t += kThr) {
+            const int i = c0 + 1 + t / kPartBlocks, e = t % kPartBlocks;
+            const int a = s_first + i;
+            if (tables[(int64_t)(a - 1) * max_blocks + p * kPartBlocks + e] !=
+                tables[(int64_t)a * max_blocks + p * kPartBlocks + e])
+              atomicAnd(&joins, ~(1u << i));
+          }
+          __syncthreads();
+          const uint32_t jm = joins;
+          __syncthreads();  // joins is rewritten by the next candidate run
+          // the runs inside it: a member that does not join its predecessor,
+          // then those that do
+          for (int s0 = c0; s0 + 1 < c0 + kc; ++s0) {
+            if (!((jm >> (s0 + 1)) & 1u) || (s0 > c0 && ((jm >> s0) & 1u))) continue;
+            int k = 2;
+            while (s0 + k < c0 + kc && ((jm >> (s0 + k)) & 1u)) ++k;
+            mfma_partition<KV, QT, D, G, kRunRows / 16, false, OutCode, PKV_SHARED_PARTS, kSharedWaves>(
+                SeqRows{s_first + s0, k, lens, max_context_len}, kPart, g, p, sh, out, ws_o, ws_ml, q, kpool,
+                vpool, tables, max_blocks, Hkv, num_blocks, scale_log2, v_mul, max_parts);
+          }
+        }
       }
-    }
-    __syncthreads();
-    const uint32_t jm = joins;
-    // a run: a member that does not join its predecessor, then those that do
-    for (int s0 = 0; s0 + 1 < KM; ++s0) {
-      if (!((jm >> (s0 + 1)) & 1u) || ((jm >> s0) & 1u)) continue;
-      int k = 2;
-      while (s0 + k < KM && ((jm >> (s0 + k)) & 1u)) ++k;
-      mfma_partition<KV, QT, D, G, kRunRows / 16, false, OutCode, PKV_SHARED_PARTS, kSharedWaves>(
-          SeqRows{s_first + s0, k, lens, max_context_len}, kPart, g, p, sh, out, ws_o, ws_ml, q, kpool, vpool,
-          tables, max_blocks, Hkv, num_blocks, scale_log2, v_mul, max_parts);
+      __syncthreads();  // cmask is rewritten by the next round
     }
   }
 }
@@ -1067,7 +1097,7 @@ template <typename KV, typename QT, int D, int G, int OutCode>
 void launch_shared(const DecodeArgs& a) {
   constexpr int KM = kRunRows / G;
   hipLaunchKernelGGL((decode_shared_kernel<KV, QT, D, G, OutCode>),
-                     dim3((unsigned)a.Hkv, (unsigned)((a.B + KM - 1) / KM), (unsigned)a.max_parts),
+                     dim3((unsigned)a.Hkv, (unsigned)((a.B + KM - 1) / KM), (unsigned)kRunSlots),
                      dim3(kSharedWaves * 64),
                      0, a.stream, a.out, a.ws_o, a.ws_ml, (const typename QT::bits*)a.q, a.kpool, a.vpool,
                      a.tables, a.max_blocks, a.lens, a.B, a.Hkv, a.num_blocks, a.max_context_len, a.scale_log2,
