@@ -340,15 +340,16 @@ prefill_chunk_kernel(void* __restrict__ out, const uint16_t* __restrict__ q,
   // ---- the three compute phases of a 64-key step ----------------------------
   f32x4 st[RT][4];  // S^T tiles: st[rt][kt] holds, for row r16, keys 32(kt/2) + key_base[kt%2] + r
   u32x4 pb[RT][2];  // fp16 probabilities as B operands of O^T += V^T P^T, per 32-key half
-  // All K operand reads are issued before the MFMAs (one LDS latency per
-  // phase); the MFMAs run dim-slice outermost so 4 x RT accumulation chains
-  // are in flight.
+  // The K operand reads go in dim-slice order, four (one per key tile) ahead
+  // of the 4 x RT MFMAs that use them, so the LDS reads of later slices
+  // overlap the products of earlier ones; the MFMAs run dim-slice outermost
+  // so 4 x RT accumulation chains are in flight.
   auto phase_qk = [&](const unsigned char* kl) {
     u32x4 ka[4][DC];
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt)
+    for (int dc = 0; dc < DC; ++dc)
 #pragma unroll
-      for (int dc = 0; dc < DC; ++dc)
+      for (int kt = 0; kt < 4; ++kt)
         ka[kt][dc] = *reinterpret_cast<const u32x4*>(kl + (kt >> 1) * 2 * TILE + k_row_off[kt & 1] +
                                                      dc * 4 * kBlockSize * 16);
 #pragma unroll
@@ -361,8 +362,11 @@ prefill_chunk_kernel(void* __restrict__ out, const uint16_t* __restrict__ q,
       for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) st[rt][kt] = mfma_qk<T>(ka[kt][dc], bq[rt][dc], st[rt][kt]);
-    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 4 * DC, 0);
-    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 4 * DC * RT, 0);
+#pragma unroll
+    for (int dc = 0; dc < DC; ++dc) {
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 4, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 4 * RT, 0);
+    }
   };
   // Online softmax, one row per lane; kDiag: the step reaches the causal
   // diagonal (or the end of the context) and needs the mask.  The reference
@@ -411,7 +415,10 @@ prefill_chunk_kernel(void* __restrict__ out, const uint16_t* __restrict__ q,
       }
     }
   };
-  // O^T += V^T P^T, and the row sums as ones . P^T; all V operand reads first.
+  // O^T += V^T P^T, and the row sums as ones . P^T.  Per 32-key half, the V
+  // operand reads go in two groups of DT / 2, the first ahead of the row-sum
+  // MFMAs (which need none), the second ahead of the first DT / 2 dim tiles'
+  // products, so LDS reads and MFMAs overlap.
   auto phase_pv = [&](const unsigned char* vl) {
     u32x4 va[2][DT];
 #pragma unroll
@@ -428,8 +435,14 @@ prefill_chunk_kernel(void* __restrict__ out, const uint16_t* __restrict__ q,
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) o[rt][dt] = mfma_pv(va[kh][dt], pb[rt][kh], o[rt][dt]);
     }
-    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2 * DT, 0);
-    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 2 * RT * (DT + 1), 0);
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh) {
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, DT / 2, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, RT, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, DT / 2, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, RT * DT / 2, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, RT * DT / 2, 0);
+    }
   };
 
   // ---- schedule ----------------------------------------------------------------
