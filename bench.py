@@ -170,17 +170,17 @@ def mixed_step(steps, warmup, seed):
 
 def host_allocator_us(b, reps=5):
     """Per-step cost of the host block manager on this batch: append one token
-    to every sequence and export the block tables (median of reps).  Run after
-    the timed steps: it advances the host state of b's pool."""
+    to every sequence (one batched call, which also returns the slot
+    mapping) and export the block tables (median of reps).  Run after the
+    timed steps: it advances the host state of b's pool."""
     import numpy as np
     import paged_kv_cache_gather_amd as pkv
-    seqs = b.decode.seqs
+    seqs = np.asarray(b.decode.seqs, dtype=np.int64)
     maxb = int(-(-(b.decode.lens.max() + reps) // 16))
     times = []
     for _ in range(reps):
         t0 = time.perf_counter()
-        for q in seqs:
-            pkv.paged_kv_seq_append(b.pool, q, 1)
+        pkv.paged_kv_seqs_append(b.pool, seqs)
         pkv.paged_kv_block_tables(b.pool, seqs, maxb)
         times.append(time.perf_counter() - t0)
     return float(np.median(times)) * 1e6

@@ -148,6 +148,30 @@ int paged_kv_seq_fork(pkv_pool* pool, int64_t parent, int64_t n_prefix_tokens, i
 int paged_kv_seq_append(pkv_pool* pool, int64_t seq, int64_t n_tokens, int64_t* slot_mapping_out,
                         int32_t* cow_pairs_out, int32_t max_cow, int32_t* n_cow);
 
+/* A step's appends in one call (the per-step host work of "The skeleton of a
+ * scheduler", LLM Serving from Scratch: every running sequence gets its next
+ * token's slot).  Sequence seqs[i] gets n_tokens[i] new tokens (one each when
+ * n_tokens is NULL), in list order, each exactly as paged_kv_seq_append would
+ * append it (new blocks from the head of the free queue, copy-on-write of a
+ * shared partly filled last block).
+ *   seqs            host int64 [n]
+ *   n_tokens        host int64 [n], >= 0, or NULL
+ *   slot_mapping_out host int64 [sum of the counts] (may be NULL): the slots
+ *                   of sequence 0's new tokens, then sequence 1's, ...
+ *   cow_pairs_out   host int32 [2 * max_cow] (src, dst) pairs in order (may
+ *                   be NULL when max_cow is 0); *n_cow receives their number
+ *   *n_done         receives the number of sequences appended.
+ * The sequences are appended one after another; the first that cannot be
+ * stops the call with its code — PKV_ENOMEM_BLOCKS (the free queue is
+ * short), PKV_ESTATE (unknown or swapped-out sequence) or PKV_EINVAL (no
+ * room left in cow_pairs_out) — with the earlier ones appended and reported
+ * (*n_done, their slots and pairs) and that one and the later ones
+ * unchanged, so the caller can preempt and call again for the rest.
+ * PKV_EINVAL before any change for a negative count or NULL list. */
+int paged_kv_seqs_append(pkv_pool* pool, const int64_t* seqs, int32_t n, const int64_t* n_tokens,
+                         int64_t* slot_mapping_out, int32_t* cow_pairs_out, int32_t max_cow, int32_t* n_cow,
+                         int32_t* n_done);
+
 /* Blocks the append of n_tokens would take from the free queue (new blocks
  * plus a copy-on-write block), without changing anything. */
 int paged_kv_seq_blocks_needed(pkv_pool* pool, int64_t seq, int64_t n_tokens, int64_t* n_blocks);

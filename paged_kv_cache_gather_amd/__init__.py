@@ -74,6 +74,7 @@ _sig("paged_kv_destroy", ctypes.c_int, _P)
 _sig("paged_kv_seq_create", ctypes.c_int, _P, _pi64)
 _sig("paged_kv_seq_fork", ctypes.c_int, _P, _i64, _i64, _pi64)
 _sig("paged_kv_seq_append", ctypes.c_int, _P, _i64, _i64, _P, _P, _i32, _pi32)
+_sig("paged_kv_seqs_append", ctypes.c_int, _P, _P, _i32, _P, _P, _P, _i32, _pi32, _pi32)
 _sig("paged_kv_seq_blocks_needed", ctypes.c_int, _P, _i64, _i64, _pi64)
 _sig("paged_kv_seq_free", ctypes.c_int, _P, _i64)
 _sig("paged_kv_seq_len", ctypes.c_int, _P, _i64, _pi64)
@@ -257,6 +258,37 @@ def paged_kv_seq_append(pool: Pool, seq: int, n_tokens: int):
     _check(_lib.paged_kv_seq_append(pool.handle, seq, n_tokens, slots.ctypes.data, cow.ctypes.data, 1,
                                     ctypes.byref(ncow)))
     return slots, [(int(cow[0]), int(cow[1]))] if ncow.value else []
+
+
+def paged_kv_seqs_append(pool: Pool, seqs, n_tokens=None):
+    """A step's appends in one call: n_tokens[i] (default one) new tokens for
+    seqs[i], in order.  Returns (slot_mapping int64 [sum of the counts], cow
+    pairs list[(src, dst)]).  If a sequence cannot be appended the error
+    raised carries n_done, slots and cow for the sequences before it, which
+    stay appended."""
+    s = np.ascontiguousarray(seqs, dtype=np.int64).reshape(-1)
+    if n_tokens is None:
+        counts, total = None, s.size
+    else:
+        counts = np.ascontiguousarray(n_tokens, dtype=np.int64).reshape(-1)
+        if counts.size != s.size:
+            raise PagedKVError(PKV_EINVAL, "n_tokens must have one count per sequence")
+        total = int(np.maximum(counts, 0).sum())
+    slots = np.empty(total, dtype=np.int64)
+    cow = np.empty(2 * max(s.size, 1), dtype=np.int32)  # at most one pair per sequence
+    ncow, ndone = _i32(), _i32()
+    rc = _lib.paged_kv_seqs_append(pool.handle, s.ctypes.data if s.size else None, s.size,
+                                   counts.ctypes.data if counts is not None else None, slots.ctypes.data,
+                                   cow.ctypes.data, s.size, ctypes.byref(ncow), ctypes.byref(ndone))
+    pairs = [(int(cow[2 * i]), int(cow[2 * i + 1])) for i in range(ncow.value)]
+    if rc != PKV_OK:
+        done = ndone.value
+        err = (OutOfBlocks if rc == PKV_ENOMEM_BLOCKS else PagedKVError)(rc, last_error())
+        err.n_done = done
+        err.slots = slots[:done if counts is None else int(counts[:done].sum())]
+        err.cow = pairs
+        raise err
+    return slots, pairs
 
 
 def paged_kv_prefix_cache_enable(pool: Pool, enable: bool = True):

@@ -18,7 +18,7 @@ import numpy as np
 import torch
 
 import synth
-from . import (paged_kv_alloc, paged_kv_seq_create, paged_kv_seq_fork, paged_kv_seq_append,
+from . import (paged_kv_alloc, paged_kv_seq_create, paged_kv_seq_fork, paged_kv_seq_append, paged_kv_seqs_append,
                paged_kv_seq_free, paged_kv_block_tables, paged_kv_copy_blocks, reshape_and_cache,
                reshape_and_cache_fp8, paged_attention_decode, paged_attention_decode_fp8,
                paged_attention_decode_fp8_partitions, paged_attention_decode_fp8_reduce,
@@ -174,13 +174,8 @@ class DeviceBatch:
             seqs[s] = seq
         for r in roots.values():
             paged_kv_seq_free(self.pool, r)
-        # this step's appended token
-        new_slots = np.empty(B, dtype=np.int64)
-        cow_all = []
-        for s in range(B):
-            sl, cow = paged_kv_seq_append(self.pool, seqs[s], 1)
-            new_slots[s] = sl[0]
-            cow_all += cow
+        # this step's appended token, one batched call for the whole batch
+        new_slots, cow_all = paged_kv_seqs_append(self.pool, seqs)
         self._cow(cow_all)
         k_new = torch.empty((B, w.n_kv_heads, w.head_dim), dtype=self.tdt, device=self.device)
         v_new = torch.empty_like(k_new)
@@ -216,14 +211,10 @@ class DeviceBatch:
                 self._write("chunk", c, 0, int(ctx[c]), slots)
             seqs.append(seq)
         total = int(qlen.sum())
-        slots_all = np.empty(total, dtype=np.int64)
         cu = np.zeros(n + 1, dtype=np.int32)
-        cow_all = []
-        for c in range(n):
-            sl, cow = paged_kv_seq_append(self.pool, seqs[c], int(qlen[c]))
-            cu[c + 1] = cu[c] + qlen[c]
-            slots_all[cu[c]:cu[c + 1]] = sl
-            cow_all += cow
+        cu[1:] = np.cumsum(qlen)
+        # the chunks' new tokens, one batched call
+        slots_all, cow_all = paged_kv_seqs_append(self.pool, seqs, qlen)
         self._cow(cow_all)
         k_new = torch.empty((total, w.n_kv_heads, w.head_dim), dtype=self.tdt, device=self.device)
         v_new = torch.empty_like(k_new)

@@ -318,23 +318,18 @@ int paged_kv_seq_blocks_needed(pkv_pool* pool, int64_t seq, int64_t n_tokens, in
   return ok();
 }
 
-static int append_impl(const char* fn, pkv_pool* pool, int64_t seq, const int32_t* tokens, int64_t n_tokens,
-                       int64_t* slot_mapping_out, int32_t* cow_pairs_out, int32_t max_cow, int32_t* n_cow) {
-  const std::string F(fn);
-  if (!pool) return fail(PKV_EINVAL, F + ": pool is NULL");
-  if (n_tokens < 0) return fail(PKV_EINVAL, F + ": n_tokens < 0");
-  if (max_cow < 0 || (max_cow > 0 && !cow_pairs_out))
-    return fail(PKV_EINVAL, F + ": cow_pairs_out is NULL with max_cow > 0");
-  std::lock_guard<std::mutex> lk(pool->mu);
-  auto it = pool->seqs.find(seq);
-  if (it == pool->seqs.end()) return fail(PKV_ESTATE, F + ": unknown sequence");
-  Sequence& s = it->second;
+// The append of n_tokens to s, the pool's lock held: all or nothing (the
+// checks come before any change).  Writes the slots, and at most one
+// copy-on-write pair if max_cow allows it; *n_cow receives 0 or 1.
+static int append_locked(const std::string& F, pkv_pool* pool, Sequence& s, const int32_t* tokens,
+                         int64_t n_tokens, int64_t* slot_mapping_out, int32_t* cow_pairs_out, int32_t max_cow,
+                         int32_t* n_cow) {
   if (s.swapped) return fail(PKV_ESTATE, F + ": sequence is swapped out");
   const int64_t bs = pool->block_size;
   const int64_t L = s.len;
   const bool cow = n_tokens > 0 && L % bs != 0 && pool->ref[s.table[L / bs]] > 1;
   if (cow && max_cow < 1)
-    return fail(PKV_EINVAL, F + ": append needs a copy-on-write pair but max_cow is 0");
+    return fail(PKV_EINVAL, F + ": the append needs a copy-on-write pair and max_cow leaves no room");
   const int64_t need = pool->need(s, n_tokens);
   if (need > pool->count)
     return fail(PKV_ENOMEM_BLOCKS, "out of KV blocks: need " + std::to_string(need) + ", free " +
@@ -363,7 +358,56 @@ static int append_impl(const char* fn, pkv_pool* pool, int64_t seq, const int32_
     s.tokens.clear();
     s.tokens.shrink_to_fit();
   }
-  if (n_cow) *n_cow = ncow;
+  *n_cow = ncow;
+  return ok();
+}
+
+static int append_impl(const char* fn, pkv_pool* pool, int64_t seq, const int32_t* tokens, int64_t n_tokens,
+                       int64_t* slot_mapping_out, int32_t* cow_pairs_out, int32_t max_cow, int32_t* n_cow) {
+  const std::string F(fn);
+  if (!pool) return fail(PKV_EINVAL, F + ": pool is NULL");
+  if (n_tokens < 0) return fail(PKV_EINVAL, F + ": n_tokens < 0");
+  if (max_cow < 0 || (max_cow > 0 && !cow_pairs_out))
+    return fail(PKV_EINVAL, F + ": cow_pairs_out is NULL with max_cow > 0");
+  std::lock_guard<std::mutex> lk(pool->mu);
+  auto it = pool->seqs.find(seq);
+  if (it == pool->seqs.end()) return fail(PKV_ESTATE, F + ": unknown sequence");
+  int32_t ncow = 0;
+  const int rc = append_locked(F, pool, it->second, tokens, n_tokens, slot_mapping_out, cow_pairs_out, max_cow,
+                               &ncow);
+  if (rc == PKV_OK && n_cow) *n_cow = ncow;
+  return rc;
+}
+
+int paged_kv_seqs_append(pkv_pool* pool, const int64_t* seqs, int32_t n, const int64_t* n_tokens,
+                         int64_t* slot_mapping_out, int32_t* cow_pairs_out, int32_t max_cow, int32_t* n_cow,
+                         int32_t* n_done) {
+  const std::string F("paged_kv_seqs_append");
+  if (n_done) *n_done = 0;
+  if (n_cow) *n_cow = 0;
+  if (!pool) return fail(PKV_EINVAL, F + ": pool is NULL");
+  if (n < 0 || (n > 0 && !seqs)) return fail(PKV_EINVAL, F + ": bad sequence list");
+  if (max_cow < 0 || (max_cow > 0 && !cow_pairs_out))
+    return fail(PKV_EINVAL, F + ": cow_pairs_out is NULL with max_cow > 0");
+  if (n_tokens)
+    for (int32_t i = 0; i < n; ++i)
+      if (n_tokens[i] < 0) return fail(PKV_EINVAL, F + ": n_tokens < 0");
+  std::lock_guard<std::mutex> lk(pool->mu);
+  int64_t off = 0;
+  int32_t ncow = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    auto it = pool->seqs.find(seqs[i]);
+    if (it == pool->seqs.end()) return fail(PKV_ESTATE, F + ": unknown sequence " + std::to_string(seqs[i]));
+    const int64_t nt = n_tokens ? n_tokens[i] : 1;
+    int32_t c = 0;
+    const int rc = append_locked(F, pool, it->second, nullptr, nt, slot_mapping_out ? slot_mapping_out + off : nullptr,
+                                 cow_pairs_out ? cow_pairs_out + 2 * ncow : nullptr, max_cow - ncow, &c);
+    if (rc != PKV_OK) return rc;  // sequences 0 .. i-1 stay appended and reported
+    off += nt;
+    ncow += c;
+    if (n_cow) *n_cow = ncow;
+    if (n_done) *n_done = i + 1;
+  }
   return ok();
 }
 

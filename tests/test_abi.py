@@ -144,6 +144,84 @@ def test_block_manager_matches_model(ops, nblocks, seed):
     assert pkv.paged_kv_num_free(p) == m.num_free()
 
 
+step_ops = st.lists(st.tuples(st.sampled_from(["create", "fork", "free", "step"]),
+                              st.integers(0, 1000), st.integers(0, 40),
+                              st.lists(st.integers(0, 20), min_size=1, max_size=8)),
+                    min_size=1, max_size=40)
+
+
+@settings(max_examples=150, deadline=None)
+@given(ops=step_ops, nblocks=st.integers(1, 40), seed=st.integers(0, 2**16))
+def test_batched_append_matches_model(ops, nblocks, seed):
+    # paged_kv_seqs_append = the per-sequence appends in list order, stopping
+    # at the first that cannot be made (the ones before it stay made)
+    order = np.random.default_rng(seed).permutation(nblocks)
+    p = pkv.paged_kv_alloc(nblocks, 1, 64, "f16", initial_free_order=order)
+    m = bm.BlockManagerModel(nblocks, 16, order)
+    live_p, live_m = [], []
+    for op, pick, n, counts in ops:
+        if op == "create" or not live_p:
+            live_p.append(pkv.paged_kv_seq_create(p))
+            live_m.append(m.create())
+            continue
+        i = pick % len(live_p)
+        if op == "fork":
+            k = pick % (m.lens[live_m[i]] + 1)
+            live_p.append(pkv.paged_kv_seq_fork(p, live_p[i], k))
+            live_m.append(m.fork(live_m[i], k))
+        elif op == "free":
+            pkv.paged_kv_seq_free(p, live_p.pop(i))
+            m.release(live_m.pop(i))
+        else:
+            idx = [(pick + 7 * j) % len(live_p) for j in range(len(counts))]
+            want_slots, want_cow, done = [], [], len(idx)
+            for j, (k, c) in enumerate(zip(idx, counts)):
+                try:
+                    sm, cm = m.append(live_m[k], c)
+                except bm.OutOfBlocks:
+                    done = j
+                    break
+                want_slots += sm
+                want_cow += cm
+            seqs = [live_p[k] for k in idx]
+            if done == len(idx):
+                sp, cp = pkv.paged_kv_seqs_append(p, seqs, counts)
+            else:
+                with pytest.raises(pkv.OutOfBlocks) as e:
+                    pkv.paged_kv_seqs_append(p, seqs, counts)
+                assert e.value.n_done == done
+                sp, cp = e.value.slots, e.value.cow
+            assert sp.tolist() == want_slots and cp == want_cow
+        _compare(p, m, live_p, live_m)
+
+
+def test_batched_append_defaults_and_errors():
+    p = pkv.paged_kv_alloc(8, 1, 64, "f16")
+    a, b = pkv.paged_kv_seq_create(p), pkv.paged_kv_seq_create(p)
+    pkv.paged_kv_seq_append(p, a, 20)
+    c = pkv.paged_kv_seq_fork(p, a, 20)  # shares a partly filled block with a
+    shared = int(pkv.paged_kv_seq_table(p, a)[1])
+    slots, cow = pkv.paged_kv_seqs_append(p, [a, b, c])  # one token each
+    assert [pkv.paged_kv_seq_len(p, x) for x in (a, b, c)] == [21, 1, 21]
+    # a copies the shared block; c, its last holder by then, writes in place
+    fresh = int(pkv.paged_kv_seq_table(p, a)[1])
+    assert cow == [(shared, fresh)] and int(pkv.paged_kv_seq_table(p, c)[1]) == shared
+    assert slots.tolist() == [fresh * 16 + 4, int(pkv.paged_kv_seq_table(p, b)[0]) * 16, shared * 16 + 4]
+    assert pkv.paged_kv_seqs_append(p, [], None)[0].size == 0
+    with pytest.raises(pkv.PagedKVError) as e:  # negative count: nothing changes
+        pkv.paged_kv_seqs_append(p, [a, b], [1, -1])
+    assert e.value.code == pkv.PKV_EINVAL and pkv.paged_kv_seq_len(p, a) == 21
+    with pytest.raises(pkv.PagedKVError) as e:  # unknown sequence part-way
+        pkv.paged_kv_seqs_append(p, [a, 12345, b], [2, 1, 1])
+    assert e.value.code == pkv.PKV_ESTATE and e.value.n_done == 1 and e.value.slots.size == 2
+    assert [pkv.paged_kv_seq_len(p, x) for x in (a, b)] == [23, 1]
+    pkv.paged_kv_swap_space(p, 8)
+    pkv.paged_kv_seq_swap_out(p, b)
+    with pytest.raises(pkv.PagedKVError) as e:  # swapped-out sequence part-way
+        pkv.paged_kv_seqs_append(p, [a, b], [1, 1])
+    assert e.value.code == pkv.PKV_ESTATE and e.value.n_done == 1
+
+
 def test_device_entry_points_validate_before_launch():
     # host-side validation returns codes without touching a GPU
     lib = ctypes.CDLL(pkv.LIB_PATH)
