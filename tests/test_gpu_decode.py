@@ -134,6 +134,23 @@ def test_decode_full_size_sampled(cfg):
     _check_all(w, out, w.dtype, sample)
 
 
+def test_decode_large_batch_sampled():
+    # 3000 short sequences: 375 run windows, groups of 8 and 5 sharing
+    # prefixes, lengths from 1 to 1100 (most single-partition)
+    n = 3000
+    rng = np.random.default_rng(17)
+    lens = rng.integers(1, 1101, size=n)
+    group = np.where(np.arange(n) % 16 < 13, (np.arange(n) // 8) % 40, -1)
+    plen = np.where(group >= 0, np.minimum(lens - 1, 520), 0)
+    w = synth.custom_workload("large_batch", 32, 8, 128, "bf16", 70000, seed=18, decode_lens=lens,
+                              prefix_len=plen, prefix_group=group)
+    print("decode large_batch", flush=True)
+    b, out = _run_decode(w, "f32", fill="device")
+    assert torch.isfinite(out.float()).all()
+    sample = sorted(set(rng.choice(n, size=40, replace=False).tolist() + [0, 7, 8, n - 1, int(np.argmax(lens))]))
+    _check_all(w, out, "f32", sample)
+
+
 def test_config3_step_sampled_with_bf16_out():
     # the workload the benchmark times: config 3, bf16 out, same launch shape
     w = synth.make_workload(3, seed=0)
