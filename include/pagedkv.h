@@ -410,6 +410,34 @@ int paged_attention_decode(void* out, int32_t out_dtype, const void* q, const vo
                            int32_t max_context_len, float scale, int32_t kv_dtype, void* workspace,
                            int64_t workspace_bytes, void* stream);
 
+/* One decode step's cache write and attention in one call:
+ * reshape_and_cache of each sequence's new token (k_new / v_new row s into
+ * slot_mapping[s]), then paged_attention_decode, with the same results (the
+ * step of "The decode stage, and how to spot the waste", Life of a prompt:
+ * append the new key and value, then attend over all of them).  With f16 /
+ * bf16 pools the rows are written by extra workgroups of the shared-run
+ * kernel, so the write needs no launch of its own; with f32 pools the write
+ * is launched first.  The new token's block must be the sequence's own (as
+ * paged_kv_seq_append leaves it, copy-on-write done) and context_lens must
+ * already count the new token.
+ *   k_new, v_new   device [num_seqs][n_kv_heads * head_dim] rows, kv_dtype,
+ *                  token strides k_new_stride / v_new_stride in elements
+ *                  (16-byte aligned rows).
+ *   slot_mapping   device int64 [num_seqs]; a slot outside the pool skips
+ *                  that row's write.
+ * Everything else as paged_attention_decode.  Every argument is checked
+ * before anything is launched.  8-bit pools: PKV_EINVAL (use
+ * reshape_and_cache_fp8, then paged_attention_decode_fp8). */
+int paged_attention_decode_append(void* out, int32_t out_dtype, const void* q, const void* k_new,
+                                  const void* v_new, int64_t k_new_stride, int64_t v_new_stride,
+                                  const int64_t* slot_mapping, void* k_pool, void* v_pool,
+                                  const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                  const int32_t* context_lens, int32_t num_seqs, int32_t n_q_heads,
+                                  int32_t n_kv_heads, int32_t head_dim, int32_t block_size,
+                                  int64_t num_blocks, int32_t max_context_len, float scale,
+                                  int32_t kv_dtype, void* workspace, int64_t workspace_bytes,
+                                  void* stream);
+
 /* Decode attention over an 8-bit cache (PKV_FP8_E4M3 pools written by
  * reshape_and_cache_fp8): the same result as paged_attention_decode with
  * every cached key and value replaced by value(code) * k_scale (resp.

@@ -28,38 +28,14 @@ reshape_and_cache_kernel(const unsigned char* __restrict__ key, const unsigned c
                          int64_t kstride_b, int64_t vstride_b, unsigned char* __restrict__ kpool,
                          unsigned char* __restrict__ vpool, const int64_t* __restrict__ slots,
                          int64_t T, int64_t num_slots, int H, int D) {
-  constexpr int X = 16 / ES;  // elements per 16-byte chunk
-  const int C = D / X;        // chunks per head row
+  const int C = D * ES / 16;  // chunks per head row
   const int64_t total = T * H * C;
   for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
        idx += (int64_t)gridDim.x * blockDim.x) {
     const int64_t i = idx % T;
     const int64_t rest = idx / T;
-    const int g = (int)(rest % H);
-    const int c = (int)(rest / H);
-    const int64_t slot = slots[i];
-    if (slot < 0 || slot >= num_slots) continue;
-    const int64_t blk = slot / kBlockSize;
-    const int off = (int)(slot % kBlockSize);
-    const int64_t tile = blk * H + g;
-    const u32x4 kv = ld16(key + i * kstride_b + ((int64_t)g * D + c * X) * ES);
-    const u32x4 vv = ld16(value + i * vstride_b + ((int64_t)g * D + c * X) * ES);
-    st16(kpool + (((tile * C + c) * kBlockSize + off) * 16), kv);
-    unsigned char* vrow = vpool + ((tile * D + (int64_t)c * X) * kBlockSize + off) * ES;
-    if constexpr (ES == 4) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        *reinterpret_cast<uint32_t*>(vrow + (int64_t)e * kBlockSize * ES) = vv[e];
-    } else if constexpr (ES == 1) {
-#pragma unroll
-      for (int e = 0; e < 16; ++e) vrow[(int64_t)e * kBlockSize] = (unsigned char)(vv[e >> 2] >> (8 * (e & 3)));
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const uint16_t h = (uint16_t)((e & 1) ? (vv[e >> 1] >> 16) : (vv[e >> 1] & 0xffffu));
-        *reinterpret_cast<uint16_t*>(vrow + (int64_t)e * kBlockSize * ES) = h;
-      }
-    }
+    cache_write_chunk<ES>(key, value, kstride_b, vstride_b, kpool, vpool, slots[i], num_slots, i,
+                          (int)(rest % H), (int)(rest / H), H, D);
   }
 }
 

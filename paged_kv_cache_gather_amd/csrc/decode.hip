@@ -796,6 +796,24 @@ __device__ __forceinline__ void mfma_partition(const Rows& R, int n, int g, int 
 // candidate runs, counted over its partitions in order, go round-robin to the
 // kRunSlots slots, so that runs of one window (and partitions) are served side
 // by side instead of one after another.
+// This step's new K/V rows can be written by extra workgroups of the
+// shared-run launch (grid z >= kRunSlots), so that the cache write costs no
+// launch of its own and fills CUs the runs leave idle.  A run never covers
+// a new token's block — the block a sequence appends into is its own after
+// copy-on-write, so its ids differ from every neighbour's — hence the write
+// and the runs touch disjoint bytes, and the per-sequence pass, launched
+// after, reads the new rows.
+struct AppendArgs {
+  const unsigned char* key = nullptr;    // new rows: token i's K row at key + i * kstride_b
+  const unsigned char* value = nullptr;
+  int64_t kstride_b = 0, vstride_b = 0;  // bytes between consecutive tokens' rows
+  unsigned char* kpool = nullptr;        // the pools, written
+  unsigned char* vpool = nullptr;
+  const int64_t* slots = nullptr;        // slot of new token i (outside the pool: skipped)
+  int64_t T = 0;                         // new tokens (0: no cache write)
+  int64_t num_slots = 0;
+};
+
 constexpr int kSharedWaves = PKV_SHARED_WAVES;  // waves per shared-run workgroup (4 or 8)
 constexpr int kRunSlots = PKV_RUN_SLOTS;        // workgroups per run window
 constexpr int kProbeParts = 64;                 // partitions probed per round
@@ -805,13 +823,28 @@ decode_shared_kernel(void* __restrict__ out, float* __restrict__ ws_o, float* __
                      const typename QT::bits* __restrict__ q, const unsigned char* __restrict__ kpool,
                      const unsigned char* __restrict__ vpool, const int32_t* __restrict__ tables,
                      int max_blocks, const int32_t* __restrict__ lens, int B, int Hkv, int64_t num_blocks,
-                     int max_context_len, float scale_log2, float v_mul, int max_parts) {
+                     int max_context_len, float scale_log2, float v_mul, int max_parts, AppendArgs app) {
   if constexpr (KV::kBytes == 4) {
     return;
   } else {
     constexpr int KM = kRunRows / G;
     static_assert(KM <= 32, "run window fits a 32-bit mask");
     constexpr int kThr = kSharedWaves * 64;
+    if (blockIdx.z >= kRunSlots) {  // the cache write of this step's new tokens (16-bit pools)
+      if constexpr (KV::kBytes == 2) {
+        const int C = D * 2 / 16;
+        const int64_t total = app.T * Hkv * C;
+        const int64_t wg = ((int64_t)(blockIdx.z - kRunSlots) * gridDim.y + blockIdx.y) * gridDim.x + blockIdx.x;
+        const int64_t stride = (int64_t)(gridDim.z - kRunSlots) * gridDim.y * gridDim.x * kThr;
+        for (int64_t idx = wg * kThr + threadIdx.x; idx < total; idx += stride) {
+          const int64_t i = idx % app.T;  // tokens fastest, as in reshape_and_cache
+          const int64_t rest = idx / app.T;
+          cache_write_chunk<2>(app.key, app.value, app.kstride_b, app.vstride_b, app.kpool, app.vpool, app.slots[i],
+                               app.num_slots, i, (int)(rest % Hkv), (int)(rest / Hkv), Hkv, D);
+        }
+      }
+      return;
+    }
     __shared__ __attribute__((aligned(16))) RunLds<D, kRunRows, kSharedWaves> sh;
     __shared__ uint32_t cmask[kProbeParts];  // per partition: bit i = member i may join member i - 1
     __shared__ uint32_t joins;
@@ -1087,6 +1120,7 @@ struct DecodeArgs {
   float v_mul;  // 8-bit cache: the V pool's scale
   int max_parts;
   hipStream_t stream;
+  AppendArgs app;  // this step's cache write, done by the shared-run launch (16-bit pools)
   // verify attention
   const int32_t* cu_q = nullptr;
   int total_q = 0, max_q_len = 0;
@@ -1096,12 +1130,22 @@ struct DecodeArgs {
 template <typename KV, typename QT, int D, int G, int OutCode>
 void launch_shared(const DecodeArgs& a) {
   constexpr int KM = kRunRows / G;
+  const int64_t windows = (a.B + KM - 1) / KM;
+  // z layers of cache-write workgroups: one thread per 16-byte chunk of the
+  // new rows (grid-stride beyond 64 layers)
+  int64_t nz = 0;
+  if (KV::kBytes == 2 && a.app.T > 0) {
+    const int64_t items = a.app.T * a.Hkv * (D * 2 / 16);
+    const int64_t per_layer = (int64_t)a.Hkv * windows * kSharedWaves * 64;
+    nz = (items + per_layer - 1) / per_layer;
+    nz = nz > 64 ? 64 : nz;
+  }
   hipLaunchKernelGGL((decode_shared_kernel<KV, QT, D, G, OutCode>),
-                     dim3((unsigned)a.Hkv, (unsigned)((a.B + KM - 1) / KM), (unsigned)kRunSlots),
+                     dim3((unsigned)a.Hkv, (unsigned)windows, (unsigned)(kRunSlots + nz)),
                      dim3(kSharedWaves * 64),
                      0, a.stream, a.out, a.ws_o, a.ws_ml, (const typename QT::bits*)a.q, a.kpool, a.vpool,
                      a.tables, a.max_blocks, a.lens, a.B, a.Hkv, a.num_blocks, a.max_context_len, a.scale_log2,
-                     a.v_mul, a.max_parts);
+                     a.v_mul, a.max_parts, a.app);
 }
 
 template <int D, int OutCode>
@@ -1215,7 +1259,8 @@ static int decode_impl(const char* fn, bool pa, bool re, bool fp8, void* out, in
                        const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
                        int32_t num_seqs, int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
                        int32_t block_size, int64_t num_blocks, int32_t max_context_len, float scale,
-                       int32_t kv_dtype, void* workspace, int64_t workspace_bytes, void* stream) {
+                       int32_t kv_dtype, void* workspace, int64_t workspace_bytes, void* stream,
+                       const pkv::AppendArgs* app = nullptr) {
   const std::string F(fn);
   if (!pkv::esize_of(kv_dtype)) return fail(PKV_EINVAL, F + ": unknown kv dtype");
   if (fp8 != (kv_dtype == PKV_FP8_E4M3))
@@ -1271,6 +1316,7 @@ static int decode_impl(const char* fn, bool pa, bool re, bool fp8, void* out, in
   a.v_mul = v_scale;
   a.max_parts = max_parts;
   a.stream = (hipStream_t)stream;
+  if (app) a.app = *app;
   using pkv::dispatch_d;
   using pkv::Fp8;
   using pkv::Plain;
@@ -1309,6 +1355,63 @@ static int decode_impl(const char* fn, bool pa, bool re, bool fp8, void* out, in
   out, out_dtype, q, kv_dtype, k_pool, v_pool, 1.0f, 1.0f, block_tables, max_blocks_per_seq,       \
       context_lens, num_seqs, n_q_heads, n_kv_heads, head_dim, block_size, num_blocks,             \
       max_context_len, scale, kv_dtype, workspace, workspace_bytes, stream
+
+// Fused cache write + decode: the new rows go in with the shared-run launch
+// (16-bit pools) or a cache-write launch first (fp32 pools).
+extern "C" int paged_attention_decode_append(void* out, int32_t out_dtype, const void* q, const void* k_new,
+                                             const void* v_new, int64_t k_new_stride, int64_t v_new_stride,
+                                             const int64_t* slot_mapping, void* k_pool, void* v_pool,
+                                             const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                             const int32_t* context_lens, int32_t num_seqs, int32_t n_q_heads,
+                                             int32_t n_kv_heads, int32_t head_dim, int32_t block_size,
+                                             int64_t num_blocks, int32_t max_context_len, float scale,
+                                             int32_t kv_dtype, void* workspace, int64_t workspace_bytes,
+                                             void* stream) {
+  const std::string F("paged_attention_decode_append");
+  if (kv_dtype == PKV_FP8_E4M3)
+    return fail(PKV_EINVAL, F + ": 8-bit pools take reshape_and_cache_fp8, then paged_attention_decode_fp8");
+  const int es = pkv::esize_of(kv_dtype);
+  if (!es) return fail(PKV_EINVAL, F + ": unknown kv dtype");
+  if (num_seqs > 0) {
+    if (!k_new || !v_new || !slot_mapping) return fail(PKV_EINVAL, F + ": NULL new rows or slot mapping");
+    const int64_t row = (int64_t)n_kv_heads * head_dim;
+    if (n_kv_heads < 1 || k_new_stride < row || v_new_stride < row)
+      return fail(PKV_EINVAL, F + ": token stride shorter than a row");
+    if (!pkv::aligned16(k_new) || !pkv::aligned16(v_new) || (k_new_stride * es) % 16 || (v_new_stride * es) % 16)
+      return fail(PKV_EINVAL, F + ": new rows and their strides must be 16-byte aligned");
+  }
+  if (kv_dtype == PKV_F32) {  // no shared-run launch: the cache write goes first
+    // the attention's arguments are checked before anything is launched
+    const int vr = decode_impl(F.c_str(), false, false, false, out, out_dtype, q, kv_dtype, k_pool, v_pool, 1.0f,
+                               1.0f, block_tables, max_blocks_per_seq, context_lens, num_seqs, n_q_heads,
+                               n_kv_heads, head_dim, block_size, num_blocks, max_context_len, scale, kv_dtype,
+                               workspace, workspace_bytes, stream);
+    if (vr != PKV_OK) return vr;
+    if (num_seqs > 0) {
+      const int rc = reshape_and_cache(k_new, v_new, k_new_stride, v_new_stride, k_pool, v_pool, slot_mapping,
+                                       num_seqs, num_blocks, n_kv_heads, head_dim, block_size, kv_dtype, stream);
+      if (rc != PKV_OK) return rc;
+    }
+    return decode_impl(F.c_str(), true, true, false, out, out_dtype, q, kv_dtype, k_pool, v_pool, 1.0f, 1.0f,
+                       block_tables, max_blocks_per_seq, context_lens, num_seqs, n_q_heads, n_kv_heads, head_dim,
+                       block_size, num_blocks, max_context_len, scale, kv_dtype, workspace, workspace_bytes,
+                       stream);
+  }
+  pkv::AppendArgs app;
+  app.key = (const unsigned char*)k_new;
+  app.value = (const unsigned char*)v_new;
+  app.kstride_b = k_new_stride * es;
+  app.vstride_b = v_new_stride * es;
+  app.kpool = (unsigned char*)k_pool;
+  app.vpool = (unsigned char*)v_pool;
+  app.slots = slot_mapping;
+  app.T = num_seqs;
+  app.num_slots = num_blocks * (int64_t)pkv::kBlockSize;
+  return decode_impl(F.c_str(), true, true, false, out, out_dtype, q, kv_dtype, k_pool, v_pool, 1.0f, 1.0f,
+                     block_tables, max_blocks_per_seq, context_lens, num_seqs, n_q_heads, n_kv_heads, head_dim,
+                     block_size, num_blocks, max_context_len, scale, kv_dtype, workspace, workspace_bytes, stream,
+                     &app);
+}
 
 extern "C" int paged_attention_decode(PKV_DECODE_PARAMS) {
   return decode_impl("paged_attention_decode", true, true, false, PKV_DECODE_ARGS);

@@ -113,4 +113,41 @@ __device__ __forceinline__ int64_t clamp_block(int64_t b, int64_t num_blocks) {
   return b < 0 ? 0 : (b >= num_blocks ? num_blocks - 1 : b);
 }
 
+// One item of a cache write (a bit copy): the 16-byte chunk c of new token
+// i's row for KV head g goes to its slot in the pool layout.  The K chunk
+// stays one 16-byte unit (x = 16 / ES consecutive dims of one token); the V
+// chunk is spread over its x dim-rows, one element each (V tiles are
+// dim-major).  A slot outside [0, num_slots) is skipped (padding).
+template <int ES>
+__device__ __forceinline__ void cache_write_chunk(const unsigned char* __restrict__ key,
+                                                  const unsigned char* __restrict__ value, int64_t kstride_b,
+                                                  int64_t vstride_b, unsigned char* __restrict__ kpool,
+                                                  unsigned char* __restrict__ vpool, int64_t slot, int64_t num_slots,
+                                                  int64_t i, int g, int c, int H, int D) {
+  constexpr int X = 16 / ES;  // elements per 16-byte chunk
+  constexpr int BS = 16;      // tokens per block
+  const int C = D / X;        // chunks per head row
+  if (slot < 0 || slot >= num_slots) return;
+  const int64_t blk = slot / BS;
+  const int off = (int)(slot % BS);
+  const int64_t tile = blk * H + g;
+  const u32x4 kv = ld16(key + i * kstride_b + ((int64_t)g * D + c * X) * ES);
+  const u32x4 vv = ld16(value + i * vstride_b + ((int64_t)g * D + c * X) * ES);
+  st16(kpool + (((tile * C + c) * BS + off) * 16), kv);
+  unsigned char* vrow = vpool + ((tile * D + (int64_t)c * X) * BS + off) * ES;
+  if constexpr (ES == 4) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) *reinterpret_cast<uint32_t*>(vrow + (int64_t)e * BS * ES) = vv[e];
+  } else if constexpr (ES == 1) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) vrow[(int64_t)e * BS] = (unsigned char)(vv[e >> 2] >> (8 * (e & 3)));
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const uint16_t h = (uint16_t)((e & 1) ? (vv[e >> 1] >> 16) : (vv[e >> 1] & 0xffffu));
+      *reinterpret_cast<uint16_t*>(vrow + (int64_t)e * BS * ES) = h;
+    }
+  }
+}
+
 }  // namespace pkv

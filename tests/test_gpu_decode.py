@@ -134,6 +134,53 @@ def test_decode_full_size_sampled(cfg):
     _check_all(w, out, w.dtype, sample)
 
 
+FUSED = [
+    # name, Hq, Hkv, d, dtype, lens, prefix_len, prefix_group
+    ("fused_shared_cow", 32, 8, 128, "bf16", [1100, 1100, 1500, 1030, 600, 17, 1, 2049, 513],
+     [1030, 1030, 1030, 1029, 0, 0, 0, 0, 0], [0, 0, 0, 0, -1, -1, -1, -1, -1]),
+    ("fused_f16_d64", 32, 4, 64, "f16", [700, 700, 129, 2048], [600, 600, 0, 0], [0, 0, -1, -1]),
+    ("fused_f32", 8, 2, 64, "f32", [5, 600, 1], [0, 0, 0], [-1, -1, -1]),
+]
+
+
+@pytest.mark.parametrize("name,Hq,Hkv,d,dtype,lens,plen,pgroup", FUSED, ids=[c[0] for c in FUSED])
+def test_decode_append_in_one_call(name, Hq, Hkv, d, dtype, lens, plen, pgroup):
+    # paged_attention_decode_append = reshape_and_cache + paged_attention_decode,
+    # bit for bit (output and pools), and within tolerance of the oracle
+    from paged_kv_cache_gather_amd.batch import DeviceBatch
+    w = synth.custom_workload(name, Hq, Hkv, d, dtype, 1024, seed=23, decode_lens=lens, prefix_len=plen,
+                              prefix_group=pgroup)
+    print(f"decode_append {name}", flush=True)
+    sep = DeviceBatch(w, DEV, fill="host", out_dtype="f32")
+    one = DeviceBatch(w, DEV, fill="host", out_dtype="f32")
+    out_sep, out_one = sep.new_decode_out(), one.new_decode_out()
+    sep.append_decode()
+    sep.attend_decode(out_sep)
+    one.step_decode(out_one)
+    torch.cuda.synchronize()
+    assert torch.equal(out_sep.view(torch.int32), out_one.view(torch.int32))
+    assert torch.equal(sep.k_pool.view(torch.uint8), one.k_pool.view(torch.uint8))
+    assert torch.equal(sep.v_pool.view(torch.uint8), one.v_pool.view(torch.uint8))
+    _check_all(w, out_one, "f32")
+
+
+def test_decode_append_skips_padding_slots():
+    from paged_kv_cache_gather_amd.batch import DeviceBatch
+    w = synth.custom_workload("fused_pad", 32, 8, 128, "bf16", 512, seed=24, decode_lens=[300, 40, 900])
+    sep = DeviceBatch(w, DEV, fill="host", out_dtype="f32")
+    one = DeviceBatch(w, DEV, fill="host", out_dtype="f32")
+    for b in (sep, one):
+        b.decode.slots[1] = -1  # this row is not written
+    out_sep, out_one = sep.new_decode_out(), one.new_decode_out()
+    sep.append_decode()
+    sep.attend_decode(out_sep)
+    one.step_decode(out_one)
+    torch.cuda.synchronize()
+    assert torch.equal(out_sep.view(torch.int32), out_one.view(torch.int32))
+    assert torch.equal(sep.k_pool.view(torch.uint8), one.k_pool.view(torch.uint8))
+    assert torch.equal(sep.v_pool.view(torch.uint8), one.v_pool.view(torch.uint8))
+
+
 def test_decode_large_batch_sampled():
     # 3000 short sequences: 375 run windows, groups of 8 and 5 sharing
     # prefixes, lengths from 1 to 1100 (most single-partition)

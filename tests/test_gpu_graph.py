@@ -64,6 +64,13 @@ def test_decode_step_replays():
     _replays_match(step, [out])
 
 
+def test_decode_step_in_one_call_replays():
+    b = _decode_batch()
+    out = b.new_decode_out()
+    print("graph decode_append", flush=True)
+    _replays_match(lambda: b.step_decode(out), [out])
+
+
 def test_decode_step_over_an_8bit_cache_replays():
     b = _decode_batch(kv_cache="fp8_e4m3", k_scale=FP8_K_SCALE, v_scale=FP8_V_SCALE)
     out = b.new_decode_out()
