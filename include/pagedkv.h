@@ -458,6 +458,27 @@ int paged_attention_decode_fp8(void* out, int32_t out_dtype, const void* q, int3
                                int32_t head_dim, int32_t block_size, int64_t num_blocks,
                                int32_t max_context_len, float scale, void* workspace,
                                int64_t workspace_bytes, void* stream);
+/* The decode step over 8-bit pools in one call: reshape_and_cache_fp8 of
+ * each sequence's new row (k_new / v_new in q_dtype, quantised with the
+ * pools' scales), then paged_attention_decode_fp8, with the same results.
+ * The rows are quantised by extra workgroups of the shared-run kernel (no
+ * launch of their own), as in paged_attention_decode_append, whose
+ * conditions hold here too (the new token's block is the sequence's own,
+ * context_lens count it).  k_new / v_new: device [num_seqs][n_kv_heads *
+ * head_dim] rows of q_dtype with token strides in elements (16-byte aligned);
+ * slot_mapping device int64 [num_seqs] (a slot outside the pool skips that
+ * row).  Everything else as paged_attention_decode_fp8; every argument is
+ * checked before anything is launched. */
+int paged_attention_decode_fp8_append(void* out, int32_t out_dtype, const void* q, int32_t q_dtype,
+                                      const void* k_new, const void* v_new, int64_t k_new_stride,
+                                      int64_t v_new_stride, const int64_t* slot_mapping, void* k_pool,
+                                      void* v_pool, float k_scale, float v_scale,
+                                      const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                      const int32_t* context_lens, int32_t num_seqs, int32_t n_q_heads,
+                                      int32_t n_kv_heads, int32_t head_dim, int32_t block_size,
+                                      int64_t num_blocks, int32_t max_context_len, float scale,
+                                      void* workspace, int64_t workspace_bytes, void* stream);
+
 /* Its two passes, as paged_attention_decode_partitions / _reduce are for
  * paged_attention_decode (same arguments and ordering rule). */
 int paged_attention_decode_fp8_partitions(void* out, int32_t out_dtype, const void* q, int32_t q_dtype,

@@ -102,6 +102,8 @@ _sig("paged_attention_decode_partition_size", _i32)
 _sig("paged_attention_decode_workspace_bytes", _i64, _i32, _i32, _i32, _i32)
 _sig("paged_attention_decode", ctypes.c_int, _P, _i32, _P, _P, _P, _P, _i32, _P, _i32, _i32, _i32,
      _i32, _i32, _i64, _i32, _f32, _i32, _P, _i64, _P)
+_sig("paged_attention_decode_fp8_append", ctypes.c_int, _P, _i32, _P, _i32, _P, _P, _i64, _i64, _P, _P, _P, _f32,
+     _f32, _P, _i32, _P, _i32, _i32, _i32, _i32, _i32, _i64, _i32, _f32, _P, _i64, _P)
 _sig("paged_attention_decode_append", ctypes.c_int, _P, _i32, _P, _P, _P, _i64, _i64, _P, _P, _P, _P, _i32, _P,
      _i32, _i32, _i32, _i32, _i32, _i64, _i32, _f32, _i32, _P, _i64, _P)
 for _n in ("paged_attention_decode_partitions", "paged_attention_decode_reduce"):
@@ -655,6 +657,49 @@ def paged_attention_decode_fp8(out: torch.Tensor, q: torch.Tensor, k_pool: torch
     k_scale, v_scale): out [B, Hq, d] (f32 or q's dtype); q [B, Hq, d] f16 or bf16."""
     _decode_fp8_call(_lib.paged_attention_decode_fp8, out, q, k_pool, v_pool, block_tables, context_lens,
                      max_context_len, n_kv_heads, num_blocks, scale, k_scale, v_scale, workspace, block_size, stream)
+
+
+
+def paged_attention_decode_fp8_append(out: torch.Tensor, q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
+                                      slot_mapping: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
+                                      block_tables: torch.Tensor, context_lens: torch.Tensor, max_context_len: int,
+                                      n_kv_heads: int, num_blocks: int, scale: float, k_scale: float, v_scale: float,
+                                      workspace=None, block_size: int = BLOCK_SIZE, stream=None):
+    """reshape_and_cache_fp8 of each sequence's new row (q's dtype), then
+    paged_attention_decode_fp8, in one call; arguments as those two."""
+    _dev(out, "out")
+    _dev(q, "q")
+    _dev(k_pool, "k_pool")
+    _dev(v_pool, "v_pool")
+    _dev(block_tables, "block_tables", torch.int32)
+    _dev(context_lens, "context_lens", torch.int32)
+    _dev(slot_mapping, "slot_mapping", torch.int64)
+    _dev(k_new, "k_new", q.dtype, contiguous=False)
+    _dev(v_new, "v_new", q.dtype, contiguous=False)
+    if not (_is_codes(k_pool) and _is_codes(v_pool)):
+        raise PagedKVError(PKV_EINVAL, "8-bit pools must be uint8 or float8_e4m3fn tensors")
+    if q.dim() != 3 or out.shape != q.shape:
+        raise PagedKVError(PKV_EINVAL, "q and out must be [num_seqs, n_q_heads, head_dim]")
+    B, Hq, d = q.shape
+    if block_tables.dim() != 2 or block_tables.shape[0] != B or context_lens.numel() != B:
+        raise PagedKVError(PKV_EINVAL, "block_tables/context_lens must have one row per sequence")
+    if slot_mapping.numel() != B or k_new.shape[0] != B or v_new.shape[0] != B:
+        raise PagedKVError(PKV_EINVAL, "k_new, v_new and slot_mapping must have one row per sequence")
+    for t, name in ((k_new, "k_new"), (v_new, "v_new")):
+        if t[0].numel() != n_kv_heads * d or (t.dim() > 1 and not t[0].is_contiguous()):
+            raise PagedKVError(PKV_EINVAL, f"{name} rows must be contiguous [n_kv_heads*head_dim]")
+    need = num_blocks * n_kv_heads * block_size * d
+    if k_pool.numel() < need or v_pool.numel() < need:
+        raise PagedKVError(PKV_EINVAL, "pool tensors smaller than num_blocks blocks")
+    ws_bytes = 0
+    if workspace is not None:
+        _dev(workspace, "workspace")
+        ws_bytes = workspace.numel() * workspace.element_size()
+    _check(_lib.paged_attention_decode_fp8_append(
+        _ptr(out), dtype_code(out.dtype), _ptr(q), dtype_code(q.dtype), _ptr(k_new), _ptr(v_new), k_new.stride(0),
+        v_new.stride(0), _ptr(slot_mapping), _ptr(k_pool), _ptr(v_pool), float(k_scale), float(v_scale),
+        _ptr(block_tables), block_tables.shape[1], _ptr(context_lens), B, Hq, n_kv_heads, d, block_size, num_blocks,
+        max_context_len, float(scale), _ptr(workspace), ws_bytes, _stream(stream, q.device)))
 
 
 def paged_attention_decode_fp8_partitions(out, q, k_pool, v_pool, block_tables, context_lens, max_context_len,

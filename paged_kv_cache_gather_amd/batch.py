@@ -23,7 +23,7 @@ from . import (paged_kv_alloc, paged_kv_seq_create, paged_kv_seq_fork, paged_kv_
                reshape_and_cache_fp8, paged_attention_decode, paged_attention_decode_fp8,
                paged_attention_decode_fp8_partitions, paged_attention_decode_fp8_reduce,
                paged_attention_decode_workspace_bytes, paged_attention_decode_partitions,
-               paged_attention_decode_append,
+               paged_attention_decode_append, paged_attention_decode_fp8_append,
                paged_attention_decode_reduce, paged_attention_prefill_chunk, paged_attention_verify,
                paged_attention_verify_workspace_bytes, paged_attention_verify_fp8, BLOCK_SIZE)
 
@@ -254,12 +254,14 @@ class DeviceBatch:
 
     def step_decode(self, out: torch.Tensor, stream=None):
         """The decode step in one call: the new rows' cache write and the
-        attention (paged_attention_decode_append; 8-bit pools: the two calls)."""
+        attention (paged_attention_decode_append, or its 8-bit variant)."""
         d = self.decode
         w = self.w
         if self.fp8:
-            self.append_decode(stream=stream)
-            self.attend_decode(out, stream=stream)
+            paged_attention_decode_fp8_append(out, d.q, d.k_new.view(w.n_decode, -1), d.v_new.view(w.n_decode, -1),
+                                              d.slots, self.k_pool, self.v_pool, d.tables, d.lens_dev,
+                                              d.max_context_len, w.n_kv_heads, w.num_blocks, w.scale, self.k_scale,
+                                              self.v_scale, workspace=d.workspace, stream=stream)
             return
         paged_attention_decode_append(out, d.q, d.k_new.view(w.n_decode, -1), d.v_new.view(w.n_decode, -1), d.slots,
                                       self.k_pool, self.v_pool, d.tables, d.lens_dev, d.max_context_len,

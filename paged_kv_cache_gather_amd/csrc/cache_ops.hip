@@ -39,43 +39,6 @@ reshape_and_cache_kernel(const unsigned char* __restrict__ key, const unsigned c
   }
 }
 
-// fp32 -> E4M3 code of the nearest value (ties to even): finite magnitudes
-// beyond 448 and infinities saturate first, NaN stays NaN.  Four values per
-// 32-bit word, the first in the low byte.
-__device__ __forceinline__ float e4m3_saturate(float y) {
-  return y != y ? y : fminf(fmaxf(y, -448.f), 448.f);
-}
-__device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
-  uint32_t w = __builtin_amdgcn_cvt_pk_fp8_f32(e4m3_saturate(a), e4m3_saturate(b), 0, false);
-  return __builtin_amdgcn_cvt_pk_fp8_f32(e4m3_saturate(c), e4m3_saturate(d), w, true);
-}
-
-// 16 source elements (one 16-dim chunk of a row) -> 16 codes, x * inv each.
-template <typename S>
-__device__ __forceinline__ u32x4 quantise16(const unsigned char* src, float inv) {
-  float f[16];
-  if constexpr (S::kBytes == 4) {
-#pragma unroll
-    for (int h = 0; h < 4; ++h) {
-      const u32x4 w = ld16(src + 16 * h);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) f[4 * h + e] = __uint_as_float(w[e]);
-    }
-  } else {
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const u32x4 w = ld16(src + 16 * h);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) unpack2<S>(w[e], f[8 * h + 2 * e], f[8 * h + 2 * e + 1]);
-    }
-  }
-  u32x4 r;
-#pragma unroll
-  for (int e = 0; e < 4; ++e)
-    r[e] = e4m3x4(f[4 * e] * inv, f[4 * e + 1] * inv, f[4 * e + 2] * inv, f[4 * e + 3] * inv);
-  return r;
-}
-
 // One work item = one 16-dim chunk of one token's head row: the K chunk is
 // one 16-byte store, the V chunk 16 one-byte stores (dim-major V).
 template <typename S>
@@ -90,19 +53,8 @@ reshape_and_cache_fp8_kernel(const unsigned char* __restrict__ key, const unsign
        idx += (int64_t)gridDim.x * blockDim.x) {
     const int64_t i = idx % T;
     const int64_t rest = idx / T;
-    const int g = (int)(rest % H);
-    const int c = (int)(rest / H);
-    const int64_t slot = slots[i];
-    if (slot < 0 || slot >= num_slots) continue;
-    const int64_t tile = (slot / kBlockSize) * H + g;
-    const int off = (int)(slot % kBlockSize);
-    const int64_t col = ((int64_t)g * D + c * 16) * S::kBytes;
-    const u32x4 kq = quantise16<S>(key + i * kstride_b + col, k_inv);
-    const u32x4 vq = quantise16<S>(value + i * vstride_b + col, v_inv);
-    st16(kpool + ((tile * C + c) * kBlockSize + off) * 16, kq);
-    unsigned char* vrow = vpool + (tile * D + (int64_t)c * 16) * kBlockSize + off;
-#pragma unroll
-    for (int e = 0; e < 16; ++e) vrow[(int64_t)e * kBlockSize] = (unsigned char)(vq[e >> 2] >> (8 * (e & 3)));
+    cache_write_chunk_fp8<S>(key, value, kstride_b, vstride_b, kpool, vpool, slots[i], num_slots, i,
+                             (int)(rest % H), (int)(rest / H), H, D, k_inv, v_inv);
   }
 }
 

@@ -812,6 +812,7 @@ struct AppendArgs {
   const int64_t* slots = nullptr;        // slot of new token i (outside the pool: skipped)
   int64_t T = 0;                         // new tokens (0: no cache write)
   int64_t num_slots = 0;
+  float k_inv = 1.f, v_inv = 1.f;        // 8-bit pools: the rows are quantised (x * inv), source type QT
 };
 
 constexpr int kSharedWaves = PKV_SHARED_WAVES;  // waves per shared-run workgroup (4 or 8)
@@ -830,18 +831,21 @@ decode_shared_kernel(void* __restrict__ out, float* __restrict__ ws_o, float* __
     constexpr int KM = kRunRows / G;
     static_assert(KM <= 32, "run window fits a 32-bit mask");
     constexpr int kThr = kSharedWaves * 64;
-    if (blockIdx.z >= kRunSlots) {  // the cache write of this step's new tokens (16-bit pools)
-      if constexpr (KV::kBytes == 2) {
-        const int C = D * 2 / 16;
-        const int64_t total = app.T * Hkv * C;
-        const int64_t wg = ((int64_t)(blockIdx.z - kRunSlots) * gridDim.y + blockIdx.y) * gridDim.x + blockIdx.x;
-        const int64_t stride = (int64_t)(gridDim.z - kRunSlots) * gridDim.y * gridDim.x * kThr;
-        for (int64_t idx = wg * kThr + threadIdx.x; idx < total; idx += stride) {
-          const int64_t i = idx % app.T;  // tokens fastest, as in reshape_and_cache
-          const int64_t rest = idx / app.T;
+    if (blockIdx.z >= kRunSlots) {  // the cache write of this step's new tokens
+      const int C = D * KV::kBytes / 16;  // 16-byte pool chunks per head row
+      const int64_t total = app.T * Hkv * C;
+      const int64_t wg = ((int64_t)(blockIdx.z - kRunSlots) * gridDim.y + blockIdx.y) * gridDim.x + blockIdx.x;
+      const int64_t stride = (int64_t)(gridDim.z - kRunSlots) * gridDim.y * gridDim.x * kThr;
+      for (int64_t idx = wg * kThr + threadIdx.x; idx < total; idx += stride) {
+        const int64_t i = idx % app.T;  // tokens fastest, as in reshape_and_cache
+        const int64_t rest = idx / app.T;
+        if constexpr (KV::kBytes == 2)
           cache_write_chunk<2>(app.key, app.value, app.kstride_b, app.vstride_b, app.kpool, app.vpool, app.slots[i],
                                app.num_slots, i, (int)(rest % Hkv), (int)(rest / Hkv), Hkv, D);
-        }
+        else
+          cache_write_chunk_fp8<QT>(app.key, app.value, app.kstride_b, app.vstride_b, app.kpool, app.vpool,
+                                    app.slots[i], app.num_slots, i, (int)(rest % Hkv), (int)(rest / Hkv), Hkv, D,
+                                    app.k_inv, app.v_inv);
       }
       return;
     }
@@ -1131,11 +1135,11 @@ template <typename KV, typename QT, int D, int G, int OutCode>
 void launch_shared(const DecodeArgs& a) {
   constexpr int KM = kRunRows / G;
   const int64_t windows = (a.B + KM - 1) / KM;
-  // z layers of cache-write workgroups: one thread per 16-byte chunk of the
-  // new rows (grid-stride beyond 64 layers)
+  // z layers of cache-write workgroups: one thread per 16-byte pool chunk of
+  // the new rows (grid-stride beyond 64 layers)
   int64_t nz = 0;
-  if (KV::kBytes == 2 && a.app.T > 0) {
-    const int64_t items = a.app.T * a.Hkv * (D * 2 / 16);
+  if (a.app.T > 0) {
+    const int64_t items = a.app.T * a.Hkv * (D * KV::kBytes / 16);
     const int64_t per_layer = (int64_t)a.Hkv * windows * kSharedWaves * 64;
     nz = (items + per_layer - 1) / per_layer;
     nz = nz > 64 ? 64 : nz;
@@ -1436,6 +1440,50 @@ extern "C" int paged_attention_decode_reduce(PKV_DECODE_PARAMS) {
 extern "C" int paged_attention_decode_fp8(PKV_DECODE_FP8_PARAMS) {
   return decode_impl("paged_attention_decode_fp8", true, true, true, PKV_DECODE_FP8_ARGS);
 }
+// Fused quantising cache write + decode over 8-bit pools: the new rows (in
+// the query's type) are quantised by the shared-run launch.
+extern "C" int paged_attention_decode_fp8_append(void* out, int32_t out_dtype, const void* q, int32_t q_dtype,
+                                                 const void* k_new, const void* v_new, int64_t k_new_stride,
+                                                 int64_t v_new_stride, const int64_t* slot_mapping, void* k_pool,
+                                                 void* v_pool, float k_scale, float v_scale,
+                                                 const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                                 const int32_t* context_lens, int32_t num_seqs, int32_t n_q_heads,
+                                                 int32_t n_kv_heads, int32_t head_dim, int32_t block_size,
+                                                 int64_t num_blocks, int32_t max_context_len, float scale,
+                                                 void* workspace, int64_t workspace_bytes, void* stream) {
+  const std::string F("paged_attention_decode_fp8_append");
+  if (q_dtype != PKV_F16 && q_dtype != PKV_BF16) return fail(PKV_EINVAL, F + ": q dtype must be f16 or bf16");
+  const int es = pkv::esize_of(q_dtype);
+  pkv::AppendArgs app;
+  if (num_seqs > 0) {
+    if (!k_new || !v_new || !slot_mapping) return fail(PKV_EINVAL, F + ": NULL new rows or slot mapping");
+    const int64_t row = (int64_t)n_kv_heads * head_dim;
+    if (n_kv_heads < 1 || k_new_stride < row || v_new_stride < row)
+      return fail(PKV_EINVAL, F + ": token stride shorter than a row");
+    if (!pkv::aligned16(k_new) || !pkv::aligned16(v_new) || (k_new_stride * es) % 16 || (v_new_stride * es) % 16)
+      return fail(PKV_EINVAL, F + ": new rows and their strides must be 16-byte aligned");
+    if (!std::isfinite(k_scale) || !std::isfinite(v_scale) || !(k_scale > 0.f) || !(v_scale > 0.f))
+      return fail(PKV_EINVAL, F + ": k_scale and v_scale must be finite and > 0");
+    // the reciprocals are rounded to nearest once, here, as by reshape_and_cache_fp8
+    app.k_inv = 1.0f / k_scale;
+    app.v_inv = 1.0f / v_scale;
+    if (!std::isfinite(app.k_inv) || !std::isfinite(app.v_inv)) return fail(PKV_EINVAL, F + ": scale too small");
+  }
+  app.key = (const unsigned char*)k_new;
+  app.value = (const unsigned char*)v_new;
+  app.kstride_b = k_new_stride * es;
+  app.vstride_b = v_new_stride * es;
+  app.kpool = (unsigned char*)k_pool;
+  app.vpool = (unsigned char*)v_pool;
+  app.slots = slot_mapping;
+  app.T = num_seqs;
+  app.num_slots = num_blocks * (int64_t)pkv::kBlockSize;
+  return decode_impl(F.c_str(), true, true, true, out, out_dtype, q, q_dtype, k_pool, v_pool, k_scale, v_scale,
+                     block_tables, max_blocks_per_seq, context_lens, num_seqs, n_q_heads, n_kv_heads, head_dim,
+                     block_size, num_blocks, max_context_len, scale, PKV_FP8_E4M3, workspace, workspace_bytes,
+                     stream, &app);
+}
+
 extern "C" int paged_attention_decode_fp8_partitions(PKV_DECODE_FP8_PARAMS) {
   return decode_impl("paged_attention_decode_fp8_partitions", true, false, true, PKV_DECODE_FP8_ARGS);
 }

@@ -150,4 +150,67 @@ __device__ __forceinline__ void cache_write_chunk(const unsigned char* __restric
   }
 }
 
+// fp32 -> E4M3 code of the nearest value (ties to even): finite magnitudes
+// beyond 448 and infinities saturate first, NaN stays NaN.  Four values per
+// 32-bit word, the first in the low byte.
+__device__ __forceinline__ float e4m3_saturate(float y) {
+  return y != y ? y : fminf(fmaxf(y, -448.f), 448.f);
+}
+__device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
+  uint32_t w = __builtin_amdgcn_cvt_pk_fp8_f32(e4m3_saturate(a), e4m3_saturate(b), 0, false);
+  return __builtin_amdgcn_cvt_pk_fp8_f32(e4m3_saturate(c), e4m3_saturate(d), w, true);
+}
+
+// 16 source elements (one 16-dim chunk of a row) -> 16 codes, x * inv each.
+template <typename S>
+__device__ __forceinline__ u32x4 quantise16(const unsigned char* src, float inv) {
+  float f[16];
+  if constexpr (S::kBytes == 4) {
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      const u32x4 w = ld16(src + 16 * h);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) f[4 * h + e] = __uint_as_float(w[e]);
+    }
+  } else {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const u32x4 w = ld16(src + 16 * h);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) unpack2<S>(w[e], f[8 * h + 2 * e], f[8 * h + 2 * e + 1]);
+    }
+  }
+  u32x4 r;
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+    r[e] = e4m3x4(f[4 * e] * inv, f[4 * e + 1] * inv, f[4 * e + 2] * inv, f[4 * e + 3] * inv);
+  return r;
+}
+
+// One item of a quantising cache write into 8-bit pools: the 16-dim chunk c
+// of new token i's row for KV head g (source type S) becomes 16 E4M3 codes
+// of x * inv (inv = the host-rounded reciprocal of the pool's scale); the K
+// chunk is one 16-byte store, the V chunk 16 one-byte stores (dim-major V).
+// A slot outside [0, num_slots) is skipped.
+template <typename S>
+__device__ __forceinline__ void cache_write_chunk_fp8(const unsigned char* __restrict__ key,
+                                                      const unsigned char* __restrict__ value, int64_t kstride_b,
+                                                      int64_t vstride_b, unsigned char* __restrict__ kpool,
+                                                      unsigned char* __restrict__ vpool, int64_t slot,
+                                                      int64_t num_slots, int64_t i, int g, int c, int H, int D,
+                                                      float k_inv, float v_inv) {
+  constexpr int BS = 16;  // tokens per block
+  const int C = D / 16;   // 16-dim chunks per head row
+  if (slot < 0 || slot >= num_slots) return;
+  const int64_t tile = (slot / BS) * H + g;
+  const int off = (int)(slot % BS);
+  const int64_t col = ((int64_t)g * D + c * 16) * S::kBytes;
+  const u32x4 kq = quantise16<S>(key + i * kstride_b + col, k_inv);
+  const u32x4 vq = quantise16<S>(value + i * vstride_b + col, v_inv);
+  st16(kpool + ((tile * C + c) * BS + off) * 16, kq);
+  unsigned char* vrow = vpool + (tile * D + (int64_t)c * 16) * BS + off;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) vrow[(int64_t)e * BS] = (unsigned char)(vq[e >> 2] >> (8 * (e & 3)));
+}
+
 }  // namespace pkv

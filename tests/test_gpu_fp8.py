@@ -156,6 +156,35 @@ def test_decode_fp8_small(name, Hq, Hkv, d, dtype, lens, out_kind):
     _check(w, out, out_dtype)
 
 
+FP8_FUSED = [
+    # name, Hq, Hkv, d, q dtype, lens, prefix_len, prefix_group
+    ("fused8_shared_cow", 32, 8, 128, "bf16", [1100, 1100, 1500, 1030, 600, 17, 1, 2049],
+     [1030, 1030, 1030, 1029, 0, 0, 0, 0], [0, 0, 0, 0, -1, -1, -1, -1]),
+    ("fused8_f16_d64", 32, 4, 64, "f16", [700, 700, 129, 513], [600, 600, 0, 0], [0, 0, -1, -1]),
+]
+
+
+@pytest.mark.parametrize("name,Hq,Hkv,d,dtype,lens,plen,pgroup", FP8_FUSED, ids=[c[0] for c in FP8_FUSED])
+def test_decode_fp8_append_in_one_call(name, Hq, Hkv, d, dtype, lens, plen, pgroup):
+    # paged_attention_decode_fp8_append = reshape_and_cache_fp8 +
+    # paged_attention_decode_fp8, bit for bit (output and pools)
+    from paged_kv_cache_gather_amd.batch import DeviceBatch
+    w = synth.custom_workload(name, Hq, Hkv, d, dtype, 1024, seed=25, decode_lens=lens, prefix_len=plen,
+                              prefix_group=pgroup)
+    print(f"fp8 decode_append {name}", flush=True)
+    kw = dict(fill="host", out_dtype="f32", kv_cache="fp8_e4m3", k_scale=FP8_K_SCALE, v_scale=FP8_V_SCALE)
+    sep, one = DeviceBatch(w, DEV, **kw), DeviceBatch(w, DEV, **kw)
+    out_sep, out_one = sep.new_decode_out(), one.new_decode_out()
+    sep.append_decode()
+    sep.attend_decode(out_sep)
+    one.step_decode(out_one)
+    torch.cuda.synchronize()
+    assert torch.equal(out_sep.view(torch.int32), out_one.view(torch.int32))
+    assert torch.equal(sep.k_pool.view(torch.uint8), one.k_pool.view(torch.uint8))
+    assert torch.equal(sep.v_pool.view(torch.uint8), one.v_pool.view(torch.uint8))
+    _check(w, out_one, "f32")
+
+
 FP8_RUNS = [
     # name, Hq, Hkv, d, dtype, lens, prefix_len, prefix_group
     ("runs_gqa4", 32, 8, 128, "bf16",

@@ -83,6 +83,13 @@ def test_decode_step_over_an_8bit_cache_replays():
     _replays_match(step, [out])
 
 
+def test_decode_step_in_one_call_over_an_8bit_cache_replays():
+    b = _decode_batch(kv_cache="fp8_e4m3", k_scale=FP8_K_SCALE, v_scale=FP8_V_SCALE)
+    out = b.new_decode_out()
+    print("graph decode_fp8_append", flush=True)
+    _replays_match(lambda: b.step_decode(out), [out])
+
+
 def test_prefill_and_verify_steps_replay():
     from paged_kv_cache_gather_amd.batch import DeviceBatch
     w = synth.custom_workload("graph_chunks", 32, 8, 128, "bf16", 2048, seed=43, chunk_ctx=[0, 700, 1500],
