@@ -13,8 +13,10 @@
 //
 // How (gfx950): three kernels per step on one stream.  decode_shared_kernel
 // first serves the partitions that neighbouring sequences share (see the
-// section on shared partitions below); decode_partition_kernel serves the
-// rest; decode_reduce_kernel merges split-context partials.  Over an 8-bit
+// section on shared partitions below) — and, when the step is one
+// paged_attention_decode_append call, writes the new tokens' K/V rows with
+// extra workgroups; decode_partition_kernel serves the rest;
+// decode_reduce_kernel merges split-context partials.  Over an 8-bit
 // (E4M3) cache the rest is served by decode_fp8_partition_kernel instead, on
 // MFMA like the shared kernel: the codes are widened in registers, exactly,
 // and the pools' scales fold into the softmax scale (keys) and the written
