@@ -275,6 +275,42 @@ def test_fp8_entry_points_validate_before_launch():
     assert write(ks=1e-45) == pkv.PKV_EINVAL  # reciprocal overflows
 
 
+def test_one_call_decode_steps_validate_before_launch():
+    # paged_attention_decode_append / _fp8_append check every argument (cache
+    # write and attention alike) before launching anything; with fake device
+    # pointers and no GPU, a launch would surface as PKV_EHIP instead
+    lib = ctypes.CDLL(pkv.LIB_PATH)
+    f8, bf16, f32 = pkv.PKV_FP8_E4M3, pkv.PKV_BF16, pkv.PKV_F32
+    fake = ctypes.c_void_p(1 << 20)
+    i64, flt = ctypes.c_int64, ctypes.c_float
+    lib.paged_attention_decode_append.restype = ctypes.c_int
+
+    def app(kv=bf16, k_new=fake, slots=fake, kstride=1024, d=128, max_ctx=64, maxb=4):
+        return lib.paged_attention_decode_append(fake, f32, fake, k_new, fake, i64(kstride), i64(1024), slots, fake,
+                                                 fake, fake, maxb, fake, 1, 32, 8, d, 16, i64(8), max_ctx, flt(0.1),
+                                                 kv, fake, i64(1 << 20), None)
+    assert app(kv=f8) == pkv.PKV_EINVAL             # 8-bit pools take the _fp8 call
+    assert app(k_new=None) == pkv.PKV_EINVAL
+    assert app(slots=None) == pkv.PKV_EINVAL
+    assert app(kstride=1000) == pkv.PKV_EINVAL      # shorter than a row of 8 x 128
+    assert app(k_new=ctypes.c_void_p((1 << 20) + 2)) == pkv.PKV_EINVAL  # unaligned rows
+    assert app(d=96) == pkv.PKV_EUNSUPPORTED
+    assert app(max_ctx=80) == pkv.PKV_EINVAL        # beyond the table width: the attention's check
+    for kv in (f32, pkv.PKV_F16):                    # fp32 pools write first: still nothing launched
+        assert app(kv=kv, max_ctx=80) == pkv.PKV_EINVAL
+    lib.paged_attention_decode_fp8_append.restype = ctypes.c_int
+
+    def app8(q_dtype=bf16, ks=1.0, vs=1.0, slots=fake, max_ctx=64):
+        return lib.paged_attention_decode_fp8_append(fake, f32, fake, q_dtype, fake, fake, i64(1024), i64(1024), slots,
+                                                     fake, fake, flt(ks), flt(vs), fake, 4, fake, 1, 32, 8, 128, 16,
+                                                     i64(8), max_ctx, flt(0.1), fake, i64(1 << 20), None)
+    assert app8(q_dtype=f32) == pkv.PKV_EINVAL
+    assert app8(ks=0.0) == pkv.PKV_EINVAL and app8(vs=float("nan")) == pkv.PKV_EINVAL
+    assert app8(ks=1e-45) == pkv.PKV_EINVAL        # reciprocal overflows
+    assert app8(slots=None) == pkv.PKV_EINVAL
+    assert app8(max_ctx=80) == pkv.PKV_EINVAL
+
+
 def test_fp8_pool_sizing():
     # one byte per element: half the bytes per token of a 16-bit cache, twice the blocks per budget
     assert pkv.paged_kv_bytes_per_token(32, 8, 128, "fp8_e4m3") == oracle.kv_bytes_per_token(32, 8, 128, 1)
