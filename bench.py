@@ -299,18 +299,20 @@ def swap_leg(b, n_seqs=32, reps=10):
             "out_frac_of_copy": t_d2h / t_out, "in_frac_of_copy": t_h2d / t_in}
 
 
-def verify_bytes(b):
+def verify_bytes(b, kv_elem_bytes=None):
     """Algorithmic bytes of one verify launch: every sequence's keys and
-    values (its context plus the new tokens) once per KV head, the queries,
-    block-table entries, lengths and the outputs."""
+    values (its context plus the new tokens) once per KV head (kv_elem_bytes
+    per element: 1 for 8-bit pools), the queries, block-table entries, lengths
+    and the outputs."""
     import numpy as np
     w, p = b.w, b.prefill
     keys = (p.ctx + p.qlen).astype(np.int64)
     eb = w.elem_bytes
+    kb = eb if kv_elem_bytes is None else kv_elem_bytes
     total_q = int(p.qlen.sum())
-    kv = int(keys.sum()) * 2 * w.head_dim * eb * w.n_kv_heads
+    kv = int(keys.sum()) * 2 * w.head_dim * kb * w.n_kv_heads
     other = (2 * total_q * w.n_q_heads * w.head_dim * eb + int((-(-keys // 16)).sum()) * 4 + 8 * len(keys))
-    return {"unit_bytes": 2 * w.head_dim * eb * w.n_kv_heads, "kv_bytes": kv, "other_bytes": other,
+    return {"unit_bytes": 2 * w.head_dim * kb * w.n_kv_heads, "kv_bytes": kv, "other_bytes": other,
             "algorithmic_bytes": kv + other}
 
 
@@ -368,7 +370,52 @@ def verify_leg(steps, warmup, seed, k=5):
                                     if seed == 0 else None),
                         "algorithmic_bytes": by["algorithmic_bytes"]},
            "bytes": by}
-    del b
+    del b, out
+    torch.cuda.empty_cache()
+    res["fp8"] = verify_fp8(w, steps, warmup)
+    return res
+
+
+def verify_fp8(w, steps, warmup):
+    """The same verify step over 8-bit (E4M3) pools: the new rows quantised
+    by reshape_and_cache_fp8, then paged_attention_verify_fp8."""
+    import numpy as np
+    import torch
+    from paged_kv_cache_gather_amd.batch import DeviceBatch
+    b = DeviceBatch(w, "cuda:0", fill="device", kv_cache="fp8_e4m3", k_scale=FP8_K_SCALE, v_scale=FP8_V_SCALE)
+    out = b.new_prefill_out()
+    st = torch.cuda.current_stream()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+
+    def step(e=None):
+        rec = (lambda i: e[i].record(st)) if e is not None else (lambda i: None)
+        rec(0)
+        b.append_prefill()
+        rec(1)
+        b.attend_verify(out)
+        rec(2)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    for i in range(steps):
+        step(ev[i])
+    torch.cuda.synchronize()
+    app = np.array([e[0].elapsed_time(e[1]) for e in ev]) * 1e3
+    ver = np.array([e[1].elapsed_time(e[2]) for e in ev]) * 1e3
+    by = verify_bytes(b, kv_elem_bytes=1)
+    ach = by["algorithmic_bytes"] / (ver.mean() * 1e-6) / 1e9
+    toks = int(w.chunk_qlen.sum())
+    log(f"verify over 8-bit pools: append {app.mean():.1f} us | verify {ver.mean():.1f} us = {ach:.0f} GB/s "
+        f"({ach / HBM_PEAK_GBS:.1%})")
+    res = {"kv_cache": "fp8_e4m3", "step_us": float(app.mean() + ver.mean()),
+           "tokens_per_s": toks / ((app.mean() + ver.mean()) * 1e-6),
+           "breakdown_us": {"append": float(app.mean()), "verify": float(ver.mean())},
+           "roofline": {"bound": "hbm", "kernel": "verify_partition_kernel<FP8, ...> + decode_reduce_kernel",
+                        "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": ach / HBM_PEAK_GBS,
+                        "traffic": None, "algorithmic_bytes": by["algorithmic_bytes"]},
+           "bytes": by}
+    del b, out
     torch.cuda.empty_cache()
     return res
 
