@@ -12,7 +12,9 @@
 // one token together), while a V chunk is spread over x dim-rows, one
 // element each, since V tiles are dim-major.  Consecutive lanes take
 // consecutive tokens, so tokens that fill one block (a prefill chunk) write
-// contiguous runs.
+// contiguous runs.  The per-item bodies (cache_write_chunk,
+// cache_write_chunk_fp8) live in pkv_device.h: the decode launch of
+// paged_attention_decode_append uses them too.
 #include <cmath>
 #include <string>
 

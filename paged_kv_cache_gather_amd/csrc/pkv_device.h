@@ -1,5 +1,7 @@
 // Device-side helpers for the gfx950 kernels: element types, 16-byte vector
-// accesses, conversions and wave64 reductions.
+// accesses, conversions, wave64 reductions, and the per-item bodies of the
+// cache writes (plain and quantising), shared by the cache-write kernels and
+// the decode launch that writes a step's new rows.
 #pragma once
 
 #include <hip/hip_runtime.h>
