@@ -140,6 +140,9 @@ FUSED = [
      [1030, 1030, 1030, 1029, 0, 0, 0, 0, 0], [0, 0, 0, 0, -1, -1, -1, -1, -1]),
     ("fused_f16_d64", 32, 4, 64, "f16", [700, 700, 129, 2048], [600, 600, 0, 0], [0, 0, -1, -1]),
     ("fused_f32", 8, 2, 64, "f32", [5, 600, 1], [0, 0, 0], [-1, -1, -1]),
+    # MHA (32-sequence run windows) and G = 16 (2-sequence windows)
+    ("fused_mha", 8, 8, 128, "f16", [1300, 1300, 600, 1030], [1200, 1200, 0, 1029], [0, 0, -1, 0]),
+    ("fused_gqa16", 32, 2, 64, "bf16", [900, 900, 100, 513, 513], [600, 600, 0, 512, 512], [0, 0, -1, 1, 1]),
 ]
 
 
