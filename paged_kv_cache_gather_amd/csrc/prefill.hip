@@ -232,9 +232,12 @@ prefill_chunk_kernel(void* __restrict__ out, const uint16_t* __restrict__ q,
     k_row_off[sub] = (kr >> 4) * TILE + ((kr & 15) + q4 * kBlockSize) * 16;
     key_base[sub] = pair_key(4 * q4, sub);  // key of score element r = 0 held by this lane
   }
-  // V^T operand: dims 16dt + r16, the lane group's 8 keys; odd groups of 8
-  // dims keep their two 16-byte halves swapped (bank-conflict-free reads)
-  const int v_off = (q4 >> 1) * TILE + r16 * 32 + (((q4 & 1) ^ (r16 >> 3)) * 16);
+  // V^T operand: dims 16dt + r16, the lane group's 8 keys.  A dim row is 32
+  // bytes (16 keys); lane group q4 reads half q4 & 1 of the rows of block
+  // q4 >> 1.  Unswizzled rows measure free of LDS bank conflicts for this
+  // pattern on gfx950; swapping the halves of every other group of 8 rows
+  // doubled the LDS cycles of these reads.
+  const int v_off = (q4 >> 1) * TILE + r16 * 32 + (q4 & 1) * 16;
   const u32x4 ones = {0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u};  // fp16 1.0 x 8
 
   f32x4 o[RT][DT];
@@ -292,9 +295,8 @@ prefill_chunk_kernel(void* __restrict__ out, const uint16_t* __restrict__ q,
     for (int k = 0; k < NCH; ++k) raw[k] = *reinterpret_cast<const u32x4*>(&lds[buf][1][(tid + kPfThreads * k) * 16]);
   };
   // Raw V chunks -> fp16, keys at or past the context zeroed (blocks past the
-  // end become zeros), written to the swizzled slot of their dim row; odd
-  // blocks with their 4-key halves swapped.  Both halves of a dim row belong
-  // to adjacent lanes of one wave, so the in-place exchange is race-free.
+  // end become zeros), written back in place (each thread rewrites the 16
+  // bytes it read); odd blocks with their 4-key halves swapped.
   auto finish_step = [&](int s, int buf, const u32x4 (&raw)[NCH]) {
 #pragma unroll
     for (int k = 0; k < NCH; ++k) {
@@ -304,7 +306,7 @@ prefill_chunk_kernel(void* __restrict__ out, const uint16_t* __restrict__ q,
       const int j = off / 32, hf = (off % 32) / 16;  // dim j, keys 8hf..8hf+7
       u32x4 v = lb < nblk ? v_chunk_to_f16<T>(raw[k], L - (lb * kBlockSize + 8 * hf)) : u32x4{0, 0, 0, 0};
       if (bi & 1) v = u32x4{v[2], v[3], v[0], v[1]};
-      *reinterpret_cast<u32x4*>(&lds[buf][1][bi * TILE + j * 32 + ((hf ^ ((j >> 3) & 1)) * 16)]) = v;
+      *reinterpret_cast<u32x4*>(&lds[buf][1][bi * TILE + j * 32 + hf * 16]) = v;
     }
   };
   // Wait until at most `keep` vector-memory operations of this wave are
