@@ -236,7 +236,7 @@ prefill_chunk_kernel(void* __restrict__ out, const uint16_t* __restrict__ q,
   // bytes (16 keys); lane group q4 reads half q4 & 1 of the rows of block
   // q4 >> 1.  Unswizzled rows measure free of LDS bank conflicts for this
   // pattern on gfx950; swapping the halves of every other group of 8 rows
-  // doubled the LDS cycles of these reads.
+  // made these reads 2-way bank conflicted.
   const int v_off = (q4 >> 1) * TILE + r16 * 32 + (q4 & 1) * 16;
   const u32x4 ones = {0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u};  // fp16 1.0 x 8
 
