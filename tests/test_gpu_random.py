@@ -1,0 +1,173 @@
+"""Seeded random configurations against the fp64 oracle.
+
+Each case draws, from its own seed, a GQA ratio (1, 2, 4, 8 or 16), a head
+dimension (64 or 128), a dtype, an output dtype and a ragged batch whose
+lengths mix uniform draws with the edges of blocks (16 tokens) and of decode
+partitions (512 tokens), plus groups of neighbouring sequences forked from a
+shared prefix (members may take shorter prefixes; some prefixes span whole
+partitions, so the shared-run path serves them).  The same draws drive:
+
+* the one-call decode step, checked bit for bit against the cache write and
+  attention as separate calls and within tolerance of the oracle;
+* the same step over 8-bit pools, against the oracle on the dequantised cache;
+* chunked prefill over cached contexts (sampled rows of every chunk);
+* verify attention (a few new tokens per sequence, every row)."""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from tests.conftest import gpu_available
+from tests.helpers import (FP8_K_SCALE, FP8_V_SCALE, assert_close, decode_reference, decode_reference_fp8,
+                           prefill_reference, tolerance)
+
+pytestmark = [pytest.mark.gpu, pytest.mark.skipif(not gpu_available(), reason="needs a GPU")]
+
+DEV = "cuda:0"
+EDGES = [1, 2, 15, 16, 17, 511, 512, 513, 1023, 1024, 1025, 1536, 2047, 2048, 2049]
+
+
+def _heads(rng):
+    while True:
+        G = int(rng.choice([1, 2, 4, 8, 16]))
+        Hkv = int(rng.choice([1, 2, 4, 8]))
+        if G * Hkv <= 64:
+            return G * Hkv, Hkv
+
+
+def _decode_case(seed, dtypes=("f16", "bf16")):
+    rng = np.random.default_rng(seed)
+    Hq, Hkv = _heads(rng)
+    d = int(rng.choice([64, 128]))
+    dtype = str(rng.choice(dtypes))
+    B = int(rng.integers(1, 25))
+    lens = [int(rng.choice(EDGES)) if rng.random() < 0.5 else int(rng.integers(1, 3001)) for _ in range(B)]
+    plen, pgroup = [0] * B, [-1] * B
+    s, g = 0, 0
+    while s < B:
+        k = int(rng.integers(2, 9))
+        if rng.random() < 0.45 and s + k <= B:
+            P = int(rng.choice([512, 1024, 1025, 1536, 16 * int(rng.integers(1, 130)), int(rng.integers(1, 2100))]))
+            for m in range(s, s + k):
+                p = P if rng.random() < 0.7 else int(rng.integers(1, P + 1))
+                lens[m] = max(lens[m], p + 1)
+                plen[m], pgroup[m] = p, g
+            g += 1
+            s += k
+        else:
+            s += 1
+    nb = sum(-(-L // 16) + 1 for L in lens) + 64
+    out_kind = "f32" if rng.random() < 0.5 else dtype
+    name = f"rand{seed}_Hq{Hq}_Hkv{Hkv}_d{d}_{dtype}_B{B}"
+    w = synth.custom_workload(name, Hq, Hkv, d, dtype, nb, seed=seed, decode_lens=lens, prefix_len=plen,
+                              prefix_group=pgroup)
+    return w, out_kind
+
+
+def _describe(w):
+    return (f"{w.name} lens={w.decode_lens.tolist()} prefix_len={w.prefix_len.tolist()} "
+            f"groups={w.prefix_group.tolist()}")
+
+
+@pytest.mark.parametrize("seed", range(100, 112))
+def test_random_decode_step(seed):
+    from paged_kv_cache_gather_amd.batch import DeviceBatch
+    w, out_kind = _decode_case(seed)
+    print(f"random decode {_describe(w)} out={out_kind}", flush=True)
+    sep = DeviceBatch(w, DEV, fill="host", out_dtype=out_kind)
+    one = DeviceBatch(w, DEV, fill="host", out_dtype=out_kind)
+    out_sep, out_one = sep.new_decode_out(), one.new_decode_out()
+    sep.append_decode()
+    sep.attend_decode(out_sep)
+    one.step_decode(out_one)
+    torch.cuda.synchronize()
+    bits = torch.int32 if out_one.element_size() == 4 else torch.int16
+    assert torch.equal(out_sep.view(bits), out_one.view(bits)), "one-call step differs from separate calls"
+    assert torch.equal(sep.k_pool.view(torch.uint8), one.k_pool.view(torch.uint8))
+    assert torch.equal(sep.v_pool.view(torch.uint8), one.v_pool.view(torch.uint8))
+    atol, rtol = tolerance(w.dtype, out_kind)
+    got = out_one.double().cpu().numpy()
+    for s in range(w.n_decode):
+        assert_close(f"{w.name} seq {s} L={int(w.decode_lens[s])}", got[s], decode_reference(w, s), atol, rtol)
+
+
+@pytest.mark.parametrize("seed", range(200, 206))
+def test_random_decode_step_over_8bit_pools(seed):
+    from paged_kv_cache_gather_amd.batch import DeviceBatch
+    w, out_kind = _decode_case(seed)
+    print(f"random fp8 decode {_describe(w)} out={out_kind}", flush=True)
+    b = DeviceBatch(w, DEV, fill="host", out_dtype=out_kind, kv_cache="fp8_e4m3", k_scale=FP8_K_SCALE,
+                    v_scale=FP8_V_SCALE)
+    out = b.new_decode_out()
+    b.step_decode(out)
+    torch.cuda.synchronize()
+    atol, rtol = tolerance(w.dtype, out_kind)
+    got = out.double().cpu().numpy()
+    for s in range(w.n_decode):
+        assert_close(f"{w.name} fp8 seq {s} L={int(w.decode_lens[s])}", got[s], decode_reference_fp8(w, s),
+                     atol, rtol)
+
+
+CTX_EDGES = [0, 1, 15, 16, 17, 63, 64, 65, 511, 512, 513]
+Q_EDGES = [1, 2, 15, 16, 17, 63, 64, 65, 127, 128, 129]
+
+
+def _chunk_case(seed, max_q):
+    rng = np.random.default_rng(seed)
+    Hq, Hkv = _heads(rng)
+    d = int(rng.choice([64, 128]))
+    dtype = str(rng.choice(["f16", "bf16"]))
+    n = int(rng.integers(1, 7))
+    ctx = [int(rng.choice(CTX_EDGES)) if rng.random() < 0.5 else int(rng.integers(0, 1501)) for _ in range(n)]
+    if max_q > 16:
+        ql = [int(rng.choice(Q_EDGES)) if rng.random() < 0.5 else int(rng.integers(1, max_q + 1)) for _ in range(n)]
+    else:
+        ql = [int(rng.integers(1, max_q + 1)) for _ in range(n)]
+    nb = sum(-(-(c + q) // 16) + 1 for c, q in zip(ctx, ql)) + 64
+    out_kind = "f32" if rng.random() < 0.5 else dtype
+    name = f"rand{seed}_Hq{Hq}_Hkv{Hkv}_d{d}_{dtype}_n{n}"
+    w = synth.custom_workload(name, Hq, Hkv, d, dtype, nb, seed=seed, chunk_ctx=ctx, chunk_qlen=ql)
+    return w, out_kind
+
+
+def _check_chunks(w, out, out_kind, rows_per_chunk, seed):
+    atol, rtol = tolerance(w.dtype, out_kind)
+    got = out.double().cpu().numpy()
+    cu = np.concatenate([[0], np.cumsum(w.chunk_qlen)])
+    rng = np.random.default_rng(seed)
+    for c in range(w.n_chunks):
+        ql = int(w.chunk_qlen[c])
+        if ql <= rows_per_chunk:
+            rows = np.arange(ql)
+        else:
+            rows = np.unique(np.concatenate([[0, ql - 1], rng.choice(ql, rows_per_chunk, replace=False)]))
+        assert_close(f"{w.name} chunk {c} ctx={int(w.chunk_ctx[c])} q={ql}", got[cu[c] + rows],
+                     prefill_reference(w, c, rows), atol, rtol)
+
+
+@pytest.mark.parametrize("seed", range(300, 306))
+def test_random_prefill_chunks(seed):
+    from paged_kv_cache_gather_amd.batch import DeviceBatch
+    w, out_kind = _chunk_case(seed, 300)
+    print(f"random prefill {w.name} ctx={w.chunk_ctx.tolist()} q={w.chunk_qlen.tolist()} out={out_kind}",
+          flush=True)
+    b = DeviceBatch(w, DEV, fill="host", out_dtype=out_kind)
+    b.append_prefill()
+    out = b.new_prefill_out()
+    b.attend_prefill(out)
+    torch.cuda.synchronize()
+    _check_chunks(w, out, out_kind, 24, seed)
+
+
+@pytest.mark.parametrize("seed", range(400, 406))
+def test_random_verify(seed):
+    from paged_kv_cache_gather_amd.batch import DeviceBatch
+    w, out_kind = _chunk_case(seed, 9)
+    print(f"random verify {w.name} ctx={w.chunk_ctx.tolist()} q={w.chunk_qlen.tolist()} out={out_kind}",
+          flush=True)
+    b = DeviceBatch(w, DEV, fill="host", out_dtype=out_kind)
+    b.append_prefill()
+    out = b.new_prefill_out()
+    b.attend_verify(out)
+    torch.cuda.synchronize()
+    _check_chunks(w, out, out_kind, 1 << 30, seed)
