@@ -169,15 +169,45 @@ prefill_chunk_kernel(void* __restrict__ out, const uint16_t* __restrict__ q,
   __shared__ __attribute__((aligned(16))) unsigned char lds[NBUF][2][4 * TILE];  // [buffer][K, V]
   static_assert(kPfWaves == 8, "the phase schedule pairs waves w and w + 4 on one SIMD");
 
-  const int c = blockIdx.z;
+  // Longest work first.  The causal work of a (chunk, query tile) unit grows
+  // with the chunk's context length L, and the chunks of one call can differ
+  // by two orders of magnitude; dispatched in index order, a long chunk that
+  // comes late sets the kernel's length.  So grid slot z takes the chunk of
+  // rank z in decreasing L (ties by index) and slot y the chunk's y-th tile
+  // from the end.  Every workgroup ranks the chunks itself (each thread one
+  // chunk, against a copy of all L in LDS), so nothing is precomputed; with
+  // more chunks than threads the chunks keep their index order.
+  __shared__ int rank_len[kPfThreads];
+  __shared__ int rank_pick;
+  int c = blockIdx.z;
+  if (gridDim.z <= (unsigned)kPfThreads) {
+    const int n = gridDim.z, t = threadIdx.x;
+    if (t < n) {
+      const int l = lens[t];
+      rank_len[t] = l < 0 ? 0 : (l > max_context_len ? max_context_len : l);
+    }
+    __syncthreads();
+    if (t < n) {
+      const int mine = rank_len[t];
+      int r = 0;
+      for (int j = 0; j < n; ++j) {
+        const int other = rank_len[j];
+        r += (other > mine) | ((other == mine) & (j < t));
+      }
+      if (r == (int)blockIdx.z) rank_pick = t;
+    }
+    __syncthreads();
+    c = rank_pick;
+  }
   const int qs = cu_q[c];
   int qlen = cu_q[c + 1] - qs;
   int L = lens[c];
   L = L < 0 ? 0 : (L > max_context_len ? max_context_len : L);
   qlen = qlen < 0 ? 0 : (qlen > L ? L : qlen);
   const int ctx = L - qlen;
-  const int tile0 = blockIdx.y * TWG;
-  if (tile0 >= qlen) return;
+  const int tile_idx = (qlen + TWG - 1) / TWG - 1 - (int)blockIdx.y;
+  if (tile_idx < 0) return;
+  const int tile0 = tile_idx * TWG;
 
   const int hgroups = G / GW;
   const int g = blockIdx.x / hgroups;
