@@ -109,3 +109,27 @@ def test_decode_equals_last_prefill_row():
     torch.cuda.synchronize()
     np.testing.assert_allclose(od.cpu().numpy()[0], op.cpu().numpy()[0], rtol=2e-3, atol=2e-3)
     assert_close("decode vs oracle", od.cpu().numpy()[0], decode_reference(wd, 0), atol, rtol)
+
+
+def test_dispatch_order_ties_and_ranked_chunks():
+    # chunks are dispatched in decreasing context length; equal lengths (ties,
+    # ranked by index) with different context/query splits, and one shorter
+    ctx = [100, 50, 0, 140, 100, 120, 0, 30, 150, 149]
+    ql = [60, 110, 160, 20, 60, 40, 1, 130, 10, 11]
+    w = synth.custom_workload("ties", 16, 4, 128, "bf16", 512, seed=13, chunk_ctx=ctx, chunk_qlen=ql)
+    print("prefill ties", flush=True)
+    _, out = _run_prefill(w, "f32")
+    _check_chunks(w, out, "f32")
+
+
+def test_more_chunks_than_the_ranking_covers():
+    # beyond 512 chunks the workgroups keep index order
+    rng = np.random.default_rng(17)
+    n = 600
+    ctx = rng.integers(0, 120, size=n).tolist()
+    ql = rng.integers(1, 5, size=n).tolist()
+    nb = sum(-(-(c + q) // 16) + 1 for c, q in zip(ctx, ql)) + 16
+    w = synth.custom_workload("many_chunks", 8, 2, 64, "f16", nb, seed=17, chunk_ctx=ctx, chunk_qlen=ql)
+    print(f"prefill {n} chunks", flush=True)
+    _, out = _run_prefill(w, "f32")
+    _check_chunks(w, out, "f32")
