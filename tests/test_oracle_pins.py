@@ -169,6 +169,60 @@ def test_equal_scores_average_the_values():
     np.testing.assert_allclose(out[0, 0], v[:, 0].mean(axis=0), rtol=0, atol=1e-14)
 
 
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_long_context_two_level_scores_closed_form(dtype):
+    # 16500 tokens (33 partitions of 512) of 16-bit K/V written through a
+    # shuffled block table and read back by the paged gather.  Keys take two
+    # values per KV head, +u_g for the first n_a tokens and -u_g after, and
+    # query head h holds c_h u_g / |u_g|^2, so every score is +-scale c_h and
+    # the softmax average is a closed form of two plain sums:
+    #   out = (e^{a} S_A + e^{-a} S_B) / (n_A e^{a} + n_B e^{-a}),  a = scale c_h
+    # (c_h = 0: equal scores, the mean of V).  Queries at the last position
+    # and at an interior one (causal: keys 0..pos).
+    rng = np.random.default_rng(21)
+    L, Hkv, G, d, bs, n_a = 16500, 2, 4, 64, 16, 6100
+    Hq, scale = Hkv * G, 1.0 / 8.0
+
+    def to_bits(x):
+        if dtype == "f16":
+            return x.astype(np.float16).view(np.uint16)
+        return (torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16).view(torch.int16).numpy()
+                .view(np.uint16))
+
+    u_bits = to_bits(rng.standard_normal((Hkv, d)))
+    u = oracle.decode(dtype, u_bits)
+    kbits = np.empty((L, Hkv, d), np.uint16)
+    neg = to_bits(-u)
+    kbits[:n_a] = u_bits
+    kbits[n_a:] = neg
+    vbits = to_bits(rng.standard_normal((L, Hkv, d)))
+    nblk = -(-L // bs)
+    nb = nblk + 9
+    table = rng.permutation(nb)[:nblk].astype(np.int32)
+    slots = [oracle.slot(table, t, bs) for t in range(L)]
+    kp = np.zeros(oracle.pool_elems(nb, bs, Hkv, d), np.uint16)
+    vp = np.zeros_like(kp)
+    oracle.scatter(dtype, kbits, vbits, kp, vp, slots, nb, bs, Hkv, d)
+    k, v = oracle.gather(dtype, kp, vp, nb, bs, Hkv, d, table, L)
+    c = np.array([0.0, 3.0, 12.0, -16.0] * Hkv)
+    q = np.empty((2, Hq, d))
+    for h in range(Hq):
+        ug = u[h // G]
+        q[:, h] = c[h] * ug / np.dot(ug, ug)
+    positions = [L - 1, 9000]
+    out, _ = oracle.attention(q, positions, k, v, scale, n_threads=4)
+    vv = oracle.decode(dtype, vbits)
+    for r, pos in enumerate(positions):
+        na, nbk = min(n_a, pos + 1), max(0, pos + 1 - n_a)
+        for h in range(Hq):
+            g, a = h // G, scale * c[h]
+            sa = vv[:na, g].sum(axis=0)
+            sb = vv[n_a:pos + 1, g].sum(axis=0)
+            exp = (math.exp(a) * sa + math.exp(-a) * sb) / (na * math.exp(a) + nbk * math.exp(-a))
+            np.testing.assert_allclose(out[r, h], exp, rtol=1e-11, atol=1e-13,
+                                       err_msg=f"{dtype} row {r} head {h}")
+
+
 def test_dominant_key_selects_its_value():
     rng = np.random.default_rng(5)
     N, d = 9, 4
