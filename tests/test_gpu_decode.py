@@ -249,3 +249,50 @@ def test_placement_invariance_and_determinism():
         torch.cuda.synchronize()
         assert np.array_equal(out.cpu().numpy(), out2.cpu().numpy())
     assert np.array_equal(outs[0][1], outs[1][1])
+
+
+def test_long_context_two_level_scores_closed_form():
+    # 16500 bf16 tokens (33 partitions) through a shuffled block table; keys
+    # +u_g for the first 6100 tokens and -u_g after, so every score is +-a_h and
+    # the output is a closed form of two plain sums, computed here without the
+    # oracle: out = (e^a S_A + e^-a S_B) / (n_A e^a + n_B e^-a)  (a = 0: mean of V)
+    import math
+    import paged_kv_cache_gather_amd as pkv
+    rng = np.random.default_rng(31)
+    L, Hkv, G, d, bs, n_a = 16500, 2, 4, 128, 16, 6100
+    Hq, scale, dt = Hkv * G, 1.0 / math.sqrt(128), torch.bfloat16
+    u = torch.from_numpy(rng.standard_normal((Hkv, d)).astype(np.float32)).to(dt)
+    k_rows = torch.empty((L, Hkv, d), dtype=dt)
+    k_rows[:n_a] = u
+    k_rows[n_a:] = -u
+    v_rows = torch.from_numpy(rng.standard_normal((L, Hkv, d)).astype(np.float32)).to(dt)
+    nblk = -(-L // bs)
+    nb = nblk + 9
+    table = rng.permutation(nb)[:nblk].astype(np.int32)
+    t = np.arange(L)
+    slots = torch.from_numpy((table[t // bs].astype(np.int64) * bs + t % bs)).to(DEV)
+    k_pool = torch.zeros(nb * Hkv * bs * d, dtype=dt, device=DEV)
+    v_pool = torch.zeros_like(k_pool)
+    print("decode closed form, 16500 tokens", flush=True)
+    pkv.reshape_and_cache(k_rows.reshape(L, Hkv * d).to(DEV), v_rows.reshape(L, Hkv * d).to(DEV), k_pool, v_pool,
+                          slots, nb, Hkv, d)
+    c = [0.0, 3.0, 12.0, -16.0] * Hkv
+    u64 = u.double().numpy()
+    q = torch.stack([torch.from_numpy(c[h] * u64[h // G] / np.dot(u64[h // G], u64[h // G])) for h in range(Hq)])
+    q = q.to(dt)
+    out = torch.empty((1, Hq, d), dtype=torch.float32, device=DEV)
+    ws = torch.empty(pkv.paged_attention_decode_workspace_bytes(1, Hq, d, L) // 4 + 1, dtype=torch.float32,
+                     device=DEV)
+    pkv.paged_attention_decode(out, q[None].to(DEV), k_pool, v_pool, torch.from_numpy(table[None]).to(DEV),
+                               torch.tensor([L], dtype=torch.int32, device=DEV), L, Hkv, nb, scale, ws)
+    torch.cuda.synchronize()
+    got = out[0].double().cpu().numpy()
+    vv = v_rows.double().numpy()
+    q64 = q.double().numpy()
+    atol, rtol = tolerance("bf16", "f32")
+    for h in range(Hq):
+        g = h // G
+        a = scale * float(np.dot(q64[h], u64[g]))
+        sa, sb = vv[:n_a, g].sum(axis=0), vv[n_a:, g].sum(axis=0)
+        exp = (math.exp(a) * sa + math.exp(-a) * sb) / (n_a * math.exp(a) + (L - n_a) * math.exp(-a))
+        assert_close(f"closed form head {h} (a = {a:.3f})", got[h], exp, atol, rtol)
