@@ -66,7 +66,11 @@ extern "C" {
  * pool carries one fp32 scale, a cached value being value(code) * scale. */
 #define PKV_FP8_E4M3 3
 
-/* Text of the last error on this thread ("" after a success). */
+/* Text of the last error on this thread ("" after a success).  A failing
+ * call changes nothing and reports why, so that the caller can react instead
+ * of crashing — as the scheduler of "The skeleton of a scheduler" (LLM
+ * Serving from Scratch) reacts to running out of blocks by preempting.  The
+ * string is owned by the library and valid until this thread's next call. */
 const char* pkv_last_error(void);
 
 /* ------------------------------------------------------------------------
@@ -114,10 +118,17 @@ int paged_kv_alloc(const pkv_pool_desc* desc, pkv_pool** out);
  * num_blocks * n_kv_heads * block_size * head_dim * esize each. */
 int paged_kv_pool_bytes(const pkv_pool_desc* desc, int64_t* k_bytes, int64_t* v_bytes);
 
-/* Free the host state.  Device pools are untouched (the caller owns them). */
+/* Free the host state: the per-sequence block tables and the free block
+ * queue, the small CPU-side bookkeeping of "Back to the queue, and into vLLM
+ * proper" (Life of a prompt).  Device pools are untouched (the caller owns
+ * them).  PKV_EINVAL for NULL; the handle is invalid afterwards. */
 int paged_kv_destroy(pkv_pool* pool);
 
-/* New empty sequence; *seq receives its id (ids count up from 0). */
+/* New empty sequence with an empty block table: a request admitted from the
+ * waiting queue gets its own ordered list of block ids ("admit" in "The
+ * skeleton of a scheduler", LLM Serving from Scratch; the page table of "Back
+ * to the queue, and into vLLM proper", Life of a prompt).  No block is taken
+ * until tokens are appended.  *seq receives its id (ids count up from 0). */
 int paged_kv_seq_create(pkv_pool* pool, int64_t* seq);
 
 /* New sequence that shares the physical blocks holding the parent's first
@@ -239,7 +250,11 @@ int paged_kv_seq_table(pkv_pool* pool, int64_t seq, int32_t* blocks_out, int64_t
 int paged_kv_block_tables(pkv_pool* pool, const int64_t* seqs, int32_t n, int32_t max_blocks,
                           int32_t* tables_out, int32_t* lens_out);
 
-/* Free blocks in the queue. */
+/* Free blocks in the queue (*n): what an admission test such as
+ * can_allocate, or the out_of_blocks check before preempting, compares a
+ * request's needs with ("The skeleton of a scheduler", LLM Serving from
+ * Scratch; the free block queue of "Back to the queue, and into vLLM proper",
+ * Life of a prompt). */
 int paged_kv_num_free(pkv_pool* pool, int64_t* n);
 
 /* Reference count of one block (0 for a free block). */
@@ -370,7 +385,15 @@ int paged_kv_swap_blocks(const void* src_k_pool, const void* src_v_pool, int64_t
 int32_t paged_attention_decode_partition_size(void);
 
 /* Device workspace bytes paged_attention_decode needs for these sizes
- * (0 when every sequence fits in one partition). */
+ * (0 when every sequence fits in one partition): the partial softmax states
+ * (max, sum and unnormalised output, fp32) of every partition of every
+ * (sequence, query head), num_seqs * n_q_heads * ceil(max_context_len /
+ * partition size) * (head_dim + 2) * 4 bytes.  The attention is the decode
+ * step of "The decode stage, and how to spot the waste" (Life of a prompt):
+ * one query against the sequence's full K and V; splitting the context into
+ * partitions whose states are merged afterwards is this library's way of
+ * spreading one long sequence over many compute units (the pages give no
+ * kernel design).  0 for non-positive arguments. */
 int64_t paged_attention_decode_workspace_bytes(int32_t num_seqs, int32_t n_q_heads,
                                                int32_t head_dim, int32_t max_context_len);
 

@@ -380,25 +380,29 @@ __device__ __forceinline__ f32x4 mfma_f16(u32x4 a, u32x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a),
                                                 __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
 }
-// 8 bf16 / f16 values -> 8 fp16 (bf16: round toward zero, exact for values
-// fp16 holds, saturating beyond its range).
-template <typename T>
-__device__ __forceinline__ u32x4 to_f16x8(u32x4 v) {
-  if constexpr (T::kCode == PKV_BF16) {
-    u32x4 r;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      r[i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(bf16lo(v[i]), bf16hi(v[i])));
-    return r;
-  } else {
-    return v;
-  }
-}
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x2v_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
   const f32x2_t v = {lo, hi};
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2v_t));
+}
+typedef __bf16 bf16x2v_t __attribute__((ext_vector_type(2)));
+// two fp32 -> two bf16 (round to nearest even), the first in the low half
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  const f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2v_t));
+}
+__device__ __forceinline__ f32x4 mfma_bf16(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b),
+                                                 c, 0, 0, 0);
+}
+// A probability p as a pair of bf16 values hi + lo with hi = bf16(p) and lo =
+// bf16(p - hi): their sum carries p to about 2^-17 relative, so a bf16 V
+// operand (exact, any finite value) and the pair give two exact-product
+// MFMAs whose sum is p * v to that precision.
+__device__ __forceinline__ void split_bf16x2(float a, float b, uint32_t& hi, uint32_t& lo) {
+  hi = pack_bf16x2(a, b);
+  lo = pack_bf16x2(a - bf16lo(hi), b - bf16hi(hi));
 }
 // Max / sum over lanes l, l^16, l^32, l^48 (the lanes holding one MFMA row).
 __device__ __forceinline__ float rows4_max(float x) {
@@ -486,8 +490,11 @@ struct TokenRows {
 //    into operand layout (key order: see kNatural below).  8-bit keys are
 //    widened to the query's type, and a lane's 16-byte K chunk (16 dims)
 //    feeds two contraction slices; the query operands take the same dims;
-//  * softmax over the wave's keys (base 2), probabilities in fp16;
-//  * O^T += V^T P^T with V loaded into operand layout and widened to fp16;
+//  * softmax over the wave's keys (base 2);
+//  * O^T += V^T P^T with V loaded into operand layout: fp16 V with fp16
+//    probabilities; bf16 V unconverted (any finite value) with each
+//    probability split into a bf16 pair hi + lo, two products per tile;
+//    8-bit V widened exactly to fp16, with fp16 probabilities;
 //    the waves' (max, sum, o) are merged through LDS and written as each
 //    member's partition result (8-bit values: times v_mul, the pool scale).
 template <typename KV, typename QT, int D, int G, int RT, bool Masked, int OutCode, int NH, int NW, typename Rows>
@@ -508,6 +515,7 @@ __device__ __forceinline__ void mfma_partition(const Rows& R, int n, int g, int 
   static_assert(KV::kBytes != 4, "fp32 K/V have no MFMA path");
   constexpr bool kNatural = !F8;
   static_assert(F8 || (KV::kBytes == 2 && KV::kCode == QT::kCode), "16-bit K/V take queries of their type");
+  constexpr bool kSplitP = !F8 && KV::kCode == PKV_BF16;  // bf16 V: exact operand, P as a bf16 pair
   static_assert(Masked || !kCausal, "causal rows need the masked path");
   constexpr int DC = D / 32;                         // 32-dim slices of the score contraction
   constexpr int DT = D / 16;                         // 16-dim tiles of the output
@@ -660,7 +668,10 @@ __device__ __forceinline__ void mfma_partition(const Rows& R, int n, int g, int 
         }
       }
       // exact softmax over the wave's keys, per row (running over the parts)
+      // bf16 V is kept exact: P goes to the matrix cores as a bf16 pair
+      // (hi, lo), two products per tile; fp16 and 8-bit V take fp16 P
       u32x4 pb[HB / 2][RT];
+      u32x4 pbl[kSplitP ? HB / 2 : 1][RT];
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) {
         float mx = -INFINITY;
@@ -699,10 +710,21 @@ __device__ __forceinline__ void mfma_partition(const Rows& R, int n, int g, int 
         // B operand of the pair: the lane's four keys of tile 2 kp, then of 2 kp + 1
 #pragma unroll
         for (int kp = 0; kp < HB / 2; ++kp)
-          pb[kp][rt] = u32x4{pack_f16x2(st[2 * kp][rt][0], st[2 * kp][rt][1]),
-                             pack_f16x2(st[2 * kp][rt][2], st[2 * kp][rt][3]),
-                             pack_f16x2(st[2 * kp + 1][rt][0], st[2 * kp + 1][rt][1]),
-                             pack_f16x2(st[2 * kp + 1][rt][2], st[2 * kp + 1][rt][3])};
+          if constexpr (kSplitP) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              uint32_t hi, lo;
+              split_bf16x2(st[2 * kp + (e >> 1)][rt][2 * (e & 1)], st[2 * kp + (e >> 1)][rt][2 * (e & 1) + 1], hi,
+                           lo);
+              pb[kp][rt][e] = hi;
+              pbl[kp][rt][e] = lo;
+            }
+          } else {
+            pb[kp][rt] = u32x4{pack_f16x2(st[2 * kp][rt][0], st[2 * kp][rt][1]),
+                               pack_f16x2(st[2 * kp][rt][2], st[2 * kp][rt][3]),
+                               pack_f16x2(st[2 * kp + 1][rt][0], st[2 * kp + 1][rt][1]),
+                               pack_f16x2(st[2 * kp + 1][rt][2], st[2 * kp + 1][rt][3])};
+          }
       }
       // O^T += V^T P^T over each pair's 32 keys
 #pragma unroll
@@ -728,10 +750,18 @@ __device__ __forceinline__ void mfma_partition(const Rows& R, int n, int g, int 
                   vv[2 * half + e] &= 2 * e + 1 < nv ? 0xffffffffu : (2 * e < nv ? 0x0000ffffu : 0u);
               }
             }
-            va = to_f16x8<KV>(vv);
+            va = vv;  // f16 V as it is; bf16 V with the split probabilities
           }
+          if constexpr (kSplitP) {
 #pragma unroll
-          for (int rt = 0; rt < RT; ++rt) o[rt][dt] = mfma_f16(va, pb[kp][rt], o[rt][dt]);
+            for (int rt = 0; rt < RT; ++rt) {
+              o[rt][dt] = mfma_bf16(va, pb[kp][rt], o[rt][dt]);
+              o[rt][dt] = mfma_bf16(va, pbl[kp][rt], o[rt][dt]);
+            }
+          } else {
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) o[rt][dt] = mfma_f16(va, pb[kp][rt], o[rt][dt]);
+          }
         }
     }
   } else {
@@ -775,6 +805,10 @@ __device__ __forceinline__ void mfma_partition(const Rows& R, int n, int g, int 
   __syncthreads();
   for (int i = tid; i < rows * D; i += NW * 64) {
     const int row = i / D, j = i % D;
+    // a causal row whose keys all lie in earlier partitions has no result
+    // here: the partitions that hold its keys write it (its partition count
+    // is at most p)
+    if (kCausal && p >= sh.row_parts[row]) continue;
     float acc = 0.f;
 #pragma unroll
     for (int x = 0; x < NW; ++x) acc = fmaf(sh.wgt[row][x], sh.o[x][row][j], acc);

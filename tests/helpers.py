@@ -68,12 +68,29 @@ def prefill_reference(w, c, rows=None, n_threads=8):
 FP8_K_SCALE, FP8_V_SCALE = 0.0125, 0.0103
 
 
+_QTABLES = {}
+
+
+def _quantise(dtype, bits, scale):
+    """The oracle's E4M3 quantiser applied to raw 16-bit (or fp32) rows.  A
+    16-bit element has at most 65536 bit patterns, so the quantiser runs once
+    on every pattern and the rows are looked up in that table (the same
+    function values; the oracle's exhaustive search is slow per element)."""
+    if dtype == "f32":
+        return oracle.quantize_e4m3(oracle.decode(dtype, bits).astype(np.float32), scale)
+    key = (dtype, float(scale))
+    if key not in _QTABLES:
+        pats = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+        _QTABLES[key] = oracle.quantize_e4m3(oracle.decode(dtype, pats).astype(np.float32), scale)
+    return _QTABLES[key][np.ascontiguousarray(bits).view(np.uint16)]
+
+
 def quantised_kv(w, kind, idx, t0, t1, k_scale=FP8_K_SCALE, v_scale=FP8_V_SCALE):
     """Dequantised fp64 K/V of positions [t0, t1): the workload's rows put
     through the oracle's E4M3 quantiser and read back with the scales."""
     k, v = w.kv(kind, idx, t0, t1)
-    kq = oracle.quantize_e4m3(oracle.decode(w.dtype, k).astype(np.float32), k_scale)
-    vq = oracle.quantize_e4m3(oracle.decode(w.dtype, v).astype(np.float32), v_scale)
+    kq = _quantise(w.dtype, k, k_scale)
+    vq = _quantise(w.dtype, v, v_scale)
     return oracle.dequantize_e4m3(kq, k_scale), oracle.dequantize_e4m3(vq, v_scale)
 
 
@@ -96,3 +113,32 @@ def prefill_reference_fp8(w, c, rows=None, k_scale=FP8_K_SCALE, v_scale=FP8_V_SC
     qb = w.q("chunk", c, ctx, ctx + ql)[rows]
     out, _ = oracle.attention(oracle.decode(w.dtype, qb), ctx + rows, k, v, w.scale, n_threads=n_threads)
     return out
+
+
+def oracle_workers() -> int:
+    """Host threads for the oracle in the GPU tests: the machine's CPU share is
+    16 threads, whatever os.cpu_count() reports."""
+    import os
+    return max(1, min(os.cpu_count() or 1, 16))
+
+
+def decode_references(w, seqs, fp8=False):
+    """Oracle outputs {s: [Hq, d]} for many decode sequences of w: each
+    sequence's K/V are regenerated on the host and its oracle run in a worker
+    thread (the oracle's C loops and numpy's large-array work release the
+    interpreter lock)."""
+    from concurrent.futures import ThreadPoolExecutor
+    ref = decode_reference_fp8 if fp8 else decode_reference
+    seqs = list(seqs)
+    if fp8 and w.dtype != "f32":  # fill the quantiser's tables before the threads start
+        _quantise(w.dtype, np.zeros(1, np.uint16), FP8_K_SCALE)
+        _quantise(w.dtype, np.zeros(1, np.uint16), FP8_V_SCALE)
+    with ThreadPoolExecutor(oracle_workers()) as ex:
+        return dict(zip(seqs, ex.map(lambda s: ref(w, s), seqs)))
+
+
+def prefill_references(w, chunks, fp8=False):
+    """Oracle outputs {c: [q_len, Hq, d]} for every row of the given chunks
+    (the oracle's own threads split each chunk's rows and heads)."""
+    ref = prefill_reference_fp8 if fp8 else prefill_reference
+    return {c: ref(w, c, n_threads=oracle_workers()) for c in chunks}
