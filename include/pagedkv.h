@@ -461,6 +461,31 @@ int paged_attention_decode_append(void* out, int32_t out_dtype, const void* q, c
                                   int32_t kv_dtype, void* workspace, int64_t workspace_bytes,
                                   void* stream);
 
+/* paged_attention_decode_append for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): the same arguments without the workspace, the same
+ * results.  The split-context partials go to a scratch array the library
+ * holds in device memory, one copy per GPU, of
+ * paged_attention_decode_noalloc_max_workspace_bytes() bytes (64 MiB); its
+ * address is looked up on the first call on each device (the current device,
+ * which must be the one `stream` belongs to).  PKV_EINVAL when
+ * paged_attention_decode_workspace_bytes(num_seqs, n_q_heads, head_dim,
+ * max_context_len) exceeds it.  Nothing is allocated.  Every call on one GPU
+ * shares that GPU's scratch, so calls that overlap on one GPU (different
+ * streams, or threads without ordering) race; calls queued on one stream are
+ * ordered and safe. */
+int paged_attention_decode_append_noalloc(void* out, int32_t out_dtype, const void* q, const void* k_new,
+                                          const void* v_new, int64_t k_new_stride, int64_t v_new_stride,
+                                          const int64_t* slot_mapping, void* k_pool, void* v_pool,
+                                          const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                          const int32_t* context_lens, int32_t num_seqs, int32_t n_q_heads,
+                                          int32_t n_kv_heads, int32_t head_dim, int32_t block_size,
+                                          int64_t num_blocks, int32_t max_context_len, float scale,
+                                          int32_t kv_dtype, void* stream);
+
+/* Bytes of the scratch paged_attention_decode_append_noalloc uses per GPU. */
+int64_t paged_attention_decode_noalloc_max_workspace_bytes(void);
+
 /* Decode attention over an 8-bit cache (PKV_FP8_E4M3 pools written by
  * reshape_and_cache_fp8): the same result as paged_attention_decode with
  * every cached key and value replaced by value(code) * k_scale (resp.
@@ -589,8 +614,9 @@ int64_t paged_attention_verify_workspace_bytes(int32_t total_q, int32_t n_q_head
  * cu_q_lens[c] .. cu_q_lens[c+1]-1 of q / out, query i at absolute position
  * context_lens[c] - q_len + i, keys already appended), computed the way a
  * decode step is: 512-token split-context partitions read once per KV head
- * for all of the sequence's new tokens (MFMA, fp32 accumulation, fp16
- * probabilities), partial states merged per token.
+ * for all of the sequence's new tokens (MFMA, fp32 accumulation; bf16 values
+ * are exact operands with each probability split into a bf16 pair, fp16
+ * values take fp16 probabilities), partial states merged per token.
  *   workspace  device, >= paged_attention_verify_workspace_bytes(total_q,
  *              n_q_heads, head_dim, max_context_len) bytes (NULL when 0).
  * Supported: kv_dtype PKV_F16 or PKV_BF16 (out PKV_F32 or kv_dtype),

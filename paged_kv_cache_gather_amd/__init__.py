@@ -106,6 +106,9 @@ _sig("paged_attention_decode_fp8_append", ctypes.c_int, _P, _i32, _P, _i32, _P, 
      _f32, _P, _i32, _P, _i32, _i32, _i32, _i32, _i32, _i64, _i32, _f32, _P, _i64, _P)
 _sig("paged_attention_decode_append", ctypes.c_int, _P, _i32, _P, _P, _P, _i64, _i64, _P, _P, _P, _P, _i32, _P,
      _i32, _i32, _i32, _i32, _i32, _i64, _i32, _f32, _i32, _P, _i64, _P)
+_sig("paged_attention_decode_append_noalloc", ctypes.c_int, _P, _i32, _P, _P, _P, _i64, _i64, _P, _P, _P, _P, _i32,
+     _P, _i32, _i32, _i32, _i32, _i32, _i64, _i32, _f32, _i32, _P)
+_sig("paged_attention_decode_noalloc_max_workspace_bytes", _i64)
 for _n in ("paged_attention_decode_partitions", "paged_attention_decode_reduce"):
     _sig(_n, ctypes.c_int, _P, _i32, _P, _P, _P, _P, _i32, _P, _i32, _i32, _i32, _i32, _i32, _i64, _i32, _f32,
          _i32, _P, _i64, _P)
@@ -604,6 +607,46 @@ def paged_attention_decode_append(out: torch.Tensor, q: torch.Tensor, k_new: tor
         _ptr(context_lens), B, Hq, n_kv_heads, d, block_size, num_blocks, max_context_len, float(scale),
         dtype_code(k_pool.dtype), _ptr(workspace), ws_bytes, _stream(stream, q.device)))
 
+def paged_attention_decode_noalloc_max_workspace_bytes() -> int:
+    return int(_lib.paged_attention_decode_noalloc_max_workspace_bytes())
+
+
+def paged_attention_decode_append_noalloc(out: torch.Tensor, q: torch.Tensor, k_new: torch.Tensor,
+                                          v_new: torch.Tensor, slot_mapping: torch.Tensor, k_pool: torch.Tensor,
+                                          v_pool: torch.Tensor, block_tables: torch.Tensor,
+                                          context_lens: torch.Tensor, max_context_len: int, n_kv_heads: int,
+                                          num_blocks: int, scale: float, block_size: int = BLOCK_SIZE, stream=None):
+    """paged_attention_decode_append without a workspace argument: the
+    library's own per-GPU scratch holds the split-context partials and nothing
+    is allocated (same arguments otherwise)."""
+    _dev(out, "out")
+    _dev(q, "q", k_pool.dtype)
+    _dev(k_pool, "k_pool")
+    _dev(v_pool, "v_pool", k_pool.dtype)
+    _dev(block_tables, "block_tables", torch.int32)
+    _dev(context_lens, "context_lens", torch.int32)
+    _dev(slot_mapping, "slot_mapping", torch.int64)
+    _dev(k_new, "k_new", k_pool.dtype, contiguous=False)
+    _dev(v_new, "v_new", k_pool.dtype, contiguous=False)
+    if q.dim() != 3 or out.shape != q.shape:
+        raise PagedKVError(PKV_EINVAL, "q and out must be [num_seqs, n_q_heads, head_dim]")
+    B, Hq, d = q.shape
+    if block_tables.dim() != 2 or block_tables.shape[0] != B or context_lens.numel() != B:
+        raise PagedKVError(PKV_EINVAL, "block_tables/context_lens must have one row per sequence")
+    if slot_mapping.numel() != B or k_new.shape[0] != B or v_new.shape[0] != B:
+        raise PagedKVError(PKV_EINVAL, "k_new, v_new and slot_mapping must have one row per sequence")
+    for t, name in ((k_new, "k_new"), (v_new, "v_new")):
+        if t[0].numel() != n_kv_heads * d or (t.dim() > 1 and not t[0].is_contiguous()):
+            raise PagedKVError(PKV_EINVAL, f"{name} rows must be contiguous [n_kv_heads*head_dim]")
+    need = num_blocks * n_kv_heads * block_size * d
+    if k_pool.numel() < need or v_pool.numel() < need:
+        raise PagedKVError(PKV_EINVAL, "pool tensors smaller than num_blocks blocks")
+    _check(_lib.paged_attention_decode_append_noalloc(
+        _ptr(out), dtype_code(out.dtype), _ptr(q), _ptr(k_new), _ptr(v_new), k_new.stride(0), v_new.stride(0),
+        _ptr(slot_mapping), _ptr(k_pool), _ptr(v_pool), _ptr(block_tables), block_tables.shape[1],
+        _ptr(context_lens), B, Hq, n_kv_heads, d, block_size, num_blocks, max_context_len, float(scale),
+        dtype_code(k_pool.dtype), _stream(stream, q.device)))
+
 
 def paged_attention_decode_partitions(out, q, k_pool, v_pool, block_tables, context_lens, max_context_len,
                                       n_kv_heads, num_blocks, scale, workspace=None,
@@ -825,3 +868,4 @@ def paged_attention_prefill_chunk(out: torch.Tensor, q: torch.Tensor, k_pool: to
 
 __all__ = [n for n in dir() if n.startswith(("paged_", "reshape_", "pkv", "PKV_", "Pool", "PagedKV",
                                                  "OutOfBlocks", "last_error", "dtype_code", "BLOCK_SIZE"))]
+

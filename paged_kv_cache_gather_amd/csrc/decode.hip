@@ -52,6 +52,7 @@
 #include <math.h>
 
 #include <cmath>
+#include <mutex>
 #include <string>
 #include <type_traits>
 
@@ -1451,6 +1452,71 @@ extern "C" int paged_attention_decode_append(void* out, int32_t out_dtype, const
                      block_tables, max_blocks_per_seq, context_lens, num_seqs, n_q_heads, n_kv_heads, head_dim,
                      block_size, num_blocks, max_context_len, scale, kv_dtype, workspace, workspace_bytes, stream,
                      &app);
+}
+
+// ---- the decode step for callers that cannot allocate ----------------------
+// paged_attention_decode_append with its workspace (the split-context
+// partials) in device memory the library itself holds: a file-scope array,
+// one copy per GPU, present from the moment the library's code is loaded on
+// that GPU until the process ends.  Host code never names the array in a
+// kernel argument or copy: its device address is looked up once per device
+// (hipGetSymbolAddress, with that device current) and that address is used.
+// Nothing in it must start at zero: every partial a merge reads is written by
+// the same call's partition pass first.
+namespace {
+constexpr int64_t kNoAllocScratchBytes = 64ll << 20;
+constexpr int kMaxDevices = 64;
+}  // namespace
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[kMaxDevices];
+
+// Device address of this GPU's scratch, looked up on the first call per
+// device (the current device: the one the caller's stream belongs to).
+static int scratch_for_current_device(const std::string& F, void** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(PKV_EHIP, F + ": hipGetDevice: " + hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(PKV_EUNSUPPORTED, F + ": device index beyond 63");
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(PKV_EHIP, F + ": hipGetSymbolAddress(scratch): " + hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return ok();
+}
+
+extern "C" int64_t paged_attention_decode_noalloc_max_workspace_bytes(void) { return kNoAllocScratchBytes; }
+
+extern "C" int paged_attention_decode_append_noalloc(void* out, int32_t out_dtype, const void* q, const void* k_new,
+                                                     const void* v_new, int64_t k_new_stride, int64_t v_new_stride,
+                                                     const int64_t* slot_mapping, void* k_pool, void* v_pool,
+                                                     const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                                     const int32_t* context_lens, int32_t num_seqs,
+                                                     int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
+                                                     int32_t block_size, int64_t num_blocks,
+                                                     int32_t max_context_len, float scale, int32_t kv_dtype,
+                                                     void* stream) {
+  const std::string F("paged_attention_decode_append_noalloc");
+  const int64_t need = paged_attention_decode_workspace_bytes(num_seqs, n_q_heads, head_dim, max_context_len);
+  if (need > kNoAllocScratchBytes)
+    return fail(PKV_EINVAL, F + ": the split-context partials need " + std::to_string(need) +
+                                " bytes, more than the library's " + std::to_string(kNoAllocScratchBytes) +
+                                "-byte scratch (use paged_attention_decode_append with a workspace)");
+  void* ws = nullptr;
+  if (need > 0) {
+    const int rc = scratch_for_current_device(F, &ws);
+    if (rc != PKV_OK) return rc;
+  }
+  return paged_attention_decode_append(out, out_dtype, q, k_new, v_new, k_new_stride, v_new_stride, slot_mapping,
+                                       k_pool, v_pool, block_tables, max_blocks_per_seq, context_lens, num_seqs,
+                                       n_q_heads, n_kv_heads, head_dim, block_size, num_blocks, max_context_len,
+                                       scale, kv_dtype, ws, need > 0 ? kNoAllocScratchBytes : 0, stream);
 }
 
 extern "C" int paged_attention_decode(PKV_DECODE_PARAMS) {
