@@ -9,22 +9,24 @@ over a 32768-block pool.  One step = append each sequence's new token
 (reshape_and_cache) + paged decode attention (partition pass + split-K
 reduce), inputs resident in HBM.
 
-Prints one JSON line: decode tokens/s (one layer; the step as one
-paged_attention_decode_append call, whose cache write rides in the
-shared-run launch — the three separate calls and the one call replayed from
-a HIP graph are reported beside it) with the partition pass's achieved HBM bandwidth
-against the 8 TB/s peak, and the fp64 oracle timed on a bounded sample of the
-same batch on the host cores.  The partition pass is
-two kernels queued back to back on the caller's stream: decode_shared_kernel
-(partitions whose blocks neighbouring sequences share, read once for all of
-them) and decode_partition_kernel (every other partition); it is timed with
-HIP events around the whole pass.  The JSON also carries the same step over
-an 8-bit (E4M3) cache (fp8_kv_decode: rows quantised on the way in, half the
-bytes per step), the swap copies of 32 sequences between HBM and pinned host
-blocks (swap), verify attention of 5 new tokens per sequence (verify), and
-the mixed chunked-prefill + decode step.
+Timing: before every timed step a 1 GiB device read evicts the L2 caches
+and the 256 MB Infinity Cache (outside the timed events), so K/V come from
+HBM as they would between the layers of a forward pass; each step is
+bracketed by HIP events on the stream it runs on.  Prints one JSON line:
+decode tokens/s for one layer (batch / mean step time, the step being one
+paged_attention_decode_append call, whose cache write rides in the shared-run
+launch), with the partition pass's achieved HBM bandwidth against the
+8 TB/s peak (the pass is decode_shared_kernel then decode_partition_kernel,
+timed together with events in the three-call form of the step).  Beside it:
+the same timings with warm caches, read-only bandwidth ceilings over the
+batch's tiles, the fp64 oracle timed on the host cores (gather + attention
+from host pools, all sequences on one thread per core and a sample on one
+thread), the same step over an 8-bit (E4M3) cache, the toy, TinyLlama- and
+OPT-13B-shaped decode batches with their own rooflines, the swap copies of 32
+sequences, verify attention of 5 new tokens per sequence, and the mixed
+chunked-prefill + decode step with the prefill kernel's MFMA fraction.
 
-  python bench.py [--steps K] [--warmup W] [--workload 2|3|4] [--no-cpu-baseline] [--no-fp8] [--no-mixed]
+  python bench.py [--steps K] [--warmup W] [--workload 2|3|4] [--no-cpu-baseline] [--no-fp8] [--no-mixed] ...
   python bench.py --copy-calibration     # plain device copy of a known size
 """
 import argparse
@@ -112,9 +114,10 @@ def prefill_flops(w):
     return 4 * w.head_dim * w.n_q_heads * pairs, pairs
 
 
-def mixed_step(steps, warmup, seed):
+def mixed_step(steps, warmup, seed, flush):
     """The mixed chunked-prefill + decode step (16 chunks of 512 queries and
-    240 decodes): append both, then prefill attention and decode attention."""
+    240 decodes): append both, then prefill attention and decode attention,
+    each timed step after a cache flush."""
     import numpy as np
     import torch
     import synth
@@ -140,11 +143,11 @@ def mixed_step(steps, warmup, seed):
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
     for i in range(steps):
+        flush()
         step(ev[i])
     torch.cuda.synchronize()
-    ms = (time.perf_counter() - t0) * 1e3 / steps
+    ms = float(np.mean([e[0].elapsed_time(e[4]) for e in ev]))
     pre = np.array([e[1].elapsed_time(e[2]) for e in ev])
     dpart = np.array([e[2].elapsed_time(e[3]) for e in ev])
     flops, pairs = prefill_flops(w)
@@ -316,7 +319,7 @@ def verify_bytes(b, kv_elem_bytes=None):
             "algorithmic_bytes": kv + other}
 
 
-def verify_leg(steps, warmup, seed, k=5):
+def verify_leg(steps, warmup, seed, flush, k=5):
     """Checking k drafted tokens per sequence (k + 1 - 1 = k new query tokens
     each) on the Llama-3-8B-shaped batch: 256 sequences with the decode
     batch's context lengths; one step = append the new tokens + verify
@@ -350,6 +353,7 @@ def verify_leg(steps, warmup, seed, k=5):
         step()
     torch.cuda.synchronize()
     for i in range(steps):
+        flush()
         step(ev[i])
     torch.cuda.synchronize()
     app = np.array([e[0].elapsed_time(e[1]) for e in ev]) * 1e3
@@ -372,11 +376,11 @@ def verify_leg(steps, warmup, seed, k=5):
            "bytes": by}
     del b, out
     torch.cuda.empty_cache()
-    res["fp8"] = verify_fp8(w, steps, warmup)
+    res["fp8"] = verify_fp8(w, steps, warmup, flush)
     return res
 
 
-def verify_fp8(w, steps, warmup):
+def verify_fp8(w, steps, warmup, flush):
     """The same verify step over 8-bit (E4M3) pools: the new rows quantised
     by reshape_and_cache_fp8, then paged_attention_verify_fp8."""
     import numpy as np
@@ -399,6 +403,7 @@ def verify_fp8(w, steps, warmup):
         step()
     torch.cuda.synchronize()
     for i in range(steps):
+        flush()
         step(ev[i])
     torch.cuda.synchronize()
     app = np.array([e[0].elapsed_time(e[1]) for e in ev]) * 1e3
@@ -413,34 +418,83 @@ def verify_fp8(w, steps, warmup):
            "breakdown_us": {"append": float(app.mean()), "verify": float(ver.mean())},
            "roofline": {"bound": "hbm", "kernel": "verify_partition_kernel<FP8, ...> + decode_reduce_kernel",
                         "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": ach / HBM_PEAK_GBS,
-                        "traffic": None, "algorithmic_bytes": by["algorithmic_bytes"]},
+                        "traffic": (profiled_traffic("verify_fp8_llama3_8b_verify", ["decode.hip", "pkv_device.h"])
+                                    if w.seed == 0 else None),
+                        "algorithmic_bytes": by["algorithmic_bytes"]},
            "bytes": by}
     del b, out
     torch.cuda.empty_cache()
     return res
 
 
-def cpu_baseline(w, n_seqs):
-    """The fp64 oracle (as it stands) on every k-th sequence of the batch."""
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(w, tables, sample_1thread=32):
+    """The fp64 oracle as it stands, timed on the host: for each decode
+    sequence, gather its K/V from host copies of the pools through its block
+    table (oracle.gather) and run the attention (oracle.attention).  The host
+    pools are written by the oracle's own scatter from the seeded generator's
+    rows (not timed).  Timed twice: every sequence with one worker thread per
+    host core (up to 16, the GPU machine's share), and a sample on one thread."""
     import numpy as np
+    from concurrent.futures import ThreadPoolExecutor
     import oracle
     threads = max(1, min(os.cpu_count() or 1, 16))
-    stride = max(1, w.n_decode // n_seqs)
-    sample = list(range(0, w.n_decode, stride))[:n_seqs]
-    inputs = []
-    for s in sample:
-        L = int(w.decode_lens[s])
+    H, d, bs = w.n_kv_heads, w.head_dim, 16
+    pool_elems = w.num_blocks * H * bs * d
+    cont = np.uint32 if w.dtype == "f32" else np.uint16
+    kp, vp = np.zeros(pool_elems, cont), np.zeros(pool_elems, cont)
+    lens = w.decode_lens.astype(np.int64)
+
+    def fill(s):
+        L = int(lens[s])
         k, v = w.kv("decode", s, 0, L)
-        inputs.append((w.q("decode", s, L - 1, L), k, v, L))
+        t = np.arange(L)
+        slots = tables[s, t // bs].astype(np.int64) * bs + t % bs
+        oracle.scatter(w.dtype, k, v, kp, vp, slots, w.num_blocks, bs, H, d)
+        return oracle.decode(w.dtype, w.q("decode", s, L - 1, L))
+
     t0 = time.perf_counter()
-    for q, k, v, L in inputs:
-        oracle.attention(oracle.decode(w.dtype, q), [L - 1], oracle.decode(w.dtype, k), oracle.decode(w.dtype, v),
-                         w.scale, n_threads=threads)
-    dt = time.perf_counter() - t0
-    toks = int(sum(x[3] for x in inputs))
-    return {"value": len(sample) / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"{len(sample)} of {w.n_decode} decode sequences (every {stride}th, {toks} context "
-                      f"tokens), fp64 decode+attention from contiguous K/V, {dt:.2f} s"}
+    with ThreadPoolExecutor(threads) as ex:
+        qs = list(ex.map(fill, range(w.n_decode)))  # shared prefix blocks get the same bytes from every member
+    t_fill = time.perf_counter() - t0
+
+    def one(s):
+        L = int(lens[s])
+        k, v = oracle.gather(w.dtype, kp, vp, w.num_blocks, bs, H, d, tables[s, :-(-L // bs)], L)
+        out, _ = oracle.attention(qs[s], [L - 1], k, v, w.scale)
+        return out
+
+    t0 = time.perf_counter()
+    with ThreadPoolExecutor(threads) as ex:
+        list(ex.map(one, range(w.n_decode)))
+    t_all = time.perf_counter() - t0
+    stride = max(1, w.n_decode // sample_1thread)
+    sample = list(range(0, w.n_decode, stride))[:sample_1thread]
+    t0 = time.perf_counter()
+    for s in sample:
+        one(s)
+    t_one = time.perf_counter() - t0
+    toks = int(lens.sum())
+    log(f"oracle: {w.n_decode} sequences on {threads} threads in {t_all:.2f} s "
+        f"({w.n_decode / t_all:.1f} tokens/s); {len(sample)} on 1 thread in {t_one:.2f} s "
+        f"({len(sample) / t_one:.2f} tokens/s); host cores {os.cpu_count()} ({_cpu_model()})")
+    return {"value": w.n_decode / t_all, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"all {w.n_decode} decode sequences of {w.name} ({toks} context tokens): fp64 gather "
+                      f"from host pools through the block tables + attention, one worker thread per core, "
+                      f"{t_all:.2f} s",
+            "host_cpu_count": os.cpu_count(), "cpu_model": _cpu_model(),
+            "one_thread": {"value": len(sample) / t_one, "unit": "tokens/s", "cores": 1,
+                           "sample": f"{len(sample)} sequences (every {stride}th), {t_one:.2f} s"},
+            "host_pool_fill_s": t_fill}
 
 
 def copy_calibration():
@@ -454,10 +508,45 @@ def copy_calibration():
     log(f"copied {n} bytes x5")
 
 
-def time_decode(b, out, K, W):
-    """W untimed then K timed decode steps of batch b: append the new tokens,
-    then the partition pass and the reduce, with HIP events between them on
-    the stream they run on."""
+class CacheFlush:
+    """Evicts L2 (8 x 4 MB) and the 256 MB Infinity Cache before a timed
+    step, outside the timed events, so the step reads its K/V from HBM as it
+    would between the layers of a forward pass.  The default reads a 1 GiB
+    device buffer (paged_kv_read_tiles, contiguous): the caches end up full of
+    clean lines of unrelated data.  mode="write" writes the buffer instead,
+    which also evicts but leaves up to ~290 MB of dirty lines that are
+    written back while the timed step runs (reported beside the headline,
+    not as it)."""
+
+    def __init__(self, device="cuda:0", nbytes=1 << 30, mode="read"):
+        import torch
+        self.buf = torch.ones(nbytes, dtype=torch.uint8, device=device)
+        self.sink = torch.zeros(1, dtype=torch.int32, device=device)
+        self.mode = mode
+        self.i = 0
+
+    def __call__(self):
+        import paged_kv_cache_gather_amd as pkv
+        if self.mode == "write":
+            self.i ^= 1
+            self.buf.fill_(self.i)
+        else:
+            n = self.buf.numel() // 4096
+            pkv.paged_kv_read_tiles(self.buf, None, None, n, n, 4096, self.sink)
+
+
+def _stats_us(ms):
+    import numpy as np
+    us = np.asarray(ms) * 1e3
+    return {"mean": float(us.mean()), "median": float(np.median(us)), "p10": float(np.percentile(us, 10)),
+            "p90": float(np.percentile(us, 90))}
+
+
+def time_decode(b, out, K, W, flush=None):
+    """W untimed then K timed decode steps of batch b as three calls: append
+    the new tokens, then the partition pass and the reduce, with HIP events
+    between them on the stream they run on.  With flush, the caches are
+    flushed before every step (outside the events)."""
     import numpy as np
     import torch
     stream = torch.cuda.current_stream()
@@ -479,30 +568,45 @@ def time_decode(b, out, K, W):
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(K):
+        if flush is not None:
+            flush()
         step(ev[i])
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    return {"ms_step": (t1 - t0) * 1e3 / K,
+    return {"wall_ms_step": (t1 - t0) * 1e3 / K,
+            "step_ms": np.array([ev[i][0].elapsed_time(ev[i][3]) for i in range(K)]),
             "part_ms": np.array([ev[i][1].elapsed_time(ev[i][2]) for i in range(K)]),
             "append_ms": np.array([ev[i][0].elapsed_time(ev[i][1]) for i in range(K)]),
             "reduce_ms": np.array([ev[i][2].elapsed_time(ev[i][3]) for i in range(K)])}
 
 
-def fused_step(b, out, K, W):
-    """The step in one call (paged_attention_decode_append: the new rows'
-    cache write rides in the shared-run launch, then the per-sequence pass and
-    the merge): W untimed and K timed eager steps, then the same step captured
-    once in a HIP graph and replayed K times back to back, each timed as wall
-    clock between two synchronisations (HIP events around the replays too)."""
+def fused_step(b, out, K, W, flush):
+    """The step in one call (paged_attention_decode_append or its 8-bit
+    variant: the new rows' cache write rides in the shared-run launch, then
+    the per-sequence pass and the merge).  Timed three ways: K eager steps,
+    each after a cache flush, with HIP events around each step (the
+    headline); K eager steps back to back, wall clock between two
+    synchronisations (caches warm from the previous step); and the step
+    captured once in a HIP graph, replayed K times after flushes (events)."""
+    import numpy as np
     import torch
+    st = torch.cuda.current_stream()
     for _ in range(W):
         b.step_decode(out)
     torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    for i in range(K):
+        flush()
+        ev[i][0].record(st)
+        b.step_decode(out)
+        ev[i][1].record(st)
+    torch.cuda.synchronize()
+    flushed = np.array([e0.elapsed_time(e1) for e0, e1 in ev])
     t0 = time.perf_counter()
     for _ in range(K):
         b.step_decode(out)
     torch.cuda.synchronize()
-    eager_us = (time.perf_counter() - t0) * 1e6 / K
+    warm_us = (time.perf_counter() - t0) * 1e6 / K
     side = torch.cuda.Stream()  # default priority
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
@@ -515,16 +619,15 @@ def fused_step(b, out, K, W):
     for _ in range(3):
         graph.replay()
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0 = time.perf_counter()
-    e0.record()
-    for _ in range(K):
+    for i in range(K):
+        flush()
+        ev[i][0].record(st)
         graph.replay()
-    e1.record()
+        ev[i][1].record(st)
     torch.cuda.synchronize()
-    us = (time.perf_counter() - t0) * 1e6 / K
-    return {"us_per_step": us, "event_us_per_step": e0.elapsed_time(e1) * 1e3 / K,
-            "tokens_per_s": b.w.n_decode / (us * 1e-6), "steps": K, "eager_us_per_step": eager_us}
+    graph_flushed = np.array([e0.elapsed_time(e1) for e0, e1 in ev])
+    return {"flushed_us": _stats_us(flushed), "back_to_back_wall_us": warm_us,
+            "graph_flushed_us": _stats_us(graph_flushed)}
 
 
 # scales of the 8-bit leg: the synthetic values are standard normal quantiles
@@ -532,48 +635,122 @@ def fused_step(b, out, K, W):
 FP8_K_SCALE, FP8_V_SCALE = 0.0125, 0.0103
 
 
-def fp8_decode_leg(w, K, W, out_dtype, seed, modes=True):
-    """The same decode step over an 8-bit (E4M3) cache: the new rows are
-    quantised on the way in, the partition pass reads half the bytes
-    (decode_shared_kernel + decode_fp8_partition_kernel).  The step is one
-    paged_attention_decode_fp8_append call (the quantising write rides in the
-    shared-run launch); the three-call run (reshape_and_cache_fp8, partition
-    pass, merge, with events between them) gives the breakdown and the
-    roofline."""
+def decode_leg(w, K, W, out_dtype, seed, flush, fp8=False, modes=True, profile=None):
+    """One decode workload: build the batch on the device, then time the
+    step.  The step is one paged_attention_decode_append call (or its 8-bit
+    variant), K times after a cache flush each, with HIP events around each
+    step: tokens/s = B / mean step time.  The three-call form (append,
+    partition pass, merge, events between them) gives the breakdown and the
+    partition pass's roofline, flushed as well; the same without flushes and
+    the one call back to back (wall clock) and from a HIP graph are reported
+    beside it."""
     import torch
     from paged_kv_cache_gather_amd.batch import DeviceBatch
-    b = DeviceBatch(w, "cuda:0", fill="device", out_dtype=out_dtype, kv_cache="fp8_e4m3", k_scale=FP8_K_SCALE,
-                    v_scale=FP8_V_SCALE)
+    kw = dict(kv_cache="fp8_e4m3", k_scale=FP8_K_SCALE, v_scale=FP8_V_SCALE) if fp8 else {}
+    log(f"building {w.name}{' (8-bit cache)' if fp8 else ''}: {w.description}")
+    b = DeviceBatch(w, "cuda:0", fill="device", out_dtype=out_dtype, **kw)
     out = b.new_decode_out()
-    t = time_decode(b, out, K, W)
+    t = time_decode(b, out, K, W, flush)
+    warm = time_decode(b, out, K, 2)
+    wflush = time_decode(b, out, K, 2, CacheFlush(mode="write") if flush is not None else None)
     by = decode_bytes(b)
-    part_us = float(t["part_ms"].mean()) * 1e3
-    achieved = by["algorithmic_bytes"] / (part_us * 1e-6) / 1e9
-    ms_step = t["ms_step"]
-    g = fused_step(b, out, K, W) if modes else None
-    if g:
-        ms_step = g["eager_us_per_step"] * 1e-3
-    log(f"fp8 cache: step {ms_step * 1e3:.1f} us | three calls {t['ms_step'] * 1e3:.1f} us: append "
-        f"{t['append_ms'].mean() * 1e3:.1f} us | partitions {part_us:.1f} us = {achieved:.0f} GB/s "
-        f"({achieved / HBM_PEAK_GBS:.1%}) | reduce {t['reduce_ms'].mean() * 1e3:.1f} us")
-    res = {"kv_cache": "fp8_e4m3 (OCP E4M3, one fp32 scale per pool)", "k_scale": FP8_K_SCALE,
-           "v_scale": FP8_V_SCALE, "ms_per_step": ms_step, "tokens_per_s": w.n_decode / (ms_step * 1e-3),
-           "step": ("paged_attention_decode_fp8_append" if g else
-                    "reshape_and_cache_fp8, then paged_attention_decode_fp8 (three calls)"),
-           "step_modes": ({"one_call_ms": ms_step, "one_call_graph_replay_ms": g["us_per_step"] * 1e-3,
-                           "three_calls_ms": t["ms_step"]} if g else {"three_calls_ms": t["ms_step"]}),
-           "breakdown_us": {"append": float(t["append_ms"].mean()) * 1e3, "partitions": part_us,
-                            "reduce": float(t["reduce_ms"].mean()) * 1e3},
-           "roofline": {"bound": "hbm", "kernel": "decode partition pass, 8-bit cache "
-                                                  "(decode_fp8_partition_kernel + decode_shared_kernel)",
-                        "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                        "traffic": (profiled_traffic("decode_fp8_partition_llama3_8b_decode",
-                                                     ["decode.hip", "pkv_device.h"])
-                                    if w.name == "llama3_8b_decode" and seed == 0 else None),
-                        "algorithmic_bytes": by["algorithmic_bytes"]},
-           "bytes": by}
-    del b
-    torch.cuda.empty_cache()
+    part = _stats_us(t["part_ms"])
+    achieved = by["algorithmic_bytes"] / (part["mean"] * 1e-6) / 1e9
+    warm_part = _stats_us(warm["part_ms"])
+    g = fused_step(b, out, K, W, flush) if modes else None
+    step_us = g["flushed_us"]["mean"] if g else _stats_us(t["step_ms"])["mean"]
+    tok_s = w.n_decode / (step_us * 1e-6)
+    log(f"{w.name}{' fp8' if fp8 else ''}: step {step_us:.1f} us ({tok_s / 1e6:.3f} M tokens/s, flushed) | "
+        f"partitions {part['mean']:.1f} us = {achieved:.0f} GB/s ({achieved / HBM_PEAK_GBS:.1%}; caches warm: "
+        f"{warm_part['mean']:.1f} us) | append {t['append_ms'].mean() * 1e3:.1f} | reduce "
+        f"{t['reduce_ms'].mean() * 1e3:.1f} us" + (f" | back to back {g['back_to_back_wall_us']:.1f} us, graph "
+                                                   f"{g['graph_flushed_us']['mean']:.1f} us" if g else ""))
+    kernel = ("decode partition pass (decode_shared_kernel + " +
+              ("decode_fp8_partition_kernel)" if fp8 else "decode_partition_kernel)"))
+    res = {
+        "workload": w.name, "description": w.description, "batch": w.n_decode,
+        "kv_cache": "fp8_e4m3 (OCP E4M3, one fp32 scale per pool)" if fp8 else w.dtype,
+        "out_dtype": str(b.out_dtype).replace("torch.", ""),
+        "step": ((("paged_attention_decode_fp8_append" if fp8 else "paged_attention_decode_append") +
+                  " (cache write + partition pass + split-K reduce in one call)") if g else
+                 "cache write, partition pass, reduce (three calls)"),
+        "us_per_step": step_us, "tokens_per_s": tok_s,
+        "timing": {"caches": "1 GiB read through the caches before every timed step (outside the events)",
+                   "one_call_flushed_us": g["flushed_us"] if g else None,
+                   "one_call_back_to_back_wall_us": g["back_to_back_wall_us"] if g else None,
+                   "one_call_graph_flushed_us": g["graph_flushed_us"] if g else None,
+                   "three_calls_flushed_us": _stats_us(t["step_ms"]),
+                   "three_calls_warm_us": _stats_us(warm["step_ms"])},
+        "breakdown_us": {"append": float(t["append_ms"].mean()) * 1e3, "partitions": part["mean"],
+                         "reduce": float(t["reduce_ms"].mean()) * 1e3},
+        "roofline": {"bound": "hbm", "kernel": kernel, "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": (profiled_traffic(profile, ["decode.hip", "pkv_device.h"])
+                                 if profile and seed == 0 else None),
+                     "algorithmic_bytes": by["algorithmic_bytes"], "launch_us": part,
+                     "caches_warm": {"launch_us": warm_part,
+                                     "achieved": by["algorithmic_bytes"] / (warm_part["mean"] * 1e-6) / 1e9},
+                     "after_write_flush": {"launch_us": _stats_us(wflush["part_ms"]),
+                                           "achieved": by["algorithmic_bytes"] /
+                                           (float(wflush["part_ms"].mean()) * 1e-3) / 1e9}},
+        "bytes": by,
+        "logical_gbs": (by["logical_kv_bytes"] + by["other_bytes"]) / (part["mean"] * 1e-6) / 1e9,
+    }
+    if fp8:
+        res["k_scale"], res["v_scale"] = FP8_K_SCALE, FP8_V_SCALE
+    return b, out, res
+
+
+def ceiling_leg(b, K, flush, part_achieved):
+    """Read-only passes beside the decode pass (paged_kv_read_tiles): every
+    (block, KV head) tile the batch's tables name, read once (K tiles, then V
+    tiles), in table order and in a random order, and a contiguous read of the
+    same number of bytes; each timed K times after a cache flush.  They give
+    what the chip delivers for this access pattern with no arithmetic."""
+    import numpy as np
+    import torch
+    import paged_kv_cache_gather_amd as pkv
+    w, d = b.w, b.decode
+    nb = -(-d.lens.astype(np.int64) // 16)
+    blocks = np.concatenate([d.tables_host[s, :nb[s]] for s in range(w.n_decode)]).astype(np.int64)
+    _, first = np.unique(blocks, return_index=True)
+    uniq = blocks[np.sort(first)]
+    tiles = (uniq[:, None] * w.n_kv_heads + np.arange(w.n_kv_heads)).reshape(-1)
+    n_k = tiles.size
+    tile_bytes = 16 * w.head_dim * b.k_pool.element_size()
+    nbytes = 2 * n_k * tile_bytes
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda:0")
+    st = torch.cuda.current_stream()
+    perm = np.random.default_rng(1).permutation(n_k)
+    lists = {"table_order": np.concatenate([tiles, tiles]),
+             "random_order": np.concatenate([tiles[perm], tiles[perm]])}
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+        for e0, e1 in ev:
+            flush()
+            e0.record(st)
+            fn()
+            e1.record(st)
+        torch.cuda.synchronize()
+        return _stats_us([e0.elapsed_time(e1) for e0, e1 in ev])
+
+    res = {"kernel": "read_tiles_kernel", "tiles": int(2 * n_k), "tile_bytes": tile_bytes, "bytes": nbytes}
+    for name, lst in lists.items():
+        dev = torch.from_numpy(lst).to("cuda:0")
+        t = timed(lambda: pkv.paged_kv_read_tiles(b.k_pool, b.v_pool, dev, n_k, 2 * n_k, tile_bytes, sink))
+        res[name] = {"us": t, "gbs": nbytes / (t["mean"] * 1e-6) / 1e9}
+    if b.k_pool.numel() * b.k_pool.element_size() >= nbytes:
+        t = timed(lambda: pkv.paged_kv_read_tiles(b.k_pool, None, None, 2 * n_k, 2 * n_k, tile_bytes, sink))
+        res["contiguous"] = {"us": t, "gbs": nbytes / (t["mean"] * 1e-6) / 1e9}
+    for name in ("table_order", "random_order", "contiguous"):
+        if name in res:
+            res[name]["decode_pass_frac"] = part_achieved / res[name]["gbs"]
+    log("read ceilings: " + ", ".join(f"{n} {res[n]['gbs']:.0f} GB/s" for n in ("table_order", "random_order",
+                                                                                 "contiguous") if n in res)
+        + f" ({nbytes / 1e9:.3f} GB) | decode pass {part_achieved:.0f} GB/s")
     return res
 
 
@@ -586,7 +763,6 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--out-dtype", default="kv", choices=["kv", "f32"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample", type=int, default=256)
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--no-mixed", action="store_true", help="skip the mixed prefill+decode step")
     ap.add_argument("--only-mixed", action="store_true", help="run only the mixed prefill+decode step")
@@ -595,6 +771,9 @@ def main():
     ap.add_argument("--no-verify", action="store_true", help="skip the verify-attention leg")
     ap.add_argument("--only-verify", action="store_true", help="run only the verify-attention leg")
     ap.add_argument("--only-fp8", action="store_true", help="run only the 8-bit-cache decode leg")
+    ap.add_argument("--no-other-workloads", action="store_true",
+                    help="skip the toy, TinyLlama- and OPT-13B-shaped decode legs")
+    ap.add_argument("--no-ceilings", action="store_true", help="skip the read-only bandwidth ceilings")
     ap.add_argument("--no-step-modes", action="store_true",
                     help="time only the three-call step (no one-call or graph runs; for kernel profiles)")
     args = ap.parse_args()
@@ -606,66 +785,43 @@ def main():
                           "n_gpus": args.gpus}), flush=True)
         sys.exit(2)
 
-    import numpy as np
     import torch
     import synth
-    from paged_kv_cache_gather_amd.batch import DeviceBatch
 
     if args.copy_calibration:
         copy_calibration()
         return
-
+    flush = CacheFlush()
+    K, W = args.steps, args.warmup
+    out_dtype = None if args.out_dtype == "kv" else "f32"
     if args.only_mixed:
-        print(json.dumps(mixed_step(args.steps, args.warmup, args.seed)), flush=True)
+        print(json.dumps(mixed_step(args.steps, args.warmup, args.seed, flush)), flush=True)
         return
     if args.only_verify:
-        print(json.dumps(verify_leg(args.steps, args.warmup, args.seed)), flush=True)
+        print(json.dumps(verify_leg(args.steps, args.warmup, args.seed, flush)), flush=True)
         return
-
     w = synth.make_workload(args.workload, seed=args.seed)
+    profile = {3: "decode_partition_llama3_8b_decode", 2: "decode_partition_tinyllama_decode",
+               4: "decode_partition_opt13b_decode"}
     if args.only_fp8:
-        print(json.dumps(fp8_decode_leg(w, args.steps, args.warmup, None if args.out_dtype == "kv" else "f32",
-                                        args.seed, not args.no_step_modes)), flush=True)
+        b, _, r = decode_leg(w, K, W, out_dtype, args.seed, flush, fp8=True, modes=not args.no_step_modes,
+                             profile="decode_fp8_partition_llama3_8b_decode" if args.workload == 3 else None)
+        print(json.dumps(r), flush=True)
         return
-    log(f"building {w.name}: {w.description}")
-    t_build = time.perf_counter()
-    b = DeviceBatch(w, "cuda:0", fill="device", out_dtype=None if args.out_dtype == "kv" else "f32")
-    log(f"built in {time.perf_counter() - t_build:.1f} s")
-    out = b.new_decode_out()
-    K, W = args.steps, args.warmup
-    t = time_decode(b, out, K, W)
-    ms_step, part_ms, append_ms, reduce_ms = t["ms_step"], t["part_ms"], t["append_ms"], t["reduce_ms"]
-    by = decode_bytes(b)
-    part_s = float(part_ms.mean()) * 1e-3
-    achieved = by["algorithmic_bytes"] / part_s / 1e9
-    logical = (by["logical_kv_bytes"] + by["other_bytes"]) / part_s / 1e9
-    # the headline: the step in one call (K steps between two
-    # synchronisations); the eager run above, three calls with events between
-    # them, gives the breakdown and the partition pass's roofline; the one
-    # call replayed from a HIP graph is reported beside it
-    eager_ms_step = ms_step
-    g = None
-    if not args.no_step_modes:
-        g = fused_step(b, out, K, W)
-        ms_step = g["eager_us_per_step"] * 1e-3
-    tok_s = w.n_decode / (ms_step * 1e-3)
-    if g:
-        log(f"step in one call {g['eager_us_per_step']:.1f} us ({tok_s / 1e6:.3f} M tokens/s) | replayed from a "
-            f"HIP graph {g['us_per_step']:.1f} us | three calls {eager_ms_step * 1e3:.1f} us")
-    log(f"eager three-call step {eager_ms_step * 1e3:.1f} us | append {append_ms.mean() * 1e3:.1f} us | partitions "
-        f"{part_ms.mean() * 1e3:.1f} us (p10 {np.percentile(part_ms, 10) * 1e3:.1f}, p90 "
-        f"{np.percentile(part_ms, 90) * 1e3:.1f}) | reduce {reduce_ms.mean() * 1e3:.1f} us")
-    log(f"unique {by['unique_kv_bytes'] / 1e9:.3f} GB, logical {by['logical_kv_bytes'] / 1e9:.3f} GB -> "
-        f"{achieved:.0f} GB/s unique ({achieved / HBM_PEAK_GBS:.1%}), {logical:.0f} GB/s logical")
 
+    t_build = time.perf_counter()
+    b, out, head = decode_leg(w, K, W, out_dtype, args.seed, flush, modes=not args.no_step_modes,
+                              profile=profile[args.workload])
+    log(f"built and timed in {time.perf_counter() - t_build:.1f} s")
+    by = head["bytes"]
     res = {
         "metric": "paged-attn decode tokens/sec and achieved HBM GB/s (% of peak), 1 GPU",
-        "value": tok_s,
+        "value": head["tokens_per_s"],
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": K,
         "warmup": W,
-        "ms_per_step": ms_step,
+        "ms_per_step": head["us_per_step"] * 1e-3,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -674,40 +830,49 @@ def main():
         "config": {"workload": w.name, "description": w.description, "layers": 1,
                    "batch": w.n_decode, "n_q_heads": w.n_q_heads, "n_kv_heads": w.n_kv_heads,
                    "head_dim": w.head_dim, "block_size": w.block_size, "num_blocks": w.num_blocks,
-                   "out_dtype": str(b.out_dtype).replace("torch.", ""), "seed": args.seed,
-                   "step": ("paged_attention_decode_append (cache write + decode partition pass + split-K "
-                            "reduce)" if g else "reshape_and_cache, then paged_attention_decode (three calls)")},
-        "roofline": {"bound": "hbm",
-                     "kernel": "decode partition pass (decode_partition_kernel + decode_shared_kernel)",
-                     "achieved": achieved,
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": (profiled_traffic("decode_partition_llama3_8b_decode", ["decode.hip", "pkv_device.h"])
-                                 if w.name == "llama3_8b_decode" and args.seed == 0 else None),
-                     "algorithmic_bytes": by["algorithmic_bytes"]},
-        "breakdown_us": {"append": float(append_ms.mean()) * 1e3, "partitions": float(part_ms.mean()) * 1e3,
-                         "reduce": float(reduce_ms.mean()) * 1e3,
-                         "host_allocator_step": host_allocator_us(b)},
+                   "out_dtype": head["out_dtype"], "seed": args.seed, "step": head["step"],
+                   "timing": "each timed step follows a 1 GiB device read that evicts L2 and the Infinity "
+                             "Cache; HIP events around each step; value = batch / mean step time"},
+        "roofline": head["roofline"],
+        "breakdown_us": dict(head["breakdown_us"], host_allocator_step=host_allocator_us(b)),
+        "timing": head["timing"],
         "bytes": by,
-        "logical_gbs": logical,
-        "step_modes": ({"one_call_ms": ms_step, "one_call_graph_replay_ms": g["us_per_step"] * 1e-3,
-                        "three_calls_ms": eager_ms_step,
-                        "three_calls_tokens_per_s": w.n_decode / (eager_ms_step * 1e-3)} if g else
-                       {"three_calls_ms": eager_ms_step, "note": "--no-step-modes: value is the three-call step"}),
+        "logical_gbs": head["logical_gbs"],
         "prefix_cache_host": prefix_cache_host(),
     }
+    if not args.no_ceilings:
+        res["read_ceilings"] = ceiling_leg(b, K, flush, head["roofline"]["achieved"])
     if not args.no_swap:
         res["swap"] = swap_leg(b)
-    if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(w, args.cpu_sample)
+    tables = b.decode.tables_host
     del b, out
     torch.cuda.empty_cache()
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(w, tables)
     if not args.no_fp8:
-        res["fp8_kv_decode"] = fp8_decode_leg(w, K, W, None if args.out_dtype == "kv" else "f32", args.seed,
-                                              not args.no_step_modes)
+        b, _, r = decode_leg(w, K, W, out_dtype, args.seed, flush, fp8=True, modes=not args.no_step_modes,
+                             profile="decode_fp8_partition_llama3_8b_decode" if args.workload == 3 else None)
+        res["fp8_kv_decode"] = r
+        del b
+        torch.cuda.empty_cache()
+    if not args.no_other_workloads:
+        res["other_workloads"] = {}
+        for cfg in (1, 2, 3, 4):
+            if cfg == args.workload:
+                continue
+            wo = synth.make_workload(cfg, seed=args.seed)
+            b, _, r = decode_leg(wo, K, W, out_dtype, args.seed, flush, modes=not args.no_step_modes,
+                                 profile=profile.get(cfg))
+            tables = b.decode.tables_host
+            del b
+            torch.cuda.empty_cache()
+            if not args.no_cpu_baseline:
+                r["cpu_baseline"] = cpu_baseline(wo, tables)
+            res["other_workloads"][wo.name] = r
     if not args.no_verify:
-        res["verify"] = verify_leg(max(5, K // 2), max(2, W // 2), args.seed)
+        res["verify"] = verify_leg(max(5, K // 2), max(2, W // 2), args.seed, flush)
     if not args.no_mixed:
-        res["mixed_step"] = mixed_step(max(5, K // 2), max(2, W // 2), args.seed)
+        res["mixed_step"] = mixed_step(max(5, K // 2), max(2, W // 2), args.seed, flush)
     print(json.dumps(res), flush=True)
 
 

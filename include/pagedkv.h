@@ -644,6 +644,26 @@ int paged_attention_verify_fp8(void* out, int32_t out_dtype, const void* q, int3
                                int64_t num_blocks, int32_t max_context_len, float scale,
                                void* workspace, int64_t workspace_bytes, void* stream);
 
+/* ------------------------------------------------------------------------
+ * Measurement
+ * ------------------------------------------------------------------------ */
+
+/* A read-only pass over tiles of one or two pools: the bandwidth an
+ * HBM-bound kernel with this access pattern can reach, with no attention
+ * arithmetic (the decode kernels read the (block, KV head) tiles a step's
+ * block tables name, "How the attention kernel actually reads paged blocks",
+ * vLLM Serving deep dive).  Entry e of tiles (device int64 [n_tiles]) names
+ * tile tiles[e], the tile_bytes bytes at pool + tiles[e] * tile_bytes, of
+ * k_pool for e < n_k_tiles and of v_pool after; tiles NULL reads tiles 0,
+ * 1, ..., n_tiles - 1 of k_pool, a contiguous read of n_tiles * tile_bytes
+ * bytes (n_k_tiles must then equal n_tiles, PKV_EINVAL otherwise).  Every tile byte is loaded once, 16 bytes
+ * per lane; sink (device uint32 [1]) is written only when the bytes' XOR hits
+ * a fixed value (it keeps the loads alive).  tile_bytes a positive multiple of
+ * 16, pools 16-byte aligned; tiles outside the pools are the caller's
+ * contract. */
+int paged_kv_read_tiles(const void* k_pool, const void* v_pool, const int64_t* tiles, int64_t n_k_tiles,
+                        int64_t n_tiles, int64_t tile_bytes, uint32_t* sink, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -121,6 +121,7 @@ _sig("paged_attention_verify", ctypes.c_int, _P, _i32, _P, _P, _P, _P, _i32, _P,
      _i32, _i32, _i64, _i32, _f32, _i32, _P, _i64, _P)
 _sig("paged_attention_verify_fp8", ctypes.c_int, _P, _i32, _P, _i32, _P, _P, _f32, _f32, _P, _i32, _P, _P, _i32, _i32,
      _i32, _i32, _i32, _i32, _i32, _i64, _i32, _f32, _P, _i64, _P)
+_sig("paged_kv_read_tiles", ctypes.c_int, _P, _P, _P, _i64, _i64, _i64, _P, _P)
 _sig("paged_attention_prefill_chunk", ctypes.c_int, _P, _i32, _P, _P, _P, _P, _i32, _P, _P, _i32,
      _i32, _i32, _i32, _i32, _i32, _i32, _i64, _i32, _f32, _i32, _P)
 
@@ -869,3 +870,20 @@ def paged_attention_prefill_chunk(out: torch.Tensor, q: torch.Tensor, k_pool: to
 __all__ = [n for n in dir() if n.startswith(("paged_", "reshape_", "pkv", "PKV_", "Pool", "PagedKV",
                                                  "OutOfBlocks", "last_error", "dtype_code", "BLOCK_SIZE"))]
 
+
+def paged_kv_read_tiles(k_pool: torch.Tensor, v_pool, tiles, n_k_tiles: int, n_tiles: int, tile_bytes: int,
+                        sink: torch.Tensor, stream=None):
+    """Read-only pass over pool tiles (a bandwidth ceiling beside the decode
+    kernels); tiles: device int64 [n_tiles] or None for a contiguous read."""
+    _dev(k_pool, "k_pool")
+    if v_pool is not None:
+        _dev(v_pool, "v_pool")
+    if tiles is not None:
+        _dev(tiles, "tiles", torch.int64)
+        if tiles.numel() < n_tiles:
+            raise PagedKVError(PKV_EINVAL, "tiles shorter than n_tiles")
+    _dev(sink, "sink")
+    if tiles is None and n_tiles * tile_bytes > k_pool.numel() * k_pool.element_size():
+        raise PagedKVError(PKV_EINVAL, "contiguous read beyond the buffer")
+    _check(_lib.paged_kv_read_tiles(_ptr(k_pool), _ptr(v_pool), _ptr(tiles), n_k_tiles, n_tiles, tile_bytes,
+                                    _ptr(sink), _stream(stream, k_pool.device)))

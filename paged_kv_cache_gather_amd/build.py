@@ -13,7 +13,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build", "pagedkv")
 LIB = os.path.join(HERE, "libpagedkv.so")
 
-SOURCES = ["block_manager.cpp", "cache_ops.hip", "decode.hip", "prefill.hip"]
+SOURCES = ["block_manager.cpp", "cache_ops.hip", "decode.hip", "prefill.hip", "ceiling.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 # -packed-fp32-ops: keep the compiler from forming packed fp32 instructions.
