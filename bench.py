@@ -704,8 +704,9 @@ def decode_leg(w, K, W, out_dtype, seed, flush, fp8=False, modes=True, profile=N
 def ceiling_leg(b, K, flush, part_achieved):
     """Read-only passes beside the decode pass (paged_kv_read_tiles): every
     (block, KV head) tile the batch's tables name, read once (K tiles, then V
-    tiles), in table order and in a random order, and a contiguous read of the
-    same number of bytes; each timed K times after a cache flush.  They give
+    tiles), in table order and in a random order, and the same number of
+    tiles from the start of each pool (contiguous bytes); each timed K times
+    after a cache flush.  They give
     what the chip delivers for this access pattern with no arithmetic."""
     import numpy as np
     import torch
@@ -742,9 +743,10 @@ def ceiling_leg(b, K, flush, part_achieved):
         dev = torch.from_numpy(lst).to("cuda:0")
         t = timed(lambda: pkv.paged_kv_read_tiles(b.k_pool, b.v_pool, dev, n_k, 2 * n_k, tile_bytes, sink))
         res[name] = {"us": t, "gbs": nbytes / (t["mean"] * 1e-6) / 1e9}
-    if b.k_pool.numel() * b.k_pool.element_size() >= nbytes:
-        t = timed(lambda: pkv.paged_kv_read_tiles(b.k_pool, None, None, 2 * n_k, 2 * n_k, tile_bytes, sink))
-        res["contiguous"] = {"us": t, "gbs": nbytes / (t["mean"] * 1e-6) / 1e9}
+    # the same number of tiles from the start of each pool: contiguous bytes
+    ident = torch.arange(n_k, dtype=torch.int64, device="cuda:0").repeat(2)
+    t = timed(lambda: pkv.paged_kv_read_tiles(b.k_pool, b.v_pool, ident, n_k, 2 * n_k, tile_bytes, sink))
+    res["contiguous"] = {"us": t, "gbs": nbytes / (t["mean"] * 1e-6) / 1e9}
     for name in ("table_order", "random_order", "contiguous"):
         if name in res:
             res[name]["decode_pass_frac"] = part_achieved / res[name]["gbs"]
