@@ -26,7 +26,7 @@ OPT-13B-shaped decode batches with their own rooflines, the swap copies of 32
 sequences, verify attention of 5 new tokens per sequence, and the mixed
 chunked-prefill + decode step with the prefill kernel's MFMA fraction.
 
-  python bench.py [--steps K] [--warmup W] [--workload 2|3|4] [--no-cpu-baseline] [--no-fp8] [--no-mixed] ...
+  python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline] [--no-fp8] [--no-mixed] ...
   python bench.py --copy-calibration     # plain device copy of a known size
 """
 import argparse
@@ -122,7 +122,7 @@ def mixed_step(steps, warmup, seed, flush):
     import torch
     import synth
     from paged_kv_cache_gather_amd.batch import DeviceBatch
-    w = synth.make_workload(5, seed=seed)
+    w = synth.make_workload("llama3_8b_mixed", seed=seed)
     log(f"building {w.name}: {w.description}")
     b = DeviceBatch(w, "cuda:0", fill="device")
     outp, outd = b.new_prefill_out(), b.new_decode_out()
@@ -329,7 +329,7 @@ def verify_leg(steps, warmup, seed, flush, k=5):
     import torch
     import synth
     from paged_kv_cache_gather_amd.batch import DeviceBatch
-    lens = synth.make_workload(3, seed).decode_lens
+    lens = synth.make_workload("llama3_8b_decode", seed).decode_lens
     w = synth.custom_workload("llama3_8b_verify", 32, 8, 128, "bf16", 70000, seed, chunk_ctx=lens - 1,
                               chunk_qlen=np.full(lens.size, k),
                               description=f"Llama-3-8B-shaped verify step: 256 sequences, {k} new tokens each over "
@@ -761,7 +761,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", type=int, default=3, choices=[2, 3, 4])
+    ap.add_argument("--workload", default="llama3_8b_decode",
+                    choices=["tinyllama_decode", "llama3_8b_decode", "opt13b_decode"])
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--out-dtype", default="kv", choices=["kv", "f32"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -803,11 +804,10 @@ def main():
         print(json.dumps(verify_leg(args.steps, args.warmup, args.seed, flush)), flush=True)
         return
     w = synth.make_workload(args.workload, seed=args.seed)
-    profile = {3: "decode_partition_llama3_8b_decode", 2: "decode_partition_tinyllama_decode",
-               4: "decode_partition_opt13b_decode"}
+    profile = {n: "decode_partition_" + n for n in ("llama3_8b_decode", "tinyllama_decode", "opt13b_decode")}
     if args.only_fp8:
         b, _, r = decode_leg(w, K, W, out_dtype, args.seed, flush, fp8=True, modes=not args.no_step_modes,
-                             profile="decode_fp8_partition_llama3_8b_decode" if args.workload == 3 else None)
+                             profile="decode_fp8_partition_llama3_8b_decode" if args.workload == "llama3_8b_decode" else None)
         print(json.dumps(r), flush=True)
         return
 
@@ -853,18 +853,18 @@ def main():
         res["cpu_baseline"] = cpu_baseline(w, tables)
     if not args.no_fp8:
         b, _, r = decode_leg(w, K, W, out_dtype, args.seed, flush, fp8=True, modes=not args.no_step_modes,
-                             profile="decode_fp8_partition_llama3_8b_decode" if args.workload == 3 else None)
+                             profile="decode_fp8_partition_llama3_8b_decode" if args.workload == "llama3_8b_decode" else None)
         res["fp8_kv_decode"] = r
         del b
         torch.cuda.empty_cache()
     if not args.no_other_workloads:
         res["other_workloads"] = {}
-        for cfg in (1, 2, 3, 4):
-            if cfg == args.workload:
+        for name in ("toy_f32_decode", "tinyllama_decode", "llama3_8b_decode", "opt13b_decode"):
+            if name == args.workload:
                 continue
-            wo = synth.make_workload(cfg, seed=args.seed)
+            wo = synth.make_workload(name, seed=args.seed)
             b, _, r = decode_leg(wo, K, W, out_dtype, args.seed, flush, modes=not args.no_step_modes,
-                                 profile=profile.get(cfg))
+                                 profile=profile.get(name))
             tables = b.decode.tables_host
             del b
             torch.cuda.empty_cache()

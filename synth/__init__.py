@@ -224,49 +224,46 @@ def custom_workload(name, n_q_heads, n_kv_heads, head_dim, dtype, num_blocks, se
                     free_order=order, description=description)
 
 
-WORKLOADS = {
-    1: "toy_f32_decode",
-    2: "tinyllama_decode",
-    3: "llama3_8b_decode",
-    4: "opt13b_decode",
-    5: "llama3_8b_mixed",
-}
+WORKLOADS = ("toy_f32_decode", "tinyllama_decode", "llama3_8b_decode", "opt13b_decode", "llama3_8b_mixed")
+# tag of each workload's length / context streams (fixed, so its inputs never change)
+_TAG = {name: i + 1 for i, name in enumerate(WORKLOADS)}
 
 
-def make_workload(cfg: int, seed: int = 0) -> Workload:
-    """The five workloads of the benchmark plan, by number (1..5)."""
-    if cfg == 1:
+def make_workload(name: str, seed: int = 0) -> Workload:
+    """The benchmark's five workloads, by name (see WORKLOADS)."""
+    if name not in _TAG:
+        raise ValueError(f"unknown workload {name!r}")
+    tag = _TAG[name]
+    if name == "toy_f32_decode":
         return custom_workload(
-            WORKLOADS[1], 4, 2, 64, "f32", 8, seed, decode_lens=[4, 7, 2],
+            name, 4, 2, 64, "f32", 8, seed, decode_lens=[4, 7, 2],
             description="fp32 decode, 3 sequences of 4/7/2 keys, GQA 4:2, d=64, 8-block pool")
-    if cfg == 2:
-        lens = _rng(seed, _P_LENS, 2).integers(128, 2048 + 1, size=64)
+    if name == "tinyllama_decode":
+        lens = _rng(seed, _P_LENS, tag).integers(128, 2048 + 1, size=64)
         return custom_workload(
-            WORKLOADS[2], 32, 4, 64, "f16", 16384, seed, decode_lens=lens,
+            name, 32, 4, 64, "f16", 16384, seed, decode_lens=lens,
             description="TinyLlama-shaped fp16 decode, B=64, L~U[128,2048], Hq32/Hkv4, d=64")
-    if cfg == 3:
-        lens = _rng(seed, _P_LENS, 3).integers(512, 4096 + 1, size=256)
+    if name == "llama3_8b_decode":
+        lens = _rng(seed, _P_LENS, tag).integers(512, 4096 + 1, size=256)
         group = np.arange(256) // 8
         plen = np.minimum(lens - 1, 1024)
         return custom_workload(
-            WORKLOADS[3], 32, 8, 128, "bf16", 32768, seed, decode_lens=lens,
+            name, 32, 8, 128, "bf16", 32768, seed, decode_lens=lens,
             prefix_len=plen, prefix_group=group,
             description="Llama-3-8B-shaped bf16 decode, B=256, L~U[512,4096], groups of 8 "
                         "sharing a 1024-token prefix, Hq32/Hkv8, d=128")
-    if cfg == 4:
+    if name == "opt13b_decode":
         return custom_workload(
-            WORKLOADS[4], 40, 40, 128, "f16", 8192, seed, decode_lens=np.full(32, 2048),
+            name, 40, 40, 128, "f16", 8192, seed, decode_lens=np.full(32, 2048),
             description="OPT-13B-shaped fp16 MHA decode, B=32, L=2048, Hq=Hkv=40, d=128")
-    if cfg == 5:
-        r = _rng(seed, _P_CTX, 5)
-        ctx = r.integers(0, 7680 + 1, size=16)
-        lens = _rng(seed, _P_LENS, 5).integers(256, 8192 + 1, size=240)
-        return custom_workload(
-            WORKLOADS[5], 32, 8, 128, "bf16", 131072, seed, decode_lens=lens,
-            chunk_ctx=ctx, chunk_qlen=np.full(16, 512),
-            description="Llama-3-8B-shaped bf16 mixed step: 16 prefill chunks of 512 queries "
-                        "over contexts U[0,7680] plus 240 decodes with L~U[256,8192]")
-    raise ValueError(f"unknown workload {cfg}")
+    r = _rng(seed, _P_CTX, tag)
+    ctx = r.integers(0, 7680 + 1, size=16)
+    lens = _rng(seed, _P_LENS, tag).integers(256, 8192 + 1, size=240)
+    return custom_workload(
+        name, 32, 8, 128, "bf16", 131072, seed, decode_lens=lens,
+        chunk_ctx=ctx, chunk_qlen=np.full(16, 512),
+        description="Llama-3-8B-shaped bf16 mixed step: 16 prefill chunks of 512 queries "
+                    "over contexts U[0,7680] plus 240 decodes with L~U[256,8192]")
 
 
 # ---------------------------------------------------------------------------

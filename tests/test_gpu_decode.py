@@ -34,7 +34,7 @@ def _check_all(w, out, out_dtype, seqs=None):
 
 
 def test_config1_toy_f32():
-    w = synth.make_workload(1, seed=0)
+    w = synth.make_workload("toy_f32_decode", seed=0)
     print(f"decode {w.name}", flush=True)
     _, out = _run_decode(w)
     _check_all(w, out, "f32")
@@ -121,14 +121,14 @@ def test_decode_shared_partition_runs(name, Hq, Hkv, d, dtype, lens, plen, pgrou
     _check_all(w, out, "f32")
 
 
-@pytest.mark.parametrize("cfg", [2, 3, 4])
-def test_decode_full_size_sampled(cfg):
-    w = synth.make_workload(cfg, seed=0)
+@pytest.mark.parametrize("name", ["tinyllama_decode", "llama3_8b_decode", "opt13b_decode"])
+def test_decode_full_size_sampled(name):
+    w = synth.make_workload(name, seed=0)
     print(f"decode full {w.name}", flush=True)
     b, out = _run_decode(w, None, fill="device")
     got = out.float()
     assert torch.isfinite(got).all()
-    rng = np.random.default_rng(cfg)
+    rng = np.random.default_rng(synth.WORKLOADS.index(name) + 1)
     sample = sorted(set(rng.choice(w.n_decode, size=6, replace=False).tolist()
                         + [int(np.argmax(w.decode_lens)), int(np.argmin(w.decode_lens))]))
     _check_all(w, out, w.dtype, sample)
@@ -202,8 +202,8 @@ def test_decode_large_batch_sampled():
 
 
 def test_config3_step_sampled_with_bf16_out():
-    # the workload the benchmark times: config 3, bf16 out, same launch shape
-    w = synth.make_workload(3, seed=0)
+    # the workload the benchmark times: the Llama-3-8B decode batch, bf16 out, same launch shape
+    w = synth.make_workload("llama3_8b_decode", seed=0)
     b, out = _run_decode(w, "bf16", fill="device")
     _check_all(w, out, "bf16", [0, 7, 8, 100, 255])
 

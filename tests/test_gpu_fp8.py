@@ -211,7 +211,7 @@ def test_decode_fp8_shared_partition_runs(name, Hq, Hkv, d, dtype, lens, plen, p
 def test_decode_fp8_full_size_sampled():
     # the Llama-3-8B-shaped workload (256 sequences, groups of 8 sharing a
     # 1024-token prefix) in the launch shape the benchmark times, bf16 out
-    w = synth.make_workload(3, seed=0)
+    w = synth.make_workload("llama3_8b_decode", seed=0)
     print("fp8 decode full llama3_8b_decode", flush=True)
     b, out = _run_decode_fp8(w, "bf16", fill="device")
     assert torch.isfinite(out.float()).all()

@@ -33,10 +33,10 @@ def _check_decode(w, out, out_dtype, refs, name):
         assert_close(f"{name} seq {s} L={int(w.decode_lens[s])}", got[s], ref, atol, rtol)
 
 
-@pytest.mark.parametrize("cfg", [2, 3, 4])
-def test_decode_step_every_sequence(cfg):
+@pytest.mark.parametrize("name", ["tinyllama_decode", "llama3_8b_decode", "opt13b_decode"])
+def test_decode_step_every_sequence(name):
     from paged_kv_cache_gather_amd.batch import DeviceBatch
-    w = synth.make_workload(cfg, seed=0)
+    w = synth.make_workload(name, seed=0)
     print(f"full-size decode step {w.name}: {w.n_decode} sequences", flush=True)
     b = DeviceBatch(w, DEV, fill="device")
     out = b.new_decode_out()
@@ -48,7 +48,7 @@ def test_decode_step_every_sequence(cfg):
 
 def test_decode_fp8_step_every_sequence():
     from paged_kv_cache_gather_amd.batch import DeviceBatch
-    w = synth.make_workload(3, seed=0)
+    w = synth.make_workload("llama3_8b_decode", seed=0)
     print(f"full-size 8-bit decode step {w.name}", flush=True)
     b = DeviceBatch(w, DEV, fill="device", kv_cache="fp8_e4m3", k_scale=FP8_K_SCALE, v_scale=FP8_V_SCALE)
     out = b.new_decode_out()
@@ -63,7 +63,7 @@ def mixed():
     """The mixed step as the benchmark runs it: both appends, then prefill
     attention and decode attention (partition pass, then merge)."""
     from paged_kv_cache_gather_amd.batch import DeviceBatch
-    w = synth.make_workload(5, seed=0)
+    w = synth.make_workload("llama3_8b_mixed", seed=0)
     print(f"full-size mixed step {w.name}", flush=True)
     b = DeviceBatch(w, DEV, fill="device")
     outp, outd = b.new_prefill_out(), b.new_decode_out()
@@ -100,7 +100,7 @@ def test_verify_every_row():
     from paged_kv_cache_gather_amd.batch import DeviceBatch
     from tests.helpers import prefill_reference, oracle_workers
     from concurrent.futures import ThreadPoolExecutor
-    lens = synth.make_workload(3, 0).decode_lens
+    lens = synth.make_workload("llama3_8b_decode", 0).decode_lens
     w = synth.custom_workload("llama3_8b_verify", 32, 8, 128, "bf16", 70000, 0, chunk_ctx=lens - 1,
                               chunk_qlen=np.full(lens.size, 5))
     print("full-size verify: 256 sequences x 5 new tokens", flush=True)

@@ -62,11 +62,11 @@ def test_prefill_small(name, Hq, Hkv, d, dtype, ctx, ql, out_kind):
 
 
 def test_config5_prefill_sampled_rows():
-    w = synth.make_workload(5, seed=0)
+    w = synth.make_workload("llama3_8b_mixed", seed=0)
     print("prefill full llama3_8b_mixed", flush=True)
     b, out = _run_prefill(w, None, fill="device")
     assert torch.isfinite(out.float()).all()
-    sub = synth.make_workload(5, seed=0)
+    sub = synth.make_workload("llama3_8b_mixed", seed=0)
     keep = [int(np.argmin(w.chunk_ctx)), int(np.argmax(w.chunk_ctx)), 3, 9]
     cu = np.concatenate([[0], np.cumsum(w.chunk_qlen)])
     atol, rtol = tolerance(w.dtype, w.dtype)
@@ -74,7 +74,7 @@ def test_config5_prefill_sampled_rows():
     rng = np.random.default_rng(5)
     for c in keep:
         rows = np.unique(np.concatenate([[0, 511], rng.choice(512, 24, replace=False)]))
-        assert_close(f"cfg5 chunk {c} ctx={int(w.chunk_ctx[c])}", got[cu[c] + rows], prefill_reference(sub, c, rows),
+        assert_close(f"mixed-step chunk {c} ctx={int(w.chunk_ctx[c])}", got[cu[c] + rows], prefill_reference(sub, c, rows),
                      atol, rtol)
 
 

@@ -63,7 +63,7 @@ def test_verify_small(name, Hq, Hkv, d, dtype, ctx, ql, out_kind):
 
 
 def _llama3_verify_batch(seed=0, k=5):
-    lens = synth.make_workload(3, seed).decode_lens  # the decode batch's context lengths
+    lens = synth.make_workload("llama3_8b_decode", seed).decode_lens  # the decode batch's context lengths
     return synth.custom_workload("llama3_8b_verify", 32, 8, 128, "bf16", 70000, seed, chunk_ctx=lens - 1,
                                  chunk_qlen=np.full(lens.size, k))
 

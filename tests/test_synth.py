@@ -49,32 +49,32 @@ def test_value_distribution():
     assert abs(v.mean()) < 0.01 and abs(v.std() - 1.0) < 0.01
 
 
-@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
-def test_workload_recipes(cfg):
-    w = synth.make_workload(cfg, seed=0)
+@pytest.mark.parametrize("name", synth.WORKLOADS)
+def test_workload_recipes(name):
+    w = synth.make_workload(name, seed=0)
     assert sorted(w.free_order.tolist()) == list(range(w.num_blocks))
-    if cfg == 1:
+    if name == "toy_f32_decode":
         assert w.decode_lens.tolist() == [4, 7, 2] and w.dtype == "f32" and w.num_blocks == 8
-    if cfg == 2:
+    if name == "tinyllama_decode":
         assert w.n_decode == 64 and w.decode_lens.min() >= 128 and w.decode_lens.max() <= 2048
-    if cfg == 3:
+    if name == "llama3_8b_decode":
         assert w.n_decode == 256 and w.decode_lens.min() >= 512 and w.decode_lens.max() <= 4096
         assert np.array_equal(w.prefix_group, np.arange(256) // 8)
         assert np.array_equal(w.prefix_len, np.minimum(w.decode_lens - 1, 1024))
-    if cfg == 4:
+    if name == "opt13b_decode":
         assert np.all(w.decode_lens == 2048) and w.n_q_heads == w.n_kv_heads == 40
-    if cfg == 5:
+    if name == "llama3_8b_mixed":
         assert w.n_chunks == 16 and np.all(w.chunk_qlen == 512)
         assert w.chunk_ctx.max() + 512 <= 8192
         assert w.n_decode == 240 and w.decode_lens.min() >= 256 and w.decode_lens.max() <= 8192
         assert int(w.decode_lens.sum() + w.chunk_qlen.sum()) > 0
     # same seed, same workload
-    w2 = synth.make_workload(cfg, seed=0)
+    w2 = synth.make_workload(name, seed=0)
     assert np.array_equal(w.decode_lens, w2.decode_lens) and np.array_equal(w.free_order, w2.free_order)
 
 
 def test_shared_prefix_tokens_come_from_group_stream():
-    w = synth.make_workload(3, seed=0)
+    w = synth.make_workload("llama3_8b_decode", seed=0)
     a, _ = w.kv("decode", 0, 0, 64)
     b, _ = w.kv("decode", 1, 0, 64)
     assert np.array_equal(a, b)  # same group, inside the prefix
