@@ -32,7 +32,9 @@
 //    same XCD, and sequences that share prefix blocks (adjacent in the batch)
 //    hit that XCD's L2.  Partitions run from the last to the first, so the
 //    long sequences' extra partitions start early.
-//  * Each wave owns 128 consecutive tokens of the partition end to end:
+//  * The partition's blocks are dealt evenly to the four waves (up to 128
+//    consecutive tokens each, so a partly filled last partition keeps every
+//    wave busy); each wave takes its tokens end to end:
 //    - scores: one token per lane; the lane reads its token's whole K row
 //      (16-byte chunks; the K layout keeps x dims of one token together, so
 //      each wave instruction reads 4 blocks x 256 contiguous bytes) and forms
@@ -43,7 +45,8 @@
 //    - values: each wave instruction reads 1 KiB of a block's dim-major V
 //      tile; lane l gets D/64 dims x (16/CPR) tokens and accumulates p*v in
 //      fp32 with the probabilities read from LDS; the CPR lanes sharing a
-//      dim are added with shuffles.
+//      dim are added with shuffles.  The next block's loads are issued
+//      before this block's products where registers allow.
 //  * The four waves' (max, sum, o) states are merged through LDS.  A sequence
 //    that fits in one partition writes its normalised output; otherwise each
 //    partition writes (max, sum, unnormalised o) to the workspace and
@@ -118,8 +121,14 @@ __device__ __forceinline__ void partition_rows(
   const int Hq = Hkv * G;
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform per wave
-  const int wt0 = w * TPW;                                  // wave's first token (partition-local)
-  const int wn = n - wt0 < 0 ? 0 : (n - wt0 > TPW ? TPW : n - wt0);
+  // the partition's blocks are dealt evenly to the waves, so a partly filled
+  // (last) partition keeps every wave busy; wave w takes blocks [bw0, bw1),
+  // at most TPW tokens
+  const int nbp = (n + kBlockSize - 1) / kBlockSize;
+  const int bw0 = (w * nbp) / kWaves, bw1 = ((w + 1) * nbp) / kWaves;
+  const int wt0 = bw0 * kBlockSize;                         // wave's first token (partition-local)
+  const int wend = bw1 * kBlockSize < n ? bw1 * kBlockSize : n;
+  const int wn = wend - wt0 < 0 ? 0 : wend - wt0;            // its tokens
   float(*sp)[R] = reinterpret_cast<float(*)[R]>(smem) + w * TPW;
 
   // ---- scores: one token per lane, R rows, whole K row ---------------------
@@ -130,7 +139,7 @@ __device__ __forceinline__ void partition_rows(
     float acc[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) acc[r] = 0.f;
-    if (it * 64 < wn && tl < n) {
+    if (it * 64 + lane < wn) {
       const int64_t blk = clamp_block(tab[tl >> 4], num_blocks);
       const unsigned char* kp = kpool + (((blk * Hkv + g) * C) * kBlockSize + (tl & 15)) * 16;
       u32x4 kc[C];
@@ -155,7 +164,7 @@ __device__ __forceinline__ void partition_rows(
       }
     }
 #pragma unroll
-    for (int r = 0; r < R; ++r) sreg[it][r] = tl < n ? acc[r] * scale_log2 : -INFINITY;
+    for (int r = 0; r < R; ++r) sreg[it][r] = it * 64 + lane < wn ? acc[r] * scale_log2 : -INFINITY;
   }
 
   // ---- wave-local softmax state -------------------------------------------
@@ -169,7 +178,7 @@ __device__ __forceinline__ void partition_rows(
   }
 #pragma unroll
   for (int it = 0; it < IT; ++it) {
-    const bool valid = wt0 + it * 64 + lane < n;
+    const bool valid = it * 64 + lane < wn;
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       const float e = valid ? __builtin_amdgcn_exp2f(sreg[it][r] - mw[r]) : 0.f;
@@ -206,10 +215,23 @@ __device__ __forceinline__ void partition_rows(
 #pragma unroll
     for (int i = 0; i < NI; ++i) vv[i] = ld16(vp + i * 1024);
   };
-  u32x4 vcur[NI];
+  // block bl + 1's loads are issued before block bl's products while the
+  // accumulators stay small (R * NI <= 16: G <= 4 at head_dim 128, G <= 8 at
+  // 64); beyond, the second buffer costs occupancy or spills
+  constexpr bool kPipeV = R * NI <= 16;
+  u32x4 vcur[NI], vnxt[NI];
+  if constexpr (kPipeV) {
+    if (nbw > 0) load_v(0, vnxt);
+  }
 #pragma unroll 1
   for (int bl = 0; bl < nbw; ++bl) {
-    load_v(bl, vcur);
+    if constexpr (kPipeV) {
+#pragma unroll
+      for (int i = 0; i < NI; ++i) vcur[i] = vnxt[i];
+      if (bl + 1 < nbw) load_v(bl + 1, vnxt);
+    } else {
+      load_v(bl, vcur);
+    }
     const int tb = wt0 / kBlockSize + bl;  // partition-local block
     const int ntok = n - tb * kBlockSize;
     const float(*pb)[R] = sp + bl * kBlockSize + tg * TPC;
