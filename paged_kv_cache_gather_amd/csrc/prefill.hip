@@ -409,7 +409,13 @@ prefill_chunk_kernel(void* __restrict__ out, const uint16_t* __restrict__ q,
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
       if constexpr (kDiag) {
-        const int lim = ctx + i0 + 16 * (rt / HW) + r16 - kStepKeys * s;  // last visible key of the step
+        // last visible key of the step; rows past the chunk's last query
+        // repeat that query (their loads were clamped) and take its limit,
+        // so no key past the context (a stale slot, or a tile this call did
+        // not stage) enters their scores or the wave's rescale vote
+        int tok = i0 + 16 * (rt / HW) + r16;
+        tok = tok < qlen ? tok : qlen - 1;
+        const int lim = ctx + tok - kStepKeys * s;
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
