@@ -865,6 +865,8 @@ def main():
             wo = synth.make_workload(name, seed=args.seed)
             b, _, r = decode_leg(wo, K, W, out_dtype, args.seed, flush, modes=not args.no_step_modes,
                                  profile=profile.get(name))
+            if not args.no_ceilings and wo.dtype != "f32":
+                r["read_ceilings"] = ceiling_leg(b, K, flush, r["roofline"]["achieved"])
             tables = b.decode.tables_host
             del b
             torch.cuda.empty_cache()
