@@ -19,8 +19,9 @@
 //    all of them.
 //  * Keys advance 64 at a time (4 blocks).  The step's K and V tiles are
 //    staged in LDS with direct global->LDS loads issued three steps ahead
-//    (four buffers, no registers); each thread rewrites the V chunks it loaded
-//    as fp16, because the P.V product runs in fp16 (see below).
+//    (rings of four K and five V buffers, no registers); each thread rewrites
+//    the V chunks it loaded as fp16, because the P.V product runs in fp16
+//    (see below).
 //  * Scores are formed transposed, S^T = K Q^T (A = K tile from LDS, B = the
 //    wave's Q rows kept in registers), so each lane owns one query row: the
 //    online softmax (base 2) needs one cross-lane max per row tile and step,
@@ -34,9 +35,11 @@
 //    (u = 2^-11) rather than bf16 (u = 2^-8): the latter's error on short
 //    causal rows comes close to the 2e-3 tolerance.  Row sums of P come from
 //    an MFMA against ones.
-//  * A step is four phases between workgroup barriers (QK, softmax, PV,
+//  * A step is two phases between workgroup barriers: the products (this
+//    step's QK, then the previous step's PV) and the vector work (softmax,
 //    staging); waves 4..7, which share SIMDs with waves 0..3, run one phase
-//    behind, so MFMA and VALU phases of the two groups overlap.
+//    behind, so in every phase each SIMD has one wave on the matrix cores and
+//    one on the vector units.
 //  * The causal mask is applied only on steps that reach the diagonal; keys
 //    past the context are masked and their V entries zeroed when staged.
 #include <math.h>
@@ -165,8 +168,12 @@ prefill_chunk_kernel(void* __restrict__ out, const uint16_t* __restrict__ q,
   constexpr int NCH = 4 * CPT / kPfThreads;  // staging chunks per thread per step (K and V each)
 
   constexpr int kAhead = 3;           // steps whose loads are in flight while a step is consumed
-  constexpr int NBUF = kAhead + 1;
-  __shared__ __attribute__((aligned(16))) unsigned char lds[NBUF][2][4 * TILE];  // [buffer][K, V]
+  // K(t) is read one step before V(t), so V keeps one buffer more
+  constexpr int NK = kAhead + 1, NV = kAhead + 2;
+  __shared__ __attribute__((aligned(16))) unsigned char ldsK[NK][4 * TILE];
+  __shared__ __attribute__((aligned(16))) unsigned char ldsV[NV][4 * TILE];
+  auto kbuf = [&](int t) -> unsigned char* { return ldsK[t % NK]; };
+  auto vbuf = [&](int t) -> unsigned char* { return ldsV[t % NV]; };
   static_assert(kPfWaves == 8, "the phase schedule pairs waves w and w + 4 on one SIMD");
 
   // Longest work first.  The causal work of a (chunk, query tile) unit grows
@@ -296,7 +303,7 @@ prefill_chunk_kernel(void* __restrict__ out, const uint16_t* __restrict__ q,
       blk[k] = tab[lb < nblk ? lb : nblk - 1];
     }
   };
-  auto issue_blocks = [&](int t, const int32_t (&blk)[NCH], int buf) {
+  auto issue_blocks = [&](int t, const int32_t (&blk)[NCH]) {
 #pragma unroll
     for (int k = 0; k < NCH; ++k) {
       const int lb = 4 * t + __builtin_amdgcn_readfirstlane((tid + kPfThreads * k) / CPT);
@@ -304,8 +311,8 @@ prefill_chunk_kernel(void* __restrict__ out, const uint16_t* __restrict__ q,
         const int off = ((tid + kPfThreads * k) % CPT) * 16;
         const int64_t base = (clamp_block(blk[k], num_blocks) * Hkv + g) * (int64_t)TILE + off;
         const int wbase = (kPfThreads * k + 64 * w) * 16;
-        dma16(kpool + base, lds_offset(&lds[buf][0][wbase]));
-        dma16(vpool + base, lds_offset(&lds[buf][1][wbase]));
+        dma16(kpool + base, lds_offset(kbuf(t) + wbase));
+        dma16(vpool + base, lds_offset(vbuf(t) + wbase));
       }
     }
   };
@@ -320,14 +327,14 @@ prefill_chunk_kernel(void* __restrict__ out, const uint16_t* __restrict__ q,
     return n;
   };
   // This thread's raw V chunks of a staged step (after its loads landed).
-  auto read_raw = [&](int buf, u32x4 (&raw)[NCH]) {
+  auto read_raw = [&](int t, u32x4 (&raw)[NCH]) {
 #pragma unroll
-    for (int k = 0; k < NCH; ++k) raw[k] = *reinterpret_cast<const u32x4*>(&lds[buf][1][(tid + kPfThreads * k) * 16]);
+    for (int k = 0; k < NCH; ++k) raw[k] = *reinterpret_cast<const u32x4*>(vbuf(t) + (tid + kPfThreads * k) * 16);
   };
   // Raw V chunks -> fp16, keys at or past the context zeroed (blocks past the
   // end become zeros), written back in place (each thread rewrites the 16
   // bytes it read); odd blocks with their 4-key halves swapped.
-  auto finish_step = [&](int s, int buf, const u32x4 (&raw)[NCH]) {
+  auto finish_step = [&](int s, const u32x4 (&raw)[NCH]) {
 #pragma unroll
     for (int k = 0; k < NCH; ++k) {
       const int ci = tid + kPfThreads * k;
@@ -336,7 +343,7 @@ prefill_chunk_kernel(void* __restrict__ out, const uint16_t* __restrict__ q,
       const int j = off / 32, hf = (off % 32) / 16;  // dim j, keys 8hf..8hf+7
       u32x4 v = lb < nblk ? v_chunk_to_f16<T>(raw[k], L - (lb * kBlockSize + 8 * hf)) : u32x4{0, 0, 0, 0};
       if (bi & 1) v = u32x4{v[2], v[3], v[0], v[1]};
-      *reinterpret_cast<u32x4*>(&lds[buf][1][bi * TILE + j * 32 + hf * 16]) = v;
+      *reinterpret_cast<u32x4*>(vbuf(s) + bi * TILE + j * 32 + hf * 16) = v;
     }
   };
   // Wait until at most `keep` vector-memory operations of this wave are
@@ -484,19 +491,24 @@ prefill_chunk_kernel(void* __restrict__ out, const uint16_t* __restrict__ q,
   };
 
   // ---- schedule ----------------------------------------------------------------
-  // A step is four phases separated by workgroup barriers: QK (MFMA), softmax
-  // (VALU), PV (MFMA), staging (loads for kAhead steps on, V conversion of the
-  // next step).  Waves 4..7 run one phase behind waves 0..3; as waves w and
-  // w + 4 share a SIMD, one of them issues MFMAs while the other runs VALU work.
-  // Every wave passes the same number of barriers (4 per step plus one).
+  // A step s is two phases separated by workgroup barriers:
+  //  * M(s), on the matrix cores: S(s) = K(s) Q^T, then O += P(s-1) V(s-1);
+  //  * X(s), on the vector units: issue the loads of step s + kAhead, the
+  //    softmax of step s, and the fp16 rewrite of this thread's V chunks of
+  //    step s + 1.
+  // Waves 4..7 run one phase behind waves 0..3; as waves w and w + 4 share a
+  // SIMD, one of them issues MFMAs while the other runs vector work.  Every
+  // wave passes the same number of barriers (2 per step plus one).
   //
-  // Hazards, with phase k of the workgroup between barriers k-1 and k (waves
-  // 0..3 run step s's phases at 4s..4s+3, waves 4..7 at 4s+1..4s+4):
-  //  * K(s+1) is read from phase 4s+4 on; each wave waits for its own loads of
-  //    step s+1 in its PV phase (at 4s+2 or 4s+3);
-  //  * converted V(s+1) is written at 4s+3 / 4s+4 and read from 4s+6 on;
-  //  * buffer (s+kAhead) % NBUF, loaded at 4s+3 / 4s+4, last held step s-1,
-  //    whose final read (PV of waves 4..7) is at 4s-1.
+  // Hazards, with phase k of the workgroup between barriers k and k + 1 and
+  // M(s) in phase 2s (waves 0..3) or 2s + 1 (waves 4..7):
+  //  * K(t) and V(t) are issued in X(t - 3); each thread waits for its own
+  //    loads of step t at the start of M(t - 1) (phase <= 2t - 1), so K(t) is
+  //    complete when read in phases 2t and 2t + 1;
+  //  * V(t) is rewritten as fp16 by its loaders in X(t - 1) (phase <= 2t) and
+  //    read in M(t + 1) (phases 2t + 2, 2t + 3);
+  //  * K(t)'s buffer is reloaded (for K(t + NK)) in X(t + 1), phase >= 2t + 3;
+  //    V(t)'s (for V(t + NV)) in X(t + 2), phase >= 2t + 5.
   const int grp = w >> 2;
   int s_diag = (ctx + i0 + 1) / kStepKeys;  // first step with a key past row i0's position
   s_diag = s_diag < nsteps ? s_diag : nsteps;
@@ -504,13 +516,13 @@ prefill_chunk_kernel(void* __restrict__ out, const uint16_t* __restrict__ q,
   for (int t = 0; t < kAhead && t < nsteps; ++t) {
     int32_t blk[NCH];
     load_blocks(t, blk);
-    issue_blocks(t, blk, t);
+    issue_blocks(t, blk);
   }
   {
     wait_vm(n_loads(1) + n_loads(2));  // step 0's loads have landed
     u32x4 raw[NCH];
     read_raw(0, raw);
-    finish_step(0, 0, raw);
+    finish_step(0, raw);
   }
   lds_barrier();
   if (grp) lds_barrier();
@@ -521,26 +533,27 @@ prefill_chunk_kernel(void* __restrict__ out, const uint16_t* __restrict__ q,
   auto run_steps = [&](auto diag_tag, int s_begin, int s_end) __attribute__((always_inline)) {
 #pragma unroll 1
     for (int s = s_begin; s < s_end; ++s) {
-      const int buf = s % NBUF;
       const bool work = active && kStepKeys * s < kmax_w;
-      if (work) phase_qk(lds[buf][0]);
-      lds_barrier();
-      int32_t blk[NCH];
-      load_blocks(s + kAhead, blk);  // in flight during the softmax
-      if (work) phase_softmax(diag_tag, s);
-      lds_barrier();
+      const bool work_prev = s > 0 && active && kStepKeys * (s - 1) < kmax_w;
       wait_vm(n_loads(s + 2));  // this thread's loads of step s + 1 have landed
-      u32x4 raw[NCH];
-      read_raw((s + 1) % NBUF, raw);
-      if (work) phase_pv(lds[buf][1]);
+      int32_t blk[NCH];
+      load_blocks(s + kAhead, blk);  // in flight during the products
+      if (work) phase_qk(kbuf(s));
+      if (work_prev) phase_pv(vbuf(s - 1));
       lds_barrier();
-      issue_blocks(s + kAhead, blk, (s + kAhead) % NBUF);
-      if (s + 1 < nsteps) finish_step(s + 1, (s + 1) % NBUF, raw);
+      issue_blocks(s + kAhead, blk);
+      if (work) phase_softmax(diag_tag, s);
+      if (s + 1 < nsteps) {
+        u32x4 raw[NCH];
+        read_raw(s + 1, raw);
+        finish_step(s + 1, raw);
+      }
       if (grp == 0 || s + 1 < nsteps) lds_barrier();
     }
   };
   run_steps(std::false_type{}, 0, s_diag);
   run_steps(std::true_type{}, s_diag, nsteps);
+  if (active && kStepKeys * (nsteps - 1) < kmax_w) phase_pv(vbuf(nsteps - 1));
 
   // ---- normalise and write the wave's rows ---------------------------------
   if (!active) return;
