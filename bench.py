@@ -114,6 +114,25 @@ def prefill_flops(w):
     return 4 * w.head_dim * w.n_q_heads * pairs, pairs
 
 
+WARM_MS = 200.0  # minimum wall time of untimed work before a leg's timed steps
+
+
+def warm(fn, count):
+    """`count` untimed calls of fn, then more until they have kept the GPU
+    busy for at least WARM_MS of wall time: after host-side work the GPU's
+    clocks take tens of milliseconds of load to settle (the first ~20 mixed
+    steps after building a batch run ~12 % slower than the rest)."""
+    import torch
+    for _ in range(count):
+        fn()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    while (time.perf_counter() - t0) * 1e3 < WARM_MS:
+        for _ in range(4):
+            fn()
+        torch.cuda.synchronize()
+
+
 def mixed_step(steps, warmup, seed, flush):
     """The mixed chunked-prefill + decode step (16 chunks of 512 queries and
     240 decodes): append both, then prefill attention and decode attention,
@@ -140,9 +159,7 @@ def mixed_step(steps, warmup, seed, flush):
         b.attend_decode_split(outd, between=lambda: rec(3))
         rec(4)
 
-    for _ in range(warmup):
-        step()
-    torch.cuda.synchronize()
+    warm(step, warmup)
     for i in range(steps):
         flush()
         step(ev[i])
@@ -172,6 +189,42 @@ def mixed_step(steps, warmup, seed, flush):
                    "unit": "GB/s",
                    "frac": by["algorithmic_bytes"] / (dpart.mean() * 1e-3) / 1e9 / HBM_PEAK_GBS},
     }
+
+
+def mfma_ceiling_leg(prefill_tflops, iters=2000, reps=5):
+    """The matrix-core rate beside the prefill kernel (paged_kv_mfma_rate):
+    16x16x32 bf16 MFMAs from one and from two waves per SIMD, one wave per
+    SIMD with the softmax's vector mix running on the other, and that vector
+    mix alone; one workgroup per CU, best of `reps` launches."""
+    import numpy as np
+    import torch
+    import paged_kv_cache_gather_amd as pkv
+    n_wg = torch.cuda.get_device_properties(0).multi_processor_count
+    sink = torch.zeros(1, dtype=torch.float32, device="cuda:0")
+    st = torch.cuda.current_stream()
+    res = {"kernel": "mfma_rate_kernel", "workgroups": n_wg, "iters": iters}
+    names = {0: "one_wave_per_simd", 1: "two_waves_per_simd", 2: "with_softmax_mix_beside", 3: "softmax_mix_alone"}
+    for mode, name in names.items():
+        pkv.paged_kv_mfma_rate(mode, n_wg, iters, sink)
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for e0, e1 in ev:
+            e0.record(st)
+            pkv.paged_kv_mfma_rate(mode, n_wg, iters, sink)
+            e1.record(st)
+        torch.cuda.synchronize()
+        us = float(np.min([e0.elapsed_time(e1) for e0, e1 in ev])) * 1e3
+        waves = {0: 4, 1: 8, 2: 4, 3: 0}[mode]
+        flops = n_wg * waves * iters * 8 * 16384
+        r = {"us": us}
+        if flops:
+            r["tflops"] = flops / (us * 1e-6) / 1e12
+            r["frac_of_peak"] = r["tflops"] / MFMA_BF16_PEAK_TFLOPS
+            r["prefill_frac"] = prefill_tflops / r["tflops"]
+        res[name] = r
+    log("matrix-core rate: " + ", ".join(f"{n} {res[n]['tflops']:.0f} TFLOP/s" for n in names.values()
+                                         if "tflops" in res[n])
+        + f" | vector mix alone {res['softmax_mix_alone']['us']:.1f} us | prefill {prefill_tflops:.0f} TFLOP/s")
+    return res
 
 
 def host_allocator_us(b, reps=5):
@@ -349,9 +402,7 @@ def verify_leg(steps, warmup, seed, flush, k=5):
         b.attend_prefill(out)
         rec(3)
 
-    for _ in range(warmup):
-        step()
-    torch.cuda.synchronize()
+    warm(step, warmup)
     for i in range(steps):
         flush()
         step(ev[i])
@@ -399,9 +450,7 @@ def verify_fp8(w, steps, warmup, flush):
         b.attend_verify(out)
         rec(2)
 
-    for _ in range(warmup):
-        step()
-    torch.cuda.synchronize()
+    warm(step, warmup)
     for i in range(steps):
         flush()
         step(ev[i])
@@ -563,9 +612,7 @@ def time_decode(b, out, K, W, flush=None):
         if e is not None:
             e[3].record(stream)
 
-    for _ in range(W):
-        step()
-    torch.cuda.synchronize()
+    warm(step, W)
     t0 = time.perf_counter()
     for i in range(K):
         if flush is not None:
@@ -591,9 +638,7 @@ def fused_step(b, out, K, W, flush):
     import numpy as np
     import torch
     st = torch.cuda.current_stream()
-    for _ in range(W):
-        b.step_decode(out)
-    torch.cuda.synchronize()
+    warm(lambda: b.step_decode(out), W)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
     for i in range(K):
         flush()
@@ -757,10 +802,13 @@ def ceiling_leg(b, K, flush, part_achieved):
 
 
 def main():
+    global WARM_MS
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warm-ms", type=float, default=WARM_MS,
+                    help="after the W warmup steps, keep warming each leg until this much wall time has passed")
     ap.add_argument("--workload", default="llama3_8b_decode",
                     choices=["tinyllama_decode", "llama3_8b_decode", "opt13b_decode"])
     ap.add_argument("--seed", type=int, default=0)
@@ -784,7 +832,7 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(json.dumps({"error": "bench.py measures one GPU: this library has no multi-GPU path "
-                                   "(decode shards by sequence or KV head with no exchange; see DESIGN.md)",
+                                   "(decode would shard by sequence or by KV head with no exchange)",
                           "n_gpus": args.gpus}), flush=True)
         sys.exit(2)
 
@@ -795,10 +843,14 @@ def main():
         copy_calibration()
         return
     flush = CacheFlush()
+    WARM_MS = args.warm_ms
     K, W = args.steps, args.warmup
     out_dtype = None if args.out_dtype == "kv" else "f32"
     if args.only_mixed:
-        print(json.dumps(mixed_step(args.steps, args.warmup, args.seed, flush)), flush=True)
+        r = mixed_step(args.steps, args.warmup, args.seed, flush)
+        if not args.no_ceilings:
+            r["mfma_ceiling"] = mfma_ceiling_leg(r["prefill"]["achieved"])
+        print(json.dumps(r), flush=True)
         return
     if args.only_verify:
         print(json.dumps(verify_leg(args.steps, args.warmup, args.seed, flush)), flush=True)
@@ -823,6 +875,7 @@ def main():
         "n_gpus": 1,
         "steps": K,
         "warmup": W,
+        "warmup_min_ms": WARM_MS,
         "ms_per_step": head["us_per_step"] * 1e-3,
         "higher_is_better": True,
         "scaling": "weak",
@@ -877,6 +930,8 @@ def main():
         res["verify"] = verify_leg(max(5, K // 2), max(2, W // 2), args.seed, flush)
     if not args.no_mixed:
         res["mixed_step"] = mixed_step(max(5, K // 2), max(2, W // 2), args.seed, flush)
+        if not args.no_ceilings:
+            res["mixed_step"]["mfma_ceiling"] = mfma_ceiling_leg(res["mixed_step"]["prefill"]["achieved"])
     print(json.dumps(res), flush=True)
 
 

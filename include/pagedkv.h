@@ -664,6 +664,21 @@ int paged_attention_verify_fp8(void* out, int32_t out_dtype, const void* q, int3
 int paged_kv_read_tiles(const void* k_pool, const void* v_pool, const int64_t* tiles, int64_t n_k_tiles,
                         int64_t n_tiles, int64_t tile_bytes, uint32_t* sink, void* stream);
 
+/* The matrix-core rate beside the chunked-prefill kernel, whose Q K^T and
+ * P V products ("The detour, what really happens inside one forward pass",
+ * Life of a prompt) are 16x16x32 bf16/fp16 MFMAs issued by two waves per SIMD
+ * while the partner wave runs the softmax.  n_workgroups workgroups of 512
+ * threads, one per CU, each of whose waves 0..3 issues iters x 8 independent
+ * 16x16x32 bf16 MFMAs (16384 flops each); mode 0: waves 4..7 idle; mode 1:
+ * waves 4..7 issue the same MFMAs; mode 2: waves 4..7 run, per eight partner
+ * MFMAs, 4 exps and 14 other vector operations (the prefill softmax's mix);
+ * mode 3: that vector work alone.  Matrix flops per launch: n_workgroups *
+ * W * iters * 8 * 16384 with W = 8 in mode 1, 4 in modes 0 and 2, 0 in mode 3.
+ * sink (device float [1]) is written only if a result hits a fixed value.
+ * Errors: PKV_EINVAL for a mode outside 0..3, n_workgroups outside
+ * [1, 65535], iters outside [1, 2^24] or a NULL sink. */
+int paged_kv_mfma_rate(int32_t mode, int32_t n_workgroups, int32_t iters, float* sink, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -122,6 +122,7 @@ _sig("paged_attention_verify", ctypes.c_int, _P, _i32, _P, _P, _P, _P, _i32, _P,
 _sig("paged_attention_verify_fp8", ctypes.c_int, _P, _i32, _P, _i32, _P, _P, _f32, _f32, _P, _i32, _P, _P, _i32, _i32,
      _i32, _i32, _i32, _i32, _i32, _i64, _i32, _f32, _P, _i64, _P)
 _sig("paged_kv_read_tiles", ctypes.c_int, _P, _P, _P, _i64, _i64, _i64, _P, _P)
+_sig("paged_kv_mfma_rate", ctypes.c_int, _i32, _i32, _i32, _P, _P)
 _sig("paged_attention_prefill_chunk", ctypes.c_int, _P, _i32, _P, _P, _P, _P, _i32, _P, _P, _i32,
      _i32, _i32, _i32, _i32, _i32, _i32, _i64, _i32, _f32, _i32, _P)
 
@@ -887,3 +888,12 @@ def paged_kv_read_tiles(k_pool: torch.Tensor, v_pool, tiles, n_k_tiles: int, n_t
         raise PagedKVError(PKV_EINVAL, "contiguous read beyond the buffer")
     _check(_lib.paged_kv_read_tiles(_ptr(k_pool), _ptr(v_pool), _ptr(tiles), n_k_tiles, n_tiles, tile_bytes,
                                     _ptr(sink), _stream(stream, k_pool.device)))
+
+
+def paged_kv_mfma_rate(mode: int, n_workgroups: int, iters: int, sink: torch.Tensor, stream=None):
+    """The matrix-core rate beside the prefill kernel (16x16x32 bf16 MFMAs;
+    mode 0: one wave per SIMD, 1: two, 2: one with a softmax-like vector
+    wave beside it, 3: that vector wave alone); sink: device float32 [1]."""
+    _dev(sink, "sink", torch.float32)
+    _check(_lib.paged_kv_mfma_rate(int(mode), int(n_workgroups), int(iters), _ptr(sink),
+                                   _stream(stream, sink.device)))

@@ -1,5 +1,6 @@
-// Read-only bandwidth passes that the benchmark sets beside the decode
-// kernels: the same (block, KV head) tiles a decode step reads through its
+// Ceilings that the benchmark sets beside the attention kernels.
+//
+// Read-only bandwidth passes, beside the decode kernels: the same (block, KV head) tiles a decode step reads through its
 // block tables ("How the attention kernel actually reads paged blocks", vLLM
 // Serving deep dive: block by block, wherever the table points), read once
 // each with no attention arithmetic, and a plain contiguous read of the same
@@ -13,6 +14,17 @@
 // instruction covers 1 KiB.  Each thread has kUnroll loads in flight before
 // it folds them into a running XOR; the result is stored only if it hits a
 // constant, which keeps every load alive without a store per thread.
+//
+// The matrix-core rate, beside the chunked-prefill kernel (whose products
+// are 16x16x32 bf16 MFMAs, two waves to a SIMD, each pairing its products
+// with the other wave's softmax): one 512-thread workgroup per CU (its LDS
+// reservation keeps a second one off the CU), waves w and w + 4 on one SIMD.
+// Mode 0: waves 0..3 issue MFMAs (eight independent accumulators), 4..7 idle;
+// mode 1: all eight waves issue MFMAs; mode 2: waves 0..3 issue MFMAs while
+// 4..7 run the prefill softmax's vector mix (per eight MFMAs of the partner:
+// four exps and fourteen other vector operations, fma / max / pack, as in a
+// 64-key step's 68 MFMAs against ~32 exps and ~120 other operations); mode
+// 3: that vector mix alone.  Nothing here is the method's arithmetic.
 #include <string>
 
 #include "pkv_device.h"
@@ -50,6 +62,58 @@ read_tiles_kernel(const unsigned char* __restrict__ kpool, const unsigned char* 
   if (x == 0x9e3779b9u) sink[0] = x;
 }
 
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+constexpr int kRateThreads = 512;
+constexpr int kRateChains = 8;  // independent accumulators per wave
+
+template <int MODE>
+__global__ void __launch_bounds__(kRateThreads, 1) mfma_rate_kernel(int iters, float seed, float* __restrict__ sink) {
+  __shared__ float reserve[36 * 1024];  // 144 KiB: one workgroup per CU
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const bool mfma_wave = w < 4 || MODE == 1;
+  const bool valu_wave = w >= 4 && (MODE == 2 || MODE == 3);
+  float r = 0.f;
+  if (mfma_wave && MODE != 3) {
+    bf16x8_t a, b;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      a[i] = (__bf16)(seed * (float)(lane + i));
+      b[i] = (__bf16)(seed * (float)(i - lane));
+    }
+    f32x4 c[kRateChains];
+#pragma unroll
+    for (int k = 0; k < kRateChains; ++k) c[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+      for (int k = 0; k < kRateChains; ++k) c[k] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c[k], 0, 0, 0);
+    }
+#pragma unroll
+    for (int k = 0; k < kRateChains; ++k) r += c[k][0] + c[k][1] + c[k][2] + c[k][3];
+  }
+  if (valu_wave) {
+    float x[4], m = seed;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) x[k] = seed * (float)(lane + k);
+    uint32_t pk = 0;
+    for (int it = 0; it < iters; ++it) {
+      // per eight partner MFMAs: 4 exps, 4 fmas, 4 maxima, 2 packs, 4 adds
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(x[k], 0.5f, -m));
+        m = fmaxf(m, e);
+        x[k] = x[k] + e * 0.25f;
+      }
+      pk ^= __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(x[0], x[1])) ^
+            __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(x[2], x[3]));
+    }
+    r += x[0] + x[1] + x[2] + x[3] + m + (float)(pk & 1u);
+  }
+  reserve[threadIdx.x] = r;
+  __syncthreads();
+  const float v = reserve[(threadIdx.x + 64) % kRateThreads];
+  if (v == 1234.5f) sink[0] = v;  // keeps the work alive
+}
+
 }  // namespace
 }  // namespace pkv
 
@@ -76,5 +140,23 @@ extern "C" int paged_kv_read_tiles(const void* k_pool, const void* v_pool, const
                      tile_bytes, sink);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(PKV_EHIP, std::string("paged_kv_read_tiles: ") + hipGetErrorString(e));
+  return ok();
+}
+
+extern "C" int paged_kv_mfma_rate(int32_t mode, int32_t n_workgroups, int32_t iters, float* sink, void* stream) {
+  if (mode < 0 || mode > 3) return fail(PKV_EINVAL, "paged_kv_mfma_rate: mode must be 0..3");
+  if (n_workgroups < 1 || n_workgroups > 65535 || iters < 1 || iters > (1 << 24))
+    return fail(PKV_EINVAL, "paged_kv_mfma_rate: n_workgroups in [1, 65535], iters in [1, 2^24]");
+  if (!sink) return fail(PKV_EINVAL, "paged_kv_mfma_rate: NULL sink");
+  const dim3 grid((unsigned)n_workgroups), block(pkv::kRateThreads);
+  const hipStream_t st = (hipStream_t)stream;
+  switch (mode) {
+    case 0: hipLaunchKernelGGL(pkv::mfma_rate_kernel<0>, grid, block, 0, st, iters, 1e-3f, sink); break;
+    case 1: hipLaunchKernelGGL(pkv::mfma_rate_kernel<1>, grid, block, 0, st, iters, 1e-3f, sink); break;
+    case 2: hipLaunchKernelGGL(pkv::mfma_rate_kernel<2>, grid, block, 0, st, iters, 1e-3f, sink); break;
+    default: hipLaunchKernelGGL(pkv::mfma_rate_kernel<3>, grid, block, 0, st, iters, 1e-3f, sink); break;
+  }
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(PKV_EHIP, std::string("paged_kv_mfma_rate: ") + hipGetErrorString(e));
   return ok();
 }
