@@ -117,19 +117,28 @@ def prefill_flops(w):
 WARM_MS = 200.0  # minimum wall time of untimed work before a leg's timed steps
 
 
-def warm(fn, count):
+def warm(fn, count, flush=None):
     """`count` untimed calls of fn, then more until they have kept the GPU
     busy for at least WARM_MS of wall time: after host-side work the GPU's
     clocks take tens of milliseconds of load to settle (the first ~20 mixed
-    steps after building a batch run ~12 % slower than the rest)."""
+    steps after building a batch run ~12 % slower than the rest).  With
+    `flush`, each call follows a cache flush as the timed ones do, so every
+    launch of the leg sees the same cache state (and a kernel trace's
+    averages agree with the timed steps)."""
     import torch
-    for _ in range(count):
+
+    def one():
+        if flush is not None:
+            flush()
         fn()
+
+    for _ in range(count):
+        one()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     while (time.perf_counter() - t0) * 1e3 < WARM_MS:
         for _ in range(4):
-            fn()
+            one()
         torch.cuda.synchronize()
 
 
@@ -159,7 +168,7 @@ def mixed_step(steps, warmup, seed, flush):
         b.attend_decode_split(outd, between=lambda: rec(3))
         rec(4)
 
-    warm(step, warmup)
+    warm(step, warmup, flush)
     for i in range(steps):
         flush()
         step(ev[i])
@@ -402,7 +411,7 @@ def verify_leg(steps, warmup, seed, flush, k=5):
         b.attend_prefill(out)
         rec(3)
 
-    warm(step, warmup)
+    warm(step, warmup, flush)
     for i in range(steps):
         flush()
         step(ev[i])
@@ -450,7 +459,7 @@ def verify_fp8(w, steps, warmup, flush):
         b.attend_verify(out)
         rec(2)
 
-    warm(step, warmup)
+    warm(step, warmup, flush)
     for i in range(steps):
         flush()
         step(ev[i])
@@ -612,7 +621,7 @@ def time_decode(b, out, K, W, flush=None):
         if e is not None:
             e[3].record(stream)
 
-    warm(step, W)
+    warm(step, W, flush)
     t0 = time.perf_counter()
     for i in range(K):
         if flush is not None:
@@ -638,7 +647,7 @@ def fused_step(b, out, K, W, flush):
     import numpy as np
     import torch
     st = torch.cuda.current_stream()
-    warm(lambda: b.step_decode(out), W)
+    warm(lambda: b.step_decode(out), W, flush)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
     for i in range(K):
         flush()
