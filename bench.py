@@ -636,6 +636,25 @@ def time_decode(b, out, K, W, flush=None):
             "reduce_ms": np.array([ev[i][2].elapsed_time(ev[i][3]) for i in range(K)])}
 
 
+def time_attend(b, out, K, W, flush=None):
+    """K timed one-call decode attentions (paged_attention_decode, no cache
+    write), each after a cache flush when given: the whole-context path's
+    single launch."""
+    import numpy as np
+    import torch
+    st = torch.cuda.current_stream()
+    warm(lambda: b.attend_decode(out), W, flush)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    for e0, e1 in ev:
+        if flush is not None:
+            flush()
+        e0.record(st)
+        b.attend_decode(out)
+        e1.record(st)
+    torch.cuda.synchronize()
+    return np.array([e0.elapsed_time(e1) for e0, e1 in ev])
+
+
 def fused_step(b, out, K, W, flush):
     """The step in one call (paged_attention_decode_append or its 8-bit
     variant: the new rows' cache write rides in the shared-run launch, then
@@ -704,39 +723,58 @@ def decode_leg(w, K, W, out_dtype, seed, flush, fp8=False, modes=True, profile=N
     log(f"building {w.name}{' (8-bit cache)' if fp8 else ''}: {w.description}")
     b = DeviceBatch(w, "cuda:0", fill="device", out_dtype=out_dtype, **kw)
     out = b.new_decode_out()
+    import paged_kv_cache_gather_amd as pkv
+    whole = (not fp8) and pkv.paged_attention_decode_whole_context(
+        w.n_decode, w.n_q_heads, w.n_kv_heads, w.head_dim, w.dtype, b.decode.max_context_len)
     t = time_decode(b, out, K, W, flush)
-    warm = time_decode(b, out, K, 2)
-    wflush = time_decode(b, out, K, 2, CacheFlush(mode="write") if flush is not None else None)
+    warm3 = time_decode(b, out, K, 2)
     by = decode_bytes(b)
-    part = _stats_us(t["part_ms"])
+    split_part = _stats_us(t["part_ms"])
+    if whole:
+        # the one-call forms take the whole-context path: its single launch
+        # is the pass; the split path's partition pass is reported beside it
+        part_ms = time_attend(b, out, K, W, flush)
+        warm_ms = time_attend(b, out, K, 2)
+        wflush_ms = time_attend(b, out, K, 2, CacheFlush(mode="write") if flush is not None else None)
+    else:
+        part_ms = t["part_ms"]
+        warm_ms = warm3["part_ms"]
+        wflush_ms = time_decode(b, out, K, 2, CacheFlush(mode="write") if flush is not None else None)["part_ms"]
+    part = _stats_us(part_ms)
     achieved = by["algorithmic_bytes"] / (part["mean"] * 1e-6) / 1e9
-    warm_part = _stats_us(warm["part_ms"])
+    warm_part = _stats_us(warm_ms)
     g = fused_step(b, out, K, W, flush) if modes else None
     step_us = g["flushed_us"]["mean"] if g else _stats_us(t["step_ms"])["mean"]
     tok_s = w.n_decode / (step_us * 1e-6)
     log(f"{w.name}{' fp8' if fp8 else ''}: step {step_us:.1f} us ({tok_s / 1e6:.3f} M tokens/s, flushed) | "
-        f"partitions {part['mean']:.1f} us = {achieved:.0f} GB/s ({achieved / HBM_PEAK_GBS:.1%}; caches warm: "
+        f"{'whole-context launch' if whole else 'partitions'} {part['mean']:.1f} us = {achieved:.0f} GB/s "
+        f"({achieved / HBM_PEAK_GBS:.1%}; caches warm: "
         f"{warm_part['mean']:.1f} us) | append {t['append_ms'].mean() * 1e3:.1f} | reduce "
         f"{t['reduce_ms'].mean() * 1e3:.1f} us" + (f" | back to back {g['back_to_back_wall_us']:.1f} us, graph "
-                                                   f"{g['graph_flushed_us']['mean']:.1f} us" if g else ""))
-    kernel = ("decode partition pass (decode_shared_kernel + " +
+                                                   f"{g['graph_flushed_us']['mean']:.1f} us" if g else "")
+        + (f" | split path's partitions {split_part['mean']:.1f} us" if whole else ""))
+    kernel = ("decode_whole_kernel (whole-context path: one launch)" if whole else
+              "decode partition pass (decode_shared_kernel + " +
               ("decode_fp8_partition_kernel)" if fp8 else "decode_partition_kernel)"))
     res = {
         "workload": w.name, "description": w.description, "batch": w.n_decode,
         "kv_cache": "fp8_e4m3 (OCP E4M3, one fp32 scale per pool)" if fp8 else w.dtype,
         "out_dtype": str(b.out_dtype).replace("torch.", ""),
         "step": ((("paged_attention_decode_fp8_append" if fp8 else "paged_attention_decode_append") +
-                  " (cache write + partition pass + split-K reduce in one call)") if g else
+                  (" (cache write, then the whole-context launch)" if whole else
+                   " (cache write + partition pass + split-K reduce in one call)")) if g else
                  "cache write, partition pass, reduce (three calls)"),
+        "path": "whole-context" if whole else "split-context",
         "us_per_step": step_us, "tokens_per_s": tok_s,
         "timing": {"caches": "1 GiB read through the caches before every timed step (outside the events)",
                    "one_call_flushed_us": g["flushed_us"] if g else None,
                    "one_call_back_to_back_wall_us": g["back_to_back_wall_us"] if g else None,
                    "one_call_graph_flushed_us": g["graph_flushed_us"] if g else None,
                    "three_calls_flushed_us": _stats_us(t["step_ms"]),
-                   "three_calls_warm_us": _stats_us(warm["step_ms"])},
-        "breakdown_us": {"append": float(t["append_ms"].mean()) * 1e3, "partitions": part["mean"],
-                         "reduce": float(t["reduce_ms"].mean()) * 1e3},
+                   "three_calls_warm_us": _stats_us(warm3["step_ms"])},
+        "breakdown_us": {"append": float(t["append_ms"].mean()) * 1e3, "partitions": split_part["mean"],
+                         "reduce": float(t["reduce_ms"].mean()) * 1e3,
+                         **({"whole_context_launch": part["mean"]} if whole else {})},
         "roofline": {"bound": "hbm", "kernel": kernel, "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS,
                      "traffic": (profiled_traffic(profile, ["decode.hip", "pkv_device.h"])
@@ -744,9 +782,9 @@ def decode_leg(w, K, W, out_dtype, seed, flush, fp8=False, modes=True, profile=N
                      "algorithmic_bytes": by["algorithmic_bytes"], "launch_us": part,
                      "caches_warm": {"launch_us": warm_part,
                                      "achieved": by["algorithmic_bytes"] / (warm_part["mean"] * 1e-6) / 1e9},
-                     "after_write_flush": {"launch_us": _stats_us(wflush["part_ms"]),
+                     "after_write_flush": {"launch_us": _stats_us(wflush_ms),
                                            "achieved": by["algorithmic_bytes"] /
-                                           (float(wflush["part_ms"].mean()) * 1e-3) / 1e9}},
+                                           (float(wflush_ms.mean()) * 1e-3) / 1e9}},
         "bytes": by,
         "logical_gbs": (by["logical_kv_bytes"] + by["other_bytes"]) / (part["mean"] * 1e-6) / 1e9,
     }

@@ -384,6 +384,18 @@ int paged_kv_swap_blocks(const void* src_k_pool, const void* src_v_pool, int64_t
 /* Context tokens one decode partition covers (the split-context unit). */
 int32_t paged_attention_decode_partition_size(void);
 
+/* 1 when paged_attention_decode and paged_attention_decode_append take the
+ * whole-context path for these sizes, 0 otherwise (the split-context path;
+ * paged_attention_decode_partitions / _reduce always split).  The path is
+ * taken when max_context_len <= 2048, num_seqs * n_kv_heads <= 256 (the
+ * decode of a small batch is bound by the latency of one round of reads, not
+ * by HBM bandwidth) and (n_q_heads / n_kv_heads) * head_dim * element bytes
+ * <= 1024; never for 8-bit pools.  ("The decode stage, and how to spot the
+ * waste", Life of a prompt: the same attention, one query per sequence.)
+ * Invalid sizes give 0. */
+int32_t paged_attention_decode_whole_context(int32_t num_seqs, int32_t n_q_heads, int32_t n_kv_heads,
+                                             int32_t head_dim, int32_t kv_dtype, int32_t max_context_len);
+
 /* Device workspace bytes paged_attention_decode needs for these sizes
  * (0 when every sequence fits in one partition): the partial softmax states
  * (max, sum and unnormalised output, fp32) of every partition of every
@@ -412,6 +424,11 @@ int64_t paged_attention_decode_workspace_bytes(int32_t num_seqs, int32_t n_q_hea
  * sharing", vLLM Serving deep dive), one workgroup reads that partition once
  * for all of them (up to 32 query rows, on MFMA; f16/bf16 K/V only): a
  * third kernel, queued on `stream` before the per-sequence partition pass.
+ * Short contexts in a small batch (paged_attention_decode_whole_context
+ * says when): one launch instead, one workgroup per (sequence, KV head)
+ * taking the whole context with its blocks dealt to 16 waves and the waves'
+ * softmax states merged on chip; no partition is split or shared, the
+ * workspace is not touched.
  *   out           device [num_seqs][n_q_heads][head_dim], out_dtype
  *                 (PKV_F32, or the KV dtype).
  *   q             device [num_seqs][n_q_heads][head_dim], kv_dtype.
@@ -439,8 +456,9 @@ int paged_attention_decode(void* out, int32_t out_dtype, const void* q, const vo
  * step of "The decode stage, and how to spot the waste", Life of a prompt:
  * append the new key and value, then attend over all of them).  With f16 /
  * bf16 pools the rows are written by extra workgroups of the shared-run
- * kernel, so the write needs no launch of its own; with f32 pools the write
- * is launched first.  The new token's block must be the sequence's own (as
+ * kernel, or on the whole-context path by the workgroup of each (sequence,
+ * KV head) before it reads, so the write needs no launch of its own; with
+ * f32 pools the write is launched first.  The new token's block must be the sequence's own (as
  * paged_kv_seq_append leaves it, copy-on-write done) and context_lens must
  * already count the new token.
  *   k_new, v_new   device [num_seqs][n_kv_heads * head_dim] rows, kv_dtype,

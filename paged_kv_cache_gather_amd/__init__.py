@@ -123,6 +123,7 @@ _sig("paged_attention_verify_fp8", ctypes.c_int, _P, _i32, _P, _i32, _P, _P, _f3
      _i32, _i32, _i32, _i32, _i32, _i64, _i32, _f32, _P, _i64, _P)
 _sig("paged_kv_read_tiles", ctypes.c_int, _P, _P, _P, _i64, _i64, _i64, _P, _P)
 _sig("paged_kv_mfma_rate", ctypes.c_int, _i32, _i32, _i32, _P, _P)
+_sig("paged_attention_decode_whole_context", ctypes.c_int32, _i32, _i32, _i32, _i32, _i32, _i32)
 _sig("paged_attention_prefill_chunk", ctypes.c_int, _P, _i32, _P, _P, _P, _P, _i32, _P, _P, _i32,
      _i32, _i32, _i32, _i32, _i32, _i32, _i64, _i32, _f32, _i32, _P)
 
@@ -897,3 +898,12 @@ def paged_kv_mfma_rate(mode: int, n_workgroups: int, iters: int, sink: torch.Ten
     _dev(sink, "sink", torch.float32)
     _check(_lib.paged_kv_mfma_rate(int(mode), int(n_workgroups), int(iters), _ptr(sink),
                                    _stream(stream, sink.device)))
+
+
+def paged_attention_decode_whole_context(num_seqs: int, n_q_heads: int, n_kv_heads: int, head_dim: int,
+                                         kv_dtype, max_context_len: int) -> bool:
+    """Whether paged_attention_decode / _append take the one-launch
+    whole-context path for these sizes (short contexts, small batch)."""
+    return bool(_lib.paged_attention_decode_whole_context(int(num_seqs), int(n_q_heads), int(n_kv_heads),
+                                                          int(head_dim), dtype_code(kv_dtype),
+                                                          int(max_context_len)))

@@ -98,9 +98,10 @@ __device__ __forceinline__ int clamp_len(int L, int max_context_len) {
   return L < 0 ? 0 : (L > max_context_len ? max_context_len : L);
 }
 
-// The partition pass of sequence s, KV head g, partition p (n tokens): the G
-// query heads of the KV head are the workgroup's R = G rows.
-template <typename T, int D, int G, int OutCode>
+// The partition pass of sequence s, KV head g, partition p (n tokens) of PART
+// context tokens, on WAVES waves: the G query heads of the KV head are the
+// workgroup's R = G rows.
+template <typename T, int D, int G, int OutCode, int PART = kPart, int WAVES = kWaves>
 __device__ __forceinline__ void partition_rows(
     float* __restrict__ smem, float (*__restrict__ sml)[2], void* __restrict__ out, float* __restrict__ ws_o,
     float* __restrict__ ws_ml, const typename T::bits* __restrict__ q, const unsigned char* __restrict__ kpool,
@@ -111,7 +112,7 @@ __device__ __forceinline__ void partition_rows(
   constexpr int ES = T::kBytes;
   constexpr int X = 16 / ES;                 // elements per 16-byte chunk
   constexpr int C = D / X;                   // chunks per K row
-  constexpr int TPW = kPart / kWaves;        // context tokens per wave
+  constexpr int TPW = PART / WAVES;          // context tokens per wave
   constexpr int IT = TPW / 64;               // score iterations per wave (one token per lane)
   constexpr int CPR = ES;                    // 16-byte chunks per V dim-row of one block
   constexpr int TPC = kBlockSize / CPR;      // tokens per V chunk
@@ -125,7 +126,7 @@ __device__ __forceinline__ void partition_rows(
   // (last) partition keeps every wave busy; wave w takes blocks [bw0, bw1),
   // at most TPW tokens
   const int nbp = (n + kBlockSize - 1) / kBlockSize;
-  const int bw0 = (w * nbp) / kWaves, bw1 = ((w + 1) * nbp) / kWaves;
+  const int bw0 = (w * nbp) / WAVES, bw1 = ((w + 1) * nbp) / WAVES;
   const int wt0 = bw0 * kBlockSize;                         // wave's first token (partition-local)
   const int wend = bw1 * kBlockSize < n ? bw1 * kBlockSize : n;
   const int wn = wend - wt0 < 0 ? 0 : wend - wt0;            // its tokens
@@ -290,20 +291,20 @@ __device__ __forceinline__ void partition_rows(
   __syncthreads();
 
   // ---- merge the waves' partial softmax states ------------------------------
-  for (int i = tid; i < R * D; i += kThreads) {
+  for (int i = tid; i < R * D; i += WAVES * 64) {
     const int r = i / D, j = i % D;
     float Mx = sml[r][0];
 #pragma unroll
-    for (int k = 1; k < kWaves; ++k) Mx = fmaxf(Mx, sml[k * R + r][0]);
+    for (int k = 1; k < WAVES; ++k) Mx = fmaxf(Mx, sml[k * R + r][0]);
     float acc = 0.f, l = 0.f;
 #pragma unroll
-    for (int k = 0; k < kWaves; ++k) {
+    for (int k = 0; k < WAVES; ++k) {
       const float f = __builtin_amdgcn_exp2f(sml[k * R + r][0] - Mx);  // 0 for a wave with no tokens
       acc = fmaf(f, so[k][r][j], acc);
       l = fmaf(f, sml[k * R + r][1], l);
     }
     const int64_t row = (int64_t)s * Hq + g * G + r;
-    const int nparts = (clamp_len(lens[s], max_context_len) + kPart - 1) / kPart;
+    const int nparts = (clamp_len(lens[s], max_context_len) + PART - 1) / PART;
     if (nparts == 1) {
       store_out<OutCode>(out, row * D + j, acc / l);
     } else {
@@ -1048,6 +1049,62 @@ decode_partition_kernel(void* __restrict__ out, float* __restrict__ ws_o, float*
                                    num_blocks, max_context_len, scale_log2, max_parts);
 }
 
+// ---- short contexts in a small batch: one launch, no merge ------------------
+// When every context fits kWholeSpan tokens and the batch has few (sequence,
+// KV head) pairs, split partitions and the merge would leave the chip idle
+// between three launches.  Instead one workgroup of kWholeWaves waves takes
+// a whole (sequence, KV head): the sequence's blocks are dealt evenly to its
+// waves (a short context still uses all of them), the waves' softmax states
+// merge in LDS and the output is written directly.  Partitions that
+// neighbours share are read per sequence on this path.
+constexpr int kWholeSpan = 2048;      // context tokens one workgroup takes
+constexpr int kWholeWaves = 16;       // its waves (4 per SIMD)
+constexpr int kWholeMaxUnits = 256;   // (sequence, KV head) pairs: one workgroup per CU
+
+// Does a batch take the whole-context path?  The per-wave accumulators must
+// leave the 16-wave workgroup within 128 registers (G x D x element bytes
+// <= 1024: G <= 8 at head_dim 64, G <= 4 at 128 for 16-bit pools).
+inline bool whole_context(int B, int Hkv, int G, int D, int es, int max_context_len) {
+  return max_context_len <= kWholeSpan && (int64_t)B * Hkv <= kWholeMaxUnits && G * D * es <= 1024;
+}
+
+// With this step's new rows (app.T > 0), the workgroup of (sequence s, KV
+// head g) first writes head g of sequence s's new row into the pool: the
+// row's block is the sequence's own (copy-on-write done before the append),
+// so no other workgroup reads it, and a workgroup-scope release / acquire
+// around a barrier orders the write before this workgroup's reads.
+template <typename T, int D, int G, int OutCode>
+__global__ void __launch_bounds__(kWholeWaves * 64, 1)
+decode_whole_kernel(void* __restrict__ out, const typename T::bits* __restrict__ q, const unsigned char* kpool,
+                    const unsigned char* vpool, const int32_t* __restrict__ tables, int max_blocks,
+                    const int32_t* __restrict__ lens, int Hkv, int64_t num_blocks, int max_context_len,
+                    float scale_log2, AppendArgs app) {
+  constexpr int RMAX = G;
+  constexpr int SMEM = (kWholeSpan > kWholeWaves * D ? kWholeSpan : kWholeWaves * D) * RMAX;
+  __shared__ __attribute__((aligned(16))) float smem[SMEM];
+  __shared__ float sml[kWholeWaves * RMAX][2];
+  const int g = blockIdx.x, s = blockIdx.y;
+  if (app.T > 0) {  // uniform
+    constexpr int C = D * T::kBytes / 16;  // 16-byte pool chunks per head row
+    if (s < app.T && threadIdx.x < C)
+      cache_write_chunk<T::kBytes>(app.key, app.value, app.kstride_b, app.vstride_b, app.kpool, app.vpool,
+                                   app.slots[s], app.num_slots, s, g, threadIdx.x, Hkv, D);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __syncthreads();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+  }
+  const int L = clamp_len(lens[s], max_context_len);
+  if (L == 0) {  // defined result for an empty context: zeros
+    for (int i = threadIdx.x; i < G * D; i += kWholeWaves * 64)
+      store_out<OutCode>(out, ((int64_t)s * Hkv * G + g * G) * D + i, 0.f);
+    return;
+  }
+  partition_rows<T, D, G, OutCode, kWholeSpan, kWholeWaves>(smem, sml, out, nullptr, nullptr, q, kpool, vpool,
+                                                            tables + (int64_t)s * max_blocks, lens, s, g, 0, L, Hkv,
+                                                            num_blocks, max_context_len, scale_log2, 1);
+}
+
+
 template <int D, int OutCode, bool PerToken>
 __global__ void __launch_bounds__(64)
 decode_reduce_kernel(void* __restrict__ out, const float* __restrict__ ws_o, const float* __restrict__ ws_ml,
@@ -1221,7 +1278,22 @@ void launch_reduce(const DecodeArgs& a, int G) {
 }
 
 template <typename T, int D, int G, int OutCode>
+void launch_whole(const DecodeArgs& a) {
+  if constexpr (G * D * T::kBytes <= 1024) {
+    hipLaunchKernelGGL((decode_whole_kernel<T, D, G, OutCode>), dim3((unsigned)a.Hkv, (unsigned)a.B),
+                       dim3(kWholeWaves * 64), 0, a.stream, a.out, (const typename T::bits*)a.q, a.kpool, a.vpool,
+                       a.tables, a.max_blocks, a.lens, a.Hkv, a.num_blocks, a.max_context_len, a.scale_log2,
+                       a.app);
+  }
+}
+
+template <typename T, int D, int G, int OutCode>
 void launch_decode(const DecodeArgs& a, bool partitions, bool reduce) {
+  // the one-call form (partitions and merge together) of a short, small batch
+  if (partitions && reduce && whole_context(a.B, a.Hkv, G, D, T::kBytes, a.max_context_len)) {
+    launch_whole<T, D, G, OutCode>(a);
+    return;
+  }
   if (partitions && T::kBytes == 2) launch_shared<T, T, D, G, OutCode>(a);
   if (partitions)
     hipLaunchKernelGGL((decode_partition_kernel<T, D, G, OutCode>),
@@ -1306,6 +1378,15 @@ using pkv::fail;
 using pkv::ok;
 
 extern "C" int32_t paged_attention_decode_partition_size(void) { return pkv::kPart; }
+
+extern "C" int32_t paged_attention_decode_whole_context(int32_t num_seqs, int32_t n_q_heads, int32_t n_kv_heads,
+                                                        int32_t head_dim, int32_t kv_dtype, int32_t max_context_len) {
+  const int es = pkv::esize_of(kv_dtype);
+  if (num_seqs <= 0 || n_kv_heads <= 0 || n_q_heads <= 0 || n_q_heads % n_kv_heads || max_context_len < 0 ||
+      kv_dtype == PKV_FP8_E4M3 || !es)
+    return 0;
+  return pkv::whole_context(num_seqs, n_kv_heads, n_q_heads / n_kv_heads, head_dim, es, max_context_len) ? 1 : 0;
+}
 
 extern "C" int64_t paged_attention_decode_workspace_bytes(int32_t num_seqs, int32_t n_q_heads,
                                                           int32_t head_dim, int32_t max_context_len) {
