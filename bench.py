@@ -124,7 +124,9 @@ def warm(fn, count, flush=None):
     steps after building a batch run ~12 % slower than the rest).  With
     `flush`, each call follows a cache flush as the timed ones do, so every
     launch of the leg sees the same cache state (and a kernel trace's
-    averages agree with the timed steps)."""
+    averages agree with the timed steps); without it, or with the
+    write-flush variant (diagnostic timings that follow a read-flushed leg),
+    only the `count` calls run."""
     import torch
 
     def one():
@@ -135,6 +137,8 @@ def warm(fn, count, flush=None):
     for _ in range(count):
         one()
     torch.cuda.synchronize()
+    if flush is None or getattr(flush, "mode", "read") != "read":
+        return  # unflushed and write-flushed timings follow a read-flushed leg: the clocks are up already
     t0 = time.perf_counter()
     while (time.perf_counter() - t0) * 1e3 < WARM_MS:
         for _ in range(4):
@@ -903,7 +907,8 @@ def main():
         print(json.dumps(verify_leg(args.steps, args.warmup, args.seed, flush)), flush=True)
         return
     w = synth.make_workload(args.workload, seed=args.seed)
-    profile = {n: "decode_partition_" + n for n in ("llama3_8b_decode", "tinyllama_decode", "opt13b_decode")}
+    profile = {n: "decode_partition_" + n for n in ("llama3_8b_decode", "opt13b_decode")}
+    profile["tinyllama_decode"] = "decode_whole_tinyllama_decode"  # the whole-context path
     if args.only_fp8:
         b, _, r = decode_leg(w, K, W, out_dtype, args.seed, flush, fp8=True, modes=not args.no_step_modes,
                              profile="decode_fp8_partition_llama3_8b_decode" if args.workload == "llama3_8b_decode" else None)
