@@ -869,8 +869,6 @@ def paged_attention_prefill_chunk(out: torch.Tensor, q: torch.Tensor, k_pool: to
         _stream(stream, q.device)))
 
 
-__all__ = [n for n in dir() if n.startswith(("paged_", "reshape_", "pkv", "PKV_", "Pool", "PagedKV",
-                                                 "OutOfBlocks", "last_error", "dtype_code", "BLOCK_SIZE"))]
 
 
 def paged_kv_read_tiles(k_pool: torch.Tensor, v_pool, tiles, n_k_tiles: int, n_tiles: int, tile_bytes: int,
@@ -907,3 +905,7 @@ def paged_attention_decode_whole_context(num_seqs: int, n_q_heads: int, n_kv_hea
     return bool(_lib.paged_attention_decode_whole_context(int(num_seqs), int(n_q_heads), int(n_kv_heads),
                                                           int(head_dim), dtype_code(kv_dtype),
                                                           int(max_context_len)))
+
+
+__all__ = [n for n in dir() if n.startswith(("paged_", "reshape_", "pkv", "PKV_", "Pool", "PagedKV",
+                                                 "OutOfBlocks", "last_error", "dtype_code", "BLOCK_SIZE"))]
