@@ -240,6 +240,73 @@ def mfma_ceiling_leg(prefill_tflops, iters=2000, reps=5):
     return res
 
 
+def sweep_decode(K, W, seed, flush):
+    """Decode attention (paged_attention_decode, one call) across batch sizes
+    and uniform context lengths: Llama-3-8B heads (Hq 32 / Hkv 8, d 128, bf16),
+    no shared prefixes, random block placement, each timed call after a cache
+    flush.  The batches at and below 2048 keys with at most 256 (sequence, KV
+    head) pairs take the whole-context path."""
+    import numpy as np
+    import torch
+    import synth
+    import paged_kv_cache_gather_amd as pkv
+    from paged_kv_cache_gather_amd.batch import DeviceBatch
+    rows = []
+    for B in (32, 64, 128, 256):
+        for L in (512, 1024, 2048, 4096, 8192):
+            w = synth.custom_workload(f"sweep_b{B}_l{L}", 32, 8, 128, "bf16", B * (L // 16) + 64, seed,
+                                      decode_lens=[L] * B)
+            b = DeviceBatch(w, "cuda:0", fill="device")
+            b.append_decode()
+            out = b.new_decode_out()
+            us = _stats_us(time_attend(b, out, K, W, flush))["mean"]
+            by = decode_bytes(b)["algorithmic_bytes"]
+            path = "whole" if pkv.paged_attention_decode_whole_context(B, 32, 8, 128, "bf16", L) else "split"
+            rows.append({"B": B, "L": L, "us": us, "bytes": by, "gbs": by / (us * 1e-6) / 1e9, "path": path})
+            log(f"decode sweep B={B:4d} L={L:5d}: {us:8.1f} us  {rows[-1]['gbs']:6.0f} GB/s  ({path})")
+            del b, out
+            torch.cuda.empty_cache()
+    return rows
+
+
+def sweep_prefill(K, W, seed, flush):
+    """The chunked-prefill kernel across head shapes: 16 chunks of 512 queries
+    over cached contexts U[0, 7680] (numpy's default generator, seed `seed`),
+    Hq 32, each timed launch after a cache flush."""
+    import numpy as np
+    import torch
+    import synth
+    from paged_kv_cache_gather_amd.batch import DeviceBatch
+    ctx = np.random.default_rng(seed).integers(0, 7680 + 1, size=16)
+    rows = []
+    for name, hkv, d, dt in (("GQA 4 (Hkv 8), d 128, bf16", 8, 128, "bf16"), ("MHA (Hkv 32), d 128, f16", 32, 128, "f16"),
+                             ("GQA 2 (Hkv 16), d 128, bf16", 16, 128, "bf16"),
+                             ("GQA 16 (Hkv 2), d 128, bf16", 2, 128, "bf16"),
+                             ("GQA 8 (Hkv 4), d 64, f16", 4, 64, "f16"), ("GQA 4 (Hkv 8), d 64, bf16", 8, 64, "bf16")):
+        nb = int(((ctx + 512 + 15) // 16).sum()) + 64
+        w = synth.custom_workload("sweep_prefill", 32, hkv, d, dt, nb, seed, chunk_ctx=ctx, chunk_qlen=[512] * 16)
+        b = DeviceBatch(w, "cuda:0", fill="device")
+        b.append_prefill()
+        out = b.new_prefill_out()
+        st = torch.cuda.current_stream()
+        warm(lambda: b.attend_prefill(out), W, flush)
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+        for e0, e1 in ev:
+            flush()
+            e0.record(st)
+            b.attend_prefill(out)
+            e1.record(st)
+        torch.cuda.synchronize()
+        us = float(np.mean([e0.elapsed_time(e1) for e0, e1 in ev])) * 1e3
+        flops, _ = prefill_flops(w)
+        tf = flops / (us * 1e-6) / 1e12
+        rows.append({"shape": name, "us": us, "tflops": tf, "frac": tf / MFMA_BF16_PEAK_TFLOPS})
+        log(f"prefill sweep {name:30s}: {us:8.1f} us  {tf:5.0f} TFLOP/s  {tf / MFMA_BF16_PEAK_TFLOPS:.1%}")
+        del b, out
+        torch.cuda.empty_cache()
+    return rows
+
+
 def host_allocator_us(b, reps=5):
     """Per-step cost of the host block manager on this batch: append one token
     to every sequence (one batched call, which also returns the slot
@@ -872,6 +939,9 @@ def main():
     ap.add_argument("--no-swap", action="store_true", help="skip the swap-copy leg")
     ap.add_argument("--no-verify", action="store_true", help="skip the verify-attention leg")
     ap.add_argument("--only-verify", action="store_true", help="run only the verify-attention leg")
+    ap.add_argument("--sweep", choices=("decode", "prefill"),
+                    help="time decode across batch sizes and context lengths, or prefill across head shapes, "
+                         "and print one JSON line of rows (not the benchmark line)")
     ap.add_argument("--only-fp8", action="store_true", help="run only the 8-bit-cache decode leg")
     ap.add_argument("--no-other-workloads", action="store_true",
                     help="skip the toy, TinyLlama- and OPT-13B-shaped decode legs")
@@ -902,6 +972,10 @@ def main():
         if not args.no_ceilings:
             r["mfma_ceiling"] = mfma_ceiling_leg(r["prefill"]["achieved"])
         print(json.dumps(r), flush=True)
+        return
+    if args.sweep:
+        fn = sweep_decode if args.sweep == "decode" else sweep_prefill
+        print(json.dumps({"sweep": args.sweep, "rows": fn(K, W, args.seed, flush)}), flush=True)
         return
     if args.only_verify:
         print(json.dumps(verify_leg(args.steps, args.warmup, args.seed, flush)), flush=True)
