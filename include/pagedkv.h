@@ -387,10 +387,11 @@ int32_t paged_attention_decode_partition_size(void);
 /* 1 when paged_attention_decode and paged_attention_decode_append take the
  * whole-context path for these sizes, 0 otherwise (the split-context path;
  * paged_attention_decode_partitions / _reduce always split).  The path is
- * taken when max_context_len <= 2048, num_seqs * n_kv_heads <= 256 (the
- * decode of a small batch is bound by the latency of one round of reads, not
- * by HBM bandwidth) and (n_q_heads / n_kv_heads) * head_dim * element bytes
- * <= 1024; never for 8-bit pools.  ("The decode stage, and how to spot the
+ * taken when max_context_len <= 2048, (n_q_heads / n_kv_heads) * head_dim *
+ * element bytes <= 1024 and, with P = num_seqs * n_kv_heads, either P <= 256
+ * and (P >= 128 or max_context_len <= 1536), or P <= 512 and max_context_len
+ * >= 768 (the decode of a small batch is bound by the latency of one or two
+ * rounds of reads, not by HBM bandwidth); never for 8-bit pools.  ("The decode stage, and how to spot the
  * waste", Life of a prompt: the same attention, one query per sequence.)
  * Invalid sizes give 0. */
 int32_t paged_attention_decode_whole_context(int32_t num_seqs, int32_t n_q_heads, int32_t n_kv_heads,

@@ -1059,13 +1059,22 @@ decode_partition_kernel(void* __restrict__ out, float* __restrict__ ws_o, float*
 // neighbours share are read per sequence on this path.
 constexpr int kWholeSpan = 2048;      // context tokens one workgroup takes
 constexpr int kWholeWaves = 16;       // its waves (4 per SIMD)
-constexpr int kWholeMaxUnits = 256;   // (sequence, KV head) pairs: one workgroup per CU
 
 // Does a batch take the whole-context path?  The per-wave accumulators must
 // leave the 16-wave workgroup within 128 registers (G x D x element bytes
-// <= 1024: G <= 8 at head_dim 64, G <= 4 at 128 for 16-bit pools).
+// <= 1024: G <= 8 at head_dim 64, G <= 4 at 128 for 16-bit pools).  Measured
+// against the split path on uniform and prefix-sharing batches (Llama-3-8B
+// heads): up to 256 (sequence, KV head) pairs — one round of workgroups, one
+// per CU — it wins except when fewer than 128 pairs hold contexts past 1536
+// tokens (then too few CUs take part, and the split path's 4x more
+// workgroups win); up to 512 pairs it wins from 768-token contexts on; past
+// that, or for shorter contexts, reading shared partitions once and the
+// split path's occupancy win.
 inline bool whole_context(int B, int Hkv, int G, int D, int es, int max_context_len) {
-  return max_context_len <= kWholeSpan && (int64_t)B * Hkv <= kWholeMaxUnits && G * D * es <= 1024;
+  if (max_context_len > kWholeSpan || G * D * es > 1024) return false;
+  const int64_t units = (int64_t)B * Hkv;
+  if (units <= 256) return units >= 128 || max_context_len <= 1536;
+  return units <= 512 && max_context_len >= 768;
 }
 
 // With this step's new rows (app.T > 0), the workgroup of (sequence s, KV

@@ -19,6 +19,13 @@ pytestmark = [pytest.mark.gpu, pytest.mark.skipif(not gpu_available(), reason="n
 DEV = "cuda:0"
 LENS = [1, 15, 16, 17, 100, 511, 512, 513, 1024, 1500, 2047, 2048]
 
+
+def _lens(n_kv_heads):
+    """LENS repeated to 128 (sequence, KV head) pairs: contexts up to 2048
+    take the whole-context path from 128 pairs on."""
+    n = -(-128 // n_kv_heads)
+    return [LENS[i % len(LENS)] for i in range(max(n, len(LENS)))]
+
 CASES = [
     # name, Hq, Hkv, d, dtype
     ("tinyllama_gqa8_d64_f16", 32, 4, 64, "f16"),
@@ -41,7 +48,7 @@ def _whole(w, max_len):
 @pytest.mark.parametrize("out_kind", ["f32", "kv"])
 def test_whole_context_matches_oracle_and_split_path(name, Hq, Hkv, d, dtype, out_kind):
     from paged_kv_cache_gather_amd.batch import DeviceBatch
-    w = synth.custom_workload(name, Hq, Hkv, d, dtype, 2048, seed=71, decode_lens=LENS)
+    w = synth.custom_workload(name, Hq, Hkv, d, dtype, 4096, seed=71, decode_lens=_lens(Hkv))
     out_dtype = "f32" if out_kind == "f32" else dtype
     b = DeviceBatch(w, DEV, fill="host", out_dtype=out_dtype)
     assert _whole(w, b.decode.max_context_len)
@@ -67,7 +74,7 @@ def test_whole_context_with_shared_prefixes_and_forks():
     from paged_kv_cache_gather_amd.batch import DeviceBatch
     # groups forked from shared prefixes (the split path would read them once
     # per run; this path reads them per sequence)
-    lens = [1800, 1800, 2048, 1200, 700, 700, 520, 33]
+    lens = [1500, 1500, 1536, 1200, 700, 700, 520, 33]
     w = synth.custom_workload("whole_shared", 32, 8, 128, "bf16", 2048, seed=72, decode_lens=lens,
                               prefix_len=[1100, 1100, 1100, 1100, 600, 600, 0, 0],
                               prefix_group=[0, 0, 0, 0, 1, 1, -1, -1])
@@ -87,7 +94,7 @@ def test_whole_context_with_shared_prefixes_and_forks():
 
 def test_whole_context_one_call_step_equals_two_calls():
     from paged_kv_cache_gather_amd.batch import DeviceBatch
-    w = synth.custom_workload("whole_append", 32, 4, 64, "f16", 2048, seed=73, decode_lens=LENS)
+    w = synth.custom_workload("whole_append", 32, 4, 64, "f16", 4096, seed=73, decode_lens=_lens(4))
     sep = DeviceBatch(w, DEV, fill="host", out_dtype="f16")
     one = DeviceBatch(w, DEV, fill="host", out_dtype="f16")
     assert _whole(w, sep.decode.max_context_len)
@@ -107,7 +114,7 @@ def test_whole_context_one_call_step_equals_two_calls():
 def test_whole_context_step_replays_from_a_graph():
     from paged_kv_cache_gather_amd.batch import DeviceBatch
     from tests.test_gpu_graph import _replays_match
-    w = synth.custom_workload("whole_graph", 32, 4, 64, "f16", 2048, seed=74, decode_lens=LENS)
+    w = synth.custom_workload("whole_graph", 32, 4, 64, "f16", 4096, seed=74, decode_lens=_lens(4))
     b = DeviceBatch(w, DEV, fill="host", out_dtype="f32")
     assert _whole(w, b.decode.max_context_len)
     print("whole context graph", flush=True)
@@ -118,9 +125,14 @@ def test_whole_context_step_replays_from_a_graph():
 def test_whole_context_limits():
     import paged_kv_cache_gather_amd as pkv
     f = pkv.paged_attention_decode_whole_context
-    assert f(64, 32, 4, 64, "f16", 2048)        # TinyLlama-shaped batch
+    assert f(64, 32, 4, 64, "f16", 2048)        # TinyLlama-shaped batch: 256 pairs
     assert not f(64, 32, 4, 64, "f16", 2049)    # a context past the span
-    assert not f(65, 32, 4, 64, "f16", 2048)    # 260 (sequence, KV head) pairs
+    assert f(32, 32, 4, 64, "f16", 2048)        # 128 pairs
+    assert not f(31, 32, 4, 64, "f16", 2048)    # 124 pairs, contexts past 1536
+    assert f(31, 32, 4, 64, "f16", 1536)        # 124 pairs, contexts up to 1536
+    assert f(128, 32, 4, 64, "f16", 768)        # 512 pairs from 768 tokens on
+    assert not f(128, 32, 4, 64, "f16", 767)
+    assert not f(129, 32, 4, 64, "f16", 2048)   # 516 pairs
     assert f(64, 16, 4, 128, "bf16", 1000)      # G 4 at head_dim 128
     assert not f(64, 32, 4, 128, "bf16", 1000)  # G 8 at head_dim 128: registers
     assert not f(8, 32, 8, 128, "fp8_e4m3", 1000)  # 8-bit pools keep their path
@@ -128,7 +140,7 @@ def test_whole_context_limits():
     assert not f(8, 30, 4, 64, "f16", 100)      # n_q_heads not a multiple
     # the split path just past the span still matches the oracle
     from paged_kv_cache_gather_amd.batch import DeviceBatch
-    w = synth.custom_workload("whole_edge", 32, 4, 64, "f16", 2048, seed=75, decode_lens=[2049, 7, 2048])
+    w = synth.custom_workload("whole_edge", 32, 4, 64, "f16", 4096, seed=75, decode_lens=[2049, 7, 2048] * 11)
     b = DeviceBatch(w, DEV, fill="host", out_dtype="f32")
     assert not _whole(w, b.decode.max_context_len)
     b.append_decode()
