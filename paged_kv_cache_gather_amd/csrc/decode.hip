@@ -22,7 +22,10 @@
 // and the pools' scales fold into the softmax scale (keys) and the written
 // partials (values).  Verify attention (verify_partition_kernel, further
 // below) serves a sequence's new tokens with the same MFMA routine as the
-// shared kernel (mfma_partition) and a causal limit per row.
+// shared kernel (mfma_partition) and a causal limit per row.  Short contexts
+// in a small batch skip all of that: decode_whole_kernel (further below)
+// runs the per-sequence routine over a whole context of up to 2048 tokens
+// on a 16-wave workgroup per (sequence, KV head), in one launch.
 // decode_partition_kernel:
 //  * Work unit = (KV head g, sequence s, partition p of 512 context tokens),
 //    one 256-thread workgroup (4 wave64s).  All G query heads that share the
