@@ -209,14 +209,20 @@ def test_config3_step_sampled_with_bf16_out():
 
 
 def test_single_key_returns_its_value_exactly():
+    # both paths: this small batch takes the whole-context launch in one
+    # call; the two-call form always splits
     w = synth.custom_workload("one_key", 32, 8, 128, "bf16", 64, seed=9, decode_lens=[1, 1, 1])
-    _, out = _run_decode(w, "f32")
-    got = out.cpu().numpy()
+    b, out = _run_decode(w, "f32")
+    split = b.new_decode_out()
+    b.attend_decode_split(split)
+    torch.cuda.synchronize()
     import oracle
-    for s in range(3):
-        _, v = w.kv("decode", s, 0, 1)
-        ref = np.repeat(oracle.decode("bf16", v)[0], 4, axis=0)
-        assert np.array_equal(got[s].astype(np.float64), ref)
+    for o in (out, split):
+        got = o.cpu().numpy()
+        for s in range(3):
+            _, v = w.kv("decode", s, 0, 1)
+            ref = np.repeat(oracle.decode("bf16", v)[0], 4, axis=0)
+            assert np.array_equal(got[s].astype(np.float64), ref)
 
 
 def test_empty_context_gives_zeros():
@@ -230,6 +236,11 @@ def test_empty_context_gives_zeros():
     lens = torch.tensor([0, 0], dtype=torch.int32, device=DEV)
     ws = torch.empty(pkv.paged_attention_decode_workspace_bytes(B, Hq, d, 64) // 4 + 1, device=DEV)
     pkv.paged_attention_decode(out, q, kp, vp, tables, lens, 64, Hkv, nb, 0.125, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(out).item() == 0
+    out.fill_(7.0)  # the split path (two calls)
+    pkv.paged_attention_decode_partitions(out, q, kp, vp, tables, lens, 64, Hkv, nb, 0.125, workspace=ws)
+    pkv.paged_attention_decode_reduce(out, q, kp, vp, tables, lens, 64, Hkv, nb, 0.125, workspace=ws)
     torch.cuda.synchronize()
     assert torch.count_nonzero(out).item() == 0
 
