@@ -26,6 +26,17 @@ def _run_decode(w, out_dtype=None, fill="host"):
     return b, out
 
 
+def _check_both_paths(w, b, out, out_dtype):
+    """out (the one-call attention, whichever path the batch's sizes pick)
+    and the two-call form (always split-context, shared runs included) on
+    the same batch, both against the oracle."""
+    split = b.new_decode_out()
+    b.attend_decode_split(split)
+    torch.cuda.synchronize()
+    _check_all(w, out, out_dtype)
+    _check_all(w, split, out_dtype)
+
+
 def _check_all(w, out, out_dtype, seqs=None):
     atol, rtol = tolerance(w.dtype, out_dtype)
     got = out.double().cpu().numpy()
@@ -59,8 +70,8 @@ def test_decode_small(name, Hq, Hkv, d, dtype, lens, out_kind):
         pytest.skip("same as f32")
     w = synth.custom_workload(name, Hq, Hkv, d, dtype, 2048, seed=3, decode_lens=lens)
     print(f"decode {name} out={out_dtype}", flush=True)
-    _, out = _run_decode(w, out_dtype)
-    _check_all(w, out, out_dtype)
+    b, out = _run_decode(w, out_dtype)
+    _check_both_paths(w, b, out, out_dtype)
 
 
 def test_decode_long_contexts():
@@ -88,7 +99,7 @@ def test_decode_shared_prefix_with_copy_on_write():
                               prefix_len=plen, prefix_group=[0, 0, 0, 0, 1, 1, 1, 1])
     print("decode prefix_cow", flush=True)
     b, out = _run_decode(w, "f32")
-    _check_all(w, out, "f32")
+    _check_both_paths(w, b, out, "f32")
 
 
 SHARED_RUNS = [
@@ -117,8 +128,8 @@ def test_decode_shared_partition_runs(name, Hq, Hkv, d, dtype, lens, plen, pgrou
     w = synth.custom_workload(name, Hq, Hkv, d, dtype, 4096, seed=13, decode_lens=lens, prefix_len=plen,
                               prefix_group=pgroup)
     print(f"decode {name}", flush=True)
-    _, out = _run_decode(w, "f32")
-    _check_all(w, out, "f32")
+    b, out = _run_decode(w, "f32")
+    _check_both_paths(w, b, out, "f32")
 
 
 @pytest.mark.parametrize("name", ["tinyllama_decode", "llama3_8b_decode", "opt13b_decode"])
@@ -141,7 +152,7 @@ FUSED = [
     ("fused_f16_d64", 32, 4, 64, "f16", [700, 700, 129, 2048], [600, 600, 0, 0], [0, 0, -1, -1]),
     ("fused_f32", 8, 2, 64, "f32", [5, 600, 1], [0, 0, 0], [-1, -1, -1]),
     # MHA (32-sequence run windows) and G = 16 (2-sequence windows)
-    ("fused_mha", 8, 8, 128, "f16", [1300, 1300, 600, 1030], [1200, 1200, 0, 1029], [0, 0, -1, 0]),
+    ("fused_mha", 8, 8, 128, "f16", [1700, 1700, 600, 1030], [1200, 1200, 0, 1029], [0, 0, -1, 0]),
     ("fused_gqa16", 32, 2, 64, "bf16", [900, 900, 100, 513, 513], [600, 600, 0, 512, 512], [0, 0, -1, 1, 1]),
 ]
 
@@ -167,9 +178,10 @@ def test_decode_append_in_one_call(name, Hq, Hkv, d, dtype, lens, plen, pgroup):
     _check_all(w, out_one, "f32")
 
 
-def test_decode_append_skips_padding_slots():
+@pytest.mark.parametrize("lens", [[300, 40, 900], [300, 40, 2100]], ids=["whole_context", "split"])
+def test_decode_append_skips_padding_slots(lens):
     from paged_kv_cache_gather_amd.batch import DeviceBatch
-    w = synth.custom_workload("fused_pad", 32, 8, 128, "bf16", 512, seed=24, decode_lens=[300, 40, 900])
+    w = synth.custom_workload("fused_pad", 32, 8, 128, "bf16", 512, seed=24, decode_lens=lens)
     sep = DeviceBatch(w, DEV, fill="host", out_dtype="f32")
     one = DeviceBatch(w, DEV, fill="host", out_dtype="f32")
     for b in (sep, one):
