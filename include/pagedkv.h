@@ -609,7 +609,11 @@ int paged_attention_decode_reduce(void* out, int32_t out_dtype, const void* q, c
  * n_kv_heads in {1, 2, 4, 8, 16}, block_size 16, scale finite and > 0
  * (PKV_EINVAL otherwise).  Products on MFMA, fp32 accumulation and softmax;
  * the P.V product takes V and the probabilities in fp16, so bf16 V entries
- * beyond fp16's range (|v| > 65504) are clamped to it. */
+ * beyond fp16's range (|v| > 65504) are clamped to it.  8-bit pools: chunks
+ * over an E4M3 cache go through paged_attention_verify_fp8, the same causal
+ * attention for up to 64 query tokens per sequence (a longer chunk in pieces
+ * of at most 64 queries, each with context_lens counting keys up to the
+ * piece's last query). */
 int paged_attention_prefill_chunk(void* out, int32_t out_dtype, const void* q, const void* k_pool,
                                   const void* v_pool, const int32_t* block_tables,
                                   int32_t max_blocks_per_seq, const int32_t* cu_q_lens,

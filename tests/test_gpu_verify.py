@@ -126,3 +126,38 @@ def test_verify_over_an_8bit_cache(name, Hq, Hkv, d, dtype, ctx, ql):
     cu = np.concatenate([[0], np.cumsum(w.chunk_qlen)])
     for c in range(w.n_chunks):
         assert_close(f"{name} seq {c}", got[cu[c]:cu[c + 1]], prefill_reference_fp8(w, c), atol, rtol)
+
+
+def test_long_chunks_over_an_8bit_cache_in_pieces():
+    # chunked prefill over an 8-bit cache: the chunk's rows are appended
+    # once, then its queries go through paged_attention_verify_fp8 in pieces
+    # of at most 64 tokens, each piece seeing the cache up to its last query
+    import paged_kv_cache_gather_amd as pkv
+    from paged_kv_cache_gather_amd.batch import DeviceBatch
+    from tests.helpers import FP8_K_SCALE, FP8_V_SCALE, prefill_reference_fp8
+    w = synth.custom_workload("fp8_long_chunks", 32, 8, 128, "bf16", 2048, seed=39, chunk_ctx=[300, 0, 1500],
+                              chunk_qlen=[200, 130, 64])
+    print("fp8 chunks in pieces of 64", flush=True)
+    b = DeviceBatch(w, DEV, fill="host", out_dtype="f32", kv_cache="fp8_e4m3", k_scale=FP8_K_SCALE,
+                    v_scale=FP8_V_SCALE)
+    b.append_prefill()
+    p = b.prefill
+    out = b.new_prefill_out()
+    cu = np.concatenate([[0], np.cumsum(w.chunk_qlen)])
+    for c in range(w.n_chunks):
+        ctx, ql = int(w.chunk_ctx[c]), int(w.chunk_qlen[c])
+        for a in range(0, ql, 64):
+            e = min(a + 64, ql)
+            r0, r1 = int(cu[c]) + a, int(cu[c]) + e
+            cu_piece = torch.tensor([0, e - a], dtype=torch.int32, device=DEV)
+            lens = torch.tensor([ctx + e], dtype=torch.int32, device=DEV)
+            need = pkv.paged_attention_verify_workspace_bytes(e - a, w.n_q_heads, w.head_dim, ctx + e)
+            ws = torch.empty(max(need // 4, 1), dtype=torch.float32, device=DEV) if need else None
+            pkv.paged_attention_verify_fp8(out[r0:r1], p.q[r0:r1], b.k_pool, b.v_pool, p.tables[c:c + 1], cu_piece,
+                                           lens, e - a, ctx + e, w.n_kv_heads, w.num_blocks, w.scale, b.k_scale,
+                                           b.v_scale, workspace=ws)
+    torch.cuda.synchronize()
+    atol, rtol = tolerance("bf16", "f32")
+    got = out.double().cpu().numpy()
+    for c in range(w.n_chunks):
+        assert_close(f"chunk {c}", got[cu[c]:cu[c + 1]], prefill_reference_fp8(w, c), atol, rtol)
