@@ -420,11 +420,13 @@ int64_t paged_attention_decode_workspace_bytes(int32_t num_seqs, int32_t n_q_hea
  * works block by block.)  Long contexts are split into partitions of
  * paged_attention_decode_partition_size() tokens whose partial softmax
  * states are merged by a second reduction kernel.
- * Shared blocks: when neighbouring sequences in the batch name the same
- * blocks for a whole partition (sequences forked from one prefix: "Memory
- * sharing", vLLM Serving deep dive), one workgroup reads that partition once
- * for all of them (up to 32 query rows, on MFMA; f16/bf16 K/V only): a
- * third kernel, queued on `stream` before the per-sequence partition pass.
+ * Shared blocks: when sequences of one aligned window of 32 / G batch
+ * entries (G = n_q_heads / n_kv_heads), in any order within it, name the
+ * same blocks for a whole partition (sequences forked from one prefix:
+ * "Memory sharing", vLLM Serving deep dive), one workgroup reads that
+ * partition once for all of them (up to 32 query rows, on MFMA; 16-bit and
+ * 8-bit K/V): a third kernel, queued on `stream` before the per-sequence
+ * partition pass.
  * Short contexts in a small batch (paged_attention_decode_whole_context
  * says when): one launch instead, one workgroup per (sequence, KV head)
  * taking the whole context with its blocks dealt to 16 waves and the waves'

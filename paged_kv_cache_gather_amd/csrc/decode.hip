@@ -12,8 +12,8 @@
 // waste", Life of a prompt).
 //
 // How (gfx950): three kernels per step on one stream.  decode_shared_kernel
-// first serves the partitions that neighbouring sequences share (see the
-// section on shared partitions below) — and, when the step is one
+// first serves the partitions that sequences of one run window share (see
+// the section on shared partitions below) — and, when the step is one
 // paged_attention_decode_append call, writes the new tokens' K/V rows with
 // extra workgroups; decode_partition_kernel serves the rest;
 // decode_reduce_kernel merges split-context partials.  Over an 8-bit
@@ -320,47 +320,48 @@ __device__ __forceinline__ void partition_rows(
   }
 }
 
-// ---- partitions shared by neighbouring sequences ----------------------------
+// ---- partitions shared by sequences of one window ---------------------------
 // Sequences forked from a common prefix name the same ref-counted physical
 // blocks for it ("Memory sharing" with reference counts, vLLM Serving deep
-// dive).  When neighbours in the batch name the same 32 blocks for a full
-// partition p, one workgroup reads those K/V bytes once and serves all of
-// them: with k sequences the partition is a (k G) x 512 x D contraction, done
-// on MFMA by decode_shared_kernel.  Runs are formed inside aligned windows of
-// KM = kRunRows / G sequences, so membership is decided from neighbours:
-// s joins the run of s - 1 when both fill p, name the same blocks for it and
-// s is not at a window start.  Runs of one sequence stay with the
-// per-sequence kernel.
+// dive).  When several sequences of the batch name the same 32 blocks for a
+// full partition p, one workgroup reads those K/V bytes once and serves all
+// of them: with k sequences the partition is a (k G) x 512 x D contraction,
+// done on MFMA by decode_shared_kernel.  Runs are formed inside aligned
+// windows of KM = kRunRows / G sequences, in any order within the window:
+//  * member i of the window is eligible for p when its context fills p;
+//  * eligible members whose first block id for p is the same form a class,
+//    led by its lowest member c;
+//  * the run of the class is c and every other member whose 32 ids for p all
+//    equal c's; a run of one sequence stays with the per-sequence kernel.
+// Both kernels take this decision the same way, so each (sequence, p) is
+// served by exactly one workgroup.
 constexpr int kRunRows = 32;                     // query rows of a shared run (two 16-row MFMA tiles)
 constexpr int kPartBlocks = kPart / kBlockSize;  // blocks per partition
 static_assert(kPartBlocks <= 64, "one wave compares a partition's block ids");
 
 // Is (s, p) served by a shared workgroup, i.e. is s in a run of two or more?
-// The loads that decide it for most (s, p) — the neighbours' lengths and
-// first block ids for p — are issued together by probe_share, before the
-// caller's own exits, so that the decision costs one round of loads; only
-// candidates (a neighbour with the same first block) compare all ids.
+// The loads that decide it for most (s, p) — every window member's length
+// and first block id for p, one member per lane — are issued together by
+// probe_share, before the caller's own exits, so that the decision costs one
+// round of loads; only a class of two or more compares all ids.  (Held as
+// wave-uniform values read by the scalar unit instead, the window did not
+// decide faster, and 32 members overflow the scalar registers.)
 struct ShareProbe {
-  int32_t id, id_prev, id_next;  // first block id of p for s, s - 1, s + 1
-  int L_prev, L_next;            // lengths of s - 1, s + 1 (-1: not in s's window)
+  int32_t id;  // lane i < KM: first block id of p for window member i
+  int L;       // and its length (-1: past the batch, or not a member lane)
 };
 
 template <typename T, int G>
 __device__ __forceinline__ ShareProbe probe_share(const int32_t* __restrict__ tables, int max_blocks,
                                                   const int32_t* __restrict__ lens, int B, int s, int p) {
-  ShareProbe r{0, 0, 0, -1, -1};
+  ShareProbe r{0, -1};
   if constexpr (T::kBytes != 4) {
     constexpr int KM = kRunRows / G;
     const int64_t col = (int64_t)p * kPartBlocks;  // < max_blocks for every p < max_parts
-    const bool hp = s % KM != 0, hn = s + 1 < B && (s + 1) % KM != 0;
-    r.id = tables[(int64_t)s * max_blocks + col];
-    if (hp) {
-      r.id_prev = tables[(int64_t)(s - 1) * max_blocks + col];
-      r.L_prev = lens[s - 1];
-    }
-    if (hn) {
-      r.id_next = tables[(int64_t)(s + 1) * max_blocks + col];
-      r.L_next = lens[s + 1];
+    const int lane = threadIdx.x & 63, a = s - s % KM + lane;
+    if (lane < KM && a < B) {
+      r.id = tables[(int64_t)a * max_blocks + col];
+      r.L = lens[a];
     }
   }
   return r;
@@ -372,22 +373,28 @@ __device__ __forceinline__ bool in_shared_run(const ShareProbe& pr, const int32_
   if constexpr (T::kBytes == 4) {
     return false;  // fp32 K/V: no MFMA path
   } else {
+    constexpr int KM = kRunRows / G;
     const int need = (p + 1) * kPart;
     if (L < need) return false;
-    // does s join s - 1, or s + 1 join s: both fill p, same first id (then all ids)
-    const bool cp = pr.L_prev >= 0 && clamp_len(pr.L_prev, max_context_len) >= need && pr.id_prev == pr.id;
-    const bool cn = pr.L_next >= 0 && clamp_len(pr.L_next, max_context_len) >= need && pr.id_next == pr.id;
-    if (!cp && !cn) return false;
+    const int me = s % KM, s_first = s - me;
+    // s's class: eligible members with s's first block id (s is one of them)
+    const int32_t id_s = __builtin_amdgcn_readlane(pr.id, me);
+    const uint32_t cls =
+        (uint32_t)__ballot(pr.L >= 0 && clamp_len(pr.L, max_context_len) >= need && pr.id == id_s);
+    if (__popc(cls) < 2) return false;
+    const int c = __builtin_ctz(cls);  // the class leader
     const int64_t col = (int64_t)p * kPartBlocks;
     const int lane = threadIdx.x & 63;
-    bool ep = true, en = true;
-    if (lane < kPartBlocks) {
-      const int32_t mine = tables[(int64_t)s * max_blocks + col + lane];
-      if (cp) ep = tables[(int64_t)(s - 1) * max_blocks + col + lane] == mine;
-      if (cn) en = tables[(int64_t)(s + 1) * max_blocks + col + lane] == mine;
+    const int32_t mine = lane < kPartBlocks ? tables[(int64_t)s * max_blocks + col + lane] : 0;
+    if (me != c)  // a member: in the run when all its ids equal the leader's
+      return __all(lane >= kPartBlocks || tables[(int64_t)(s_first + c) * max_blocks + col + lane] == mine);
+    // the leader: a run when some other member's ids all equal its own
+    for (uint32_t o = cls & (cls - 1u); o != 0u; o &= o - 1u) {
+      const int t = __builtin_ctz(o);
+      if (__all(lane >= kPartBlocks || tables[(int64_t)(s_first + t) * max_blocks + col + lane] == mine))
+        return true;
     }
-    const bool all_p = __all(ep), all_n = __all(en);
-    return (cp && all_p) || (cn && all_n);
+    return false;
   }
 }
 
@@ -481,7 +488,8 @@ __device__ __forceinline__ uint64_t ld8(const void* p) { return *reinterpret_cas
 // member r / G, query head r % G of the KV head; a member owns one query
 // token and a row of q / out in units of Hq rows (base).
 //  * SeqRows: members are sequences s .. s + k - 1 of a decode batch, one
-//    token each, sharing the partition's blocks (a shared run, or k = 1);
+//    token each, sharing the partition's blocks (here k = 1);
+//  * SetRows: members are the sequences of a shared run (below);
 //  * TokenRows: members are query tokens q0 .. q0 + k - 1 of one sequence at
 //    absolute positions pos0 .. pos0 + k - 1, each attending keys 0 .. its
 //    position (causal), as in verifying several drafted tokens at once.
@@ -494,6 +502,22 @@ struct SeqRows {
   __device__ int members() const { return k; }
   __device__ int64_t base(int mi) const { return (int64_t)s + mi; }
   __device__ int parts(int mi) const { return (clamp_len(lens[s + mi], max_context_len) + kPart - 1) / kPart; }
+  __device__ int limit(int) const { return 0x7fffffff; }
+};
+// SetRows: members are the sequences s0 + idx[0], s0 + idx[1], .. of a run
+// (idx ascending, in LDS), one token each, sharing the partition's blocks.
+struct SetRows {
+  static constexpr bool kCausal = false;
+  int s0, k;
+  const int* idx;
+  const int32_t* lens;
+  int max_context_len;
+  __device__ int table_row() const { return s0 + idx[0]; }
+  __device__ int members() const { return k; }
+  __device__ int64_t base(int mi) const { return (int64_t)s0 + idx[mi]; }
+  __device__ int parts(int mi) const {
+    return (clamp_len(lens[s0 + idx[mi]], max_context_len) + kPart - 1) / kPart;
+  }
   __device__ int limit(int) const { return 0x7fffffff; }
 };
 struct TokenRows {
@@ -863,7 +887,7 @@ __device__ __forceinline__ void mfma_partition(const Rows& R, int n, int g, int 
 // shared-run launch (grid z >= kRunSlots), so that the cache write costs no
 // launch of its own and fills CUs the runs leave idle.  A run never covers
 // a new token's block — the block a sequence appends into is its own after
-// copy-on-write, so its ids differ from every neighbour's — hence the write
+// copy-on-write, so its ids differ from every other sequence's — hence the write
 // and the runs touch disjoint bytes, and the per-sequence pass, launched
 // after, reads the new rows.
 struct AppendArgs {
@@ -880,7 +904,7 @@ struct AppendArgs {
 
 constexpr int kSharedWaves = PKV_SHARED_WAVES;  // waves per shared-run workgroup (4 or 8)
 constexpr int kRunSlots = PKV_RUN_SLOTS;        // workgroups per run window
-constexpr int kProbeParts = 64;                 // partitions probed per round
+constexpr int kProbeIds = 512;                  // window members x partitions probed per round
 template <typename KV, typename QT, int D, int G, int OutCode>
 __global__ void __launch_bounds__(kSharedWaves * 64, kSharedWaves == 8 ? 1 : 2)
 decode_shared_kernel(void* __restrict__ out, float* __restrict__ ws_o, float* __restrict__ ws_ml,
@@ -912,70 +936,96 @@ decode_shared_kernel(void* __restrict__ out, float* __restrict__ ws_o, float* __
       }
       return;
     }
+    constexpr int NP = kProbeIds / KM;  // partitions probed per round
+    static_assert(NP <= kThr, "one thread clears each partition's mask");
     __shared__ __attribute__((aligned(16))) RunLds<D, kRunRows, kSharedWaves> sh;
-    __shared__ uint32_t cmask[kProbeParts];  // per partition: bit i = member i may join member i - 1
-    __shared__ uint32_t joins;
+    __shared__ int32_t fid[NP][KM];    // first block id of each (partition, member)
+    __shared__ uint32_t clsm[NP][KM];  // members of the class that member c leads
+    __shared__ uint32_t elig[NP];      // per partition: bit i = member i fills it
+    __shared__ uint32_t lead[NP];      // per partition: bit c = c leads a class of two or more
+    __shared__ uint32_t bad;         // members of a class whose ids differ from the leader's
+    __shared__ int midx[KM];         // the run's members (window-relative, ascending)
     const int g = blockIdx.x, win = blockIdx.y, slot = blockIdx.z;
     const int s_first = win * KM;
     if (s_first >= B) return;
     const int tid = threadIdx.x;
-    int unit = 0;  // candidate runs of the window so far, in (partition, member) order
-    for (int pc = 0; pc < max_parts; pc += kProbeParts) {
-      const int np = max_parts - pc < kProbeParts ? max_parts - pc : kProbeParts;
-      // candidates, one thread per (partition, member): both fill the
-      // partition and their first block ids for it agree (one round of loads;
-      // every load is in bounds, so none waits on another)
-      if (tid < kProbeParts) cmask[tid] = 0u;
+    int unit = 0;  // candidate runs of the window so far, in (partition, leader) order
+    for (int pc = 0; pc < max_parts; pc += NP) {
+      const int np = max_parts - pc < NP ? max_parts - pc : NP;
+      // one thread per (partition, member): its first block id and whether
+      // it fills the partition (one round of loads, every one in bounds)
+      if (tid < NP) {
+        elig[tid] = 0u;
+        lead[tid] = 0u;
+      }
+      for (int t = tid; t < np * KM; t += kThr) clsm[t / KM][t % KM] = 0u;
       __syncthreads();
       for (int t = tid; t < np * KM; t += kThr) {
         const int pp = t / KM, i = t % KM, a = s_first + i, p = pc + pp;
-        if (i >= 1 && a < B) {
-          const int need = (p + 1) * kPart;
-          const int La = lens[a - 1], Lb = lens[a];
-          const int32_t ia = tables[(int64_t)(a - 1) * max_blocks + p * kPartBlocks];
-          const int32_t ib = tables[(int64_t)a * max_blocks + p * kPartBlocks];
-          if (clamp_len(La, max_context_len) >= need && clamp_len(Lb, max_context_len) >= need && ia == ib)
-            atomicOr(&cmask[pp], 1u << i);
+        if (a < B) {
+          fid[pp][i] = tables[(int64_t)a * max_blocks + p * kPartBlocks];
+          if (clamp_len(lens[a], max_context_len) >= (p + 1) * kPart) atomicOr(&elig[pp], 1u << i);
+        }
+      }
+      __syncthreads();
+      // the classes, a wave per partition: lane i finds its leader, the
+      // lowest eligible member with the same first id (ids broadcast from
+      // their lanes, no LDS round trips in the loop)
+      {
+        const int lane = tid & 63;
+        for (int pp = tid >> 6; pp < np; pp += kSharedWaves) {
+          const uint32_t el = elig[pp];
+          const int32_t id = lane < KM ? fid[pp][lane] : 0;
+          int c = lane;
+          for (uint32_t x = el; x != 0u; x &= x - 1u) {
+            const int j = __builtin_ctz(x);
+            const int32_t idj = __builtin_amdgcn_readlane(id, j);
+            c = (j < c && idj == id) ? j : c;
+          }
+          if (lane < KM && ((el >> lane) & 1u)) {
+            atomicOr(&clsm[pp][c], 1u << lane);
+            if (c != lane) atomicOr(&lead[pp], 1u << c);
+          }
         }
       }
       __syncthreads();
       for (int pp = 0; pp < np; ++pp) {
-        const uint32_t cm = cmask[pp];  // uniform
-        if (cm == 0u) continue;
         const int p = pc + pp;
-        // candidate runs: a member without its bit, then the members with it
-        for (int c0 = 0; c0 + 1 < KM; ++c0) {
-          if (!((cm >> (c0 + 1)) & 1u) || ((cm >> c0) & 1u)) continue;
-          int kc = 2;
-          while (c0 + kc < KM && ((cm >> (c0 + kc)) & 1u)) ++kc;
+        const int64_t col = (int64_t)p * kPartBlocks;
+        // classes of two or more, lowest leader first (uniform)
+        for (uint32_t ld = lead[pp]; ld != 0u; ld &= ld - 1u) {
+          const int c = __builtin_ctz(ld);
+          const uint32_t cls = clsm[pp][c];
           if (unit++ % kRunSlots != slot) continue;
-          // full comparison of the candidate run's block ids for p, one
-          // thread per (member, entry): a mismatch clears the member's bit
-          if (tid == 0) joins = cm;
+          // full comparison of the class's ids for p against the leader's,
+          // one thread per (member, entry): a mismatch drops the member
+          if (tid == 0) bad = 0u;
           __syncthreads();
-          for (int t = tid; t < (kc - 1) * kPartBlocks; t += kThr) {
-            const int i = c0 + 1 + t / kPartBlocks, e = t % kPartBlocks;
-            const int a = s_first + i;
-            if (tables[(int64_t)(a - 1) * max_blocks + p * kPartBlocks + e] !=
-                tables[(int64_t)a * max_blocks + p * kPartBlocks + e])
-              atomicAnd(&joins, ~(1u << i));
+          for (int t = tid; t < KM * kPartBlocks; t += kThr) {
+            const int i = t / kPartBlocks, e = t % kPartBlocks;
+            if (i != c && ((cls >> i) & 1u) &&
+                tables[(int64_t)(s_first + i) * max_blocks + col + e] !=
+                    tables[(int64_t)(s_first + c) * max_blocks + col + e])
+              atomicOr(&bad, 1u << i);
           }
           __syncthreads();
-          const uint32_t jm = joins;
-          __syncthreads();  // joins is rewritten by the next candidate run
-          // the runs inside it: a member that does not join its predecessor,
-          // then those that do
-          for (int s0 = c0; s0 + 1 < c0 + kc; ++s0) {
-            if (!((jm >> (s0 + 1)) & 1u) || (s0 > c0 && ((jm >> s0) & 1u))) continue;
-            int k = 2;
-            while (s0 + k < c0 + kc && ((jm >> (s0 + k)) & 1u)) ++k;
-            mfma_partition<KV, QT, D, G, kRunRows / 16, false, OutCode, PKV_SHARED_PARTS, kSharedWaves>(
-                SeqRows{s_first + s0, k, lens, max_context_len}, kPart, g, p, sh, out, ws_o, ws_ml, q, kpool,
-                vpool, tables, max_blocks, Hkv, num_blocks, scale_log2, v_mul, max_parts);
+          const uint32_t run = cls & ~bad;  // the leader and the members that join it
+          if (__popc(run) < 2) {
+            __syncthreads();  // bad is rewritten by the next class
+            continue;
           }
+          if (tid == 0) {
+            int k = 0;
+            for (uint32_t x = run; x != 0u; x &= x - 1u) midx[k++] = __builtin_ctz(x);
+          }
+          __syncthreads();
+          mfma_partition<KV, QT, D, G, kRunRows / 16, false, OutCode, PKV_SHARED_PARTS, kSharedWaves>(
+              SetRows{s_first, (int)__popc(run), midx, lens, max_context_len}, kPart, g, p, sh, out, ws_o, ws_ml, q,
+              kpool, vpool, tables, max_blocks, Hkv, num_blocks, scale_log2, v_mul, max_parts);
+          // (mfma_partition ends with a barrier: bad and midx may be rewritten)
         }
       }
-      __syncthreads();  // cmask is rewritten by the next round
+      __syncthreads();  // fid, clsm, elig and lead are rewritten by the next round
     }
   }
 }
@@ -1059,7 +1109,7 @@ decode_partition_kernel(void* __restrict__ out, float* __restrict__ ws_o, float*
 // a whole (sequence, KV head): the sequence's blocks are dealt evenly to its
 // waves (a short context still uses all of them), the waves' softmax states
 // merge in LDS and the output is written directly.  Partitions that
-// neighbours share are read per sequence on this path.
+// sequences share are read per sequence on this path.
 constexpr int kWholeSpan = 2048;      // context tokens one workgroup takes
 constexpr int kWholeWaves = 16;       // its waves (4 per SIMD)
 

@@ -117,14 +117,36 @@ SHARED_RUNS = [
      [0] * 5 + [1029] * 6 + [0], [-1] * 5 + [0] * 6 + [-1]),
     ("runs_f16_d64", 16, 4, 64, "f16", [1030, 1030, 1536, 3000, 520], [1025, 1025, 1025, 1025, 0],
      [0, 0, 0, 0, -1]),
+    # groups interleaved inside the window (runs are sets of members, not
+    # ranges); group 2's 600-token prefix shares the first block of the second
+    # partition but not the rest, so its members agree on the first id only
+    ("runs_interleaved", 32, 8, 128, "bf16",
+     [1500, 1700, 1101, 2100, 900, 1200, 1601, 800, 1300, 1650, 700, 1000, 600, 2000, 1150, 610],
+     [1100, 1600, 1100, 1600, 600, 1100, 1600, 0, 1100, 1600, 600, 600, 0, 1600, 1100, 600],
+     [0, 1, 0, 1, 2, 0, 1, -1, 0, 1, 2, 2, -1, 1, 0, 2]),
+    ("runs_interleaved_gqa8", 32, 4, 64, "f16",
+     [1100, 700, 1500, 800, 900, 1031, 650, 2000, 1200, 1040, 620, 300],
+     [1030, 600, 1030, 600, 600, 1030, 600, 1030, 1030, 1030, 600, 0],
+     [0, 1, 0, 1, 1, 0, 1, 0, 0, 0, 1, -1]),
+    # one run window of 32 sequences at G = 1, three groups dealt round robin
+    ("runs_interleaved_mha", 4, 4, 64, "f16",
+     [1200 + 13 * i if i % 3 == 0 else (700 + 7 * i if i % 3 == 1 else 530 + i) for i in range(30)] + [90, 1700, 40, 600],
+     [1100 if i % 3 == 0 else (600 if i % 3 == 1 else 520) for i in range(30)] + [0, 0, 0, 0],
+     [i % 3 for i in range(30)] + [-1, -1, -1, -1]),
+    # the class leader (lowest member with the partition's first block id)
+    # took a shorter prefix: members 1-4 agree with each other on every id of
+    # the second partition but not with it, so they stay per-sequence there
+    ("runs_leader_differs", 32, 8, 128, "bf16", [1500, 1300, 1400, 1200, 1100, 700],
+     [600, 1100, 1100, 1100, 1050, 0], [0, 0, 0, 0, 0, -1]),
 ]
 
 
 @pytest.mark.parametrize("name,Hq,Hkv,d,dtype,lens,plen,pgroup", SHARED_RUNS, ids=[c[0] for c in SHARED_RUNS])
 def test_decode_shared_partition_runs(name, Hq, Hkv, d, dtype, lens, plen, pgroup):
-    # neighbours whose full 512-token partitions use the same blocks are served
-    # by one MFMA workgroup; runs cross the 32 / G-sequence run window, some
-    # members end exactly at a partition edge
+    # sequences of one 32 / G-sequence window whose full 512-token partitions
+    # use the same blocks are served by one MFMA workgroup; groups cross the
+    # window, interleave inside it, some members end exactly at a partition
+    # edge
     w = synth.custom_workload(name, Hq, Hkv, d, dtype, 4096, seed=13, decode_lens=lens, prefix_len=plen,
                               prefix_group=pgroup)
     print(f"decode {name}", flush=True)

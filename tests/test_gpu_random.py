@@ -3,7 +3,7 @@
 Each case draws, from its own seed, a GQA ratio (1, 2, 4, 8 or 16), a head
 dimension (64 or 128), a dtype, an output dtype and a ragged batch whose
 lengths mix uniform draws with the edges of blocks (16 tokens) and of decode
-partitions (512 tokens), plus groups of neighbouring sequences forked from a
+partitions (512 tokens), plus groups of sequences forked from a
 shared prefix (members may take shorter prefixes; some prefixes span whole
 partitions, so the shared-run path serves them).  The same draws drive:
 

@@ -3,8 +3,8 @@ copy-on-write", vLLM Serving deep dive; the PagedAttention section of The
 hands-on guide to LLM Inference with vLLM): a batch whose sequences share
 ref-counted prefix blocks and the same batch with every block a private copy
 of the same bytes give the same attention, up to rounding.  On the GPU the
-two layouts take different kernels — partitions that neighbours share are
-scored once for all of them on the matrix cores, private ones on the vector
+two layouts take different kernels — partitions that sequences of one run
+window share are scored once for all of them on the matrix cores, private ones on the vector
 units — so they agree within the tolerance, not bit for bit; both are
 checked against the oracle, including shared runs that cross the run window.
 
