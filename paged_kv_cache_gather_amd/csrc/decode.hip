@@ -134,6 +134,11 @@ __device__ __forceinline__ void partition_rows(
   const int wend = bw1 * kBlockSize < n ? bw1 * kBlockSize : n;
   const int wn = wend - wt0 < 0 ? 0 : wend - wt0;            // its tokens
   float(*sp)[R] = reinterpret_cast<float(*)[R]>(smem) + w * TPW;
+  // fp16 V: the probabilities go to LDS as fp16, [R][TPW] per wave, and the
+  // products take two tokens per instruction (v_dot2_f32_f16 of a P pair and
+  // a V pair, fp32 accumulate); the other types keep fp32 P, [TPW][R]
+  constexpr bool kP16 = T::kCode == PKV_F16;
+  _Float16* sp16 = reinterpret_cast<_Float16*>(smem) + w * TPW * R;
 
   // ---- scores: one token per lane, R rows, whole K row ---------------------
   float sreg[IT][R];
@@ -186,7 +191,10 @@ __device__ __forceinline__ void partition_rows(
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       const float e = valid ? __builtin_amdgcn_exp2f(sreg[it][r] - mw[r]) : 0.f;
-      sp[it * 64 + lane][r] = e;
+      if constexpr (kP16)
+        sp16[r * TPW + it * 64 + lane] = (_Float16)e;
+      else
+        sp[it * 64 + lane][r] = e;
       sreg[it][r] = e;
     }
   }
@@ -239,6 +247,28 @@ __device__ __forceinline__ void partition_rows(
     const int tb = wt0 / kBlockSize + bl;  // partition-local block
     const int ntok = n - tb * kBlockSize;
     const float(*pb)[R] = sp + bl * kBlockSize + tg * TPC;
+    if constexpr (kP16) {
+      // the lane's TPC = 8 tokens of the block: four fp16 P pairs per row
+      u32x4 pp[R];
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+        pp[r] = *reinterpret_cast<const u32x4*>(sp16 + r * TPW + bl * kBlockSize + tg * TPC);
+      if (ntok < kBlockSize) {  // zero V of slots past the context (they may hold anything)
+        const int nv = ntok - tg * TPC;
+#pragma unroll
+        for (int i = 0; i < NI; ++i)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            vcur[i][e] &= 2 * e + 1 < nv ? 0xffffffffu : (2 * e < nv ? 0x0000ffffu : 0u);
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+#pragma unroll
+        for (int i = 0; i < NI; ++i)
+#pragma unroll
+          for (int r = 0; r < R; ++r) o[r][i] = dot2<T>(pp[r][e], vcur[i][e], o[r][i]);
+      continue;
+    }
     auto accumulate = [&](auto masked) {
 #pragma unroll
       for (int tt = 0; tt < TPC; ++tt) {
