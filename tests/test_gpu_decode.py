@@ -88,6 +88,13 @@ def test_decode_long_contexts():
     print("decode long_shared", flush=True)
     _, out = _run_decode(w, "f32", fill="device")
     _check_all(w, out, "f32")
+    # G = 1: a run window of 32 sequences probes 16 partitions per round, so
+    # 18 shared partitions take two rounds
+    w = synth.custom_workload("long_shared_mha", 4, 4, 64, "f16", 4096, seed=8, decode_lens=[9000, 5000, 9000, 8801],
+                              prefix_len=[8800, 0, 8800, 8800], prefix_group=[0, -1, 0, 0])
+    print("decode long_shared_mha", flush=True)
+    _, out = _run_decode(w, "f32", fill="device")
+    _check_all(w, out, "f32")
 
 
 def test_decode_shared_prefix_with_copy_on_write():
