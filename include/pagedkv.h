@@ -389,9 +389,10 @@ int32_t paged_attention_decode_partition_size(void);
  * paged_attention_decode_partitions / _reduce always split).  The path is
  * taken when max_context_len <= 2048, (n_q_heads / n_kv_heads) * head_dim *
  * element bytes <= 1024 and, with P = num_seqs * n_kv_heads, either P <= 256
- * and (P >= 128 or max_context_len <= 1536), or P <= 512 and max_context_len
- * >= 768 (the decode of a small batch is bound by the latency of one or two
- * rounds of reads, not by HBM bandwidth); never for 8-bit pools.  ("The decode stage, and how to spot the
+ * and (P >= 128 or max_context_len <= 1536), or 448 <= P <= 512 and
+ * max_context_len * 2 * head_dim * element bytes >= 384 KiB (the decode of a
+ * small batch is bound by the latency of one or two rounds of reads, not by
+ * HBM bandwidth); never for 8-bit pools.  ("The decode stage, and how to spot the
  * waste", Life of a prompt: the same attention, one query per sequence.)
  * Invalid sizes give 0. */
 int32_t paged_attention_decode_whole_context(int32_t num_seqs, int32_t n_q_heads, int32_t n_kv_heads,

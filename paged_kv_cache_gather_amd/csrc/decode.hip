@@ -1145,19 +1145,21 @@ constexpr int kWholeWaves = 16;       // its waves (4 per SIMD)
 
 // Does a batch take the whole-context path?  The per-wave accumulators must
 // leave the 16-wave workgroup within 128 registers (G x D x element bytes
-// <= 1024: G <= 8 at head_dim 64, G <= 4 at 128 for 16-bit pools).  Measured
-// against the split path on uniform and prefix-sharing batches (Llama-3-8B
-// heads): up to 256 (sequence, KV head) pairs — one round of workgroups, one
-// per CU — it wins except when fewer than 128 pairs hold contexts past 1536
-// tokens (then too few CUs take part, and the split path's 4x more
-// workgroups win); up to 512 pairs it wins from 768-token contexts on; past
-// that, or for shorter contexts, reading shared partitions once and the
-// split path's occupancy win.
+// <= 1024: G <= 8 at head_dim 64, G <= 4 at 128 for 16-bit pools), so one
+// workgroup fills a CU and the 256 CUs take P = (sequence, KV head) pairs in
+// rounds of 256.  Measured against the split path (Llama-3-8B and
+// TinyLlama heads, uniform and prefix-sharing batches): up to 256 pairs — one
+// round — it wins except when fewer than 128 pairs hold contexts past 1536
+// tokens (too few CUs take part; the split path's 4x more workgroups win);
+// a second round pays only when it is at least three quarters full (P >= 448)
+// and each pair reads at least 384 KiB (768 tokens at head_dim 128 in 16 bits,
+// 1536 at 64); past 512 pairs, or below those sizes, reading shared
+// partitions once and the split path's finer work units win.
 inline bool whole_context(int B, int Hkv, int G, int D, int es, int max_context_len) {
   if (max_context_len > kWholeSpan || G * D * es > 1024) return false;
   const int64_t units = (int64_t)B * Hkv;
   if (units <= 256) return units >= 128 || max_context_len <= 1536;
-  return units <= 512 && max_context_len >= 768;
+  return units >= 448 && units <= 512 && (int64_t)max_context_len * 2 * D * es >= 384 * 1024;
 }
 
 // With this step's new rows (app.T > 0), the workgroup of (sequence s, KV

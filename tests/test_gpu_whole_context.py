@@ -130,8 +130,13 @@ def test_whole_context_limits():
     assert f(32, 32, 4, 64, "f16", 2048)        # 128 pairs
     assert not f(31, 32, 4, 64, "f16", 2048)    # 124 pairs, contexts past 1536
     assert f(31, 32, 4, 64, "f16", 1536)        # 124 pairs, contexts up to 1536
-    assert f(128, 32, 4, 64, "f16", 768)        # 512 pairs from 768 tokens on
-    assert not f(128, 32, 4, 64, "f16", 767)
+    # a second round of workgroups: 448 to 512 pairs, 384 KiB or more per pair
+    assert f(128, 32, 4, 64, "f16", 1536)       # 512 pairs, d 64: from 1536 tokens on
+    assert not f(128, 32, 4, 64, "f16", 1535)
+    assert f(64, 32, 8, 128, "bf16", 768)       # 512 pairs, d 128: from 768 tokens on
+    assert not f(64, 32, 8, 128, "bf16", 767)
+    assert f(56, 32, 8, 128, "bf16", 1024)      # 448 pairs
+    assert not f(55, 32, 8, 128, "bf16", 2048)  # 440 pairs
     assert not f(129, 32, 4, 64, "f16", 2048)   # 516 pairs
     assert f(64, 16, 4, 128, "bf16", 1000)      # G 4 at head_dim 128
     assert not f(64, 32, 4, 128, "bf16", 1000)  # G 8 at head_dim 128: registers
