@@ -3,9 +3,10 @@
 Each case draws, from its own seed, a GQA ratio (1, 2, 4, 8 or 16), a head
 dimension (64 or 128), a dtype, an output dtype and a ragged batch whose
 lengths mix uniform draws with the edges of blocks (16 tokens) and of decode
-partitions (512 tokens), plus groups of sequences forked from a
-shared prefix (members may take shorter prefixes; some prefixes span whole
-partitions, so the shared-run path serves them).  The same draws drive:
+partitions (512 tokens), plus groups of sequences forked from a shared
+prefix, in half the cases interleaved in the batch (members may take shorter
+prefixes; some prefixes span whole partitions, so the shared-run path serves
+them).  The same draws drive:
 
 * the one-call decode step, checked bit for bit against the cache write and
   attention as separate calls and within tolerance of the oracle;
@@ -58,6 +59,9 @@ def _decode_case(seed, dtypes=("f16", "bf16")):
             s += 1
     nb = sum(-(-L // 16) + 1 for L in lens) + 64
     out_kind = "f32" if rng.random() < 0.5 else dtype
+    if rng.random() < 0.5:  # groups interleaved in the batch (runs are sets of window members)
+        order = rng.permutation(B)
+        lens, plen, pgroup = ([x[i] for i in order] for x in (lens, plen, pgroup))
     name = f"rand{seed}_Hq{Hq}_Hkv{Hkv}_d{d}_{dtype}_B{B}"
     w = synth.custom_workload(name, Hq, Hkv, d, dtype, nb, seed=seed, decode_lens=lens, prefix_len=plen,
                               prefix_group=pgroup)
