@@ -1033,6 +1033,8 @@ def main():
     if not args.no_fp8:
         b, _, r = decode_leg(w, K, W, out_dtype, args.seed, flush, fp8=True, modes=not args.no_step_modes,
                              profile="decode_fp8_partition_llama3_8b_decode" if args.workload == "llama3_8b_decode" else None)
+        if not args.no_ceilings:  # the same read-only passes over the 8-bit tiles (2 KiB at head_dim 128)
+            r["read_ceilings"] = ceiling_leg(b, K, flush, r["roofline"]["achieved"])
         res["fp8_kv_decode"] = r
         del b
         torch.cuda.empty_cache()
