@@ -11,7 +11,8 @@
 // One 256-thread workgroup takes kItems 16-byte chunks per thread round: item
 // i of the launch is chunk i % C of list entry i / C (C = tile_bytes / 16),
 // so consecutive lanes read consecutive bytes of a tile and a wave
-// instruction covers 1 KiB.  Each thread has kUnroll loads in flight before
+// instruction covers 1 KiB (streaming loads, as the decode kernels read their
+// K/V).  Each thread has kUnroll loads in flight before
 // it folds them into a running XOR; the result is stored only if it hits a
 // constant, which keeps every load alive without a store per thread.
 //
@@ -51,7 +52,7 @@ read_tiles_kernel(const unsigned char* __restrict__ kpool, const unsigned char* 
       const int64_t e = item / C, c = item % C;
       const int64_t t = tiles ? tiles[e] : e;
       const unsigned char* pool = e < n_k ? kpool : vpool;
-      v[u] = ld16(pool + t * tile_bytes + c * 16);
+      v[u] = ld16_stream(pool + t * tile_bytes + c * 16);
     } else {
       v[u] = u32x4{0u, 0u, 0u, 0u};
     }

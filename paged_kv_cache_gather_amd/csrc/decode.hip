@@ -153,7 +153,7 @@ __device__ __forceinline__ void partition_rows(
       const unsigned char* kp = kpool + (((blk * Hkv + g) * C) * kBlockSize + (tl & 15)) * 16;
       u32x4 kc[C];
 #pragma unroll
-      for (int c = 0; c < C; ++c) kc[c] = ld16(kp + c * (kBlockSize * 16));
+      for (int c = 0; c < C; ++c) kc[c] = ld16_stream(kp + c * (kBlockSize * 16));
 #pragma unroll
       for (int r = 0; r < R; ++r) {
         const typename T::bits* qr = q + ((int64_t)s * Hq + g * G + r) * D;
@@ -225,7 +225,7 @@ __device__ __forceinline__ void partition_rows(
     const int64_t blk = clamp_block(tab[wt0 / kBlockSize + bl], num_blocks);
     const unsigned char* vp = vpool + (blk * Hkv + g) * (int64_t)VTILE + lane * 16;
 #pragma unroll
-    for (int i = 0; i < NI; ++i) vv[i] = ld16(vp + i * 1024);
+    for (int i = 0; i < NI; ++i) vv[i] = ld16_stream(vp + i * 1024);
   };
   // block bl + 1's loads are issued before block bl's products while the
   // accumulators stay small (R * NI <= 16: G <= 4 at head_dim 128, G <= 8 at
@@ -742,7 +742,7 @@ __device__ __forceinline__ void mfma_partition(const Rows& R, int n, int g, int 
 #pragma unroll
           for (int dt = 0; dt < DT; ++dt) {
             if constexpr (F8)
-              vraw[kp][dt] = in ? ld8(vr + dt * 16 * VROW) : 0ull;
+              vraw[kp][dt] = in ? ld8_stream(vr + dt * 16 * VROW) : 0ull;
             else
               vraw[kp][dt] = ld16(vr + dt * 16 * VROW);
           }
