@@ -670,7 +670,7 @@ __device__ __forceinline__ void mfma_partition(const Rows& R, int n, int g, int 
           const unsigned char* kr = kpool + ((kb * Hkv + g) * CH + q4) * (kBlockSize * 16) + r16 * 16;
 #pragma unroll
           for (int c = 0; c < KC; ++c)
-            ka[kt][c] = in ? ld16(kr + c * 4 * kBlockSize * 16) : u32x4{0u, 0u, 0u, 0u};
+            ka[kt][c] = in ? ld16_stream(kr + c * 4 * kBlockSize * 16) : u32x4{0u, 0u, 0u, 0u};
         }
       } else {
         // tile 2 kp + sub of block pair kp, row m = 4a + r = the pair's key
@@ -731,8 +731,8 @@ __device__ __forceinline__ void mfma_partition(const Rows& R, int n, int g, int 
           const unsigned char* vrB = vpool + (vbB * Hkv + g) * (int64_t)TILE + r16 * VROW + q4 * (VROW / 4);
 #pragma unroll
           for (int dt = 0; dt < DT; ++dt) {
-            const uint64_t a = inA ? ld8(vrA + dt * 16 * VROW) : 0ull;
-            const uint64_t b = inB ? ld8(vrB + dt * 16 * VROW) : 0ull;
+            const uint64_t a = inA ? ld8_stream(vrA + dt * 16 * VROW) : 0ull;
+            const uint64_t b = inB ? ld8_stream(vrB + dt * 16 * VROW) : 0ull;
             vraw[kp][dt] = u32x4{(uint32_t)a, (uint32_t)(a >> 32), (uint32_t)b, (uint32_t)(b >> 32)};
           }
         } else {
