@@ -641,8 +641,8 @@ class CacheFlush:
     """Evicts L2 (8 x 4 MB) and the 256 MB Infinity Cache before a timed
     step, outside the timed events, so the step reads its K/V from HBM as it
     would between the layers of a forward pass.  The default reads a 1 GiB
-    device buffer (paged_kv_read_tiles, contiguous): the caches end up full of
-    clean lines of unrelated data.  mode="write" writes the buffer instead,
+    device buffer (paged_kv_read_tiles, contiguous, plain loads): the caches
+    end up full of clean lines of unrelated data.  mode="write" writes the buffer instead,
     which also evicts but leaves up to ~290 MB of dirty lines that are
     written back while the timed step runs (reported beside the headline,
     not as it)."""
@@ -661,7 +661,7 @@ class CacheFlush:
             self.buf.fill_(self.i)
         else:
             n = self.buf.numel() // 4096
-            pkv.paged_kv_read_tiles(self.buf, None, None, n, n, 4096, self.sink)
+            pkv.paged_kv_read_tiles(self.buf, None, None, n, n, 4096, self.sink, streaming=False)
 
 
 def _stats_us(ms):
@@ -901,11 +901,16 @@ def ceiling_leg(b, K, flush, part_achieved):
         torch.cuda.synchronize()
         return _stats_us([e0.elapsed_time(e1) for e0, e1 in ev])
 
-    res = {"kernel": "read_tiles_kernel", "tiles": int(2 * n_k), "tile_bytes": tile_bytes, "bytes": nbytes}
+    res = {"kernel": "read_tiles_kernel", "loads": "streaming (nontemporal), as the decode kernels read K/V",
+           "tiles": int(2 * n_k), "tile_bytes": tile_bytes, "bytes": nbytes}
     for name, lst in lists.items():
         dev = torch.from_numpy(lst).to("cuda:0")
         t = timed(lambda: pkv.paged_kv_read_tiles(b.k_pool, b.v_pool, dev, n_k, 2 * n_k, tile_bytes, sink))
         res[name] = {"us": t, "gbs": nbytes / (t["mean"] * 1e-6) / 1e9}
+        if name == "table_order":  # the same pass with plain loads
+            t = timed(lambda: pkv.paged_kv_read_tiles(b.k_pool, b.v_pool, dev, n_k, 2 * n_k, tile_bytes, sink,
+                                                      streaming=False))
+            res["table_order_plain_loads"] = {"us": t, "gbs": nbytes / (t["mean"] * 1e-6) / 1e9}
     # the same number of tiles from the start of each pool: contiguous bytes
     ident = torch.arange(n_k, dtype=torch.int64, device="cuda:0").repeat(2)
     t = timed(lambda: pkv.paged_kv_read_tiles(b.k_pool, b.v_pool, ident, n_k, 2 * n_k, tile_bytes, sink))
@@ -914,7 +919,8 @@ def ceiling_leg(b, K, flush, part_achieved):
         if name in res:
             res[name]["decode_pass_frac"] = part_achieved / res[name]["gbs"]
     log("read ceilings: " + ", ".join(f"{n} {res[n]['gbs']:.0f} GB/s" for n in ("table_order", "random_order",
-                                                                                 "contiguous") if n in res)
+                                                                                 "contiguous", "table_order_plain_loads")
+                                        if n in res)
         + f" ({nbytes / 1e9:.3f} GB) | decode pass {part_achieved:.0f} GB/s")
     return res
 

@@ -683,12 +683,15 @@ int paged_attention_verify_fp8(void* out, int32_t out_dtype, const void* q, int3
  * k_pool for e < n_k_tiles and of v_pool after; tiles NULL reads tiles 0,
  * 1, ..., n_tiles - 1 of k_pool, a contiguous read of n_tiles * tile_bytes
  * bytes (n_k_tiles must then equal n_tiles, PKV_EINVAL otherwise).  Every tile byte is loaded once, 16 bytes
- * per lane; sink (device uint32 [1]) is written only when the bytes' XOR hits
+ * per lane, with streaming (nontemporal) loads as the decode kernels read
+ * K/V when streaming is nonzero, with plain loads otherwise (a plain pass
+ * over an unrelated buffer is what leaves the caches full of other data);
+ * sink (device uint32 [1]) is written only when the bytes' XOR hits
  * a fixed value (it keeps the loads alive).  tile_bytes a positive multiple of
  * 16, pools 16-byte aligned; tiles outside the pools are the caller's
  * contract. */
 int paged_kv_read_tiles(const void* k_pool, const void* v_pool, const int64_t* tiles, int64_t n_k_tiles,
-                        int64_t n_tiles, int64_t tile_bytes, uint32_t* sink, void* stream);
+                        int64_t n_tiles, int64_t tile_bytes, int32_t streaming, uint32_t* sink, void* stream);
 
 /* The matrix-core rate beside the chunked-prefill kernel, whose Q K^T and
  * P V products ("The detour, what really happens inside one forward pass",

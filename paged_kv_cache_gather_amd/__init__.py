@@ -121,7 +121,7 @@ _sig("paged_attention_verify", ctypes.c_int, _P, _i32, _P, _P, _P, _P, _i32, _P,
      _i32, _i32, _i64, _i32, _f32, _i32, _P, _i64, _P)
 _sig("paged_attention_verify_fp8", ctypes.c_int, _P, _i32, _P, _i32, _P, _P, _f32, _f32, _P, _i32, _P, _P, _i32, _i32,
      _i32, _i32, _i32, _i32, _i32, _i64, _i32, _f32, _P, _i64, _P)
-_sig("paged_kv_read_tiles", ctypes.c_int, _P, _P, _P, _i64, _i64, _i64, _P, _P)
+_sig("paged_kv_read_tiles", ctypes.c_int, _P, _P, _P, _i64, _i64, _i64, _i32, _P, _P)
 _sig("paged_kv_mfma_rate", ctypes.c_int, _i32, _i32, _i32, _P, _P)
 _sig("paged_attention_decode_whole_context", ctypes.c_int32, _i32, _i32, _i32, _i32, _i32, _i32)
 _sig("paged_attention_prefill_chunk", ctypes.c_int, _P, _i32, _P, _P, _P, _P, _i32, _P, _P, _i32,
@@ -872,9 +872,10 @@ def paged_attention_prefill_chunk(out: torch.Tensor, q: torch.Tensor, k_pool: to
 
 
 def paged_kv_read_tiles(k_pool: torch.Tensor, v_pool, tiles, n_k_tiles: int, n_tiles: int, tile_bytes: int,
-                        sink: torch.Tensor, stream=None):
+                        sink: torch.Tensor, stream=None, streaming: bool = True):
     """Read-only pass over pool tiles (a bandwidth ceiling beside the decode
-    kernels); tiles: device int64 [n_tiles] or None for a contiguous read."""
+    kernels); tiles: device int64 [n_tiles] or None for a contiguous read;
+    streaming: nontemporal loads as the decode kernels use, else plain ones."""
     _dev(k_pool, "k_pool")
     if v_pool is not None:
         _dev(v_pool, "v_pool")
@@ -886,7 +887,7 @@ def paged_kv_read_tiles(k_pool: torch.Tensor, v_pool, tiles, n_k_tiles: int, n_t
     if tiles is None and n_tiles * tile_bytes > k_pool.numel() * k_pool.element_size():
         raise PagedKVError(PKV_EINVAL, "contiguous read beyond the buffer")
     _check(_lib.paged_kv_read_tiles(_ptr(k_pool), _ptr(v_pool), _ptr(tiles), n_k_tiles, n_tiles, tile_bytes,
-                                    _ptr(sink), _stream(stream, k_pool.device)))
+                                    1 if streaming else 0, _ptr(sink), _stream(stream, k_pool.device)))
 
 
 def paged_kv_mfma_rate(mode: int, n_workgroups: int, iters: int, sink: torch.Tensor, stream=None):

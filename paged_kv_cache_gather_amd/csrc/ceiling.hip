@@ -12,7 +12,7 @@
 // i of the launch is chunk i % C of list entry i / C (C = tile_bytes / 16),
 // so consecutive lanes read consecutive bytes of a tile and a wave
 // instruction covers 1 KiB (streaming loads, as the decode kernels read their
-// K/V).  Each thread has kUnroll loads in flight before
+// K/V, or plain ones).  Each thread has kUnroll loads in flight before
 // it folds them into a running XOR; the result is stored only if it hits a
 // constant, which keeps every load alive without a store per thread.
 //
@@ -37,6 +37,7 @@ namespace {
 constexpr int kCeilThreads = 256;
 constexpr int kUnroll = 8;
 
+template <bool Stream>
 __global__ void __launch_bounds__(kCeilThreads)
 read_tiles_kernel(const unsigned char* __restrict__ kpool, const unsigned char* __restrict__ vpool,
                   const int64_t* __restrict__ tiles, int64_t n_k, int64_t n, int64_t tile_bytes,
@@ -52,7 +53,7 @@ read_tiles_kernel(const unsigned char* __restrict__ kpool, const unsigned char* 
       const int64_t e = item / C, c = item % C;
       const int64_t t = tiles ? tiles[e] : e;
       const unsigned char* pool = e < n_k ? kpool : vpool;
-      v[u] = ld16_stream(pool + t * tile_bytes + c * 16);
+      v[u] = Stream ? ld16_stream(pool + t * tile_bytes + c * 16) : ld16(pool + t * tile_bytes + c * 16);
     } else {
       v[u] = u32x4{0u, 0u, 0u, 0u};
     }
@@ -122,7 +123,8 @@ using pkv::fail;
 using pkv::ok;
 
 extern "C" int paged_kv_read_tiles(const void* k_pool, const void* v_pool, const int64_t* tiles, int64_t n_k_tiles,
-                                   int64_t n_tiles, int64_t tile_bytes, uint32_t* sink, void* stream) {
+                                   int64_t n_tiles, int64_t tile_bytes, int32_t streaming, uint32_t* sink,
+                                   void* stream) {
   if (n_tiles < 0 || n_k_tiles < 0 || n_k_tiles > n_tiles)
     return fail(PKV_EINVAL, "paged_kv_read_tiles: bad tile counts");
   if (!tiles && n_k_tiles != n_tiles)
@@ -136,9 +138,14 @@ extern "C" int paged_kv_read_tiles(const void* k_pool, const void* v_pool, const
   const int64_t per_wg = (int64_t)pkv::kCeilThreads * pkv::kUnroll;
   const int64_t grid = (items + per_wg - 1) / per_wg;
   if (grid > 0x7fffffffll) return fail(PKV_EINVAL, "paged_kv_read_tiles: too many tiles for one launch");
-  hipLaunchKernelGGL(pkv::read_tiles_kernel, dim3((unsigned)grid), dim3(pkv::kCeilThreads), 0, (hipStream_t)stream,
-                     (const unsigned char*)k_pool, (const unsigned char*)v_pool, tiles, n_k_tiles, n_tiles,
-                     tile_bytes, sink);
+  if (streaming)
+    hipLaunchKernelGGL(pkv::read_tiles_kernel<true>, dim3((unsigned)grid), dim3(pkv::kCeilThreads), 0,
+                       (hipStream_t)stream, (const unsigned char*)k_pool, (const unsigned char*)v_pool, tiles,
+                       n_k_tiles, n_tiles, tile_bytes, sink);
+  else
+    hipLaunchKernelGGL(pkv::read_tiles_kernel<false>, dim3((unsigned)grid), dim3(pkv::kCeilThreads), 0,
+                       (hipStream_t)stream, (const unsigned char*)k_pool, (const unsigned char*)v_pool, tiles,
+                       n_k_tiles, n_tiles, tile_bytes, sink);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(PKV_EHIP, std::string("paged_kv_read_tiles: ") + hipGetErrorString(e));
   return ok();

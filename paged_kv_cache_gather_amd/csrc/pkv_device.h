@@ -99,11 +99,11 @@ __device__ __forceinline__ u32x4 ld16(const void* p) {
 }
 // Streaming (nontemporal) loads, for cache bytes a step reads once.  Used
 // where one wave instruction takes whole 128-byte lines (a K row chunk of 16
-// tokens, a 1 KiB K or V run, all four 8-byte pieces of a 16-bit V row, both
-// halves of an 8-bit V row): the hint lets
-// the caches drop the lines first.  Measured on scattered 4 KiB tiles it lifts
-// what a read-only pass gets from ~6.1 to ~6.8 TB/s; on loads that take half
-// a line per instruction (the other half in the next) it costs instead.
+// tokens, a 1 KiB K or V run, all four 8-byte pieces of a 16-bit V row,
+// both halves of an 8-bit V row): the hint lets the caches drop the lines
+// first.  Measured on scattered 4 KiB tiles it lifts what a read-only pass
+// gets from ~6.1 to ~6.7 TB/s; on loads that take half a line per
+// instruction (the other half in the next) it costs instead.
 __device__ __forceinline__ u32x4 ld16_stream(const void* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
 }

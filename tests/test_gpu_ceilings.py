@@ -29,11 +29,12 @@ def test_read_tiles_reads_the_listed_tiles():
         torch.cuda.synchronize()
         got = int(sink.item()) & 0xFFFFFFFF
         assert got == (MAGIC if hit else 0), (tiles, n_k, hex(got))
-    # contiguous read of k_pool only
-    sink = torch.zeros(1, dtype=torch.int32, device=DEV)
-    pkv.paged_kv_read_tiles(v, None, None, 4, 4, 64, sink)
-    torch.cuda.synchronize()
-    assert int(sink.item()) & 0xFFFFFFFF == MAGIC
+    # contiguous read of k_pool only, streaming and plain loads
+    for streaming in (True, False):
+        sink = torch.zeros(1, dtype=torch.int32, device=DEV)
+        pkv.paged_kv_read_tiles(v, None, None, 4, 4, 64, sink, streaming=streaming)
+        torch.cuda.synchronize()
+        assert int(sink.item()) & 0xFFFFFFFF == MAGIC
 
 
 def test_read_tiles_rejects_bad_arguments():
