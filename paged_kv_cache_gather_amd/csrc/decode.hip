@@ -588,11 +588,15 @@ __device__ __forceinline__ void mfma_partition(const Rows& R, int n, int g, int 
                                                int64_t num_blocks, float scale_log2, float v_mul, int max_parts) {
   constexpr bool F8 = KV::kBytes == 1;
   constexpr bool kCausal = Rows::kCausal;
-  // key order of the score tiles: 16-bit K/V take each block's tokens in
-  // order (a K operand instruction reads 1 KiB contiguous; a lane's eight
-  // keys are four of each block of a pair, two 8-byte V pieces); 8-bit K/V
-  // keep the paired order (a lane's eight keys are one 8-byte V piece, where
-  // natural order would need 4-byte pieces and twice the V instructions)
+  // key order of the score tiles.  16-bit K/V, natural order: tile kt is
+  // block kt of the part, row m its token m (a K operand instruction reads
+  // 1 KiB, whole lines; a lane's eight keys of a product are four of each
+  // block of a pair, two 8-byte V pieces).  8-bit K/V, line order: tile
+  // 2 kp + h holds tokens 8 h .. 8 h + 7 of both blocks of pair kp (each
+  // chunk group reads two whole 128-byte lines), and the probabilities are
+  // realigned across lane groups before the value product so that a lane's
+  // eight keys are eight consecutive keys of one block, one 8-byte V piece
+  // (natural order would need 4-byte V pieces and twice the V instructions).
   static_assert(KV::kBytes != 4, "fp32 K/V have no MFMA path");
   constexpr bool kNatural = !F8;
   static_assert(F8 || (KV::kBytes == 2 && KV::kCode == QT::kCode), "16-bit K/V take queries of their type");
@@ -673,20 +677,19 @@ __device__ __forceinline__ void mfma_partition(const Rows& R, int n, int g, int 
             ka[kt][c] = in ? ld16_stream(kr + c * 4 * kBlockSize * 16) : u32x4{0u, 0u, 0u, 0u};
         }
       } else {
-        // tile 2 kp + sub of block pair kp, row m = 4a + r = the pair's key
-        // 8a + 4 sub + r (lane group a owns keys 8a .. 8a + 7)
-        const int k_half = r16 >> 3;                          // which block of the pair
-        const int k_tok = 8 * ((r16 >> 2) & 1) + (r16 & 3);  // token, + 4 sub
+        // line order: tile 2 kp + h, row m = block 2 kp + m / 8 of the part,
+        // token 8 h + m % 8 (each chunk group reads two whole lines)
+        const int k_half = r16 >> 3, k_tok = r16 & 7;
 #pragma unroll
         for (int kp = 0; kp < HB / 2; ++kp) {
           const bool in = !Masked || hbase + (2 * kp + k_half) * kBlockSize < n;
           const int64_t kb = clamp_block(tab[hb + 2 * kp + k_half], num_blocks);
           const unsigned char* kr = kpool + ((kb * Hkv + g) * CH + q4) * (kBlockSize * 16) + k_tok * 16;
 #pragma unroll
-          for (int sub = 0; sub < 2; ++sub)
+          for (int h = 0; h < 2; ++h)
 #pragma unroll
             for (int c = 0; c < KC; ++c)
-              ka[2 * kp + sub][c] = in ? ld16(kr + (4 * sub + c * 4 * kBlockSize) * 16) : u32x4{0u, 0u, 0u, 0u};
+              ka[2 * kp + h][c] = in ? ld16_stream(kr + (8 * h + c * 4 * kBlockSize) * 16) : u32x4{0u, 0u, 0u, 0u};
         }
       }
       f32x4 st[HB][RT];
@@ -717,8 +720,8 @@ __device__ __forceinline__ void mfma_partition(const Rows& R, int n, int g, int 
       // V operands, issued next, ahead of the softmax: lane (q4, r16) takes
       // dim 16 dt + r16 and the eight keys its probabilities cover — natural
       // order: keys 4 q4 .. 4 q4 + 3 of both blocks of the pair (two 8-byte
-      // pieces of the dim's rows); paired order: keys 8 q4 .. 8 q4 + 7 of the
-      // pair (one piece of block q4 / 2's row)
+      // pieces of the dim's rows); line order (8-bit): keys 8 q4 .. 8 q4 + 7
+      // of the pair, after the realignment (one piece of block q4 / 2's row)
       vraw_t vraw[HB / 2][DT];
 #pragma unroll
       for (int kp = 0; kp < HB / 2; ++kp) {
@@ -763,7 +766,8 @@ __device__ __forceinline__ void mfma_partition(const Rows& R, int n, int g, int 
             float x = st[kt][rt][r] * scale_log2;
             if constexpr (Masked) {  // keys past the context may hold anything
               const int key = kNatural ? hbase + kt * kBlockSize + 4 * q4 + r
-                                       : hbase + (kt >> 1) * 2 * kBlockSize + 8 * q4 + 4 * (kt & 1) + r;
+                                       : hbase + ((kt >> 1) * 2 + (q4 >> 1)) * kBlockSize + 8 * (kt & 1) +
+                                             4 * (q4 & 1) + r;
               x = key < (kCausal ? klim[rt] : n) ? x : -INFINITY;
             }
             st[kt][rt][r] = x;
@@ -805,6 +809,15 @@ __device__ __forceinline__ void mfma_partition(const Rows& R, int n, int g, int 
                                pack_f16x2(st[2 * kp][rt][2], st[2 * kp][rt][3]),
                                pack_f16x2(st[2 * kp + 1][rt][0], st[2 * kp + 1][rt][1]),
                                pack_f16x2(st[2 * kp + 1][rt][2], st[2 * kp + 1][rt][3])};
+            if constexpr (!kNatural) {
+              // line order: lane group q4 holds tokens 4 (q4 & 1) .. + 3 of
+              // block q4 / 2 in each tile; the odd rows of tile 2 kp's words
+              // trade with the even rows of tile 2 kp + 1's, leaving lane group
+              // q4 tokens 8 (q4 & 1) .. + 7 of block q4 / 2, as its V piece
+              const auto a0 = __builtin_amdgcn_permlane16_swap(pb[kp][rt][0], pb[kp][rt][2], false, false);
+              const auto a1 = __builtin_amdgcn_permlane16_swap(pb[kp][rt][1], pb[kp][rt][3], false, false);
+              pb[kp][rt] = u32x4{a0[0], a1[0], a0[1], a1[1]};
+            }
           }
       }
       // O^T += V^T P^T over each pair's 32 keys
