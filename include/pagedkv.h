@@ -387,8 +387,8 @@ int32_t paged_attention_decode_partition_size(void);
 /* 1 when paged_attention_decode and paged_attention_decode_append take the
  * whole-context path for these sizes, 0 otherwise (the split-context path;
  * paged_attention_decode_partitions / _reduce always split).  The path is
- * taken when max_context_len <= 2048, (n_q_heads / n_kv_heads) * head_dim *
- * element bytes <= 1024 and, with P = num_seqs * n_kv_heads, either P <= 256
+ * taken when max_context_len <= 2048 (for fp32 pools also (n_q_heads /
+ * n_kv_heads) * head_dim * 4 <= 1024) and, with P = num_seqs * n_kv_heads, either P <= 256
  * and (P >= 128 or max_context_len <= 1536), or 448 <= P <= 512 and
  * max_context_len * 2 * head_dim * element bytes >= 384 KiB (the decode of a
  * small batch is bound by the latency of one or two rounds of reads, not by
@@ -430,9 +430,10 @@ int64_t paged_attention_decode_workspace_bytes(int32_t num_seqs, int32_t n_q_hea
  * partition pass.
  * Short contexts in a small batch (paged_attention_decode_whole_context
  * says when): one launch instead, one workgroup per (sequence, KV head)
- * taking the whole context with its blocks dealt to 16 waves and the waves'
- * softmax states merged on chip; no partition is split or shared, the
- * workspace is not touched.
+ * taking the whole context with its blocks dealt to 16 waves (16-bit K/V
+ * on MFMA, the G query rows in one 16-row tile; fp32 K/V on the vector
+ * units) and the waves' softmax states merged on chip; no partition is
+ * split or shared, the workspace is not touched.
  *   out           device [num_seqs][n_q_heads][head_dim], out_dtype
  *                 (PKV_F32, or the KV dtype).
  *   q             device [num_seqs][n_q_heads][head_dim], kv_dtype.

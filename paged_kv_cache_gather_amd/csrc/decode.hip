@@ -482,14 +482,14 @@ __device__ __forceinline__ float rows4_sum(float x) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
-template <int D, int ROWS, int NW = kWaves>
+template <int D, int ROWS, int NW = kWaves, int PBLK = kPartBlocks>
 struct RunLds {
   float o[NW][ROWS][D + 4];  // the waves' unnormalised outputs (rows padded: LDS banks)
   float ml[NW][ROWS][2];     // and (max, sum) per row
   float wgt[ROWS][NW];       // merge weights 2^(m_w - M) per row
   float row_m[ROWS], row_l[ROWS];
   int row_parts[ROWS];        // partitions of the row's sequence
-  int32_t blk[kPartBlocks];   // the partition's block ids
+  int32_t blk[PBLK];          // the partition's block ids
 };
 
 // 8 E4M3 codes (two words, the first code in the low byte) -> one 8-element
@@ -522,7 +522,8 @@ __device__ __forceinline__ uint64_t ld8(const void* p) { return *reinterpret_cas
 //  * SetRows: members are the sequences of a shared run (below);
 //  * TokenRows: members are query tokens q0 .. q0 + k - 1 of one sequence at
 //    absolute positions pos0 .. pos0 + k - 1, each attending keys 0 .. its
-//    position (causal), as in verifying several drafted tokens at once.
+//    position (causal), as in verifying several drafted tokens at once;
+//  * WholeRows: one sequence over its whole context (the whole-context path).
 struct SeqRows {
   static constexpr bool kCausal = false;
   int s, k;
@@ -559,6 +560,17 @@ struct TokenRows {
   __device__ int parts(int mi) const { return (pos0 + mi + kPart) / kPart; }  // partitions holding keys 0 .. pos
   __device__ int limit(int mi) const { return pos0 + mi + 1; }
 };
+// WholeRows: the G query heads of sequence s over its whole context, one
+// "partition" of up to kWholeSpan tokens whose result is final (no merge).
+struct WholeRows {
+  static constexpr bool kCausal = false;
+  int s;
+  __device__ int table_row() const { return s; }
+  __device__ int members() const { return 1; }
+  __device__ int64_t base(int) const { return s; }
+  __device__ int parts(int) const { return 1; }
+  __device__ int limit(int) const { return 0x7fffffff; }
+};
 
 // One partition on MFMA for the query rows R describes, whose members all
 // read the same blocks for it (16 RT rows: row r = member r / G, head r % G;
@@ -578,8 +590,9 @@ struct TokenRows {
 //    8-bit V widened exactly to fp16, with fp16 probabilities;
 //    the waves' (max, sum, o) are merged through LDS and written as each
 //    member's partition result (8-bit values: times v_mul, the pool scale).
-template <typename KV, typename QT, int D, int G, int RT, bool Masked, int OutCode, int NH, int NW, typename Rows>
-__device__ __forceinline__ void mfma_partition(const Rows& R, int n, int g, int p, RunLds<D, 16 * RT, NW>& sh,
+template <typename KV, typename QT, int D, int G, int RT, bool Masked, int OutCode, int NH, int NW,
+          int PBLK = kPartBlocks, typename Rows>
+__device__ __forceinline__ void mfma_partition(const Rows& R, int n, int g, int p, RunLds<D, 16 * RT, NW, PBLK>& sh,
                                                void* __restrict__ out, float* __restrict__ ws_o,
                                                float* __restrict__ ws_ml, const typename QT::bits* __restrict__ q,
                                                const unsigned char* __restrict__ kpool,
@@ -608,7 +621,7 @@ __device__ __forceinline__ void mfma_partition(const Rows& R, int n, int g, int 
   constexpr int KC = F8 ? D / 64 : DC;               // K chunks per lane and score tile
   constexpr int VROW = kBlockSize * KV::kBytes;      // bytes of one dim of a V tile
   constexpr int TILE = D * VROW;                     // bytes of one (block, head) tile
-  constexpr int WB = kPartBlocks / NW;               // blocks per wave (NW waves of 64 lanes)
+  constexpr int WB = PBLK / NW;                      // blocks per wave (NW waves of 64 lanes)
   constexpr int HB = WB / NH;                        // blocks per part of a wave
   static_assert(HB % 2 == 0 && HB * NH == WB, "wave parts take whole block pairs");
   using vraw_t = typename std::conditional<F8, uint64_t, u32x4>::type;
@@ -636,9 +649,8 @@ __device__ __forceinline__ void mfma_partition(const Rows& R, int n, int g, int 
   }
 
   // the partition's block ids, read once into LDS (0 past the valid tokens)
-  if (tid < kPartBlocks)
-    sh.blk[tid] =
-        (!Masked || tid * kBlockSize < n) ? tables[(int64_t)R.table_row() * max_blocks + p * kPartBlocks + tid] : 0;
+  if (tid < PBLK)
+    sh.blk[tid] = (!Masked || tid * kBlockSize < n) ? tables[(int64_t)R.table_row() * max_blocks + p * PBLK + tid] : 0;
   __syncthreads();
   const int32_t* tab = sh.blk + w * WB;
   const int wbase = w * WB * kBlockSize;  // the wave's first token in the partition
@@ -1152,16 +1164,20 @@ decode_partition_kernel(void* __restrict__ out, float* __restrict__ ws_o, float*
 // a whole (sequence, KV head): the sequence's blocks are dealt evenly to its
 // waves (a short context still uses all of them), the waves' softmax states
 // merge in LDS and the output is written directly.  Partitions that
-// sequences share are read per sequence on this path.
+// sequences share are read per sequence on this path.  16-bit pools run the
+// MFMA partition routine (the G query rows padded to one 16-row tile: with
+// G = 8 the vector routine's products, not the reads, set its pace); fp32
+// pools the vector routine.
 constexpr int kWholeSpan = 2048;      // context tokens one workgroup takes
 constexpr int kWholeWaves = 16;       // its waves (4 per SIMD)
+constexpr int kWholeBlocks = kWholeSpan / kBlockSize;
 
-// Does a batch take the whole-context path?  The per-wave accumulators must
-// leave the 16-wave workgroup within 128 registers (G x D x element bytes
-// <= 1024: G <= 8 at head_dim 64, G <= 4 at 128 for 16-bit pools), so one
-// workgroup fills a CU and the 256 CUs take P = (sequence, KV head) pairs in
-// rounds of 256.  Measured against the split path (Llama-3-8B and
-// TinyLlama heads, uniform and prefix-sharing batches): up to 256 pairs — one
+// Does a batch take the whole-context path?  One workgroup fills a CU and the
+// 256 CUs take P = (sequence, KV head) pairs in rounds of 256.  16-bit pools
+// take any G (one 16-row MFMA tile); on fp32 pools the vector routine's
+// per-wave accumulators must stay within 128 registers (G x D x 4 <= 1024).
+// Measured against the split path (Llama-3-8B and TinyLlama heads, G = 8
+// and 16 at head_dim 128, uniform and prefix-sharing batches): up to 256 pairs — one
 // round — it wins except when fewer than 128 pairs hold contexts past 1536
 // tokens (too few CUs take part; the split path's 4x more workgroups win);
 // a second round pays only when it is at least three quarters full (P >= 448)
@@ -1169,7 +1185,7 @@ constexpr int kWholeWaves = 16;       // its waves (4 per SIMD)
 // 1536 at 64); past 512 pairs, or below those sizes, reading shared
 // partitions once and the split path's finer work units win.
 inline bool whole_context(int B, int Hkv, int G, int D, int es, int max_context_len) {
-  if (max_context_len > kWholeSpan || G * D * es > 1024) return false;
+  if (max_context_len > kWholeSpan || (es == 4 && G * D * es > 1024)) return false;
   const int64_t units = (int64_t)B * Hkv;
   if (units <= 256) return units >= 128 || max_context_len <= 1536;
   return units >= 448 && units <= 512 && (int64_t)max_context_len * 2 * D * es >= 384 * 1024;
@@ -1186,10 +1202,7 @@ decode_whole_kernel(void* __restrict__ out, const typename T::bits* __restrict__
                     const unsigned char* vpool, const int32_t* __restrict__ tables, int max_blocks,
                     const int32_t* __restrict__ lens, int Hkv, int64_t num_blocks, int max_context_len,
                     float scale_log2, AppendArgs app) {
-  constexpr int RMAX = G;
-  constexpr int SMEM = (kWholeSpan > kWholeWaves * D ? kWholeSpan : kWholeWaves * D) * RMAX;
-  __shared__ __attribute__((aligned(16))) float smem[SMEM];
-  __shared__ float sml[kWholeWaves * RMAX][2];
+  static_assert(G <= 16, "one 16-row tile");
   const int g = blockIdx.x, s = blockIdx.y;
   if (app.T > 0) {  // uniform
     constexpr int C = D * T::kBytes / 16;  // 16-byte pool chunks per head row
@@ -1206,9 +1219,22 @@ decode_whole_kernel(void* __restrict__ out, const typename T::bits* __restrict__
       store_out<OutCode>(out, ((int64_t)s * Hkv * G + g * G) * D + i, 0.f);
     return;
   }
-  partition_rows<T, D, G, OutCode, kWholeSpan, kWholeWaves>(smem, sml, out, nullptr, nullptr, q, kpool, vpool,
-                                                            tables + (int64_t)s * max_blocks, lens, s, g, 0, L, Hkv,
-                                                            num_blocks, max_context_len, scale_log2, 1);
+  if constexpr (T::kBytes == 2) {
+    // each wave's 8 blocks in parts of 4 (head_dim 64) or 2 (128): within
+    // 128 registers at 4 waves per SIMD
+    __shared__ __attribute__((aligned(16))) RunLds<D, 16, kWholeWaves, kWholeBlocks> sh;
+    mfma_partition<T, T, D, G, 1, true, OutCode, D == 64 ? 2 : 4, kWholeWaves, kWholeBlocks>(
+        WholeRows{s}, L, g, 0, sh, out, nullptr, nullptr, q, kpool, vpool, tables, max_blocks, Hkv, num_blocks,
+        scale_log2, 1.f, 1);
+  } else {
+    constexpr int RMAX = G;
+    constexpr int SMEM = (kWholeSpan > kWholeWaves * D ? kWholeSpan : kWholeWaves * D) * RMAX;
+    __shared__ __attribute__((aligned(16))) float smem[SMEM];
+    __shared__ float sml[kWholeWaves * RMAX][2];
+    partition_rows<T, D, G, OutCode, kWholeSpan, kWholeWaves>(smem, sml, out, nullptr, nullptr, q, kpool, vpool,
+                                                              tables + (int64_t)s * max_blocks, lens, s, g, 0, L,
+                                                              Hkv, num_blocks, max_context_len, scale_log2, 1);
+  }
 }
 
 
@@ -1386,7 +1412,7 @@ void launch_reduce(const DecodeArgs& a, int G) {
 
 template <typename T, int D, int G, int OutCode>
 void launch_whole(const DecodeArgs& a) {
-  if constexpr (G * D * T::kBytes <= 1024) {
+  if constexpr (T::kBytes == 2 || G * D * T::kBytes <= 1024) {
     hipLaunchKernelGGL((decode_whole_kernel<T, D, G, OutCode>), dim3((unsigned)a.Hkv, (unsigned)a.B),
                        dim3(kWholeWaves * 64), 0, a.stream, a.out, (const typename T::bits*)a.q, a.kpool, a.vpool,
                        a.tables, a.max_blocks, a.lens, a.Hkv, a.num_blocks, a.max_context_len, a.scale_log2,

@@ -33,6 +33,8 @@ CASES = [
     ("gqa4_d128_bf16", 16, 4, 128, "bf16"),
     ("gqa2_d128_f16", 8, 4, 128, "f16"),
     ("mha_d128_bf16", 4, 4, 128, "bf16"),
+    ("gqa8_d128_bf16", 32, 4, 128, "bf16"),
+    ("gqa16_d128_f16", 32, 2, 128, "f16"),
     ("gqa4_d64_f32", 8, 2, 64, "f32"),
     ("gqa2_d128_f32", 4, 2, 128, "f32"),
 ]
@@ -139,7 +141,10 @@ def test_whole_context_limits():
     assert not f(55, 32, 8, 128, "bf16", 2048)  # 440 pairs
     assert not f(129, 32, 4, 64, "f16", 2048)   # 516 pairs
     assert f(64, 16, 4, 128, "bf16", 1000)      # G 4 at head_dim 128
-    assert not f(64, 32, 4, 128, "bf16", 1000)  # G 8 at head_dim 128: registers
+    assert f(64, 32, 4, 128, "bf16", 1000)      # G 8 at head_dim 128 (16-bit: MFMA)
+    assert f(64, 64, 4, 128, "f16", 1000)       # G 16
+    assert f(64, 16, 4, 64, "f32", 1000)        # fp32 pools: G x d x 4 <= 1024
+    assert not f(64, 32, 4, 64, "f32", 1000)    # fp32, G 8 at head_dim 64: registers
     assert not f(8, 32, 8, 128, "fp8_e4m3", 1000)  # 8-bit pools keep their path
     assert not f(0, 32, 4, 64, "f16", 100)
     assert not f(8, 30, 4, 64, "f16", 100)      # n_q_heads not a multiple
