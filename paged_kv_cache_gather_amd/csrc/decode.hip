@@ -1119,6 +1119,11 @@ decode_fp8_partition_kernel(void* __restrict__ out, float* __restrict__ ws_o, fl
                                                   scale_log2, v_mul, max_parts);
 }
 
+// The per-sequence partitions of 16-bit pools: the vector routine for G <= 4
+// query rows per KV head; from G = 8 on the MFMA routine (the G rows padded to
+// one 16-row tile, at most half of it idle), where the vector units' G
+// products per cached element, not the reads, would set the pace.
+constexpr int kSeqMfmaMinG = 8;
 template <typename T, int D, int G, int OutCode>
 __global__ void __launch_bounds__(kThreads, PKV_DECODE_MIN_WAVES)
 decode_partition_kernel(void* __restrict__ out, float* __restrict__ ws_o, float* __restrict__ ws_ml,
@@ -1126,12 +1131,6 @@ decode_partition_kernel(void* __restrict__ out, float* __restrict__ ws_o, float*
                         const unsigned char* __restrict__ vpool, const int32_t* __restrict__ tables,
                         int max_blocks, const int32_t* __restrict__ lens, int Hkv, int64_t num_blocks,
                         int max_context_len, float scale_log2, int max_parts) {
-  constexpr int RMAX = G;
-  // Per-wave probabilities [kWaves][TPW][R]; after the V pass the same memory
-  // holds the waves' partial outputs [kWaves][R][D].
-  constexpr int SMEM = (kPart > kWaves * D ? kPart : kWaves * D) * RMAX;
-  __shared__ __attribute__((aligned(16))) float smem[SMEM];
-  __shared__ float sml[kWaves * RMAX][2];
 
   // last partitions first: long sequences' work starts early, the tail is
   // made of partitions every sequence has
@@ -1151,10 +1150,21 @@ decode_partition_kernel(void* __restrict__ out, float* __restrict__ ws_o, float*
   if (in_shared_run<T, G>(pr, tables, max_blocks, max_context_len, s, p, L)) return;
   const int t0 = p * kPart;
   const int n = (L - t0) < kPart ? (L - t0) : kPart;  // tokens in this partition
-  const int32_t* tab = tables + (int64_t)s * max_blocks + t0 / kBlockSize;
-
-  partition_rows<T, D, G, OutCode>(smem, sml, out, ws_o, ws_ml, q, kpool, vpool, tab, lens, s, g, p, n, Hkv,
-                                   num_blocks, max_context_len, scale_log2, max_parts);
+  if constexpr (T::kBytes == 2 && G >= kSeqMfmaMinG) {
+    __shared__ __attribute__((aligned(16))) RunLds<D, 16> sh;
+    mfma_partition<T, T, D, G, 1, true, OutCode, 2, kWaves>(SeqRows{s, 1, lens, max_context_len}, n, g, p, sh, out,
+                                                           ws_o, ws_ml, q, kpool, vpool, tables, max_blocks, Hkv,
+                                                           num_blocks, scale_log2, 1.f, max_parts);
+  } else {
+    // Per-wave probabilities [kWaves][TPW][R]; after the V pass the same
+    // memory holds the waves' partial outputs [kWaves][R][D].
+    constexpr int SMEM = (kPart > kWaves * D ? kPart : kWaves * D) * G;
+    __shared__ __attribute__((aligned(16))) float smem[SMEM];
+    __shared__ float sml[kWaves * G][2];
+    const int32_t* tab = tables + (int64_t)s * max_blocks + t0 / kBlockSize;
+    partition_rows<T, D, G, OutCode>(smem, sml, out, ws_o, ws_ml, q, kpool, vpool, tab, lens, s, g, p, n, Hkv,
+                                     num_blocks, max_context_len, scale_log2, max_parts);
+  }
 }
 
 // ---- short contexts in a small batch: one launch, no merge ------------------

@@ -58,6 +58,8 @@ SMALL = [
     ("opt13b_small", 40, 40, 128, "f16", [2048, 2048, 1, 31]),
     ("gqa2_small", 8, 4, 128, "bf16", [3, 16, 17, 511, 512, 1537]),
     ("gqa16_small", 32, 2, 64, "bf16", [100, 900]),
+    ("gqa8_d128_edges", 64, 8, 128, "bf16", [3, 16, 17, 511, 512, 513, 1537, 3000]),
+    ("gqa16_d128_f16", 32, 2, 128, "f16", [1, 100, 511, 512, 513, 2049]),
     ("f32_d128", 8, 2, 128, "f32", [5, 600]),
 ]
 
