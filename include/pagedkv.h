@@ -392,7 +392,7 @@ int32_t paged_attention_decode_partition_size(void);
  * and (P >= 128 or max_context_len <= 1536), or 448 <= P <= 512 and
  * max_context_len * 2 * head_dim * element bytes >= 384 KiB (the decode of a
  * small batch is bound by the latency of one or two rounds of reads, not by
- * HBM bandwidth); never for 8-bit pools.  ("The decode stage, and how to spot the
+ * HBM bandwidth); the same rule for 8-bit pools (element bytes 1).  ("The decode stage, and how to spot the
  * waste", Life of a prompt: the same attention, one query per sequence.)
  * Invalid sizes give 0. */
 int32_t paged_attention_decode_whole_context(int32_t num_seqs, int32_t n_q_heads, int32_t n_kv_heads,
@@ -518,7 +518,10 @@ int64_t paged_attention_decode_noalloc_max_workspace_bytes(void);
  * of paged_attention_decode.  The codes are widened exactly to q_dtype for the
  * score products and to fp16 for the value products (both on MFMA, fp32
  * accumulation, probabilities in fp16); k_scale folds into the softmax scale
- * and v_scale into the output.  k_scale, v_scale finite and > 0.  Half the
+ * and v_scale into the output.  Short contexts in a small batch take the
+ * whole-context launch as paged_attention_decode does
+ * (paged_attention_decode_whole_context with PKV_FP8_E4M3 says when).
+ * k_scale, v_scale finite and > 0.  Half the
  * bytes of a 16-bit cache per decode step ("Quantization", vLLM Serving deep
  * dive). */
 int paged_attention_decode_fp8(void* out, int32_t out_dtype, const void* q, int32_t q_dtype,

@@ -1206,19 +1206,27 @@ inline bool whole_context(int B, int Hkv, int G, int D, int es, int max_context_
 // row's block is the sequence's own (copy-on-write done before the append),
 // so no other workgroup reads it, and a workgroup-scope release / acquire
 // around a barrier orders the write before this workgroup's reads.
-template <typename T, int D, int G, int OutCode>
+// KV is the pools' type, QT the queries' (the same for 16-bit and fp32
+// pools; fp16 or bf16 queries over 8-bit pools, whose values are scaled by
+// v_mul and whose new rows are quantised on the way in).
+template <typename KV, typename QT, int D, int G, int OutCode>
 __global__ void __launch_bounds__(kWholeWaves * 64, 1)
-decode_whole_kernel(void* __restrict__ out, const typename T::bits* __restrict__ q, const unsigned char* kpool,
+decode_whole_kernel(void* __restrict__ out, const typename QT::bits* __restrict__ q, const unsigned char* kpool,
                     const unsigned char* vpool, const int32_t* __restrict__ tables, int max_blocks,
                     const int32_t* __restrict__ lens, int Hkv, int64_t num_blocks, int max_context_len,
-                    float scale_log2, AppendArgs app) {
+                    float scale_log2, float v_mul, AppendArgs app) {
   static_assert(G <= 16, "one 16-row tile");
   const int g = blockIdx.x, s = blockIdx.y;
   if (app.T > 0) {  // uniform
-    constexpr int C = D * T::kBytes / 16;  // 16-byte pool chunks per head row
-    if (s < app.T && threadIdx.x < C)
-      cache_write_chunk<T::kBytes>(app.key, app.value, app.kstride_b, app.vstride_b, app.kpool, app.vpool,
-                                   app.slots[s], app.num_slots, s, g, threadIdx.x, Hkv, D);
+    constexpr int C = D * KV::kBytes / 16;  // 16-byte pool chunks per head row
+    if (s < app.T && threadIdx.x < C) {
+      if constexpr (KV::kBytes == 1)
+        cache_write_chunk_fp8<QT>(app.key, app.value, app.kstride_b, app.vstride_b, app.kpool, app.vpool,
+                                  app.slots[s], app.num_slots, s, g, threadIdx.x, Hkv, D, app.k_inv, app.v_inv);
+      else
+        cache_write_chunk<KV::kBytes>(app.key, app.value, app.kstride_b, app.vstride_b, app.kpool, app.vpool,
+                                      app.slots[s], app.num_slots, s, g, threadIdx.x, Hkv, D);
+    }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
     __syncthreads();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
@@ -1229,14 +1237,15 @@ decode_whole_kernel(void* __restrict__ out, const typename T::bits* __restrict__
       store_out<OutCode>(out, ((int64_t)s * Hkv * G + g * G) * D + i, 0.f);
     return;
   }
-  if constexpr (T::kBytes == 2) {
-    // each wave's 8 blocks in parts of 4 (head_dim 64) or 2 (128): within
-    // 128 registers at 4 waves per SIMD
+  if constexpr (KV::kBytes != 4) {
+    // each wave's 8 blocks in parts of 4 (head_dim 64, and 8-bit pools) or 2
+    // (16-bit at 128): within 128 registers at 4 waves per SIMD
     __shared__ __attribute__((aligned(16))) RunLds<D, 16, kWholeWaves, kWholeBlocks> sh;
-    mfma_partition<T, T, D, G, 1, true, OutCode, D == 64 ? 2 : 4, kWholeWaves, kWholeBlocks>(
-        WholeRows{s}, L, g, 0, sh, out, nullptr, nullptr, q, kpool, vpool, tables, max_blocks, Hkv, num_blocks,
-        scale_log2, 1.f, 1);
+    mfma_partition<KV, QT, D, G, 1, true, OutCode, (D == 64 || KV::kBytes == 1) ? 2 : 4, kWholeWaves,
+                   kWholeBlocks>(WholeRows{s}, L, g, 0, sh, out, nullptr, nullptr, q, kpool, vpool, tables,
+                                 max_blocks, Hkv, num_blocks, scale_log2, v_mul, 1);
   } else {
+    using T = KV;
     constexpr int RMAX = G;
     constexpr int SMEM = (kWholeSpan > kWholeWaves * D ? kWholeSpan : kWholeWaves * D) * RMAX;
     __shared__ __attribute__((aligned(16))) float smem[SMEM];
@@ -1420,13 +1429,13 @@ void launch_reduce(const DecodeArgs& a, int G) {
                        a.max_context_len, a.max_parts);
 }
 
-template <typename T, int D, int G, int OutCode>
+template <typename KV, typename QT, int D, int G, int OutCode>
 void launch_whole(const DecodeArgs& a) {
-  if constexpr (T::kBytes == 2 || G * D * T::kBytes <= 1024) {
-    hipLaunchKernelGGL((decode_whole_kernel<T, D, G, OutCode>), dim3((unsigned)a.Hkv, (unsigned)a.B),
-                       dim3(kWholeWaves * 64), 0, a.stream, a.out, (const typename T::bits*)a.q, a.kpool, a.vpool,
+  if constexpr (KV::kBytes != 4 || G * D * KV::kBytes <= 1024) {
+    hipLaunchKernelGGL((decode_whole_kernel<KV, QT, D, G, OutCode>), dim3((unsigned)a.Hkv, (unsigned)a.B),
+                       dim3(kWholeWaves * 64), 0, a.stream, a.out, (const typename QT::bits*)a.q, a.kpool, a.vpool,
                        a.tables, a.max_blocks, a.lens, a.Hkv, a.num_blocks, a.max_context_len, a.scale_log2,
-                       a.app);
+                       a.v_mul, a.app);
   }
 }
 
@@ -1434,7 +1443,7 @@ template <typename T, int D, int G, int OutCode>
 void launch_decode(const DecodeArgs& a, bool partitions, bool reduce) {
   // the one-call form (partitions and merge together) of a short, small batch
   if (partitions && reduce && whole_context(a.B, a.Hkv, G, D, T::kBytes, a.max_context_len)) {
-    launch_whole<T, D, G, OutCode>(a);
+    launch_whole<T, T, D, G, OutCode>(a);
     return;
   }
   if (partitions && T::kBytes == 2) launch_shared<T, T, D, G, OutCode>(a);
@@ -1448,9 +1457,13 @@ void launch_decode(const DecodeArgs& a, bool partitions, bool reduce) {
 }
 
 // 8-bit cache: shared runs, then the per-sequence MFMA partitions, then the
-// reduction.
+// reduction (a short, small batch: the whole-context launch instead).
 template <typename QT, int D, int G, int OutCode>
 void launch_decode_fp8(const DecodeArgs& a, bool partitions, bool reduce) {
+  if (partitions && reduce && whole_context(a.B, a.Hkv, G, D, FP8::kBytes, a.max_context_len)) {
+    launch_whole<FP8, QT, D, G, OutCode>(a);
+    return;
+  }
   if (partitions) {
     launch_shared<FP8, QT, D, G, OutCode>(a);
     hipLaunchKernelGGL((decode_fp8_partition_kernel<QT, D, G, OutCode>),
@@ -1525,8 +1538,7 @@ extern "C" int32_t paged_attention_decode_partition_size(void) { return pkv::kPa
 extern "C" int32_t paged_attention_decode_whole_context(int32_t num_seqs, int32_t n_q_heads, int32_t n_kv_heads,
                                                         int32_t head_dim, int32_t kv_dtype, int32_t max_context_len) {
   const int es = pkv::esize_of(kv_dtype);
-  if (num_seqs <= 0 || n_kv_heads <= 0 || n_q_heads <= 0 || n_q_heads % n_kv_heads || max_context_len < 0 ||
-      kv_dtype == PKV_FP8_E4M3 || !es)
+  if (num_seqs <= 0 || n_kv_heads <= 0 || n_q_heads <= 0 || n_q_heads % n_kv_heads || max_context_len < 0 || !es)
     return 0;
   return pkv::whole_context(num_seqs, n_kv_heads, n_q_heads / n_kv_heads, head_dim, es, max_context_len) ? 1 : 0;
 }

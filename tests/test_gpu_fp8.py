@@ -156,6 +156,47 @@ def test_decode_fp8_small(name, Hq, Hkv, d, dtype, lens, out_kind):
     _check(w, out, out_dtype)
 
 
+WHOLE_LENS = [1, 15, 16, 17, 100, 511, 512, 513, 1024, 1500, 2047, 2048]
+FP8_WHOLE = [
+    # name, Hq, Hkv, d, q dtype
+    ("whole_tinyllama_f16", 32, 4, 64, "f16"),
+    ("whole_gqa4_d128_bf16", 32, 8, 128, "bf16"),
+    ("whole_gqa16_d128_f16", 32, 2, 128, "f16"),
+    ("whole_mha_d64_bf16", 8, 8, 64, "bf16"),
+]
+
+
+@pytest.mark.parametrize("name,Hq,Hkv,d,dtype", FP8_WHOLE, ids=[c[0] for c in FP8_WHOLE])
+def test_decode_fp8_whole_context(name, Hq, Hkv, d, dtype):
+    # short contexts, 128 (sequence, KV head) pairs: the whole-context launch,
+    # against the dequantised oracle and against the split path; the one-call
+    # step (quantising write inside the launch) bit for bit against the write
+    # followed by the attention
+    import paged_kv_cache_gather_amd as pkv
+    from paged_kv_cache_gather_amd.batch import DeviceBatch
+    n = -(-128 // Hkv)
+    lens = [WHOLE_LENS[i % len(WHOLE_LENS)] for i in range(max(n, len(WHOLE_LENS)))]
+    w = synth.custom_workload(name, Hq, Hkv, d, dtype, 4096, seed=27, decode_lens=lens)
+    kw = dict(fill="host", out_dtype="f32", kv_cache="fp8_e4m3", k_scale=FP8_K_SCALE, v_scale=FP8_V_SCALE)
+    sep, one = DeviceBatch(w, DEV, **kw), DeviceBatch(w, DEV, **kw)
+    assert pkv.paged_attention_decode_whole_context(w.n_decode, Hq, Hkv, d, "fp8_e4m3", sep.decode.max_context_len)
+    print(f"fp8 whole context {name}", flush=True)
+    out_sep, out_one, out_split = sep.new_decode_out(), one.new_decode_out(), sep.new_decode_out()
+    sep.append_decode()
+    sep.attend_decode(out_sep)
+    sep.attend_decode_split(out_split)
+    one.step_decode(out_one)
+    torch.cuda.synchronize()
+    assert torch.equal(out_sep.view(torch.int32), out_one.view(torch.int32))
+    assert torch.equal(sep.k_pool.view(torch.uint8), one.k_pool.view(torch.uint8))
+    assert torch.equal(sep.v_pool.view(torch.uint8), one.v_pool.view(torch.uint8))
+    _check(w, out_one, "f32")
+    atol, rtol = tolerance(dtype, "f32")
+    got, split = out_one.double().cpu().numpy(), out_split.double().cpu().numpy()
+    for s in range(w.n_decode):
+        assert_close(f"{name} whole vs split seq {s}", got[s], split[s], 2 * atol, 2 * rtol)
+
+
 FP8_FUSED = [
     # name, Hq, Hkv, d, q dtype, lens, prefix_len, prefix_group
     ("fused8_shared_cow", 32, 8, 128, "bf16", [1100, 1100, 1500, 1030, 600, 17, 1, 2049],

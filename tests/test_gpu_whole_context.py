@@ -145,7 +145,10 @@ def test_whole_context_limits():
     assert f(64, 64, 4, 128, "f16", 1000)       # G 16
     assert f(64, 16, 4, 64, "f32", 1000)        # fp32 pools: G x d x 4 <= 1024
     assert not f(64, 32, 4, 64, "f32", 1000)    # fp32, G 8 at head_dim 64: registers
-    assert not f(8, 32, 8, 128, "fp8_e4m3", 1000)  # 8-bit pools keep their path
+    assert f(8, 32, 8, 128, "fp8_e4m3", 1000)  # 8-bit pools: the same rule
+    assert not f(8, 32, 8, 128, "fp8_e4m3", 2000)  # 64 pairs, contexts past 1536
+    assert f(64, 32, 8, 128, "fp8_e4m3", 1536)  # 512 pairs, 384 KiB per pair at 1 byte
+    assert not f(64, 32, 8, 128, "fp8_e4m3", 1535)
     assert not f(0, 32, 4, 64, "f16", 100)
     assert not f(8, 30, 4, 64, "f16", 100)      # n_q_heads not a multiple
     # the split path just past the span still matches the oracle
