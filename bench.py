@@ -795,8 +795,8 @@ def decode_leg(w, K, W, out_dtype, seed, flush, fp8=False, modes=True, profile=N
     b = DeviceBatch(w, "cuda:0", fill="device", out_dtype=out_dtype, **kw)
     out = b.new_decode_out()
     import paged_kv_cache_gather_amd as pkv
-    whole = (not fp8) and pkv.paged_attention_decode_whole_context(
-        w.n_decode, w.n_q_heads, w.n_kv_heads, w.head_dim, w.dtype, b.decode.max_context_len)
+    whole = pkv.paged_attention_decode_whole_context(
+        w.n_decode, w.n_q_heads, w.n_kv_heads, w.head_dim, "fp8_e4m3" if fp8 else w.dtype, b.decode.max_context_len)
     t = time_decode(b, out, K, W, flush)
     warm3 = time_decode(b, out, K, 2)
     by = decode_bytes(b)

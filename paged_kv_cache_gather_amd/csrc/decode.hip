@@ -1183,22 +1183,25 @@ constexpr int kWholeWaves = 16;       // its waves (4 per SIMD)
 constexpr int kWholeBlocks = kWholeSpan / kBlockSize;
 
 // Does a batch take the whole-context path?  One workgroup fills a CU and the
-// 256 CUs take P = (sequence, KV head) pairs in rounds of 256.  16-bit pools
-// take any G (one 16-row MFMA tile); on fp32 pools the vector routine's
-// per-wave accumulators must stay within 128 registers (G x D x 4 <= 1024).
-// Measured against the split path (Llama-3-8B and TinyLlama heads, G = 8
-// and 16 at head_dim 128, uniform and prefix-sharing batches): up to 256 pairs — one
-// round — it wins except when fewer than 128 pairs hold contexts past 1536
-// tokens (too few CUs take part; the split path's 4x more workgroups win);
-// a second round pays only when it is at least three quarters full (P >= 448)
-// and each pair reads at least 384 KiB (768 tokens at head_dim 128 in 16 bits,
-// 1536 at 64); past 512 pairs, or below those sizes, reading shared
-// partitions once and the split path's finer work units win.
+// 256 CUs take P = (sequence, KV head) pairs in rounds of 256.  16-bit and
+// 8-bit pools take any G (one 16-row MFMA tile); on fp32 pools the vector
+// routine's per-wave accumulators must stay within 128 registers
+// (G x D x 4 <= 1024).  Measured against the split path on uniform and
+// prefix-sharing batches: up to 256 pairs — one round — the whole-context
+// launch wins except when fewer than 128 pairs hold contexts past 1536 tokens
+// (too few CUs take part; the split path's 4x more workgroups win).  A second
+// round: on the MFMA routine it wins from 384 pairs on at every length up to
+// the span (TinyLlama and Llama-3-8B heads, 384 to 640 pairs) and loses at
+// 320; it stops at 512 pairs, past which reading shared partitions once and
+// the split path's finer work units win on prefix-sharing batches.  The
+// vector routine (fp32 pools) keeps the band it was measured for: 448 to
+// 512 pairs with at least 384 KiB per pair.
 inline bool whole_context(int B, int Hkv, int G, int D, int es, int max_context_len) {
   if (max_context_len > kWholeSpan || (es == 4 && G * D * es > 1024)) return false;
   const int64_t units = (int64_t)B * Hkv;
   if (units <= 256) return units >= 128 || max_context_len <= 1536;
-  return units >= 448 && units <= 512 && (int64_t)max_context_len * 2 * D * es >= 384 * 1024;
+  if (es == 4) return units >= 448 && units <= 512 && (int64_t)max_context_len * 2 * D * es >= 384 * 1024;
+  return units >= 384 && units <= 512;
 }
 
 // With this step's new rows (app.T > 0), the workgroup of (sequence s, KV

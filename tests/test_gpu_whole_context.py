@@ -132,14 +132,17 @@ def test_whole_context_limits():
     assert f(32, 32, 4, 64, "f16", 2048)        # 128 pairs
     assert not f(31, 32, 4, 64, "f16", 2048)    # 124 pairs, contexts past 1536
     assert f(31, 32, 4, 64, "f16", 1536)        # 124 pairs, contexts up to 1536
-    # a second round of workgroups: 448 to 512 pairs, 384 KiB or more per pair
-    assert f(128, 32, 4, 64, "f16", 1536)       # 512 pairs, d 64: from 1536 tokens on
-    assert not f(128, 32, 4, 64, "f16", 1535)
-    assert f(64, 32, 8, 128, "bf16", 768)       # 512 pairs, d 128: from 768 tokens on
-    assert not f(64, 32, 8, 128, "bf16", 767)
-    assert f(56, 32, 8, 128, "bf16", 1024)      # 448 pairs
-    assert not f(55, 32, 8, 128, "bf16", 2048)  # 440 pairs
+    # a second round of workgroups: 384 to 512 pairs at any length (16-bit and 8-bit pools)
+    assert f(128, 32, 4, 64, "f16", 1535)       # 512 pairs
+    assert f(48, 32, 8, 128, "bf16", 2048)      # 384 pairs
+    assert not f(47, 32, 8, 128, "bf16", 2048)  # 376 pairs
+    assert not f(40, 32, 8, 128, "bf16", 1024)  # 320 pairs
+    assert f(56, 32, 8, 128, "bf16", 512)       # 448 pairs
     assert not f(129, 32, 4, 64, "f16", 2048)   # 516 pairs
+    # fp32 pools (the vector routine): 448 to 512 pairs, 384 KiB or more per pair
+    assert f(256, 4, 2, 128, "f32", 384)        # 512 pairs, 384 KiB
+    assert not f(256, 4, 2, 128, "f32", 383)
+    assert not f(192, 4, 2, 128, "f32", 2048)   # 384 pairs
     assert f(64, 16, 4, 128, "bf16", 1000)      # G 4 at head_dim 128
     assert f(64, 32, 4, 128, "bf16", 1000)      # G 8 at head_dim 128 (16-bit: MFMA)
     assert f(64, 64, 4, 128, "f16", 1000)       # G 16
@@ -147,8 +150,8 @@ def test_whole_context_limits():
     assert not f(64, 32, 4, 64, "f32", 1000)    # fp32, G 8 at head_dim 64: registers
     assert f(8, 32, 8, 128, "fp8_e4m3", 1000)  # 8-bit pools: the same rule
     assert not f(8, 32, 8, 128, "fp8_e4m3", 2000)  # 64 pairs, contexts past 1536
-    assert f(64, 32, 8, 128, "fp8_e4m3", 1536)  # 512 pairs, 384 KiB per pair at 1 byte
-    assert not f(64, 32, 8, 128, "fp8_e4m3", 1535)
+    assert f(64, 32, 8, 128, "fp8_e4m3", 100)   # 512 pairs
+    assert not f(40, 32, 8, 128, "fp8_e4m3", 1000)  # 320 pairs
     assert not f(0, 32, 4, 64, "f16", 100)
     assert not f(8, 30, 4, 64, "f16", 100)      # n_q_heads not a multiple
     # the split path just past the span still matches the oracle
