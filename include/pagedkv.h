@@ -387,11 +387,13 @@ int32_t paged_attention_decode_partition_size(void);
 /* 1 when paged_attention_decode and paged_attention_decode_append take the
  * whole-context path for these sizes, 0 otherwise (the split-context path;
  * paged_attention_decode_partitions / _reduce always split).  The path is
- * taken when max_context_len <= 2048 and, with P = num_seqs * n_kv_heads,
- * either P <= 256 and (P >= 128 or max_context_len <= 1536), or 384 <= P <=
- * 512 (16-bit and 8-bit pools) — for fp32 pools instead (n_q_heads /
- * n_kv_heads) * head_dim * 4 <= 1024 and the second band 448 <= P <= 512 with
- * max_context_len * 2 * head_dim * 4 >= 384 KiB (the decode of a small batch
+ * taken, with P = num_seqs * n_kv_heads, for 16-bit and 8-bit pools when
+ * max_context_len <= 4096 and either P <= 256 and (P >= 128 or
+ * max_context_len <= 1536), or 384 <= P <= 512 and max_context_len <= 2048;
+ * for fp32 pools when max_context_len <= 2048, (n_q_heads / n_kv_heads) *
+ * head_dim * 4 <= 1024 and either P <= 256 and (P >= 128 or max_context_len
+ * <= 1536), or 448 <= P <= 512 with max_context_len * 2 * head_dim * 4 >= 384
+ * KiB (the decode of a small batch
  * is bound by the latency of one or two rounds of reads, not by HBM
  * bandwidth).  ("The decode stage, and how to spot the
  * waste", Life of a prompt: the same attention, one query per sequence.)

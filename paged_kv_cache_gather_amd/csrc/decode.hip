@@ -561,7 +561,7 @@ struct TokenRows {
   __device__ int limit(int mi) const { return pos0 + mi + 1; }
 };
 // WholeRows: the G query heads of sequence s over its whole context, one
-// "partition" of up to kWholeSpan tokens whose result is final (no merge).
+// "partition" of up to kWholeSpanM tokens whose result is final (no merge).
 struct WholeRows {
   static constexpr bool kCausal = false;
   int s;
@@ -1168,8 +1168,8 @@ decode_partition_kernel(void* __restrict__ out, float* __restrict__ ws_o, float*
 }
 
 // ---- short contexts in a small batch: one launch, no merge ------------------
-// When every context fits kWholeSpan tokens and the batch has few (sequence,
-// KV head) pairs, split partitions and the merge would leave the chip idle
+// When every context fits the span (kWholeSpanM tokens on the MFMA routine,
+// kWholeSpan on the vector one) and the batch has few (sequence, KV head) pairs, split partitions and the merge would leave the chip idle
 // between three launches.  Instead one workgroup of kWholeWaves waves takes
 // a whole (sequence, KV head): the sequence's blocks are dealt evenly to its
 // waves (a short context still uses all of them), the waves' softmax states
@@ -1178,30 +1178,35 @@ decode_partition_kernel(void* __restrict__ out, float* __restrict__ ws_o, float*
 // MFMA partition routine (the G query rows padded to one 16-row tile: with
 // G = 8 the vector routine's products, not the reads, set its pace); fp32
 // pools the vector routine.
-constexpr int kWholeSpan = 2048;      // context tokens one workgroup takes
+constexpr int kWholeSpan = 2048;      // context tokens one workgroup takes (vector routine)
+constexpr int kWholeSpanM = 4096;     // and on the MFMA routine (16-bit and 8-bit pools)
 constexpr int kWholeWaves = 16;       // its waves (4 per SIMD)
-constexpr int kWholeBlocks = kWholeSpan / kBlockSize;
 
 // Does a batch take the whole-context path?  One workgroup fills a CU and the
 // 256 CUs take P = (sequence, KV head) pairs in rounds of 256.  16-bit and
-// 8-bit pools take any G (one 16-row MFMA tile); on fp32 pools the vector
-// routine's per-wave accumulators must stay within 128 registers
-// (G x D x 4 <= 1024).  Measured against the split path on uniform and
-// prefix-sharing batches: up to 256 pairs — one round — the whole-context
-// launch wins except when fewer than 128 pairs hold contexts past 1536 tokens
-// (too few CUs take part; the split path's 4x more workgroups win).  A second
-// round: on the MFMA routine it wins from 384 pairs on at every length up to
-// the span (TinyLlama and Llama-3-8B heads, 384 to 640 pairs) and loses at
-// 320; it stops at 512 pairs, past which reading shared partitions once and
-// the split path's finer work units win on prefix-sharing batches.  The
-// vector routine (fp32 pools) keeps the band it was measured for: 448 to
-// 512 pairs with at least 384 KiB per pair.
+// 8-bit pools take any G (one 16-row MFMA tile) and contexts up to 4096
+// tokens; on fp32 pools the vector routine's per-wave accumulators must stay
+// within 128 registers (G x D x 4 <= 1024) and its span is 2048.  Measured
+// against the split path on uniform and prefix-sharing batches: up to 256
+// pairs — one round — the whole-context launch wins except when fewer than
+// 128 pairs hold contexts past 1536 tokens (too few CUs take part; the split
+// path's 4x more workgroups win).  A second round: on the MFMA routine it
+// wins from 384 pairs on at every length up to 2048 (TinyLlama and
+// Llama-3-8B heads, 384 to 640 pairs) and loses at 320; it stops at 512
+// pairs and 2048 tokens, past which reading shared partitions once and the
+// split path's finer work units win on prefix-sharing batches.  The vector
+// routine (fp32 pools) keeps the band it was measured for: 448 to 512 pairs
+// with at least 384 KiB per pair.
 inline bool whole_context(int B, int Hkv, int G, int D, int es, int max_context_len) {
-  if (max_context_len > kWholeSpan || (es == 4 && G * D * es > 1024)) return false;
   const int64_t units = (int64_t)B * Hkv;
+  if (es == 4) {
+    if (max_context_len > kWholeSpan || G * D * es > 1024) return false;
+    if (units <= 256) return units >= 128 || max_context_len <= 1536;
+    return units >= 448 && units <= 512 && (int64_t)max_context_len * 2 * D * es >= 384 * 1024;
+  }
+  if (max_context_len > kWholeSpanM) return false;
   if (units <= 256) return units >= 128 || max_context_len <= 1536;
-  if (es == 4) return units >= 448 && units <= 512 && (int64_t)max_context_len * 2 * D * es >= 384 * 1024;
-  return units >= 384 && units <= 512;
+  return units >= 384 && units <= 512 && max_context_len <= kWholeSpan;
 }
 
 // With this step's new rows (app.T > 0), the workgroup of (sequence s, KV
@@ -1212,7 +1217,10 @@ inline bool whole_context(int B, int Hkv, int G, int D, int es, int max_context_
 // KV is the pools' type, QT the queries' (the same for 16-bit and fp32
 // pools; fp16 or bf16 queries over 8-bit pools, whose values are scaled by
 // v_mul and whose new rows are quantised on the way in).
-template <typename KV, typename QT, int D, int G, int OutCode>
+// SPAN: the launch's span (kWholeSpan, or kWholeSpanM when a context of the
+// batch needs it): each wave takes SPAN / 16 / kWholeWaves blocks, so a batch
+// of short contexts keeps all 16 waves busy.
+template <typename KV, typename QT, int D, int G, int OutCode, int SPAN>
 __global__ void __launch_bounds__(kWholeWaves * 64, 1)
 decode_whole_kernel(void* __restrict__ out, const typename QT::bits* __restrict__ q, const unsigned char* kpool,
                     const unsigned char* vpool, const int32_t* __restrict__ tables, int max_blocks,
@@ -1241,14 +1249,16 @@ decode_whole_kernel(void* __restrict__ out, const typename QT::bits* __restrict_
     return;
   }
   if constexpr (KV::kBytes != 4) {
-    // each wave's 8 blocks in parts of 4 (head_dim 64, and 8-bit pools) or 2
+    // each wave's blocks in parts of 4 (head_dim 64, and 8-bit pools) or 2
     // (16-bit at 128): within 128 registers at 4 waves per SIMD
-    __shared__ __attribute__((aligned(16))) RunLds<D, 16, kWholeWaves, kWholeBlocks> sh;
-    mfma_partition<KV, QT, D, G, 1, true, OutCode, (D == 64 || KV::kBytes == 1) ? 2 : 4, kWholeWaves,
-                   kWholeBlocks>(WholeRows{s}, L, g, 0, sh, out, nullptr, nullptr, q, kpool, vpool, tables,
+    constexpr int PB = SPAN / kBlockSize;
+    __shared__ __attribute__((aligned(16))) RunLds<D, 16, kWholeWaves, PB> sh;
+    mfma_partition<KV, QT, D, G, 1, true, OutCode, (PB / kWholeWaves) / ((D == 64 || KV::kBytes == 1) ? 4 : 2),
+                   kWholeWaves, PB>(WholeRows{s}, L, g, 0, sh, out, nullptr, nullptr, q, kpool, vpool, tables,
                                  max_blocks, Hkv, num_blocks, scale_log2, v_mul, 1);
   } else {
     using T = KV;
+    static_assert(SPAN == kWholeSpan, "the vector routine's span");
     constexpr int RMAX = G;
     constexpr int SMEM = (kWholeSpan > kWholeWaves * D ? kWholeSpan : kWholeWaves * D) * RMAX;
     __shared__ __attribute__((aligned(16))) float smem[SMEM];
@@ -1434,12 +1444,20 @@ void launch_reduce(const DecodeArgs& a, int G) {
 
 template <typename KV, typename QT, int D, int G, int OutCode>
 void launch_whole(const DecodeArgs& a) {
-  if constexpr (KV::kBytes != 4 || G * D * KV::kBytes <= 1024) {
-    hipLaunchKernelGGL((decode_whole_kernel<KV, QT, D, G, OutCode>), dim3((unsigned)a.Hkv, (unsigned)a.B),
-                       dim3(kWholeWaves * 64), 0, a.stream, a.out, (const typename QT::bits*)a.q, a.kpool, a.vpool,
-                       a.tables, a.max_blocks, a.lens, a.Hkv, a.num_blocks, a.max_context_len, a.scale_log2,
-                       a.v_mul, a.app);
+  const dim3 grid((unsigned)a.Hkv, (unsigned)a.B), block(kWholeWaves * 64);
+  const auto* q = (const typename QT::bits*)a.q;
+  if constexpr (KV::kBytes != 4) {
+    if (a.max_context_len > kWholeSpan) {
+      hipLaunchKernelGGL((decode_whole_kernel<KV, QT, D, G, OutCode, kWholeSpanM>), grid, block, 0, a.stream, a.out,
+                         q, a.kpool, a.vpool, a.tables, a.max_blocks, a.lens, a.Hkv, a.num_blocks, a.max_context_len,
+                         a.scale_log2, a.v_mul, a.app);
+      return;
+    }
   }
+  if constexpr (KV::kBytes != 4 || G * D * KV::kBytes <= 1024)
+    hipLaunchKernelGGL((decode_whole_kernel<KV, QT, D, G, OutCode, kWholeSpan>), grid, block, 0, a.stream, a.out, q,
+                       a.kpool, a.vpool, a.tables, a.max_blocks, a.lens, a.Hkv, a.num_blocks, a.max_context_len,
+                       a.scale_log2, a.v_mul, a.app);
 }
 
 template <typename T, int D, int G, int OutCode>

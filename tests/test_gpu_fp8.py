@@ -156,7 +156,7 @@ def test_decode_fp8_small(name, Hq, Hkv, d, dtype, lens, out_kind):
     _check(w, out, out_dtype)
 
 
-WHOLE_LENS = [1, 15, 16, 17, 100, 511, 512, 513, 1024, 1500, 2047, 2048]
+WHOLE_LENS = [1, 15, 16, 17, 100, 511, 512, 513, 1024, 1500, 2047, 2048, 3071, 4096]
 FP8_WHOLE = [
     # name, Hq, Hkv, d, q dtype
     ("whole_tinyllama_f16", 32, 4, 64, "f16"),
@@ -176,7 +176,7 @@ def test_decode_fp8_whole_context(name, Hq, Hkv, d, dtype):
     from paged_kv_cache_gather_amd.batch import DeviceBatch
     n = -(-128 // Hkv)
     lens = [WHOLE_LENS[i % len(WHOLE_LENS)] for i in range(max(n, len(WHOLE_LENS)))]
-    w = synth.custom_workload(name, Hq, Hkv, d, dtype, 4096, seed=27, decode_lens=lens)
+    w = synth.custom_workload(name, Hq, Hkv, d, dtype, 8192, seed=27, decode_lens=lens)
     kw = dict(fill="host", out_dtype="f32", kv_cache="fp8_e4m3", k_scale=FP8_K_SCALE, v_scale=FP8_V_SCALE)
     sep, one = DeviceBatch(w, DEV, **kw), DeviceBatch(w, DEV, **kw)
     assert pkv.paged_attention_decode_whole_context(w.n_decode, Hq, Hkv, d, "fp8_e4m3", sep.decode.max_context_len)

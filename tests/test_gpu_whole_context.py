@@ -18,13 +18,15 @@ pytestmark = [pytest.mark.gpu, pytest.mark.skipif(not gpu_available(), reason="n
 
 DEV = "cuda:0"
 LENS = [1, 15, 16, 17, 100, 511, 512, 513, 1024, 1500, 2047, 2048]
+LONG = [2049, 3071, 4095, 4096]  # past the vector routine's span, within the MFMA routine's
 
 
-def _lens(n_kv_heads):
-    """LENS repeated to 128 (sequence, KV head) pairs: contexts up to 2048
-    take the whole-context path from 128 pairs on."""
+def _lens(n_kv_heads, long=True):
+    """LENS (and LONG) repeated to 128 (sequence, KV head) pairs: contexts up
+    to the span take the whole-context path from 128 pairs on."""
+    base = LENS + LONG if long else LENS
     n = -(-128 // n_kv_heads)
-    return [LENS[i % len(LENS)] for i in range(max(n, len(LENS)))]
+    return [base[i % len(base)] for i in range(max(n, len(base)))]
 
 CASES = [
     # name, Hq, Hkv, d, dtype
@@ -50,7 +52,7 @@ def _whole(w, max_len):
 @pytest.mark.parametrize("out_kind", ["f32", "kv"])
 def test_whole_context_matches_oracle_and_split_path(name, Hq, Hkv, d, dtype, out_kind):
     from paged_kv_cache_gather_amd.batch import DeviceBatch
-    w = synth.custom_workload(name, Hq, Hkv, d, dtype, 4096, seed=71, decode_lens=_lens(Hkv))
+    w = synth.custom_workload(name, Hq, Hkv, d, dtype, 8192, seed=71, decode_lens=_lens(Hkv, dtype != "f32"))
     out_dtype = "f32" if out_kind == "f32" else dtype
     b = DeviceBatch(w, DEV, fill="host", out_dtype=out_dtype)
     assert _whole(w, b.decode.max_context_len)
@@ -128,13 +130,16 @@ def test_whole_context_limits():
     import paged_kv_cache_gather_amd as pkv
     f = pkv.paged_attention_decode_whole_context
     assert f(64, 32, 4, 64, "f16", 2048)        # TinyLlama-shaped batch: 256 pairs
-    assert not f(64, 32, 4, 64, "f16", 2049)    # a context past the span
+    assert f(64, 32, 4, 64, "f16", 4096)        # the MFMA routine's span
+    assert not f(64, 32, 4, 64, "f16", 4097)    # a context past the span
+    assert not f(64, 8, 4, 64, "f32", 2049)     # past the vector routine's span (fp32 pools)
     assert f(32, 32, 4, 64, "f16", 2048)        # 128 pairs
     assert not f(31, 32, 4, 64, "f16", 2048)    # 124 pairs, contexts past 1536
     assert f(31, 32, 4, 64, "f16", 1536)        # 124 pairs, contexts up to 1536
     # a second round of workgroups: 384 to 512 pairs at any length (16-bit and 8-bit pools)
     assert f(128, 32, 4, 64, "f16", 1535)       # 512 pairs
     assert f(48, 32, 8, 128, "bf16", 2048)      # 384 pairs
+    assert not f(48, 32, 8, 128, "bf16", 2049)  # a second round only up to 2048 tokens
     assert not f(47, 32, 8, 128, "bf16", 2048)  # 376 pairs
     assert not f(40, 32, 8, 128, "bf16", 1024)  # 320 pairs
     assert f(56, 32, 8, 128, "bf16", 512)       # 448 pairs
@@ -156,7 +161,7 @@ def test_whole_context_limits():
     assert not f(8, 30, 4, 64, "f16", 100)      # n_q_heads not a multiple
     # the split path just past the span still matches the oracle
     from paged_kv_cache_gather_amd.batch import DeviceBatch
-    w = synth.custom_workload("whole_edge", 32, 4, 64, "f16", 4096, seed=75, decode_lens=[2049, 7, 2048] * 11)
+    w = synth.custom_workload("whole_edge", 32, 4, 64, "f16", 8192, seed=75, decode_lens=[4097, 7, 4096] * 11)
     b = DeviceBatch(w, DEV, fill="host", out_dtype="f32")
     assert not _whole(w, b.decode.max_context_len)
     b.append_decode()
