@@ -1169,15 +1169,16 @@ decode_partition_kernel(void* __restrict__ out, float* __restrict__ ws_o, float*
 
 // ---- short contexts in a small batch: one launch, no merge ------------------
 // When every context fits the span (kWholeSpanM tokens on the MFMA routine,
-// kWholeSpan on the vector one) and the batch has few (sequence, KV head) pairs, split partitions and the merge would leave the chip idle
-// between three launches.  Instead one workgroup of kWholeWaves waves takes
-// a whole (sequence, KV head): the sequence's blocks are dealt evenly to its
-// waves (a short context still uses all of them), the waves' softmax states
-// merge in LDS and the output is written directly.  Partitions that
-// sequences share are read per sequence on this path.  16-bit pools run the
-// MFMA partition routine (the G query rows padded to one 16-row tile: with
-// G = 8 the vector routine's products, not the reads, set its pace); fp32
-// pools the vector routine.
+// kWholeSpan on the vector one) and the batch has few (sequence, KV head)
+// pairs, split partitions and the merge would leave the chip idle between
+// three launches.  Instead one workgroup of kWholeWaves waves takes a whole
+// (sequence, KV head), the waves' softmax states merge in LDS and the output
+// is written directly.  Partitions that sequences share are read per sequence
+// on this path.  16-bit and 8-bit pools run the MFMA partition routine (the G
+// query rows padded to one 16-row tile: with G = 8 the vector routine's
+// products, not the reads, set its pace), each wave taking a fixed run of
+// consecutive blocks; fp32 pools the vector routine, which deals the
+// sequence's blocks evenly to the waves.
 constexpr int kWholeSpan = 2048;      // context tokens one workgroup takes (vector routine)
 constexpr int kWholeSpanM = 4096;     // and on the MFMA routine (16-bit and 8-bit pools)
 constexpr int kWholeWaves = 16;       // its waves (4 per SIMD)
