@@ -591,7 +591,7 @@ struct WholeRows {
 //    the waves' (max, sum, o) are merged through LDS and written as each
 //    member's partition result (8-bit values: times v_mul, the pool scale).
 template <typename KV, typename QT, int D, int G, int RT, bool Masked, int OutCode, int NH, int NW,
-          int PBLK = kPartBlocks, typename Rows>
+          int PBLK = kPartBlocks, bool kEven = false, typename Rows>
 __device__ __forceinline__ void mfma_partition(const Rows& R, int n, int g, int p, RunLds<D, 16 * RT, NW, PBLK>& sh,
                                                void* __restrict__ out, float* __restrict__ ws_o,
                                                float* __restrict__ ws_ml, const typename QT::bits* __restrict__ q,
@@ -652,8 +652,18 @@ __device__ __forceinline__ void mfma_partition(const Rows& R, int n, int g, int 
   if (tid < PBLK)
     sh.blk[tid] = (!Masked || tid * kBlockSize < n) ? tables[(int64_t)R.table_row() * max_blocks + p * PBLK + tid] : 0;
   __syncthreads();
-  const int32_t* tab = sh.blk + w * WB;
-  const int wbase = w * WB * kBlockSize;  // the wave's first token in the partition
+  // the wave's blocks: WB from block w WB, or (kEven) the valid blocks dealt
+  // evenly in whole pairs, so that a short context keeps every wave busy;
+  // nw = the end of the wave's tokens (partition-relative)
+  int wb = WB;
+  if constexpr (kEven) {
+    const int per = ((n + kBlockSize - 1) / kBlockSize + NW - 1) / NW;
+    wb = (per + 1) & ~1;
+    wb = wb < WB ? wb : WB;
+  }
+  const int32_t* tab = sh.blk + w * wb;
+  const int wbase = w * wb * kBlockSize;  // the wave's first token in the partition
+  const int nw = kEven ? (n < wbase + wb * kBlockSize ? n : wbase + wb * kBlockSize) : n;
   float m[RT], l[RT];
   f32x4 o[RT][DT];
 #pragma unroll
@@ -661,7 +671,7 @@ __device__ __forceinline__ void mfma_partition(const Rows& R, int n, int g, int 
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) o[rt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  if (!Masked || wbase < n) {  // uniform per wave
+  if (!Masked || wbase < nw) {  // uniform per wave
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
       m[rt] = -INFINITY;
@@ -673,7 +683,7 @@ __device__ __forceinline__ void mfma_partition(const Rows& R, int n, int g, int 
     for (int h = 0; h < NH; ++h) {
       const int hb = h * HB;                      // the part's first block (wave-local)
       const int hbase = wbase + hb * kBlockSize;  // and token (partition-local)
-      if (Masked && hbase >= n) break;            // uniform
+      if (Masked && hbase >= nw) break;           // uniform
       // K operands: score tile kt, row m
       u32x4 ka[HB][KC];
       if constexpr (kNatural) {
@@ -681,7 +691,7 @@ __device__ __forceinline__ void mfma_partition(const Rows& R, int n, int g, int 
         // 4 chunks x 16 tokens = 1 KiB contiguous
 #pragma unroll
         for (int kt = 0; kt < HB; ++kt) {
-          const bool in = !Masked || hbase + kt * kBlockSize < n;
+          const bool in = !Masked || hbase + kt * kBlockSize < nw;
           const int64_t kb = clamp_block(tab[hb + kt], num_blocks);
           const unsigned char* kr = kpool + ((kb * Hkv + g) * CH + q4) * (kBlockSize * 16) + r16 * 16;
 #pragma unroll
@@ -694,7 +704,7 @@ __device__ __forceinline__ void mfma_partition(const Rows& R, int n, int g, int 
         const int k_half = r16 >> 3, k_tok = r16 & 7;
 #pragma unroll
         for (int kp = 0; kp < HB / 2; ++kp) {
-          const bool in = !Masked || hbase + (2 * kp + k_half) * kBlockSize < n;
+          const bool in = !Masked || hbase + (2 * kp + k_half) * kBlockSize < nw;
           const int64_t kb = clamp_block(tab[hb + 2 * kp + k_half], num_blocks);
           const unsigned char* kr = kpool + ((kb * Hkv + g) * CH + q4) * (kBlockSize * 16) + k_tok * 16;
 #pragma unroll
@@ -738,8 +748,8 @@ __device__ __forceinline__ void mfma_partition(const Rows& R, int n, int g, int 
 #pragma unroll
       for (int kp = 0; kp < HB / 2; ++kp) {
         if constexpr (kNatural) {
-          const bool inA = !Masked || hbase + 2 * kp * kBlockSize < n;
-          const bool inB = !Masked || hbase + (2 * kp + 1) * kBlockSize < n;
+          const bool inA = !Masked || hbase + 2 * kp * kBlockSize < nw;
+          const bool inB = !Masked || hbase + (2 * kp + 1) * kBlockSize < nw;
           const int64_t vbA = clamp_block(tab[hb + 2 * kp], num_blocks);
           const int64_t vbB = clamp_block(tab[hb + 2 * kp + 1], num_blocks);
           const unsigned char* vrA = vpool + (vbA * Hkv + g) * (int64_t)TILE + r16 * VROW + q4 * (VROW / 4);
@@ -751,7 +761,7 @@ __device__ __forceinline__ void mfma_partition(const Rows& R, int n, int g, int 
             vraw[kp][dt] = u32x4{(uint32_t)a, (uint32_t)(a >> 32), (uint32_t)b, (uint32_t)(b >> 32)};
           }
         } else {
-          const bool in = !Masked || hbase + (2 * kp + (q4 >> 1)) * kBlockSize < n;
+          const bool in = !Masked || hbase + (2 * kp + (q4 >> 1)) * kBlockSize < nw;
           const int64_t vb = clamp_block(tab[hb + 2 * kp + (q4 >> 1)], num_blocks);
           const unsigned char* vr = vpool + (vb * Hkv + g) * (int64_t)TILE + r16 * VROW + (q4 & 1) * (VROW / 2);
 #pragma unroll
@@ -780,7 +790,7 @@ __device__ __forceinline__ void mfma_partition(const Rows& R, int n, int g, int 
               const int key = kNatural ? hbase + kt * kBlockSize + 4 * q4 + r
                                        : hbase + ((kt >> 1) * 2 + (q4 >> 1)) * kBlockSize + 8 * (kt & 1) +
                                              4 * (q4 & 1) + r;
-              x = key < (kCausal ? klim[rt] : n) ? x : -INFINITY;
+              x = key < (kCausal ? (klim[rt] < nw ? klim[rt] : nw) : nw) ? x : -INFINITY;
             }
             st[kt][rt][r] = x;
             mx = fmaxf(mx, x);
@@ -841,7 +851,7 @@ __device__ __forceinline__ void mfma_partition(const Rows& R, int n, int g, int 
           if constexpr (F8) {
             uint64_t bytes = vraw[kp][dt];
             if constexpr (Masked) {  // zero the codes of keys past the context (they may be NaN codes)
-              const int nv = n - (hbase + kp * 2 * kBlockSize + 8 * q4);
+              const int nv = nw - (hbase + kp * 2 * kBlockSize + 8 * q4);
               bytes &= nv >= 8 ? ~0ull : (nv <= 0 ? 0ull : (1ull << (8 * nv)) - 1ull);
             }
             va = e4m3x8_to<F16>((uint32_t)bytes, (uint32_t)(bytes >> 32));
@@ -850,7 +860,7 @@ __device__ __forceinline__ void mfma_partition(const Rows& R, int n, int g, int 
             if constexpr (Masked) {  // zero keys past the context (they may hold NaN)
 #pragma unroll
               for (int half = 0; half < 2; ++half) {  // blocks 2 kp and 2 kp + 1
-                const int nv = n - (hbase + (2 * kp + half) * kBlockSize + 4 * q4);
+                const int nv = nw - (hbase + (2 * kp + half) * kBlockSize + 4 * q4);
 #pragma unroll
                 for (int e = 0; e < 2; ++e)
                   vv[2 * half + e] &= 2 * e + 1 < nv ? 0xffffffffu : (2 * e < nv ? 0x0000ffffu : 0u);
@@ -1176,9 +1186,9 @@ decode_partition_kernel(void* __restrict__ out, float* __restrict__ ws_o, float*
 // is written directly.  Partitions that sequences share are read per sequence
 // on this path.  16-bit and 8-bit pools run the MFMA partition routine (the G
 // query rows padded to one 16-row tile: with G = 8 the vector routine's
-// products, not the reads, set its pace), each wave taking a fixed run of
-// consecutive blocks; fp32 pools the vector routine, which deals the
-// sequence's blocks evenly to the waves.
+// products, not the reads, set its pace), fp32 pools the vector routine;
+// both deal the sequence's blocks evenly to the waves (the MFMA routine in
+// whole block pairs), so a short context keeps every wave busy.
 constexpr int kWholeSpan = 2048;      // context tokens one workgroup takes (vector routine)
 constexpr int kWholeSpanM = 4096;     // and on the MFMA routine (16-bit and 8-bit pools)
 constexpr int kWholeWaves = 16;       // its waves (4 per SIMD)
@@ -1219,8 +1229,7 @@ inline bool whole_context(int B, int Hkv, int G, int D, int es, int max_context_
 // pools; fp16 or bf16 queries over 8-bit pools, whose values are scaled by
 // v_mul and whose new rows are quantised on the way in).
 // SPAN: the launch's span (kWholeSpan, or kWholeSpanM when a context of the
-// batch needs it): each wave takes SPAN / 16 / kWholeWaves blocks, so a batch
-// of short contexts keeps all 16 waves busy.
+// batch needs it): a wave takes at most SPAN / 16 / kWholeWaves blocks.
 template <typename KV, typename QT, int D, int G, int OutCode, int SPAN>
 __global__ void __launch_bounds__(kWholeWaves * 64, 1)
 decode_whole_kernel(void* __restrict__ out, const typename QT::bits* __restrict__ q, const unsigned char* kpool,
@@ -1255,8 +1264,8 @@ decode_whole_kernel(void* __restrict__ out, const typename QT::bits* __restrict_
     constexpr int PB = SPAN / kBlockSize;
     __shared__ __attribute__((aligned(16))) RunLds<D, 16, kWholeWaves, PB> sh;
     mfma_partition<KV, QT, D, G, 1, true, OutCode, (PB / kWholeWaves) / ((D == 64 || KV::kBytes == 1) ? 4 : 2),
-                   kWholeWaves, PB>(WholeRows{s}, L, g, 0, sh, out, nullptr, nullptr, q, kpool, vpool, tables,
-                                 max_blocks, Hkv, num_blocks, scale_log2, v_mul, 1);
+                   kWholeWaves, PB, true>(WholeRows{s}, L, g, 0, sh, out, nullptr, nullptr, q, kpool, vpool, tables,
+                                       max_blocks, Hkv, num_blocks, scale_log2, v_mul, 1);
   } else {
     using T = KV;
     static_assert(SPAN == kWholeSpan, "the vector routine's span");
