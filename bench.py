@@ -572,7 +572,8 @@ def cpu_baseline(w, tables, sample_1thread=32):
     table (oracle.gather) and run the attention (oracle.attention).  The host
     pools are written by the oracle's own scatter from the seeded generator's
     rows (not timed).  Timed twice: every sequence with one worker thread per
-    host core (up to 16, the GPU machine's share), and a sample on one thread."""
+    host core (at most 16: the host cores one GPU of the node is allotted), and a
+    sample on one thread."""
     import numpy as np
     from concurrent.futures import ThreadPoolExecutor
     import oracle
