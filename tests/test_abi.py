@@ -318,3 +318,33 @@ def test_fp8_pool_sizing():
     assert pkv.paged_kv_blocks_for_budget(budget, 32, 8, 128, "fp8_e4m3") == oracle.blocks_for_budget(
         budget, 32, 8, 128, 1)
     assert pkv.paged_kv_pool_bytes(1024, 8, 128, "fp8_e4m3") == (1024 * 8 * 16 * 128,) * 2
+
+
+def _whole_rule(B, Hq, Hkv, d, dtype, L):
+    """The whole-context rule as include/pagedkv.h states it."""
+    es = {"f32": 4, "f16": 2, "bf16": 2, "fp8_e4m3": 1}[dtype]
+    P, G = B * Hkv, Hq // Hkv
+    if es == 4:
+        if L > 2048 or G * d * 4 > 1024:
+            return False
+        if P <= 256:
+            return P >= 128 or L <= 1536
+        return 448 <= P <= 512 and L * 2 * d * 4 >= 384 * 1024
+    if L > 4096:
+        return False
+    if P <= 256:
+        return P >= 128 or L <= 1536
+    return 384 <= P <= 512 and L <= 2048
+
+
+def test_whole_context_rule_as_documented():
+    # host-only: paged_attention_decode_whole_context against the header's
+    # statement of the rule over a grid of sizes, every K/V dtype
+    f = pkv.paged_attention_decode_whole_context
+    for dtype in ("f32", "f16", "bf16", "fp8_e4m3"):
+        for Hq, Hkv, d in ((32, 8, 128), (32, 4, 64), (64, 8, 128), (8, 2, 64), (4, 2, 128), (40, 40, 128)):
+            for B in (1, 8, 15, 16, 31, 32, 47, 48, 56, 64, 65, 128, 129, 256):
+                for L in (0, 1, 384, 767, 768, 1535, 1536, 1537, 2048, 2049, 3000, 4096, 4097):
+                    assert bool(f(B, Hq, Hkv, d, dtype, L)) == _whole_rule(B, Hq, Hkv, d, dtype, L), \
+                        (B, Hq, Hkv, d, dtype, L)
+    assert not f(0, 32, 8, 128, "bf16", 100) and not f(8, 30, 4, 64, "f16", 100)
